@@ -1,0 +1,265 @@
+"""Seeded synthetic inputs for paged / block-sparse-row (BSR) decode attention.
+
+This module only builds inputs: page tables, lengths and random values. It
+holds none of the attention arithmetic, so the oracle and the HIP path can both
+be fed from it without sharing any of the method.
+
+Layout of what is produced (the same for every consumer):
+
+* ``kv_indptr``  int32 [B+1]  -- request b lists pages kv_indices[kv_indptr[b]:kv_indptr[b+1]]
+* ``kv_indices`` int32 [nnz]  -- physical page ids, in logical (token) order
+* ``last_page_len`` int32 [B] -- valid tokens in the last listed page (1..P; 0 if no page)
+* ``q``  [B, H_q, d]
+* ``k_pool``, ``v_pool`` [num_pool_pages, H_kv, P, d]   (page-major, head, token, dim)
+
+The block-sparse view (FlashInfer paper explainer, "FlashInfer: Block-Sparse
+KV 캐시로 어텐션 병목을 해소하다", section on the Block-Sparse format): the KV
+cache is a block-sparse matrix whose blocks are runs of consecutive tokens; a
+request lists only its active blocks. A page table is that matrix in BSR form
+with block size = page size. Blocks that are not listed are inactive.
+
+Structure (lengths, permutations, masks) comes from
+``numpy.random.default_rng([config_id, 0])``; values come from a torch
+generator seeded with ``1_000_003 * config_id + 1`` on the device the caller
+asks for, drawn as q, then K, then V, each N(0, 1) in float32 and then cast to
+the config dtype (torch's cast, round-to-nearest-even). Every pool page that no
+request lists and every slot past ``last_page_len`` in a last page is set to
+NaN, so a kernel that touches them poisons its output.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional
+
+import numpy as np
+
+# Five workloads. Sizes follow the decode-attention study cases: a tiny fp32
+# case, a uniform Llama-3-8B-shaped batch (32 query heads, 8 KV heads,
+# head_dim 128), a skewed batch, a long-context batch, and a block-sparse
+# batch with a shared prefix.
+CONFIG_NAMES = {
+    1: "tiny_paged_f32",
+    2: "uniform_b64_l2048",
+    3: "skewed_b64_loguniform_32_32768",
+    4: "long_b2_l131072_65536",
+    5: "sparse_prefix_b32_p64",
+}
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    config_id: int
+    batch: int
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    dtype: str  # "f32" or "bf16"
+    num_pool_pages: int
+    kv_indptr: np.ndarray
+    kv_indices: np.ndarray
+    last_page_len: np.ndarray
+    # pool pages no request lists (filled with NaN)
+    unused_pages: np.ndarray
+    value_seed: int
+    # physical pages listed by more than one request (config 5 prefix)
+    shared_pages: int = 0
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def group_size(self) -> int:
+        return self.num_qo_heads // self.num_kv_heads
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def num_pages(self, b: int) -> int:
+        return int(self.kv_indptr[b + 1] - self.kv_indptr[b])
+
+    def kv_len(self, b: int) -> int:
+        n = self.num_pages(b)
+        if n == 0:
+            return 0
+        return (n - 1) * self.page_size + int(self.last_page_len[b])
+
+    def kv_lens(self) -> np.ndarray:
+        return np.array([self.kv_len(b) for b in range(self.batch)], dtype=np.int64)
+
+    def algorithmic_bytes(self, unique: bool = True) -> int:
+        """Bytes the method must move: each active K and V row once per KV
+        head, plus reading q and writing the output. With ``unique`` a
+        physical page listed by several requests counts once (shared prefix)."""
+        e = self.elem_bytes
+        if unique:
+            tok = self._unique_tokens()
+        else:
+            tok = int(self.kv_lens().sum())
+        kv = 2 * self.num_kv_heads * self.head_dim * tok * e
+        qo = 2 * self.batch * self.num_qo_heads * self.head_dim * e
+        return kv + qo
+
+    def _unique_tokens(self) -> int:
+        # token slots per physical page that some request reads
+        used = {}
+        P = self.page_size
+        for b in range(self.batch):
+            s, t = int(self.kv_indptr[b]), int(self.kv_indptr[b + 1])
+            for j in range(s, t):
+                n = P if j < t - 1 else int(self.last_page_len[b])
+                pg = int(self.kv_indices[j])
+                used[pg] = max(used.get(pg, 0), n)
+        return int(sum(used.values()))
+
+    # ------------------------------------------------------------------ values
+    def make_values(self, device="cpu"):
+        """Return (q, k_pool, v_pool) as torch tensors on ``device``."""
+        import torch
+
+        tdt = torch.float32 if self.dtype == "f32" else torch.bfloat16
+        g = torch.Generator(device=device)
+        g.manual_seed(self.value_seed)
+        B, Hq, Hkv, d, P = (self.batch, self.num_qo_heads, self.num_kv_heads,
+                            self.head_dim, self.page_size)
+        N = self.num_pool_pages
+
+        def draw(shape):
+            x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+            return x.to(tdt)
+
+        q = draw((B, Hq, d))
+        k = draw((N, Hkv, P, d))
+        v = draw((N, Hkv, P, d))
+        self._poison(k, device)
+        self._poison(v, device)
+        return q, k, v
+
+    def _poison(self, pool, device):
+        import torch
+
+        nan = float("nan")
+        if len(self.unused_pages):
+            idx = torch.as_tensor(self.unused_pages.astype(np.int64), device=device)
+            pool.index_fill_(0, idx, nan)
+        P = self.page_size
+        for b in range(self.batch):
+            n = self.num_pages(b)
+            if n == 0:
+                continue
+            ell = int(self.last_page_len[b])
+            if ell < P:
+                last = int(self.kv_indices[self.kv_indptr[b + 1] - 1])
+                pool[last, :, ell:, :] = nan
+
+
+# ---------------------------------------------------------------- structure
+def _pack(page_lists: List[List[int]], lens: List[int], page_size: int):
+    indptr = np.zeros(len(page_lists) + 1, dtype=np.int32)
+    for b, pl in enumerate(page_lists):
+        indptr[b + 1] = indptr[b] + len(pl)
+    indices = (np.concatenate([np.asarray(p, dtype=np.int32) for p in page_lists])
+               if indptr[-1] > 0 else np.zeros(0, dtype=np.int32))
+    last = np.zeros(len(page_lists), dtype=np.int32)
+    for b, L in enumerate(lens):
+        if len(page_lists[b]):
+            last[b] = L - page_size * (len(page_lists[b]) - 1)
+    return indptr, indices, last
+
+
+def paged_structure(lens, page_size, pool_pages, rng):
+    """Dense-in-logical-order paging: request b holds ceil(L_b/P) pages, taken
+    in order from one seeded permutation of the pool."""
+    npg = [(int(L) + page_size - 1) // page_size for L in lens]
+    total = sum(npg)
+    assert pool_pages >= total
+    perm = rng.permutation(pool_pages).astype(np.int32)
+    lists, off = [], 0
+    for n in npg:
+        lists.append(list(perm[off:off + n]))
+        off += n
+    indptr, indices, last = _pack(lists, [int(L) for L in lens], page_size)
+    unused = np.sort(perm[total:]).astype(np.int32)
+    return indptr, indices, last, unused
+
+
+def workload(config_id: int) -> Workload:
+    rng = np.random.default_rng([config_id, 0])
+    seed = 1_000_003 * config_id + 1
+    if config_id == 1:
+        lens = [17, 64, 100, 250]
+        ip, ix, lp, un = paged_structure(lens, 16, 40, rng)
+        return Workload(CONFIG_NAMES[1], 1, 4, 4, 1, 64, 16, "f32", 40, ip, ix, lp, un, seed)
+    if config_id == 2:
+        lens = [2048] * 64
+        ip, ix, lp, un = paged_structure(lens, 16, 10240, rng)
+        return Workload(CONFIG_NAMES[2], 2, 64, 32, 8, 128, 16, "bf16", 10240, ip, ix, lp, un, seed)
+    if config_id == 3:
+        u = rng.uniform(math.log(32.0), math.log(32768.0), size=64)
+        lens = np.clip(np.floor(np.exp(u)).astype(np.int64), 32, 32768)
+        pool = int(sum((int(L) + 15) // 16 for L in lens))
+        ip, ix, lp, un = paged_structure(lens, 16, pool, rng)
+        return Workload(CONFIG_NAMES[3], 3, 64, 32, 8, 128, 16, "bf16", pool, ip, ix, lp, un, seed)
+    if config_id == 4:
+        lens = [131072, 65536]
+        ip, ix, lp, un = paged_structure(lens, 64, 3072, rng)
+        return Workload(CONFIG_NAMES[4], 4, 2, 32, 8, 128, 64, "bf16", 3072, ip, ix, lp, un, seed)
+    if config_id == 5:
+        return _sparse_prefix(rng, seed)
+    raise ValueError(f"unknown config {config_id}")
+
+
+def _sparse_prefix(rng, seed) -> Workload:
+    """32 requests share the same 128 physical prefix pages (8192 tokens at
+    P = 64); each has a unique suffix of s_b ~ U{128..1024} tokens cut into
+    n_b = ceil(s_b/64) blocks, of which k_b = max(1, floor(n_b/4 + 1/2)) stay
+    active: always the newest block (it holds the token being decoded) plus
+    k_b - 1 others drawn without replacement, kept in ascending order. The
+    inactive suffix blocks stay in the pool (filled with NaN) but are not
+    listed."""
+    B, P, prefix_pages = 32, 64, 128
+    s = rng.integers(128, 1025, size=B)
+    nblk = [(int(x) + P - 1) // P for x in s]
+    pool = prefix_pages + sum(nblk)
+    perm = rng.permutation(pool).astype(np.int32)
+    prefix = list(perm[:prefix_pages])
+    lists, lens, off = [], [], prefix_pages
+    listed = set(prefix)
+    for b in range(B):
+        n = nblk[b]
+        k = max(1, int(math.floor(n / 4.0 + 0.5)))
+        others = rng.choice(n - 1, size=k - 1, replace=False) if k > 1 else np.zeros(0, np.int64)
+        keep = sorted(int(x) for x in others) + [n - 1]
+        phys = [int(perm[off + j]) for j in keep]
+        off += n
+        listed.update(phys)
+        ell = int(s[b]) - P * (n - 1)
+        lists.append(prefix + phys)
+        lens.append(P * (len(prefix) + len(phys) - 1) + ell)
+    ip, ix, lp = _pack(lists, lens, P)
+    unused = np.array(sorted(set(range(pool)) - listed), dtype=np.int32)
+    return Workload(CONFIG_NAMES[5], 5, B, 32, 8, 128, P, "bf16", pool, ip, ix, lp, unused,
+                    seed, shared_pages=prefix_pages)
+
+
+def random_workload(seed: int, batch: int, max_len: int, num_qo_heads: int,
+                    num_kv_heads: int, head_dim: int, page_size: int, dtype: str,
+                    empty_every: int = 0, spare_pages: int = 3,
+                    lens: Optional[List[int]] = None) -> Workload:
+    """Small ragged case for tests: lengths U{1..max_len} (or given), every
+    ``empty_every``-th request empty, a few spare pool pages left unused."""
+    rng = np.random.default_rng([seed, 7])
+    if lens is None:
+        lens = [int(x) for x in rng.integers(1, max_len + 1, size=batch)]
+        if empty_every:
+            for b in range(0, batch, empty_every):
+                lens[b] = 0
+    npg = sum((L + page_size - 1) // page_size for L in lens)
+    pool = npg + spare_pages
+    ip, ix, lp, un = paged_structure(lens, page_size, pool, rng)
+    return Workload(f"random_{seed}", 0, batch, num_qo_heads, num_kv_heads, head_dim,
+                    page_size, dtype, pool, ip, ix, lp, un, 10_000 + seed)

@@ -1,0 +1,217 @@
+"""Float64 CPU oracle for batched decode attention over a paged / BSR KV cache.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the library calls this module: only the
+tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+import it. It shares no code with the HIP path.
+
+What it computes, and where that comes from:
+
+* FlashInfer paper explainer ("FlashInfer: Block-Sparse KV 캐시로 어텐션 병목을
+  해소하다", visionhong.com), section "where the real bottleneck of attention
+  is": in decode, each new token attends over the whole KV history of its
+  request.
+* Same page, section on the Block-Sparse format: the KV cache is a block-sparse
+  matrix; a block is a run of consecutive tokens and metadata marks which
+  blocks are active; paged, dense and sparse caches are all this format.
+  Inactive blocks are skipped. Reading: a request's KV history is exactly the
+  tokens of the blocks it lists, in listed order; a block not listed does not
+  exist for that request.
+* FlashInfer 0.6.17 release write-up (llm-wiki.hwlabs.dev), section 5 on JIT
+  warm-up: the attention call is parameterised by num_heads, num_kv_heads (GQA)
+  and head_dim, and sm_scale=None means the default scale. Reading: the default
+  is 1/sqrt(head_dim); consecutive query heads share a KV head (query head h
+  reads KV head floor(h / G), G = num_heads / num_kv_heads).
+* Same explainer, benchmark section: the load-balanced scheduler cuts long
+  sequences into smaller work units. Cutting one softmax in pieces needs each
+  piece's (output, log-sum-exp) state and a merge; the merge below is the
+  closed form of softmax over a disjoint union of token sets.
+
+Everything is float64. The exact result of the method is plain softmax
+attention over the listed tokens, so the oracle is that definition, written
+out with a library matmul as its only primitive.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+NEG_INF = -math.inf
+
+
+def kv_head_of(h: int, group_size: int) -> int:
+    """Query head h reads KV head floor(h / G): consecutive query heads form
+    one GQA group."""
+    return h // group_size
+
+
+def request_tokens(kv_indptr, kv_indices, last_page_len, page_size, b) -> List[Tuple[int, int]]:
+    """(physical page, slot) of every token of request b, in logical order.
+
+    The request lists pages kv_indices[kv_indptr[b] : kv_indptr[b+1]]; every
+    listed page is full except the last, which holds last_page_len[b] tokens.
+    """
+    start, end = int(kv_indptr[b]), int(kv_indptr[b + 1])
+    toks = []
+    for j in range(start, end):
+        n = page_size if j < end - 1 else int(last_page_len[b])
+        page = int(kv_indices[j])
+        for slot in range(n):
+            toks.append((page, slot))
+    return toks
+
+
+def attend(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float):
+    """Softmax attention of query rows over one token set.
+
+    q_rows [G, d], K [T, d], V [T, d] (float64). Returns (O [G, d], LSE [G])
+    where s_t = sm_scale * q . k_t, O = sum_t softmax(s)_t v_t and
+    LSE = ln sum_t exp(s_t) (natural log of the scaled scores).
+    An empty token set gives O = 0 and LSE = -inf.
+    """
+    G, d = q_rows.shape
+    if K.shape[0] == 0:
+        return np.zeros((G, d)), np.full(G, NEG_INF)
+    s = sm_scale * (q_rows @ K.T)              # [G, T]
+    m = s.max(axis=1, keepdims=True)
+    w = np.exp(s - m)
+    den = w.sum(axis=1)
+    o = (w @ V) / den[:, None]
+    lse = m[:, 0] + np.log(den)
+    return o, lse
+
+
+def gather_kv(k_pool, v_pool, tokens, kv_head):
+    """Dense [T, d] K and V of one request for one KV head, in token order."""
+    if not tokens:
+        d = k_pool.shape[-1]
+        return np.zeros((0, d)), np.zeros((0, d))
+    pages = np.array([p for p, _ in tokens])
+    slots = np.array([s for _, s in tokens])
+    K = np.asarray(k_pool[pages, kv_head, slots, :], dtype=np.float64)
+    V = np.asarray(v_pool[pages, kv_head, slots, :], dtype=np.float64)
+    return K, V
+
+
+def decode_attention(q, k_pool, v_pool, kv_indptr, kv_indices, last_page_len, sm_scale=None):
+    """Batched GQA decode attention over a paged / BSR KV cache.
+
+    q [B, H_q, d]; k_pool, v_pool [num_pages, H_kv, P, d]; page table in BSR
+    form (kv_indptr [B+1], kv_indices, last_page_len [B]). Returns float64
+    O [B, H_q, d] and LSE [B, H_q]. sm_scale None means 1/sqrt(d).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv, P = k_pool.shape[1], k_pool.shape[2]
+    assert Hq % Hkv == 0
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    O = np.zeros((B, Hq, d))
+    LSE = np.full((B, Hq), NEG_INF)
+    for b in range(B):
+        toks = request_tokens(kv_indptr, kv_indices, last_page_len, P, b)
+        for kvh in range(Hkv):
+            heads = [h for h in range(Hq) if kv_head_of(h, G) == kvh]
+            K, V = gather_kv(k_pool, v_pool, toks, kvh)
+            o, lse = attend(q[b, heads, :], K, V, sm_scale)
+            O[b, heads, :] = o
+            LSE[b, heads] = lse
+    return O, LSE
+
+
+def decode_attention_rows(q, k_pool, v_pool, kv_indptr, kv_indices, last_page_len,
+                          rows: Sequence[Tuple[int, int]], sm_scale=None):
+    """The same definition evaluated only for the listed (b, h) rows; used to
+    check single outputs of large batches. Returns (O [n, d], LSE [n])."""
+    q = np.asarray(q, dtype=np.float64) if not hasattr(q, "numpy") else q
+    d = k_pool.shape[-1]
+    Hq = q.shape[1]
+    Hkv, P = k_pool.shape[1], k_pool.shape[2]
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    O = np.zeros((len(rows), d))
+    LSE = np.zeros(len(rows))
+    for i, (b, h) in enumerate(rows):
+        toks = request_tokens(kv_indptr, kv_indices, last_page_len, P, b)
+        K, V = gather_kv(k_pool, v_pool, toks, kv_head_of(h, G))
+        o, lse = attend(np.asarray(q[b, h:h + 1, :], dtype=np.float64), K, V, sm_scale)
+        O[i], LSE[i] = o[0], lse[0]
+    return O, LSE
+
+
+# ------------------------------------------------------------------ merging
+def merge_states(v_a, s_a, v_b, s_b):
+    """Merge two attention states over disjoint token sets A and B.
+
+    With e^{s} the softmax denominator of each set, the union has
+    s = ln(e^{s_a} + e^{s_b}) and v = (e^{s_a} v_a + e^{s_b} v_b) / e^{s}.
+    Evaluated relative to M = max(s_a, s_b). A state with s = -inf (empty set)
+    has weight zero; two empty states give v = 0, s = -inf.
+    v_* [..., d], s_* [...].
+    """
+    v_a = np.asarray(v_a, dtype=np.float64)
+    v_b = np.asarray(v_b, dtype=np.float64)
+    s_a = np.asarray(s_a, dtype=np.float64)
+    s_b = np.asarray(s_b, dtype=np.float64)
+    M = np.maximum(s_a, s_b)
+    both_empty = np.isneginf(M)
+    Ms = np.where(both_empty, 0.0, M)
+    w_a = np.where(np.isneginf(s_a), 0.0, np.exp(np.where(np.isneginf(s_a), 0.0, s_a - Ms)))
+    w_b = np.where(np.isneginf(s_b), 0.0, np.exp(np.where(np.isneginf(s_b), 0.0, s_b - Ms)))
+    den = w_a + w_b
+    safe = np.where(both_empty, 1.0, den)
+    v = (w_a[..., None] * v_a + w_b[..., None] * v_b) / safe[..., None]
+    v = np.where(both_empty[..., None], 0.0, v)
+    s = np.where(both_empty, NEG_INF, Ms + np.log(safe))
+    return v, s
+
+
+def merge_many(vs: Sequence[np.ndarray], ss: Sequence[np.ndarray]):
+    """Merge any number of states (folds merge_states left to right)."""
+    if len(vs) == 0:
+        raise ValueError("merge_many needs at least one state")
+    v, s = np.asarray(vs[0], dtype=np.float64), np.asarray(ss[0], dtype=np.float64)
+    for v2, s2 in zip(vs[1:], ss[1:]):
+        v, s = merge_states(v, s, v2, s2)
+    return v, s
+
+
+# ------------------------------------------------------- bfloat16 rounding
+def _bf16_step(v, up: bool):
+    """Adjacent bfloat16 value above (up) or below a bfloat16 value v."""
+    bits = np.asarray(v, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.int64)
+    neg = (bits >> 31) & 1
+    mag = bits & 0x7FFFFFFF
+    zero = mag == 0
+    # away from zero grows the magnitude: upward for v > 0, downward for v < 0
+    away = (neg == 0) == up
+    new = np.where(away, bits + 0x10000, bits - 0x10000)
+    new = np.where(zero, 0x10000 if up else (0x80000000 | 0x10000), new)
+    return new.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def bf16_neighbors(x):
+    """The two bfloat16 values that bracket each finite float64 x
+    (lo <= x <= hi); lo == hi exactly when x is a bfloat16 value."""
+    x = np.asarray(x, dtype=np.float64)
+    # float32 rounding is monotone and every bfloat16 value is a float32 value,
+    # so x32 stays inside x's bfloat16 bracket (possibly on its upper end).
+    x32 = x.astype(np.float32)
+    t = (x32.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+    lo = np.where(t <= x, t, _bf16_step(t, up=False))
+    hi = np.where(lo == x, lo, _bf16_step(lo, up=True))
+    return lo, hi
+
+
+def round_bf16_rne(x):
+    """Round float64 to the nearest bfloat16, ties to even mantissa, in one
+    step from float64 (no intermediate float32 rounding)."""
+    x = np.asarray(x, dtype=np.float64)
+    lo, hi = bf16_neighbors(x)
+    dlo, dhi = x - lo, hi - x  # exact: both are within one bf16 ulp of x
+    lo_even = ((lo.astype(np.float32).view(np.uint32) >> 16) & 1) == 0
+    pick_lo = (dlo < dhi) | ((dlo == dhi) & lo_even)
+    return np.where(pick_lo, lo, hi)

@@ -1,0 +1,241 @@
+"""Checks that pin the float64 oracle to things other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+an independent source: the pure-Python brute force, torch's CPU float64
+scaled_dot_product_attention (a library definition of GQA attention), closed
+forms of softmax attention, invariants of the definition, and the algebra of
+merging softmax states. They read the oracle through the module object they
+are given, so ``test_oracle_mutations`` can plant a mistake in the oracle and
+show that some pin catches it.
+"""
+import math
+
+import numpy as np
+import torch
+
+from block_sparse_kv_bsr_amd.workloads import random_workload
+from tests.bruteforce import bruteforce_decode
+
+
+def f64_inputs(w):
+    q, k, v = w.make_values("cpu")
+    return q.double().numpy(), k.double().numpy(), v.double().numpy()
+
+
+def _oracle(mod, w, q, k, v, sm_scale=None, indptr=None, indices=None, last=None):
+    return mod.decode_attention(q, k, v,
+                                w.kv_indptr if indptr is None else indptr,
+                                w.kv_indices if indices is None else indices,
+                                w.last_page_len if last is None else last,
+                                w.sm_scale if sm_scale is None else sm_scale)
+
+
+TINY_CASES = [
+    # seed, batch, max_len, Hq, Hkv, d, P, empty_every
+    (1, 3, 40, 4, 1, 8, 16, 0),
+    (2, 3, 37, 4, 2, 4, 4, 0),
+    (3, 2, 25, 2, 2, 8, 1, 0),
+    (4, 3, 40, 4, 4, 4, 16, 2),
+    (5, 2, 33, 8, 2, 8, 4, 0),
+]
+
+
+def pin_bruteforce(mod, cases=TINY_CASES, tol=1e-12):
+    for (seed, B, L, Hq, Hkv, d, P, ee) in cases:
+        w = random_workload(seed, B, L, Hq, Hkv, d, P, "f32", empty_every=ee)
+        q, k, v = f64_inputs(w)
+        O, LSE = _oracle(mod, w, q, k, v)
+        Ob, LSEb = bruteforce_decode(q, k, v, w.kv_indptr, w.kv_indices, w.last_page_len, w.sm_scale)
+        Ob, LSEb = np.array(Ob), np.array(LSEb)
+        assert np.array_equal(np.isneginf(LSE), np.isneginf(LSEb)), (seed, "empty-set pattern")
+        fin = ~np.isneginf(LSEb)
+        assert np.max(np.abs(O - Ob)) <= tol, (seed, np.max(np.abs(O - Ob)))
+        assert np.max(np.abs(LSE[fin] - LSEb[fin]), initial=0.0) <= tol, seed
+
+
+def _dense(w, k, v, b):
+    """Dense [H_kv, T, d] K and V of request b, built straight from the page
+    table (independent of the oracle's helpers)."""
+    P = w.page_size
+    rows_k, rows_v = [], []
+    pages = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+    for j, p in enumerate(pages):
+        n = P if j + 1 < len(pages) else int(w.last_page_len[b])
+        rows_k.append(k[p, :, :n, :])
+        rows_v.append(v[p, :, :n, :])
+    return np.concatenate(rows_k, axis=1), np.concatenate(rows_v, axis=1)
+
+
+def pin_sdpa(mod, seeds=(11, 12, 13), default_scale=True):
+    """torch SDPA in float64 with enable_gqa=True: query head h reads KV head
+    h // (H_q / H_kv) by torch's own definition. LSE from torch.logsumexp."""
+    F = torch.nn.functional
+    for seed in seeds:
+        w = random_workload(seed, 3, 90, 8, 2, 16, 16, "f32")
+        q, k, v = f64_inputs(w)
+        sm = None if default_scale else w.sm_scale
+        O, LSE = mod.decode_attention(q, k, v, w.kv_indptr, w.kv_indices, w.last_page_len, sm)
+        for b in range(w.batch):
+            K, V = _dense(w, k, v, b)
+            qt = torch.from_numpy(q[b][:, None, :])              # [Hq, 1, d]
+            Kt, Vt = torch.from_numpy(K), torch.from_numpy(V)    # [Hkv, T, d]
+            ref = F.scaled_dot_product_attention(qt[None], Kt[None], Vt[None], enable_gqa=True)[0]
+            assert torch.allclose(torch.from_numpy(O[b]), ref[:, 0, :], atol=1e-12, rtol=0), seed
+            G = w.num_qo_heads // w.num_kv_heads
+            Kr = Kt.repeat_interleave(G, dim=0)
+            s = (qt @ Kr.transpose(1, 2))[:, 0, :] / math.sqrt(w.head_dim)
+            lse = torch.logsumexp(s, dim=-1)
+            assert torch.allclose(torch.from_numpy(LSE[b]), lse, atol=1e-12, rtol=0), seed
+
+
+def pin_closed_forms(mod):
+    rng = np.random.default_rng(5)
+    d, P = 8, 4
+    # constant V: every output row equals that V row
+    w = random_workload(21, 3, 30, 4, 2, d, P, "f32")
+    q, k, v = f64_inputs(w)
+    vc = np.empty_like(v)
+    const = rng.standard_normal((w.num_kv_heads, d))
+    vc[:] = const[None, :, None, :]
+    O, _ = _oracle(mod, w, q, k, vc)
+    for b in range(w.batch):
+        for h in range(w.num_qo_heads):
+            assert np.allclose(O[b, h], const[h // 2], atol=1e-13, rtol=0)
+    # one-token context: O = v, LSE = sm_scale * q . k
+    w1 = random_workload(22, 4, 1, 4, 2, d, P, "f32", lens=[1, 1, 1, 1])
+    q, k, v = f64_inputs(w1)
+    O, LSE = _oracle(mod, w1, q, k, v)
+    for b in range(4):
+        p = int(w1.kv_indices[w1.kv_indptr[b]])
+        for h in range(4):
+            assert np.allclose(O[b, h], v[p, h // 2, 0], atol=1e-13, rtol=0)
+            assert abs(LSE[b, h] - (q[b, h] @ k[p, h // 2, 0]) / math.sqrt(d)) <= 1e-13
+    # K = 0: uniform weights, O = mean of V rows, LSE = ln L
+    w0 = random_workload(23, 3, 29, 4, 1, d, P, "f32")
+    q, k, v = f64_inputs(w0)
+    O, LSE = _oracle(mod, w0, q, np.zeros_like(k), v)
+    for b in range(3):
+        K, V = _dense(w0, np.zeros_like(k), v, b)
+        L = V.shape[1]
+        for h in range(4):
+            assert np.allclose(O[b, h], V[0].mean(axis=0), atol=1e-13, rtol=0)
+            assert abs(LSE[b, h] - math.log(L)) <= 1e-13
+    # every full page listed twice: same O, LSE + ln 2
+    w2 = random_workload(24, 3, 32, 4, 2, d, P, "f32", lens=[8, 16, 12])
+    q, k, v = f64_inputs(w2)
+    O, LSE = _oracle(mod, w2, q, k, v)
+    ip2, ix2 = [0], []
+    for b in range(3):
+        pages = list(w2.kv_indices[w2.kv_indptr[b]:w2.kv_indptr[b + 1]])
+        ix2 += pages + pages
+        ip2.append(len(ix2))
+    O2, LSE2 = _oracle(mod, w2, q, k, v, indptr=np.array(ip2), indices=np.array(ix2))
+    assert np.allclose(O2, O, atol=1e-13, rtol=0)
+    assert np.allclose(LSE2, LSE + math.log(2.0), atol=1e-13, rtol=0)
+
+
+def pin_invariants(mod):
+    d, P = 8, 4
+    w = random_workload(31, 4, 45, 4, 2, d, P, "f32", lens=[45, 30, 21, 9])
+    q, k, v = f64_inputs(w)
+    O, LSE = _oracle(mod, w, q, k, v)
+    # permuting the full pages (the partial page stays last) changes nothing
+    rng = np.random.default_rng(3)
+    ix = w.kv_indices.copy()
+    for b in range(w.batch):
+        s, t = w.kv_indptr[b], w.kv_indptr[b + 1]
+        if t - s > 2:
+            ix[s:t - 1] = ix[s:t - 1][rng.permutation(t - 1 - s)]
+    Op, LSEp = _oracle(mod, w, q, k, v, indices=ix)
+    assert np.allclose(Op, O, atol=1e-13, rtol=0) and np.allclose(LSEp, LSE, atol=1e-13, rtol=0)
+    # dropping a listed block = dense attention with that block's scores at -inf
+    b, drop = 1, 0
+    s, t = w.kv_indptr[b], w.kv_indptr[b + 1]
+    assert t - s >= 2
+    ip2 = w.kv_indptr.copy()
+    ip2[b + 1:] -= 1
+    ix2 = np.delete(w.kv_indices, s + drop)
+    O2, LSE2 = _oracle(mod, w, q, k, v, indptr=ip2, indices=ix2)
+    K, V = _dense(w, k, v, b)
+    G = w.num_qo_heads // w.num_kv_heads
+    for h in range(w.num_qo_heads):
+        sc = (K[h // G] @ q[b, h]) * w.sm_scale
+        sc[drop * P:(drop + 1) * P] = -np.inf
+        m = sc.max()
+        e = np.exp(sc - m)
+        assert np.allclose(O2[b, h], e @ V[h // G] / e.sum(), atol=1e-13, rtol=0)
+        assert abs(LSE2[b, h] - (m + math.log(e.sum()))) <= 1e-13
+    # identical query rows inside a GQA group give identical outputs
+    qg = q.copy()
+    qg[:, 1, :] = qg[:, 0, :]
+    Og, LSEg = _oracle(mod, w, qg, k, v)
+    assert np.array_equal(Og[:, 1], Og[:, 0]) and np.array_equal(LSEg[:, 1], LSEg[:, 0])
+
+
+def pin_merge(mod):
+    """Splitting a request's token list in two, attending over each half and
+    merging the two states gives the whole-list result."""
+    d, P = 8, 4
+    w = random_workload(41, 3, 60, 4, 2, d, P, "f32", lens=[60, 17, 33])
+    q, k, v = f64_inputs(w)
+    O, LSE = _oracle(mod, w, q, k, v)
+    for b in range(3):
+        s, t = int(w.kv_indptr[b]), int(w.kv_indptr[b + 1])
+        cut = (t - s) // 2
+        # first half: full pages only; second half keeps the partial last page
+        ipa = np.array([0, cut])
+        ipb = np.array([0, t - s - cut])
+        ixa, ixb = w.kv_indices[s:s + cut], w.kv_indices[s + cut:t]
+        lasta, lastb = np.array([P]), np.array([w.last_page_len[b]])
+        qa = q[b:b + 1]
+        Oa, La = mod.decode_attention(qa, k, v, ipa, ixa, lasta, w.sm_scale)
+        Ob, Lb = mod.decode_attention(qa, k, v, ipb, ixb, lastb, w.sm_scale)
+        Om, Lm = mod.merge_states(Oa, La, Ob, Lb)
+        assert np.allclose(Om[0], O[b], atol=1e-13, rtol=0), b
+        assert np.allclose(Lm[0], LSE[b], atol=1e-13, rtol=0), b
+        # order of the two states does not matter
+        Om2, Lm2 = mod.merge_states(Ob, Lb, Oa, La)
+        assert np.allclose(Om2, Om, atol=1e-14, rtol=0) and np.allclose(Lm2, Lm, atol=1e-14, rtol=0)
+    # an empty state is the identity; two empty states give (0, -inf)
+    va = np.random.default_rng(1).standard_normal((5, d))
+    sa = np.random.default_rng(2).standard_normal(5)
+    vz, sz = np.full((5, d), 7.0), np.full(5, -np.inf)
+    vm, sm = mod.merge_states(va, sa, vz, sz)
+    assert np.array_equal(vm, va) and np.array_equal(sm, sa)
+    vm, sm = mod.merge_states(vz, sz, vz, sz)
+    assert np.all(vm == 0) and np.all(np.isneginf(sm))
+
+
+def pin_bf16(mod):
+    """Round-to-nearest-even into bfloat16 checked against exact rational
+    arithmetic over the candidate bfloat16 values."""
+    from fractions import Fraction
+    rng = np.random.default_rng(9)
+    xs = np.concatenate([rng.standard_normal(400) * 3, rng.standard_normal(100) * 1e-3,
+                         [1 + 2 ** -8, 1 + 2 ** -8 + 2 ** -40, 1 + 2 ** -8 - 2 ** -40,
+                          -(1 + 2 ** -8 + 2 ** -40), 0.619140640, 0.0, 2.0 ** -7 * 3]])
+    got = mod.round_bf16_rne(xs)
+    lo, hi = mod.bf16_neighbors(xs)
+    for x, g, a, c in zip(xs, got, lo, hi):
+        fx = Fraction(float(x))
+        if x == 0:
+            assert g == 0
+            continue
+        e = math.frexp(abs(x))[1]
+        step = Fraction(2) ** (e - 1 - 7)
+        below = (fx // step) * step
+        above = below if below == fx else below + step
+        assert Fraction(float(a)) == below and Fraction(float(c)) == above, x
+        if below == above:
+            want = below
+        else:
+            db, da = fx - below, above - fx
+            if db != da:
+                want = below if db < da else above
+            else:
+                mant = int(abs(below) / step)
+                want = below if mant % 2 == 0 else above
+        assert Fraction(float(g)) == want, (x, g, want)
+
+
+ALL_PINS = [pin_bruteforce, pin_sdpa, pin_closed_forms, pin_invariants, pin_merge]

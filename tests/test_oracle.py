@@ -1,0 +1,90 @@
+"""The float64 oracle against its pins (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle.attention as oa
+from tests import oracle_pins as pins
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS + [pins.pin_bf16], ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(oa)
+
+
+def test_sdpa_pin_with_default_scale():
+    # sm_scale=None must mean 1/sqrt(head_dim)
+    pins.pin_sdpa(oa, seeds=(14,), default_scale=True)
+
+
+# ---- planted mistakes: each must be caught by at least one pin ----------
+def _wrong_gqa(h, G):
+    return h % 2  # interleaved heads instead of consecutive groups
+
+
+def _drop_last_page_len(kv_indptr, kv_indices, last_page_len, page_size, b):
+    start, end = int(kv_indptr[b]), int(kv_indptr[b + 1])
+    return [(int(kv_indices[j]), s) for j in range(start, end) for s in range(page_size)]
+
+
+def _attend_no_scale(q_rows, K, V, sm_scale):
+    return _orig_attend(q_rows, K, V, 1.0)
+
+
+def _attend_lse_no_max(q_rows, K, V, sm_scale):
+    o, lse = _orig_attend(q_rows, K, V, sm_scale)
+    s = sm_scale * (q_rows @ K.T) if K.shape[0] else None
+    return o, (lse - s.max(axis=1)) if s is not None else lse
+
+
+def _attend_k_for_v(q_rows, K, V, sm_scale):
+    return _orig_attend(q_rows, K, K, sm_scale)
+
+
+def _attend_log2(q_rows, K, V, sm_scale):
+    o, lse = _orig_attend(q_rows, K, V, sm_scale)
+    return o, lse / np.log(2.0)
+
+
+def _merge_swapped(v_a, s_a, v_b, s_b):
+    return _orig_merge(v_a, s_b, v_b, s_a)
+
+
+def _merge_no_max(v_a, s_a, v_b, s_b):
+    v, s = _orig_merge(v_a, s_a, v_b, s_b)
+    return v, s - np.maximum(s_a, s_b)
+
+
+def _decode_scale_1_over_d(q, k, v, ip, ix, lp, sm_scale=None):
+    if sm_scale is None:
+        sm_scale = 1.0 / q.shape[-1]
+    return _orig_decode(q, k, v, ip, ix, lp, sm_scale)
+
+
+_orig_attend = oa.attend
+_orig_merge = oa.merge_states
+_orig_decode = oa.decode_attention
+
+MUTATIONS = {
+    "gqa_interleaved": ("kv_head_of", _wrong_gqa),
+    "ignore_last_page_len": ("request_tokens", _drop_last_page_len),
+    "missing_sm_scale": ("attend", _attend_no_scale),
+    "lse_without_max": ("attend", _attend_lse_no_max),
+    "k_used_as_v": ("attend", _attend_k_for_v),
+    "lse_base_2": ("attend", _attend_log2),
+    "merge_weights_swapped": ("merge_states", _merge_swapped),
+    "merge_lse_without_max": ("merge_states", _merge_no_max),
+    "default_scale_1_over_d": ("decode_attention", _decode_scale_1_over_d),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_oracle_mutations_are_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(oa, attr, fn)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(oa)
+        except (AssertionError, ValueError, IndexError, TypeError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake {name} passed every pin"
