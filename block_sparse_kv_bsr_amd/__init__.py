@@ -1,0 +1,9 @@
+"""Paged / block-sparse-row (BSR) GQA decode attention for AMD MI355X.
+
+The compute path is the C-ABI library ``libfi_bsr.so`` (HIP kernels for
+gfx950, declared in include/fi_bsr.h); this package is its ctypes binding
+plus seeded input generators. ``plan``, ``decode`` and ``merge_states`` load
+the library on first use and raise if it is missing.
+"""
+from .binding import (FiError, Plan, decode, lib, merge_states, plan,  # noqa: F401
+                      FI_DTYPE_BF16, FI_DTYPE_F32)

@@ -1,0 +1,268 @@
+"""Thin ctypes binding over ``libfi_bsr.so`` (the C ABI in include/fi_bsr.h).
+
+Only argument marshalling lives here: torch supplies device memory and the
+current stream; every step of decode attention runs in the library's HIP
+kernels. There is no fallback: if the library is missing or a tensor is not on
+a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfi_bsr.so")
+
+FI_OK = 0
+FI_DTYPE_F32 = 0
+FI_DTYPE_BF16 = 1
+ITEM_STRIDE = 8
+MERGE_STRIDE = 4
+
+STATUS_NAMES = {0: "FI_OK", -1: "FI_ERR_INVALID_ARG", -2: "FI_ERR_UNSUPPORTED",
+                -3: "FI_ERR_WORKSPACE", -4: "FI_ERR_HIP", -5: "FI_ERR_NOMEM", -6: "FI_ERR_STATE"}
+
+# Every symbol include/fi_bsr.h declares.
+EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_merge_list",
+            "fi_plan_upload", "fi_decode_run", "fi_merge_states", "fi_plan_destroy",
+            "fi_last_error"]
+
+
+class FiError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class PlanOpts(ctypes.Structure):
+    _fields_ = [("num_cus", ctypes.c_int32), ("items_per_cu", ctypes.c_int32),
+                ("min_chunk_tokens", ctypes.c_int32), ("max_chunk_tokens", ctypes.c_int32),
+                ("fixed_chunk_tokens", ctypes.c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("num_items", ctypes.c_int64), ("num_partial_slots", ctypes.c_int64),
+                ("num_merge_tasks", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("total_kv_tokens", ctypes.c_int64), ("chunk_pages", ctypes.c_int32),
+                ("max_chunks_per_request", ctypes.c_int32),
+                ("min_chunks_split_request", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("num_qo_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                           "`python -m block_sparse_kv_bsr_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    L.fi_plan_create.argtypes = [pi32, pi32, pi32, i32, i32, i32, i32, i32, i64, i32,
+                                 ctypes.POINTER(PlanOpts), ctypes.POINTER(vp)]
+    L.fi_plan_create.restype = i32
+    L.fi_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+    L.fi_plan_get_info.restype = i32
+    L.fi_plan_work_list.argtypes = [vp, ctypes.POINTER(pi32), ctypes.POINTER(i64)]
+    L.fi_plan_work_list.restype = i32
+    L.fi_plan_merge_list.argtypes = [vp, ctypes.POINTER(pi32), ctypes.POINTER(i64)]
+    L.fi_plan_merge_list.restype = i32
+    L.fi_plan_upload.argtypes = [vp, vp, sz, vp]
+    L.fi_plan_upload.restype = i32
+    L.fi_decode_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
+    L.fi_decode_run.restype = i32
+    L.fi_merge_states.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, vp]
+    L.fi_merge_states.restype = i32
+    L.fi_plan_destroy.argtypes = [vp]
+    L.fi_plan_destroy.restype = None
+    L.fi_last_error.argtypes = []
+    L.fi_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != FI_OK:
+        raise FiError(status, lib().fi_last_error().decode())
+
+
+def _i32(a) -> np.ndarray:
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr32(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _dtype_code(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    name = str(dtype)
+    if name in ("bf16", "torch.bfloat16", "bfloat16"):
+        return FI_DTYPE_BF16
+    if name in ("f32", "torch.float32", "float32"):
+        return FI_DTYPE_F32
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+class Plan:
+    """A split-KV work plan (host memory, owned by the library)."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+        info = PlanInfo()
+        _check(lib().fi_plan_get_info(self._h, ctypes.byref(info)))
+        self.info = info.as_dict()
+        self._workspace = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def work_list(self) -> np.ndarray:
+        p = ctypes.POINTER(ctypes.c_int32)()
+        n = ctypes.c_int64()
+        _check(lib().fi_plan_work_list(self._h, ctypes.byref(p), ctypes.byref(n)))
+        if n.value == 0:
+            return np.zeros((0, ITEM_STRIDE), dtype=np.int32)
+        return np.ctypeslib.as_array(p, shape=(n.value * ITEM_STRIDE,)).reshape(-1, ITEM_STRIDE).copy()
+
+    def merge_list(self) -> np.ndarray:
+        p = ctypes.POINTER(ctypes.c_int32)()
+        n = ctypes.c_int64()
+        _check(lib().fi_plan_merge_list(self._h, ctypes.byref(p), ctypes.byref(n)))
+        if n.value == 0:
+            return np.zeros((0, MERGE_STRIDE), dtype=np.int32)
+        return np.ctypeslib.as_array(p, shape=(n.value * MERGE_STRIDE,)).reshape(-1, MERGE_STRIDE).copy()
+
+    def upload(self, workspace, stream=None):
+        """Copy the plan into ``workspace`` (a torch uint8 CUDA tensor)."""
+        _require_gpu(workspace, "workspace")
+        _check(lib().fi_plan_upload(self._h, ctypes.c_void_p(workspace.data_ptr()),
+                                    workspace.numel() * workspace.element_size(),
+                                    ctypes.c_void_p(_stream(stream))))
+        self._workspace = workspace
+
+    def ensure_uploaded(self, device, stream=None):
+        """Allocate a workspace on ``device`` and upload once."""
+        import torch
+        if self._workspace is None or self._workspace.device != torch.device(device):
+            ws = torch.empty(max(256, self.info["workspace_bytes"]), dtype=torch.uint8, device=device)
+            self.upload(ws, stream)
+        return self._workspace
+
+    @property
+    def workspace(self):
+        return self._workspace
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.fi_plan_destroy(h)
+            self._h = None
+
+
+def plan(kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int, num_kv_heads: int,
+         head_dim: int, page_size: int, num_pool_pages: int, dtype="bf16",
+         num_cus: int = 0, items_per_cu: int = 0, min_chunk_tokens: int = 0,
+         max_chunk_tokens: int = 0, fixed_chunk_tokens: int = 0) -> Plan:
+    """fi_plan_create over host page-table arrays (numpy or CPU tensors)."""
+    ip, ix, lp = _i32(kv_indptr), _i32(kv_indices), _i32(kv_last_page_len)
+    batch = len(ip) - 1
+    if len(lp) != batch:
+        raise ValueError("kv_last_page_len must have one entry per request")
+    opts = PlanOpts(num_cus, items_per_cu, min_chunk_tokens, max_chunk_tokens, fixed_chunk_tokens)
+    h = ctypes.c_void_p()
+    ix_ptr = _ptr32(ix) if ix.size else ctypes.POINTER(ctypes.c_int32)()
+    _check(lib().fi_plan_create(_ptr32(ip), ix_ptr, _ptr32(lp), batch, num_qo_heads,
+                                num_kv_heads, head_dim, page_size, int(num_pool_pages),
+                                _dtype_code(dtype), ctypes.byref(opts), ctypes.byref(h)))
+    return Plan(h.value)
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _require_gpu(t, name):
+    if not getattr(t, "is_cuda", False):
+        raise RuntimeError(f"{name} must be a GPU tensor; this library has no CPU path")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def decode(q, k_pages, v_pages, plan_: Plan, out=None, lse=None, sm_scale: Optional[float] = None,
+           workspace=None, stream=None):
+    """fi_decode_run: returns (out [B, H_q, d] in q's dtype, lse [B, H_q] float32)."""
+    import torch
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _require_gpu(t, n)
+    info = plan_.info
+    B, Hq, d = info["batch"], info["num_qo_heads"], info["head_dim"]
+    want = torch.float32 if info["dtype"] == FI_DTYPE_F32 else torch.bfloat16
+    if q.dtype != want or k_pages.dtype != want or v_pages.dtype != want:
+        raise ValueError(f"q, k_pages and v_pages must be {want}")
+    if tuple(q.shape) != (B, Hq, d):
+        raise ValueError(f"q must have shape {(B, Hq, d)}, got {tuple(q.shape)}")
+    kshape = (k_pages.shape[0], info["num_kv_heads"], info["page_size"], d)
+    if tuple(k_pages.shape) != kshape or tuple(v_pages.shape) != kshape:
+        raise ValueError(f"k_pages/v_pages must have shape [pool, {kshape[1]}, {kshape[2]}, {d}]")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=want, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _require_gpu(out, "out")
+    _require_gpu(lse, "lse")
+    if workspace is None:
+        workspace = plan_.ensure_uploaded(q.device, stream)
+    _check(lib().fi_decode_run(plan_.handle, ctypes.c_void_p(q.data_ptr()),
+                               ctypes.c_void_p(k_pages.data_ptr()),
+                               ctypes.c_void_p(v_pages.data_ptr()),
+                               ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
+                               float(sm_scale) if sm_scale else 0.0,
+                               ctypes.c_void_p(workspace.data_ptr()),
+                               workspace.numel() * workspace.element_size(),
+                               ctypes.c_void_p(_stream(stream))))
+    return out, lse
+
+
+def merge_states(v_a, s_a, v_b, s_b, v_out=None, s_out=None, stream=None):
+    """fi_merge_states over [rows, head_dim] states with float32 natural-log LSE."""
+    import torch
+    for t, n in ((v_a, "v_a"), (s_a, "s_a"), (v_b, "v_b"), (s_b, "s_b")):
+        _require_gpu(t, n)
+    if v_a.shape != v_b.shape or v_a.dim() != 2:
+        raise ValueError("v_a and v_b must both be [rows, head_dim]")
+    rows, d = v_a.shape
+    if s_a.shape != (rows,) or s_b.shape != (rows,) or s_a.dtype != torch.float32 or s_b.dtype != torch.float32:
+        raise ValueError("s_a and s_b must be float32 [rows]")
+    if v_out is None:
+        v_out = torch.empty_like(v_a)
+    if s_out is None:
+        s_out = torch.empty_like(s_a)
+    _check(lib().fi_merge_states(_dtype_code(v_a.dtype), ctypes.c_void_p(v_a.data_ptr()),
+                                 ctypes.c_void_p(s_a.data_ptr()), ctypes.c_void_p(v_b.data_ptr()),
+                                 ctypes.c_void_p(s_b.data_ptr()), ctypes.c_void_p(v_out.data_ptr()),
+                                 ctypes.c_void_p(s_out.data_ptr()), rows, d,
+                                 ctypes.c_void_p(_stream(stream))))
+    return v_out, s_out

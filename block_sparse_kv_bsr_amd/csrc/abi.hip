@@ -1,0 +1,141 @@
+// C ABI entry points that touch the device: plan upload, decode run, state
+// merge and plan destruction. The host-only planner lives in plan.cpp.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "fi_bsr.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+fi_status fail(fi_status st, const std::string& msg) {
+  fi::set_error(msg);
+  return st;
+}
+
+fi_status hip_fail(hipError_t e, const char* what) {
+  return fail(FI_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+fi_status fi_plan_upload(fi_plan* plan, void* workspace, size_t workspace_bytes,
+                         fi_stream_t stream) {
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  if (!workspace) return fail(FI_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(FI_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if ((int64_t)workspace_bytes < plan->ws.total_bytes)
+    return fail(FI_ERR_WORKSPACE, "workspace smaller than fi_plan_info.workspace_bytes (" +
+                                      std::to_string(plan->ws.total_bytes) + ")");
+  const size_t n = plan->image.size();
+  if (n > 0) {
+    if (!plan->pinned) {
+      void* h = nullptr;
+      hipError_t e = hipHostMalloc(&h, n, hipHostMallocDefault);
+      if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+      std::memcpy(h, plan->image.data(), n);
+      plan->pinned = h;
+    }
+    hipError_t e = hipMemcpyAsync(workspace, plan->pinned, n, hipMemcpyHostToDevice,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  }
+  plan->uploaded_to = workspace;
+  return FI_OK;
+}
+
+fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
+                        const void* v_pages, void* out, float* lse, float sm_scale,
+                        void* workspace, size_t workspace_bytes, fi_stream_t stream) {
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->batch == 0) return FI_OK;
+  if (!q || !out) return fail(FI_ERR_INVALID_ARG, "q or out is NULL");
+  if (plan->num_items() > 0 && (!k_pages || !v_pages))
+    return fail(FI_ERR_INVALID_ARG, "k_pages or v_pages is NULL");
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16))
+    return fail(FI_ERR_INVALID_ARG, "q, out, k_pages and v_pages must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(FI_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  if (!workspace) return fail(FI_ERR_INVALID_ARG, "workspace is NULL");
+  if ((int64_t)workspace_bytes < plan->ws.total_bytes)
+    return fail(FI_ERR_WORKSPACE, "workspace smaller than fi_plan_info.workspace_bytes");
+  if (plan->uploaded_to != workspace)
+    return fail(FI_ERR_STATE, "plan was not uploaded to this workspace (call fi_plan_upload)");
+  if (!(sm_scale > 0.f)) sm_scale = 1.0f / std::sqrt((float)plan->head_dim);
+
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  fi::DecodeArgs d{};
+  d.items = reinterpret_cast<const int32_t*>(ws + plan->ws.items);
+  d.page_ids = reinterpret_cast<const int32_t*>(ws + plan->ws.page_ids);
+  d.q = q;
+  d.k_pages = k_pages;
+  d.v_pages = v_pages;
+  d.out = out;
+  d.lse = lse;
+  d.part_o = reinterpret_cast<float*>(ws + plan->ws.part_o);
+  d.part_lse = reinterpret_cast<float*>(ws + plan->ws.part_lse);
+  d.num_items = plan->num_items();
+  d.num_qo_heads = plan->num_qo_heads;
+  d.num_kv_heads = plan->num_kv_heads;
+  d.head_dim = plan->head_dim;
+  d.page_size = plan->page_size;
+  d.group = plan->group;
+  d.bf16 = plan->dtype == FI_DTYPE_BF16;
+  d.sm_scale = sm_scale;
+  hipError_t e = fi::launch_decode(d, s);
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+
+  fi::MergePartialArgs m{};
+  m.tasks = reinterpret_cast<const int32_t*>(ws + plan->ws.merge);
+  m.part_o = d.part_o;
+  m.part_lse = d.part_lse;
+  m.out = out;
+  m.lse = lse;
+  m.num_tasks = plan->num_merge();
+  m.num_qo_heads = plan->num_qo_heads;
+  m.head_dim = plan->head_dim;
+  m.bf16 = d.bf16;
+  e = fi::launch_merge_partials(m, s);
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return FI_OK;
+}
+
+fi_status fi_merge_states(fi_dtype dtype, const void* v_a, const float* s_a, const void* v_b,
+                          const float* s_b, void* v_out, float* s_out, int64_t num_rows,
+                          int32_t head_dim, fi_stream_t stream) {
+  if (dtype != FI_DTYPE_F32 && dtype != FI_DTYPE_BF16)
+    return fail(FI_ERR_UNSUPPORTED, "dtype must be FI_DTYPE_F32 or FI_DTYPE_BF16");
+  if (head_dim != 64 && head_dim != 128) return fail(FI_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (num_rows < 0) return fail(FI_ERR_INVALID_ARG, "num_rows < 0");
+  if (num_rows == 0) return FI_OK;
+  if (!v_a || !s_a || !v_b || !s_b || !v_out || !s_out)
+    return fail(FI_ERR_INVALID_ARG, "NULL state pointer");
+  if (!aligned(v_a, 16) || !aligned(v_b, 16) || !aligned(v_out, 16))
+    return fail(FI_ERR_INVALID_ARG, "state vectors must be 16-byte aligned");
+  if (!aligned(s_a, 4) || !aligned(s_b, 4) || !aligned(s_out, 4))
+    return fail(FI_ERR_INVALID_ARG, "LSE arrays must be 4-byte aligned");
+  fi::MergeTwoArgs a{v_a, s_a, v_b, s_b, v_out, s_out, num_rows, head_dim, dtype == FI_DTYPE_BF16};
+  hipError_t e = fi::launch_merge_two(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge_states kernel launch");
+  return FI_OK;
+}
+
+void fi_plan_destroy(fi_plan* plan) {
+  if (!plan) return;
+  if (plan->pinned) {
+    // uploads from the staging copy may still be in flight
+    (void)hipDeviceSynchronize();
+    (void)hipHostFree(plan->pinned);
+  }
+  fi::plan_free_host(plan);
+}
+
+}  // extern "C"

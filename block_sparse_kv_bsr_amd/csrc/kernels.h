@@ -1,0 +1,53 @@
+// Launch interface between the C ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace fi {
+
+struct DecodeArgs {
+  const int32_t* items;     // device, [num_items][FI_ITEM_STRIDE]
+  const int32_t* page_ids;  // device, the request page lists
+  const void* q;            // [batch, num_qo_heads, head_dim]
+  const void* k_pages;      // [pool, num_kv_heads, page_size, head_dim]
+  const void* v_pages;
+  void* out;                // [batch, num_qo_heads, head_dim]
+  float* lse;               // [batch, num_qo_heads] natural log, or null
+  float* part_o;            // [slots, num_qo_heads, head_dim]
+  float* part_lse;          // [slots, num_qo_heads], log2 units
+  int64_t num_items;
+  int32_t num_qo_heads, num_kv_heads, head_dim, page_size, group;
+  bool bf16;
+  float sm_scale;
+};
+
+struct MergePartialArgs {
+  const int32_t* tasks;     // device, [num_tasks][FI_MERGE_STRIDE]
+  const float* part_o;
+  const float* part_lse;
+  void* out;
+  float* lse;
+  int64_t num_tasks;
+  int32_t num_qo_heads, head_dim;
+  bool bf16;
+};
+
+struct MergeTwoArgs {
+  const void* v_a;
+  const float* s_a;
+  const void* v_b;
+  const float* s_b;
+  void* v_out;
+  float* s_out;
+  int64_t num_rows;
+  int32_t head_dim;
+  bool bf16;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_merge_partials(const MergePartialArgs& a, hipStream_t stream);
+hipError_t launch_merge_two(const MergeTwoArgs& a, hipStream_t stream);
+
+}  // namespace fi

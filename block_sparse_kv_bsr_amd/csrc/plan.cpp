@@ -1,0 +1,280 @@
+// Load-balanced split-KV planner for paged / BSR decode attention.
+//
+// FlashInfer paper explainer ("FlashInfer: Block-Sparse KV 캐시로 어텐션 병목을
+// 해소하다", visionhong.com), benchmark section: in a skewed batch (lengths of
+// 32 and 4096 side by side) one workgroup per sequence leaves most
+// workgroups idle while the long sequences finish. The scheduler instead cuts
+// sequences into smaller work units, splits the long ones into several, and
+// interleaves them with the short ones so the GPU stays busy.
+//
+// Here a work unit is (request, KV head, chunk of whole pages). One chunk
+// length serves the whole batch: the smallest that keeps the unit count within
+// a budget of (compute units x items per CU); a request of n pages is cut into
+// k = ceil(n / C) chunks of near-equal page counts. Units are ordered longest
+// first -- the longest-processing-time rule -- so that the hardware dispatcher,
+// which starts workgroups in grid order as slots free up, places long chunks
+// first and short requests into the gaps. Requests cut into several chunks
+// write partial (output, log-sum-exp) states that a merge kernel combines.
+//
+// Plain C++17 with no HIP dependency: the planner is tested on CPU-only hosts.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <numeric>
+#include <string>
+
+#include "plan.h"
+
+namespace fi {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+void plan_free_host(fi_plan* p) { delete p; }
+
+namespace {
+
+fi_status fail(fi_status st, const std::string& msg) {
+  set_error(msg);
+  return st;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Number of items a chunk length of `c` pages produces.
+int64_t count_items(const std::vector<int64_t>& npages, int64_t c, int64_t heads) {
+  int64_t n = 0;
+  for (int64_t x : npages) n += ceil_div(x, c);
+  return n * heads;
+}
+
+}  // namespace
+}  // namespace fi
+
+extern "C" {
+
+const char* fi_last_error(void) { return fi::g_last_error.c_str(); }
+
+fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
+                         const int32_t* kv_last_page_len, int32_t batch,
+                         int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t page_size, int64_t num_pool_pages, fi_dtype dtype,
+                         const fi_plan_opts* opts, fi_plan** out_plan) {
+  using fi::fail;
+  try {
+    if (!out_plan) return fail(FI_ERR_INVALID_ARG, "out_plan is NULL");
+    *out_plan = nullptr;
+    if (batch < 0) return fail(FI_ERR_INVALID_ARG, "batch < 0");
+    if (!kv_indptr) return fail(FI_ERR_INVALID_ARG, "kv_indptr is NULL");
+    if (batch > 0 && !kv_last_page_len)
+      return fail(FI_ERR_INVALID_ARG, "kv_last_page_len is NULL");
+    if (num_qo_heads <= 0 || num_kv_heads <= 0)
+      return fail(FI_ERR_INVALID_ARG, "head counts must be positive");
+    if (num_qo_heads % num_kv_heads != 0)
+      return fail(FI_ERR_INVALID_ARG, "num_qo_heads is not a multiple of num_kv_heads");
+    const int32_t group = num_qo_heads / num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8)
+      return fail(FI_ERR_UNSUPPORTED, "GQA group size must be 1, 2, 4 or 8");
+    if (head_dim != 64 && head_dim != 128)
+      return fail(FI_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (dtype != FI_DTYPE_F32 && dtype != FI_DTYPE_BF16)
+      return fail(FI_ERR_UNSUPPORTED, "dtype must be FI_DTYPE_F32 or FI_DTYPE_BF16");
+    if (page_size < 1 || page_size > 4096)
+      return fail(FI_ERR_INVALID_ARG, "page_size must be in [1, 4096]");
+    if (num_pool_pages < 0) return fail(FI_ERR_INVALID_ARG, "num_pool_pages < 0");
+    if (kv_indptr[0] != 0) return fail(FI_ERR_INVALID_ARG, "kv_indptr[0] != 0");
+    for (int32_t b = 0; b < batch; ++b)
+      if (kv_indptr[b + 1] < kv_indptr[b])
+        return fail(FI_ERR_INVALID_ARG, "kv_indptr is not non-decreasing at request " +
+                                            std::to_string(b));
+    const int64_t nnz = batch > 0 ? kv_indptr[batch] : 0;
+    if (nnz > 0 && !kv_indices) return fail(FI_ERR_INVALID_ARG, "kv_indices is NULL");
+    for (int64_t j = 0; j < nnz; ++j)
+      if (kv_indices[j] < 0 || kv_indices[j] >= num_pool_pages)
+        return fail(FI_ERR_INVALID_ARG, "kv_indices[" + std::to_string(j) +
+                                            "] outside [0, num_pool_pages)");
+    std::vector<int64_t> npages(batch), ntok(batch);
+    int64_t total_tokens = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+      npages[b] = kv_indptr[b + 1] - kv_indptr[b];
+      const int32_t ell = kv_last_page_len[b];
+      if (npages[b] > 0) {
+        if (ell < 1 || ell > page_size)
+          return fail(FI_ERR_INVALID_ARG, "kv_last_page_len[" + std::to_string(b) +
+                                              "] outside [1, page_size]");
+        ntok[b] = (npages[b] - 1) * (int64_t)page_size + ell;
+      } else {
+        if (ell < 0 || ell > page_size)
+          return fail(FI_ERR_INVALID_ARG, "kv_last_page_len[" + std::to_string(b) +
+                                              "] outside [0, page_size]");
+        ntok[b] = 0;
+      }
+      if (ntok[b] > INT32_MAX)
+        return fail(FI_ERR_INVALID_ARG, "request longer than 2^31-1 tokens");
+      total_tokens += ntok[b];
+    }
+    fi_plan_opts o{};
+    if (opts) o = *opts;
+    if (o.num_cus < 0 || o.items_per_cu < 0 || o.min_chunk_tokens < 0 ||
+        o.max_chunk_tokens < 0 || o.fixed_chunk_tokens < 0)
+      return fail(FI_ERR_INVALID_ARG, "negative planner option");
+    const int64_t num_cus = o.num_cus ? o.num_cus : 256;
+    const int64_t items_per_cu = o.items_per_cu ? o.items_per_cu : 8;
+    const int64_t min_chunk_tokens = o.min_chunk_tokens ? o.min_chunk_tokens : 256;
+
+    // ---- chunk length (pages)
+    const int64_t max_n = batch > 0 ? *std::max_element(npages.begin(), npages.end()) : 0;
+    int64_t C = std::max<int64_t>(1, max_n);
+    if (o.fixed_chunk_tokens > 0) {
+      C = std::max<int64_t>(1, fi::ceil_div(o.fixed_chunk_tokens, page_size));
+    } else if (max_n > 0) {
+      const int64_t budget = num_cus * items_per_cu;
+      const int64_t cmin = std::max<int64_t>(1, fi::ceil_div(min_chunk_tokens, page_size));
+      if (cmin < max_n && fi::count_items(npages, max_n, num_kv_heads) <= budget) {
+        int64_t lo = cmin, hi = max_n;  // count_items is non-increasing in C
+        while (lo < hi) {
+          const int64_t mid = lo + (hi - lo) / 2;
+          if (fi::count_items(npages, mid, num_kv_heads) <= budget) hi = mid;
+          else lo = mid + 1;
+        }
+        C = lo;
+      }
+      if (o.max_chunk_tokens > 0)
+        C = std::min<int64_t>(C, std::max<int64_t>(1, o.max_chunk_tokens / page_size));
+    }
+    if (C > INT32_MAX) C = INT32_MAX;
+
+    std::unique_ptr<fi_plan> p(new fi_plan());
+    p->batch = batch;
+    p->num_qo_heads = num_qo_heads;
+    p->num_kv_heads = num_kv_heads;
+    p->head_dim = head_dim;
+    p->page_size = page_size;
+    p->group = group;
+    p->dtype = dtype;
+    p->num_pool_pages = num_pool_pages;
+    p->chunk_pages = (int32_t)C;
+    p->total_tokens = total_tokens;
+
+    // ---- items, partial slots, merge tasks
+    struct Item { int32_t f[FI_ITEM_STRIDE]; };
+    std::vector<Item> items;
+    int64_t slot = 0;
+    int32_t max_chunks = 0, min_split = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t n = npages[b];
+      const int64_t k = n > 0 ? fi::ceil_div(n, C) : 0;
+      max_chunks = std::max<int32_t>(max_chunks, (int32_t)k);
+      if (k >= 2) min_split = min_split == 0 ? (int32_t)k : std::min<int32_t>(min_split, (int32_t)k);
+      if (k != 1) {
+        p->merge.insert(p->merge.end(), {b, (int32_t)slot, (int32_t)k, 0});
+      }
+      int64_t page0 = 0;
+      for (int64_t c = 0; c < k; ++c) {
+        // near-equal cut: the first (n % k) chunks get one page more
+        const int64_t np = n / k + (c < n % k ? 1 : 0);
+        const bool has_last = page0 + np == n;
+        const int64_t tok = has_last ? (np - 1) * page_size + kv_last_page_len[b]
+                                     : np * (int64_t)page_size;
+        for (int32_t h = 0; h < num_kv_heads; ++h) {
+          Item it{};
+          it.f[FI_ITEM_REQUEST] = b;
+          it.f[FI_ITEM_KV_HEAD] = h;
+          it.f[FI_ITEM_PAGE_BEGIN] = (int32_t)(kv_indptr[b] + page0);
+          it.f[FI_ITEM_NUM_TOKENS] = (int32_t)tok;
+          it.f[FI_ITEM_SLOT] = k == 1 ? -1 : (int32_t)(slot + c);
+          it.f[FI_ITEM_CHUNK] = (int32_t)c;
+          it.f[FI_ITEM_NUM_PAGES] = (int32_t)np;
+          items.push_back(it);
+        }
+        page0 += np;
+      }
+      if (k >= 2) slot += k;
+    }
+    // longest first; ties in (request, KV head, chunk) order
+    std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
+      if (a.f[FI_ITEM_NUM_TOKENS] != b.f[FI_ITEM_NUM_TOKENS])
+        return a.f[FI_ITEM_NUM_TOKENS] > b.f[FI_ITEM_NUM_TOKENS];
+      if (a.f[FI_ITEM_REQUEST] != b.f[FI_ITEM_REQUEST])
+        return a.f[FI_ITEM_REQUEST] < b.f[FI_ITEM_REQUEST];
+      if (a.f[FI_ITEM_KV_HEAD] != b.f[FI_ITEM_KV_HEAD])
+        return a.f[FI_ITEM_KV_HEAD] < b.f[FI_ITEM_KV_HEAD];
+      return a.f[FI_ITEM_CHUNK] < b.f[FI_ITEM_CHUNK];
+    });
+    p->items.resize(items.size() * FI_ITEM_STRIDE);
+    for (size_t i = 0; i < items.size(); ++i)
+      std::memcpy(&p->items[i * FI_ITEM_STRIDE], items[i].f, sizeof(items[i].f));
+    p->num_slots = slot;
+    p->max_chunks = max_chunks;
+    p->min_chunks_split = min_split;
+
+    // ---- workspace layout and host image of its uploaded part
+    fi::WorkspaceLayout& ws = p->ws;
+    int64_t off = 0;
+    ws.items = off;
+    off = fi::align_up(off + (int64_t)p->items.size() * 4, 256);
+    ws.merge = off;
+    off = fi::align_up(off + (int64_t)p->merge.size() * 4, 256);
+    ws.page_ids = off;
+    off = fi::align_up(off + nnz * 4, 256);
+    ws.image_bytes = off;
+    ws.part_o = off;
+    off = fi::align_up(off + p->num_slots * num_qo_heads * (int64_t)head_dim * 4, 256);
+    ws.part_lse = off;
+    off = fi::align_up(off + p->num_slots * num_qo_heads * 4, 256);
+    ws.total_bytes = std::max<int64_t>(off, 256);
+    p->image.assign(ws.image_bytes, 0);
+    if (!p->items.empty())
+      std::memcpy(p->image.data() + ws.items, p->items.data(), p->items.size() * 4);
+    if (!p->merge.empty())
+      std::memcpy(p->image.data() + ws.merge, p->merge.data(), p->merge.size() * 4);
+    if (nnz > 0) std::memcpy(p->image.data() + ws.page_ids, kv_indices, nnz * 4);
+
+    *out_plan = p.release();
+    return FI_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(FI_ERR_NOMEM, "host allocation failed in fi_plan_create");
+  } catch (...) {
+    return fail(FI_ERR_INVALID_ARG, "unexpected error in fi_plan_create");
+  }
+}
+
+fi_status fi_plan_get_info(const fi_plan* p, fi_plan_info* info) {
+  if (!p || !info) return fi::fail(FI_ERR_INVALID_ARG, "NULL plan or info");
+  fi_plan_info r{};
+  r.num_items = p->num_items();
+  r.num_partial_slots = p->num_slots;
+  r.num_merge_tasks = p->num_merge();
+  r.workspace_bytes = p->ws.total_bytes;
+  r.total_kv_tokens = p->total_tokens;
+  r.chunk_pages = p->chunk_pages;
+  r.max_chunks_per_request = p->max_chunks;
+  r.min_chunks_split_request = p->min_chunks_split;
+  r.batch = p->batch;
+  r.num_qo_heads = p->num_qo_heads;
+  r.num_kv_heads = p->num_kv_heads;
+  r.head_dim = p->head_dim;
+  r.page_size = p->page_size;
+  r.dtype = (int32_t)p->dtype;
+  *info = r;
+  return FI_OK;
+}
+
+fi_status fi_plan_work_list(const fi_plan* p, const int32_t** items, int64_t* num_items) {
+  if (!p || !items || !num_items) return fi::fail(FI_ERR_INVALID_ARG, "NULL argument");
+  *items = p->items.data();
+  *num_items = p->num_items();
+  return FI_OK;
+}
+
+fi_status fi_plan_merge_list(const fi_plan* p, const int32_t** tasks, int64_t* num_tasks) {
+  if (!p || !tasks || !num_tasks) return fi::fail(FI_ERR_INVALID_ARG, "NULL argument");
+  *tasks = p->merge.data();
+  *num_tasks = p->num_merge();
+  return FI_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Host-side split-KV planner: data structures shared by the planner (plain
+// C++, no HIP headers, so it builds and is tested on a CPU-only host) and the
+// HIP launch layer.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "fi_bsr.h"
+
+namespace fi {
+
+// Byte offsets of the sections of the device workspace. Each section starts
+// on a 256-byte boundary. The first `image_bytes` are copied from the host
+// (work items, merge tasks, page ids); the rest is written by the kernels
+// (partial outputs and their log-sum-exp values).
+struct WorkspaceLayout {
+  int64_t items = 0;      // int32 [num_items][FI_ITEM_STRIDE]
+  int64_t merge = 0;      // int32 [num_merge_tasks][FI_MERGE_STRIDE]
+  int64_t page_ids = 0;   // int32 [nnz]
+  int64_t part_o = 0;     // float [num_slots][num_qo_heads][head_dim]
+  int64_t part_lse = 0;   // float [num_slots][num_qo_heads], log2 units
+  int64_t image_bytes = 0;
+  int64_t total_bytes = 0;
+};
+
+inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Record of the last fatal message for this thread.
+void set_error(const std::string& msg);
+
+}  // namespace fi
+
+struct fi_plan {
+  int32_t batch = 0, num_qo_heads = 0, num_kv_heads = 0, head_dim = 0, page_size = 0;
+  int32_t group = 0;
+  fi_dtype dtype = FI_DTYPE_BF16;
+  int64_t num_pool_pages = 0;
+  int32_t chunk_pages = 0;
+  int32_t max_chunks = 0, min_chunks_split = 0;
+  int64_t total_tokens = 0;
+  int64_t num_slots = 0;
+  std::vector<int32_t> items;   // num_items * FI_ITEM_STRIDE
+  std::vector<int32_t> merge;   // num_merge_tasks * FI_MERGE_STRIDE
+  std::vector<uint8_t> image;   // host copy of the uploaded part of the workspace
+  fi::WorkspaceLayout ws;
+  // Set by the launch layer.
+  void* pinned = nullptr;        // pinned staging copy of `image`
+  const void* uploaded_to = nullptr;
+  int64_t num_items() const { return (int64_t)items.size() / FI_ITEM_STRIDE; }
+  int64_t num_merge() const { return (int64_t)merge.size() / FI_MERGE_STRIDE; }
+};
+
+namespace fi {
+// Frees the host parts of a plan (the launch layer frees `pinned` first).
+void plan_free_host(fi_plan* p);
+}  // namespace fi

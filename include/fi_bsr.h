@@ -1,0 +1,227 @@
+/*
+ * fi_bsr.h -- C ABI of a decode-attention library for AMD MI355X (gfx950).
+ *
+ * Operation. Batched grouped-query decode attention over a KV cache held as
+ * a block-sparse-row (BSR) / paged matrix. Sources for what is computed:
+ *
+ *  - FlashInfer paper explainer, "FlashInfer: Block-Sparse KV 캐시로 어텐션
+ *    병목을 해소하다" (visionhong.com):
+ *      * section on where the attention bottleneck lies: a decode step attends
+ *        one new query token per request over that request's whole KV
+ *        history, so the step is bound by reading the KV cache from memory;
+ *      * section on the Block-Sparse format: the KV cache is a block-sparse
+ *        matrix whose blocks are runs of consecutive tokens; metadata lists
+ *        the active blocks; paged, dense and sparse layouts are all BSR;
+ *        inactive blocks are skipped;
+ *      * benchmark section: a load-balanced scheduler cuts long sequences
+ *        into several work units and interleaves them with short ones so no
+ *        workgroup idles in a skewed batch.
+ *  - FlashInfer 0.6.17 release write-up (llm-wiki.hwlabs.dev), "what is
+ *    FlashInfer" and section 5 (JIT warm-up): per-request context lengths
+ *    differ; head count, GQA ratio and block size are runtime parameters;
+ *    the call takes num_heads, num_kv_heads, head_dim and sm_scale (None =
+ *    default scale).
+ *
+ * For request b with listed pages kv_indices[kv_indptr[b] .. kv_indptr[b+1])
+ * and query head h (KV head kvh = h / G, G = num_qo_heads / num_kv_heads):
+ *     s_t      = sm_scale * <q[b,h,:], K[page_t, kvh, slot_t, :]>
+ *     out[b,h] = sum_t softmax(s)_t * V[page_t, kvh, slot_t, :]
+ *     lse[b,h] = ln sum_t exp(s_t)                 (natural log, scaled scores)
+ * over the tokens t of the listed pages in listed order: every listed page is
+ * full except the last, which holds kv_last_page_len[b] tokens. A request
+ * with no pages gets out = 0 and lse = -inf. Pages not listed (inactive
+ * blocks, spare pool pages) and slots past the last page's length are never
+ * read and may hold anything, NaN included.
+ *
+ * Memory layout (all contiguous, row-major):
+ *     q, out          [batch, num_qo_heads, head_dim]           dtype
+ *     lse             [batch, num_qo_heads]                     float32
+ *     k_pages,v_pages [num_pool_pages, num_kv_heads, page_size, head_dim] dtype
+ * dtype is float32 or bfloat16 for q, K, V and out alike. Arithmetic is
+ * float32 throughout; bfloat16 outputs are rounded to nearest even.
+ *
+ * Ownership. The caller owns every device buffer (q, pages, out, lse and the
+ * workspace). The library allocates no device memory. A plan owns host
+ * memory only (its work list and a pinned staging copy) and is immutable
+ * after fi_plan_create except for the record of which workspace it was last
+ * uploaded to. No call synchronises a stream or the device except
+ * fi_plan_destroy (releasing pinned host memory waits for the device).
+ *
+ * Errors. Every call returns an fi_status; on failure nothing is launched,
+ * the outputs are untouched, and fi_last_error() returns a message for the
+ * calling thread. No C++ exception crosses this boundary. Metadata are fully
+ * validated by fi_plan_create (host only); fi_decode_run checks pointers,
+ * alignment, workspace size and that the plan was uploaded to that
+ * workspace, then launches without reading device memory on the host.
+ *
+ * Thread safety. Distinct plans may be used from distinct threads. A plan
+ * must not be uploaded from two threads at once.
+ */
+#ifndef FI_BSR_H
+#define FI_BSR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FI_OK = 0,
+  FI_ERR_INVALID_ARG = -1, /* malformed metadata, null or misaligned pointer */
+  FI_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, group size, dtype */
+  FI_ERR_WORKSPACE = -3,   /* workspace too small */
+  FI_ERR_HIP = -4,         /* a HIP runtime call failed; message has its text */
+  FI_ERR_NOMEM = -5,       /* host allocation failed */
+  FI_ERR_STATE = -6        /* plan not uploaded to this workspace */
+} fi_status;
+
+typedef enum { FI_DTYPE_F32 = 0, FI_DTYPE_BF16 = 1 } fi_dtype;
+
+/* A hipStream_t; NULL is the null stream. */
+typedef void* fi_stream_t;
+
+typedef struct fi_plan fi_plan; /* opaque, host-owned */
+
+/* Planner knobs. Zero selects the default for every field. */
+typedef struct {
+  int32_t num_cus;            /* compute units to balance over (default 256) */
+  int32_t items_per_cu;       /* target work items per CU (default 8) */
+  int32_t min_chunk_tokens;   /* never cut a request finer than this (default 256) */
+  int32_t max_chunk_tokens;   /* cap on chunk length; 0 = no cap */
+  int32_t fixed_chunk_tokens; /* >0: use exactly this chunk length (rounded up
+                                 to whole pages) instead of the heuristic */
+} fi_plan_opts;
+
+typedef struct {
+  int64_t num_items;         /* work items = (request, KV head, chunk) */
+  int64_t num_partial_slots; /* partial states, each num_qo_heads rows */
+  int64_t num_merge_tasks;   /* requests finished by the merge kernel */
+  int64_t workspace_bytes;   /* device workspace fi_plan_upload needs */
+  int64_t total_kv_tokens;   /* sum of active tokens over the batch */
+  int32_t chunk_pages;       /* pages per chunk chosen by the planner */
+  int32_t max_chunks_per_request;
+  int32_t min_chunks_split_request; /* fewest chunks among split requests; 0 if none */
+  int32_t batch, num_qo_heads, num_kv_heads, head_dim, page_size;
+  int32_t dtype;
+} fi_plan_info;
+
+/* Fields of one work item in the list returned by fi_plan_work_list. */
+enum {
+  FI_ITEM_REQUEST = 0,    /* request b */
+  FI_ITEM_KV_HEAD = 1,    /* KV head; query heads kvh*G .. kvh*G+G-1 */
+  FI_ITEM_PAGE_BEGIN = 2, /* first page, as an index into kv_indices */
+  FI_ITEM_NUM_TOKENS = 3, /* tokens in this chunk (>= 1) */
+  FI_ITEM_SLOT = 4,       /* -1: writes out/lse directly; else partial slot */
+  FI_ITEM_CHUNK = 5,      /* chunk number within the request */
+  FI_ITEM_NUM_PAGES = 6,  /* pages in this chunk */
+  FI_ITEM_STRIDE = 8      /* int32 per item */
+};
+
+/* Fields of one merge task in the list returned by fi_plan_merge_list. */
+enum {
+  FI_MERGE_REQUEST = 0,
+  FI_MERGE_SLOT_BEGIN = 1, /* the request's partial slots are contiguous */
+  FI_MERGE_NUM_SLOTS = 2,  /* 0 for a request with no pages */
+  FI_MERGE_STRIDE = 4
+};
+
+/*
+ * Build the load-balanced split-KV plan for one decode step (the scheduler
+ * of the explainer's benchmark section). Host only; touches no device.
+ *
+ * kv_indptr        host int32 [batch+1], kv_indptr[0] = 0, non-decreasing
+ * kv_indices       host int32 [kv_indptr[batch]], each in [0, num_pool_pages)
+ * kv_last_page_len host int32 [batch]; in [1, page_size] for requests with
+ *                  pages, ignored (any value in [0, page_size]) for empty ones
+ * num_qo_heads, num_kv_heads: num_qo_heads % num_kv_heads == 0; the group
+ *                  size G = num_qo_heads / num_kv_heads must be 1, 2, 4 or 8
+ * head_dim         64 or 128
+ * page_size        block size in tokens, 1 .. 4096
+ * num_pool_pages   pages in the caller's k_pages / v_pages pools
+ * dtype            element type of q, K, V, out
+ * opts             may be NULL
+ * out_plan         receives a plan to free with fi_plan_destroy
+ *
+ * The planner picks one chunk length C (whole pages) for the batch: the
+ * smallest C of at least min_chunk_tokens for which the items
+ * sum_b ceil(n_b / C) * num_kv_heads fit in num_cus * items_per_cu (no cut
+ * if even the longest request's full length exceeds that budget), capped by
+ * max_chunk_tokens. Items are ordered longest first (ties by request, KV
+ * head, chunk) so that long chunks start early and short requests fill the
+ * gaps. The input arrays are copied; the caller may free them afterwards.
+ */
+fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
+                         const int32_t* kv_last_page_len, int32_t batch,
+                         int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t page_size, int64_t num_pool_pages, fi_dtype dtype,
+                         const fi_plan_opts* opts, fi_plan** out_plan);
+
+/* Sizes and choices of a plan. */
+fi_status fi_plan_get_info(const fi_plan* plan, fi_plan_info* info);
+
+/* Host view of the work list (num_items * FI_ITEM_STRIDE int32, in launch
+ * order) and of the merge tasks (num_merge_tasks * FI_MERGE_STRIDE int32).
+ * Valid until fi_plan_destroy. */
+fi_status fi_plan_work_list(const fi_plan* plan, const int32_t** items, int64_t* num_items);
+fi_status fi_plan_merge_list(const fi_plan* plan, const int32_t** tasks, int64_t* num_tasks);
+
+/*
+ * Copy the work list, merge tasks and page ids into the caller's device
+ * workspace (asynchronous host-to-device copy on `stream` from pinned host
+ * memory owned by the plan). workspace must be 256-byte aligned and at least
+ * info.workspace_bytes long. Call once per plan; the uploaded plan may then
+ * serve any number of fi_decode_run calls (e.g. every layer of a step).
+ */
+fi_status fi_plan_upload(fi_plan* plan, void* workspace, size_t workspace_bytes,
+                         fi_stream_t stream);
+
+/*
+ * Run decode attention for an uploaded plan on `stream` (one decode kernel
+ * over the work items, then one merge kernel for requests that were cut or
+ * are empty). No host synchronisation; safe to capture in a HIP graph once
+ * uploaded.
+ *
+ * q        device [batch, num_qo_heads, head_dim] dtype, 16-byte aligned
+ * k_pages  device [num_pool_pages, num_kv_heads, page_size, head_dim] dtype
+ * v_pages  same shape and type as k_pages
+ * out      device [batch, num_qo_heads, head_dim] dtype (written)
+ * lse      device float32 [batch, num_qo_heads] (written); may be NULL
+ * sm_scale score scale; <= 0 selects 1/sqrt(head_dim)
+ * workspace the buffer given to fi_plan_upload for this plan
+ */
+fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
+                        const void* v_pages, void* out, float* lse, float sm_scale,
+                        void* workspace, size_t workspace_bytes, fi_stream_t stream);
+
+/*
+ * Merge two attention states over disjoint token sets (the closed form of
+ * softmax over a union): with M = max(s_a, s_b),
+ *     s_out = M + ln(e^(s_a-M) + e^(s_b-M))
+ *     v_out = (e^(s_a-M) v_a + e^(s_b-M) v_b) / e^(s_out-M).
+ * A state with s = -inf (empty set) has weight 0; two such give v_out = 0,
+ * s_out = -inf. The cut-and-merge of the explainer's load-balanced scheduler
+ * needs exactly this combination of per-unit results.
+ *
+ * v_a, v_b, v_out  device [num_rows, head_dim] dtype, 16-byte aligned
+ * s_a, s_b, s_out  device float32 [num_rows], natural-log LSE
+ * head_dim         64 or 128; num_rows >= 0 (0 launches nothing)
+ * v_out/s_out may alias v_a/s_a or v_b/s_b exactly (elementwise).
+ */
+fi_status fi_merge_states(fi_dtype dtype, const void* v_a, const float* s_a,
+                          const void* v_b, const float* s_b, void* v_out, float* s_out,
+                          int64_t num_rows, int32_t head_dim, fi_stream_t stream);
+
+/* Free a plan (NULL is ignored). Waits for the device if the plan holds
+ * pinned staging memory, so uploads in flight finish first. */
+void fi_plan_destroy(fi_plan* plan);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* fi_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FI_BSR_H */

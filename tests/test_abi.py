@@ -1,0 +1,121 @@
+"""The C-ABI library on a CPU-only host: it loads, exports every function the
+header declares, and rejects malformed calls with a status and a message
+before touching any device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_kv_bsr_amd as fb
+from block_sparse_kv_bsr_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fi_bsr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fi_[a-z_]+)\s*\(", text)))
+
+
+def test_header_matches_binding_list():
+    assert declared_functions() == sorted(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = fb.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def _plan_status(indptr, indices, last, Hq=8, Hkv=2, d=128, P=16, pool=100, dtype=1, opts=None):
+    L = fb.lib()
+    ip = np.asarray(indptr, dtype=np.int32)
+    ix = np.asarray(indices, dtype=np.int32)
+    lp = np.asarray(last, dtype=np.int32)
+    h = ctypes.c_void_p()
+    p32 = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    st = L.fi_plan_create(p32(ip), p32(ix) if ix.size else None, p32(lp), len(ip) - 1, Hq, Hkv, d, P,
+                          pool, dtype, ctypes.byref(opts) if opts else None, ctypes.byref(h))
+    if st == 0:
+        L.fi_plan_destroy(h)
+    return st, L.fi_last_error().decode()
+
+
+GOOD = ([0, 2, 3], [5, 6, 7], [16, 3])
+
+
+def test_good_plan_is_ok():
+    assert _plan_status(*GOOD)[0] == 0
+
+
+@pytest.mark.parametrize("args,kw,code,needle", [
+    (([1, 2, 3], [5, 6, 7], [16, 3]), {}, -1, "kv_indptr[0]"),
+    (([0, 3, 2], [5, 6, 7], [16, 3]), {}, -1, "non-decreasing"),
+    (([0, 2, 3], [5, 6, 700], [16, 3]), {}, -1, "num_pool_pages"),
+    (([0, 2, 3], [5, -1, 7], [16, 3]), {}, -1, "num_pool_pages"),
+    (([0, 2, 3], [5, 6, 7], [0, 3]), {}, -1, "kv_last_page_len[0]"),
+    (([0, 2, 3], [5, 6, 7], [16, 17]), {}, -1, "kv_last_page_len[1]"),
+    (GOOD, {"Hq": 6, "Hkv": 4}, -1, "multiple"),
+    (GOOD, {"Hq": 24, "Hkv": 2}, -2, "group size"),
+    (GOOD, {"d": 96}, -2, "head_dim"),
+    (GOOD, {"dtype": 7}, -2, "dtype"),
+    (GOOD, {"P": 0}, -1, "page_size"),
+    (GOOD, {"Hq": 0}, -1, "positive"),
+])
+def test_plan_rejects(args, kw, code, needle):
+    st, msg = _plan_status(*args, **kw)
+    assert st == code and needle in msg, (st, msg)
+
+
+def test_negative_option_rejected():
+    o = binding.PlanOpts(-1, 0, 0, 0, 0)
+    st, msg = _plan_status(*GOOD, opts=o)
+    assert st == -1 and "option" in msg
+
+
+def test_run_without_upload_is_state_error():
+    """fi_decode_run refuses a workspace the plan was not uploaded to; the
+    check happens on the host before any launch."""
+    p = fb.plan(*[np.asarray(a) for a in GOOD], 8, 2, 128, 16, 100, "bf16")
+    L = fb.lib()
+    fake = ctypes.c_void_p(0x100000)
+    ws = p.info["workspace_bytes"]
+    st = L.fi_decode_run(p.handle, fake, fake, fake, fake, None, 0.0, fake, ws, None)
+    assert st == -6 and "upload" in L.fi_last_error().decode()
+    st = L.fi_decode_run(p.handle, fake, fake, fake, fake, None, 0.0, fake, ws - 1, None)
+    assert st == -3
+    st = L.fi_decode_run(p.handle, ctypes.c_void_p(0x100001), fake, fake, fake, None, 0.0, fake, ws, None)
+    assert st == -1 and "aligned" in L.fi_last_error().decode()
+    st = L.fi_decode_run(None, fake, fake, fake, fake, None, 0.0, fake, ws, None)
+    assert st == -1
+
+
+def test_upload_rejects_small_or_misaligned_workspace():
+    p = fb.plan(*[np.asarray(a) for a in GOOD], 8, 2, 128, 16, 100, "bf16")
+    L = fb.lib()
+    ws = p.info["workspace_bytes"]
+    assert L.fi_plan_upload(p.handle, ctypes.c_void_p(0x100000), ws - 1, None) == -3
+    assert L.fi_plan_upload(p.handle, ctypes.c_void_p(0x100010), ws, None) == -1
+    assert L.fi_plan_upload(p.handle, None, ws, None) == -1
+
+
+def test_merge_states_rejects():
+    L = fb.lib()
+    fake = ctypes.c_void_p(0x100000)
+    assert L.fi_merge_states(3, fake, fake, fake, fake, fake, fake, 4, 128, None) == -2
+    assert L.fi_merge_states(1, fake, fake, fake, fake, fake, fake, 4, 96, None) == -2
+    assert L.fi_merge_states(1, fake, fake, fake, fake, fake, fake, -1, 128, None) == -1
+    assert L.fi_merge_states(1, None, fake, fake, fake, fake, fake, 4, 128, None) == -1
+    assert L.fi_merge_states(1, fake, fake, fake, fake, fake, fake, 0, 128, None) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    p = fb.plan(*[np.asarray(a) for a in GOOD], 8, 2, 128, 16, 100, "bf16")
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    k = torch.zeros(100, 2, 16, 128, dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="GPU"):
+        fb.decode(q, k, k, p)

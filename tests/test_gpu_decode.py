@@ -1,0 +1,164 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Small ragged cases cover every built variant (dtype x head_dim x GQA group),
+page sizes that do and do not divide the 8-token step, empty requests, forced
+splits and NaN in every slot that must not be read; the five workloads run at
+full size with the same default plan bench.py times.
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_kv_bsr_amd as fb
+import oracle.attention as oa
+from block_sparse_kv_bsr_amd.workloads import random_workload, workload
+from tests.parity import compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    fb.lib()
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def run_case(w, device_values=False, what="", **opts):
+    log(f"[case] {what} B={w.batch} Hq={w.num_qo_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
+        f"P={w.page_size} {w.dtype} opts={opts}")
+    if device_values:
+        q, k, v = w.make_values("cuda")
+    else:
+        q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, w.num_qo_heads, w.num_kv_heads,
+                w.head_dim, w.page_size, w.num_pool_pages, w.dtype, **opts)
+    out, lse = fb.decode(q, k, v, p)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    qh, kh, vh = q.float().cpu().numpy(), k.float().cpu().numpy(), v.float().cpu().numpy()
+    O, LSE = oa.decode_attention(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len, w.sm_scale)
+    stats = compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE,
+                    w.dtype == "bf16", what)
+    log(f"[ok] {what} plan={p.info['num_items']} items chunk={p.info['chunk_pages']}p "
+        f"oracle {time.time() - t0:.1f}s {stats}")
+    return p, (q, k, v), (out, lse)
+
+
+SMALL = [
+    # seed, B, maxL, Hq, Hkv, d, P, dtype, empty_every
+    (1, 4, 300, 4, 1, 64, 16, "f32", 0),
+    (2, 5, 257, 8, 2, 128, 16, "bf16", 0),
+    (3, 6, 200, 8, 8, 128, 16, "bf16", 3),
+    (4, 3, 500, 16, 8, 128, 16, "bf16", 0),
+    (5, 4, 333, 32, 4, 128, 16, "bf16", 0),
+    (6, 4, 180, 8, 2, 64, 16, "bf16", 2),
+    (7, 3, 99, 4, 4, 64, 8, "f32", 0),
+    (8, 3, 140, 8, 2, 128, 16, "f32", 0),
+    (9, 3, 90, 16, 2, 64, 4, "f32", 0),
+    (10, 2, 130, 16, 2, 128, 16, "f32", 0),
+    (11, 4, 70, 8, 2, 128, 1, "bf16", 0),
+    (12, 4, 90, 8, 2, 128, 3, "bf16", 0),
+    (13, 4, 220, 8, 2, 128, 12, "bf16", 0),
+    (14, 3, 700, 8, 2, 128, 64, "bf16", 0),
+    (15, 3, 300, 8, 1, 128, 32, "bf16", 0),
+    (16, 2, 50, 4, 4, 64, 5, "f32", 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"s{c[0]}_{c[7]}_d{c[5]}_G{c[3] // c[4]}_P{c[6]}")
+def test_small_default_plan(case):
+    seed, B, L, Hq, Hkv, d, P, dt, ee = case
+    w = random_workload(seed, B, L, Hq, Hkv, d, P, dt, empty_every=ee)
+    run_case(w, what=f"small{seed}")
+
+
+@pytest.mark.parametrize("case", SMALL[:8] + SMALL[10:14], ids=lambda c: f"s{c[0]}_split")
+def test_small_forced_split(case):
+    """A tiny chunk length forces many chunks per request, partial states and
+    the merge kernel, including chunks that end inside the 8-token step."""
+    seed, B, L, Hq, Hkv, d, P, dt, ee = case
+    w = random_workload(seed, B, L, Hq, Hkv, d, P, dt, empty_every=ee)
+    run_case(w, what=f"split{seed}", fixed_chunk_tokens=max(P, 20))
+
+
+def test_single_token_and_exact_step_lengths():
+    lens = [1, 7, 8, 9, 15, 16, 17, 64, 0]
+    w = random_workload(31, len(lens), 0, 8, 2, 128, 16, "bf16", lens=lens)
+    run_case(w, what="edge-lengths")
+    run_case(w, what="edge-lengths-split", fixed_chunk_tokens=16)
+
+
+def test_all_requests_empty():
+    w = random_workload(32, 3, 0, 8, 2, 128, 16, "bf16", lens=[0, 0, 0])
+    run_case(w, what="all-empty")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_full_size(cfg):
+    w = workload(cfg)
+    p, _, _ = run_case(w, device_values=cfg > 1, what=f"config{cfg}")
+    if cfg == 4:
+        assert p.info["min_chunks_split_request"] >= 64
+
+
+def test_deterministic_for_fixed_plan():
+    w = workload(3)
+    q, k, v = w.make_values("cuda")
+    p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, w.num_qo_heads, w.num_kv_heads,
+                w.head_dim, w.page_size, w.num_pool_pages, w.dtype)
+    o1, l1 = fb.decode(q, k, v, p)
+    o2, l2 = fb.decode(q, k, v, p)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_page_order_permutation():
+    """Permuting a request's full pages (the partial page stays last) gives the
+    same result within tolerance."""
+    w = random_workload(40, 5, 600, 16, 4, 128, 16, "bf16")
+    p0, (q, k, v), (o0, l0) = run_case(w, what="perm-base")
+    rng = np.random.default_rng(1)
+    ix = w.kv_indices.copy()
+    for b in range(w.batch):
+        s, t = w.kv_indptr[b], w.kv_indptr[b + 1]
+        if t - s > 2:
+            ix[s:t - 1] = ix[s:t - 1][rng.permutation(t - 1 - s)]
+    p1 = fb.plan(w.kv_indptr, ix, w.last_page_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                 w.page_size, w.num_pool_pages, w.dtype)
+    o1, l1 = fb.decode(q, k, v, p1)
+    torch.cuda.synchronize()
+    assert (o1.float() - o0.float()).abs().max().item() <= 2 * 2 ** -7
+    assert (l1 - l0).abs().max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+def test_merge_states(dtype, d):
+    g = torch.Generator().manual_seed(5)
+    n = 1000
+    va = torch.randn(n, d, generator=g)
+    vb = torch.randn(n, d, generator=g)
+    sa = torch.randn(n, generator=g) * 4
+    sb = torch.randn(n, generator=g) * 4
+    sa[::7] = -float("inf")
+    sb[::11] = -float("inf")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    va, vb = va.to(tdt), vb.to(tdt)
+    log(f"[case] merge_states {dtype} d={d}")
+    vo, so = fb.merge_states(va.cuda(), sa.cuda(), vb.cuda(), sb.cuda())
+    torch.cuda.synchronize()
+    V, S = oa.merge_states(va.double().numpy(), sa.double().numpy(), vb.double().numpy(),
+                           sb.double().numpy())
+    compare(vo.double().cpu().numpy(), so.double().cpu().numpy(), V, S, dtype == "bf16",
+            f"merge_states {dtype} d={d}")
+    # in place on a (output aliases the first state)
+    va2, sa2 = va.cuda(), sa.cuda()
+    fb.merge_states(va2, sa2, vb.cuda(), sb.cuda(), v_out=va2, s_out=sa2)
+    torch.cuda.synchronize()
+    assert torch.equal(va2.cpu().view(torch.int16 if dtype == "bf16" else torch.int32),
+                       vo.cpu().view(torch.int16 if dtype == "bf16" else torch.int32))
