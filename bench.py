@@ -1,0 +1,270 @@
+"""Benchmark: skewed-batch paged GQA decode on one MI355X.
+
+One step = one pass of the decode hot path over one batch: the decode kernel
+over the planner's work items, then the merge kernel (fi_decode_attend +
+fi_decode_merge, i.e. fi_decode_run), with the plan built once per batch and
+uploaded before timing (a serving engine reuses one plan for every layer of a
+decode step; the host planner's own time is reported beside it). Inputs are
+resident in HBM. Before every timed step a 1 GiB fill evicts L2 and the
+256 MB Infinity Cache, outside the timed events.
+
+Prints one JSON line: achieved HBM GB/s over the algorithmic bytes (active K
+and V once per KV head + q read + output written), microseconds per batch,
+the decode kernel's roofline fraction against 8 TB/s, and the float64 CPU
+oracle timed on the host on the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config 3]
+    python bench.py --summarize-counters FETCH.csv WRITE.csv   # rocprofv3 --pmc output
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "achieved HBM GB/s (% of MI355X peak) + µs/batch, skewed-batch paged GQA decode"
+PEAK_HBM_GBS = 8000.0
+DECODE_SRC = os.path.join(ROOT, "block_sparse_kv_bsr_amd", "csrc", "decode_bsr.hip")
+COPY_PROBE_MIB = 1024
+
+
+def source_digest() -> str:
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counters_file(workload_name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"decode_bsr_counters_{workload_name}.txt")
+
+
+def read_traffic(workload_name: str):
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when there is none or the decode kernel source changed since."""
+    path = counters_file(workload_name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("decode_source_sha256_16") != source_digest():
+        return None
+    try:
+        return float(vals["scaled_fetch_bytes_per_launch"]) + float(vals["scaled_write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------- counters
+def _pmc_rows(path, counter):
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                rows.append((r.get("Kernel_Name", ""), float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_counters(fetch_csv, write_csv, workload_name):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) into bytes per decode launch, scaled by what the same counters
+    read for a plain copy of COPY_PROBE_MIB MiB in the same program."""
+    out = {}
+    for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = _pmc_rows(path, counter)
+        dec = [v for k, v in rows if "decode_bsr_kernel" in k]
+        cpy = [v for k, v in rows if "copy" in k.lower() or "elementwise" in k.lower()]
+        if not dec or not cpy:
+            raise SystemExit(f"{path}: no decode or copy dispatches with {counter}")
+        known_kib = COPY_PROBE_MIB * 1024.0
+        probe = max(cpy)
+        scale = known_kib / probe
+        out[f"{name}_kib_raw_mean"] = statistics.mean(dec)
+        out[f"{name}_copy_probe_kib"] = probe
+        out[f"{name}_scale"] = scale
+        out[f"scaled_{name}_bytes_per_launch"] = statistics.mean(dec) * 1024.0 * scale
+    path = counters_file(workload_name)
+    with open(path, "w") as f:
+        f.write(f"# decode_bsr_kernel HBM traffic, workload {workload_name}\n")
+        f.write("# from: rocprofv3 --pmc FETCH_SIZE -- python bench.py --counters-run\n")
+        f.write("#  and: rocprofv3 --pmc WRITE_SIZE -- python bench.py --counters-run\n")
+        f.write(f"# each counter scaled by (known bytes / counter) of a {COPY_PROBE_MIB} MiB copy\n")
+        f.write(f"decode_source_sha256_16 = {source_digest()}\n")
+        for k, v in out.items():
+            f.write(f"{k} = {v:.6g}\n")
+    print(open(path).read())
+
+
+# ------------------------------------------------------------------ oracle
+def cpu_baseline(w, q, k, v, min_seconds=10.0, max_passes=3):
+    """Time the float64 oracle on the host over whole batches of the same
+    workload (inputs copied to host memory first, not timed)."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import oracle.attention as oa
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: numpy BLAS default
+        threads = os.cpu_count() or 1
+    qh, kh, vh = q.float().cpu().numpy(), k.float().cpu().numpy(), v.float().cpu().numpy()
+    times = []
+    while len(times) < max_passes and sum(times) < min_seconds:
+        t0 = time.perf_counter()
+        oa.decode_attention(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len, w.sm_scale)
+        times.append(time.perf_counter() - t0)
+    per = statistics.median(times)
+    return {"value": w.algorithmic_bytes() / per / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "seconds_per_batch": per,
+            "sample": f"whole {w.name} batch ({int(w.kv_lens().sum())} KV tokens), "
+                      f"{len(times)} pass(es), median; numpy float64 on host cores"}
+
+
+# ------------------------------------------------------------------- bench
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--items-per-cu", type=int, default=0)
+    ap.add_argument("--min-chunk-tokens", type=int, default=0)
+    ap.add_argument("--fixed-chunk-tokens", type=int, default=0)
+    ap.add_argument("--counters-run", action="store_true",
+                    help="short run for rocprofv3 --pmc: a copy probe, then a few steps")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    args = ap.parse_args()
+
+    sys.path.insert(0, ROOT)
+    from block_sparse_kv_bsr_amd.workloads import workload
+    w = workload(args.config)
+
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, w.name)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this decode path runs on a single MI355X and has no multi-GPU mode.", flush=True)
+        return 2
+
+    import torch
+    import block_sparse_kv_bsr_amd as fb
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    fb.lib()
+    dev = torch.device("cuda:0")
+    q, k, v = w.make_values(dev)
+    opts = dict(items_per_cu=args.items_per_cu, min_chunk_tokens=args.min_chunk_tokens,
+                fixed_chunk_tokens=args.fixed_chunk_tokens)
+
+    # host planner time (median of 20) and upload time
+    plan_t = []
+    for _ in range(20):
+        t0 = time.perf_counter()
+        p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, w.num_qo_heads, w.num_kv_heads,
+                    w.head_dim, w.page_size, w.num_pool_pages, w.dtype, **opts)
+        plan_t.append(time.perf_counter() - t0)
+    ws = torch.empty(max(256, p.info["workspace_bytes"]), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    p.upload(ws)
+    torch.cuda.synchronize()
+    upload_s = time.perf_counter() - t0
+
+    out = torch.empty((w.batch, w.num_qo_heads, w.head_dim), dtype=q.dtype, device=dev)
+    lse = torch.empty((w.batch, w.num_qo_heads), dtype=torch.float32, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    if args.counters_run:
+        src = torch.empty(COPY_PROBE_MIB << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        args.steps, args.warmup = min(args.steps, 5), 1
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        fb.decode(q, k, v, p, out=out, lse=lse, workspace=ws, phase="attend")
+        if ev:
+            ev[1].record()
+        fb.decode(q, k, v, p, out=out, lse=lse, workspace=ws, phase="merge")
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            flush.zero_()
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.zero_()
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    dec_ms = [e[0].elapsed_time(e[1]) for e in events]
+    step_ms = [e[0].elapsed_time(e[2]) for e in events]
+    step_mean = statistics.mean(step_ms)
+    dec_mean = statistics.mean(dec_ms)
+    nbytes = w.algorithmic_bytes()
+    gbs = nbytes / (step_mean * 1e-3) / 1e9
+    dec_gbs = nbytes / (dec_mean * 1e-3) / 1e9
+    traffic = read_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_mean, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_qo_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "page_size": w.page_size, "kv_tokens": int(w.kv_lens().sum()),
+                   "algorithmic_bytes": nbytes, "parallelism": "single-gpu",
+                   "plan_items": p.info["num_items"], "chunk_pages": p.info["chunk_pages"],
+                   "l2_mall_flush_between_steps": not args.no_flush},
+        "us_per_batch": round(step_mean * 1e3, 2),
+        "us_per_batch_p10_p90": [round(1e3 * sorted(step_ms)[int(0.1 * (len(step_ms) - 1))], 2),
+                                 round(1e3 * sorted(step_ms)[int(0.9 * (len(step_ms) - 1))], 2)],
+        "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "decode_kernel_us": round(dec_mean * 1e3, 2),
+        "merge_kernel_us": round((step_mean - dec_mean) * 1e3, 2),
+        "plan_host_us": round(1e6 * statistics.median(plan_t), 1),
+        "upload_us": round(1e6 * upload_s, 1),
+        "wall_s_timed_loop": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None if traffic is None else int(traffic),
+                     "kernel": "decode_bsr_kernel"},
+    }
+    if not args.no_cpu_baseline and not args.counters_run:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

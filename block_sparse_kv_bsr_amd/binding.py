@@ -27,8 +27,8 @@ STATUS_NAMES = {0: "FI_OK", -1: "FI_ERR_INVALID_ARG", -2: "FI_ERR_UNSUPPORTED",
 
 # Every symbol include/fi_bsr.h declares.
 EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_merge_list",
-            "fi_plan_upload", "fi_decode_run", "fi_merge_states", "fi_plan_destroy",
-            "fi_last_error"]
+            "fi_plan_upload", "fi_decode_run", "fi_decode_attend", "fi_decode_merge",
+            "fi_merge_states", "fi_plan_destroy", "fi_last_error"]
 
 
 class FiError(RuntimeError):
@@ -84,6 +84,10 @@ def lib() -> ctypes.CDLL:
     L.fi_plan_upload.restype = i32
     L.fi_decode_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
     L.fi_decode_run.restype = i32
+    L.fi_decode_attend.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
+    L.fi_decode_attend.restype = i32
+    L.fi_decode_merge.argtypes = [vp, vp, vp, vp, sz, vp]
+    L.fi_decode_merge.restype = i32
     L.fi_merge_states.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, vp]
     L.fi_merge_states.restype = i32
     L.fi_plan_destroy.argtypes = [vp]
@@ -211,9 +215,7 @@ def _require_gpu(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-def decode(q, k_pages, v_pages, plan_: Plan, out=None, lse=None, sm_scale: Optional[float] = None,
-           workspace=None, stream=None):
-    """fi_decode_run: returns (out [B, H_q, d] in q's dtype, lse [B, H_q] float32)."""
+def _decode_args(q, k_pages, v_pages, plan_: Plan, out, lse, workspace, stream):
     import torch
     for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
         _require_gpu(t, n)
@@ -235,14 +237,29 @@ def decode(q, k_pages, v_pages, plan_: Plan, out=None, lse=None, sm_scale: Optio
     _require_gpu(lse, "lse")
     if workspace is None:
         workspace = plan_.ensure_uploaded(q.device, stream)
-    _check(lib().fi_decode_run(plan_.handle, ctypes.c_void_p(q.data_ptr()),
-                               ctypes.c_void_p(k_pages.data_ptr()),
-                               ctypes.c_void_p(v_pages.data_ptr()),
-                               ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
-                               float(sm_scale) if sm_scale else 0.0,
-                               ctypes.c_void_p(workspace.data_ptr()),
-                               workspace.numel() * workspace.element_size(),
-                               ctypes.c_void_p(_stream(stream))))
+    return out, lse, workspace
+
+
+def decode(q, k_pages, v_pages, plan_: Plan, out=None, lse=None, sm_scale: Optional[float] = None,
+           workspace=None, stream=None, phase: str = "run"):
+    """fi_decode_run: returns (out [B, H_q, d] in q's dtype, lse [B, H_q] float32).
+
+    ``phase`` "attend" or "merge" issues only that half (fi_decode_attend /
+    fi_decode_merge); "run" issues both."""
+    out, lse, workspace = _decode_args(q, k_pages, v_pages, plan_, out, lse, workspace, stream)
+    s = ctypes.c_void_p(_stream(stream))
+    ws = ctypes.c_void_p(workspace.data_ptr())
+    nbytes = workspace.numel() * workspace.element_size()
+    o, l = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr())
+    scale = float(sm_scale) if sm_scale else 0.0
+    if phase == "merge":
+        _check(lib().fi_decode_merge(plan_.handle, o, l, ws, nbytes, s))
+        return out, lse
+    fn = lib().fi_decode_run if phase == "run" else lib().fi_decode_attend
+    if phase not in ("run", "attend"):
+        raise ValueError(f"unknown phase {phase}")
+    _check(fn(plan_.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_pages.data_ptr()),
+              ctypes.c_void_p(v_pages.data_ptr()), o, l, scale, ws, nbytes, s))
     return out, lse
 
 

@@ -52,26 +52,40 @@ fi_status fi_plan_upload(fi_plan* plan, void* workspace, size_t workspace_bytes,
   return FI_OK;
 }
 
-fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
-                        const void* v_pages, void* out, float* lse, float sm_scale,
-                        void* workspace, size_t workspace_bytes, fi_stream_t stream) {
+namespace {
+
+// Host-side checks shared by the decode entry points; nothing is launched
+// unless they pass.
+fi_status check_run(const fi_plan* plan, void* out, float* lse, void* workspace,
+                    size_t workspace_bytes) {
   if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
   if (plan->batch == 0) return FI_OK;
-  if (!q || !out) return fail(FI_ERR_INVALID_ARG, "q or out is NULL");
-  if (plan->num_items() > 0 && (!k_pages || !v_pages))
-    return fail(FI_ERR_INVALID_ARG, "k_pages or v_pages is NULL");
-  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16))
-    return fail(FI_ERR_INVALID_ARG, "q, out, k_pages and v_pages must be 16-byte aligned");
+  if (!out) return fail(FI_ERR_INVALID_ARG, "out is NULL");
+  if (!aligned(out, 16)) return fail(FI_ERR_INVALID_ARG, "out must be 16-byte aligned");
   if (lse && !aligned(lse, 4)) return fail(FI_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   if (!workspace) return fail(FI_ERR_INVALID_ARG, "workspace is NULL");
   if ((int64_t)workspace_bytes < plan->ws.total_bytes)
     return fail(FI_ERR_WORKSPACE, "workspace smaller than fi_plan_info.workspace_bytes");
   if (plan->uploaded_to != workspace)
     return fail(FI_ERR_STATE, "plan was not uploaded to this workspace (call fi_plan_upload)");
-  if (!(sm_scale > 0.f)) sm_scale = 1.0f / std::sqrt((float)plan->head_dim);
+  return FI_OK;
+}
 
+fi_status check_inputs(const fi_plan* plan, const void* q, const void* k_pages,
+                       const void* v_pages) {
+  if (!q) return fail(FI_ERR_INVALID_ARG, "q is NULL");
+  if (plan->num_items() > 0 && (!k_pages || !v_pages))
+    return fail(FI_ERR_INVALID_ARG, "k_pages or v_pages is NULL");
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16))
+    return fail(FI_ERR_INVALID_ARG, "q, k_pages and v_pages must be 16-byte aligned");
+  return FI_OK;
+}
+
+fi_status launch_attend(const fi_plan* plan, const void* q, const void* k_pages,
+                        const void* v_pages, void* out, float* lse, float sm_scale,
+                        void* workspace, hipStream_t s) {
+  if (!(sm_scale > 0.f)) sm_scale = 1.0f / std::sqrt((float)plan->head_dim);
   char* ws = static_cast<char*>(workspace);
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   fi::DecodeArgs d{};
   d.items = reinterpret_cast<const int32_t*>(ws + plan->ws.items);
   d.page_ids = reinterpret_cast<const int32_t*>(ws + plan->ws.page_ids);
@@ -92,20 +106,61 @@ fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
   d.sm_scale = sm_scale;
   hipError_t e = fi::launch_decode(d, s);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  return FI_OK;
+}
 
+fi_status launch_merge(const fi_plan* plan, void* out, float* lse, void* workspace, hipStream_t s) {
+  char* ws = static_cast<char*>(workspace);
   fi::MergePartialArgs m{};
   m.tasks = reinterpret_cast<const int32_t*>(ws + plan->ws.merge);
-  m.part_o = d.part_o;
-  m.part_lse = d.part_lse;
+  m.part_o = reinterpret_cast<const float*>(ws + plan->ws.part_o);
+  m.part_lse = reinterpret_cast<const float*>(ws + plan->ws.part_lse);
   m.out = out;
   m.lse = lse;
   m.num_tasks = plan->num_merge();
   m.num_qo_heads = plan->num_qo_heads;
   m.head_dim = plan->head_dim;
-  m.bf16 = d.bf16;
-  e = fi::launch_merge_partials(m, s);
+  m.bf16 = plan->dtype == FI_DTYPE_BF16;
+  hipError_t e = fi::launch_merge_partials(m, s);
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   return FI_OK;
+}
+
+}  // namespace
+
+fi_status fi_decode_attend(const fi_plan* plan, const void* q, const void* k_pages,
+                           const void* v_pages, void* out, float* lse, float sm_scale,
+                           void* workspace, size_t workspace_bytes, fi_stream_t stream) {
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->batch == 0) return FI_OK;
+  fi_status st = check_inputs(plan, q, k_pages, v_pages);
+  if (st != FI_OK) return st;
+  st = check_run(plan, out, lse, workspace, workspace_bytes);
+  if (st != FI_OK) return st;
+  return launch_attend(plan, q, k_pages, v_pages, out, lse, sm_scale, workspace,
+                       static_cast<hipStream_t>(stream));
+}
+
+fi_status fi_decode_merge(const fi_plan* plan, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, fi_stream_t stream) {
+  fi_status st = check_run(plan, out, lse, workspace, workspace_bytes);
+  if (st != FI_OK || plan->batch == 0) return st;
+  return launch_merge(plan, out, lse, workspace, static_cast<hipStream_t>(stream));
+}
+
+fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
+                        const void* v_pages, void* out, float* lse, float sm_scale,
+                        void* workspace, size_t workspace_bytes, fi_stream_t stream) {
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->batch == 0) return FI_OK;
+  fi_status st = check_inputs(plan, q, k_pages, v_pages);
+  if (st != FI_OK) return st;
+  st = check_run(plan, out, lse, workspace, workspace_bytes);
+  if (st != FI_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_attend(plan, q, k_pages, v_pages, out, lse, sm_scale, workspace, s);
+  if (st != FI_OK) return st;
+  return launch_merge(plan, out, lse, workspace, s);
 }
 
 fi_status fi_merge_states(fi_dtype dtype, const void* v_a, const float* s_a, const void* v_b,

@@ -196,6 +196,21 @@ fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
                         void* workspace, size_t workspace_bytes, fi_stream_t stream);
 
 /*
+ * The two launches of fi_decode_run, exposed separately so a caller can put
+ * work or timing events between them: fi_decode_attend runs the decode kernel
+ * (requests of one chunk get their final out/lse; cut requests leave partial
+ * states in the workspace) and fi_decode_merge runs the merge kernel that
+ * finishes cut and empty requests. fi_decode_attend followed by
+ * fi_decode_merge on one stream, with the same arguments, is exactly
+ * fi_decode_run. Arguments and errors as for fi_decode_run.
+ */
+fi_status fi_decode_attend(const fi_plan* plan, const void* q, const void* k_pages,
+                           const void* v_pages, void* out, float* lse, float sm_scale,
+                           void* workspace, size_t workspace_bytes, fi_stream_t stream);
+fi_status fi_decode_merge(const fi_plan* plan, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, fi_stream_t stream);
+
+/*
  * Merge two attention states over disjoint token sets (the closed form of
  * softmax over a union): with M = max(s_a, s_b),
  *     s_out = M + ln(e^(s_a-M) + e^(s_b-M))
