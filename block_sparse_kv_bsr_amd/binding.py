@@ -51,7 +51,8 @@ class PlanInfo(ctypes.Structure):
                 ("min_chunks_split_request", ctypes.c_int32),
                 ("batch", ctypes.c_int32), ("num_qo_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("shared_pages", ctypes.c_int64)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

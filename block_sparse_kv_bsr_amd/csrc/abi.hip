@@ -103,6 +103,7 @@ fi_status launch_attend(const fi_plan* plan, const void* q, const void* k_pages,
   d.page_size = plan->page_size;
   d.group = plan->group;
   d.bf16 = plan->dtype == FI_DTYPE_BF16;
+  d.stream_kv = plan->shared_pages == 0;
   d.sm_scale = sm_scale;
   hipError_t e = fi::launch_decode(d, s);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");

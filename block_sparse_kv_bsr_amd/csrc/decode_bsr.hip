@@ -10,10 +10,13 @@
 // so the kernel is built around the page gather:
 //
 //  * One wave per item, 8 lanes per token row, 8 token rows per step: each
-//    lane issues 16-byte loads at row offsets sub*16 + j*128, so one load
-//    instruction covers eight whole 128-byte lines. Loads go straight to
-//    VGPRs: a K/V row is used by exactly one wave, so LDS staging would add
-//    traffic without reuse.
+//    lane fetches 16 bytes at row offset sub*16 + j*128, so one load
+//    instruction covers eight whole 128-byte lines.
+//  * The loads go to LDS with gfx950's direct-to-LDS loads
+//    (global_load_lds_dwordx4): a ring of kRing steps per wave stays in
+//    flight without holding VGPRs, which is what keeps enough bytes in
+//    flight per CU to stream HBM. Each lane reads back exactly the 16 bytes
+//    it fetched (ds_read_b128 at lane*16), so LDS sees no bank conflicts.
 //  * GQA packing: each K/V row is loaded once per KV head and serves all G
 //    query heads of the group (query heads kvh*G+i share KV head kvh).
 //  * Scores: bf16 pairs go through v_dot2 (two products + accumulate into
@@ -24,9 +27,11 @@
 //    when a score exceeds it by more than 8 (so exp2 stays <= 256), which
 //    makes accumulator rescales rare. The eight per-lane-group states are
 //    merged once at the end of the item.
-//  * Prefetch: a ring of kDepth token steps (K and V) is kept in flight per
-//    wave; the page-id window for 64 pages sits in one VGPR and is read with
-//    ds_bpermute.
+//  * The ring reads use inline ds_read_b128 behind explicit vmcnt waits
+//    (loads retire in issue order, so "all but the last N loads done" is a
+//    count). The compiler cannot tell which ring slot a direct-to-LDS load
+//    writes and would otherwise wait for every load in flight before each
+//    LDS read. Page ids of a chunk sit in an LDS window.
 //  * Tokens past the request's length in the last page are excluded by
 //    selection (score -inf, weight 0, V zeroed), never by multiplying by a
 //    zero weight, so whatever those slots hold (NaN included) cannot leak.
@@ -49,6 +54,9 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // The running max is raised only when a score exceeds it by more than this
 // (log2 units), so unnormalised weights stay within [0, 2^8].
 constexpr float kRescaleMargin = 8.0f;
+// Page ids of a chunk staged in LDS at a time (a wave reloads the window when
+// it walks past it).
+constexpr int kIdWindow = 256;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -86,6 +94,13 @@ __device__ __forceinline__ float sum8(float x) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// x *= f with the result tied to x's register. Used inside the rare rescale
+// branch: a plain multiply there lets the compiler keep a second copy of
+// every accumulator across the branch and copy them back on the common path.
+__device__ __forceinline__ void scale_in_place(float& x, float f) {
+  asm volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(f));
+}
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -100,7 +115,51 @@ __device__ __forceinline__ uint4 load16(const char* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-__device__ __forceinline__ uint32_t word(const uint4& v, int w) {
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+
+// Cache policy of the K/V loads. K/V rows are read once per decode step: the
+// nontemporal policy (nt) streams them past the caches instead of allocating
+// lines that will not be reused. When the plan lists a physical page for
+// several requests (a shared prefix) the default policy keeps the re-reads
+// cacheable in L2 / MALL.
+template <bool kStream>
+__device__ __forceinline__ void dma16(const char* src, void* lds_base) {
+  constexpr int kAux = kStream ? 2 : 0;  // bit 1 = nt on gfx950
+  __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)lds_base, 16, 0, kAux);
+}
+
+// s_waitcnt vmcnt(n), leaving the other counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// Read a ring stage back: n 16-byte chunks at the given LDS addresses, then
+// wait for them. The wait is tied to the outputs so no use can move above it.
+template <int N>
+__device__ __forceinline__ void lds_read_stage(const uint32_t (&addr)[N], u32x4_t (&out)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("ds_read_b128 %0, %1" : "=v"(out[i]) : "v"(addr[i]) : "memory");
+  if constexpr (N == 2) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(out[0]), "+v"(out[1]) :: "memory");
+  } else if constexpr (N == 4) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(out[0]), "+v"(out[1]), "+v"(out[2]), "+v"(out[3]) :: "memory");
+  } else {
+    static_assert(N == 8, "stage of 2, 4 or 8 chunks");
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(out[0]), "+v"(out[1]), "+v"(out[2]), "+v"(out[3]), "+v"(out[4]),
+                   "+v"(out[5]), "+v"(out[6]), "+v"(out[7])::"memory");
+  }
+}
+
+__device__ __forceinline__ uint32_t word(const u32x4_t& v, int w) {
   return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
 }
 
@@ -115,21 +174,23 @@ struct Row {
   static_assert(kLoads >= 1, "row shorter than 128 bytes");
 };
 
-// Register plan per lane: accumulators G*NE, query words G*NW, a ring of
-// kDepth (K, V) steps of 8*L words, plus ~80 for state, addressing and
-// temporaries. Two waves per SIMD (<= 256 VGPRs) when that fits, else one
-// wave (VGPRs + AGPRs, <= 512).
+// Occupancy and ring depth. The ring has 4 stages, read back two at a time.
+// VGPRs per lane: accumulators G*NE, query words G*NW, two stages read back
+// from LDS (16*L), softmax state and ~48 for addressing and temporaries.
+// LDS per wave: 4 stages of 2*L KiB plus the page-id window. Waves per SIMD:
+// as many as both budgets allow, at most 3.
 template <bool kBF16, int D, int G>
 struct Tune {
   using R = Row<kBF16, D>;
-  static constexpr int kBase = G * R::kElems + G * R::kWords + 2 * G + 80;
-  static constexpr int kStage = 8 * R::kLoads;
-  static constexpr int kWaves = kBase + 2 * kStage <= 240 ? 2 : 1;
-  static constexpr int kBudget = kWaves == 2 ? 240 : 440;
-  static constexpr int kDepth = kBase + 4 * kStage <= kBudget ? 4 : 2;
+  static constexpr int kRing = 4;
+  static constexpr int kRegs = G * R::kElems + G * R::kWords + 16 * R::kLoads + 2 * G + 48;
+  static constexpr int kByRegs = kRegs <= 168 ? 3 : (kRegs <= 240 ? 2 : 1);
+  static constexpr int kLdsPerWave = kRing * 2 * R::kLoads * 1024 + kIdWindow * 4;
+  static constexpr int kByLds = (160 * 1024) / (4 * kLdsPerWave);
+  static constexpr int kWaves = kByRegs < kByLds ? kByRegs : (kByLds >= 1 ? kByLds : 1);
 };
 
-template <bool kBF16, int D, int G, int kDepth, int kWaves>
+template <bool kBF16, int D, int G, int kRing, int kWaves, bool kStream>
 __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) {
   using R = Row<kBF16, D>;
   constexpr int L = R::kLoads;
@@ -148,6 +209,21 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   const int npg = it[FI_ITEM_NUM_PAGES];
   const int P = p.page_size;
 
+  // ---- page-id window in LDS: entry i is the id of page (wbase + i) of the
+  // chunk. Reading ids from LDS keeps the id lookup off the vector-memory
+  // counter, so fetching an id never waits for the K/V loads in flight.
+  __shared__ int s_ids[kIdWindow];
+  int wbase = 0;
+  // Every lane loads and stores unconditionally (indices clamped to the
+  // chunk), so the wait for these loads is a plain vmcnt(0) on every path.
+  auto fill_window = [&](int base) {
+#pragma unroll
+    for (int i = 0; i < kIdWindow / 64; ++i)
+      s_ids[i * 64 + lane] = p.page_ids[pb + min(base + i * 64 + lane, npg - 1)];
+    __syncthreads();
+  };
+  fill_window(0);
+
   // ---- query fragments of the G heads (same columns as the K/V fragments)
   const int64_t qrow0 = (int64_t)b * p.num_qo_heads + (int64_t)kvh * G;
   uint32_t qw[G][NW];
@@ -163,9 +239,6 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
     }
   }
 
-  // ---- page-id window: lane i holds the id of page (wbase + i) of the chunk
-  int wbase = 0;
-  int win = lane < npg ? p.page_ids[pb + lane] : 0;
 
   // ---- load cursor: page-local index and slot of this lane's next token
   int cur_pl = tg / P;
@@ -173,33 +246,58 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   const int last_pl = (ntok - 1) / P;
   const int last_slot = (ntok - 1) - last_pl * P;
   const int ngroups = (ntok + 7) >> 3;
+  const int nfull = ntok >> 3;
   const int64_t head_off = (int64_t)kvh * p.head_stride + sub * 16;
 
-  uint4 kb[kDepth][L], vb[kDepth][L];
+  // LDS ring: stage s holds the K rows (chunks 0..L-1) and V rows (chunks
+  // L..2L-1) of one step, 64 lanes x 16 bytes per chunk.
+  __shared__ __attribute__((aligned(16))) uint4 s_ring[kRing][2 * L][64];
 
-  auto issue = [&](int g, uint4 (&kr)[L], uint4 (&vr)[L]) {
-    int pl = cur_pl, sl = cur_slot;
-    if (g == ngroups - 1 && g * 8 + tg >= ntok) {  // past the end: re-read the last token
+  // Issue the K/V loads of step g into ring stage `stage`. Loads are issued
+  // on every path (a step past the end re-reads the item's last token, which
+  // is cached) so every stage is refilled exactly once per consume and the
+  // vmcnt counts below are exact.
+  auto issue = [&](int g, int stage) {
+    const bool real = g < ngroups;
+    int pl = real ? cur_pl : last_pl;
+    int sl = real ? cur_slot : last_slot;
+    if (g == ngroups - 1 && g * 8 + tg >= ntok) {  // ragged last step: clamp to the last token
       pl = last_pl;
       sl = last_slot;
     }
-    if (__builtin_amdgcn_readlane(pl, 63) - wbase >= 64) {
+    if (__builtin_amdgcn_readlane(pl, 63) - wbase >= kIdWindow) {  // rare: slide the window
+      __syncthreads();
       wbase = __builtin_amdgcn_readfirstlane(pl);
-      win = wbase + lane < npg ? p.page_ids[pb + wbase + lane] : 0;
+      fill_window(wbase);
     }
-    const int pid = __shfl(win, pl - wbase);
+    const int pid = s_ids[pl - wbase];
     const int64_t off = (int64_t)pid * p.page_stride + head_off + (int64_t)sl * R::kBytes;
     const char* kp = p.k_pages + off;
     const char* vp = p.v_pages + off;
 #pragma unroll
-    for (int j = 0; j < L; ++j) kr[j] = load16(kp + j * 128);
+    for (int j = 0; j < L; ++j) dma16<kStream>(kp + j * 128, &s_ring[stage][j][0]);
 #pragma unroll
-    for (int j = 0; j < L; ++j) vr[j] = load16(vp + j * 128);
-    cur_slot += p.step_slots;
-    cur_pl += p.step_pages;
-    if (cur_slot >= P) {
-      cur_slot -= P;
-      cur_pl += 1;
+    for (int j = 0; j < L; ++j) dma16<kStream>(vp + j * 128, &s_ring[stage][L + j][0]);
+    if (real) {
+      cur_slot += p.step_slots;
+      cur_pl += p.step_pages;
+      if (cur_slot >= P) {
+        cur_slot -= P;
+        cur_pl += 1;
+      }
+    }
+  };
+
+  auto read_stage = [&](int stage, u32x4_t (&kr)[L], u32x4_t (&vr)[L]) {
+    uint32_t addr[2 * L];
+    u32x4_t v[2 * L];
+#pragma unroll
+    for (int j = 0; j < 2 * L; ++j) addr[j] = lds_addr(&s_ring[stage][j][lane]);
+    lds_read_stage<2 * L>(addr, v);
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      kr[j] = v[j];
+      vr[j] = v[L + j];
     }
   };
 
@@ -212,7 +310,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
     for (int e = 0; e < NE; ++e) acc[h][e] = 0.f;
   }
 
-  auto consume = [&](const uint4 (&kr)[L], uint4 (&vr)[L], bool masked, bool valid) {
+  auto consume = [&](const u32x4_t (&kr)[L], u32x4_t (&vr)[L], bool masked, bool valid) {
     float s[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -240,18 +338,19 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
         vr[j].w = valid ? vr[j].w : 0u;
       }
     }
-    bool need = false;
+    // rescale only when some score passes its running max by the margin
+    float over = s[0] - m[0];
 #pragma unroll
-    for (int h = 0; h < G; ++h) need |= s[h] > m[h] + kRescaleMargin;
-    if (__any(need)) {
+    for (int h = 1; h < G; ++h) over = fmaxf(over, s[h] - m[h]);
+    if (__any(over > kRescaleMargin)) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const bool up = s[h] > m[h] + kRescaleMargin;
         const float f = up ? exp2_fast(m[h] - s[h]) : 1.f;
         m[h] = up ? s[h] : m[h];
-        l[h] *= f;
+        scale_in_place(l[h], f);
 #pragma unroll
-        for (int e = 0; e < NE; ++e) acc[h][e] *= f;
+        for (int e = 0; e < NE; ++e) scale_in_place(acc[h][e], f);
       }
     }
     float pw[G];
@@ -279,22 +378,50 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
     }
   };
 
-  // ---- main loop: ring of kDepth steps in flight
+  // ---- main loop: a ring of kRing steps in flight. Steps [0, nfull) are
+  // whole (8 valid tokens); only step ngroups-1 can be ragged. The loop
+  // consumes whole steps; the tail pass consumes what is left (<= kRing
+  // steps, all already in flight) with per-lane masking. Before stage s is
+  // read, exactly the loads of the stages issued after it may be pending.
+  constexpr int kPerStage = 2 * L;
 #pragma unroll
-  for (int s = 0; s < kDepth; ++s)
-    if (s < ngroups) issue(s, kb[s], vb[s]);
-  const bool ragged = (ntok & 7) != 0;
-  for (int g0 = 0; g0 < ngroups; g0 += kDepth) {
+  for (int s = 0; s < kRing; ++s) issue(s, s);
+  int g0 = 0;
+  for (; g0 + kRing <= nfull; g0 += kRing) {
+    // Stages are read back and refilled two at a time: the refill then asks
+    // DRAM for both halves of a 4 KiB K page (and of its V page) back to
+    // back, which keeps DRAM row hits high; refilling one 2 KiB half per
+    // step, with the arithmetic in between, let other waves' requests land
+    // in between and cost about a tenth of the bandwidth.
 #pragma unroll
-    for (int s = 0; s < kDepth; ++s) {
-      const int g = g0 + s;
-      if (g < ngroups) {
-        if (ragged && g == ngroups - 1) consume(kb[s], vb[s], true, g * 8 + tg < ntok);
-        else consume(kb[s], vb[s], false, true);
-        if (g + kDepth < ngroups) issue(g + kDepth, kb[s], vb[s]);
-      }
+    for (int s = 0; s < kRing; s += 2) {
+      u32x4_t kr0[L], vr0[L], kr1[L], vr1[L];
+      wait_vmcnt<kPerStage * (kRing - 1)>();
+      read_stage(s, kr0, vr0);
+      wait_vmcnt<kPerStage * (kRing - 2)>();
+      read_stage(s + 1, kr1, vr1);
+      issue(g0 + s + kRing, s);
+      issue(g0 + s + 1 + kRing, s + 1);
+      consume(kr0, vr0, false, true);
+      consume(kr1, vr1, false, true);
     }
   }
+#pragma unroll
+  for (int s = 0; s < kRing; ++s) {
+    const int g = g0 + s;
+    u32x4_t kr[L], vr[L];
+    if (s == 0) wait_vmcnt<kPerStage * (kRing - 1)>();
+    if (s == 1) wait_vmcnt<kPerStage * (kRing >= 2 ? kRing - 2 : 0)>();
+    if (s == 2) wait_vmcnt<kPerStage * (kRing >= 3 ? kRing - 3 : 0)>();
+    if (s == 3) wait_vmcnt<kPerStage * (kRing >= 4 ? kRing - 4 : 0)>();
+    if (g < ngroups) {
+      read_stage(s, kr, vr);
+      consume(kr, vr, true, g * 8 + tg < ntok);
+    }
+  }
+  // Loads past the end may still be in flight into the ring; let them land
+  // before the wave can exit and its LDS is handed to another workgroup.
+  wait_vmcnt<0>();
 
   // ---- merge the 8 lane-group states (lanes with equal `sub`)
 #pragma unroll
@@ -375,20 +502,25 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
 }
 
 template <bool kBF16, int D, int G>
-hipError_t launch_typed(const DecodeParams& prm, int64_t num_items, hipStream_t stream) {
+hipError_t launch_typed(const DecodeParams& prm, int64_t num_items, bool stream_kv,
+                        hipStream_t stream) {
   using T = Tune<kBF16, D, G>;
-  hipLaunchKernelGGL((decode_bsr_kernel<kBF16, D, G, T::kDepth, T::kWaves>),
-                     dim3((uint32_t)num_items), dim3(64), 0, stream, prm);
+  if (stream_kv)
+    hipLaunchKernelGGL((decode_bsr_kernel<kBF16, D, G, T::kRing, T::kWaves, true>),
+                       dim3((uint32_t)num_items), dim3(64), 0, stream, prm);
+  else
+    hipLaunchKernelGGL((decode_bsr_kernel<kBF16, D, G, T::kRing, T::kWaves, false>),
+                       dim3((uint32_t)num_items), dim3(64), 0, stream, prm);
   return hipGetLastError();
 }
 
 template <bool kBF16, int D>
-hipError_t launch_group(const DecodeParams& prm, int64_t n, int G, hipStream_t s) {
+hipError_t launch_group(const DecodeParams& prm, int64_t n, int G, bool st, hipStream_t s) {
   switch (G) {
-    case 1: return launch_typed<kBF16, D, 1>(prm, n, s);
-    case 2: return launch_typed<kBF16, D, 2>(prm, n, s);
-    case 4: return launch_typed<kBF16, D, 4>(prm, n, s);
-    case 8: return launch_typed<kBF16, D, 8>(prm, n, s);
+    case 1: return launch_typed<kBF16, D, 1>(prm, n, st, s);
+    case 2: return launch_typed<kBF16, D, 2>(prm, n, st, s);
+    case 4: return launch_typed<kBF16, D, 4>(prm, n, st, s);
+    case 8: return launch_typed<kBF16, D, 8>(prm, n, st, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -417,11 +549,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   prm.step_slots = 8 % a.page_size;
   prm.scale_log2 = a.sm_scale * kLog2e;
   if (a.bf16) {
-    if (a.head_dim == 128) return launch_group<true, 128>(prm, a.num_items, a.group, stream);
-    if (a.head_dim == 64) return launch_group<true, 64>(prm, a.num_items, a.group, stream);
+    if (a.head_dim == 128) return launch_group<true, 128>(prm, a.num_items, a.group, a.stream_kv, stream);
+    if (a.head_dim == 64) return launch_group<true, 64>(prm, a.num_items, a.group, a.stream_kv, stream);
   } else {
-    if (a.head_dim == 128) return launch_group<false, 128>(prm, a.num_items, a.group, stream);
-    if (a.head_dim == 64) return launch_group<false, 64>(prm, a.num_items, a.group, stream);
+    if (a.head_dim == 128) return launch_group<false, 128>(prm, a.num_items, a.group, a.stream_kv, stream);
+    if (a.head_dim == 64) return launch_group<false, 64>(prm, a.num_items, a.group, a.stream_kv, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -20,6 +20,7 @@ struct DecodeArgs {
   int64_t num_items;
   int32_t num_qo_heads, num_kv_heads, head_dim, page_size, group;
   bool bf16;
+  bool stream_kv;           // nontemporal K/V loads (no page listed twice)
   float sm_scale;
 };
 

@@ -158,6 +158,13 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     p->num_pool_pages = num_pool_pages;
     p->chunk_pages = (int32_t)C;
     p->total_tokens = total_tokens;
+    {
+      // physical pages that several requests (or one request twice) list
+      std::vector<int32_t> ids(kv_indices, kv_indices + nnz);
+      std::sort(ids.begin(), ids.end());
+      for (size_t j = 1; j < ids.size(); ++j)
+        if (ids[j] == ids[j - 1] && (j == 1 || ids[j - 1] != ids[j - 2])) ++p->shared_pages;
+    }
 
     // ---- items, partial slots, merge tasks
     struct Item { int32_t f[FI_ITEM_STRIDE]; };
@@ -259,6 +266,7 @@ fi_status fi_plan_get_info(const fi_plan* p, fi_plan_info* info) {
   r.head_dim = p->head_dim;
   r.page_size = p->page_size;
   r.dtype = (int32_t)p->dtype;
+  r.shared_pages = p->shared_pages;
   *info = r;
   return FI_OK;
 }

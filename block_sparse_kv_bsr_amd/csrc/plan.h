@@ -41,6 +41,7 @@ struct fi_plan {
   int32_t chunk_pages = 0;
   int32_t max_chunks = 0, min_chunks_split = 0;
   int64_t total_tokens = 0;
+  int64_t shared_pages = 0;  // distinct physical pages listed more than once
   int64_t num_slots = 0;
   std::vector<int32_t> items;   // num_items * FI_ITEM_STRIDE
   std::vector<int32_t> merge;   // num_merge_tasks * FI_MERGE_STRIDE

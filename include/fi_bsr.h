@@ -105,6 +105,9 @@ typedef struct {
   int32_t min_chunks_split_request; /* fewest chunks among split requests; 0 if none */
   int32_t batch, num_qo_heads, num_kv_heads, head_dim, page_size;
   int32_t dtype;
+  int64_t shared_pages; /* physical pages listed more than once; when 0 the
+                           kernel streams K/V past the caches (nontemporal
+                           loads), else it keeps them cacheable for re-reads */
 } fi_plan_info;
 
 /* Fields of one work item in the list returned by fi_plan_work_list. */
