@@ -159,11 +159,25 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     p->chunk_pages = (int32_t)C;
     p->total_tokens = total_tokens;
     {
-      // physical pages that several requests (or one request twice) list
-      std::vector<int32_t> ids(kv_indices, kv_indices + nnz);
-      std::sort(ids.begin(), ids.end());
-      for (size_t j = 1; j < ids.size(); ++j)
-        if (ids[j] == ids[j - 1] && (j == 1 || ids[j - 1] != ids[j - 2])) ++p->shared_pages;
+      // physical pages that several requests (or one request twice) list:
+      // a bitmap over the pool when it is not much larger than the page
+      // lists, else a sort
+      if (num_pool_pages <= 64 * nnz + 65536) {
+        std::vector<uint64_t> seen((size_t)(num_pool_pages + 63) / 64, 0), twice(seen.size(), 0);
+        for (int64_t j = 0; j < nnz; ++j) {
+          const int64_t id = kv_indices[j];
+          const uint64_t bit = 1ull << (id & 63);
+          uint64_t& w = seen[(size_t)(id >> 6)];
+          if (w & bit) twice[(size_t)(id >> 6)] |= bit;
+          w |= bit;
+        }
+        for (uint64_t w : twice) p->shared_pages += __builtin_popcountll(w);
+      } else {
+        std::vector<int32_t> ids(kv_indices, kv_indices + nnz);
+        std::sort(ids.begin(), ids.end());
+        for (size_t j = 1; j < ids.size(); ++j)
+          if (ids[j] == ids[j - 1] && (j == 1 || ids[j - 1] != ids[j - 2])) ++p->shared_pages;
+      }
     }
 
     // ---- items, partial slots, merge tasks
