@@ -174,15 +174,18 @@ struct Row {
   static_assert(kLoads >= 1, "row shorter than 128 bytes");
 };
 
-// Occupancy and ring depth. The ring has 4 stages, read back two at a time.
+// Occupancy and ring depth. The ring has 2 stages (8 KiB of K/V per wave at
+// bf16, d 128), read back and refilled together. Deeper rings were measured
+// slower on MI355X: with 4 stages (16 KiB per wave) more requests queue at
+// the memory controllers and the skewed batch lost ~4% bandwidth.
 // VGPRs per lane: accumulators G*NE, query words G*NW, two stages read back
 // from LDS (16*L), softmax state and ~48 for addressing and temporaries.
-// LDS per wave: 4 stages of 2*L KiB plus the page-id window. Waves per SIMD:
+// LDS per wave: kRing stages of 2*L KiB plus the page-id window. Waves per SIMD:
 // as many as both budgets allow, at most 3.
 template <bool kBF16, int D, int G>
 struct Tune {
   using R = Row<kBF16, D>;
-  static constexpr int kRing = 4;
+  static constexpr int kRing = 2;
   static constexpr int kRegs = G * R::kElems + G * R::kWords + 16 * R::kLoads + 2 * G + 48;
   static constexpr int kByRegs = kRegs <= 168 ? 3 : (kRegs <= 240 ? 2 : 1);
   static constexpr int kLdsPerWave = kRing * 2 * R::kLoads * 1024 + kIdWindow * 4;
@@ -190,7 +193,7 @@ struct Tune {
   static constexpr int kWaves = kByRegs < kByLds ? kByRegs : (kByLds >= 1 ? kByLds : 1);
 };
 
-template <bool kBF16, int D, int G, int kRing, int kWaves, bool kStream>
+template <bool kBF16, int D, int G, int kRing, int kWaves, bool kStream, bool kUniform>
 __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) {
   using R = Row<kBF16, D>;
   constexpr int L = R::kLoads;
@@ -284,6 +287,47 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
       if (cur_slot >= P) {
         cur_slot -= P;
         cur_pl += 1;
+      }
+    }
+  };
+
+  // Page sizes that are multiples of 8: the 8 rows of a step always sit in
+  // one page, so the page id and the row base are wave-uniform (scalar
+  // registers) and each lane adds a fixed offset (row tg, column sub). A
+  // ragged last step reads the whole 8 rows of its page (in bounds; the
+  // extra rows are masked in consume); a step past the end re-reads the last
+  // step.
+  const int last_step = ngroups - 1;
+  const int u_last_pl = (last_step * 8) / P;
+  const int u_last_slot = last_step * 8 - u_last_pl * P;
+  const int lane_off = tg * R::kBytes + sub * 16;
+  const int64_t kvh_off = (int64_t)kvh * p.head_stride;
+  int u_pl = 0, u_slot = 0, u_cached_pl = -1, u_pid = 0;
+  auto issue_uniform = [&](int g, int stage) {
+    const bool real = g < ngroups;
+    const int pl = real ? u_pl : u_last_pl;
+    const int sl = real ? u_slot : u_last_slot;
+    if (pl != u_cached_pl) {
+      if (pl - wbase >= kIdWindow) {  // rare: slide the window
+        __syncthreads();
+        wbase = pl;
+        fill_window(wbase);
+      }
+      u_pid = __builtin_amdgcn_readfirstlane(s_ids[pl - wbase]);
+      u_cached_pl = pl;
+    }
+    const int64_t base = (int64_t)u_pid * p.page_stride + kvh_off + (int64_t)sl * R::kBytes;
+    const char* kp = p.k_pages + base;
+    const char* vp = p.v_pages + base;
+#pragma unroll
+    for (int j = 0; j < L; ++j) dma16<kStream>(kp + lane_off + j * 128, &s_ring[stage][j][0]);
+#pragma unroll
+    for (int j = 0; j < L; ++j) dma16<kStream>(vp + lane_off + j * 128, &s_ring[stage][L + j][0]);
+    if (real) {
+      u_slot += 8;
+      if (u_slot == P) {
+        u_slot = 0;
+        u_pl += 1;
       }
     }
   };
@@ -385,7 +429,10 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   // read, exactly the loads of the stages issued after it may be pending.
   constexpr int kPerStage = 2 * L;
 #pragma unroll
-  for (int s = 0; s < kRing; ++s) issue(s, s);
+  for (int s = 0; s < kRing; ++s) {
+    if constexpr (kUniform) issue_uniform(s, s);
+    else issue(s, s);
+  }
   int g0 = 0;
   for (; g0 + kRing <= nfull; g0 += kRing) {
     // Stages are read back and refilled two at a time: the refill then asks
@@ -400,8 +447,13 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
       read_stage(s, kr0, vr0);
       wait_vmcnt<kPerStage * (kRing - 2)>();
       read_stage(s + 1, kr1, vr1);
-      issue(g0 + s + kRing, s);
-      issue(g0 + s + 1 + kRing, s + 1);
+      if constexpr (kUniform) {
+        issue_uniform(g0 + s + kRing, s);
+        issue_uniform(g0 + s + 1 + kRing, s + 1);
+      } else {
+        issue(g0 + s + kRing, s);
+        issue(g0 + s + 1 + kRing, s + 1);
+      }
       consume(kr0, vr0, false, true);
       consume(kr1, vr1, false, true);
     }
@@ -501,17 +553,23 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   }
 }
 
+template <bool kBF16, int D, int G, bool kStream>
+hipError_t launch_variant(const DecodeParams& prm, int64_t num_items, hipStream_t stream) {
+  using T = Tune<kBF16, D, G>;
+  if (prm.page_size % 8 == 0)
+    hipLaunchKernelGGL((decode_bsr_kernel<kBF16, D, G, T::kRing, T::kWaves, kStream, true>),
+                       dim3((uint32_t)num_items), dim3(64), 0, stream, prm);
+  else
+    hipLaunchKernelGGL((decode_bsr_kernel<kBF16, D, G, T::kRing, T::kWaves, kStream, false>),
+                       dim3((uint32_t)num_items), dim3(64), 0, stream, prm);
+  return hipGetLastError();
+}
+
 template <bool kBF16, int D, int G>
 hipError_t launch_typed(const DecodeParams& prm, int64_t num_items, bool stream_kv,
                         hipStream_t stream) {
-  using T = Tune<kBF16, D, G>;
-  if (stream_kv)
-    hipLaunchKernelGGL((decode_bsr_kernel<kBF16, D, G, T::kRing, T::kWaves, true>),
-                       dim3((uint32_t)num_items), dim3(64), 0, stream, prm);
-  else
-    hipLaunchKernelGGL((decode_bsr_kernel<kBF16, D, G, T::kRing, T::kWaves, false>),
-                       dim3((uint32_t)num_items), dim3(64), 0, stream, prm);
-  return hipGetLastError();
+  return stream_kv ? launch_variant<kBF16, D, G, true>(prm, num_items, stream)
+                   : launch_variant<kBF16, D, G, false>(prm, num_items, stream);
 }
 
 template <bool kBF16, int D>
