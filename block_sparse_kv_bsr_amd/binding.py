@@ -19,16 +19,17 @@ LIB_PATH = os.path.join(_HERE, "libfi_bsr.so")
 FI_OK = 0
 FI_DTYPE_F32 = 0
 FI_DTYPE_BF16 = 1
-ITEM_STRIDE = 8
-MERGE_STRIDE = 4
+ITEM_STRIDE = 16
+NODE_STRIDE = 8
+MERGE_FAN_IN = 32
 
 STATUS_NAMES = {0: "FI_OK", -1: "FI_ERR_INVALID_ARG", -2: "FI_ERR_UNSUPPORTED",
                 -3: "FI_ERR_WORKSPACE", -4: "FI_ERR_HIP", -5: "FI_ERR_NOMEM", -6: "FI_ERR_STATE"}
 
 # Every symbol include/fi_bsr.h declares.
-EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_merge_list",
-            "fi_plan_upload", "fi_decode_run", "fi_decode_attend", "fi_decode_merge",
-            "fi_merge_states", "fi_plan_destroy", "fi_last_error"]
+EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_merge_nodes",
+            "fi_plan_upload", "fi_decode_run", "fi_merge_states", "fi_plan_destroy",
+            "fi_last_error"]
 
 
 class FiError(RuntimeError):
@@ -45,7 +46,7 @@ class PlanOpts(ctypes.Structure):
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("num_items", ctypes.c_int64), ("num_partial_slots", ctypes.c_int64),
-                ("num_merge_tasks", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("num_merge_nodes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("total_kv_tokens", ctypes.c_int64), ("chunk_pages", ctypes.c_int32),
                 ("max_chunks_per_request", ctypes.c_int32),
                 ("min_chunks_split_request", ctypes.c_int32),
@@ -79,16 +80,12 @@ def lib() -> ctypes.CDLL:
     L.fi_plan_get_info.restype = i32
     L.fi_plan_work_list.argtypes = [vp, ctypes.POINTER(pi32), ctypes.POINTER(i64)]
     L.fi_plan_work_list.restype = i32
-    L.fi_plan_merge_list.argtypes = [vp, ctypes.POINTER(pi32), ctypes.POINTER(i64)]
-    L.fi_plan_merge_list.restype = i32
+    L.fi_plan_merge_nodes.argtypes = [vp, ctypes.POINTER(pi32), ctypes.POINTER(i64)]
+    L.fi_plan_merge_nodes.restype = i32
     L.fi_plan_upload.argtypes = [vp, vp, sz, vp]
     L.fi_plan_upload.restype = i32
     L.fi_decode_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
     L.fi_decode_run.restype = i32
-    L.fi_decode_attend.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
-    L.fi_decode_attend.restype = i32
-    L.fi_decode_merge.argtypes = [vp, vp, vp, vp, sz, vp]
-    L.fi_decode_merge.restype = i32
     L.fi_merge_states.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, vp]
     L.fi_merge_states.restype = i32
     L.fi_plan_destroy.argtypes = [vp]
@@ -147,13 +144,13 @@ class Plan:
             return np.zeros((0, ITEM_STRIDE), dtype=np.int32)
         return np.ctypeslib.as_array(p, shape=(n.value * ITEM_STRIDE,)).reshape(-1, ITEM_STRIDE).copy()
 
-    def merge_list(self) -> np.ndarray:
+    def merge_nodes(self) -> np.ndarray:
         p = ctypes.POINTER(ctypes.c_int32)()
         n = ctypes.c_int64()
-        _check(lib().fi_plan_merge_list(self._h, ctypes.byref(p), ctypes.byref(n)))
+        _check(lib().fi_plan_merge_nodes(self._h, ctypes.byref(p), ctypes.byref(n)))
         if n.value == 0:
-            return np.zeros((0, MERGE_STRIDE), dtype=np.int32)
-        return np.ctypeslib.as_array(p, shape=(n.value * MERGE_STRIDE,)).reshape(-1, MERGE_STRIDE).copy()
+            return np.zeros((0, NODE_STRIDE), dtype=np.int32)
+        return np.ctypeslib.as_array(p, shape=(n.value * NODE_STRIDE,)).reshape(-1, NODE_STRIDE).copy()
 
     def upload(self, workspace, stream=None):
         """Copy the plan into ``workspace`` (a torch uint8 CUDA tensor)."""
@@ -242,25 +239,17 @@ def _decode_args(q, k_pages, v_pages, plan_: Plan, out, lse, workspace, stream):
 
 
 def decode(q, k_pages, v_pages, plan_: Plan, out=None, lse=None, sm_scale: Optional[float] = None,
-           workspace=None, stream=None, phase: str = "run"):
-    """fi_decode_run: returns (out [B, H_q, d] in q's dtype, lse [B, H_q] float32).
-
-    ``phase`` "attend" or "merge" issues only that half (fi_decode_attend /
-    fi_decode_merge); "run" issues both."""
+           workspace=None, stream=None):
+    """fi_decode_run: returns (out [B, H_q, d] in q's dtype, lse [B, H_q] float32)."""
     out, lse, workspace = _decode_args(q, k_pages, v_pages, plan_, out, lse, workspace, stream)
     s = ctypes.c_void_p(_stream(stream))
     ws = ctypes.c_void_p(workspace.data_ptr())
     nbytes = workspace.numel() * workspace.element_size()
     o, l = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr())
     scale = float(sm_scale) if sm_scale else 0.0
-    if phase == "merge":
-        _check(lib().fi_decode_merge(plan_.handle, o, l, ws, nbytes, s))
-        return out, lse
-    fn = lib().fi_decode_run if phase == "run" else lib().fi_decode_attend
-    if phase not in ("run", "attend"):
-        raise ValueError(f"unknown phase {phase}")
-    _check(fn(plan_.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_pages.data_ptr()),
-              ctypes.c_void_p(v_pages.data_ptr()), o, l, scale, ws, nbytes, s))
+    _check(lib().fi_decode_run(plan_.handle, ctypes.c_void_p(q.data_ptr()),
+                               ctypes.c_void_p(k_pages.data_ptr()),
+                               ctypes.c_void_p(v_pages.data_ptr()), o, l, scale, ws, nbytes, s))
     return out, lse
 
 

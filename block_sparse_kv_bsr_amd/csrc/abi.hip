@@ -81,9 +81,9 @@ fi_status check_inputs(const fi_plan* plan, const void* q, const void* k_pages,
   return FI_OK;
 }
 
-fi_status launch_attend(const fi_plan* plan, const void* q, const void* k_pages,
-                        const void* v_pages, void* out, float* lse, float sm_scale,
-                        void* workspace, hipStream_t s) {
+fi_status launch_run(const fi_plan* plan, const void* q, const void* k_pages,
+                     const void* v_pages, void* out, float* lse, float sm_scale,
+                     void* workspace, hipStream_t s) {
   if (!(sm_scale > 0.f)) sm_scale = 1.0f / std::sqrt((float)plan->head_dim);
   char* ws = static_cast<char*>(workspace);
   fi::DecodeArgs d{};
@@ -96,6 +96,8 @@ fi_status launch_attend(const fi_plan* plan, const void* q, const void* k_pages,
   d.lse = lse;
   d.part_o = reinterpret_cast<float*>(ws + plan->ws.part_o);
   d.part_lse = reinterpret_cast<float*>(ws + plan->ws.part_lse);
+  d.nodes = reinterpret_cast<const int32_t*>(ws + plan->ws.nodes);
+  d.counters = reinterpret_cast<int32_t*>(ws + plan->ws.counters);
   d.num_items = plan->num_items();
   d.num_qo_heads = plan->num_qo_heads;
   d.num_kv_heads = plan->num_kv_heads;
@@ -110,44 +112,7 @@ fi_status launch_attend(const fi_plan* plan, const void* q, const void* k_pages,
   return FI_OK;
 }
 
-fi_status launch_merge(const fi_plan* plan, void* out, float* lse, void* workspace, hipStream_t s) {
-  char* ws = static_cast<char*>(workspace);
-  fi::MergePartialArgs m{};
-  m.tasks = reinterpret_cast<const int32_t*>(ws + plan->ws.merge);
-  m.part_o = reinterpret_cast<const float*>(ws + plan->ws.part_o);
-  m.part_lse = reinterpret_cast<const float*>(ws + plan->ws.part_lse);
-  m.out = out;
-  m.lse = lse;
-  m.num_tasks = plan->num_merge();
-  m.num_qo_heads = plan->num_qo_heads;
-  m.head_dim = plan->head_dim;
-  m.bf16 = plan->dtype == FI_DTYPE_BF16;
-  hipError_t e = fi::launch_merge_partials(m, s);
-  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
-  return FI_OK;
-}
-
 }  // namespace
-
-fi_status fi_decode_attend(const fi_plan* plan, const void* q, const void* k_pages,
-                           const void* v_pages, void* out, float* lse, float sm_scale,
-                           void* workspace, size_t workspace_bytes, fi_stream_t stream) {
-  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
-  if (plan->batch == 0) return FI_OK;
-  fi_status st = check_inputs(plan, q, k_pages, v_pages);
-  if (st != FI_OK) return st;
-  st = check_run(plan, out, lse, workspace, workspace_bytes);
-  if (st != FI_OK) return st;
-  return launch_attend(plan, q, k_pages, v_pages, out, lse, sm_scale, workspace,
-                       static_cast<hipStream_t>(stream));
-}
-
-fi_status fi_decode_merge(const fi_plan* plan, void* out, float* lse, void* workspace,
-                          size_t workspace_bytes, fi_stream_t stream) {
-  fi_status st = check_run(plan, out, lse, workspace, workspace_bytes);
-  if (st != FI_OK || plan->batch == 0) return st;
-  return launch_merge(plan, out, lse, workspace, static_cast<hipStream_t>(stream));
-}
 
 fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
                         const void* v_pages, void* out, float* lse, float sm_scale,
@@ -158,10 +123,8 @@ fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
   if (st != FI_OK) return st;
   st = check_run(plan, out, lse, workspace, workspace_bytes);
   if (st != FI_OK) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  st = launch_attend(plan, q, k_pages, v_pages, out, lse, sm_scale, workspace, s);
-  if (st != FI_OK) return st;
-  return launch_merge(plan, out, lse, workspace, s);
+  return launch_run(plan, q, k_pages, v_pages, out, lse, sm_scale, workspace,
+                    static_cast<hipStream_t>(stream));
 }
 
 fi_status fi_merge_states(fi_dtype dtype, const void* v_a, const float* s_a, const void* v_b,

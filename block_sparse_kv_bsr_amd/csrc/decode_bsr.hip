@@ -38,7 +38,8 @@
 //
 // The result is written directly (bf16 rounded to nearest even, natural-log
 // LSE) when the request is one chunk, else as an fp32 partial state (output
-// already divided by its own sum, LSE in log2 units) for the merge kernel.
+// already divided by its own sum, LSE in log2 units) that the request's merge
+// tree folds inside this same kernel (finish_split).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -68,8 +69,10 @@ struct DecodeParams {
   const char* v_pages;
   char* out;
   float* lse;
-  float* part_o;
-  float* part_lse;
+  float* part_o;        // [slots][G][D]
+  float* part_lse;      // [slots][G], log2 units
+  const int32_t* nodes; // merge nodes [num_nodes][FI_NODE_STRIDE]
+  int32_t* counters;    // arrivals per merge node, 0 between runs
   int64_t page_stride;  // bytes between consecutive physical pages
   int32_t head_stride;  // bytes between KV heads inside a page
   int32_t num_qo_heads;
@@ -174,18 +177,215 @@ struct Row {
   static_assert(kLoads >= 1, "row shorter than 128 bytes");
 };
 
-// Occupancy and ring depth. The ring has 2 stages (8 KiB of K/V per wave at
-// bf16, d 128), read back and refilled together. Deeper rings were measured
-// slower on MI355X: with 4 stages (16 KiB per wave) more requests queue at
-// the memory controllers and the skewed batch lost ~4% bandwidth.
+// Cross-lane exchanges over lane bits 5, 4 and 3 without the LDS path.
+// permlane32_swap(x, y) swaps the upper 32 lanes of x with the lower 32 lanes
+// of y; the sum of the two swapped registers is, in lanes 0..31, x + x's
+// value in lane l+32, and in lanes 32..63, y + y's value in lane l-32.
+// permlane16_swap does the same for odd and even 16-lane rows; a DPP row
+// rotate by 8 reads lane l ^ 8.
+__device__ __forceinline__ float swap_sum32(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_sum16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float row_ror8(float x) {
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xF, 0xF, false));
+}
+// max / sum over the 8 lanes l, l^8, l^16, ..., l^56 (the same `sub`)
+__device__ __forceinline__ float group_max8(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmaxf(x, row_ror8(x));
+}
+__device__ __forceinline__ float group_sum8(float x) {
+  x = swap_sum32(x, x);
+  x = swap_sum16(x, x);
+  return x + row_ror8(x);
+}
+
+// Partial states cross XCDs, whose L2 caches are private. Every store and
+// load of a partial is an agent-scope relaxed atomic, which gfx950 issues
+// with the sc1 cache policy: the store writes through to the device-coherent
+// level and the load reads from it, so no L2 writeback or invalidation
+// (what an agent-scope fence costs, once per wave) is needed. Pairs of floats
+// move as one 64-bit access.
+__device__ __forceinline__ void store_shared(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_shared2(float* p, float a, float b) {
+  const uint64_t u = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_shared(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_shared2(const float* p) {
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
+
+// Completes the merge tree of a cut request after this wave wrote its chunk's
+// partial state. Each node counts its children's arrivals; the wave whose
+// arrival completes a node merges the node's children (in slot order, so the
+// result does not depend on which wave arrives last), resets the counter for
+// the next run, and reports the merged state to the parent, or writes the
+// output at the root. Before its arrival is counted the wave waits for its
+// partial stores to complete (vmcnt 0): write-through stores complete only
+// once they are visible device-wide. The merging wave issues its loads only
+// after the counter read that elected it has returned.
+//
+// The merge (the closed form for softmax over a union of disjoint token sets,
+// in log2 units) is latency-bound and often the last thing a kernel does, so
+// its loads go out in as few rounds as possible. Round one reads every
+// child's LSE (value i = child * G + head in lane i % 64) together with the
+// outputs of the first kB children; the per-head maximum and weight sum come
+// from butterfly reductions over the lanes of one head (lanes equal mod G),
+// and the weights go to LDS (s_w, FI_MERGE_FAN_IN * G floats; zero past the
+// last child). Outputs move as float pairs: lane l takes floats 2l + 128c
+// (c < NC) of a slot's G*D block, so each load covers 512 contiguous bytes.
+// The wave is its whole work-group and a wave's LDS accesses execute in
+// order, so the weights need only a compiler barrier, not s_barrier (whose
+// fence would wait for the output loads still in flight).
+template <bool kBF16, int D, int G>
+__device__ void finish_split(const DecodeParams& p, int node, int lane, float* s_w) {
+  constexpr int kF = G * D;                           // floats per slot
+  constexpr int NC = (kF / 2 + 63) / 64;              // float pairs per lane
+  constexpr int kV = (FI_MERGE_FAN_IN * G + 63) / 64; // LSE values per lane
+  constexpr int kB = 64 / NC < 16 ? 64 / NC : 16;     // children in round one
+  static_assert(kB <= FI_MERGE_FAN_IN, "round one reads past the weights");
+  int hc[NC];  // query head (within the group) of each pair of this lane
+#pragma unroll
+  for (int c = 0; c < NC; ++c) hc[c] = (2 * lane + 128 * c) / D;
+  for (;;) {
+    // the node's fields are read-only: fetch them with the arrival
+    const int32_t* nd = p.nodes + (int64_t)node * FI_NODE_STRIDE;
+    const int count = nd[FI_NODE_COUNT];
+    const int sb = nd[FI_NODE_SLOT_BEGIN];
+    const int parent = nd[FI_NODE_PARENT];
+    const int out_slot = nd[FI_NODE_OUT_SLOT];
+    const int b = nd[FI_NODE_REQUEST];
+    const int kvh = nd[FI_NODE_KV_HEAD];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(p.counters + node, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != count - 1) return;
+    if (lane == 0) __hip_atomic_store(p.counters + node, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    float sv[kV];
+#pragma unroll
+    for (int j = 0; j < kV; ++j) {
+      const int i = lane + 64 * j;
+      sv[j] = i < count * G ? load_shared(p.part_lse + (int64_t)sb * G + i) : -INFINITY;
+    }
+    float2 v[kB][NC];  // children past the last re-read it, with weight 0
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const float* src = p.part_o + (int64_t)(sb + min(i, count - 1)) * kF;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int f = 2 * lane + 128 * c;
+        v[i][c] = (kF >= 128 || f < kF) ? load_shared2(src + f) : make_float2(0.f, 0.f);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kV; ++j) mx = fmaxf(mx, sv[j]);
+#pragma unroll
+    for (int o = G; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float ws = 0.f;
+#pragma unroll
+    for (int j = 0; j < kV; ++j) {
+      const float w = sv[j] == -INFINITY ? 0.f : exp2_fast(sv[j] - mx);
+      s_w[lane + 64 * j] = w;
+      ws += w;
+    }
+#pragma unroll
+    for (int o = G; o < 64; o <<= 1) ws += __shfl_xor(ws, o);
+    asm volatile("" ::: "memory");
+    // lane h < G now holds the maximum and weight sum of head h
+
+    float2 acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const float w = s_w[i * G + hc[c]];
+        acc[c].x = __builtin_fmaf(w, v[i][c].x, acc[c].x);
+        acc[c].y = __builtin_fmaf(w, v[i][c].y, acc[c].y);
+      }
+    }
+#pragma unroll 8
+    for (int i = kB; i < count; ++i) {
+      const float* src = p.part_o + (int64_t)(sb + i) * kF;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int f = 2 * lane + 128 * c;
+        if (kF >= 128 || f < kF) {
+          const float w = s_w[i * G + hc[c]];
+          const float2 x = load_shared2(src + f);
+          acc[c].x = __builtin_fmaf(w, x.x, acc[c].x);
+          acc[c].y = __builtin_fmaf(w, x.y, acc[c].y);
+        }
+      }
+    }
+    asm volatile("" ::: "memory");  // s_w is rewritten by the next level
+    const float lse2 = mx + log2_fast(ws);  // valid in lanes h < G
+    if (parent < 0) {
+      const int64_t row0 = (int64_t)b * p.num_qo_heads + (int64_t)kvh * G;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int f = 2 * lane + 128 * c;
+        const float inv = 1.f / __shfl(ws, hc[c]);
+        if (kF >= 128 || f < kF) {
+          if constexpr (kBF16)
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.out) + row0 * D + f) =
+                pack_bf16(acc[c].x * inv, acc[c].y * inv);
+          else
+            *reinterpret_cast<float2*>(reinterpret_cast<float*>(p.out) + row0 * D + f) =
+                make_float2(acc[c].x * inv, acc[c].y * inv);
+        }
+      }
+      if (lane < G && p.lse) p.lse[row0 + lane] = lse2 * kLn2;
+      return;
+    }
+    float* dst = p.part_o + (int64_t)out_slot * kF;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int f = 2 * lane + 128 * c;
+      const float inv = 1.f / __shfl(ws, hc[c]);
+      if (kF >= 128 || f < kF) store_shared2(dst + f, acc[c].x * inv, acc[c].y * inv);
+    }
+    if (lane < G) store_shared(p.part_lse + (int64_t)out_slot * G + lane, lse2);
+    node = parent;
+  }
+}
+
+// Occupancy and ring depth. Streamed (nontemporal) K/V uses a 2-stage ring
+// (8 KiB of K/V per wave at bf16, d 128), read back and refilled together:
+// deeper rings were measured slower on MI355X there, since with 4 stages
+// (16 KiB per wave) more requests queue at the memory controllers and the
+// skewed batch lost ~4% bandwidth. When pages are shared between requests
+// the loads go through the caches, whose hits return early; a 4-stage ring
+// keeps enough bytes in flight for the misses and was ~20% faster on a
+// shared-prefix batch.
 // VGPRs per lane: accumulators G*NE, query words G*NW, two stages read back
 // from LDS (16*L), softmax state and ~48 for addressing and temporaries.
 // LDS per wave: kRing stages of 2*L KiB plus the page-id window. Waves per SIMD:
 // as many as both budgets allow, at most 3.
-template <bool kBF16, int D, int G>
+template <bool kBF16, int D, int G, bool kStream>
 struct Tune {
   using R = Row<kBF16, D>;
-  static constexpr int kRing = 2;
+  static constexpr int kRing = kStream ? 2 : 4;
   static constexpr int kRegs = G * R::kElems + G * R::kWords + 16 * R::kLoads + 2 * G + 48;
   static constexpr int kByRegs = kRegs <= 168 ? 3 : (kRegs <= 240 ? 2 : 1);
   static constexpr int kLdsPerWave = kRing * 2 * R::kLoads * 1024 + kIdWindow * 4;
@@ -210,22 +410,44 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   const int ntok = it[FI_ITEM_NUM_TOKENS];
   const int slot = it[FI_ITEM_SLOT];
   const int npg = it[FI_ITEM_NUM_PAGES];
+  const int first_pid = it[FI_ITEM_FIRST_PAGE];
+  const int node = it[FI_ITEM_MERGE_NODE];
   const int P = p.page_size;
+
+  if (ntok == 0) {  // a request with no pages: out = 0, lse = -inf
+    if (tg < G) {
+      const int64_t qrow = (int64_t)b * p.num_qo_heads + (int64_t)kvh * G + tg;
+#pragma unroll
+      for (int j = 0; j < R::kLoads; ++j)
+        *reinterpret_cast<uint4*>(p.out + qrow * R::kBytes + j * 128 + sub * 16) = make_uint4(0, 0, 0, 0);
+      if (sub == 0 && p.lse) p.lse[qrow] = -INFINITY;
+    }
+    return;
+  }
 
   // ---- page-id window in LDS: entry i is the id of page (wbase + i) of the
   // chunk. Reading ids from LDS keeps the id lookup off the vector-memory
   // counter, so fetching an id never waits for the K/V loads in flight.
+  // Every lane loads and stores unconditionally (indices clamped to the
+  // chunk), so the wait for these loads is the same on every path.
   __shared__ int s_ids[kIdWindow];
   int wbase = 0;
-  // Every lane loads and stores unconditionally (indices clamped to the
-  // chunk), so the wait for these loads is a plain vmcnt(0) on every path.
-  auto fill_window = [&](int base) {
+  int wreg[kIdWindow / 64];
+  auto load_window = [&](int base) {
 #pragma unroll
     for (int i = 0; i < kIdWindow / 64; ++i)
-      s_ids[i * 64 + lane] = p.page_ids[pb + min(base + i * 64 + lane, npg - 1)];
+      wreg[i] = p.page_ids[pb + min(base + i * 64 + lane, npg - 1)];
+  };
+  auto store_window = [&]() {
+#pragma unroll
+    for (int i = 0; i < kIdWindow / 64; ++i) s_ids[i * 64 + lane] = wreg[i];
     __syncthreads();
   };
-  fill_window(0);
+  auto fill_window = [&](int base) {
+    load_window(base);
+    store_window();
+  };
+  load_window(0);  // stored below, after the first K/V loads are on their way
 
   // ---- query fragments of the G heads (same columns as the K/V fragments)
   const int64_t qrow0 = (int64_t)b * p.num_qo_heads + (int64_t)kvh * G;
@@ -241,7 +463,6 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
       qw[h][j * 4 + 3] = v.w;
     }
   }
-
 
   // ---- load cursor: page-local index and slot of this lane's next token
   int cur_pl = tg / P;
@@ -302,7 +523,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   const int u_last_slot = last_step * 8 - u_last_pl * P;
   const int lane_off = tg * R::kBytes + sub * 16;
   const int64_t kvh_off = (int64_t)kvh * p.head_stride;
-  int u_pl = 0, u_slot = 0, u_cached_pl = -1, u_pid = 0;
+  int u_pl = 0, u_slot = 0, u_cached_pl = 0, u_pid = first_pid;
   auto issue_uniform = [&](int g, int stage) {
     const bool real = g < ngroups;
     const int pl = real ? u_pl : u_last_pl;
@@ -428,10 +649,23 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   // steps, all already in flight) with per-lane masking. Before stage s is
   // read, exactly the loads of the stages issued after it may be pending.
   constexpr int kPerStage = 2 * L;
+  // The first kRing steps lie in the chunk's first page when the page holds
+  // them all: issue them from the inline page id before the window is
+  // stored, so the item's first K/V loads overlap the page-table read.
+  if constexpr (kUniform) {
+    if (kRing * 8 <= P) {
 #pragma unroll
-  for (int s = 0; s < kRing; ++s) {
-    if constexpr (kUniform) issue_uniform(s, s);
-    else issue(s, s);
+      for (int s = 0; s < kRing; ++s) issue_uniform(s, s);
+      store_window();
+    } else {
+      store_window();
+#pragma unroll
+      for (int s = 0; s < kRing; ++s) issue_uniform(s, s);
+    }
+  } else {
+    store_window();
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) issue(s, s);
   }
   int g0 = 0;
   for (; g0 + kRing <= nfull; g0 += kRing) {
@@ -475,87 +709,131 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   // before the wave can exit and its LDS is handed to another workgroup.
   wait_vmcnt<0>();
 
-  // ---- merge the 8 lane-group states (lanes with equal `sub`)
+  // ---- combine the 8 lane groups (lanes with equal `sub` hold the same
+  // columns, for different tokens). The per-head maximum and sum are
+  // all-reduced over lane bits 3..5. The G x NE accumulators are then
+  // reduce-scattered: each stage hands half of the remaining values to the
+  // partner lane and keeps the other half plus the partner's copy of it, so
+  // after the stages over lane bits 5, 4 and 3, lane group tg holds the tg-th
+  // eighth of the flattened (head, element) block, fully summed. That eighth
+  // is exactly what the lane writes out.
+  float* stage = reinterpret_cast<float*>(&s_ring[0][0][0]);
+  static_assert(sizeof(s_ring) >= sizeof(float) * G * D, "ring too small to stage a partial");
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float M = m[h];
-    M = fmaxf(M, __shfl_xor(M, 8));
-    M = fmaxf(M, __shfl_xor(M, 16));
-    M = fmaxf(M, __shfl_xor(M, 32));
+    const float M = group_max8(m[h]);
     const float f = m[h] == -INFINITY ? 0.f : exp2_fast(m[h] - M);
-    float lh = l[h] * f;
-    lh += __shfl_xor(lh, 8);
-    lh += __shfl_xor(lh, 16);
-    lh += __shfl_xor(lh, 32);
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      float a = acc[h][e] * f;
-      a += __shfl_xor(a, 8);
-      a += __shfl_xor(a, 16);
-      a += __shfl_xor(a, 32);
-      acc[h][e] = a;
-    }
+    l[h] = group_sum8(l[h] * f);
     m[h] = M;
-    l[h] = lh;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[h][e] *= f;
+  }
+  constexpr int V = G * NE;   // values per lane before the reduce-scatter
+  constexpr int VB = V / 8;   // and after
+  static_assert(VB <= NE && NE % VB == 0, "a lane's eighth must lie in one head");
+  float* a = &acc[0][0];
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) a[i] = swap_sum32(a[i], a[i + V / 2]);
+#pragma unroll
+  for (int i = 0; i < V / 4; ++i) a[i] = swap_sum16(a[i], a[i + V / 4]);
+  {
+    const bool hi = (lane & 8) != 0;
+#pragma unroll
+    for (int i = 0; i < VB; ++i) {
+      const float send = hi ? a[i] : a[i + VB];
+      const float keep = hi ? a[i + VB] : a[i];
+      a[i] = keep + row_ror8(send);
+    }
   }
 
-  // ---- epilogue: lane group tg writes query head kvh*G + tg
-  if (tg < G) {
-    float o[NE];
+  // ---- epilogue: lane (sub, tg) holds elements e0 .. e0+VB-1 of head hq
+  {
+    constexpr int PL = R::kPerLoad;
+    constexpr int SEG = VB < PL ? VB : PL;  // elements per contiguous piece
+    const int hq = tg * VB / NE;
+    const int e0 = tg * VB % NE;
     float mh = 0.f, lh = 1.f;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      if (tg == h) {
+      if (h == hq) {
         mh = m[h];
         lh = l[h];
-#pragma unroll
-        for (int e = 0; e < NE; ++e) o[e] = acc[h][e];
       }
     }
     const float inv = 1.f / lh;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) o[e] *= inv;
-    const int64_t qrow = qrow0 + tg;
-    if (slot < 0) {
-      char* dst = p.out + qrow * R::kBytes + sub * 16;
+    for (int i = 0; i < VB; ++i) a[i] *= inv;
+    const int64_t qrow = qrow0 + hq;
+    const bool lse_lane = e0 == 0 && sub == 0;
 #pragma unroll
-      for (int j = 0; j < L; ++j) {
-        uint4 v;
+    for (int sgi = 0; sgi < VB / SEG; ++sgi) {
+      const int e = e0 + sgi * SEG;
+      // element e sits at dim (e / PL) * (128 / eb) + sub * PL + e % PL
+      const int dim = (e / PL) * (128 / R::kElemBytes) + sub * PL + e % PL;
+      const float* x = a + sgi * SEG;
+      if (slot < 0) {
+        char* dst = p.out + qrow * R::kBytes + dim * R::kElemBytes;
         if constexpr (kBF16) {
-          v.x = pack_bf16(o[j * 8 + 0], o[j * 8 + 1]);
-          v.y = pack_bf16(o[j * 8 + 2], o[j * 8 + 3]);
-          v.z = pack_bf16(o[j * 8 + 4], o[j * 8 + 5]);
-          v.w = pack_bf16(o[j * 8 + 6], o[j * 8 + 7]);
+          if constexpr (SEG == 1) {
+            *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(pack_bf16(x[0], 0.f) & 0xFFFFu);
+          } else if constexpr (SEG == 2) {
+            *reinterpret_cast<uint32_t*>(dst) = pack_bf16(x[0], x[1]);
+          } else if constexpr (SEG == 4) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+          } else {
+            *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]),
+                                                        pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7]));
+          }
         } else {
-          v.x = __float_as_uint(o[j * 4 + 0]);
-          v.y = __float_as_uint(o[j * 4 + 1]);
-          v.z = __float_as_uint(o[j * 4 + 2]);
-          v.w = __float_as_uint(o[j * 4 + 3]);
+          if constexpr (SEG == 1) *reinterpret_cast<float*>(dst) = x[0];
+          else if constexpr (SEG == 2) *reinterpret_cast<float2*>(dst) = make_float2(x[0], x[1]);
+          else *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
         }
-        *reinterpret_cast<uint4*>(dst + j * 128) = v;
-      }
-      if (sub == 0 && p.lse) p.lse[qrow] = (mh + log2_fast(lh)) * kLn2;
-    } else {
-      const int64_t prow = (int64_t)slot * p.num_qo_heads + (int64_t)kvh * G + tg;
-      float* dst = p.part_o + prow * D;
+      } else {
+        // stage the G x D partial in the drained ring (row hq = head hq)
+        float* d0 = stage + hq * D + dim;
+        if constexpr (SEG == 1) *d0 = x[0];
+        else if constexpr (SEG == 2) *reinterpret_cast<float2*>(d0) = make_float2(x[0], x[1]);
+        else {
 #pragma unroll
-      for (int j = 0; j < L; ++j) {
-        // elements j*kPerLoad .. +kPerLoad-1 sit at dims j*(128/eb) + sub*kPerLoad
-        constexpr int PL = R::kPerLoad;
-        float* d0 = dst + j * (128 / R::kElemBytes) + sub * PL;
-#pragma unroll
-        for (int c = 0; c < PL; c += 4)
-          *reinterpret_cast<float4*>(d0 + c) =
-              make_float4(o[j * PL + c], o[j * PL + c + 1], o[j * PL + c + 2], o[j * PL + c + 3]);
+          for (int c = 0; c < SEG; c += 4)
+            *reinterpret_cast<float4*>(d0 + c) = make_float4(x[c], x[c + 1], x[c + 2], x[c + 3]);
+        }
       }
-      if (sub == 0) p.part_lse[prow] = mh + log2_fast(lh);
     }
+    if (lse_lane) {
+      if (slot < 0) {
+        if (p.lse) p.lse[qrow] = (mh + log2_fast(lh)) * kLn2;
+      } else {
+        store_shared(p.part_lse + (int64_t)slot * G + hq, mh + log2_fast(lh));
+      }
+    }
+  }
+  if (slot >= 0) {
+    // Write the staged partial out as float pairs, lane l taking floats
+    // 2l + 128c: each store covers 512 contiguous bytes, whole lines, which
+    // matters because these stores write through to HBM (partial lines would
+    // cost a read-modify-write each). One wave is the whole work-group and
+    // its LDS accesses execute in order, so a compiler barrier suffices.
+    asm volatile("" ::: "memory");
+    constexpr int kF = G * D;
+    float* dst = p.part_o + (int64_t)slot * kF;
+#pragma unroll
+    for (int c = 0; c < (kF / 2 + 63) / 64; ++c) {
+      const int f = 2 * lane + 128 * c;
+      if (kF >= 128 || f < kF) {
+        const float2 x = *reinterpret_cast<const float2*>(stage + f);
+        store_shared2(dst + f, x.x, x.y);
+      }
+    }
+    static_assert(kIdWindow >= FI_MERGE_FAN_IN * G, "merge weights reuse the page-id window");
+    finish_split<kBF16, D, G>(p, node, lane, reinterpret_cast<float*>(s_ids));
   }
 }
 
 template <bool kBF16, int D, int G, bool kStream>
 hipError_t launch_variant(const DecodeParams& prm, int64_t num_items, hipStream_t stream) {
-  using T = Tune<kBF16, D, G>;
+  using T = Tune<kBF16, D, G, kStream>;
   if (prm.page_size % 8 == 0)
     hipLaunchKernelGGL((decode_bsr_kernel<kBF16, D, G, T::kRing, T::kWaves, kStream, true>),
                        dim3((uint32_t)num_items), dim3(64), 0, stream, prm);
@@ -599,6 +877,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   prm.lse = a.lse;
   prm.part_o = a.part_o;
   prm.part_lse = a.part_lse;
+  prm.nodes = a.nodes;
+  prm.counters = a.counters;
   prm.head_stride = a.page_size * row;
   prm.page_stride = (int64_t)a.num_kv_heads * a.page_size * row;
   prm.num_qo_heads = a.num_qo_heads;

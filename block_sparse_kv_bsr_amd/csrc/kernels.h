@@ -15,24 +15,15 @@ struct DecodeArgs {
   const void* v_pages;
   void* out;                // [batch, num_qo_heads, head_dim]
   float* lse;               // [batch, num_qo_heads] natural log, or null
-  float* part_o;            // [slots, num_qo_heads, head_dim]
-  float* part_lse;          // [slots, num_qo_heads], log2 units
+  float* part_o;            // [slots, group, head_dim]
+  float* part_lse;          // [slots, group], log2 units
+  const int32_t* nodes;     // merge nodes [num_nodes][FI_NODE_STRIDE]
+  int32_t* counters;        // arrivals per merge node
   int64_t num_items;
   int32_t num_qo_heads, num_kv_heads, head_dim, page_size, group;
   bool bf16;
   bool stream_kv;           // nontemporal K/V loads (no page listed twice)
   float sm_scale;
-};
-
-struct MergePartialArgs {
-  const int32_t* tasks;     // device, [num_tasks][FI_MERGE_STRIDE]
-  const float* part_o;
-  const float* part_lse;
-  void* out;
-  float* lse;
-  int64_t num_tasks;
-  int32_t num_qo_heads, head_dim;
-  bool bf16;
 };
 
 struct MergeTwoArgs {
@@ -48,7 +39,6 @@ struct MergeTwoArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_merge_partials(const MergePartialArgs& a, hipStream_t stream);
 hipError_t launch_merge_two(const MergeTwoArgs& a, hipStream_t stream);
 
 }  // namespace fi

@@ -9,13 +9,9 @@
 //     s = M + log sum_i e^(s_i - M),   v = sum_i e^(s_i - M) v_i / sum_i e^(s_i - M)
 // with M = max_i s_i; an empty set has s = -inf and weight zero.
 //
-// Two kernels:
-//  * merge_partials_kernel finishes the decode run: one block per (request,
-//    query head) folds that request's partial slots (fp32, log2 units) into
-//    the output (dtype) and the natural-log LSE. A request with no pages gets
-//    out = 0 and lse = -inf.
-//  * merge_two_kernel is the standalone elementwise merge of two state arrays
-//    (natural-log LSE); each thread handles one 16-byte column of a row.
+// merge_two_kernel is the standalone elementwise merge of two state arrays
+// (natural-log LSE); each thread handles one 16-byte column of a row. (The
+// decode run merges its own partial states inside the decode kernel.)
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -34,89 +30,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2_t v = {(__bf16)a, (__bf16)b};  // round to nearest even
   return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
-// One 256-thread block per (task, query head). Thread t owns float4 column
-// t % kCols of the output row and the partial slots i = t / kCols (mod
-// kGroups), so every thread keeps several independent loads in flight; the
-// kGroups partial sums are combined through LDS at the end.
-template <bool kBF16, int D>
-__global__ __launch_bounds__(256) void merge_partials_kernel(MergePartialArgs a) {
-  constexpr int kCols = D / 4;          // float4 columns per row
-  constexpr int kGroups = 256 / kCols;  // slot groups
-  __shared__ float s_max[4];
-  __shared__ float4 s_acc[kGroups][kCols];
-  __shared__ float s_w[kGroups];
-  const int64_t row = blockIdx.x;
-  const int Hq = a.num_qo_heads;
-  const int64_t task = row / Hq;
-  const int h = (int)(row - task * Hq);
-  const int32_t* tk = a.tasks + task * FI_MERGE_STRIDE;
-  const int b = tk[FI_MERGE_REQUEST];
-  const int s0 = tk[FI_MERGE_SLOT_BEGIN];
-  const int n = tk[FI_MERGE_NUM_SLOTS];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int col = t % kCols, grp = t / kCols;
-
-  float M = -INFINITY;
-  for (int i = t; i < n; i += 256) M = fmaxf(M, a.part_lse[(int64_t)(s0 + i) * Hq + h]);
-  M = wave_max(M);
-  if (lane == 0) s_max[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float wsum = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll 4
-    for (int i = grp; i < n; i += kGroups) {
-      const int64_t prow = (int64_t)(s0 + i) * Hq + h;
-      const float si = a.part_lse[prow];
-      const float w = si == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(si - M);
-      const float4 o = *reinterpret_cast<const float4*>(a.part_o + prow * D + col * 4);
-      wsum += w;
-      acc.x = __builtin_fmaf(w, o.x, acc.x);
-      acc.y = __builtin_fmaf(w, o.y, acc.y);
-      acc.z = __builtin_fmaf(w, o.z, acc.z);
-      acc.w = __builtin_fmaf(w, o.w, acc.w);
-    }
-  }
-  s_acc[grp][col] = acc;
-  if (col == 0) s_w[grp] = wsum;
-  __syncthreads();
-  if (grp != 0) return;
-  float wt = 0.f;
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) wt += s_w[g];
-  float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
-    const float4 v = s_acc[g][col];
-    r.x += v.x;
-    r.y += v.y;
-    r.z += v.z;
-    r.w += v.w;
-  }
-  const bool empty = M == -INFINITY;
-  const float inv = empty ? 0.f : 1.f / wt;
-  const int64_t orow = (int64_t)b * Hq + h;
-  if constexpr (kBF16) {
-    uint2 v;
-    v.x = pack_bf16(r.x * inv, r.y * inv);
-    v.y = pack_bf16(r.z * inv, r.w * inv);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow * D + col * 4) = v;
-  } else {
-    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * D + col * 4) =
-        make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
-  }
-  if (col == 0 && a.lse)
-    a.lse[orow] = empty ? -INFINITY : (M + __builtin_amdgcn_logf(wt)) * kLn2;
 }
 
 // Elementwise merge of two state arrays. Thread = one 16-byte column of a row.
@@ -166,22 +79,6 @@ __global__ __launch_bounds__(256) void merge_two_kernel(MergeTwoArgs a) {
 }
 
 }  // namespace
-
-hipError_t launch_merge_partials(const MergePartialArgs& a, hipStream_t stream) {
-  if (a.num_tasks <= 0) return hipSuccess;
-  const int64_t rows = a.num_tasks * a.num_qo_heads;
-  const dim3 grid((uint32_t)rows), block(256);
-  if (a.bf16) {
-    if (a.head_dim == 128) hipLaunchKernelGGL((merge_partials_kernel<true, 128>), grid, block, 0, stream, a);
-    else if (a.head_dim == 64) hipLaunchKernelGGL((merge_partials_kernel<true, 64>), grid, block, 0, stream, a);
-    else return hipErrorInvalidValue;
-  } else {
-    if (a.head_dim == 128) hipLaunchKernelGGL((merge_partials_kernel<false, 128>), grid, block, 0, stream, a);
-    else if (a.head_dim == 64) hipLaunchKernelGGL((merge_partials_kernel<false, 64>), grid, block, 0, stream, a);
-    else return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
 
 hipError_t launch_merge_two(const MergeTwoArgs& a, hipStream_t stream) {
   if (a.num_rows <= 0) return hipSuccess;

@@ -14,7 +14,8 @@
 // first -- the longest-processing-time rule -- so that the hardware dispatcher,
 // which starts workgroups in grid order as slots free up, places long chunks
 // first and short requests into the gaps. Requests cut into several chunks
-// write partial (output, log-sum-exp) states that a merge kernel combines.
+// write partial (output, log-sum-exp) states; per KV head a small tree of
+// merge nodes (fan-in FI_MERGE_FAN_IN) combines them inside the same kernel.
 //
 // Plain C++17 with no HIP dependency: the planner is tested on CPU-only hosts.
 #include <algorithm>
@@ -180,41 +181,100 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
       }
     }
 
-    // ---- items, partial slots, merge tasks
+    // ---- items, partial slots, merge trees
     struct Item { int32_t f[FI_ITEM_STRIDE]; };
     std::vector<Item> items;
+    std::vector<int32_t>& nodes = p->nodes;
     int64_t slot = 0;
     int32_t max_chunks = 0, min_split = 0;
+    auto new_node = [&](int32_t count, int64_t slot_begin, int64_t out_slot, int32_t b,
+                        int32_t h, int32_t level) {
+      const int32_t id = (int32_t)(nodes.size() / FI_NODE_STRIDE);
+      int32_t f[FI_NODE_STRIDE] = {0};
+      f[FI_NODE_COUNT] = count;
+      f[FI_NODE_SLOT_BEGIN] = (int32_t)slot_begin;
+      f[FI_NODE_PARENT] = -1;
+      f[FI_NODE_OUT_SLOT] = (int32_t)out_slot;
+      f[FI_NODE_REQUEST] = b;
+      f[FI_NODE_KV_HEAD] = h;
+      f[FI_NODE_LEVEL] = level;
+      nodes.insert(nodes.end(), f, f + FI_NODE_STRIDE);
+      return id;
+    };
     for (int32_t b = 0; b < batch; ++b) {
       const int64_t n = npages[b];
       const int64_t k = n > 0 ? fi::ceil_div(n, C) : 0;
       max_chunks = std::max<int32_t>(max_chunks, (int32_t)k);
       if (k >= 2) min_split = min_split == 0 ? (int32_t)k : std::min<int32_t>(min_split, (int32_t)k);
-      if (k != 1) {
-        p->merge.insert(p->merge.end(), {b, (int32_t)slot, (int32_t)k, 0});
-      }
-      int64_t page0 = 0;
-      for (int64_t c = 0; c < k; ++c) {
-        // near-equal cut: the first (n % k) chunks get one page more
-        const int64_t np = n / k + (c < n % k ? 1 : 0);
-        const bool has_last = page0 + np == n;
-        const int64_t tok = has_last ? (np - 1) * page_size + kv_last_page_len[b]
-                                     : np * (int64_t)page_size;
+      if (k == 0) {  // no pages: one item per KV head writes out = 0, lse = -inf
         for (int32_t h = 0; h < num_kv_heads; ++h) {
+          Item it{};
+          it.f[FI_ITEM_REQUEST] = b;
+          it.f[FI_ITEM_KV_HEAD] = h;
+          it.f[FI_ITEM_PAGE_BEGIN] = kv_indptr[b];
+          it.f[FI_ITEM_SLOT] = -1;
+          it.f[FI_ITEM_MERGE_NODE] = -1;
+          items.push_back(it);
+        }
+        continue;
+      }
+      for (int32_t h = 0; h < num_kv_heads; ++h) {
+        // merge tree of (b, h): leaves take chunk partials in slots
+        // [leaf_base, leaf_base + k); each level groups FI_MERGE_FAN_IN children
+        const int64_t leaf_base = slot;
+        std::vector<int32_t> leaf_node(k, -1);
+        if (k >= 2) {
+          slot += k;
+          int64_t child_begin = leaf_base, nchild = k;
+          int32_t level = 0;
+          std::vector<int32_t> prev;
+          for (;;) {
+            const int64_t groups = fi::ceil_div(nchild, FI_MERGE_FAN_IN);
+            const bool root = groups == 1;
+            const int64_t out_base = root ? -1 : slot;
+            if (!root) slot += groups;
+            const int32_t first = (int32_t)(nodes.size() / FI_NODE_STRIDE);
+            for (int64_t g = 0; g < groups; ++g) {
+              const int64_t cnt = std::min<int64_t>(FI_MERGE_FAN_IN, nchild - g * FI_MERGE_FAN_IN);
+              new_node((int32_t)cnt, child_begin + g * FI_MERGE_FAN_IN, root ? -1 : out_base + g,
+                       b, h, level);
+            }
+            for (size_t i = 0; i < prev.size(); ++i)
+              nodes[(size_t)prev[i] * FI_NODE_STRIDE + FI_NODE_PARENT] =
+                  first + (int32_t)(i / FI_MERGE_FAN_IN);
+            if (level == 0)
+              for (int64_t c = 0; c < k; ++c) leaf_node[c] = first + (int32_t)(c / FI_MERGE_FAN_IN);
+            prev.clear();
+            for (int64_t g = 0; g < groups; ++g) prev.push_back(first + (int32_t)g);
+            if (root) break;
+            child_begin = out_base;
+            nchild = groups;
+            ++level;
+          }
+        }
+        int64_t page0 = 0;
+        for (int64_t c = 0; c < k; ++c) {
+          // near-equal cut: the first (n % k) chunks get one page more
+          const int64_t np = n / k + (c < n % k ? 1 : 0);
+          const bool has_last = page0 + np == n;
+          const int64_t tok = has_last ? (np - 1) * page_size + kv_last_page_len[b]
+                                       : np * (int64_t)page_size;
           Item it{};
           it.f[FI_ITEM_REQUEST] = b;
           it.f[FI_ITEM_KV_HEAD] = h;
           it.f[FI_ITEM_PAGE_BEGIN] = (int32_t)(kv_indptr[b] + page0);
           it.f[FI_ITEM_NUM_TOKENS] = (int32_t)tok;
-          it.f[FI_ITEM_SLOT] = k == 1 ? -1 : (int32_t)(slot + c);
+          it.f[FI_ITEM_SLOT] = k == 1 ? -1 : (int32_t)(leaf_base + c);
           it.f[FI_ITEM_CHUNK] = (int32_t)c;
           it.f[FI_ITEM_NUM_PAGES] = (int32_t)np;
+          it.f[FI_ITEM_FIRST_PAGE] = kv_indices[kv_indptr[b] + page0];
+          it.f[FI_ITEM_MERGE_NODE] = leaf_node[c];
           items.push_back(it);
+          page0 += np;
         }
-        page0 += np;
       }
-      if (k >= 2) slot += k;
     }
+    if (slot > INT32_MAX) return fail(FI_ERR_UNSUPPORTED, "too many partial states");
     // longest first; ties in (request, KV head, chunk) order
     std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
       if (a.f[FI_ITEM_NUM_TOKENS] != b.f[FI_ITEM_NUM_TOKENS])
@@ -234,24 +294,27 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
 
     // ---- workspace layout and host image of its uploaded part
     fi::WorkspaceLayout& ws = p->ws;
+    const int64_t nn = p->num_nodes();
     int64_t off = 0;
     ws.items = off;
     off = fi::align_up(off + (int64_t)p->items.size() * 4, 256);
-    ws.merge = off;
-    off = fi::align_up(off + (int64_t)p->merge.size() * 4, 256);
+    ws.nodes = off;
+    off = fi::align_up(off + (int64_t)nodes.size() * 4, 256);
+    ws.counters = off;
+    off = fi::align_up(off + nn * 4, 256);
     ws.page_ids = off;
     off = fi::align_up(off + nnz * 4, 256);
     ws.image_bytes = off;
     ws.part_o = off;
-    off = fi::align_up(off + p->num_slots * num_qo_heads * (int64_t)head_dim * 4, 256);
+    off = fi::align_up(off + p->num_slots * group * (int64_t)head_dim * 4, 256);
     ws.part_lse = off;
-    off = fi::align_up(off + p->num_slots * num_qo_heads * 4, 256);
+    off = fi::align_up(off + p->num_slots * group * 4, 256);
     ws.total_bytes = std::max<int64_t>(off, 256);
-    p->image.assign(ws.image_bytes, 0);
+    p->image.assign(ws.image_bytes, 0);  // counters start at 0
     if (!p->items.empty())
       std::memcpy(p->image.data() + ws.items, p->items.data(), p->items.size() * 4);
-    if (!p->merge.empty())
-      std::memcpy(p->image.data() + ws.merge, p->merge.data(), p->merge.size() * 4);
+    if (!nodes.empty())
+      std::memcpy(p->image.data() + ws.nodes, nodes.data(), nodes.size() * 4);
     if (nnz > 0) std::memcpy(p->image.data() + ws.page_ids, kv_indices, nnz * 4);
 
     *out_plan = p.release();
@@ -268,7 +331,7 @@ fi_status fi_plan_get_info(const fi_plan* p, fi_plan_info* info) {
   fi_plan_info r{};
   r.num_items = p->num_items();
   r.num_partial_slots = p->num_slots;
-  r.num_merge_tasks = p->num_merge();
+  r.num_merge_nodes = p->num_nodes();
   r.workspace_bytes = p->ws.total_bytes;
   r.total_kv_tokens = p->total_tokens;
   r.chunk_pages = p->chunk_pages;
@@ -292,10 +355,10 @@ fi_status fi_plan_work_list(const fi_plan* p, const int32_t** items, int64_t* nu
   return FI_OK;
 }
 
-fi_status fi_plan_merge_list(const fi_plan* p, const int32_t** tasks, int64_t* num_tasks) {
-  if (!p || !tasks || !num_tasks) return fi::fail(FI_ERR_INVALID_ARG, "NULL argument");
-  *tasks = p->merge.data();
-  *num_tasks = p->num_merge();
+fi_status fi_plan_merge_nodes(const fi_plan* p, const int32_t** nodes, int64_t* num_nodes) {
+  if (!p || !nodes || !num_nodes) return fi::fail(FI_ERR_INVALID_ARG, "NULL argument");
+  *nodes = p->nodes.data();
+  *num_nodes = p->num_nodes();
   return FI_OK;
 }
 

@@ -14,14 +14,15 @@ namespace fi {
 
 // Byte offsets of the sections of the device workspace. Each section starts
 // on a 256-byte boundary. The first `image_bytes` are copied from the host
-// (work items, merge tasks, page ids); the rest is written by the kernels
-// (partial outputs and their log-sum-exp values).
+// (work items, merge nodes, their arrival counters (zeros), page ids); the
+// rest is written by the kernel (partial outputs and their log-sum-exp).
 struct WorkspaceLayout {
   int64_t items = 0;      // int32 [num_items][FI_ITEM_STRIDE]
-  int64_t merge = 0;      // int32 [num_merge_tasks][FI_MERGE_STRIDE]
+  int64_t nodes = 0;      // int32 [num_nodes][FI_NODE_STRIDE]
+  int64_t counters = 0;   // int32 [num_nodes], 0 between runs
   int64_t page_ids = 0;   // int32 [nnz]
-  int64_t part_o = 0;     // float [num_slots][num_qo_heads][head_dim]
-  int64_t part_lse = 0;   // float [num_slots][num_qo_heads], log2 units
+  int64_t part_o = 0;     // float [num_slots][group][head_dim]
+  int64_t part_lse = 0;   // float [num_slots][group], log2 units
   int64_t image_bytes = 0;
   int64_t total_bytes = 0;
 };
@@ -44,14 +45,14 @@ struct fi_plan {
   int64_t shared_pages = 0;  // distinct physical pages listed more than once
   int64_t num_slots = 0;
   std::vector<int32_t> items;   // num_items * FI_ITEM_STRIDE
-  std::vector<int32_t> merge;   // num_merge_tasks * FI_MERGE_STRIDE
+  std::vector<int32_t> nodes;   // num_merge_nodes * FI_NODE_STRIDE
   std::vector<uint8_t> image;   // host copy of the uploaded part of the workspace
   fi::WorkspaceLayout ws;
   // Set by the launch layer.
   void* pinned = nullptr;        // pinned staging copy of `image`
   const void* uploaded_to = nullptr;
   int64_t num_items() const { return (int64_t)items.size() / FI_ITEM_STRIDE; }
-  int64_t num_merge() const { return (int64_t)merge.size() / FI_MERGE_STRIDE; }
+  int64_t num_nodes() const { return (int64_t)nodes.size() / FI_NODE_STRIDE; }
 };
 
 namespace fi {

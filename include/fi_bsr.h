@@ -96,8 +96,8 @@ typedef struct {
 
 typedef struct {
   int64_t num_items;         /* work items = (request, KV head, chunk) */
-  int64_t num_partial_slots; /* partial states, each num_qo_heads rows */
-  int64_t num_merge_tasks;   /* requests finished by the merge kernel */
+  int64_t num_partial_slots; /* partial states, each G rows (one KV-head group) */
+  int64_t num_merge_nodes;   /* nodes of the merge trees of cut requests */
   int64_t workspace_bytes;   /* device workspace fi_plan_upload needs */
   int64_t total_kv_tokens;   /* sum of active tokens over the batch */
   int32_t chunk_pages;       /* pages per chunk chosen by the planner */
@@ -115,19 +115,37 @@ enum {
   FI_ITEM_REQUEST = 0,    /* request b */
   FI_ITEM_KV_HEAD = 1,    /* KV head; query heads kvh*G .. kvh*G+G-1 */
   FI_ITEM_PAGE_BEGIN = 2, /* first page, as an index into kv_indices */
-  FI_ITEM_NUM_TOKENS = 3, /* tokens in this chunk (>= 1) */
+  FI_ITEM_NUM_TOKENS = 3, /* tokens in this chunk; 0 = a request with no
+                             pages (the item writes out = 0, lse = -inf) */
   FI_ITEM_SLOT = 4,       /* -1: writes out/lse directly; else partial slot */
   FI_ITEM_CHUNK = 5,      /* chunk number within the request */
   FI_ITEM_NUM_PAGES = 6,  /* pages in this chunk */
-  FI_ITEM_STRIDE = 8      /* int32 per item */
+  FI_ITEM_FIRST_PAGE = 7, /* physical id of the chunk's first page (a copy of
+                             kv_indices[FI_ITEM_PAGE_BEGIN], so the first
+                             loads need no page-table read); 0 if no pages */
+  FI_ITEM_MERGE_NODE = 8, /* merge node the partial reports to; -1 if none */
+  FI_ITEM_STRIDE = 16     /* int32 per item */
 };
 
-/* Fields of one merge task in the list returned by fi_plan_merge_list. */
+/*
+ * Fields of one merge node in the list returned by fi_plan_merge_nodes.
+ * A request cut into k chunks has, per KV head, a tree of merge nodes with
+ * at most FI_MERGE_FAN_IN children each: the leaves' children are the chunk
+ * partials, an inner node's children are its child nodes' merged states, and
+ * the root writes the request's output. The wave that brings a node's last
+ * child merges the children in slot order (so the result does not depend on
+ * arrival order) and reports to the parent.
+ */
 enum {
-  FI_MERGE_REQUEST = 0,
-  FI_MERGE_SLOT_BEGIN = 1, /* the request's partial slots are contiguous */
-  FI_MERGE_NUM_SLOTS = 2,  /* 0 for a request with no pages */
-  FI_MERGE_STRIDE = 4
+  FI_NODE_COUNT = 0,      /* children */
+  FI_NODE_SLOT_BEGIN = 1, /* children's partial slots: [begin, begin + count) */
+  FI_NODE_PARENT = 2,     /* parent node; -1 for the root */
+  FI_NODE_OUT_SLOT = 3,   /* slot the merged state goes to; -1 for the root */
+  FI_NODE_REQUEST = 4,
+  FI_NODE_KV_HEAD = 5,
+  FI_NODE_LEVEL = 6,      /* 0 for nodes whose children are chunks */
+  FI_NODE_STRIDE = 8,
+  FI_MERGE_FAN_IN = 32
 };
 
 /*
@@ -165,13 +183,14 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
 fi_status fi_plan_get_info(const fi_plan* plan, fi_plan_info* info);
 
 /* Host view of the work list (num_items * FI_ITEM_STRIDE int32, in launch
- * order) and of the merge tasks (num_merge_tasks * FI_MERGE_STRIDE int32).
+ * order) and of the merge nodes (num_merge_nodes * FI_NODE_STRIDE int32).
  * Valid until fi_plan_destroy. */
 fi_status fi_plan_work_list(const fi_plan* plan, const int32_t** items, int64_t* num_items);
-fi_status fi_plan_merge_list(const fi_plan* plan, const int32_t** tasks, int64_t* num_tasks);
+fi_status fi_plan_merge_nodes(const fi_plan* plan, const int32_t** nodes, int64_t* num_nodes);
 
 /*
- * Copy the work list, merge tasks and page ids into the caller's device
+ * Copy the work list, merge nodes (with their arrival counters set to 0) and
+ * page ids into the caller's device
  * workspace (asynchronous host-to-device copy on `stream` from pinned host
  * memory owned by the plan). workspace must be 256-byte aligned and at least
  * info.workspace_bytes long. Call once per plan; the uploaded plan may then
@@ -181,10 +200,14 @@ fi_status fi_plan_upload(fi_plan* plan, void* workspace, size_t workspace_bytes,
                          fi_stream_t stream);
 
 /*
- * Run decode attention for an uploaded plan on `stream` (one decode kernel
- * over the work items, then one merge kernel for requests that were cut or
- * are empty). No host synchronisation; safe to capture in a HIP graph once
- * uploaded.
+ * Run decode attention for an uploaded plan on `stream`: one kernel launch.
+ * Each work item attends over its chunk; an item of a request cut into
+ * several chunks writes a partial (output, log-sum-exp) state and reports to
+ * its merge node, and the item that completes a node merges that node's
+ * children (see FI_NODE_*), up to the root which writes out/lse. No host
+ * synchronisation; safe to capture in a HIP graph once uploaded. Calls that
+ * use the same workspace must not overlap (the merge counters live there);
+ * the kernel leaves every counter at 0 when it finishes.
  *
  * q        device [batch, num_qo_heads, head_dim] dtype, 16-byte aligned
  * k_pages  device [num_pool_pages, num_kv_heads, page_size, head_dim] dtype
@@ -197,21 +220,6 @@ fi_status fi_plan_upload(fi_plan* plan, void* workspace, size_t workspace_bytes,
 fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
                         const void* v_pages, void* out, float* lse, float sm_scale,
                         void* workspace, size_t workspace_bytes, fi_stream_t stream);
-
-/*
- * The two launches of fi_decode_run, exposed separately so a caller can put
- * work or timing events between them: fi_decode_attend runs the decode kernel
- * (requests of one chunk get their final out/lse; cut requests leave partial
- * states in the workspace) and fi_decode_merge runs the merge kernel that
- * finishes cut and empty requests. fi_decode_attend followed by
- * fi_decode_merge on one stream, with the same arguments, is exactly
- * fi_decode_run. Arguments and errors as for fi_decode_run.
- */
-fi_status fi_decode_attend(const fi_plan* plan, const void* q, const void* k_pages,
-                           const void* v_pages, void* out, float* lse, float sm_scale,
-                           void* workspace, size_t workspace_bytes, fi_stream_t stream);
-fi_status fi_decode_merge(const fi_plan* plan, void* out, float* lse, void* workspace,
-                          size_t workspace_bytes, fi_stream_t stream);
 
 /*
  * Merge two attention states over disjoint token sets (the closed form of

@@ -81,7 +81,7 @@ def test_small_default_plan(case):
 @pytest.mark.parametrize("case", SMALL[:8] + SMALL[10:14], ids=lambda c: f"s{c[0]}_split")
 def test_small_forced_split(case):
     """A tiny chunk length forces many chunks per request, partial states and
-    the merge kernel, including chunks that end inside the 8-token step."""
+    the in-kernel merge, including chunks that end inside the 8-token step."""
     seed, B, L, Hq, Hkv, d, P, dt, ee = case
     w = random_workload(seed, B, L, Hq, Hkv, d, P, dt, empty_every=ee)
     run_case(w, what=f"split{seed}", fixed_chunk_tokens=max(P, 20))
@@ -105,6 +105,35 @@ def test_config_full_size(cfg):
     p, _, _ = run_case(w, device_values=cfg > 1, what=f"config{cfg}")
     if cfg == 4:
         assert p.info["min_chunks_split_request"] >= 64
+
+
+@pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 128, 8, 2), ("bf16", 64, 4, 4),
+                                           ("f32", 64, 16, 2), ("f32", 128, 8, 8)])
+def test_merge_tree_levels(dtype, d, hq, hkv):
+    """One-token chunks on page size 1 cut requests into up to 1100 chunks:
+    in-kernel merge trees of one, two and three levels, a leaf node with a
+    single child (33 chunks), every per-lane merge width, and repeated runs
+    on one workspace. The runs alternate between two query sets, so a merge
+    that read a partial state left in some cache by the previous run, or a
+    counter not returned to zero, would give a wrong result."""
+    lens = [70, 33, 32, 1, 0, 1100, 2]
+    w = random_workload(41, len(lens), 0, hq, hkv, d, 1, dtype, lens=lens)
+    p, (q, k, v), (o0, l0) = run_case(w, what=f"tree-{dtype}-d{d}-G{hq // hkv}",
+                                      fixed_chunk_tokens=1)
+    assert p.merge_nodes()[:, 6].max() == 2
+    q2 = torch.flip(q, dims=[0]).contiguous()
+    o2, l2 = fb.decode(q2, k, v, p)
+    torch.cuda.synchronize()
+    O2, LSE2 = oa.decode_attention(q2.float().cpu().numpy(), k.float().cpu().numpy(),
+                                   v.float().cpu().numpy(), w.kv_indptr, w.kv_indices,
+                                   w.last_page_len, w.sm_scale)
+    compare(o2.double().cpu().numpy(), l2.double().cpu().numpy(), O2, LSE2, dtype == "bf16",
+            "tree-q2")
+    for i in range(4):
+        qi, oi, li = (q, o0, l0) if i % 2 == 0 else (q2, o2, l2)
+        o1, l1 = fb.decode(qi, k, v, p)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, oi) and torch.equal(l1, li), f"run {i}"
 
 
 def test_deterministic_for_fixed_plan():

@@ -1,5 +1,5 @@
 """The host planner (fi_plan_create) on a CPU-only host: coverage, ordering,
-slots, merge tasks and the split-then-merge result in float64."""
+slots, merge trees and the split-then-merge result in float64."""
 import math
 
 import numpy as np
@@ -7,11 +7,12 @@ import pytest
 from hypothesis import given, settings, strategies as st
 
 import block_sparse_kv_bsr_amd as fb
-from block_sparse_kv_bsr_amd.binding import ITEM_STRIDE
+from block_sparse_kv_bsr_amd.binding import ITEM_STRIDE, MERGE_FAN_IN, NODE_STRIDE
 from block_sparse_kv_bsr_amd.workloads import random_workload, workload
 import oracle.attention as oa
 
-I_REQ, I_KVH, I_PB, I_NTOK, I_SLOT, I_CHUNK, I_NP = range(7)
+I_REQ, I_KVH, I_PB, I_NTOK, I_SLOT, I_CHUNK, I_NP, I_FIRST, I_NODE = range(9)
+N_COUNT, N_SB, N_PARENT, N_OUT, N_REQ, N_KVH, N_LEVEL = range(7)
 
 
 def make_plan(w, **opts):
@@ -20,63 +21,97 @@ def make_plan(w, **opts):
 
 
 def check_plan(w, p):
-    """Every property a valid plan must have; returns (items, merges)."""
+    """Every property a valid plan must have; returns (items, nodes)."""
     info = p.info
-    items, merges = p.work_list(), p.merge_list()
+    items, nodes = p.work_list(), p.merge_nodes()
     P = w.page_size
     assert items.shape[1] == ITEM_STRIDE and info["num_items"] == len(items)
+    assert nodes.shape[1] == NODE_STRIDE and info["num_merge_nodes"] == len(nodes)
     assert info["total_kv_tokens"] == int(w.kv_lens().sum())
     # longest first, ties by (request, kv head, chunk)
     keys = [(-r[I_NTOK], r[I_REQ], r[I_KVH], r[I_CHUNK]) for r in items]
     assert keys == sorted(keys)
-    nchunks = {}
+    S = info["num_partial_slots"]
+    fed = np.zeros(S, dtype=np.int64)   # producers per partial slot
+    roots = {}
     for b in range(w.batch):
         s, t = int(w.kv_indptr[b]), int(w.kv_indptr[b + 1])
         for h in range(w.num_kv_heads):
             mine = sorted((r for r in items if r[I_REQ] == b and r[I_KVH] == h),
                           key=lambda r: r[I_CHUNK])
             if t == s:
-                assert not mine
+                # a request with no pages: one item that writes out = 0, lse = -inf
+                assert len(mine) == 1 and mine[0][I_NTOK] == 0
+                assert mine[0][I_SLOT] == -1 and mine[0][I_NODE] == -1
                 continue
             # chunks tile the page list exactly once, in order
             pos = s
             for c, r in enumerate(mine):
                 assert r[I_CHUNK] == c and r[I_PB] == pos and r[I_NP] >= 1
+                assert r[I_FIRST] == w.kv_indices[r[I_PB]]  # first physical page, inline
                 pos += r[I_NP]
                 last = pos == t
                 want = (r[I_NP] - 1) * P + int(w.last_page_len[b]) if last else r[I_NP] * P
                 assert r[I_NTOK] == want
             assert pos == t
             assert sum(r[I_NTOK] for r in mine) == w.kv_len(b)
-            nchunks[b] = len(mine)
             if len(mine) == 1:
-                assert mine[0][I_SLOT] == -1
-    # merge tasks: exactly the requests with 0 or >= 2 chunks, disjoint slot ranges
-    seen = set()
-    task_of = {int(m[0]): m for m in merges}
-    for b in range(w.batch):
-        k = nchunks.get(b, 0)
-        if k == 1:
-            assert b not in task_of
-            continue
-        m = task_of[b]
-        assert m[2] == k
-        for c in range(k):
-            sl = int(m[1]) + c
-            assert sl not in seen
-            seen.add(sl)
-            its = [r for r in items if r[I_REQ] == b and r[I_CHUNK] == c]
-            assert len(its) == w.num_kv_heads and all(r[I_SLOT] == sl for r in its)
-    assert len(seen) == info["num_partial_slots"]
-    # partial-slot bound: sum_b ceil(n_b / C) <= B + N / C
+                assert mine[0][I_SLOT] == -1 and mine[0][I_NODE] == -1
+                continue
+            for r in mine:
+                n = nodes[r[I_NODE]]
+                assert n[N_LEVEL] == 0 and n[N_REQ] == b and n[N_KVH] == h
+                assert n[N_SB] <= r[I_SLOT] < n[N_SB] + n[N_COUNT]
+                fed[r[I_SLOT]] += 1
+    for i, n in enumerate(nodes):
+        assert 1 <= n[N_COUNT] <= MERGE_FAN_IN
+        assert 0 <= n[N_SB] and n[N_SB] + n[N_COUNT] <= S
+        if n[N_PARENT] < 0:
+            assert n[N_OUT] == -1
+            key = (int(n[N_REQ]), int(n[N_KVH]))
+            assert key not in roots
+            roots[key] = i
+        else:
+            par = nodes[n[N_PARENT]]
+            assert par[N_LEVEL] == n[N_LEVEL] + 1
+            assert (par[N_REQ], par[N_KVH]) == (n[N_REQ], n[N_KVH])
+            assert par[N_SB] <= n[N_OUT] < par[N_SB] + par[N_COUNT]
+            fed[n[N_OUT]] += 1
+    # every slot is one node's child and has exactly one producer
+    owner = np.zeros(S, dtype=np.int64)
+    for n in nodes:
+        owner[n[N_SB]:n[N_SB] + n[N_COUNT]] += 1
+    assert np.all(owner == 1) and np.all(fed == 1)
+    split = {(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)
+             if sum(1 for r in items if r[I_REQ] == b and r[I_KVH] == h and r[I_SLOT] >= 0)}
+    assert set(roots) == split
+    # partial-slot bound per KV head: sum_b ceil(n_b / C) leaves plus at most
+    # ceil(k / 31) inner slots for a request cut into k chunks
     C = info["chunk_pages"]
     N = int(w.kv_indptr[-1])
     assert sum(math.ceil(w.num_pages(b) / C) for b in range(w.batch)) <= w.batch + N / C
     # workspace holds every section
-    Hq, d = w.num_qo_heads, w.head_dim
-    need = len(items) * 32 + len(merges) * 16 + N * 4 + info["num_partial_slots"] * Hq * (d + 1) * 4
+    G, d = w.group_size, w.head_dim
+    need = len(items) * ITEM_STRIDE * 4 + len(nodes) * (NODE_STRIDE + 1) * 4 + N * 4 + S * G * (d + 1) * 4
     assert info["workspace_bytes"] >= need
-    return items, merges
+    return items, nodes
+
+
+def tree_merge(items, nodes, leaf_state):
+    """Folds chunk states up each merge tree as the plan prescribes (children
+    in slot order, the oracle's float64 merge at every node); returns
+    {(b, kv head): (v, lse)} from the roots."""
+    slot_state = {int(r[I_SLOT]): leaf_state[i] for i, r in enumerate(items) if r[I_SLOT] >= 0}
+    out = {}
+    for i in sorted(range(len(nodes)), key=lambda i: nodes[i][N_LEVEL]):
+        n = nodes[i]
+        kids = [slot_state[s] for s in range(n[N_SB], n[N_SB] + n[N_COUNT])]
+        st = oa.merge_many([k[0] for k in kids], [k[1] for k in kids])
+        if n[N_PARENT] < 0:
+            out[(int(n[N_REQ]), int(n[N_KVH]))] = st
+        else:
+            slot_state[int(n[N_OUT])] = st
+    return out
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
@@ -110,33 +145,45 @@ def test_fixed_chunk(fixed):
     check_plan(w, p)
 
 
-def test_cut_and_merge_equals_whole():
+@pytest.mark.parametrize("fixed,lens", [(24, None), (1, [70, 33, 32, 1, 0, 1100])])
+def test_cut_and_merge_equals_whole(fixed, lens):
     """Running every work item as attention over its own tokens (float64
-    oracle) and merging each request's chunk states with the oracle's merge
-    gives the whole-request result: the plan covers every token once and the
-    merge algebra is right."""
-    w = random_workload(77, 6, 260, 8, 2, 64, 4, "f32", empty_every=4)
-    p = make_plan(w, fixed_chunk_tokens=24)
-    items, _ = check_plan(w, p)
+    oracle) and folding the chunk states up the plan's merge trees gives the
+    whole-request result: the plan covers every token once and its trees
+    reach every chunk exactly once (page size 1 with one-token chunks gives
+    trees of two and three levels)."""
+    if lens is None:
+        w = random_workload(77, 6, 260, 8, 2, 64, 4, "f32", empty_every=4)
+    else:
+        w = random_workload(78, len(lens), 1, 8, 2, 64, 1, "f32", lens=lens)
+    p = make_plan(w, fixed_chunk_tokens=fixed)
+    items, nodes = check_plan(w, p)
+    if lens is not None:
+        assert nodes[:, N_LEVEL].max() == 2
     q, k, v = (t.double().numpy() for t in w.make_values("cpu"))
     O, LSE = oa.decode_attention(q, k, v, w.kv_indptr, w.kv_indices, w.last_page_len, w.sm_scale)
     G = w.group_size
-    states = {}
+    leaf = []
     for r in items:
         b, h, pb, ntok, npg = int(r[I_REQ]), int(r[I_KVH]), int(r[I_PB]), int(r[I_NTOK]), int(r[I_NP])
+        if ntok == 0:
+            leaf.append(None)
+            continue
         last = ntok - (npg - 1) * w.page_size
         toks = oa.request_tokens(np.array([0, npg]), w.kv_indices[pb:pb + npg], np.array([last]),
                                  w.page_size, 0)
         K, V = oa.gather_kv(k, v, toks, h)
-        o, lse = oa.attend(q[b, h * G:(h + 1) * G], K, V, w.sm_scale)
-        states.setdefault((b, h), []).append((int(r[I_CHUNK]), o, lse))
+        leaf.append(oa.attend(q[b, h * G:(h + 1) * G], K, V, w.sm_scale))
+    merged = tree_merge(items, nodes, leaf)
+    for i, r in enumerate(items):
+        if r[I_SLOT] < 0 and r[I_NTOK] > 0:
+            merged[(int(r[I_REQ]), int(r[I_KVH]))] = leaf[i]
     for b in range(w.batch):
         for h in range(w.num_kv_heads):
-            got = sorted(states.get((b, h), []), key=lambda x: x[0])
-            if not got:
+            if w.kv_len(b) == 0:
                 assert np.all(np.isneginf(LSE[b, h * G:(h + 1) * G]))
                 continue
-            vo, so = oa.merge_many([g[1] for g in got], [g[2] for g in got])
+            vo, so = merged[(b, h)]
             assert np.allclose(vo, O[b, h * G:(h + 1) * G], atol=1e-12, rtol=0)
             assert np.allclose(so, LSE[b, h * G:(h + 1) * G], atol=1e-12, rtol=0)
 
@@ -144,7 +191,8 @@ def test_cut_and_merge_equals_whole():
 def test_empty_batch_and_all_empty():
     p = fb.plan(np.array([0]), np.array([], dtype=np.int32), np.array([], dtype=np.int32),
                 8, 2, 128, 16, 0, "bf16")
-    assert p.info["num_items"] == 0 and p.info["num_merge_tasks"] == 0
+    assert p.info["num_items"] == 0 and p.info["num_merge_nodes"] == 0
     p = fb.plan(np.array([0, 0, 0]), np.array([], dtype=np.int32), np.array([0, 0]), 8, 2, 128, 16, 4, "bf16")
-    assert p.info["num_items"] == 0 and p.info["num_merge_tasks"] == 2
-    assert p.merge_list()[:, 2].tolist() == [0, 0]
+    items = p.work_list()
+    assert p.info["num_items"] == 4 and p.info["num_merge_nodes"] == 0
+    assert items[:, I_NTOK].tolist() == [0] * 4 and items[:, I_SLOT].tolist() == [-1] * 4
