@@ -21,6 +21,7 @@ FI_DTYPE_F32 = 0
 FI_DTYPE_BF16 = 1
 ITEM_STRIDE = 16
 NODE_STRIDE = 8
+PITEM_STRIDE = 8
 MERGE_FAN_IN = 32
 
 STATUS_NAMES = {0: "FI_OK", -1: "FI_ERR_INVALID_ARG", -2: "FI_ERR_UNSUPPORTED",
@@ -28,8 +29,8 @@ STATUS_NAMES = {0: "FI_OK", -1: "FI_ERR_INVALID_ARG", -2: "FI_ERR_UNSUPPORTED",
 
 # Every symbol include/fi_bsr.h declares.
 EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_merge_nodes",
-            "fi_plan_upload", "fi_decode_run", "fi_merge_states", "fi_plan_destroy",
-            "fi_last_error"]
+            "fi_plan_prefix_items", "fi_plan_prefix_members", "fi_plan_upload", "fi_decode_run",
+            "fi_merge_states", "fi_plan_destroy", "fi_last_error"]
 
 
 class FiError(RuntimeError):
@@ -41,7 +42,7 @@ class FiError(RuntimeError):
 class PlanOpts(ctypes.Structure):
     _fields_ = [("num_cus", ctypes.c_int32), ("items_per_cu", ctypes.c_int32),
                 ("min_chunk_tokens", ctypes.c_int32), ("max_chunk_tokens", ctypes.c_int32),
-                ("fixed_chunk_tokens", ctypes.c_int32)]
+                ("fixed_chunk_tokens", ctypes.c_int32), ("cascade", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -53,7 +54,8 @@ class PlanInfo(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("num_qo_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("shared_pages", ctypes.c_int64)]
+                ("shared_pages", ctypes.c_int64), ("num_prefix_items", ctypes.c_int64),
+                ("num_prefix_groups", ctypes.c_int32), ("prefix_rows_per_item", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -80,8 +82,9 @@ def lib() -> ctypes.CDLL:
     L.fi_plan_get_info.restype = i32
     L.fi_plan_work_list.argtypes = [vp, ctypes.POINTER(pi32), ctypes.POINTER(i64)]
     L.fi_plan_work_list.restype = i32
-    L.fi_plan_merge_nodes.argtypes = [vp, ctypes.POINTER(pi32), ctypes.POINTER(i64)]
-    L.fi_plan_merge_nodes.restype = i32
+    for name in ("fi_plan_merge_nodes", "fi_plan_prefix_items", "fi_plan_prefix_members"):
+        getattr(L, name).argtypes = [vp, ctypes.POINTER(pi32), ctypes.POINTER(i64)]
+        getattr(L, name).restype = i32
     L.fi_plan_upload.argtypes = [vp, vp, sz, vp]
     L.fi_plan_upload.restype = i32
     L.fi_decode_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
@@ -144,13 +147,22 @@ class Plan:
             return np.zeros((0, ITEM_STRIDE), dtype=np.int32)
         return np.ctypeslib.as_array(p, shape=(n.value * ITEM_STRIDE,)).reshape(-1, ITEM_STRIDE).copy()
 
-    def merge_nodes(self) -> np.ndarray:
+    def _view(self, fn, stride) -> np.ndarray:
         p = ctypes.POINTER(ctypes.c_int32)()
         n = ctypes.c_int64()
-        _check(lib().fi_plan_merge_nodes(self._h, ctypes.byref(p), ctypes.byref(n)))
+        _check(fn(self._h, ctypes.byref(p), ctypes.byref(n)))
         if n.value == 0:
-            return np.zeros((0, NODE_STRIDE), dtype=np.int32)
-        return np.ctypeslib.as_array(p, shape=(n.value * NODE_STRIDE,)).reshape(-1, NODE_STRIDE).copy()
+            return np.zeros((0, stride), dtype=np.int32)
+        return np.ctypeslib.as_array(p, shape=(n.value * stride,)).reshape(-1, stride).copy()
+
+    def merge_nodes(self) -> np.ndarray:
+        return self._view(lib().fi_plan_merge_nodes, NODE_STRIDE)
+
+    def prefix_items(self) -> np.ndarray:
+        return self._view(lib().fi_plan_prefix_items, PITEM_STRIDE)
+
+    def prefix_members(self) -> np.ndarray:
+        return self._view(lib().fi_plan_prefix_members, 1).reshape(-1)
 
     def upload(self, workspace, stream=None):
         """Copy the plan into ``workspace`` (a torch uint8 CUDA tensor)."""
@@ -182,13 +194,14 @@ class Plan:
 def plan(kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int, num_kv_heads: int,
          head_dim: int, page_size: int, num_pool_pages: int, dtype="bf16",
          num_cus: int = 0, items_per_cu: int = 0, min_chunk_tokens: int = 0,
-         max_chunk_tokens: int = 0, fixed_chunk_tokens: int = 0) -> Plan:
+         max_chunk_tokens: int = 0, fixed_chunk_tokens: int = 0, cascade: int = 0) -> Plan:
     """fi_plan_create over host page-table arrays (numpy or CPU tensors)."""
     ip, ix, lp = _i32(kv_indptr), _i32(kv_indices), _i32(kv_last_page_len)
     batch = len(ip) - 1
     if len(lp) != batch:
         raise ValueError("kv_last_page_len must have one entry per request")
-    opts = PlanOpts(num_cus, items_per_cu, min_chunk_tokens, max_chunk_tokens, fixed_chunk_tokens)
+    opts = PlanOpts(num_cus, items_per_cu, min_chunk_tokens, max_chunk_tokens, fixed_chunk_tokens,
+                    cascade)
     h = ctypes.c_void_p()
     ix_ptr = _ptr32(ix) if ix.size else ctypes.POINTER(ctypes.c_int32)()
     _check(lib().fi_plan_create(_ptr32(ip), ix_ptr, _ptr32(lp), batch, num_qo_heads,

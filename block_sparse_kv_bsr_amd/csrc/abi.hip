@@ -107,6 +107,29 @@ fi_status launch_run(const fi_plan* plan, const void* q, const void* k_pages,
   d.bf16 = plan->dtype == FI_DTYPE_BF16;
   d.stream_kv = plan->shared_pages == 0;
   d.sm_scale = sm_scale;
+  if (plan->num_pitems() > 0) {
+    // shared prefixes first: their partials must be in place before the
+    // decode kernel's merge trees read them
+    fi::PrefixArgs pa{};
+    pa.pitems = reinterpret_cast<const int32_t*>(ws + plan->ws.pitems);
+    pa.members = reinterpret_cast<const int32_t*>(ws + plan->ws.members);
+    pa.prefix_slot = reinterpret_cast<const int32_t*>(ws + plan->ws.prefix_slot);
+    pa.page_ids = d.page_ids;
+    pa.q = q;
+    pa.k_pages = k_pages;
+    pa.v_pages = v_pages;
+    pa.part_o = d.part_o;
+    pa.part_lse = d.part_lse;
+    pa.num_items = plan->num_pitems();
+    pa.num_qo_heads = plan->num_qo_heads;
+    pa.num_kv_heads = plan->num_kv_heads;
+    pa.head_dim = plan->head_dim;
+    pa.page_size = plan->page_size;
+    pa.group = plan->group;
+    pa.sm_scale = sm_scale;
+    const hipError_t ep = fi::launch_prefix(pa, s);
+    if (ep != hipSuccess) return hip_fail(ep, "shared-prefix kernel launch");
+  }
   hipError_t e = fi::launch_decode(d, s);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   return FI_OK;

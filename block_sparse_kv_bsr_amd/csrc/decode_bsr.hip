@@ -231,8 +231,10 @@ __device__ __forceinline__ float2 load_shared2(const float* p) {
 }
 
 // Completes the merge tree of a cut request after this wave wrote its chunk's
-// partial state. Each node counts its children's arrivals; the wave whose
-// arrival completes a node merges the node's children (in slot order, so the
+// partial state. Each node counts its children's arrivals (shared-prefix
+// partials, written by an earlier kernel, are already in place and do not
+// report); the wave whose arrival completes a node merges all of the node's
+// children (in slot order, so the
 // result does not depend on which wave arrives last), resets the counter for
 // the next run, and reports the merged state to the parent, or writes the
 // output at the root. Before its arrival is counted the wave waits for its
@@ -266,6 +268,7 @@ __device__ void finish_split(const DecodeParams& p, int node, int lane, float* s
     // the node's fields are read-only: fetch them with the arrival
     const int32_t* nd = p.nodes + (int64_t)node * FI_NODE_STRIDE;
     const int count = nd[FI_NODE_COUNT];
+    const int arrivals = nd[FI_NODE_ARRIVALS];  // children that report here
     const int sb = nd[FI_NODE_SLOT_BEGIN];
     const int parent = nd[FI_NODE_PARENT];
     const int out_slot = nd[FI_NODE_OUT_SLOT];
@@ -276,7 +279,7 @@ __device__ void finish_split(const DecodeParams& p, int node, int lane, float* s
     if (lane == 0)
       old = __hip_atomic_fetch_add(p.counters + node, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __builtin_amdgcn_readfirstlane(old);
-    if (old != count - 1) return;
+    if (old != arrivals - 1) return;
     if (lane == 0) __hip_atomic_store(p.counters + node, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     float sv[kV];

@@ -26,6 +26,21 @@ struct DecodeArgs {
   float sm_scale;
 };
 
+struct PrefixArgs {
+  const int32_t* pitems;       // device, [num_items][FI_PITEM_STRIDE]
+  const int32_t* members;      // device, request ids of the prefix groups
+  const int32_t* prefix_slot;  // device, [batch][num_kv_heads] first prefix slot
+  const int32_t* page_ids;     // device, the request page lists
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  float* part_o;
+  float* part_lse;
+  int64_t num_items;
+  int32_t num_qo_heads, num_kv_heads, head_dim, page_size, group;
+  float sm_scale;
+};
+
 struct MergeTwoArgs {
   const void* v_a;
   const float* s_a;
@@ -40,5 +55,6 @@ struct MergeTwoArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge_two(const MergeTwoArgs& a, hipStream_t stream);
+hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream);
 
 }  // namespace fi

@@ -122,23 +122,89 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     if (o.num_cus < 0 || o.items_per_cu < 0 || o.min_chunk_tokens < 0 ||
         o.max_chunk_tokens < 0 || o.fixed_chunk_tokens < 0)
       return fail(FI_ERR_INVALID_ARG, "negative planner option");
+    if (o.cascade < -1 || o.cascade > 1) return fail(FI_ERR_INVALID_ARG, "cascade must be -1, 0 or 1");
     const int64_t num_cus = o.num_cus ? o.num_cus : 256;
     const int64_t items_per_cu = o.items_per_cu ? o.items_per_cu : 8;
     const int64_t min_chunk_tokens = o.min_chunk_tokens ? o.min_chunk_tokens : 256;
 
-    // ---- chunk length (pages)
-    const int64_t max_n = batch > 0 ? *std::max_element(npages.begin(), npages.end()) : 0;
+    // ---- shared-prefix groups: requests (of two pages or more) whose lists
+    // start with the same physical page; the group's prefix is the longest
+    // run of leading pages all members share, never a member's last page
+    struct Group {
+      int64_t member_base, members, lcp, chunks, row_blocks;
+      int32_t first;  // a member; its first lcp pages are the prefix
+    };
+    std::vector<Group> groups;
+    std::vector<int32_t> members;
+    std::vector<int32_t> group_of(batch, -1);
+    std::vector<int64_t> pre_pages(batch, 0);
+    const int64_t kPrefixRows = 128;
+    if (o.cascade >= 0 && dtype == FI_DTYPE_BF16 && batch >= 2) {
+      std::vector<std::pair<int32_t, int32_t>> firsts;  // (first page, request)
+      for (int32_t b = 0; b < batch; ++b)
+        if (npages[b] >= 2) firsts.emplace_back(kv_indices[kv_indptr[b]], b);
+      std::sort(firsts.begin(), firsts.end());
+      for (size_t i = 0; i < firsts.size();) {
+        size_t j = i;
+        while (j < firsts.size() && firsts[j].first == firsts[i].first) ++j;
+        if (j - i >= 2) {
+          const int32_t b0 = firsts[i].second;
+          int64_t lcp = npages[b0] - 1;
+          for (size_t t = i + 1; t < j; ++t) {
+            const int32_t b = firsts[t].second;
+            const int64_t lim = std::min<int64_t>(lcp, npages[b] - 1);
+            int64_t q = 0;
+            while (q < lim && kv_indices[kv_indptr[b] + q] == kv_indices[kv_indptr[b0] + q]) ++q;
+            lcp = q;
+          }
+          lcp = std::min<int64_t>(lcp, (int64_t)(FI_MERGE_FAN_IN - 1) * FI_PREFIX_MAX_PAGES);
+          const int64_t saved = (int64_t)(j - i - 1) * lcp * page_size * head_dim * 4 * num_kv_heads;
+          if (lcp >= 1 && (o.cascade == 1 || saved >= (int64_t(8) << 20))) {
+            Group g{};
+            g.member_base = (int64_t)members.size();
+            g.members = (int64_t)(j - i);
+            g.lcp = lcp;
+            g.first = b0;
+            g.row_blocks = fi::ceil_div(g.members * group, kPrefixRows);
+            for (size_t t = i; t < j; ++t) {
+              const int32_t b = firsts[t].second;
+              members.push_back(b);
+              group_of[b] = (int32_t)groups.size();
+              pre_pages[b] = lcp;
+            }
+            groups.push_back(g);
+          }
+        }
+        i = j;
+      }
+      // prefix chunks per group: about num_cus prefix items in all, at most
+      // FI_MERGE_FAN_IN - 1 per tree so every tree's first node still has a
+      // decode child (nodes complete only inside the decode kernel)
+      int64_t blocks = 0;
+      for (const Group& g : groups) blocks += g.row_blocks;
+      for (Group& g : groups) {
+        const int64_t want = fi::ceil_div(num_cus, std::max<int64_t>(1, blocks * num_kv_heads));
+        g.chunks = std::max<int64_t>(1, std::min<int64_t>({want, g.lcp, FI_MERGE_FAN_IN - 1}));
+        // no prefix item spans more than FI_PREFIX_MAX_PAGES pages
+        g.chunks = std::max<int64_t>(g.chunks, fi::ceil_div(g.lcp, FI_PREFIX_MAX_PAGES));
+      }
+    }
+    std::vector<int64_t> dpages(batch);  // pages left to the decode items
+    for (int32_t b = 0; b < batch; ++b) dpages[b] = npages[b] - pre_pages[b];
+
+    // ---- chunk length (pages) of the decode items
+    const int64_t max_n = batch > 0 ? *std::max_element(dpages.begin(), dpages.end()) : 0;
     int64_t C = std::max<int64_t>(1, max_n);
     if (o.fixed_chunk_tokens > 0) {
       C = std::max<int64_t>(1, fi::ceil_div(o.fixed_chunk_tokens, page_size));
     } else if (max_n > 0) {
       const int64_t budget = num_cus * items_per_cu;
       const int64_t cmin = std::max<int64_t>(1, fi::ceil_div(min_chunk_tokens, page_size));
-      if (cmin < max_n && fi::count_items(npages, max_n, num_kv_heads) <= budget) {
+      if (cmin < max_n && fi::count_items(dpages, max_n, num_kv_heads) <= budget) {
         int64_t lo = cmin, hi = max_n;  // count_items is non-increasing in C
         while (lo < hi) {
           const int64_t mid = lo + (hi - lo) / 2;
-          if (fi::count_items(npages, mid, num_kv_heads) <= budget) hi = mid;
+          if (fi::count_items(dpages, mid, num_kv_heads) <= budget) hi = mid;
           else lo = mid + 1;
         }
         C = lo;
@@ -159,14 +225,22 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     p->num_pool_pages = num_pool_pages;
     p->chunk_pages = (int32_t)C;
     p->total_tokens = total_tokens;
+    p->num_groups = (int32_t)groups.size();
+    p->prefix_rows = (int32_t)kPrefixRows;
+    p->members = members;
     {
-      // physical pages that several requests (or one request twice) list:
-      // a bitmap over the pool when it is not much larger than the page
-      // lists, else a sort
+      // physical pages that the decode items read more than once (several
+      // requests, or one request twice; a cascade's prefix pages are read by
+      // the prefix items instead): a bitmap over the pool when it is not
+      // much larger than the page lists, else a sort
+      std::vector<int32_t> ids;
+      ids.reserve((size_t)nnz);
+      for (int32_t b = 0; b < batch; ++b)
+        for (int64_t j = kv_indptr[b] + pre_pages[b]; j < kv_indptr[b + 1]; ++j)
+          ids.push_back(kv_indices[j]);
       if (num_pool_pages <= 64 * nnz + 65536) {
         std::vector<uint64_t> seen((size_t)(num_pool_pages + 63) / 64, 0), twice(seen.size(), 0);
-        for (int64_t j = 0; j < nnz; ++j) {
-          const int64_t id = kv_indices[j];
+        for (const int32_t id : ids) {
           const uint64_t bit = 1ull << (id & 63);
           uint64_t& w = seen[(size_t)(id >> 6)];
           if (w & bit) twice[(size_t)(id >> 6)] |= bit;
@@ -174,7 +248,6 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
         }
         for (uint64_t w : twice) p->shared_pages += __builtin_popcountll(w);
       } else {
-        std::vector<int32_t> ids(kv_indices, kv_indices + nnz);
         std::sort(ids.begin(), ids.end());
         for (size_t j = 1; j < ids.size(); ++j)
           if (ids[j] == ids[j - 1] && (j == 1 || ids[j - 1] != ids[j - 2])) ++p->shared_pages;
@@ -185,10 +258,12 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     struct Item { int32_t f[FI_ITEM_STRIDE]; };
     std::vector<Item> items;
     std::vector<int32_t>& nodes = p->nodes;
+    std::vector<int32_t>& pslot = p->prefix_slot;
+    if (!groups.empty()) pslot.assign((size_t)batch * num_kv_heads, -1);
     int64_t slot = 0;
     int32_t max_chunks = 0, min_split = 0;
-    auto new_node = [&](int32_t count, int64_t slot_begin, int64_t out_slot, int32_t b,
-                        int32_t h, int32_t level) {
+    auto new_node = [&](int32_t count, int32_t arrivals, int64_t slot_begin, int64_t out_slot,
+                        int32_t b, int32_t h, int32_t level) {
       const int32_t id = (int32_t)(nodes.size() / FI_NODE_STRIDE);
       int32_t f[FI_NODE_STRIDE] = {0};
       f[FI_NODE_COUNT] = count;
@@ -198,12 +273,15 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
       f[FI_NODE_REQUEST] = b;
       f[FI_NODE_KV_HEAD] = h;
       f[FI_NODE_LEVEL] = level;
+      f[FI_NODE_ARRIVALS] = arrivals;
       nodes.insert(nodes.end(), f, f + FI_NODE_STRIDE);
       return id;
     };
     for (int32_t b = 0; b < batch; ++b) {
-      const int64_t n = npages[b];
+      const int64_t n = dpages[b];
+      const int64_t pre = pre_pages[b];
       const int64_t k = n > 0 ? fi::ceil_div(n, C) : 0;
+      const int64_t cpre = group_of[b] >= 0 ? groups[group_of[b]].chunks : 0;
       max_chunks = std::max<int32_t>(max_chunks, (int32_t)k);
       if (k >= 2) min_split = min_split == 0 ? (int32_t)k : std::min<int32_t>(min_split, (int32_t)k);
       if (k == 0) {  // no pages: one item per KV head writes out = 0, lse = -inf
@@ -218,37 +296,43 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
         }
         continue;
       }
+      const int64_t nchild = cpre + k;
       for (int32_t h = 0; h < num_kv_heads; ++h) {
-        // merge tree of (b, h): leaves take chunk partials in slots
-        // [leaf_base, leaf_base + k); each level groups FI_MERGE_FAN_IN children
+        // merge tree of (b, h): leaves take the cpre prefix partials, then
+        // the k chunk partials, in slots [leaf_base, leaf_base + nchild);
+        // each level groups FI_MERGE_FAN_IN children
         const int64_t leaf_base = slot;
-        std::vector<int32_t> leaf_node(k, -1);
-        if (k >= 2) {
-          slot += k;
-          int64_t child_begin = leaf_base, nchild = k;
+        std::vector<int32_t> leaf_node(nchild, -1);
+        if (nchild >= 2) {
+          slot += nchild;
+          if (cpre > 0) pslot[(size_t)b * num_kv_heads + h] = (int32_t)leaf_base;
+          int64_t child_begin = leaf_base, nch = nchild;
           int32_t level = 0;
           std::vector<int32_t> prev;
           for (;;) {
-            const int64_t groups = fi::ceil_div(nchild, FI_MERGE_FAN_IN);
-            const bool root = groups == 1;
+            const int64_t ngroups = fi::ceil_div(nch, FI_MERGE_FAN_IN);
+            const bool root = ngroups == 1;
             const int64_t out_base = root ? -1 : slot;
-            if (!root) slot += groups;
+            if (!root) slot += ngroups;
             const int32_t first = (int32_t)(nodes.size() / FI_NODE_STRIDE);
-            for (int64_t g = 0; g < groups; ++g) {
-              const int64_t cnt = std::min<int64_t>(FI_MERGE_FAN_IN, nchild - g * FI_MERGE_FAN_IN);
-              new_node((int32_t)cnt, child_begin + g * FI_MERGE_FAN_IN, root ? -1 : out_base + g,
-                       b, h, level);
+            for (int64_t g = 0; g < ngroups; ++g) {
+              const int64_t c0 = g * FI_MERGE_FAN_IN;
+              const int64_t cnt = std::min<int64_t>(FI_MERGE_FAN_IN, nch - c0);
+              // prefix partials (level 0, children [0, cpre)) do not report
+              const int64_t quiet = level == 0 ? std::max<int64_t>(0, std::min(cpre, c0 + cnt) - c0) : 0;
+              new_node((int32_t)cnt, (int32_t)(cnt - quiet), child_begin + c0,
+                       root ? -1 : out_base + g, b, h, level);
             }
             for (size_t i = 0; i < prev.size(); ++i)
               nodes[(size_t)prev[i] * FI_NODE_STRIDE + FI_NODE_PARENT] =
                   first + (int32_t)(i / FI_MERGE_FAN_IN);
             if (level == 0)
-              for (int64_t c = 0; c < k; ++c) leaf_node[c] = first + (int32_t)(c / FI_MERGE_FAN_IN);
+              for (int64_t c = 0; c < nchild; ++c) leaf_node[c] = first + (int32_t)(c / FI_MERGE_FAN_IN);
             prev.clear();
-            for (int64_t g = 0; g < groups; ++g) prev.push_back(first + (int32_t)g);
+            for (int64_t g = 0; g < ngroups; ++g) prev.push_back(first + (int32_t)g);
             if (root) break;
             child_begin = out_base;
-            nchild = groups;
+            nch = ngroups;
             ++level;
           }
         }
@@ -262,13 +346,13 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
           Item it{};
           it.f[FI_ITEM_REQUEST] = b;
           it.f[FI_ITEM_KV_HEAD] = h;
-          it.f[FI_ITEM_PAGE_BEGIN] = (int32_t)(kv_indptr[b] + page0);
+          it.f[FI_ITEM_PAGE_BEGIN] = (int32_t)(kv_indptr[b] + pre + page0);
           it.f[FI_ITEM_NUM_TOKENS] = (int32_t)tok;
-          it.f[FI_ITEM_SLOT] = k == 1 ? -1 : (int32_t)(leaf_base + c);
+          it.f[FI_ITEM_SLOT] = nchild == 1 ? -1 : (int32_t)(leaf_base + cpre + c);
           it.f[FI_ITEM_CHUNK] = (int32_t)c;
           it.f[FI_ITEM_NUM_PAGES] = (int32_t)np;
-          it.f[FI_ITEM_FIRST_PAGE] = kv_indices[kv_indptr[b] + page0];
-          it.f[FI_ITEM_MERGE_NODE] = leaf_node[c];
+          it.f[FI_ITEM_FIRST_PAGE] = kv_indices[kv_indptr[b] + pre + page0];
+          it.f[FI_ITEM_MERGE_NODE] = leaf_node[cpre + c];
           items.push_back(it);
           page0 += np;
         }
@@ -292,6 +376,32 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     p->max_chunks = max_chunks;
     p->min_chunks_split = min_split;
 
+    // ---- shared-prefix items: (group, KV head, block of members, chunk)
+    for (int64_t gi = 0; gi < (int64_t)groups.size(); ++gi) {
+      const Group& g = groups[gi];
+      const int64_t per_block = kPrefixRows / group;
+      for (int64_t c = 0, page0 = 0; c < g.chunks; ++c) {
+        const int64_t np = g.lcp / g.chunks + (c < g.lcp % g.chunks ? 1 : 0);
+        for (int32_t h = 0; h < num_kv_heads; ++h) {
+          for (int64_t rb = 0; rb < g.row_blocks; ++rb) {
+            const int64_t m0 = rb * per_block;
+            const int64_t nm = std::min<int64_t>(per_block, g.members - m0);
+            int32_t f[FI_PITEM_STRIDE] = {0};
+            f[FI_PITEM_GROUP] = (int32_t)gi;
+            f[FI_PITEM_KV_HEAD] = h;
+            f[FI_PITEM_MEMBER_BASE] = (int32_t)g.member_base;
+            f[FI_PITEM_ROW_BEGIN] = (int32_t)m0;
+            f[FI_PITEM_NUM_ROWS] = (int32_t)(nm * group);
+            f[FI_PITEM_CHUNK] = (int32_t)c;
+            f[FI_PITEM_PAGE_BEGIN] = (int32_t)(kv_indptr[g.first] + page0);
+            f[FI_PITEM_NUM_PAGES] = (int32_t)np;
+            p->pitems.insert(p->pitems.end(), f, f + FI_PITEM_STRIDE);
+          }
+        }
+        page0 += np;
+      }
+    }
+
     // ---- workspace layout and host image of its uploaded part
     fi::WorkspaceLayout& ws = p->ws;
     const int64_t nn = p->num_nodes();
@@ -304,6 +414,12 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     off = fi::align_up(off + nn * 4, 256);
     ws.page_ids = off;
     off = fi::align_up(off + nnz * 4, 256);
+    ws.pitems = off;
+    off = fi::align_up(off + (int64_t)p->pitems.size() * 4, 256);
+    ws.members = off;
+    off = fi::align_up(off + (int64_t)members.size() * 4, 256);
+    ws.prefix_slot = off;
+    off = fi::align_up(off + (int64_t)pslot.size() * 4, 256);
     ws.image_bytes = off;
     ws.part_o = off;
     off = fi::align_up(off + p->num_slots * group * (int64_t)head_dim * 4, 256);
@@ -311,10 +427,14 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     off = fi::align_up(off + p->num_slots * group * 4, 256);
     ws.total_bytes = std::max<int64_t>(off, 256);
     p->image.assign(ws.image_bytes, 0);  // counters start at 0
-    if (!p->items.empty())
-      std::memcpy(p->image.data() + ws.items, p->items.data(), p->items.size() * 4);
-    if (!nodes.empty())
-      std::memcpy(p->image.data() + ws.nodes, nodes.data(), nodes.size() * 4);
+    auto put = [&](int64_t at, const std::vector<int32_t>& v) {
+      if (!v.empty()) std::memcpy(p->image.data() + at, v.data(), v.size() * 4);
+    };
+    put(ws.items, p->items);
+    put(ws.nodes, nodes);
+    put(ws.pitems, p->pitems);
+    put(ws.members, members);
+    put(ws.prefix_slot, pslot);
     if (nnz > 0) std::memcpy(p->image.data() + ws.page_ids, kv_indices, nnz * 4);
 
     *out_plan = p.release();
@@ -344,6 +464,9 @@ fi_status fi_plan_get_info(const fi_plan* p, fi_plan_info* info) {
   r.page_size = p->page_size;
   r.dtype = (int32_t)p->dtype;
   r.shared_pages = p->shared_pages;
+  r.num_prefix_items = p->num_pitems();
+  r.num_prefix_groups = p->num_groups;
+  r.prefix_rows_per_item = p->prefix_rows;
   *info = r;
   return FI_OK;
 }
@@ -359,6 +482,20 @@ fi_status fi_plan_merge_nodes(const fi_plan* p, const int32_t** nodes, int64_t* 
   if (!p || !nodes || !num_nodes) return fi::fail(FI_ERR_INVALID_ARG, "NULL argument");
   *nodes = p->nodes.data();
   *num_nodes = p->num_nodes();
+  return FI_OK;
+}
+
+fi_status fi_plan_prefix_items(const fi_plan* p, const int32_t** items, int64_t* num_items) {
+  if (!p || !items || !num_items) return fi::fail(FI_ERR_INVALID_ARG, "NULL argument");
+  *items = p->pitems.data();
+  *num_items = p->num_pitems();
+  return FI_OK;
+}
+
+fi_status fi_plan_prefix_members(const fi_plan* p, const int32_t** members, int64_t* num_members) {
+  if (!p || !members || !num_members) return fi::fail(FI_ERR_INVALID_ARG, "NULL argument");
+  *members = p->members.data();
+  *num_members = (int64_t)p->members.size();
   return FI_OK;
 }
 

@@ -21,6 +21,9 @@ struct WorkspaceLayout {
   int64_t nodes = 0;      // int32 [num_nodes][FI_NODE_STRIDE]
   int64_t counters = 0;   // int32 [num_nodes], 0 between runs
   int64_t page_ids = 0;   // int32 [nnz]
+  int64_t pitems = 0;     // int32 [num_prefix_items][FI_PITEM_STRIDE]
+  int64_t members = 0;    // int32 request ids of the prefix groups
+  int64_t prefix_slot = 0;  // int32 [batch][num_kv_heads]: first prefix slot or -1
   int64_t part_o = 0;     // float [num_slots][group][head_dim]
   int64_t part_lse = 0;   // float [num_slots][group], log2 units
   int64_t image_bytes = 0;
@@ -46,6 +49,10 @@ struct fi_plan {
   int64_t num_slots = 0;
   std::vector<int32_t> items;   // num_items * FI_ITEM_STRIDE
   std::vector<int32_t> nodes;   // num_merge_nodes * FI_NODE_STRIDE
+  std::vector<int32_t> pitems;  // num_prefix_items * FI_PITEM_STRIDE
+  std::vector<int32_t> members; // request ids, grouped
+  std::vector<int32_t> prefix_slot;  // [batch * num_kv_heads], empty without groups
+  int32_t num_groups = 0, prefix_rows = 0;
   std::vector<uint8_t> image;   // host copy of the uploaded part of the workspace
   fi::WorkspaceLayout ws;
   // Set by the launch layer.
@@ -53,6 +60,7 @@ struct fi_plan {
   const void* uploaded_to = nullptr;
   int64_t num_items() const { return (int64_t)items.size() / FI_ITEM_STRIDE; }
   int64_t num_nodes() const { return (int64_t)nodes.size() / FI_NODE_STRIDE; }
+  int64_t num_pitems() const { return (int64_t)pitems.size() / FI_PITEM_STRIDE; }
 };
 
 namespace fi {

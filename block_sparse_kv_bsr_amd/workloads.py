@@ -263,3 +263,49 @@ def random_workload(seed: int, batch: int, max_len: int, num_qo_heads: int,
     ip, ix, lp, un = paged_structure(lens, page_size, pool, rng)
     return Workload(f"random_{seed}", 0, batch, num_qo_heads, num_kv_heads, head_dim,
                     page_size, dtype, pool, ip, ix, lp, un, 10_000 + seed)
+
+
+def prefix_workload(seed: int, groups: List[tuple], singles: int, suffix_max: int,
+                    num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
+                    dtype: str, extra_shared: bool = True) -> Workload:
+    """Requests that share prefixes, for cascade tests. ``groups`` lists
+    (members, prefix_pages): the members of a group all begin with the same
+    prefix_pages physical pages, then a private suffix of U{1..suffix_max}
+    tokens. With ``extra_shared`` the first two members of each group also
+    share the page after the prefix (so the common run is longer for some
+    members than for all). ``singles`` more requests share nothing. The batch
+    order is a seeded shuffle, so group members are not adjacent."""
+    rng = np.random.default_rng([seed, 11])
+    P = page_size
+    reqs = []  # (shared page ids, suffix tokens)
+    next_page = 0
+    for members, prefix_pages in groups:
+        prefix = list(range(next_page, next_page + prefix_pages))
+        next_page += prefix_pages
+        extra = None
+        if extra_shared and members >= 2:
+            extra = next_page
+            next_page += 1
+        for m in range(members):
+            shared = prefix + ([extra] if extra is not None and m < 2 else [])
+            reqs.append((shared, int(rng.integers(1, suffix_max + 1))))
+    for _ in range(singles):
+        reqs.append(([], int(rng.integers(1, suffix_max + 1))))
+    order = rng.permutation(len(reqs))
+    reqs = [reqs[i] for i in order]
+    lists, lens = [], []
+    for shared, suf in reqs:
+        n = (suf + P - 1) // P
+        own = list(range(next_page, next_page + n))
+        next_page += n
+        lists.append(shared + own)
+        lens.append(P * len(shared) + suf)
+    pool = next_page + 3
+    perm = rng.permutation(pool).astype(np.int32)  # scatter the ids over the pool
+    lists = [[int(perm[x]) for x in pl] for pl in lists]
+    ip, ix, lp = _pack(lists, lens, P)
+    listed = set(int(x) for x in ix)
+    unused = np.array(sorted(set(range(pool)) - listed), dtype=np.int32)
+    shared_ids = sum(1 for v in np.unique(ix, return_counts=True)[1] if v > 1)
+    return Workload(f"prefix_{seed}", 0, len(lists), num_qo_heads, num_kv_heads, head_dim, P,
+                    dtype, pool, ip, ix, lp, unused, 20_000 + seed, shared_pages=shared_ids)

@@ -92,6 +92,9 @@ typedef struct {
   int32_t max_chunk_tokens;   /* cap on chunk length; 0 = no cap */
   int32_t fixed_chunk_tokens; /* >0: use exactly this chunk length (rounded up
                                  to whole pages) instead of the heuristic */
+  int32_t cascade;            /* shared-prefix cascade: 0 = when it pays
+                                 (see fi_plan_create), 1 = whenever requests
+                                 share a prefix, -1 = never */
 } fi_plan_opts;
 
 typedef struct {
@@ -105,9 +108,14 @@ typedef struct {
   int32_t min_chunks_split_request; /* fewest chunks among split requests; 0 if none */
   int32_t batch, num_qo_heads, num_kv_heads, head_dim, page_size;
   int32_t dtype;
-  int64_t shared_pages; /* physical pages listed more than once; when 0 the
-                           kernel streams K/V past the caches (nontemporal
-                           loads), else it keeps them cacheable for re-reads */
+  int64_t shared_pages; /* physical pages the decode items read more than
+                           once (a cascade's prefix pages excluded); when 0
+                           the kernel streams K/V past the caches
+                           (nontemporal loads), else it keeps them cacheable
+                           for re-reads */
+  int64_t num_prefix_items;  /* shared-prefix work items (0: no cascade) */
+  int32_t num_prefix_groups; /* groups of requests sharing a prefix */
+  int32_t prefix_rows_per_item; /* query rows one prefix item covers (128) */
 } fi_plan_info;
 
 /* Fields of one work item in the list returned by fi_plan_work_list. */
@@ -144,8 +152,36 @@ enum {
   FI_NODE_REQUEST = 4,
   FI_NODE_KV_HEAD = 5,
   FI_NODE_LEVEL = 6,      /* 0 for nodes whose children are chunks */
+  FI_NODE_ARRIVALS = 7,   /* children that report during the decode kernel:
+                             COUNT minus the shared-prefix partials, which
+                             are complete before it starts */
   FI_NODE_STRIDE = 8,
   FI_MERGE_FAN_IN = 32
+};
+
+/*
+ * Fields of one shared-prefix work item (fi_plan_prefix_items). Requests
+ * whose page lists start with the same physical pages form a group; the
+ * common run of whole pages (never a request's last page) is the group's
+ * prefix. A prefix item attends the query rows of up to
+ * prefix_rows_per_item / G members of one group (row r: member
+ * ROW_BEGIN + r / G, query head KV_HEAD * G + r % G) over one chunk of the
+ * prefix, and writes one partial state per member, into the first slots of
+ * that member's merge tree.
+ */
+enum {
+  FI_PITEM_GROUP = 0,
+  FI_PITEM_KV_HEAD = 1,
+  FI_PITEM_MEMBER_BASE = 2, /* index of the group's first member in the member list */
+  FI_PITEM_ROW_BEGIN = 3,   /* first member (within the group) of this item */
+  FI_PITEM_NUM_ROWS = 4,    /* query rows: members in this item x G */
+  FI_PITEM_CHUNK = 5,       /* prefix chunk number = child index in the trees */
+  FI_PITEM_PAGE_BEGIN = 6,  /* first page, as an index into kv_indices */
+  FI_PITEM_NUM_PAGES = 7,   /* at most FI_PREFIX_MAX_PAGES */
+  FI_PITEM_STRIDE = 8,
+  FI_PREFIX_MAX_PAGES = 256 /* a group's prefix is at most (FI_MERGE_FAN_IN - 1)
+                               chunks of this many pages; shared pages past
+                               that stay with the decode items */
 };
 
 /*
@@ -172,6 +208,15 @@ enum {
  * max_chunk_tokens. Items are ordered longest first (ties by request, KV
  * head, chunk) so that long chunks start early and short requests fill the
  * gaps. The input arrays are copied; the caller may free them afterwards.
+ *
+ * Shared prefixes (composable block-sparse formats, explainer's Block-Sparse
+ * section; cascade attention): for bf16, requests whose page lists begin with
+ * the same physical page are grouped and their common leading run of whole
+ * pages (excluding each request's last page) is attended once per KV head
+ * for all the group's query rows by a matrix-core kernel; each member's
+ * remaining pages go through the decode items, and the two states meet in
+ * the member's merge tree. With opts->cascade = 0 a group is formed when the
+ * prefix re-reads it saves, (members - 1) x prefix bytes, reach 8 MiB.
  */
 fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
                          const int32_t* kv_last_page_len, int32_t batch,
@@ -187,6 +232,10 @@ fi_status fi_plan_get_info(const fi_plan* plan, fi_plan_info* info);
  * Valid until fi_plan_destroy. */
 fi_status fi_plan_work_list(const fi_plan* plan, const int32_t** items, int64_t* num_items);
 fi_status fi_plan_merge_nodes(const fi_plan* plan, const int32_t** nodes, int64_t* num_nodes);
+/* Host view of the shared-prefix items (num_prefix_items * FI_PITEM_STRIDE
+ * int32) and of the member list (request ids, grouped). */
+fi_status fi_plan_prefix_items(const fi_plan* plan, const int32_t** items, int64_t* num_items);
+fi_status fi_plan_prefix_members(const fi_plan* plan, const int32_t** members, int64_t* num_members);
 
 /*
  * Copy the work list, merge nodes (with their arrival counters set to 0) and

@@ -13,7 +13,7 @@ import torch
 
 import block_sparse_kv_bsr_amd as fb
 import oracle.attention as oa
-from block_sparse_kv_bsr_amd.workloads import random_workload, workload
+from block_sparse_kv_bsr_amd.workloads import prefix_workload, random_workload, workload
 from tests.parity import compare
 
 pytestmark = pytest.mark.gpu
@@ -134,6 +134,45 @@ def test_merge_tree_levels(dtype, d, hq, hkv):
         o1, l1 = fb.decode(qi, k, v, p)
         torch.cuda.synchronize()
         assert torch.equal(o1, oi) and torch.equal(l1, li), f"run {i}"
+
+
+CASCADE = [
+    # seed, groups [(members, prefix pages)], singles, suffix_max, Hq, Hkv, d, P, fixed chunk
+    (1, [(5, 3)], 2, 40, 8, 2, 64, 4, 0),
+    (2, [(3, 1), (4, 6)], 3, 70, 16, 4, 128, 8, 16),
+    (3, [(40, 2)], 0, 20, 16, 4, 64, 4, 0),          # two row blocks of members
+    (4, [(2, 9)], 1, 9, 4, 4, 64, 3, 3),             # G 1, page size 3 (prefix 30 tokens)
+    (5, [(3, 4)], 0, 5, 32, 4, 128, 16, 0),          # G 8
+    (6, [(33, 40), (2, 3)], 4, 300, 32, 8, 128, 16, 64),  # 40-page prefix, 31 chunks
+    (7, [(6, 5)], 2, 700, 32, 8, 128, 64, 0),        # page size 64
+]
+
+
+@pytest.mark.parametrize("case", CASCADE, ids=lambda c: f"cascade{c[0]}")
+def test_cascade(case):
+    """Shared prefixes through the matrix-core prefix kernel (forced on), then
+    the decode kernel and its merge trees; repeated runs on one workspace give
+    identical results."""
+    seed, groups, singles, smax, hq, hkv, d, P, fixed = case
+    w = prefix_workload(seed, groups, singles, smax, hq, hkv, d, P, "bf16")
+    p, (q, k, v), (o0, l0) = run_case(w, what=f"cascade{seed}", cascade=1, fixed_chunk_tokens=fixed)
+    assert p.info["num_prefix_items"] > 0
+    for _ in range(2):
+        o1, l1 = fb.decode(q, k, v, p)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o0) and torch.equal(l1, l0)
+
+
+def test_cascade_matches_plain_decode_on_shared_prefix_workload():
+    """The sparse shared-prefix workload with and without the cascade: both
+    within tolerance of the oracle (run_case), and of each other."""
+    w = workload(5)
+    p1, vals, (o1, l1) = run_case(w, device_values=True, what="config5-cascade")
+    assert p1.info["num_prefix_items"] > 0
+    p0, _, (o0, l0) = run_case(w, device_values=True, what="config5-plain", cascade=-1)
+    assert p0.info["num_prefix_items"] == 0
+    assert (o1.float() - o0.float()).abs().max().item() <= 2 * 2 ** -7
+    assert (l1 - l0).abs().max().item() <= 1e-4
 
 
 def test_deterministic_for_fixed_plan():
