@@ -108,6 +108,7 @@ def cpu_baseline(w, q, k, v, min_seconds=10.0, max_passes=3):
     """Time the float64 oracle on the host over whole batches of the same
     workload (inputs copied to host memory first, not timed)."""
     import numpy as np
+    import torch
     sys.path.insert(0, ROOT)
     import oracle.attention as oa
     try:
@@ -115,7 +116,12 @@ def cpu_baseline(w, q, k, v, min_seconds=10.0, max_passes=3):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # threadpoolctl missing: numpy BLAS default
         threads = os.cpu_count() or 1
-    qh, kh, vh = q.float().cpu().numpy(), k.float().cpu().numpy(), v.float().cpu().numpy()
+    qh = q.float().cpu().numpy()
+    if w.dtype == "fp8":  # the oracle attends over the dequantised cache
+        kh = oa.dequantize_e4m3(k.view(torch.uint8).cpu().numpy(), w.k_scale)
+        vh = oa.dequantize_e4m3(v.view(torch.uint8).cpu().numpy(), w.v_scale)
+    else:
+        kh, vh = k.float().cpu().numpy(), v.float().cpu().numpy()
     times = []
     while len(times) < max_passes and sum(times) < min_seconds:
         t0 = time.perf_counter()
@@ -198,7 +204,7 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record()
-        fb.decode(q, k, v, p, out=out, lse=lse, workspace=ws)
+        fb.decode(q, k, v, p, out=out, lse=lse, workspace=ws, k_scale=w.k_scale, v_scale=w.v_scale)
         if ev:
             ev[1].record()
 
@@ -234,7 +240,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": {"bf16": "bf16", "f32": "f32", "fp8": "fp8_e4m3 K/V, bf16 q/out"}[w.dtype],
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_qo_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,

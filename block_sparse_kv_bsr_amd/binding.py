@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libfi_bsr.so")
 FI_OK = 0
 FI_DTYPE_F32 = 0
 FI_DTYPE_BF16 = 1
+FI_DTYPE_FP8_E4M3 = 2
 ITEM_STRIDE = 16
 NODE_STRIDE = 8
 PITEM_STRIDE = 8
@@ -30,7 +31,7 @@ STATUS_NAMES = {0: "FI_OK", -1: "FI_ERR_INVALID_ARG", -2: "FI_ERR_UNSUPPORTED",
 # Every symbol include/fi_bsr.h declares.
 EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_merge_nodes",
             "fi_plan_prefix_items", "fi_plan_prefix_members", "fi_plan_upload", "fi_decode_run",
-            "fi_merge_states", "fi_plan_destroy", "fi_last_error"]
+            "fi_decode_run_scaled", "fi_merge_states", "fi_plan_destroy", "fi_last_error"]
 
 
 class FiError(RuntimeError):
@@ -89,6 +90,9 @@ def lib() -> ctypes.CDLL:
     L.fi_plan_upload.restype = i32
     L.fi_decode_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
     L.fi_decode_run.restype = i32
+    f32 = ctypes.c_float
+    L.fi_decode_run_scaled.argtypes = [vp, vp, vp, vp, f32, f32, vp, vp, f32, vp, sz, vp]
+    L.fi_decode_run_scaled.restype = i32
     L.fi_merge_states.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, vp]
     L.fi_merge_states.restype = i32
     L.fi_plan_destroy.argtypes = [vp]
@@ -122,6 +126,8 @@ def _dtype_code(dtype) -> int:
         return FI_DTYPE_BF16
     if name in ("f32", "torch.float32", "float32"):
         return FI_DTYPE_F32
+    if name in ("fp8", "fp8_e4m3", "torch.float8_e4m3fn", "float8_e4m3fn"):
+        return FI_DTYPE_FP8_E4M3
     raise ValueError(f"unsupported dtype {dtype}")
 
 
@@ -233,8 +239,10 @@ def _decode_args(q, k_pages, v_pages, plan_: Plan, out, lse, workspace, stream):
     info = plan_.info
     B, Hq, d = info["batch"], info["num_qo_heads"], info["head_dim"]
     want = torch.float32 if info["dtype"] == FI_DTYPE_F32 else torch.bfloat16
-    if q.dtype != want or k_pages.dtype != want or v_pages.dtype != want:
-        raise ValueError(f"q, k_pages and v_pages must be {want}")
+    want_kv = {FI_DTYPE_F32: (torch.float32,), FI_DTYPE_BF16: (torch.bfloat16,),
+               FI_DTYPE_FP8_E4M3: (torch.float8_e4m3fn, torch.uint8)}[info["dtype"]]
+    if q.dtype != want or k_pages.dtype not in want_kv or v_pages.dtype not in want_kv:
+        raise ValueError(f"q must be {want} and k_pages, v_pages one of {want_kv}")
     if tuple(q.shape) != (B, Hq, d):
         raise ValueError(f"q must have shape {(B, Hq, d)}, got {tuple(q.shape)}")
     kshape = (k_pages.shape[0], info["num_kv_heads"], info["page_size"], d)
@@ -252,17 +260,19 @@ def _decode_args(q, k_pages, v_pages, plan_: Plan, out, lse, workspace, stream):
 
 
 def decode(q, k_pages, v_pages, plan_: Plan, out=None, lse=None, sm_scale: Optional[float] = None,
-           workspace=None, stream=None):
-    """fi_decode_run: returns (out [B, H_q, d] in q's dtype, lse [B, H_q] float32)."""
+           workspace=None, stream=None, k_scale: float = 1.0, v_scale: float = 1.0):
+    """fi_decode_run_scaled: returns (out [B, H_q, d] in q's dtype, lse [B, H_q]
+    float32). k_scale / v_scale dequantise an fp8 KV cache."""
     out, lse, workspace = _decode_args(q, k_pages, v_pages, plan_, out, lse, workspace, stream)
     s = ctypes.c_void_p(_stream(stream))
     ws = ctypes.c_void_p(workspace.data_ptr())
     nbytes = workspace.numel() * workspace.element_size()
     o, l = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr())
     scale = float(sm_scale) if sm_scale else 0.0
-    _check(lib().fi_decode_run(plan_.handle, ctypes.c_void_p(q.data_ptr()),
-                               ctypes.c_void_p(k_pages.data_ptr()),
-                               ctypes.c_void_p(v_pages.data_ptr()), o, l, scale, ws, nbytes, s))
+    _check(lib().fi_decode_run_scaled(plan_.handle, ctypes.c_void_p(q.data_ptr()),
+                                      ctypes.c_void_p(k_pages.data_ptr()),
+                                      ctypes.c_void_p(v_pages.data_ptr()), float(k_scale),
+                                      float(v_scale), o, l, scale, ws, nbytes, s))
     return out, lse
 
 

@@ -82,8 +82,8 @@ fi_status check_inputs(const fi_plan* plan, const void* q, const void* k_pages,
 }
 
 fi_status launch_run(const fi_plan* plan, const void* q, const void* k_pages,
-                     const void* v_pages, void* out, float* lse, float sm_scale,
-                     void* workspace, hipStream_t s) {
+                     const void* v_pages, float k_scale, float v_scale, void* out, float* lse,
+                     float sm_scale, void* workspace, hipStream_t s) {
   if (!(sm_scale > 0.f)) sm_scale = 1.0f / std::sqrt((float)plan->head_dim);
   char* ws = static_cast<char*>(workspace);
   fi::DecodeArgs d{};
@@ -104,7 +104,9 @@ fi_status launch_run(const fi_plan* plan, const void* q, const void* k_pages,
   d.head_dim = plan->head_dim;
   d.page_size = plan->page_size;
   d.group = plan->group;
-  d.bf16 = plan->dtype == FI_DTYPE_BF16;
+  d.kv_bytes = plan->dtype == FI_DTYPE_F32 ? 4 : plan->dtype == FI_DTYPE_BF16 ? 2 : 1;
+  d.k_scale = k_scale;
+  d.v_scale = v_scale;
   d.stream_kv = plan->shared_pages == 0;
   d.sm_scale = sm_scale;
   if (plan->num_pitems() > 0) {
@@ -137,17 +139,27 @@ fi_status launch_run(const fi_plan* plan, const void* q, const void* k_pages,
 
 }  // namespace
 
-fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
-                        const void* v_pages, void* out, float* lse, float sm_scale,
-                        void* workspace, size_t workspace_bytes, fi_stream_t stream) {
+fi_status fi_decode_run_scaled(const fi_plan* plan, const void* q, const void* k_pages,
+                               const void* v_pages, float k_scale, float v_scale, void* out,
+                               float* lse, float sm_scale, void* workspace,
+                               size_t workspace_bytes, fi_stream_t stream) {
   if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || std::isinf(k_scale) || std::isinf(v_scale))
+    return fail(FI_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (plan->batch == 0) return FI_OK;
   fi_status st = check_inputs(plan, q, k_pages, v_pages);
   if (st != FI_OK) return st;
   st = check_run(plan, out, lse, workspace, workspace_bytes);
   if (st != FI_OK) return st;
-  return launch_run(plan, q, k_pages, v_pages, out, lse, sm_scale, workspace,
+  return launch_run(plan, q, k_pages, v_pages, k_scale, v_scale, out, lse, sm_scale, workspace,
                     static_cast<hipStream_t>(stream));
+}
+
+fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
+                        const void* v_pages, void* out, float* lse, float sm_scale,
+                        void* workspace, size_t workspace_bytes, fi_stream_t stream) {
+  return fi_decode_run_scaled(plan, q, k_pages, v_pages, 1.f, 1.f, out, lse, sm_scale, workspace,
+                              workspace_bytes, stream);
 }
 
 fi_status fi_merge_states(fi_dtype dtype, const void* v_a, const float* s_a, const void* v_b,

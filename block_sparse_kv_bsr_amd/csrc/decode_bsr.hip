@@ -60,6 +60,7 @@ constexpr float kRescaleMargin = 8.0f;
 constexpr int kIdWindow = 256;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 struct DecodeParams {
   const int32_t* items;
@@ -79,7 +80,8 @@ struct DecodeParams {
   int32_t page_size;
   int32_t step_pages;   // 8 tokens = step_pages pages + step_slots slots
   int32_t step_slots;
-  float scale_log2;     // sm_scale * log2(e)
+  float scale_log2;     // sm_scale * k_scale * log2(e)
+  float v_scale;        // multiplies the output (V dequantisation)
 };
 
 template <int kCtrl>
@@ -166,15 +168,25 @@ __device__ __forceinline__ uint32_t word(const u32x4_t& v, int w) {
   return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
 }
 
-template <bool kBF16, int D>
+// Geometry of one token row. kKv = bytes per K/V element: 4 (fp32 cache, fp32
+// q/out), 2 (bf16 cache, bf16 q/out) or 1 (fp8 e4m3 cache, bf16 q/out). Lane
+// `sub` of a row holds the elements of dims j*kDimStride + sub*kPerLoad ..
+// +kPerLoad-1 for j < kLoads: one 16-byte K/V load each, and the q elements of
+// the same dims.
+template <int kKv, int D>
 struct Row {
-  static constexpr int kElemBytes = kBF16 ? 2 : 4;
-  static constexpr int kBytes = D * kElemBytes;          // one token row
-  static constexpr int kLoads = kBytes / 128;            // 16-byte loads per lane
-  static constexpr int kWords = kLoads * 4;              // 32-bit words per lane
+  static constexpr bool kQoBF16 = kKv < 4;               // q and out in bf16
+  static constexpr int kQoBytes = kQoBF16 ? 2 : 4;
+  static constexpr int kBytes = D * kQoBytes;            // one q / out row
+  static constexpr int kKvBytes = D * kKv;               // one K / V row
+  static constexpr int kLoads = kKvBytes / 128;          // 16-byte K/V loads per lane
+  static constexpr int kKvWords = kLoads * 4;            // K/V words per lane
   static constexpr int kElems = D / 8;                   // elements per lane
-  static constexpr int kPerLoad = 16 / kElemBytes;       // elements per load
-  static_assert(kLoads >= 1, "row shorter than 128 bytes");
+  static constexpr int kPerLoad = 16 / kKv;              // elements per K/V load
+  static constexpr int kDimStride = 128 / kKv;           // dims between a lane's loads
+  static constexpr int kWords = kElems * kQoBytes / 4;   // q words per lane
+  static constexpr int kQLoads = kPerLoad * kQoBytes / 16;  // 16-byte q loads per K/V load
+  static_assert(kLoads >= 1, "K/V row shorter than 128 bytes");
 };
 
 // Cross-lane exchanges over lane bits 5, 4 and 3 without the LDS path.
@@ -254,7 +266,7 @@ __device__ __forceinline__ float2 load_shared2(const float* p) {
 // The wave is its whole work-group and a wave's LDS accesses execute in
 // order, so the weights need only a compiler barrier, not s_barrier (whose
 // fence would wait for the output loads still in flight).
-template <bool kBF16, int D, int G>
+template <int kKv, int D, int G>
 __device__ void finish_split(const DecodeParams& p, int node, int lane, float* s_w) {
   constexpr int kF = G * D;                           // floats per slot
   constexpr int NC = (kF / 2 + 63) / 64;              // float pairs per lane
@@ -348,9 +360,9 @@ __device__ void finish_split(const DecodeParams& p, int node, int lane, float* s
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int f = 2 * lane + 128 * c;
-        const float inv = 1.f / __shfl(ws, hc[c]);
+        const float inv = p.v_scale / __shfl(ws, hc[c]);
         if (kF >= 128 || f < kF) {
-          if constexpr (kBF16)
+          if constexpr (Row<kKv, D>::kQoBF16)
             *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.out) + row0 * D + f) =
                 pack_bf16(acc[c].x * inv, acc[c].y * inv);
           else
@@ -385,10 +397,14 @@ __device__ void finish_split(const DecodeParams& p, int node, int lane, float* s
 // from LDS (16*L), softmax state and ~48 for addressing and temporaries.
 // LDS per wave: kRing stages of 2*L KiB plus the page-id window. Waves per SIMD:
 // as many as both budgets allow, at most 3.
-template <bool kBF16, int D, int G, bool kStream>
+template <int kKv, int D, int G, bool kStream>
 struct Tune {
-  using R = Row<kBF16, D>;
-  static constexpr int kRing = kStream ? 2 : 4;
+  using R = Row<kKv, D>;
+  // An fp8 stage holds half the bytes of a bf16 one and its waves spend less
+  // time per step; 8 stages (16 KiB in flight per wave, the most that still
+  // fits 2 waves per SIMD in LDS) measured 17% faster than 4 on the skewed
+  // batch.
+  static constexpr int kRing = kKv == 1 ? 8 : (kStream ? 2 : 4);
   static constexpr int kRegs = G * R::kElems + G * R::kWords + 16 * R::kLoads + 2 * G + 48;
   static constexpr int kByRegs = kRegs <= 168 ? 3 : (kRegs <= 240 ? 2 : 1);
   static constexpr int kLdsPerWave = kRing * 2 * R::kLoads * 1024 + kIdWindow * 4;
@@ -396,9 +412,9 @@ struct Tune {
   static constexpr int kWaves = kByRegs < kByLds ? kByRegs : (kByLds >= 1 ? kByLds : 1);
 };
 
-template <bool kBF16, int D, int G, int kRing, int kWaves, bool kStream, bool kUniform>
+template <int kKv, int D, int G, int kRing, int kWaves, bool kStream, bool kUniform>
 __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) {
-  using R = Row<kBF16, D>;
+  using R = Row<kKv, D>;
   constexpr int L = R::kLoads;
   constexpr int NW = R::kWords;
   constexpr int NE = R::kElems;
@@ -421,7 +437,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
     if (tg < G) {
       const int64_t qrow = (int64_t)b * p.num_qo_heads + (int64_t)kvh * G + tg;
 #pragma unroll
-      for (int j = 0; j < R::kLoads; ++j)
+      for (int j = 0; j < R::kBytes / 128; ++j)
         *reinterpret_cast<uint4*>(p.out + qrow * R::kBytes + j * 128 + sub * 16) = make_uint4(0, 0, 0, 0);
       if (sub == 0 && p.lse) p.lse[qrow] = -INFINITY;
     }
@@ -459,11 +475,16 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   for (int h = 0; h < G; ++h) {
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-      const uint4 v = load16(p.q + (qrow0 + h) * R::kBytes + j * 128 + sub * 16);
-      qw[h][j * 4 + 0] = v.x;
-      qw[h][j * 4 + 1] = v.y;
-      qw[h][j * 4 + 2] = v.z;
-      qw[h][j * 4 + 3] = v.w;
+#pragma unroll
+      for (int x = 0; x < R::kQLoads; ++x) {
+        const int dim = j * R::kDimStride + sub * R::kPerLoad;
+        const uint4 v = load16(p.q + (qrow0 + h) * R::kBytes + dim * R::kQoBytes + x * 16);
+        const int w0 = (j * R::kQLoads + x) * 4;
+        qw[h][w0 + 0] = v.x;
+        qw[h][w0 + 1] = v.y;
+        qw[h][w0 + 2] = v.z;
+        qw[h][w0 + 3] = v.w;
+      }
     }
   }
 
@@ -498,7 +519,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
       fill_window(wbase);
     }
     const int pid = s_ids[pl - wbase];
-    const int64_t off = (int64_t)pid * p.page_stride + head_off + (int64_t)sl * R::kBytes;
+    const int64_t off = (int64_t)pid * p.page_stride + head_off + (int64_t)sl * R::kKvBytes;
     const char* kp = p.k_pages + off;
     const char* vp = p.v_pages + off;
 #pragma unroll
@@ -524,7 +545,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   const int last_step = ngroups - 1;
   const int u_last_pl = (last_step * 8) / P;
   const int u_last_slot = last_step * 8 - u_last_pl * P;
-  const int lane_off = tg * R::kBytes + sub * 16;
+  const int lane_off = tg * R::kKvBytes + sub * 16;
   const int64_t kvh_off = (int64_t)kvh * p.head_stride;
   int u_pl = 0, u_slot = 0, u_cached_pl = 0, u_pid = first_pid;
   auto issue_uniform = [&](int g, int stage) {
@@ -540,7 +561,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
       u_pid = __builtin_amdgcn_readfirstlane(s_ids[pl - wbase]);
       u_cached_pl = pl;
     }
-    const int64_t base = (int64_t)u_pid * p.page_stride + kvh_off + (int64_t)sl * R::kBytes;
+    const int64_t base = (int64_t)u_pid * p.page_stride + kvh_off + (int64_t)sl * R::kKvBytes;
     const char* kp = p.k_pages + base;
     const char* vp = p.v_pages + base;
 #pragma unroll
@@ -583,14 +604,27 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float d = 0.f;
+      if constexpr (kKv == 1) {
+        // 4 fp8 per K word, widened exactly to two bf16 pairs (converted
+        // once per word and reused by all G heads)
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const uint32_t kw = word(kr[w / 4], w % 4);
-        if constexpr (kBF16) {
-          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kw),
-                                              __builtin_bit_cast(bf16x2_t, qw[h][w]), d, false);
-        } else {
-          d = __builtin_fmaf(__uint_as_float(kw), __uint_as_float(qw[h][w]), d);
+        for (int w = 0; w < R::kKvWords; ++w) {
+          const uint32_t kw = word(kr[w / 4], w % 4);
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw, 1.0f, false),
+                                              __builtin_bit_cast(bf16x2_t, qw[h][2 * w]), d, false);
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw, 1.0f, true),
+                                              __builtin_bit_cast(bf16x2_t, qw[h][2 * w + 1]), d, false);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const uint32_t kw = word(kr[w / 4], w % 4);
+          if constexpr (kKv == 2) {
+            d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kw),
+                                                __builtin_bit_cast(bf16x2_t, qw[h][w]), d, false);
+          } else {
+            d = __builtin_fmaf(__uint_as_float(kw), __uint_as_float(qw[h][w]), d);
+          }
         }
       }
       s[h] = sum8(d) * p.scale_log2;
@@ -629,9 +663,19 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
       l[h] += pw[h];
     }
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
+    for (int w = 0; w < R::kKvWords; ++w) {
       const uint32_t vw = word(vr[w / 4], w % 4);
-      if constexpr (kBF16) {
+      if constexpr (kKv == 1) {
+        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(vw, false);
+        const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(vw, true);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          acc[h][4 * w] = __builtin_fmaf(pw[h], lo[0], acc[h][4 * w]);
+          acc[h][4 * w + 1] = __builtin_fmaf(pw[h], lo[1], acc[h][4 * w + 1]);
+          acc[h][4 * w + 2] = __builtin_fmaf(pw[h], hi[0], acc[h][4 * w + 2]);
+          acc[h][4 * w + 3] = __builtin_fmaf(pw[h], hi[1], acc[h][4 * w + 3]);
+        }
+      } else if constexpr (kKv == 2) {
         const float v0 = bf16_lo(vw), v1 = bf16_hi(vw);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -753,6 +797,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   {
     constexpr int PL = R::kPerLoad;
     constexpr int SEG = VB < PL ? VB : PL;  // elements per contiguous piece
+    static_assert(SEG <= 4 || SEG % 8 == 0 || !R::kQoBF16, "bf16 pieces are 1, 2, 4 or 8k elements");
     const int hq = tg * VB / NE;
     const int e0 = tg * VB % NE;
     float mh = 0.f, lh = 1.f;
@@ -763,7 +808,9 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
         lh = l[h];
       }
     }
-    const float inv = 1.f / lh;
+    // V's dequantisation scale is applied once, where a final output is
+    // written (here, or at the root of a merge tree); partials stay unscaled
+    const float inv = (slot < 0 ? p.v_scale : 1.f) / lh;
 #pragma unroll
     for (int i = 0; i < VB; ++i) a[i] *= inv;
     const int64_t qrow = qrow0 + hq;
@@ -771,12 +818,12 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
 #pragma unroll
     for (int sgi = 0; sgi < VB / SEG; ++sgi) {
       const int e = e0 + sgi * SEG;
-      // element e sits at dim (e / PL) * (128 / eb) + sub * PL + e % PL
-      const int dim = (e / PL) * (128 / R::kElemBytes) + sub * PL + e % PL;
+      // element e sits at dim (e / PL) * kDimStride + sub * PL + e % PL
+      const int dim = (e / PL) * R::kDimStride + sub * PL + e % PL;
       const float* x = a + sgi * SEG;
       if (slot < 0) {
-        char* dst = p.out + qrow * R::kBytes + dim * R::kElemBytes;
-        if constexpr (kBF16) {
+        char* dst = p.out + qrow * R::kBytes + dim * R::kQoBytes;
+        if constexpr (R::kQoBF16) {
           if constexpr (SEG == 1) {
             *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(pack_bf16(x[0], 0.f) & 0xFFFFu);
           } else if constexpr (SEG == 2) {
@@ -784,8 +831,11 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
           } else if constexpr (SEG == 4) {
             *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
           } else {
-            *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]),
-                                                        pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7]));
+#pragma unroll
+            for (int c = 0; c < SEG; c += 8)
+              *reinterpret_cast<uint4*>(dst + 2 * c) =
+                  make_uint4(pack_bf16(x[c], x[c + 1]), pack_bf16(x[c + 2], x[c + 3]),
+                             pack_bf16(x[c + 4], x[c + 5]), pack_bf16(x[c + 6], x[c + 7]));
           }
         } else {
           if constexpr (SEG == 1) *reinterpret_cast<float*>(dst) = x[0];
@@ -830,36 +880,36 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
       }
     }
     static_assert(kIdWindow >= FI_MERGE_FAN_IN * G, "merge weights reuse the page-id window");
-    finish_split<kBF16, D, G>(p, node, lane, reinterpret_cast<float*>(s_ids));
+    finish_split<kKv, D, G>(p, node, lane, reinterpret_cast<float*>(s_ids));
   }
 }
 
-template <bool kBF16, int D, int G, bool kStream>
+template <int kKv, int D, int G, bool kStream>
 hipError_t launch_variant(const DecodeParams& prm, int64_t num_items, hipStream_t stream) {
-  using T = Tune<kBF16, D, G, kStream>;
+  using T = Tune<kKv, D, G, kStream>;
   if (prm.page_size % 8 == 0)
-    hipLaunchKernelGGL((decode_bsr_kernel<kBF16, D, G, T::kRing, T::kWaves, kStream, true>),
+    hipLaunchKernelGGL((decode_bsr_kernel<kKv, D, G, T::kRing, T::kWaves, kStream, true>),
                        dim3((uint32_t)num_items), dim3(64), 0, stream, prm);
   else
-    hipLaunchKernelGGL((decode_bsr_kernel<kBF16, D, G, T::kRing, T::kWaves, kStream, false>),
+    hipLaunchKernelGGL((decode_bsr_kernel<kKv, D, G, T::kRing, T::kWaves, kStream, false>),
                        dim3((uint32_t)num_items), dim3(64), 0, stream, prm);
   return hipGetLastError();
 }
 
-template <bool kBF16, int D, int G>
+template <int kKv, int D, int G>
 hipError_t launch_typed(const DecodeParams& prm, int64_t num_items, bool stream_kv,
                         hipStream_t stream) {
-  return stream_kv ? launch_variant<kBF16, D, G, true>(prm, num_items, stream)
-                   : launch_variant<kBF16, D, G, false>(prm, num_items, stream);
+  return stream_kv ? launch_variant<kKv, D, G, true>(prm, num_items, stream)
+                   : launch_variant<kKv, D, G, false>(prm, num_items, stream);
 }
 
-template <bool kBF16, int D>
+template <int kKv, int D>
 hipError_t launch_group(const DecodeParams& prm, int64_t n, int G, bool st, hipStream_t s) {
   switch (G) {
-    case 1: return launch_typed<kBF16, D, 1>(prm, n, st, s);
-    case 2: return launch_typed<kBF16, D, 2>(prm, n, st, s);
-    case 4: return launch_typed<kBF16, D, 4>(prm, n, st, s);
-    case 8: return launch_typed<kBF16, D, 8>(prm, n, st, s);
+    case 1: return launch_typed<kKv, D, 1>(prm, n, st, s);
+    case 2: return launch_typed<kKv, D, 2>(prm, n, st, s);
+    case 4: return launch_typed<kKv, D, 4>(prm, n, st, s);
+    case 8: return launch_typed<kKv, D, 8>(prm, n, st, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -868,8 +918,7 @@ hipError_t launch_group(const DecodeParams& prm, int64_t n, int G, bool st, hipS
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_items <= 0) return hipSuccess;
-  const int eb = a.bf16 ? 2 : 4;
-  const int row = a.head_dim * eb;
+  const int row = a.head_dim * a.kv_bytes;  // one K/V row
   DecodeParams prm;
   prm.items = a.items;
   prm.page_ids = a.page_ids;
@@ -888,13 +937,17 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   prm.page_size = a.page_size;
   prm.step_pages = 8 / a.page_size;
   prm.step_slots = 8 % a.page_size;
-  prm.scale_log2 = a.sm_scale * kLog2e;
-  if (a.bf16) {
-    if (a.head_dim == 128) return launch_group<true, 128>(prm, a.num_items, a.group, a.stream_kv, stream);
-    if (a.head_dim == 64) return launch_group<true, 64>(prm, a.num_items, a.group, a.stream_kv, stream);
-  } else {
-    if (a.head_dim == 128) return launch_group<false, 128>(prm, a.num_items, a.group, a.stream_kv, stream);
-    if (a.head_dim == 64) return launch_group<false, 64>(prm, a.num_items, a.group, a.stream_kv, stream);
+  // the K dequantisation scale multiplies every score, the V one the output
+  prm.scale_log2 = a.sm_scale * a.k_scale * kLog2e;
+  prm.v_scale = a.v_scale;
+  if (a.kv_bytes == 2) {
+    if (a.head_dim == 128) return launch_group<2, 128>(prm, a.num_items, a.group, a.stream_kv, stream);
+    if (a.head_dim == 64) return launch_group<2, 64>(prm, a.num_items, a.group, a.stream_kv, stream);
+  } else if (a.kv_bytes == 4) {
+    if (a.head_dim == 128) return launch_group<4, 128>(prm, a.num_items, a.group, a.stream_kv, stream);
+    if (a.head_dim == 64) return launch_group<4, 64>(prm, a.num_items, a.group, a.stream_kv, stream);
+  } else if (a.kv_bytes == 1) {
+    if (a.head_dim == 128) return launch_group<1, 128>(prm, a.num_items, a.group, a.stream_kv, stream);
   }
   return hipErrorInvalidValue;
 }

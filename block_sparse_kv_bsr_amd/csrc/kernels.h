@@ -21,9 +21,10 @@ struct DecodeArgs {
   int32_t* counters;        // arrivals per merge node
   int64_t num_items;
   int32_t num_qo_heads, num_kv_heads, head_dim, page_size, group;
-  bool bf16;
+  int32_t kv_bytes;          // 4 fp32, 2 bf16, 1 fp8 e4m3 (q/out bf16)
   bool stream_kv;           // nontemporal K/V loads (no page listed twice)
   float sm_scale;
+  float k_scale, v_scale;   // K/V dequantisation scales (1 unless fp8)
 };
 
 struct PrefixArgs {

@@ -81,8 +81,10 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
       return fail(FI_ERR_UNSUPPORTED, "GQA group size must be 1, 2, 4 or 8");
     if (head_dim != 64 && head_dim != 128)
       return fail(FI_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
-    if (dtype != FI_DTYPE_F32 && dtype != FI_DTYPE_BF16)
-      return fail(FI_ERR_UNSUPPORTED, "dtype must be FI_DTYPE_F32 or FI_DTYPE_BF16");
+    if (dtype != FI_DTYPE_F32 && dtype != FI_DTYPE_BF16 && dtype != FI_DTYPE_FP8_E4M3)
+      return fail(FI_ERR_UNSUPPORTED, "dtype must be FI_DTYPE_F32, FI_DTYPE_BF16 or FI_DTYPE_FP8_E4M3");
+    if (dtype == FI_DTYPE_FP8_E4M3 && head_dim != 128)
+      return fail(FI_ERR_UNSUPPORTED, "an fp8 KV cache needs head_dim 128");
     if (page_size < 1 || page_size > 4096)
       return fail(FI_ERR_INVALID_ARG, "page_size must be in [1, 4096]");
     if (num_pool_pages < 0) return fail(FI_ERR_INVALID_ARG, "num_pool_pages < 0");

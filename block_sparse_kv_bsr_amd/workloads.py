@@ -44,7 +44,13 @@ CONFIG_NAMES = {
     3: "skewed_b64_loguniform_32_32768",
     4: "long_b2_l131072_65536",
     5: "sparse_prefix_b32_p64",
+    6: "skewed_b64_loguniform_32_32768_fp8kv",
 }
+
+# fp8 KV caches hold x / FP8_SCALE rounded to OCP E4M3 (torch's cast, round
+# to nearest even; |x / scale| <= 448 for |x| <= 7); the kernel multiplies by
+# the scale again.
+FP8_SCALE = 1.0 / 64.0
 
 
 @dataclasses.dataclass
@@ -56,7 +62,7 @@ class Workload:
     num_kv_heads: int
     head_dim: int
     page_size: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "fp8" (K/V fp8 e4m3 with q/out bf16)
     num_pool_pages: int
     kv_indptr: np.ndarray
     kv_indices: np.ndarray
@@ -66,6 +72,9 @@ class Workload:
     value_seed: int
     # physical pages listed by more than one request (config 5 prefix)
     shared_pages: int = 0
+    # dequantisation scales of an fp8 KV cache (1 otherwise)
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def sm_scale(self) -> float:
@@ -77,7 +86,13 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
+        """Bytes per q / out element."""
         return 4 if self.dtype == "f32" else 2
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        """Bytes per K / V element in the cache."""
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
 
     def num_pages(self, b: int) -> int:
         return int(self.kv_indptr[b + 1] - self.kv_indptr[b])
@@ -95,13 +110,12 @@ class Workload:
         """Bytes the method must move: each active K and V row once per KV
         head, plus reading q and writing the output. With ``unique`` a
         physical page listed by several requests counts once (shared prefix)."""
-        e = self.elem_bytes
         if unique:
             tok = self._unique_tokens()
         else:
             tok = int(self.kv_lens().sum())
-        kv = 2 * self.num_kv_heads * self.head_dim * tok * e
-        qo = 2 * self.batch * self.num_qo_heads * self.head_dim * e
+        kv = 2 * self.num_kv_heads * self.head_dim * tok * self.kv_elem_bytes
+        qo = 2 * self.batch * self.num_qo_heads * self.head_dim * self.elem_bytes
         return kv + qo
 
     def _unique_tokens(self) -> int:
@@ -118,7 +132,9 @@ class Workload:
 
     # ------------------------------------------------------------------ values
     def make_values(self, device="cpu"):
-        """Return (q, k_pool, v_pool) as torch tensors on ``device``."""
+        """Return (q, k_pool, v_pool) as torch tensors on ``device``. For an
+        fp8 cache the pools are float8_e4m3fn holding x / k_scale (resp.
+        v_scale) of the same float32 draws."""
         import torch
 
         tdt = torch.float32 if self.dtype == "f32" else torch.bfloat16
@@ -133,6 +149,12 @@ class Workload:
             return x.to(tdt)
 
         q = draw((B, Hq, d))
+        if self.dtype == "fp8":
+            def draw_fp8(shape, scale):
+                x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+                self._poison(x, device)  # NaN stays NaN through the cast
+                return (x / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+            return q, draw_fp8((N, Hkv, P, d), self.k_scale), draw_fp8((N, Hkv, P, d), self.v_scale)
         k = draw((N, Hkv, P, d))
         v = draw((N, Hkv, P, d))
         self._poison(k, device)
@@ -210,6 +232,10 @@ def workload(config_id: int) -> Workload:
         return Workload(CONFIG_NAMES[4], 4, 2, 32, 8, 128, 64, "bf16", 3072, ip, ix, lp, un, seed)
     if config_id == 5:
         return _sparse_prefix(rng, seed)
+    if config_id == 6:  # the skewed batch over an fp8 KV cache
+        w = workload(3)
+        return dataclasses.replace(w, name=CONFIG_NAMES[6], config_id=6, dtype="fp8",
+                                   value_seed=seed, k_scale=FP8_SCALE, v_scale=FP8_SCALE)
     raise ValueError(f"unknown config {config_id}")
 
 
@@ -261,8 +287,10 @@ def random_workload(seed: int, batch: int, max_len: int, num_qo_heads: int,
     npg = sum((L + page_size - 1) // page_size for L in lens)
     pool = npg + spare_pages
     ip, ix, lp, un = paged_structure(lens, page_size, pool, rng)
+    scale = FP8_SCALE if dtype == "fp8" else 1.0
     return Workload(f"random_{seed}", 0, batch, num_qo_heads, num_kv_heads, head_dim,
-                    page_size, dtype, pool, ip, ix, lp, un, 10_000 + seed)
+                    page_size, dtype, pool, ip, ix, lp, un, 10_000 + seed,
+                    k_scale=scale, v_scale=scale)
 
 
 def prefix_workload(seed: int, groups: List[tuple], singles: int, suffix_max: int,

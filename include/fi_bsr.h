@@ -77,7 +77,15 @@ typedef enum {
   FI_ERR_STATE = -6        /* plan not uploaded to this workspace */
 } fi_status;
 
-typedef enum { FI_DTYPE_F32 = 0, FI_DTYPE_BF16 = 1 } fi_dtype;
+/*
+ * Element types of a plan. FI_DTYPE_FP8_E4M3 is a quantised KV cache (the
+ * quantisation/dequantisation fused into the attention kernel, explainer's
+ * JIT section): K and V pages hold OCP FP8 E4M3 bytes (1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN) that
+ * stand for byte_value * k_scale (resp. v_scale); q and out are bf16;
+ * head_dim 128 only. fi_merge_states takes FI_DTYPE_F32 or FI_DTYPE_BF16.
+ */
+typedef enum { FI_DTYPE_F32 = 0, FI_DTYPE_BF16 = 1, FI_DTYPE_FP8_E4M3 = 2 } fi_dtype;
 
 /* A hipStream_t; NULL is the null stream. */
 typedef void* fi_stream_t;
@@ -194,7 +202,7 @@ enum {
  *                  pages, ignored (any value in [0, page_size]) for empty ones
  * num_qo_heads, num_kv_heads: num_qo_heads % num_kv_heads == 0; the group
  *                  size G = num_qo_heads / num_kv_heads must be 1, 2, 4 or 8
- * head_dim         64 or 128
+ * head_dim         64 or 128 (128 for FI_DTYPE_FP8_E4M3)
  * page_size        block size in tokens, 1 .. 4096
  * num_pool_pages   pages in the caller's k_pages / v_pages pools
  * dtype            element type of q, K, V, out
@@ -258,10 +266,12 @@ fi_status fi_plan_upload(fi_plan* plan, void* workspace, size_t workspace_bytes,
  * use the same workspace must not overlap (the merge counters live there);
  * the kernel leaves every counter at 0 when it finishes.
  *
- * q        device [batch, num_qo_heads, head_dim] dtype, 16-byte aligned
- * k_pages  device [num_pool_pages, num_kv_heads, page_size, head_dim] dtype
+ * q        device [batch, num_qo_heads, head_dim], 16-byte aligned; fp32 for
+ *          FI_DTYPE_F32, bf16 otherwise
+ * k_pages  device [num_pool_pages, num_kv_heads, page_size, head_dim] of the
+ *          plan's dtype (bytes for FI_DTYPE_FP8_E4M3)
  * v_pages  same shape and type as k_pages
- * out      device [batch, num_qo_heads, head_dim] dtype (written)
+ * out      device [batch, num_qo_heads, head_dim], same type as q (written)
  * lse      device float32 [batch, num_qo_heads] (written); may be NULL
  * sm_scale score scale; <= 0 selects 1/sqrt(head_dim)
  * workspace the buffer given to fi_plan_upload for this plan
@@ -269,6 +279,19 @@ fi_status fi_plan_upload(fi_plan* plan, void* workspace, size_t workspace_bytes,
 fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
                         const void* v_pages, void* out, float* lse, float sm_scale,
                         void* workspace, size_t workspace_bytes, fi_stream_t stream);
+
+/*
+ * fi_decode_run with dequantisation scales: every K element counts as
+ * k_scale times its stored value and every V element as v_scale times its
+ * stored value (the scores are sm_scale * k_scale * q.k, the output is
+ * v_scale times the weighted sum of stored V). Meant for FI_DTYPE_FP8_E4M3
+ * plans; valid for every dtype. fi_decode_run is this call with both scales
+ * 1. Scales must be finite and positive.
+ */
+fi_status fi_decode_run_scaled(const fi_plan* plan, const void* q, const void* k_pages,
+                               const void* v_pages, float k_scale, float v_scale, void* out,
+                               float* lse, float sm_scale, void* workspace,
+                               size_t workspace_bytes, fi_stream_t stream);
 
 /*
  * Merge two attention states over disjoint token sets (the closed form of
@@ -281,7 +304,7 @@ fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
  *
  * v_a, v_b, v_out  device [num_rows, head_dim] dtype, 16-byte aligned
  * s_a, s_b, s_out  device float32 [num_rows], natural-log LSE
- * head_dim         64 or 128; num_rows >= 0 (0 launches nothing)
+ * head_dim         64 or 128 (128 for FI_DTYPE_FP8_E4M3); num_rows >= 0 (0 launches nothing)
  * v_out/s_out may alias v_a/s_a or v_b/s_b exactly (elementwise).
  */
 fi_status fi_merge_states(fi_dtype dtype, const void* v_a, const float* s_a,

@@ -26,6 +26,12 @@ What it computes, and where that comes from:
   piece's (output, log-sum-exp) state and a merge; the merge below is the
   closed form of softmax over a disjoint union of token sets.
 
+* Same explainer, JIT section: quantisation / dequantisation around attention
+  is fused into the attention kernel. Reading: with a quantised KV cache the
+  method computes plain attention over the dequantised values, K = k_scale *
+  code and V = v_scale * code; ``dequantize_e4m3`` decodes OCP FP8 E4M3 codes
+  from the format's definition.
+
 Everything is float64. The exact result of the method is plain softmax
 attention over the listed tokens, so the oracle is that definition, written
 out with a library matmul as its only primitive.
@@ -215,3 +221,19 @@ def round_bf16_rne(x):
     lo_even = ((lo.astype(np.float32).view(np.uint32) >> 16) & 1) == 0
     pick_lo = (dlo < dhi) | ((dlo == dhi) & lo_even)
     return np.where(pick_lo, lo, hi)
+
+
+def dequantize_e4m3(codes, scale: float = 1.0) -> np.ndarray:
+    """OCP FP8 E4M3 (E4M3FN) codes (uint8) to float64, times ``scale``.
+
+    The format: bit 7 sign; bits 6..3 exponent e with bias 7; bits 2..0
+    mantissa m. e = 0 is subnormal, (m / 8) * 2^-6; otherwise (1 + m / 8) *
+    2^(e - 7). There are no infinities; e = 15 with m = 7 is NaN, so the
+    largest finite magnitude is 1.75 * 2^8 = 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = sign * mag * scale
+    return np.where((e == 15) & (m == 7), np.nan, out)

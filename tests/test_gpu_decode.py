@@ -29,6 +29,16 @@ def log(*a):
     print(*a, flush=True)
 
 
+def host_values(w, q, k, v):
+    """q, K, V for the oracle in float64 (an fp8 cache dequantised by the
+    oracle's own E4M3 decoder and scales)."""
+    qh = q.double().cpu().numpy()
+    if w.dtype == "fp8":
+        return (qh, oa.dequantize_e4m3(k.view(torch.uint8).cpu().numpy(), w.k_scale),
+                oa.dequantize_e4m3(v.view(torch.uint8).cpu().numpy(), w.v_scale))
+    return qh, k.double().cpu().numpy(), v.double().cpu().numpy()
+
+
 def run_case(w, device_values=False, what="", **opts):
     log(f"[case] {what} B={w.batch} Hq={w.num_qo_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
         f"P={w.page_size} {w.dtype} opts={opts}")
@@ -38,13 +48,13 @@ def run_case(w, device_values=False, what="", **opts):
         q, k, v = (t.cuda() for t in w.make_values("cpu"))
     p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, w.num_qo_heads, w.num_kv_heads,
                 w.head_dim, w.page_size, w.num_pool_pages, w.dtype, **opts)
-    out, lse = fb.decode(q, k, v, p)
+    out, lse = fb.decode(q, k, v, p, k_scale=w.k_scale, v_scale=w.v_scale)
     torch.cuda.synchronize()
     t0 = time.time()
-    qh, kh, vh = q.float().cpu().numpy(), k.float().cpu().numpy(), v.float().cpu().numpy()
+    qh, kh, vh = host_values(w, q, k, v)
     O, LSE = oa.decode_attention(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len, w.sm_scale)
     stats = compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE,
-                    w.dtype == "bf16", what)
+                    w.dtype != "f32", what)
     log(f"[ok] {what} plan={p.info['num_items']} items chunk={p.info['chunk_pages']}p "
         f"oracle {time.time() - t0:.1f}s {stats}")
     return p, (q, k, v), (out, lse)
@@ -173,6 +183,51 @@ def test_cascade_matches_plain_decode_on_shared_prefix_workload():
     assert p0.info["num_prefix_items"] == 0
     assert (o1.float() - o0.float()).abs().max().item() <= 2 * 2 ** -7
     assert (l1 - l0).abs().max().item() <= 1e-4
+
+
+FP8 = [
+    # seed, B, maxL, Hq, Hkv, P, empty_every, fixed chunk
+    (51, 4, 300, 8, 2, 16, 0, 0),
+    (52, 5, 257, 8, 8, 16, 3, 0),     # G 1
+    (53, 3, 500, 16, 8, 16, 0, 48),   # G 2, forced split
+    (54, 4, 333, 32, 4, 16, 0, 32),   # G 8, forced split
+    (55, 4, 90, 8, 2, 3, 2, 0),       # page size 3 (per-lane addressing)
+    (56, 3, 700, 8, 2, 64, 0, 64),
+    (57, 4, 70, 8, 2, 1, 0, 20),
+]
+
+
+@pytest.mark.parametrize("case", FP8, ids=lambda c: f"fp8_s{c[0]}_G{c[3] // c[4]}_P{c[5]}")
+def test_fp8_kv(case):
+    """fp8 e4m3 K/V with bf16 q/out, dequantised inside the kernel, against the
+    oracle over the dequantised cache; NaN codes in every slot that must not
+    be read."""
+    seed, B, L, hq, hkv, P, ee, fixed = case
+    w = random_workload(seed, B, L, hq, hkv, 128, P, "fp8", empty_every=ee)
+    run_case(w, what=f"fp8-{seed}", fixed_chunk_tokens=fixed)
+
+
+def test_fp8_skewed_batch_full_size():
+    w = workload(6)
+    p, (q, k, v), (o0, l0) = run_case(w, device_values=True, what="config6-fp8")
+    o1, l1 = fb.decode(q, k, v, p, k_scale=w.k_scale, v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o0) and torch.equal(l1, l0)
+
+
+def test_kv_scales_on_bf16_cache():
+    """fi_decode_run_scaled on a bf16 cache: scaling K by a and V by c equals
+    the oracle with K and V multiplied by a and c."""
+    w = random_workload(58, 4, 200, 8, 2, 128, 16, "bf16")
+    q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, w.num_qo_heads, w.num_kv_heads,
+                w.head_dim, w.page_size, w.num_pool_pages, w.dtype)
+    out, lse = fb.decode(q, k, v, p, k_scale=0.5, v_scale=3.0)
+    torch.cuda.synchronize()
+    qh, kh, vh = host_values(w, q, k, v)
+    O, LSE = oa.decode_attention(qh, 0.5 * kh, 3.0 * vh, w.kv_indptr, w.kv_indices, w.last_page_len,
+                                 w.sm_scale)
+    compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE, True, "kv-scales")
 
 
 def test_deterministic_for_fixed_plan():

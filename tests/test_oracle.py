@@ -88,3 +88,24 @@ def test_oracle_mutations_are_caught(name, monkeypatch):
         except (AssertionError, ValueError, IndexError, TypeError):
             caught.append(pin.__name__)
     assert caught, f"planted mistake {name} passed every pin"
+
+
+def test_e4m3_decoder_matches_the_format_and_torch():
+    """The oracle's FP8 E4M3 decoder against points the format fixes (zero,
+    the smallest subnormal 2^-9, one, the largest finite 448, NaN) and
+    against torch's float8_e4m3fn for all 256 codes (the cast the input
+    generator uses)."""
+    import torch
+    d = oa.dequantize_e4m3
+    assert d(0x00) == 0.0 and d(0x80) == 0.0 and np.signbit(d(0x80))
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9 and d(0x08) == 2.0 ** -6
+    assert d(0x38) == 1.0 and d(0xB8) == -1.0 and d(0x3C) == 1.5
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0
+    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF))
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = d(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert d(codes, 0.25)[0x38] == 0.25
