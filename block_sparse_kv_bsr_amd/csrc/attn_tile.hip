@@ -1,0 +1,408 @@
+// Attention of many query rows against one shared run of paged K/V, on the
+// matrix cores of gfx950 (bf16). Used for shared prefixes (cascade).
+//
+// Composable block-sparse formats (FlashInfer paper explainer, "FlashInfer:
+// Block-Sparse KV 캐시로 어텐션 병목을 해소하다", visionhong.com, Block-Sparse
+// section): a KV cache can be described by more than one block-sparse
+// matrix. When many requests begin with the same pages, that prefix is one
+// block all of their query rows share; computing it once per KV head for
+// every row of the group turns each request re-reading the prefix into one
+// matrix problem. Each row's prefix state (o, lse) is merged with the row's
+// state over its own pages by the decode kernel's merge tree (softmax over a
+// disjoint union, the closed form behind the explainer's split scheduler).
+//
+// One workgroup of 8 waves per item. Wave w owns query rows 32(w%4) ..
+// +31 and the tokens 32(w/4) .. +31 of every 64-token block, so two waves
+// share each SIMD and hide each other's latencies; the two partial softmax
+// states of a row are merged through LDS at the end. K/V blocks stream into
+// an LDS ring of kStages stages with gfx950's direct-to-LDS loads (no
+// staging registers), one barrier per block. Per 32 tokens of a wave:
+//   S^T[token, row] = K . Q^T     v_mfma_f32_32x32x16_bf16, D/16 steps
+//   online softmax per row (a lane owns one row: 16 tokens in the lane, the
+//   other 16 in lane l^32)
+//   O^T[d, row] += V^T . P^T      2 token steps x D/32 tiles
+// Lane layout of v_mfma_f32_32x32x16_bf16 (A 32x16, B 16x32, C 32x32):
+// A[m][k] in lane m + 32*(k/8), element k%8; B[k][n] in lane n + 32*(k/8);
+// C[m][n] in lane n + 32*((m%8)/4), element 4*(m/8) + m%4.
+// P^T comes straight from the S^T accumulators: the PV contraction index
+// enumerates the block's tokens in the order the S^T layout leaves them in
+// the lanes. V^T fragments come from the row-major V tile through
+// ds_read_b64_tr_b16: within each 16-lane group, output lane 4p+q element k
+// is element q of input lane 4k+p, so input lanes pointing at
+// V[tok_k][d0 + 4p] hand every output lane four tokens of one column.
+// 16-byte pieces of each K and V row are XOR-swizzled in LDS (through the
+// source address of the direct-to-LDS loads) so both reads stay at or below
+// two-way bank conflicts.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fi_bsr.h"
+#include "kernels.h"
+
+namespace fi {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+
+constexpr int kWaves = 8;
+constexpr int kBlock = 64;   // tokens per ring stage (32 per wave half)
+constexpr int kIds = 256;    // page-id window
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kMargin = 8.0f;  // lazy-rescale margin, log2 units
+
+struct TileParams {
+  const int32_t* pitems;
+  const int32_t* members;
+  const int32_t* prefix_slot;
+  const int32_t* page_ids;
+  const char* q;
+  const char* k_pages;
+  const char* v_pages;
+  float* part_o;
+  float* part_lse;
+  int64_t page_stride;  // bytes between physical pages
+  int64_t head_stride;  // bytes between KV heads within a page
+  int num_qo_heads;
+  int num_kv_heads;
+  int page_size;
+  int group;
+  float scale_log2;     // sm_scale * log2(e)
+};
+
+template <int D>
+struct Geom {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kPieces = kRowBytes / 16;          // 16-byte pieces per row
+  static constexpr int kBlockBytes = kBlock * kRowBytes;  // one K (or V) block
+  static constexpr int kRowsPerDma = 1024 / kRowBytes;    // rows one wave-wide load covers
+  static constexpr int kDmaPerWave = kBlockBytes / 1024 / kWaves;
+  static constexpr int kStages = D == 128 ? 3 : 5;        // 96 / 80 KiB of K+V in flight
+  static_assert(kDmaPerWave >= 1, "block does not cover the workgroup");
+  // piece swizzles: K read 16 rows x 1 piece, V read 8 rows x 4 pieces at a time
+  static __device__ __forceinline__ int swz_k(int t) { return t % kPieces; }
+  static_assert(kStages * 2 * kBlockBytes >= 4 * 32 * D * 4, "ring too small for the final merge");
+  static __device__ __forceinline__ int swz_v(int t) { return (4 * (t % 4)) % kPieces; }
+};
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// s_waitcnt vmcnt(n), leaving the other counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt lgkmcnt(0) with the registers the inline-asm LDS reads wrote as
+// operands, so no use of them can be scheduled above the wait.
+template <int N>
+__device__ __forceinline__ void lgkm_wait_tied(u32x4_t (&r)[N]) {
+  if constexpr (N == 4) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3])::"memory");
+  } else {
+    static_assert(N == 8, "4 or 8 fragments");
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
+                   "+v"(r[7])::"memory");
+  }
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_tied(u32x2_t (&r)[N][2]) {
+  if constexpr (N == 2) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0][0]), "+v"(r[0][1]), "+v"(r[1][0]), "+v"(r[1][1])::"memory");
+  } else {
+    static_assert(N == 4, "2 or 4 tiles");
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(r[0][0]), "+v"(r[0][1]), "+v"(r[1][0]), "+v"(r[1][1]), "+v"(r[2][0]), "+v"(r[2][1]),
+                   "+v"(r[3][0]), "+v"(r[3][1])::"memory");
+  }
+}
+
+__device__ __forceinline__ float max_with_partner32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
+  using Gm = Geom<D>;
+  constexpr int NS = Gm::kStages;
+  constexpr int kRB = Gm::kRowBytes;
+  __shared__ __attribute__((aligned(1024))) char s_ring[NS][2][Gm::kBlockBytes];
+  __shared__ int s_pid[kIds];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wrow = wave & 3;   // row block of this wave
+  const int wtok = wave >> 2;  // token half of every block
+  const int half = lane >> 5;
+  const int32_t* it = p.pitems + (int64_t)blockIdx.x * FI_PITEM_STRIDE;
+  const int h = it[FI_PITEM_KV_HEAD];
+  const int member_base = it[FI_PITEM_MEMBER_BASE];
+  const int row_begin = it[FI_PITEM_ROW_BEGIN];
+  const int nrows = it[FI_PITEM_NUM_ROWS];
+  const int chunk = it[FI_PITEM_CHUNK];
+  const int page_begin = it[FI_PITEM_PAGE_BEGIN];
+  const int npg = it[FI_PITEM_NUM_PAGES];  // <= FI_PREFIX_MAX_PAGES = kIds
+  const int ntok = npg * p.page_size;
+  const int G = p.group;
+
+  // ---- page ids of the item (one window: an item has at most kIds pages)
+  if (tid < kIds) s_pid[tid] = p.page_ids[page_begin + min(tid, npg - 1)];
+
+  // ---- this lane's query row (column n = lane % 32 of the wave's tiles)
+  const int row = wrow * 32 + (lane & 31);
+  const bool row_ok = row < nrows;
+  const int b = p.members[member_base + row_begin + (row_ok ? row / G : 0)];
+  const int gi = row_ok ? row % G : 0;
+  // Q^T as the B operand: lane holds Q[row][16s + 8*half .. +8] for step s
+  // (a padding row loads row 0 of the group's first member and zeroes it, so
+  // the loads are unconditional)
+  bf16x8_t qf[D / 16];
+  {
+    const char* qrow = p.q + ((int64_t)b * p.num_qo_heads + (int64_t)h * G + gi) * kRB;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      uint4 v = *reinterpret_cast<const uint4*>(qrow + (16 * s + 8 * half) * 2);
+      if (!row_ok) v = make_uint4(0, 0, 0, 0);
+      qf[s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  // q and the page ids are in before any K/V load is issued, so the waits on
+  // the ring below count K/V loads only
+  wait_vmcnt<0>();
+  __syncthreads();  // s_pid is written
+
+  // ---- direct-to-LDS loads of block j into stage st: wave-wide load i of
+  // wave w fills rows (w*kDmaPerWave + i) * kRowsPerDma + lane / kPieces,
+  // piece lane % kPieces of the swizzled layout, from the global piece it
+  // stands for. Blocks past the end re-read the last token (same count of
+  // loads on every path, so the vmcnt waits below are exact). Prefix K/V is
+  // read once per row block (one, unless a group holds over 128 query
+  // rows), so the loads carry the nontemporal policy (aux bit 1 = nt on
+  // gfx950) and stream past the caches.
+  const int64_t head_off = (int64_t)h * p.head_stride;
+  const int dma_row = lane / Gm::kPieces;
+  const int dma_piece = lane % Gm::kPieces;
+  auto issue = [&](int j, int st) {
+#pragma unroll
+    for (int i = 0; i < Gm::kDmaPerWave; ++i) {
+      const int t = (wave * Gm::kDmaPerWave + i) * Gm::kRowsPerDma + dma_row;
+      const int tok = min(j * kBlock + t, ntok - 1);
+      const int pid = s_pid[tok / p.page_size];
+      const int64_t row_off = (int64_t)pid * p.page_stride + head_off + (int64_t)(tok % p.page_size) * kRB;
+      const int kp = dma_piece ^ Gm::swz_k(t);
+      const int vp = dma_piece ^ Gm::swz_v(t);
+      char* kdst = &s_ring[st][0][(wave * Gm::kDmaPerWave + i) * 1024];
+      char* vdst = &s_ring[st][1][(wave * Gm::kDmaPerWave + i) * 1024];
+      __builtin_amdgcn_global_load_lds((global_void_t*)(p.k_pages + row_off + kp * 16),
+                                       (lds_void_t*)kdst, 16, 0, 2);
+      __builtin_amdgcn_global_load_lds((global_void_t*)(p.v_pages + row_off + vp * 16),
+                                       (lds_void_t*)vdst, 16, 0, 2);
+    }
+  };
+
+  f32x16_t o[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int nblocks = (ntok + kBlock - 1) / kBlock;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s, s);
+
+  // addresses that depend only on the lane
+  const int kt = 32 * wtok + (lane & 31);  // K row this lane reads (token of the S^T tile)
+  const int g16 = lane >> 4, L16 = lane & 15;
+  const int v_k = L16 >> 2, v_p = L16 & 3;  // this lane's input role in a transposed read
+
+  for (int j = 0; j < nblocks; ++j) {
+    const int st = j % NS;
+    // this wave's loads of block j have landed (later blocks may be in flight)
+    wait_vmcnt<2 * Gm::kDmaPerWave * (NS - 2)>();
+    // every wave's loads of block j have landed, and every wave is done
+    // reading block j-1, whose stage is refilled next
+    __builtin_amdgcn_s_barrier();
+    issue(j + NS - 1, (j + NS - 1) % NS);
+
+    const char* kst = s_ring[st][0];
+    const char* vst = s_ring[st][1];
+    // ---- S^T = K . Q^T
+    u32x4_t kv[D / 16];
+#pragma unroll
+    for (int q = 0; q < D / 16; ++q) {
+      const uint32_t a = lds_u32(kst + kt * kRB + (((2 * q + half) ^ Gm::swz_k(kt)) * 16));
+      asm volatile("ds_read_b128 %0, %1" : "=v"(kv[q]) : "v"(a) : "memory");
+    }
+    lgkm_wait_tied<D / 16>(kv);
+    // two independent accumulation chains halve the dependent-MFMA latency
+    f32x16_t s, s1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = s1[r] = 0.f;
+#pragma unroll
+    for (int q = 0; q < D / 16; q += 2) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv[q]), qf[q], s, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv[q + 1]), qf[q + 1], s1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] += s1[r];
+
+    // ---- online softmax; element r holds token m = 4*half + 8*(r/4) + r%4
+    const int tok0 = j * kBlock + 32 * wtok;
+    float mb = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 4 * half + 8 * (r >> 2) + (r & 3);
+      s[r] = tok0 + m < ntok ? s[r] * p.scale_log2 : -INFINITY;
+      mb = fmaxf(mb, s[r]);
+    }
+    mb = max_with_partner32(mb);  // -inf only if this half of the block is all past the end
+    // The running max is raised only when the block's max passes it by more
+    // than kMargin (weights stay <= 2^kMargin), so the accumulators, which
+    // live in AGPRs and cost a read, a multiply and a write each, are rescaled
+    // rarely after the first block.
+    const bool up = mb > m_run + kMargin;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float alpha = up ? __builtin_amdgcn_exp2f(m_run - mb) : 1.f;  // 0 on the first block
+      l_run *= alpha;
+      if (j > 0) {  // the accumulators are still zero on the first block
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      }
+      m_run = up ? mb : m_run;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      // a masked token has weight 0 (also while m_run is still -inf)
+      s[r] = s[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[r] - m_run);
+      ps += s[r];
+    }
+    l_run += sum_with_partner32(ps);
+
+    // ---- O^T += V^T . P^T over two steps of 16 tokens. Step ks takes
+    // elements 8ks .. 8ks+7 of s: contraction index 8*half + i is token
+    // 4*half + 16ks + 8*(i/4) + i%4. This lane's A fragment (d = 32t + lane%32)
+    // comes from two transposed reads: tokens 4*half + 16ks + 0..3, then +8.
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t pb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[i] = (__bf16)s[8 * ks + i];
+      u32x2_t va[D / 32][2];
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+        for (int run = 0; run < 2; ++run) {
+          // input role: token 4*(g16/2) + 16ks + 8run + v_k, columns
+          // 32t + 16*(g16%2) + 4*v_p .. +3
+          const int tok = 32 * wtok + 4 * (g16 >> 1) + 16 * ks + 8 * run + v_k;
+          const int d = 32 * t + 16 * (g16 & 1) + 4 * v_p;
+          const uint32_t a = lds_u32(vst + tok * kRB + (((d >> 3) ^ Gm::swz_v(tok)) * 16) + (d & 7) * 2);
+          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(va[t][run]) : "v"(a) : "memory");
+        }
+      }
+      lgkm_wait_tied<D / 32>(va);
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        const u32x4_t av = {va[t][0][0], va[t][0][1], va[t][1][0], va[t][1][1]};
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[t], 0, 0, 0);
+      }
+    }
+  }
+  // loads past the end may still be landing in the ring
+  wait_vmcnt<0>();
+
+  // ---- merge the two token halves of each row: waves 4..7 hand (m, l, o)
+  // to waves 0..3 through the (drained) ring, lane-for-lane
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(&s_ring[0][0][0]);  // [4 waves][D/32][16][64]
+  __shared__ float s_ml[4][2][64];
+  if (wtok == 1) {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[((wrow * (D / 32) + t) * 16 + r) * 64 + lane] = o[t][r];
+    s_ml[wrow][0][lane] = m_run;
+    s_ml[wrow][1][lane] = l_run;
+  }
+  __syncthreads();
+  if (wtok == 1) return;
+  {
+    const float m2 = s_ml[wrow][0][lane], l2 = s_ml[wrow][1][lane];
+    const float mm = fmaxf(m_run, m2);  // finite: token 0 is in this (first) half
+    const float a1 = __builtin_amdgcn_exp2f(m_run - mm);
+    const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        o[t][r] = o[t][r] * a1 + xo[((wrow * (D / 32) + t) * 16 + r) * 64 + lane] * a2;
+    l_run = l_run * a1 + l2 * a2;
+    m_run = mm;
+  }
+
+  // ---- partial state of this row: o / l and lse (log2 units)
+  if (!row_ok) return;
+  const int slot = p.prefix_slot[(int64_t)b * p.num_kv_heads + h] + chunk;
+  const int64_t prow = (int64_t)slot * G + gi;
+  const float inv = 1.f / l_run;
+  float* dst = p.part_o + prow * D;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      // elements 4*q4 .. +3 are d = 32t + 8*q4 + 4*half .. +3
+      const int d = 32 * t + 8 * q4 + 4 * half;
+      *reinterpret_cast<float4*>(dst + d) =
+          make_float4(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv, o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv);
+    }
+  }
+  if (half == 0) p.part_lse[prow] = m_run + __builtin_amdgcn_logf(l_run);
+}
+
+}  // namespace
+
+hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream) {
+  if (a.num_items <= 0) return hipSuccess;
+  TileParams p;
+  p.pitems = a.pitems;
+  p.members = a.members;
+  p.prefix_slot = a.prefix_slot;
+  p.page_ids = a.page_ids;
+  p.q = static_cast<const char*>(a.q);
+  p.k_pages = static_cast<const char*>(a.k_pages);
+  p.v_pages = static_cast<const char*>(a.v_pages);
+  p.part_o = a.part_o;
+  p.part_lse = a.part_lse;
+  const int64_t row = (int64_t)a.head_dim * 2;
+  p.head_stride = (int64_t)a.page_size * row;
+  p.page_stride = (int64_t)a.num_kv_heads * a.page_size * row;
+  p.num_qo_heads = a.num_qo_heads;
+  p.num_kv_heads = a.num_kv_heads;
+  p.page_size = a.page_size;
+  p.group = a.group;
+  p.scale_log2 = a.sm_scale * kLog2e;
+  const dim3 grid((uint32_t)a.num_items), block(64 * kWaves);
+  if (a.head_dim == 128) hipLaunchKernelGGL(tile_attend_kernel<128>, grid, block, 0, stream, p);
+  else if (a.head_dim == 64) hipLaunchKernelGGL(tile_attend_kernel<64>, grid, block, 0, stream, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace fi
