@@ -45,6 +45,9 @@ CONFIG_NAMES = {
     4: "long_b2_l131072_65536",
     5: "sparse_prefix_b32_p64",
     6: "skewed_b64_loguniform_32_32768_fp8kv",
+    # prefill / append (several query tokens per request, causal)
+    7: "prefill_b16_l2048_causal",
+    8: "append_b64_q128_skewed",
 }
 
 # fp8 KV caches hold x / FP8_SCALE rounded to OCP E4M3 (torch's cast, round
@@ -209,6 +212,118 @@ def paged_structure(lens, page_size, pool_pages, rng):
     return indptr, indices, last, unused
 
 
+@dataclasses.dataclass
+class PrefillWorkload(Workload):
+    """Several query tokens per request: request b's n_b query tokens are
+    rows qo_indptr[b] .. qo_indptr[b+1]-1 of q [N, H_q, d]; they are the
+    request's newest cached tokens (n_b <= L_b when causal)."""
+    qo_indptr: np.ndarray = None
+    causal: bool = True
+
+    @property
+    def num_qo_tokens(self) -> int:
+        return int(self.qo_indptr[-1])
+
+    def qo_lens(self) -> np.ndarray:
+        return np.diff(self.qo_indptr).astype(np.int64)
+
+    def visible_pairs(self) -> int:
+        """Sum over query tokens of the KV tokens each attends."""
+        tot = 0
+        for L, n in zip(self.kv_lens(), self.qo_lens()):
+            L, n = int(L), int(n)
+            if self.causal:
+                # query i sees max(0, L - n + i + 1) tokens
+                lo = max(0, n - L)
+                tot += sum(L - n + i + 1 for i in range(lo, n))
+            else:
+                tot += L * n
+        return tot
+
+    def flops(self) -> int:
+        """QK^T and PV: 2 * d multiply-adds each per (query head, visible token)."""
+        return 4 * self.head_dim * self.num_qo_heads * self.visible_pairs()
+
+    def algorithmic_bytes(self, unique: bool = True) -> int:
+        tok = self._unique_tokens() if unique else int(self.kv_lens().sum())
+        kv = 2 * self.num_kv_heads * self.head_dim * tok * self.kv_elem_bytes
+        qo = 2 * self.num_qo_tokens * self.num_qo_heads * self.head_dim * self.elem_bytes
+        return kv + qo
+
+    def make_values(self, device="cpu"):
+        """(q [N, H_q, d], k_pool, v_pool) drawn like the decode workloads:
+        q, then K, then V, N(0, 1) float32 cast to the dtype."""
+        import torch
+
+        if self.dtype != "bf16":
+            raise ValueError("prefill workloads are bf16")
+        g = torch.Generator(device=device)
+        g.manual_seed(self.value_seed)
+        Hq, Hkv, d, P = self.num_qo_heads, self.num_kv_heads, self.head_dim, self.page_size
+        N = self.num_pool_pages
+
+        def draw(shape):
+            return torch.randn(shape, generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+
+        q = draw((self.num_qo_tokens, Hq, d))
+        k = draw((N, Hkv, P, d))
+        v = draw((N, Hkv, P, d))
+        self._poison(k, device)
+        self._poison(v, device)
+        return q, k, v
+
+
+def _qo_indptr(qo_lens) -> np.ndarray:
+    ip = np.zeros(len(qo_lens) + 1, dtype=np.int32)
+    ip[1:] = np.cumsum(np.asarray(qo_lens, dtype=np.int64))
+    return ip
+
+
+def prefill_workload(config_id: int) -> PrefillWorkload:
+    """7: 16 prompts of 2048 tokens each, all of them queries (pure causal
+    prefill), page size 16, pool with 20% spare pages. 8: the skewed batch's
+    64 histories (log-uniform lengths in [32, 32768]) with their newest
+    min(128, L_b) tokens as queries (a chunk appended to each request).
+    32 query / 8 KV heads, head_dim 128, bf16."""
+    rng = np.random.default_rng([config_id, 0])
+    seed = 1_000_003 * config_id + 1
+    if config_id == 7:
+        lens = [2048] * 16
+        ip, ix, lp, un = paged_structure(lens, 16, 2560, rng)
+        return PrefillWorkload(CONFIG_NAMES[7], 7, 16, 32, 8, 128, 16, "bf16", 2560, ip, ix, lp,
+                               un, seed, qo_indptr=_qo_indptr(lens), causal=True)
+    if config_id == 8:
+        base = workload(3)
+        qo = [min(128, int(L)) for L in base.kv_lens()]
+        return PrefillWorkload(CONFIG_NAMES[8], 8, base.batch, 32, 8, 128, 16, "bf16",
+                               base.num_pool_pages, base.kv_indptr, base.kv_indices,
+                               base.last_page_len, base.unused_pages, seed,
+                               qo_indptr=_qo_indptr(qo), causal=True)
+    raise ValueError(f"unknown prefill config {config_id}")
+
+
+def random_prefill_workload(seed: int, batch: int, max_len: int, num_qo_heads: int,
+                            num_kv_heads: int, head_dim: int, page_size: int,
+                            causal: bool = True, max_qo: Optional[int] = None,
+                            lens: Optional[List[int]] = None,
+                            qo_lens: Optional[List[int]] = None,
+                            spare_pages: int = 3) -> PrefillWorkload:
+    """Small ragged prefill case: KV lengths U{1..max_len} (or given), query
+    counts U{1..min(L_b, max_qo)} (or given; 0 allowed), bf16."""
+    rng = np.random.default_rng([seed, 13])
+    if lens is None:
+        lens = [int(x) for x in rng.integers(1, max_len + 1, size=batch)]
+    if qo_lens is None:
+        cap = max_qo if max_qo is not None else max_len
+        qo_lens = [int(rng.integers(1, max(1, min(L, cap)) + 1)) if L > 0 else 0 for L in lens]
+    npg = sum((L + page_size - 1) // page_size for L in lens)
+    pool = npg + spare_pages
+    ip, ix, lp, un = paged_structure(lens, page_size, pool, rng)
+    return PrefillWorkload(f"prefill_{seed}", 0, len(lens), num_qo_heads, num_kv_heads, head_dim,
+                           page_size, "bf16", pool, ip, ix, lp, un, 30_000 + seed,
+                           qo_indptr=_qo_indptr(qo_lens), causal=causal)
+
+
 def workload(config_id: int) -> Workload:
     rng = np.random.default_rng([config_id, 0])
     seed = 1_000_003 * config_id + 1
@@ -232,6 +347,8 @@ def workload(config_id: int) -> Workload:
         return Workload(CONFIG_NAMES[4], 4, 2, 32, 8, 128, 64, "bf16", 3072, ip, ix, lp, un, seed)
     if config_id == 5:
         return _sparse_prefix(rng, seed)
+    if config_id in (7, 8):
+        return prefill_workload(config_id)
     if config_id == 6:  # the skewed batch over an fp8 KV cache
         w = workload(3)
         return dataclasses.replace(w, name=CONFIG_NAMES[6], config_id=6, dtype="fp8",

@@ -32,6 +32,15 @@ What it computes, and where that comes from:
   code and V = v_scale * code; ``dequantize_e4m3`` decodes OCP FP8 E4M3 codes
   from the format's definition.
 
+* Same explainer, section on where the attention bottleneck lies: prefill
+  attends every token of the prompt at once (and is bound by arithmetic, not
+  memory). Reading (the pages give no formula): the query tokens of a
+  request are its newest tokens, already in the cache, and each attends
+  causally, to itself and every earlier token. A request holding L tokens
+  with n query tokens gives query i (0-based) the first L - n + i + 1 tokens;
+  n = 1 is the decode step above. Without the causal mask every query sees
+  all L tokens.
+
 Everything is float64. The exact result of the method is plain softmax
 attention over the listed tokens, so the oracle is that definition, written
 out with a library matmul as its only primitive.
@@ -145,6 +154,81 @@ def decode_attention_rows(q, k_pool, v_pool, kv_indptr, kv_indices, last_page_le
         K, V = gather_kv(k_pool, v_pool, toks, kv_head_of(h, G))
         o, lse = attend(np.asarray(q[b, h:h + 1, :], dtype=np.float64), K, V, sm_scale)
         O[i], LSE[i] = o[0], lse[0]
+    return O, LSE
+
+
+def visible_tokens(kv_len: int, qo_len: int, i: int, causal: bool) -> int:
+    """Tokens of a request holding kv_len tokens that its query token i of
+    qo_len (0-based) attends: causally the first kv_len - qo_len + i + 1 (the
+    queries are the newest tokens), else all kv_len; never below 0."""
+    if not causal:
+        return kv_len
+    return max(0, kv_len - qo_len + i + 1)
+
+
+def prefill_attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, last_page_len,
+                      causal=True, sm_scale=None):
+    """Batched GQA attention of several query tokens per request (prefill,
+    or a chunk appended to a history) over a paged / BSR KV cache.
+
+    q [N, H_q, d]: request b's query tokens are rows qo_indptr[b] ..
+    qo_indptr[b+1]-1, in token order. k_pool, v_pool and the page table are
+    as for decode_attention. Query token i of request b attends the first
+    visible_tokens(L_b, n_b, i, causal) tokens of the request. Returns float64
+    O [N, H_q, d] and LSE [N, H_q] (natural log); a query that sees no token
+    gets O = 0 and LSE = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    N, Hq, d = q.shape
+    Hkv, P = k_pool.shape[1], k_pool.shape[2]
+    assert Hq % Hkv == 0
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    O = np.zeros((N, Hq, d))
+    LSE = np.full((N, Hq), NEG_INF)
+    B = len(qo_indptr) - 1
+    for b in range(B):
+        q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
+        n = q1 - q0
+        if n == 0:
+            continue
+        toks = request_tokens(kv_indptr, kv_indices, last_page_len, P, b)
+        L = len(toks)
+        for kvh in range(Hkv):
+            heads = [h for h in range(Hq) if kv_head_of(h, G) == kvh]
+            K, V = gather_kv(k_pool, v_pool, toks, kvh)
+            for i in range(n):
+                c = visible_tokens(L, n, i, causal)
+                o, lse = attend(q[q0 + i, heads, :], K[:c], V[:c], sm_scale)
+                O[q0 + i, heads, :] = o
+                LSE[q0 + i, heads] = lse
+    return O, LSE
+
+
+def prefill_attention_rows(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, last_page_len,
+                           rows: Sequence[Tuple[int, int]], causal=True, sm_scale=None):
+    """prefill_attention evaluated only for the listed (query row, head)
+    pairs; used to check single outputs of large batches. Returns
+    (O [n, d], LSE [n])."""
+    d = k_pool.shape[-1]
+    Hq = q.shape[1]
+    Hkv, P = k_pool.shape[1], k_pool.shape[2]
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    qo_indptr = np.asarray(qo_indptr)
+    O = np.zeros((len(rows), d))
+    LSE = np.zeros(len(rows))
+    for j, (r, h) in enumerate(rows):
+        b = int(np.searchsorted(qo_indptr, r, side="right")) - 1
+        n = int(qo_indptr[b + 1] - qo_indptr[b])
+        i = r - int(qo_indptr[b])
+        toks = request_tokens(kv_indptr, kv_indices, last_page_len, P, b)
+        c = visible_tokens(len(toks), n, i, causal)
+        K, V = gather_kv(k_pool, v_pool, toks[:c], kv_head_of(h, G))
+        o, lse = attend(np.asarray(q[r, h:h + 1, :], dtype=np.float64), K, V, sm_scale)
+        O[j], LSE[j] = o[0], lse[0]
     return O, LSE
 
 

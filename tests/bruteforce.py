@@ -36,3 +36,40 @@ def bruteforce_decode(q, k_pool, v_pool, indptr, indices, last, sm_scale):
                 O[b][h][i] = num / den
             LSE[b][h] = top + math.log(den)
     return O, LSE
+
+
+def bruteforce_prefill(q, k_pool, v_pool, qo_indptr, indptr, indices, last, sm_scale, causal):
+    """Several query tokens per request, written out with plain loops. The
+    query tokens of a request are its newest cached tokens: with n queries
+    over L cached tokens, query i sits at position L - n + i and (causal)
+    sees positions 0 .. L - n + i."""
+    N, Hq, d = q.shape
+    Hkv, P = k_pool.shape[1], k_pool.shape[2]
+    G = Hq // Hkv
+    O = [[[0.0] * d for _ in range(Hq)] for _ in range(N)]
+    LSE = [[-math.inf] * Hq for _ in range(N)]
+    for b in range(len(qo_indptr) - 1):
+        toks = []
+        first, stop = int(indptr[b]), int(indptr[b + 1])
+        for j in range(first, stop):
+            count = P if j + 1 < stop else int(last[b])
+            toks.extend((int(indices[j]), slot) for slot in range(count))
+        n = int(qo_indptr[b + 1]) - int(qo_indptr[b])
+        for i in range(n):
+            row = int(qo_indptr[b]) + i
+            pos = len(toks) - n + i  # this query's own position
+            seen = [t for k, t in enumerate(toks) if (k <= pos or not causal)]
+            for h in range(Hq):
+                g = h // G
+                if not seen:
+                    continue
+                scores = [sm_scale * math.fsum(float(q[row, h, c]) * float(k_pool[p, g, s, c])
+                                               for c in range(d)) for (p, s) in seen]
+                top = max(scores)
+                ws = [math.exp(x - top) for x in scores]
+                den = math.fsum(ws)
+                for c in range(d):
+                    O[row][h][c] = math.fsum(w * float(v_pool[p, g, s, c])
+                                             for w, (p, s) in zip(ws, seen)) / den
+                LSE[row][h] = top + math.log(den)
+    return O, LSE

@@ -13,8 +13,8 @@ import math
 import numpy as np
 import torch
 
-from block_sparse_kv_bsr_amd.workloads import random_workload
-from tests.bruteforce import bruteforce_decode
+from block_sparse_kv_bsr_amd.workloads import random_prefill_workload, random_workload
+from tests.bruteforce import bruteforce_decode, bruteforce_prefill
 
 
 def f64_inputs(w):
@@ -239,3 +239,98 @@ def pin_bf16(mod):
 
 
 ALL_PINS = [pin_bruteforce, pin_sdpa, pin_closed_forms, pin_invariants, pin_merge]
+
+
+# ------------------------------------------------------------------ prefill
+def _prefill(mod, w, q, k, v, causal=None, qo_indptr=None):
+    return mod.prefill_attention(q, k, v, w.qo_indptr if qo_indptr is None else qo_indptr,
+                                 w.kv_indptr, w.kv_indices, w.last_page_len,
+                                 w.causal if causal is None else causal, w.sm_scale)
+
+
+PREFILL_TINY = [
+    # seed, batch, max_len, Hq, Hkv, d, P, causal
+    (51, 3, 23, 4, 1, 4, 4, True),
+    (52, 3, 19, 4, 2, 8, 16, True),
+    (53, 2, 17, 2, 2, 4, 1, False),
+    (54, 3, 21, 8, 2, 4, 4, True),
+]
+
+
+def pin_prefill_bruteforce(mod, tol=1e-12):
+    for (seed, B, L, Hq, Hkv, d, P, causal) in PREFILL_TINY:
+        w = random_prefill_workload(seed, B, L, Hq, Hkv, d, P, causal=causal)
+        q, k, v = f64_inputs(w)
+        O, LSE = _prefill(mod, w, q, k, v)
+        Ob, LSEb = bruteforce_prefill(q, k, v, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                      w.last_page_len, w.sm_scale, causal)
+        assert np.max(np.abs(O - np.array(Ob))) <= tol, seed
+        assert np.max(np.abs(LSE - np.array(LSEb))) <= tol, seed
+
+
+def pin_prefill_is_decode_per_row(mod):
+    """One query token per request (causal) is the decode step; without the
+    mask every query token is a decode step over the whole request."""
+    w = random_prefill_workload(61, 4, 40, 4, 2, 8, 4, causal=True, qo_lens=[1, 1, 1, 1])
+    q, k, v = f64_inputs(w)
+    O, LSE = _prefill(mod, w, q, k, v)
+    Od, LSEd = mod.decode_attention(q, k, v, w.kv_indptr, w.kv_indices, w.last_page_len, w.sm_scale)
+    assert np.allclose(O, Od, atol=1e-13, rtol=0) and np.allclose(LSE, LSEd, atol=1e-13, rtol=0)
+    w = random_prefill_workload(62, 3, 30, 4, 2, 8, 4, causal=False)
+    q, k, v = f64_inputs(w)
+    O, LSE = _prefill(mod, w, q, k, v)
+    for b in range(w.batch):
+        for r in range(int(w.qo_indptr[b]), int(w.qo_indptr[b + 1])):
+            qb = q[r][None]
+            ip = np.array([0, w.kv_indptr[b + 1] - w.kv_indptr[b]])
+            ix = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+            Od, LSEd = mod.decode_attention(qb, k, v, ip, ix, w.last_page_len[b:b + 1], w.sm_scale)
+            assert np.allclose(O[r], Od[0], atol=1e-13, rtol=0), (b, r)
+            assert np.allclose(LSE[r], LSEd[0], atol=1e-13, rtol=0), (b, r)
+
+
+def pin_prefill_causal_prefix(mod):
+    """Causal query i of a request with n queries over L tokens is a decode
+    step over the request cut after token L - n + i (its own position): the
+    page table is truncated by hand, pages and last-page length included."""
+    w = random_prefill_workload(63, 3, 45, 4, 2, 8, 4, causal=True, lens=[45, 13, 8],
+                                qo_lens=[9, 13, 3])
+    q, k, v = f64_inputs(w)
+    O, LSE = _prefill(mod, w, q, k, v)
+    P = w.page_size
+    for b in range(w.batch):
+        L = int(w.kv_lens()[b])
+        n = int(w.qo_indptr[b + 1] - w.qo_indptr[b])
+        pages = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+        for i in range(n):
+            keep = L - n + i + 1
+            npg = (keep + P - 1) // P
+            ip, ix = np.array([0, npg]), pages[:npg]
+            last = np.array([keep - P * (npg - 1)])
+            r = int(w.qo_indptr[b]) + i
+            Od, LSEd = mod.decode_attention(q[r][None], k, v, ip, ix, last, w.sm_scale)
+            assert np.allclose(O[r], Od[0], atol=1e-13, rtol=0), (b, i)
+            assert np.allclose(LSE[r], LSEd[0], atol=1e-13, rtol=0), (b, i)
+
+
+def pin_prefill_sdpa(mod):
+    """A whole prompt as queries (n = L): torch's causal scaled dot-product
+    attention in float64 (its mask aligns query i with key i, which is the
+    same as the newest-token alignment when n = L), GQA by enable_gqa."""
+    F = torch.nn.functional
+    w = random_prefill_workload(64, 3, 50, 8, 2, 16, 16, causal=True, lens=[50, 31, 7],
+                                qo_lens=[50, 31, 7])
+    q, k, v = f64_inputs(w)
+    O, LSE = _prefill(mod, w, q, k, v)
+    for b in range(w.batch):
+        K, V = _dense(w, k, v, b)                              # [Hkv, L, d]
+        r0, r1 = int(w.qo_indptr[b]), int(w.qo_indptr[b + 1])
+        qt = torch.from_numpy(q[r0:r1]).transpose(0, 1)[None]  # [1, Hq, n, d]
+        ref = F.scaled_dot_product_attention(qt, torch.from_numpy(K)[None],
+                                             torch.from_numpy(V)[None], is_causal=True,
+                                             enable_gqa=True)[0]
+        assert torch.allclose(torch.from_numpy(O[r0:r1]).transpose(0, 1), ref, atol=1e-12, rtol=0), b
+
+
+PREFILL_PINS = [pin_prefill_bruteforce, pin_prefill_is_decode_per_row, pin_prefill_causal_prefix,
+                pin_prefill_sdpa]

@@ -6,7 +6,8 @@ import oracle.attention as oa
 from tests import oracle_pins as pins
 
 
-@pytest.mark.parametrize("pin", pins.ALL_PINS + [pins.pin_bf16], ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", pins.ALL_PINS + pins.PREFILL_PINS + [pins.pin_bf16],
+                         ids=lambda f: f.__name__)
 def test_pin(pin):
     pin(oa)
 
@@ -75,6 +76,40 @@ MUTATIONS = {
     "merge_lse_without_max": ("merge_states", _merge_no_max),
     "default_scale_1_over_d": ("decode_attention", _decode_scale_1_over_d),
 }
+
+
+def _visible_off_by_one(kv_len, qo_len, i, causal):
+    return max(0, kv_len - qo_len + i) if causal else kv_len
+
+
+def _visible_top_left(kv_len, qo_len, i, causal):
+    return min(kv_len, i + 1) if causal else kv_len
+
+
+def _visible_no_mask(kv_len, qo_len, i, causal):
+    return kv_len
+
+
+PREFILL_MUTATIONS = {
+    "causal_excludes_own_token": ("visible_tokens", _visible_off_by_one),
+    "causal_top_left_aligned": ("visible_tokens", _visible_top_left),
+    "causal_mask_ignored": ("visible_tokens", _visible_no_mask),
+    "gqa_interleaved": ("kv_head_of", _wrong_gqa),
+    "k_used_as_v": ("attend", _attend_k_for_v),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_MUTATIONS))
+def test_prefill_oracle_mutations_are_caught(name, monkeypatch):
+    attr, fn = PREFILL_MUTATIONS[name]
+    monkeypatch.setattr(oa, attr, fn)
+    caught = []
+    for pin in pins.PREFILL_PINS:
+        try:
+            pin(oa)
+        except (AssertionError, ValueError, IndexError, TypeError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake {name} passed every prefill pin"
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
