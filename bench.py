@@ -14,6 +14,7 @@ the decode kernel's roofline fraction against 8 TB/s, and the float64 CPU
 oracle timed on the host on the same workload.
 
     python bench.py [--steps K] [--warmup W] [--config 3]
+    python bench.py --config 7|8        # prefill / append: TFLOP/s on matrix cores
     python bench.py --summarize-counters FETCH.csv WRITE.csv   # rocprofv3 --pmc output
 """
 from __future__ import annotations
@@ -30,6 +31,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "achieved HBM GB/s (% of MI355X peak) + µs/batch, skewed-batch paged GQA decode"
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 DECODE_SRC = os.path.join(ROOT, "block_sparse_kv_bsr_amd", "csrc", "decode_bsr.hip")
 COPY_PROBE_MIB = 1024
 
@@ -134,6 +136,140 @@ def cpu_baseline(w, q, k, v, min_seconds=10.0, max_passes=3):
                       f"{len(times)} pass(es), median; numpy float64 on host cores"}
 
 
+def cpu_baseline_prefill(w, q, k, v, min_seconds=10.0):
+    """Time the float64 prefill oracle on the host over whole requests of the
+    workload, one after another, until min_seconds have passed; report its
+    rate in the benchmark's unit (algorithmic TFLOP/s)."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import oracle.attention as oa
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    kh, vh = k.float().cpu().numpy(), v.float().cpu().numpy()
+    qo = w.qo_indptr
+    L = w.kv_lens()
+    flops = 0
+    spent = 0.0
+    done = 0
+    for b in range(w.batch):
+        n = int(qo[b + 1] - qo[b])
+        if n == 0:
+            continue
+        qh = q[int(qo[b]):int(qo[b + 1])].float().cpu().numpy()
+        ip = np.array([0, w.kv_indptr[b + 1] - w.kv_indptr[b]], dtype=np.int64)
+        ix = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+        t0 = time.perf_counter()
+        oa.prefill_attention(qh, kh, vh, np.array([0, n]), ip, ix, w.last_page_len[b:b + 1],
+                             w.causal, w.sm_scale)
+        spent += time.perf_counter() - t0
+        Lb = int(L[b])
+        pairs = sum(max(0, Lb - n + i + 1) for i in range(n)) if w.causal else Lb * n
+        flops += 4 * w.head_dim * w.num_qo_heads * pairs
+        done += 1
+        if spent >= min_seconds:
+            break
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(spent, 2),
+            "sample": f"the first {done} request(s) of {w.name} (whole requests, all heads), "
+                      "numpy float64 on host cores"}
+
+
+def bench_prefill(args, w):
+    """Prefill / append: one step = fi_prefill_run over the batch (the tile
+    kernel, plus the merge kernel when some tile is cut). Reported as
+    algorithmic TFLOP/s (4 d H_q flops per attended (query, token) pair)
+    against the bf16 dense matrix-core peak."""
+    import torch
+    import block_sparse_kv_bsr_amd as fb
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    fb.lib()
+    dev = torch.device("cuda:0")
+    q, k, v = w.make_values(dev)
+    plan_t = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        p = fb.prefill_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len,
+                            w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                            w.num_pool_pages, causal=w.causal,
+                            fixed_chunk_tokens=args.fixed_chunk_tokens,
+                            items_per_cu=args.items_per_cu)
+        plan_t.append(time.perf_counter() - t0)
+    ws = torch.empty(max(256, p.info["workspace_bytes"]), dtype=torch.uint8, device=dev)
+    p.upload(ws)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.num_qo_tokens, w.num_qo_heads), dtype=torch.float32, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        fb.prefill(q, k, v, p, out=out, lse=lse, workspace=ws)
+        if ev:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            flush.zero_()
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.zero_()
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [e[0].elapsed_time(e[1]) for e in events]
+    step_mean = statistics.mean(step_ms)
+    flops = w.flops()
+    tflops = flops / (step_mean * 1e-3) / 1e12
+    nbytes = w.algorithmic_bytes()
+    kernels = "tile_attend_kernel" + (" + prefill_merge_kernel" if p.info["num_merges"] else "")
+    result = {
+        "metric": "algorithmic TFLOP/s (% of MI355X bf16 dense peak) + µs/batch, "
+                  "paged causal prefill / append attention",
+        "value": round(tflops, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_mean, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_qo_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "page_size": w.page_size, "qo_tokens": w.num_qo_tokens,
+                   "kv_tokens": int(w.kv_lens().sum()), "causal": bool(w.causal),
+                   "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+                   "parallelism": "single-gpu", "plan_items": p.info["num_items"],
+                   "plan_merges": p.info["num_merges"], "chunk_tokens": p.info["chunk_tokens"],
+                   "l2_mall_flush_between_steps": not args.no_flush},
+        "us_per_batch": round(step_mean * 1e3, 2),
+        "us_per_batch_p10_p90": [round(1e3 * sorted(step_ms)[int(0.1 * (len(step_ms) - 1))], 2),
+                                 round(1e3 * sorted(step_ms)[int(0.9 * (len(step_ms) - 1))], 2)],
+        "hbm_gbs_algorithmic": round(nbytes / (step_mean * 1e-3) / 1e9, 1),
+        "plan_host_us": round(1e6 * statistics.median(plan_t), 1),
+        "wall_s_timed_loop": round(wall, 4),
+        # the step's events bracket the tile kernel and, for a cut tile, the
+        # merge kernel after it on the same stream: the figure is a lower bound
+        # on the tile kernel's own rate when there is a merge
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": kernels},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_prefill(w, q, k, v)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 # ------------------------------------------------------------------- bench
 def main():
     ap = argparse.ArgumentParser()
@@ -163,6 +299,8 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "this decode path runs on a single MI355X and has no multi-GPU mode.", flush=True)
         return 2
+    if hasattr(w, "qo_indptr"):
+        return bench_prefill(args, w)
 
     import torch
     import block_sparse_kv_bsr_amd as fb

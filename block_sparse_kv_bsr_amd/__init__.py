@@ -2,8 +2,9 @@
 
 The compute path is the C-ABI library ``libfi_bsr.so`` (HIP kernels for
 gfx950, declared in include/fi_bsr.h); this package is its ctypes binding
-plus seeded input generators. ``plan``, ``decode`` and ``merge_states`` load
-the library on first use and raise if it is missing.
+plus seeded input generators. ``plan``, ``decode``, ``merge_states``,
+``prefill_plan`` and ``prefill`` load the library on first use and raise if it
+is missing.
 """
-from .binding import (FiError, Plan, decode, lib, merge_states, plan,  # noqa: F401
-                      FI_DTYPE_BF16, FI_DTYPE_F32)
+from .binding import (FiError, Plan, PrefillPlan, decode, lib, merge_states, plan,  # noqa: F401
+                      prefill, prefill_plan, FI_DTYPE_BF16, FI_DTYPE_F32)

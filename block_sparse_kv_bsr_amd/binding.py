@@ -31,7 +31,14 @@ STATUS_NAMES = {0: "FI_OK", -1: "FI_ERR_INVALID_ARG", -2: "FI_ERR_UNSUPPORTED",
 # Every symbol include/fi_bsr.h declares.
 EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_merge_nodes",
             "fi_plan_prefix_items", "fi_plan_prefix_members", "fi_plan_upload", "fi_decode_run",
-            "fi_decode_run_scaled", "fi_merge_states", "fi_plan_destroy", "fi_last_error"]
+            "fi_decode_run_scaled", "fi_merge_states", "fi_plan_destroy", "fi_last_error",
+            "fi_prefill_plan_create", "fi_prefill_plan_get_info", "fi_prefill_plan_work_list",
+            "fi_prefill_plan_merges", "fi_prefill_plan_upload", "fi_prefill_run",
+            "fi_prefill_plan_destroy"]
+QITEM_STRIDE = 12
+QMERGE_STRIDE = 8
+PREFILL_ROWS = 256
+PREFILL_MAX_PAGES = 256
 
 
 class FiError(RuntimeError):
@@ -57,6 +64,25 @@ class PlanInfo(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("shared_pages", ctypes.c_int64), ("num_prefix_items", ctypes.c_int64),
                 ("num_prefix_groups", ctypes.c_int32), ("prefix_rows_per_item", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class PrefillOpts(ctypes.Structure):
+    _fields_ = [("num_cus", ctypes.c_int32), ("items_per_cu", ctypes.c_int32),
+                ("fixed_chunk_tokens", ctypes.c_int32), ("num_xcds", ctypes.c_int32)]
+
+
+class PrefillInfo(ctypes.Structure):
+    _fields_ = [("num_items", ctypes.c_int64), ("num_tiles", ctypes.c_int64),
+                ("num_merges", ctypes.c_int64), ("num_partial_slots", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64), ("total_qo_tokens", ctypes.c_int64),
+                ("total_kv_tokens", ctypes.c_int64), ("visible_pairs", ctypes.c_int64),
+                ("tokens_per_tile", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("num_qo_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("causal", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -97,6 +123,21 @@ def lib() -> ctypes.CDLL:
     L.fi_merge_states.restype = i32
     L.fi_plan_destroy.argtypes = [vp]
     L.fi_plan_destroy.restype = None
+    L.fi_prefill_plan_create.argtypes = [pi32, pi32, pi32, pi32, i32, i32, i32, i32, i32, i64,
+                                         i32, i32, ctypes.POINTER(PrefillOpts),
+                                         ctypes.POINTER(vp)]
+    L.fi_prefill_plan_create.restype = i32
+    L.fi_prefill_plan_get_info.argtypes = [vp, ctypes.POINTER(PrefillInfo)]
+    L.fi_prefill_plan_get_info.restype = i32
+    for name in ("fi_prefill_plan_work_list", "fi_prefill_plan_merges"):
+        getattr(L, name).argtypes = [vp, ctypes.POINTER(pi32), ctypes.POINTER(i64)]
+        getattr(L, name).restype = i32
+    L.fi_prefill_plan_upload.argtypes = [vp, vp, sz, vp]
+    L.fi_prefill_plan_upload.restype = i32
+    L.fi_prefill_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
+    L.fi_prefill_run.restype = i32
+    L.fi_prefill_plan_destroy.argtypes = [vp]
+    L.fi_prefill_plan_destroy.restype = None
     L.fi_last_error.argtypes = []
     L.fi_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -296,3 +337,110 @@ def merge_states(v_a, s_a, v_b, s_b, v_out=None, s_out=None, stream=None):
                                  ctypes.c_void_p(s_out.data_ptr()), rows, d,
                                  ctypes.c_void_p(_stream(stream))))
     return v_out, s_out
+
+
+# ------------------------------------------------------------------ prefill
+class PrefillPlan:
+    """A prefill / append work list (host memory, owned by the library)."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+        info = PrefillInfo()
+        _check(lib().fi_prefill_plan_get_info(self._h, ctypes.byref(info)))
+        self.info = info.as_dict()
+        self._workspace = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def _view(self, fn, stride) -> np.ndarray:
+        p = ctypes.POINTER(ctypes.c_int32)()
+        n = ctypes.c_int64()
+        _check(fn(self._h, ctypes.byref(p), ctypes.byref(n)))
+        if n.value == 0:
+            return np.zeros((0, stride), dtype=np.int32)
+        return np.ctypeslib.as_array(p, shape=(n.value * stride,)).reshape(-1, stride).copy()
+
+    def work_list(self) -> np.ndarray:
+        return self._view(lib().fi_prefill_plan_work_list, QITEM_STRIDE)
+
+    def merges(self) -> np.ndarray:
+        return self._view(lib().fi_prefill_plan_merges, QMERGE_STRIDE)
+
+    def upload(self, workspace, stream=None):
+        _require_gpu(workspace, "workspace")
+        _check(lib().fi_prefill_plan_upload(self._h, ctypes.c_void_p(workspace.data_ptr()),
+                                            workspace.numel() * workspace.element_size(),
+                                            ctypes.c_void_p(_stream(stream))))
+        self._workspace = workspace
+
+    def ensure_uploaded(self, device, stream=None):
+        import torch
+        if self._workspace is None or self._workspace.device != torch.device(device):
+            ws = torch.empty(max(256, self.info["workspace_bytes"]), dtype=torch.uint8, device=device)
+            self.upload(ws, stream)
+        return self._workspace
+
+    @property
+    def workspace(self):
+        return self._workspace
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.fi_prefill_plan_destroy(h)
+            self._h = None
+
+
+def prefill_plan(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int,
+                 num_kv_heads: int, head_dim: int, page_size: int, num_pool_pages: int,
+                 causal: bool = True, dtype="bf16", num_cus: int = 0, items_per_cu: int = 0,
+                 fixed_chunk_tokens: int = 0, num_xcds: int = 0) -> PrefillPlan:
+    """fi_prefill_plan_create over host arrays (numpy or CPU tensors)."""
+    qp, ip, ix, lp = _i32(qo_indptr), _i32(kv_indptr), _i32(kv_indices), _i32(kv_last_page_len)
+    batch = len(ip) - 1
+    if len(lp) != batch or len(qp) != batch + 1:
+        raise ValueError("qo_indptr, kv_indptr and kv_last_page_len disagree on the batch size")
+    opts = PrefillOpts(num_cus, items_per_cu, fixed_chunk_tokens, num_xcds)
+    h = ctypes.c_void_p()
+    ix_ptr = _ptr32(ix) if ix.size else ctypes.POINTER(ctypes.c_int32)()
+    _check(lib().fi_prefill_plan_create(_ptr32(qp), _ptr32(ip), ix_ptr, _ptr32(lp), batch,
+                                        num_qo_heads, num_kv_heads, head_dim, page_size,
+                                        int(num_pool_pages), _dtype_code(dtype), int(bool(causal)),
+                                        ctypes.byref(opts), ctypes.byref(h)))
+    return PrefillPlan(h.value)
+
+
+def prefill(q, k_pages, v_pages, plan_: PrefillPlan, out=None, lse=None,
+            sm_scale: Optional[float] = None, workspace=None, stream=None):
+    """fi_prefill_run: returns (out [N, H_q, d] bf16, lse [N, H_q] float32)."""
+    import torch
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _require_gpu(t, n)
+    info = plan_.info
+    N, Hq, d = info["total_qo_tokens"], info["num_qo_heads"], info["head_dim"]
+    if q.dtype != torch.bfloat16 or k_pages.dtype != torch.bfloat16 or v_pages.dtype != torch.bfloat16:
+        raise ValueError("prefill takes bf16 q, k_pages and v_pages")
+    if tuple(q.shape) != (N, Hq, d):
+        raise ValueError(f"q must have shape {(N, Hq, d)}, got {tuple(q.shape)}")
+    kshape = (k_pages.shape[0], info["num_kv_heads"], info["page_size"], d)
+    if tuple(k_pages.shape) != kshape or tuple(v_pages.shape) != kshape:
+        raise ValueError(f"k_pages/v_pages must have shape [pool, {kshape[1]}, {kshape[2]}, {d}]")
+    if out is None:
+        out = torch.empty((N, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
+    _require_gpu(out, "out")
+    _require_gpu(lse, "lse")
+    if workspace is None:
+        workspace = plan_.ensure_uploaded(q.device, stream)
+    scale = float(sm_scale) if sm_scale else 0.0
+    _check(lib().fi_prefill_run(plan_.handle, ctypes.c_void_p(q.data_ptr()),
+                                ctypes.c_void_p(k_pages.data_ptr()),
+                                ctypes.c_void_p(v_pages.data_ptr()),
+                                ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
+                                scale, ctypes.c_void_p(workspace.data_ptr()),
+                                workspace.numel() * workspace.element_size(),
+                                ctypes.c_void_p(_stream(stream))))
+    return out, lse

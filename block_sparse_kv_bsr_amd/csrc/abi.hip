@@ -1,5 +1,6 @@
-// C ABI entry points that touch the device: plan upload, decode run, state
-// merge and plan destruction. The host-only planner lives in plan.cpp.
+// C ABI entry points that touch the device: plan uploads, the decode and
+// prefill runs, state merge and plan destruction. The host-only planners
+// live in plan.cpp and prefill_plan.cpp.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -23,17 +24,15 @@ fi_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-}  // namespace
-
-extern "C" {
-
-fi_status fi_plan_upload(fi_plan* plan, void* workspace, size_t workspace_bytes,
-                         fi_stream_t stream) {
+// Copies a plan's host image into the workspace through a pinned staging
+// copy the plan keeps (allocated on first use).
+template <class Plan>
+fi_status upload(Plan* plan, void* workspace, size_t workspace_bytes, fi_stream_t stream) {
   if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
   if (!workspace) return fail(FI_ERR_INVALID_ARG, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(FI_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
   if ((int64_t)workspace_bytes < plan->ws.total_bytes)
-    return fail(FI_ERR_WORKSPACE, "workspace smaller than fi_plan_info.workspace_bytes (" +
+    return fail(FI_ERR_WORKSPACE, "workspace smaller than the plan's workspace_bytes (" +
                                       std::to_string(plan->ws.total_bytes) + ")");
   const size_t n = plan->image.size();
   if (n > 0) {
@@ -51,6 +50,78 @@ fi_status fi_plan_upload(fi_plan* plan, void* workspace, size_t workspace_bytes,
   plan->uploaded_to = workspace;
   return FI_OK;
 }
+
+template <class Plan>
+void destroy(Plan* plan) {
+  if (!plan) return;
+  if (plan->pinned) {
+    // uploads from the staging copy may still be in flight
+    (void)hipDeviceSynchronize();
+    (void)hipHostFree(plan->pinned);
+  }
+  fi::plan_free_host(plan);
+}
+
+}  // namespace
+
+extern "C" {
+
+fi_status fi_plan_upload(fi_plan* plan, void* workspace, size_t workspace_bytes,
+                         fi_stream_t stream) {
+  return upload(plan, workspace, workspace_bytes, stream);
+}
+
+fi_status fi_prefill_plan_upload(fi_prefill_plan* plan, void* workspace, size_t workspace_bytes,
+                                 fi_stream_t stream) {
+  return upload(plan, workspace, workspace_bytes, stream);
+}
+
+fi_status fi_prefill_run(const fi_prefill_plan* plan, const void* q, const void* k_pages,
+                         const void* v_pages, void* out, float* lse, float sm_scale,
+                         void* workspace, size_t workspace_bytes, fi_stream_t stream) {
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->num_items() == 0) return FI_OK;
+  if (!q || !out) return fail(FI_ERR_INVALID_ARG, "q or out is NULL");
+  if (!k_pages || !v_pages) return fail(FI_ERR_INVALID_ARG, "k_pages or v_pages is NULL");
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16))
+    return fail(FI_ERR_INVALID_ARG, "q, k_pages, v_pages and out must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(FI_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  if (!workspace) return fail(FI_ERR_INVALID_ARG, "workspace is NULL");
+  if ((int64_t)workspace_bytes < plan->ws.total_bytes)
+    return fail(FI_ERR_WORKSPACE, "workspace smaller than fi_prefill_info.workspace_bytes");
+  if (plan->uploaded_to != workspace)
+    return fail(FI_ERR_STATE, "plan was not uploaded to this workspace (call fi_prefill_plan_upload)");
+  if (!(sm_scale > 0.f)) sm_scale = 1.0f / std::sqrt((float)plan->head_dim);
+  char* ws = static_cast<char*>(workspace);
+  fi::PrefillArgs a{};
+  a.items = reinterpret_cast<const int32_t*>(ws + plan->ws.items);
+  a.merges = reinterpret_cast<const int32_t*>(ws + plan->ws.merges);
+  a.page_ids = reinterpret_cast<const int32_t*>(ws + plan->ws.page_ids);
+  a.q = q;
+  a.k_pages = k_pages;
+  a.v_pages = v_pages;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = reinterpret_cast<float*>(ws + plan->ws.part_o);
+  a.part_lse = reinterpret_cast<float*>(ws + plan->ws.part_lse);
+  a.num_items = plan->num_items();
+  a.num_merges = plan->num_merges();
+  a.num_qo_heads = plan->num_qo_heads;
+  a.num_kv_heads = plan->num_kv_heads;
+  a.head_dim = plan->head_dim;
+  a.page_size = plan->page_size;
+  a.group = plan->group;
+  a.causal = plan->causal;
+  a.sm_scale = sm_scale;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = fi::launch_prefill(a, s);
+  if (e != hipSuccess) return hip_fail(e, "prefill tile kernel launch");
+  e = fi::launch_prefill_merge(a, s);
+  if (e != hipSuccess) return hip_fail(e, "prefill merge kernel launch");
+  return FI_OK;
+}
+
+void fi_prefill_plan_destroy(fi_prefill_plan* plan) { destroy(plan); }
 
 namespace {
 
@@ -182,14 +253,6 @@ fi_status fi_merge_states(fi_dtype dtype, const void* v_a, const float* s_a, con
   return FI_OK;
 }
 
-void fi_plan_destroy(fi_plan* plan) {
-  if (!plan) return;
-  if (plan->pinned) {
-    // uploads from the staging copy may still be in flight
-    (void)hipDeviceSynchronize();
-    (void)hipHostFree(plan->pinned);
-  }
-  fi::plan_free_host(plan);
-}
+void fi_plan_destroy(fi_plan* plan) { destroy(plan); }
 
 }  // extern "C"

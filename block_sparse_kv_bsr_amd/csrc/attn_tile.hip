@@ -1,5 +1,6 @@
-// Attention of many query rows against one shared run of paged K/V, on the
-// matrix cores of gfx950 (bf16). Used for shared prefixes (cascade).
+// Attention of many query rows against one run of paged K/V, on the matrix
+// cores of gfx950 (bf16). Two uses: shared prefixes (cascade) and prefill /
+// append (several query tokens per request, causal).
 //
 // Composable block-sparse formats (FlashInfer paper explainer, "FlashInfer:
 // Block-Sparse KV 캐시로 어텐션 병목을 해소하다", visionhong.com, Block-Sparse
@@ -11,16 +12,29 @@
 // state over its own pages by the decode kernel's merge tree (softmax over a
 // disjoint union, the closed form behind the explainer's split scheduler).
 //
-// One workgroup of 8 waves per item. Wave w owns query rows 32(w%4) ..
-// +31 and the tokens 32(w/4) .. +31 of every 64-token block, so two waves
-// share each SIMD and hide each other's latencies; the two partial softmax
-// states of a row are merged through LDS at the end. K/V blocks stream into
+// Prefill (same explainer, section on where the attention bottleneck lies:
+// prefill attends all prompt tokens at once and is bound by arithmetic): a
+// tile is up to 256 query rows of one request and KV head -- 256 / G query
+// tokens times the G query heads of the KV head -- over one chunk of the
+// request's pages. The queries are the request's newest cached tokens, so
+// with the causal mask row r attends the first VISIBLE + r / G tokens of the
+// request; the mask is a per-row token limit. A tile with one chunk writes
+// bf16 out and lse itself; a cut tile writes partial states that the merge
+// kernel combines.
+//
+// One workgroup of 8 waves per item, two per SIMD. Shared prefix: wave w
+// owns query rows 32(w%4) .. +31 and the tokens 32(w/4) .. +31 of every
+// 64-token block; the two partial softmax states of a row are merged through
+// LDS at the end. Prefill: wave w owns rows 32w .. +31 and both 32-token
+// halves of every block, one after the other, so a K/V block serves 256 rows
+// and the matrix work of one half overlaps the softmax of the other. K/V blocks stream into
 // an LDS ring of kStages stages with gfx950's direct-to-LDS loads (no
 // staging registers), one barrier per block. Per 32 tokens of a wave:
 //   S^T[token, row] = K . Q^T     v_mfma_f32_32x32x16_bf16, D/16 steps
 //   online softmax per row (a lane owns one row: 16 tokens in the lane, the
 //   other 16 in lane l^32)
-//   O^T[d, row] += V^T . P^T      2 token steps x D/32 tiles
+//   O^T[d, row] += V^T . P^T      2 token steps x D/32 tiles, P split in
+//                                 two bf16 parts (hi + lo) for precision
 // Lane layout of v_mfma_f32_32x32x16_bf16 (A 32x16, B 16x32, C 32x32):
 // A[m][k] in lane m + 32*(k/8), element k%8; B[k][n] in lane n + 32*(k/8);
 // C[m][n] in lane n + 32*((m%8)/4), element 4*(m/8) + m%4.
@@ -54,12 +68,15 @@ constexpr int kWaves = 8;
 constexpr int kBlock = 64;   // tokens per ring stage (32 per wave half)
 constexpr int kIds = 256;    // page-id window
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kMargin = 8.0f;  // lazy-rescale margin, log2 units
 
 struct TileParams {
-  const int32_t* pitems;
+  const int32_t* pitems;       // prefix items, or prefill items (FI_QITEM_*)
   const int32_t* members;
   const int32_t* prefix_slot;
+  __bf16* out;                 // prefill: [N, num_qo_heads, D]
+  float* lse;                  // prefill: [N, num_qo_heads] natural log, or null
   const int32_t* page_ids;
   const char* q;
   const char* k_pages;
@@ -72,6 +89,7 @@ struct TileParams {
   int num_kv_heads;
   int page_size;
   int group;
+  int causal;           // prefill: row r attends VISIBLE + r / G tokens
   float scale_log2;     // sm_scale * log2(e)
 };
 
@@ -133,9 +151,23 @@ __device__ __forceinline__ float sum_with_partner32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
+// Wave roles. Shared prefixes: 4 row groups of 32 rows (128 rows); the two
+// waves of a row group take the two 32-token halves of every block and merge
+// their states at the end. Prefill: 8 row groups (256 rows); each wave takes
+// both halves of every block itself, as two sub-blocks whose products are
+// independent, so one sub-block's matrix work overlaps the other's softmax.
+template <bool kPrefill>
+struct Roles {
+  static constexpr bool kSplit = !kPrefill;
+  static constexpr int kRowGroups = kSplit ? 4 : 8;
+  static constexpr int kSub = kSplit ? 1 : 2;  // 32-token sub-blocks per wave and block
+};
+static_assert(FI_PREFILL_ROWS == 32 * 8, "a prefill tile is 8 row groups of 32 rows");
+
+template <int D, bool kPrefill>
 __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   using Gm = Geom<D>;
+  using R = Roles<kPrefill>;
   constexpr int NS = Gm::kStages;
   constexpr int kRB = Gm::kRowBytes;
   __shared__ __attribute__((aligned(1024))) char s_ring[NS][2][Gm::kBlockBytes];
@@ -144,34 +176,75 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wrow = wave & 3;   // row block of this wave
-  const int wtok = wave >> 2;  // token half of every block
+  const int wrow = R::kSplit ? (wave & 3) : wave;  // row group of this wave
+  const int wtok = R::kSplit ? (wave >> 2) : 0;    // first 32-token half it takes
   const int half = lane >> 5;
-  const int32_t* it = p.pitems + (int64_t)blockIdx.x * FI_PITEM_STRIDE;
-  const int h = it[FI_PITEM_KV_HEAD];
-  const int member_base = it[FI_PITEM_MEMBER_BASE];
-  const int row_begin = it[FI_PITEM_ROW_BEGIN];
-  const int nrows = it[FI_PITEM_NUM_ROWS];
-  const int chunk = it[FI_PITEM_CHUNK];
-  const int page_begin = it[FI_PITEM_PAGE_BEGIN];
-  const int npg = it[FI_PITEM_NUM_PAGES];  // <= FI_PREFIX_MAX_PAGES = kIds
-  const int ntok = npg * p.page_size;
   const int G = p.group;
+  // this lane's query row (column n = lane % 32 of the wave's tiles)
+  const int row = wrow * 32 + (lane & 31);
+
+  int h, nrows, page_begin, npg, ntok;
+  int lim;              // tokens of the chunk this row attends (may be <= 0)
+  int64_t q_index;      // row of q (and, for prefill, of out / lse) x heads + head
+  // prefix: partial row = prefix_slot[b][h] + chunk; prefill: slot (-1 = direct)
+  int slot_base;
+  int gi;
+  bool row_ok;
+  if constexpr (!kPrefill) {
+    const int32_t* it = p.pitems + (int64_t)blockIdx.x * FI_PITEM_STRIDE;
+    h = it[FI_PITEM_KV_HEAD];
+    const int member_base = it[FI_PITEM_MEMBER_BASE];
+    const int row_begin = it[FI_PITEM_ROW_BEGIN];
+    nrows = it[FI_PITEM_NUM_ROWS];
+    const int chunk = it[FI_PITEM_CHUNK];
+    page_begin = it[FI_PITEM_PAGE_BEGIN];
+    npg = it[FI_PITEM_NUM_PAGES];  // <= FI_PREFIX_MAX_PAGES = kIds
+    ntok = npg * p.page_size;
+    row_ok = row < nrows;
+    const int b = p.members[member_base + row_begin + (row_ok ? row / G : 0)];
+    gi = row_ok ? row % G : 0;
+    q_index = (int64_t)b * p.num_qo_heads + (int64_t)h * G + gi;
+    lim = ntok;
+    slot_base = row_ok ? p.prefix_slot[(int64_t)b * p.num_kv_heads + h] + chunk : 0;
+  } else {
+    const int32_t* it = p.pitems + (int64_t)blockIdx.x * FI_QITEM_STRIDE;
+    h = it[FI_QITEM_KV_HEAD];
+    const int qo_row = it[FI_QITEM_QO_ROW];
+    nrows = it[FI_QITEM_NUM_QO] * G;
+    const int kv_begin = it[FI_QITEM_KV_BEGIN];
+    ntok = it[FI_QITEM_NUM_KV];
+    const int visible = it[FI_QITEM_VISIBLE];
+    page_begin = it[FI_QITEM_PAGE_BEGIN];
+    slot_base = it[FI_QITEM_SLOT];
+    npg = (ntok + p.page_size - 1) / p.page_size;  // <= FI_PREFILL_MAX_PAGES = kIds
+    row_ok = row < nrows;
+    const int qi = row_ok ? row / G : 0;
+    gi = row_ok ? row % G : 0;
+    q_index = (int64_t)(qo_row + qi) * p.num_qo_heads + (int64_t)h * G + gi;
+    lim = visible + (p.causal ? qi : 0) - kv_begin;
+    if (ntok == 0) {
+      // a tile that attends nothing (a request with no pages, no mask):
+      // out = 0, lse = -inf, and no K/V read at all
+      if (wtok == 0 && row_ok) {
+        __bf16* dst = p.out + q_index * D;
+        for (int d = 4 * half; d < D; d += 8)
+          *reinterpret_cast<uint2*>(dst + d) = make_uint2(0u, 0u);
+        if (half == 0 && p.lse) p.lse[q_index] = -INFINITY;
+      }
+      return;
+    }
+  }
+  lim = min(lim, ntok);
 
   // ---- page ids of the item (one window: an item has at most kIds pages)
   if (tid < kIds) s_pid[tid] = p.page_ids[page_begin + min(tid, npg - 1)];
 
-  // ---- this lane's query row (column n = lane % 32 of the wave's tiles)
-  const int row = wrow * 32 + (lane & 31);
-  const bool row_ok = row < nrows;
-  const int b = p.members[member_base + row_begin + (row_ok ? row / G : 0)];
-  const int gi = row_ok ? row % G : 0;
   // Q^T as the B operand: lane holds Q[row][16s + 8*half .. +8] for step s
-  // (a padding row loads row 0 of the group's first member and zeroes it, so
-  // the loads are unconditional)
+  // (a padding row loads the tile's first row and zeroes it, so the loads
+  // are unconditional)
   bf16x8_t qf[D / 16];
   {
-    const char* qrow = p.q + ((int64_t)b * p.num_qo_heads + (int64_t)h * G + gi) * kRB;
+    const char* qrow = p.q + q_index * kRB;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       uint4 v = *reinterpret_cast<const uint4*>(qrow + (16 * s + 8 * half) * 2);
@@ -190,8 +263,10 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   // stands for. Blocks past the end re-read the last token (same count of
   // loads on every path, so the vmcnt waits below are exact). Prefix K/V is
   // read once per row block (one, unless a group holds over 128 query
-  // rows), so the loads carry the nontemporal policy (aux bit 1 = nt on
-  // gfx950) and stream past the caches.
+  // rows), so those loads carry the nontemporal policy (aux bit 1 = nt on
+  // gfx950) and stream past the caches; prefill tiles of one request and KV
+  // head read the same K/V, so theirs stay cacheable.
+  constexpr int kAux = kPrefill ? 0 : 2;
   const int64_t head_off = (int64_t)h * p.head_stride;
   const int dma_row = lane / Gm::kPieces;
   const int dma_piece = lane % Gm::kPieces;
@@ -207,9 +282,9 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
       char* kdst = &s_ring[st][0][(wave * Gm::kDmaPerWave + i) * 1024];
       char* vdst = &s_ring[st][1][(wave * Gm::kDmaPerWave + i) * 1024];
       __builtin_amdgcn_global_load_lds((global_void_t*)(p.k_pages + row_off + kp * 16),
-                                       (lds_void_t*)kdst, 16, 0, 2);
+                                       (lds_void_t*)kdst, 16, 0, kAux);
       __builtin_amdgcn_global_load_lds((global_void_t*)(p.v_pages + row_off + vp * 16),
-                                       (lds_void_t*)vdst, 16, 0, 2);
+                                       (lds_void_t*)vdst, 16, 0, kAux);
     }
   };
 
@@ -225,9 +300,15 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   for (int s = 0; s < NS - 1; ++s) issue(s, s);
 
   // addresses that depend only on the lane
-  const int kt = 32 * wtok + (lane & 31);  // K row this lane reads (token of the S^T tile)
   const int g16 = lane >> 4, L16 = lane & 15;
   const int v_k = L16 >> 2, v_p = L16 & 3;  // this lane's input role in a transposed read
+  // Scores stay unscaled; exp2(c * s - c * m) is one fma and an exp. The
+  // running max m is raised only when a sub-block's max passes it by more
+  // than kMargin in log2 units (weights stay <= 2^kMargin), so the
+  // accumulators, which cost a read, a multiply and a write each, are
+  // rescaled rarely after the first block.
+  const float c = p.scale_log2;
+  const float margin = kMargin / c;
 
   for (int j = 0; j < nblocks; ++j) {
     const int st = j % NS;
@@ -240,94 +321,112 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
 
     const char* kst = s_ring[st][0];
     const char* vst = s_ring[st][1];
-    // ---- S^T = K . Q^T
-    u32x4_t kv[D / 16];
+    // ---- S^T = K . Q^T of every sub-block first (independent chains)
+    f32x16_t sc[R::kSub];
 #pragma unroll
-    for (int q = 0; q < D / 16; ++q) {
-      const uint32_t a = lds_u32(kst + kt * kRB + (((2 * q + half) ^ Gm::swz_k(kt)) * 16));
-      asm volatile("ds_read_b128 %0, %1" : "=v"(kv[q]) : "v"(a) : "memory");
-    }
-    lgkm_wait_tied<D / 16>(kv);
-    // two independent accumulation chains halve the dependent-MFMA latency
-    f32x16_t s, s1;
+    for (int sb = 0; sb < R::kSub; ++sb) {
+      const int kt = 32 * (wtok + sb) + (lane & 31);  // K row = token of the S^T tile
+      u32x4_t kv[D / 16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = s1[r] = 0.f;
-#pragma unroll
-    for (int q = 0; q < D / 16; q += 2) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv[q]), qf[q], s, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv[q + 1]), qf[q + 1], s1, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] += s1[r];
-
-    // ---- online softmax; element r holds token m = 4*half + 8*(r/4) + r%4
-    const int tok0 = j * kBlock + 32 * wtok;
-    float mb = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 4 * half + 8 * (r >> 2) + (r & 3);
-      s[r] = tok0 + m < ntok ? s[r] * p.scale_log2 : -INFINITY;
-      mb = fmaxf(mb, s[r]);
-    }
-    mb = max_with_partner32(mb);  // -inf only if this half of the block is all past the end
-    // The running max is raised only when the block's max passes it by more
-    // than kMargin (weights stay <= 2^kMargin), so the accumulators, which
-    // live in AGPRs and cost a read, a multiply and a write each, are rescaled
-    // rarely after the first block.
-    const bool up = mb > m_run + kMargin;
-    if (__builtin_amdgcn_ballot_w64(up)) {
-      const float alpha = up ? __builtin_amdgcn_exp2f(m_run - mb) : 1.f;  // 0 on the first block
-      l_run *= alpha;
-      if (j > 0) {  // the accumulators are still zero on the first block
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      for (int q = 0; q < D / 16; ++q) {
+        const uint32_t a = lds_u32(kst + kt * kRB + (((2 * q + half) ^ Gm::swz_k(kt)) * 16));
+        asm volatile("ds_read_b128 %0, %1" : "=v"(kv[q]) : "v"(a) : "memory");
       }
-      m_run = up ? mb : m_run;
-    }
-    float ps = 0.f;
+      lgkm_wait_tied<D / 16>(kv);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // a masked token has weight 0 (also while m_run is still -inf)
-      s[r] = s[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[r] - m_run);
-      ps += s[r];
+      for (int r = 0; r < 16; ++r) sc[sb][r] = 0.f;
+#pragma unroll
+      for (int q = 0; q < D / 16; ++q)
+        sc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv[q]), qf[q], sc[sb], 0, 0, 0);
     }
-    l_run += sum_with_partner32(ps);
 
-    // ---- O^T += V^T . P^T over two steps of 16 tokens. Step ks takes
-    // elements 8ks .. 8ks+7 of s: contraction index 8*half + i is token
-    // 4*half + 16ks + 8*(i/4) + i%4. This lane's A fragment (d = 32t + lane%32)
-    // comes from two transposed reads: tokens 4*half + 16ks + 0..3, then +8.
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t pb;
+    for (int sb = 0; sb < R::kSub; ++sb) {
+      f32x16_t& sv = sc[sb];
+      // ---- online softmax; element r holds token m = 4*half + 8*(r/4) + r%4
+      const int tok0 = j * kBlock + 32 * (wtok + sb);
+      if (__builtin_amdgcn_ballot_w64(tok0 + 32 > lim)) {  // some row stops in here
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = (__bf16)s[8 * ks + i];
-      u32x2_t va[D / 32][2];
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-#pragma unroll
-        for (int run = 0; run < 2; ++run) {
-          // input role: token 4*(g16/2) + 16ks + 8run + v_k, columns
-          // 32t + 16*(g16%2) + 4*v_p .. +3
-          const int tok = 32 * wtok + 4 * (g16 >> 1) + 16 * ks + 8 * run + v_k;
-          const int d = 32 * t + 16 * (g16 & 1) + 4 * v_p;
-          const uint32_t a = lds_u32(vst + tok * kRB + (((d >> 3) ^ Gm::swz_v(tok)) * 16) + (d & 7) * 2);
-          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(va[t][run]) : "v"(a) : "memory");
+        for (int r = 0; r < 16; ++r) {
+          const int m = 4 * half + 8 * (r >> 2) + (r & 3);
+          if (tok0 + m >= lim) sv[r] = -INFINITY;
         }
       }
-      lgkm_wait_tied<D / 32>(va);
+      float mb = sv[0];
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        const u32x4_t av = {va[t][0][0], va[t][0][1], va[t][1][0], va[t][1][1]};
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[t], 0, 0, 0);
+      for (int r = 1; r < 16; ++r) mb = fmaxf(mb, sv[r]);
+      mb = max_with_partner32(mb);  // -inf if the row attends none of these tokens
+      const bool up = mb > m_run + margin;
+      if (__builtin_amdgcn_ballot_w64(up)) {
+        const float alpha = up ? __builtin_amdgcn_exp2f((m_run - mb) * c) : 1.f;  // 0 at first
+        l_run *= alpha;
+        if (j > 0 || sb > 0) {  // the accumulators are still zero before that
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        }
+        m_run = up ? mb : m_run;
+      }
+      // a row with no token yet has m = -inf and only masked scores: weight 0
+      const float mc = m_run == -INFINITY ? 0.f : m_run * c;
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sv[r] = __builtin_amdgcn_exp2f(fmaf(sv[r], c, -mc));
+        ps += sv[r];
+      }
+      l_run += sum_with_partner32(ps);
+
+      // ---- O^T += V^T . P^T over two steps of 16 tokens. Step ks takes
+      // elements 8ks .. 8ks+7: contraction index 8*half + i is token
+      // 4*half + 16ks + 8*(i/4) + i%4 of the sub-block. This lane's A fragment
+      // (d = 32t + lane%32) comes from two transposed reads: tokens
+      // 4*half + 16ks + 0..3, then +8.
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        // P = hi + lo in two bf16 parts (hi = P rounded to bf16, lo = the
+        // rounding error rounded again): P alone in bf16 carries a relative
+        // error up to 2^-8, which a row that attends few tokens does not
+        // average away; hi + lo is within about 2^-16 of P.
+        bf16x8_t pb, pl;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const __bf16 hi = (__bf16)sv[8 * ks + i];
+          pb[i] = hi;
+          pl[i] = (__bf16)(sv[8 * ks + i] - (float)hi);
+        }
+        u32x2_t va[D / 32][2];
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+          for (int run = 0; run < 2; ++run) {
+            // input role: token 4*(g16/2) + 16ks + 8run + v_k, columns
+            // 32t + 16*(g16%2) + 4*v_p .. +3
+            const int tok = 32 * (wtok + sb) + 4 * (g16 >> 1) + 16 * ks + 8 * run + v_k;
+            const int d = 32 * t + 16 * (g16 & 1) + 4 * v_p;
+            const uint32_t a = lds_u32(vst + tok * kRB + (((d >> 3) ^ Gm::swz_v(tok)) * 16) + (d & 7) * 2);
+            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(va[t][run]) : "v"(a) : "memory");
+          }
+        }
+        lgkm_wait_tied<D / 32>(va);
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+          const u32x4_t av = {va[t][0][0], va[t][0][1], va[t][1][0], va[t][1][1]};
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[t], 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+          const u32x4_t av = {va[t][0][0], va[t][0][1], va[t][1][0], va[t][1][1]};
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pl, o[t], 0, 0, 0);
+        }
       }
     }
   }
   // loads past the end may still be landing in the ring
   wait_vmcnt<0>();
 
+  if constexpr (R::kSplit) {
   // ---- merge the two token halves of each row: waves 4..7 hand (m, l, o)
   // to waves 0..3 through the (drained) ring, lane-for-lane
   __syncthreads();
@@ -344,10 +443,11 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   __syncthreads();
   if (wtok == 1) return;
   {
+    // either half may have attended nothing (m = -inf, l = 0, o = 0)
     const float m2 = s_ml[wrow][0][lane], l2 = s_ml[wrow][1][lane];
-    const float mm = fmaxf(m_run, m2);  // finite: token 0 is in this (first) half
-    const float a1 = __builtin_amdgcn_exp2f(m_run - mm);
-    const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
+    const float mm = fmaxf(m_run, m2);
+    const float a1 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - mm) * c);
+    const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mm) * c);
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -356,12 +456,36 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
     l_run = l_run * a1 + l2 * a2;
     m_run = mm;
   }
+  }  // kSplit
 
-  // ---- partial state of this row: o / l and lse (log2 units)
+  // ---- this row's state: o / l and lse; a row that attended nothing has
+  // o = 0 and lse = -inf
   if (!row_ok) return;
-  const int slot = p.prefix_slot[(int64_t)b * p.num_kv_heads + h] + chunk;
-  const int64_t prow = (int64_t)slot * G + gi;
-  const float inv = 1.f / l_run;
+  const bool empty = l_run == 0.f;
+  const float inv = empty ? 0.f : 1.f / l_run;
+  // log2 units of the scaled scores (m_run is an unscaled score)
+  const float lse2 = empty ? -INFINITY : m_run * c + __builtin_amdgcn_logf(l_run);
+  if (kPrefill && slot_base < 0) {
+    // the tile's only chunk: bf16 out and natural-log lse of the row
+    __bf16* dst = p.out + q_index * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * t + 8 * q4 + 4 * half;
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        const bf16x4_t v = {(__bf16)(o[t][4 * q4] * inv), (__bf16)(o[t][4 * q4 + 1] * inv),
+                            (__bf16)(o[t][4 * q4 + 2] * inv), (__bf16)(o[t][4 * q4 + 3] * inv)};
+        *reinterpret_cast<bf16x4_t*>(dst + d) = v;
+      }
+    }
+    if (half == 0 && p.lse) p.lse[q_index] = lse2 * kLn2;
+    return;
+  }
+  // partial state: prefix rows go to slot prefix_slot[b][h] + chunk (G rows
+  // per slot), prefill rows to slot * 128 + row
+  const int64_t prow = kPrefill ? (int64_t)slot_base * FI_PREFILL_ROWS + row
+                                : (int64_t)slot_base * G + gi;
   float* dst = p.part_o + prow * D;
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) {
@@ -373,14 +497,14 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
           make_float4(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv, o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv);
     }
   }
-  if (half == 0) p.part_lse[prow] = m_run + __builtin_amdgcn_logf(l_run);
+  if (half == 0) p.part_lse[prow] = lse2;
 }
 
 }  // namespace
 
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream) {
   if (a.num_items <= 0) return hipSuccess;
-  TileParams p;
+  TileParams p{};
   p.pitems = a.pitems;
   p.members = a.members;
   p.prefix_slot = a.prefix_slot;
@@ -399,8 +523,36 @@ hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream) {
   p.group = a.group;
   p.scale_log2 = a.sm_scale * kLog2e;
   const dim3 grid((uint32_t)a.num_items), block(64 * kWaves);
-  if (a.head_dim == 128) hipLaunchKernelGGL(tile_attend_kernel<128>, grid, block, 0, stream, p);
-  else if (a.head_dim == 64) hipLaunchKernelGGL(tile_attend_kernel<64>, grid, block, 0, stream, p);
+  if (a.head_dim == 128) hipLaunchKernelGGL((tile_attend_kernel<128, false>), grid, block, 0, stream, p);
+  else if (a.head_dim == 64) hipLaunchKernelGGL((tile_attend_kernel<64, false>), grid, block, 0, stream, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  if (a.num_items <= 0) return hipSuccess;
+  TileParams p{};
+  p.pitems = a.items;
+  p.page_ids = a.page_ids;
+  p.out = static_cast<__bf16*>(a.out);
+  p.lse = a.lse;
+  p.q = static_cast<const char*>(a.q);
+  p.k_pages = static_cast<const char*>(a.k_pages);
+  p.v_pages = static_cast<const char*>(a.v_pages);
+  p.part_o = a.part_o;
+  p.part_lse = a.part_lse;
+  const int64_t row = (int64_t)a.head_dim * 2;
+  p.head_stride = (int64_t)a.page_size * row;
+  p.page_stride = (int64_t)a.num_kv_heads * a.page_size * row;
+  p.num_qo_heads = a.num_qo_heads;
+  p.num_kv_heads = a.num_kv_heads;
+  p.page_size = a.page_size;
+  p.group = a.group;
+  p.causal = a.causal;
+  p.scale_log2 = a.sm_scale * kLog2e;
+  const dim3 grid((uint32_t)a.num_items), block(64 * kWaves);
+  if (a.head_dim == 128) hipLaunchKernelGGL((tile_attend_kernel<128, true>), grid, block, 0, stream, p);
+  else if (a.head_dim == 64) hipLaunchKernelGGL((tile_attend_kernel<64, true>), grid, block, 0, stream, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

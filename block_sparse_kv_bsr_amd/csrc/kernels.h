@@ -42,6 +42,22 @@ struct PrefixArgs {
   float sm_scale;
 };
 
+struct PrefillArgs {
+  const int32_t* items;     // device, [num_items][FI_QITEM_STRIDE]
+  const int32_t* merges;    // device, [num_merges][FI_QMERGE_STRIDE]
+  const int32_t* page_ids;  // device, the request page lists
+  const void* q;            // bf16 [N, num_qo_heads, head_dim]
+  const void* k_pages;
+  const void* v_pages;
+  void* out;                // bf16 [N, num_qo_heads, head_dim]
+  float* lse;               // [N, num_qo_heads] natural log, or null
+  float* part_o;            // [slots, FI_PREFILL_ROWS, head_dim]
+  float* part_lse;          // [slots, FI_PREFILL_ROWS], log2 units
+  int64_t num_items, num_merges;
+  int32_t num_qo_heads, num_kv_heads, head_dim, page_size, group, causal;
+  float sm_scale;
+};
+
 struct MergeTwoArgs {
   const void* v_a;
   const float* s_a;
@@ -57,5 +73,7 @@ struct MergeTwoArgs {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge_two(const MergeTwoArgs& a, hipStream_t stream);
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_merge(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace fi

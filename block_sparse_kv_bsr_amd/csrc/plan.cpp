@@ -53,6 +53,44 @@ int64_t count_items(const std::vector<int64_t>& npages, int64_t c, int64_t heads
 }
 
 }  // namespace
+
+fi_status check_page_table(const int32_t* kv_indptr, const int32_t* kv_indices,
+                           const int32_t* kv_last_page_len, int32_t batch, int32_t page_size,
+                           int64_t num_pool_pages, std::vector<int64_t>* tokens) {
+  if (!kv_indptr) return fail(FI_ERR_INVALID_ARG, "kv_indptr is NULL");
+  if (batch > 0 && !kv_last_page_len) return fail(FI_ERR_INVALID_ARG, "kv_last_page_len is NULL");
+  if (page_size < 1 || page_size > 4096)
+    return fail(FI_ERR_INVALID_ARG, "page_size must be in [1, 4096]");
+  if (num_pool_pages < 0) return fail(FI_ERR_INVALID_ARG, "num_pool_pages < 0");
+  if (kv_indptr[0] != 0) return fail(FI_ERR_INVALID_ARG, "kv_indptr[0] != 0");
+  for (int32_t b = 0; b < batch; ++b)
+    if (kv_indptr[b + 1] < kv_indptr[b])
+      return fail(FI_ERR_INVALID_ARG, "kv_indptr is not non-decreasing at request " +
+                                          std::to_string(b));
+  const int64_t nnz = batch > 0 ? kv_indptr[batch] : 0;
+  if (nnz > 0 && !kv_indices) return fail(FI_ERR_INVALID_ARG, "kv_indices is NULL");
+  for (int64_t j = 0; j < nnz; ++j)
+    if (kv_indices[j] < 0 || kv_indices[j] >= num_pool_pages)
+      return fail(FI_ERR_INVALID_ARG, "kv_indices[" + std::to_string(j) +
+                                          "] outside [0, num_pool_pages)");
+  tokens->assign(batch, 0);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t npages = kv_indptr[b + 1] - kv_indptr[b];
+    const int32_t ell = kv_last_page_len[b];
+    if (npages > 0) {
+      if (ell < 1 || ell > page_size)
+        return fail(FI_ERR_INVALID_ARG, "kv_last_page_len[" + std::to_string(b) +
+                                            "] outside [1, page_size]");
+      (*tokens)[b] = (npages - 1) * (int64_t)page_size + ell;
+    } else if (ell < 0 || ell > page_size) {
+      return fail(FI_ERR_INVALID_ARG, "kv_last_page_len[" + std::to_string(b) +
+                                          "] outside [0, page_size]");
+    }
+    if ((*tokens)[b] > INT32_MAX) return fail(FI_ERR_INVALID_ARG, "request longer than 2^31-1 tokens");
+  }
+  return FI_OK;
+}
+
 }  // namespace fi
 
 extern "C" {
@@ -85,38 +123,17 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
       return fail(FI_ERR_UNSUPPORTED, "dtype must be FI_DTYPE_F32, FI_DTYPE_BF16 or FI_DTYPE_FP8_E4M3");
     if (dtype == FI_DTYPE_FP8_E4M3 && head_dim != 128)
       return fail(FI_ERR_UNSUPPORTED, "an fp8 KV cache needs head_dim 128");
-    if (page_size < 1 || page_size > 4096)
-      return fail(FI_ERR_INVALID_ARG, "page_size must be in [1, 4096]");
-    if (num_pool_pages < 0) return fail(FI_ERR_INVALID_ARG, "num_pool_pages < 0");
-    if (kv_indptr[0] != 0) return fail(FI_ERR_INVALID_ARG, "kv_indptr[0] != 0");
-    for (int32_t b = 0; b < batch; ++b)
-      if (kv_indptr[b + 1] < kv_indptr[b])
-        return fail(FI_ERR_INVALID_ARG, "kv_indptr is not non-decreasing at request " +
-                                            std::to_string(b));
+    std::vector<int64_t> ntok;
+    {
+      const fi_status st = fi::check_page_table(kv_indptr, kv_indices, kv_last_page_len, batch,
+                                                page_size, num_pool_pages, &ntok);
+      if (st != FI_OK) return st;
+    }
     const int64_t nnz = batch > 0 ? kv_indptr[batch] : 0;
-    if (nnz > 0 && !kv_indices) return fail(FI_ERR_INVALID_ARG, "kv_indices is NULL");
-    for (int64_t j = 0; j < nnz; ++j)
-      if (kv_indices[j] < 0 || kv_indices[j] >= num_pool_pages)
-        return fail(FI_ERR_INVALID_ARG, "kv_indices[" + std::to_string(j) +
-                                            "] outside [0, num_pool_pages)");
-    std::vector<int64_t> npages(batch), ntok(batch);
+    std::vector<int64_t> npages(batch);
     int64_t total_tokens = 0;
     for (int32_t b = 0; b < batch; ++b) {
       npages[b] = kv_indptr[b + 1] - kv_indptr[b];
-      const int32_t ell = kv_last_page_len[b];
-      if (npages[b] > 0) {
-        if (ell < 1 || ell > page_size)
-          return fail(FI_ERR_INVALID_ARG, "kv_last_page_len[" + std::to_string(b) +
-                                              "] outside [1, page_size]");
-        ntok[b] = (npages[b] - 1) * (int64_t)page_size + ell;
-      } else {
-        if (ell < 0 || ell > page_size)
-          return fail(FI_ERR_INVALID_ARG, "kv_last_page_len[" + std::to_string(b) +
-                                              "] outside [0, page_size]");
-        ntok[b] = 0;
-      }
-      if (ntok[b] > INT32_MAX)
-        return fail(FI_ERR_INVALID_ARG, "request longer than 2^31-1 tokens");
       total_tokens += ntok[b];
     }
     fi_plan_opts o{};

@@ -63,7 +63,36 @@ struct fi_plan {
   int64_t num_pitems() const { return (int64_t)pitems.size() / FI_PITEM_STRIDE; }
 };
 
+// Work list of one prefill / append call. Workspace sections (each on a
+// 256-byte boundary): items, merges and page ids (copied from the host),
+// then the partial states of cut tiles (written by the tile kernel).
+struct fi_prefill_plan {
+  int32_t batch = 0, num_qo_heads = 0, num_kv_heads = 0, head_dim = 0, page_size = 0;
+  int32_t group = 0, causal = 1, tokens_per_tile = 0, chunk_tokens = 0;
+  int64_t num_pool_pages = 0, total_qo = 0, total_kv = 0, visible_pairs = 0;
+  int64_t num_tiles = 0, num_slots = 0;
+  std::vector<int32_t> items;   // num_items * FI_QITEM_STRIDE
+  std::vector<int32_t> merges;  // num_merges * FI_QMERGE_STRIDE
+  struct {
+    int64_t items = 0, merges = 0, page_ids = 0, part_o = 0, part_lse = 0;
+    int64_t image_bytes = 0, total_bytes = 0;
+  } ws;
+  std::vector<uint8_t> image;
+  void* pinned = nullptr;
+  const void* uploaded_to = nullptr;
+  int64_t num_items() const { return (int64_t)items.size() / FI_QITEM_STRIDE; }
+  int64_t num_merges() const { return (int64_t)merges.size() / FI_QMERGE_STRIDE; }
+};
+
 namespace fi {
 // Frees the host parts of a plan (the launch layer frees `pinned` first).
 void plan_free_host(fi_plan* p);
+void plan_free_host(fi_prefill_plan* p);
+
+// Checks a BSR page table (kv_indptr, kv_indices, kv_last_page_len) and
+// fills the token count of each request. On failure sets the error message
+// and returns the status.
+fi_status check_page_table(const int32_t* kv_indptr, const int32_t* kv_indices,
+                           const int32_t* kv_last_page_len, int32_t batch, int32_t page_size,
+                           int64_t num_pool_pages, std::vector<int64_t>* tokens);
 }  // namespace fi

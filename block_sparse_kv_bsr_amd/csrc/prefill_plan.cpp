@@ -1,0 +1,308 @@
+// Work list for prefill / append attention over a paged / BSR KV cache.
+//
+// FlashInfer paper explainer ("FlashInfer: Block-Sparse KV 캐시로 어텐션 병목을
+// 해소하다", visionhong.com), section on where the attention bottleneck lies:
+// prefill attends every token of a prompt at once and is bound by arithmetic.
+// The query tokens of a request are its newest cached tokens; with the causal
+// mask query i of n over L cached tokens attends the first L - n + i + 1.
+//
+// A tile is up to FI_PREFILL_ROWS query rows of one (request, KV head): its
+// FI_PREFILL_ROWS / G query tokens times the G query heads that share the KV
+// head, so every K/V row a workgroup loads serves all of them (a matrix
+// problem for the matrix cores). A tile attends the tokens its last query
+// sees. The same load-balancing idea as the decode planner (explainer,
+// benchmark section: cut long work into units and interleave them with
+// short ones) applies: a tile whose range is long is cut into KV chunks of
+// whole pages, and a merge pass combines the chunks' partial states. The
+// tiles of one (request, KV head) read the same K/V, so they are kept on one
+// L2 domain (XCD) of the chip: pairs are dealt to per-XCD bins by the
+// longest-processing-time rule and the bins interleaved in the order the
+// dispatcher deals workgroups to XCDs.
+//
+// Plain C++17 with no HIP dependency: the planner is tested on CPU-only hosts.
+#include <algorithm>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <string>
+
+#include "plan.h"
+
+namespace fi {
+
+void plan_free_host(fi_prefill_plan* p) { delete p; }
+
+namespace {
+
+fi_status fail(fi_status st, const std::string& msg) {
+  set_error(msg);
+  return st;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+}  // namespace fi
+
+extern "C" {
+
+fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                 const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                                 int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t page_size, int64_t num_pool_pages,
+                                 fi_dtype dtype, int32_t causal, const fi_prefill_opts* opts,
+                                 fi_prefill_plan** out_plan) {
+  using fi::ceil_div;
+  using fi::fail;
+  try {
+    if (!out_plan) return fail(FI_ERR_INVALID_ARG, "out_plan is NULL");
+    *out_plan = nullptr;
+    if (batch < 0) return fail(FI_ERR_INVALID_ARG, "batch < 0");
+    if (!qo_indptr) return fail(FI_ERR_INVALID_ARG, "qo_indptr is NULL");
+    if (num_qo_heads <= 0 || num_kv_heads <= 0)
+      return fail(FI_ERR_INVALID_ARG, "head counts must be positive");
+    if (num_qo_heads % num_kv_heads != 0)
+      return fail(FI_ERR_INVALID_ARG, "num_qo_heads is not a multiple of num_kv_heads");
+    const int32_t group = num_qo_heads / num_kv_heads;
+    if (group > FI_PREFILL_ROWS)
+      return fail(FI_ERR_UNSUPPORTED, "GQA group size above " + std::to_string(FI_PREFILL_ROWS));
+    if (head_dim != 64 && head_dim != 128)
+      return fail(FI_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (dtype != FI_DTYPE_BF16) return fail(FI_ERR_UNSUPPORTED, "prefill needs FI_DTYPE_BF16");
+    std::vector<int64_t> kvlen;
+    {
+      const fi_status st = fi::check_page_table(kv_indptr, kv_indices, kv_last_page_len, batch,
+                                                page_size, num_pool_pages, &kvlen);
+      if (st != FI_OK) return st;
+    }
+    if (qo_indptr[0] != 0) return fail(FI_ERR_INVALID_ARG, "qo_indptr[0] != 0");
+    for (int32_t b = 0; b < batch; ++b) {
+      if (qo_indptr[b + 1] < qo_indptr[b])
+        return fail(FI_ERR_INVALID_ARG, "qo_indptr is not non-decreasing at request " +
+                                            std::to_string(b));
+      if (causal && qo_indptr[b + 1] - qo_indptr[b] > kvlen[b])
+        return fail(FI_ERR_INVALID_ARG, "request " + std::to_string(b) +
+                                            " has more query tokens than cached tokens "
+                                            "(causal queries are the newest cached tokens)");
+    }
+    const int64_t total_qo = batch > 0 ? qo_indptr[batch] : 0;
+    if (total_qo * (int64_t)num_qo_heads > INT32_MAX)
+      return fail(FI_ERR_INVALID_ARG, "query rows x heads exceed 2^31-1");
+    fi_prefill_opts o{};
+    if (opts) o = *opts;
+    if (o.num_cus < 0 || o.items_per_cu < 0 || o.fixed_chunk_tokens < 0 || o.num_xcds < 0)
+      return fail(FI_ERR_INVALID_ARG, "negative planner option");
+    const int64_t num_cus = o.num_cus ? o.num_cus : 256;
+    const int64_t items_per_cu = o.items_per_cu ? o.items_per_cu : 4;
+    const int64_t num_xcds = o.num_xcds ? o.num_xcds : 8;
+
+    auto p = std::make_unique<fi_prefill_plan>();
+    p->batch = batch;
+    p->num_qo_heads = num_qo_heads;
+    p->num_kv_heads = num_kv_heads;
+    p->head_dim = head_dim;
+    p->page_size = page_size;
+    p->group = group;
+    p->causal = causal ? 1 : 0;
+    p->num_pool_pages = num_pool_pages;
+    p->total_qo = total_qo;
+    const int64_t T = FI_PREFILL_ROWS / group;  // query tokens per tile
+    p->tokens_per_tile = (int32_t)T;
+
+    // ---- tiles: (request, KV head, block of T query tokens); the range a
+    // tile attends is what its last query sees
+    struct Tile {
+      int32_t b, qo_row, nqo;
+      int64_t visible, range;
+    };
+    std::vector<Tile> tiles;
+    int64_t work = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t n = qo_indptr[b + 1] - qo_indptr[b], L = kvlen[b];
+      p->total_kv += L;
+      for (int64_t i = 0; i < n; ++i) p->visible_pairs += causal ? L - n + i + 1 : L;
+      for (int64_t t0 = 0; t0 < n; t0 += T) {
+        const int64_t nq = std::min<int64_t>(T, n - t0);
+        const int64_t vis = causal ? L - n + t0 + 1 : L;
+        const int64_t range = causal ? vis + nq - 1 : L;
+        tiles.push_back({b, (int32_t)(qo_indptr[b] + t0), (int32_t)nq, vis, range});
+        work += range * num_kv_heads;
+      }
+    }
+    p->num_tiles = (int64_t)tiles.size() * num_kv_heads;
+
+    // ---- one chunk length C (whole pages, at most FI_PREFILL_MAX_PAGES)
+    const int64_t cap = (int64_t)FI_PREFILL_MAX_PAGES * page_size;
+    int64_t C;
+    if (o.fixed_chunk_tokens > 0) {
+      C = ceil_div(o.fixed_chunk_tokens, page_size) * page_size;
+    } else {
+      const int64_t want = std::max<int64_t>(ceil_div(work, num_cus * items_per_cu), 512);
+      C = ceil_div(want, page_size) * page_size;
+    }
+    C = std::min(C, cap);
+
+    // ---- items, longest chunk first
+    int32_t longest = 0;
+    for (const Tile& t : tiles) {
+      const int64_t k = std::max<int64_t>(1, ceil_div(t.range, C));
+      for (int32_t h = 0; h < num_kv_heads; ++h) {
+        const int64_t slot0 = k > 1 ? p->num_slots : -1;
+        if (k > 1) {
+          int32_t m[FI_QMERGE_STRIDE] = {0};
+          m[FI_QMERGE_QO_ROW] = t.qo_row;
+          m[FI_QMERGE_NUM_QO] = t.nqo;
+          m[FI_QMERGE_KV_HEAD] = h;
+          m[FI_QMERGE_SLOT_BEGIN] = (int32_t)slot0;
+          m[FI_QMERGE_NUM_CHUNKS] = (int32_t)k;
+          p->merges.insert(p->merges.end(), m, m + FI_QMERGE_STRIDE);
+          p->num_slots += k;
+        }
+        for (int64_t c = 0; c < k; ++c) {
+          const int64_t begin = c * C;
+          const int64_t len = std::min<int64_t>(C, t.range - begin);
+          int32_t f[FI_QITEM_STRIDE] = {0};
+          f[FI_QITEM_REQUEST] = t.b;
+          f[FI_QITEM_KV_HEAD] = h;
+          f[FI_QITEM_QO_ROW] = t.qo_row;
+          f[FI_QITEM_NUM_QO] = t.nqo;
+          f[FI_QITEM_KV_BEGIN] = (int32_t)begin;
+          f[FI_QITEM_NUM_KV] = (int32_t)std::max<int64_t>(len, 0);
+          f[FI_QITEM_VISIBLE] = (int32_t)t.visible;
+          f[FI_QITEM_PAGE_BEGIN] = (int32_t)(kv_indptr[t.b] + begin / page_size);
+          f[FI_QITEM_SLOT] = k > 1 ? (int32_t)(slot0 + c) : -1;
+          f[FI_QITEM_CHUNK] = (int32_t)c;
+          longest = std::max(longest, f[FI_QITEM_NUM_KV]);
+          p->items.insert(p->items.end(), f, f + FI_QITEM_STRIDE);
+        }
+      }
+    }
+    p->chunk_tokens = longest;
+
+    // ---- order: (request, KV head) pairs dealt to num_xcds bins, heaviest
+    // first into the least loaded bin; bins interleaved item by item
+    {
+      const int64_t n = p->num_items();
+      const int32_t* it = p->items.data();
+      auto key = [&](int64_t i, int f) { return it[i * FI_QITEM_STRIDE + f]; };
+      // items of each pair, longest chunk first
+      std::vector<int64_t> order(n);
+      for (int64_t i = 0; i < n; ++i) order[i] = i;
+      std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b) {
+        for (int f : {FI_QITEM_REQUEST, FI_QITEM_KV_HEAD})
+          if (key(a, f) != key(b, f)) return key(a, f) < key(b, f);
+        if (key(a, FI_QITEM_NUM_KV) != key(b, FI_QITEM_NUM_KV))
+          return key(a, FI_QITEM_NUM_KV) > key(b, FI_QITEM_NUM_KV);
+        for (int f : {FI_QITEM_QO_ROW, FI_QITEM_CHUNK})
+          if (key(a, f) != key(b, f)) return key(a, f) < key(b, f);
+        return false;
+      });
+      struct Pair {
+        int64_t begin, end, work;
+      };
+      std::vector<Pair> pairs;
+      for (int64_t i = 0; i < n;) {
+        int64_t j = i, w = 0;
+        while (j < n && key(order[j], FI_QITEM_REQUEST) == key(order[i], FI_QITEM_REQUEST) &&
+               key(order[j], FI_QITEM_KV_HEAD) == key(order[i], FI_QITEM_KV_HEAD)) {
+          // a chunk's blocks of 64 tokens, plus one for the item's fixed costs
+          w += (key(order[j], FI_QITEM_NUM_KV) + 63) / 64 + 1;
+          ++j;
+        }
+        pairs.push_back({i, j, w});
+        i = j;
+      }
+      std::vector<int64_t> by_work(pairs.size());
+      for (size_t i = 0; i < pairs.size(); ++i) by_work[i] = (int64_t)i;
+      std::stable_sort(by_work.begin(), by_work.end(),
+                       [&](int64_t a, int64_t b) { return pairs[a].work > pairs[b].work; });
+      std::vector<std::vector<int64_t>> bins((size_t)num_xcds);
+      std::vector<int64_t> load((size_t)num_xcds, 0);
+      for (int64_t pi : by_work) {
+        const size_t x = (size_t)(std::min_element(load.begin(), load.end()) - load.begin());
+        load[x] += pairs[pi].work;
+        for (int64_t j = pairs[pi].begin; j < pairs[pi].end; ++j) bins[x].push_back(order[j]);
+      }
+      std::vector<int32_t> sorted;
+      sorted.reserve(p->items.size());
+      for (size_t j = 0, left = (size_t)n; left > 0; ++j)
+        for (auto& bin : bins)
+          if (j < bin.size()) {
+            sorted.insert(sorted.end(), it + bin[j] * FI_QITEM_STRIDE,
+                          it + (bin[j] + 1) * FI_QITEM_STRIDE);
+            --left;
+          }
+      p->items.swap(sorted);
+    }
+
+    // ---- workspace layout and host image of its uploaded part
+    const int64_t nnz = batch > 0 ? kv_indptr[batch] : 0;
+    auto& ws = p->ws;
+    int64_t off = 0;
+    ws.items = off;
+    off = fi::align_up(off + (int64_t)p->items.size() * 4, 256);
+    ws.merges = off;
+    off = fi::align_up(off + (int64_t)p->merges.size() * 4, 256);
+    ws.page_ids = off;
+    off = fi::align_up(off + nnz * 4, 256);
+    ws.image_bytes = off;
+    ws.part_o = off;
+    off = fi::align_up(off + p->num_slots * FI_PREFILL_ROWS * (int64_t)head_dim * 4, 256);
+    ws.part_lse = off;
+    off = fi::align_up(off + p->num_slots * FI_PREFILL_ROWS * 4, 256);
+    ws.total_bytes = std::max<int64_t>(off, 256);
+    p->image.assign(ws.image_bytes, 0);
+    if (!p->items.empty()) std::memcpy(p->image.data() + ws.items, p->items.data(), p->items.size() * 4);
+    if (!p->merges.empty())
+      std::memcpy(p->image.data() + ws.merges, p->merges.data(), p->merges.size() * 4);
+    if (nnz > 0) std::memcpy(p->image.data() + ws.page_ids, kv_indices, nnz * 4);
+
+    *out_plan = p.release();
+    return FI_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(FI_ERR_NOMEM, "host allocation failed in fi_prefill_plan_create");
+  } catch (...) {
+    return fail(FI_ERR_INVALID_ARG, "unexpected error in fi_prefill_plan_create");
+  }
+}
+
+fi_status fi_prefill_plan_get_info(const fi_prefill_plan* p, fi_prefill_info* info) {
+  if (!p || !info) return fi::fail(FI_ERR_INVALID_ARG, "NULL plan or info");
+  fi_prefill_info r{};
+  r.num_items = p->num_items();
+  r.num_tiles = p->num_tiles;
+  r.num_merges = p->num_merges();
+  r.num_partial_slots = p->num_slots;
+  r.workspace_bytes = p->ws.total_bytes;
+  r.total_qo_tokens = p->total_qo;
+  r.total_kv_tokens = p->total_kv;
+  r.visible_pairs = p->visible_pairs;
+  r.tokens_per_tile = p->tokens_per_tile;
+  r.chunk_tokens = p->chunk_tokens;
+  r.batch = p->batch;
+  r.num_qo_heads = p->num_qo_heads;
+  r.num_kv_heads = p->num_kv_heads;
+  r.head_dim = p->head_dim;
+  r.page_size = p->page_size;
+  r.causal = p->causal;
+  *info = r;
+  return FI_OK;
+}
+
+fi_status fi_prefill_plan_work_list(const fi_prefill_plan* p, const int32_t** items,
+                                    int64_t* num_items) {
+  if (!p || !items || !num_items) return fi::fail(FI_ERR_INVALID_ARG, "NULL argument");
+  *items = p->items.data();
+  *num_items = p->num_items();
+  return FI_OK;
+}
+
+fi_status fi_prefill_plan_merges(const fi_prefill_plan* p, const int32_t** merges,
+                                 int64_t* num_merges) {
+  if (!p || !merges || !num_merges) return fi::fail(FI_ERR_INVALID_ARG, "NULL argument");
+  *merges = p->merges.data();
+  *num_merges = p->num_merges();
+  return FI_OK;
+}
+
+}  // extern "C"

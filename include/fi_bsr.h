@@ -315,6 +315,159 @@ fi_status fi_merge_states(fi_dtype dtype, const void* v_a, const float* s_a,
  * pinned staging memory, so uploads in flight finish first. */
 void fi_plan_destroy(fi_plan* plan);
 
+/* ======================================================================
+ * Prefill / append: several query tokens per request over the same paged /
+ * BSR cache (explainer, section on where the attention bottleneck lies:
+ * prefill attends all tokens of a prompt at once and is bound by
+ * arithmetic, not memory).
+ *
+ * Request b has n_b = qo_indptr[b+1] - qo_indptr[b] query tokens, rows
+ * qo_indptr[b] .. qo_indptr[b+1]-1 of q. They are the request's newest
+ * tokens, already written to its pages: with L_b cached tokens, query i
+ * (0-based) sits at position L_b - n_b + i and, with the causal mask,
+ * attends the first L_b - n_b + i + 1 tokens (itself and everything
+ * before); without it, all L_b. n_b = 1 is the decode step. For query row r
+ * of request b and query head h (KV head h / G):
+ *     out[r,h] = sum_t softmax(s)_t V[page_t, h/G, slot_t, :],
+ *     lse[r,h] = ln sum_t exp(s_t),  s_t = sm_scale <q[r,h,:], K[...]>
+ * over the attended tokens t; a query that attends no token (only possible
+ * without the mask, for a request with no pages) gets out = 0, lse = -inf.
+ *
+ * Layout: q, out [N, num_qo_heads, head_dim] bf16 (N = qo_indptr[batch]),
+ * lse [N, num_qo_heads] float32, K/V pages as for decode, bf16.
+ * ====================================================================== */
+typedef struct fi_prefill_plan fi_prefill_plan; /* opaque, host-owned */
+
+/* Planner knobs. Zero selects the default for every field. */
+typedef struct {
+  int32_t num_cus;            /* compute units to balance over (default 256) */
+  int32_t items_per_cu;       /* target work items per CU (default 4) */
+  int32_t fixed_chunk_tokens; /* >0: cut KV ranges into chunks of exactly this
+                                 many tokens (rounded up to whole pages, at
+                                 most FI_PREFILL_MAX_PAGES pages) */
+  int32_t num_xcds;           /* L2 domains the dispatcher deals workgroups
+                                 over in turn (default 8, MI355X's XCDs) */
+} fi_prefill_opts;
+
+typedef struct {
+  int64_t num_items;          /* tiles x KV chunks */
+  int64_t num_tiles;          /* (request, KV head, block of query tokens) */
+  int64_t num_merges;         /* tiles cut into several KV chunks */
+  int64_t num_partial_slots;  /* partial states of FI_PREFILL_ROWS rows each */
+  int64_t workspace_bytes;    /* device workspace fi_prefill_plan_upload needs */
+  int64_t total_qo_tokens;    /* N */
+  int64_t total_kv_tokens;    /* sum of L_b */
+  int64_t visible_pairs;      /* sum over query tokens of the tokens each attends */
+  int32_t tokens_per_tile;    /* query tokens per tile: FI_PREFILL_ROWS / G */
+  int32_t chunk_tokens;       /* longest KV chunk of an item */
+  int32_t batch, num_qo_heads, num_kv_heads, head_dim, page_size, causal;
+} fi_prefill_info;
+
+/*
+ * Fields of one prefill work item (fi_prefill_plan_work_list). A tile is
+ * FI_PREFILL_ROWS query rows of one request and KV head: row j is query
+ * token j / G of the tile and query head KV_HEAD * G + j % G. An item
+ * attends a tile over one chunk of the request's tokens; a tile whose
+ * attended range exceeds one chunk is cut into several items whose partial
+ * states a merge pass combines.
+ */
+enum {
+  FI_QITEM_REQUEST = 0,
+  FI_QITEM_KV_HEAD = 1,
+  FI_QITEM_QO_ROW = 2,     /* row of q / out of the tile's first query token */
+  FI_QITEM_NUM_QO = 3,     /* query tokens in the tile (rows = NUM_QO x G) */
+  FI_QITEM_KV_BEGIN = 4,   /* first token of the chunk (request order, whole pages) */
+  FI_QITEM_NUM_KV = 5,     /* tokens in the chunk; 0 only for a tile that attends nothing */
+  FI_QITEM_VISIBLE = 6,    /* tokens the tile's first query attends; with the causal
+                              mask query j of the tile attends VISIBLE + j */
+  FI_QITEM_PAGE_BEGIN = 7, /* index into kv_indices of the chunk's first page */
+  FI_QITEM_SLOT = 8,       /* -1: the item writes out / lse; else its partial slot */
+  FI_QITEM_CHUNK = 9,      /* chunk number within the tile */
+  FI_QITEM_STRIDE = 12,
+  FI_PREFILL_ROWS = 256,      /* query rows per tile */
+  FI_PREFILL_MAX_PAGES = 256  /* pages per chunk at most */
+};
+
+/* Fields of one merge of a cut tile (fi_prefill_plan_merges): its chunks'
+ * partial states sit in slots SLOT_BEGIN .. SLOT_BEGIN + NUM_CHUNKS - 1. */
+enum {
+  FI_QMERGE_QO_ROW = 0,
+  FI_QMERGE_NUM_QO = 1,
+  FI_QMERGE_KV_HEAD = 2,
+  FI_QMERGE_SLOT_BEGIN = 3,
+  FI_QMERGE_NUM_CHUNKS = 4,
+  FI_QMERGE_STRIDE = 8
+};
+
+/*
+ * Build the work list of one prefill / append call. Host only.
+ *
+ * qo_indptr        host int32 [batch+1], qo_indptr[0] = 0, non-decreasing;
+ *                  with causal != 0 every n_b <= L_b
+ * kv_indptr, kv_indices, kv_last_page_len: the page table, as for
+ *                  fi_plan_create (L_b tokens per request)
+ * num_qo_heads, num_kv_heads: G = num_qo_heads / num_kv_heads in 1 .. 128
+ * head_dim         64 or 128
+ * page_size        1 .. 4096
+ * dtype            FI_DTYPE_BF16 (q, K, V, out)
+ * causal           nonzero: the causal mask above; 0: every query attends all
+ * opts             may be NULL
+ *
+ * Tiles: each request's query tokens in blocks of FI_PREFILL_ROWS / G, per
+ * KV head. A tile attends the tokens its last query sees; that range is cut
+ * into chunks of C tokens (whole pages, at most FI_PREFILL_MAX_PAGES
+ * pages), C chosen so the items fill num_cus x items_per_cu (never finer
+ * than 512 tokens) unless fixed_chunk_tokens is set.
+ *
+ * Order: every tile of one (request, KV head) reads the same K/V, so the
+ * pairs are dealt to num_xcds bins, heaviest pair first into the least
+ * loaded bin, and the bins are interleaved item by item: item i runs on L2
+ * domain i mod num_xcds (the dispatcher hands workgroups to the XCDs in
+ * turn) and the tiles of a pair share that domain's L2. Within a bin pairs
+ * keep their dealing order and a pair's items go longest chunk first (ties
+ * by query row, chunk).
+ */
+fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                 const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                                 int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t page_size, int64_t num_pool_pages,
+                                 fi_dtype dtype, int32_t causal, const fi_prefill_opts* opts,
+                                 fi_prefill_plan** out_plan);
+
+fi_status fi_prefill_plan_get_info(const fi_prefill_plan* plan, fi_prefill_info* info);
+
+/* Host views of the items (num_items * FI_QITEM_STRIDE int32, launch order)
+ * and of the merges (num_merges * FI_QMERGE_STRIDE int32). */
+fi_status fi_prefill_plan_work_list(const fi_prefill_plan* plan, const int32_t** items,
+                                    int64_t* num_items);
+fi_status fi_prefill_plan_merges(const fi_prefill_plan* plan, const int32_t** merges,
+                                 int64_t* num_merges);
+
+/* Copy items, merges and page ids into the caller's device workspace
+ * (256-byte aligned, at least info.workspace_bytes), asynchronously on
+ * `stream` from pinned memory the plan owns. */
+fi_status fi_prefill_plan_upload(fi_prefill_plan* plan, void* workspace, size_t workspace_bytes,
+                                 fi_stream_t stream);
+
+/*
+ * Run prefill / append attention for an uploaded plan on `stream`: the tile
+ * kernel (matrix cores), then, if some tile was cut, the merge kernel. No
+ * host synchronisation. Calls that use the same workspace must not overlap.
+ *
+ * q        device bf16 [N, num_qo_heads, head_dim], 16-byte aligned
+ * k_pages, v_pages  device bf16 [num_pool_pages, num_kv_heads, page_size, head_dim]
+ * out      device bf16 [N, num_qo_heads, head_dim] (written)
+ * lse      device float32 [N, num_qo_heads] (written); may be NULL
+ * sm_scale score scale; <= 0 selects 1/sqrt(head_dim)
+ */
+fi_status fi_prefill_run(const fi_prefill_plan* plan, const void* q, const void* k_pages,
+                         const void* v_pages, void* out, float* lse, float sm_scale,
+                         void* workspace, size_t workspace_bytes, fi_stream_t stream);
+
+/* Free a prefill plan (NULL is ignored); waits for the device if it holds
+ * pinned staging memory. */
+void fi_prefill_plan_destroy(fi_prefill_plan* plan);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* fi_last_error(void);
 

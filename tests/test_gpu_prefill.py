@@ -1,0 +1,148 @@
+"""GPU parity of prefill / append attention: the HIP tile kernel (and the
+merge kernel for cut tiles) through the C ABI against the float64 oracle.
+
+Small ragged cases cover both head sizes, GQA groups 1..8 and one that is
+not a power of two, page sizes 1..64, causal and unmasked, single-chunk
+tiles (direct output) and cut tiles (forced chunk lengths, merge kernel),
+requests with no queries and an unmasked request with no pages. The two
+full-size workloads run with the plan bench.py times and are checked on
+sampled rows.
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_kv_bsr_amd as fb
+import oracle.attention as oa
+from block_sparse_kv_bsr_amd.workloads import random_prefill_workload, workload
+from tests.parity import compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    fb.lib()
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def make_plan(w, **kw):
+    return fb.prefill_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len,
+                           w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                           w.num_pool_pages, causal=w.causal, **kw)
+
+
+def run_case(w, what, **opts):
+    log(f"[case] {what} B={w.batch} N={w.num_qo_tokens} Hq={w.num_qo_heads} "
+        f"Hkv={w.num_kv_heads} d={w.head_dim} P={w.page_size} causal={w.causal} opts={opts}")
+    q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    p = make_plan(w, **opts)
+    out, lse = fb.prefill(q, k, v, p)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    qh, kh, vh = (t.double().cpu().numpy() for t in (q, k, v))
+    O, LSE = oa.prefill_attention(qh, kh, vh, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                  w.last_page_len, w.causal, w.sm_scale)
+    stats = compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE, True, what)
+    log(f"[ok] {what} items={p.info['num_items']} merges={p.info['num_merges']} "
+        f"oracle {time.time() - t0:.1f}s {stats}")
+    return p, (q, k, v), (out, lse)
+
+
+CASES = [
+    # seed, B, maxL, Hq, Hkv, d, P, causal, max_qo, fixed_chunk
+    (1, 4, 300, 8, 2, 64, 16, True, None, 0),
+    (2, 3, 200, 4, 4, 64, 4, True, None, 32),
+    (3, 5, 150, 16, 2, 128, 16, True, 40, 48),
+    (4, 3, 90, 4, 1, 64, 1, False, None, 7),
+    (5, 4, 260, 8, 2, 128, 64, True, 1, 0),
+    (6, 2, 500, 12, 2, 64, 16, True, None, 16),
+    (7, 3, 700, 32, 8, 128, 16, True, None, 0),
+    (8, 3, 700, 32, 8, 128, 16, True, None, 128),
+    (9, 4, 333, 8, 8, 128, 3, False, 200, 0),
+    (10, 2, 1000, 4, 1, 128, 64, True, 300, 192),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"seed{c[0]}")
+def test_prefill_small(case):
+    seed, B, L, Hq, Hkv, d, P, causal, max_qo, fixed = case
+    w = random_prefill_workload(seed, B, L, Hq, Hkv, d, P, causal=causal, max_qo=max_qo)
+    p, _, _ = run_case(w, f"prefill seed{seed}", fixed_chunk_tokens=fixed)
+    if fixed:
+        assert p.info["num_merges"] > 0
+
+
+def test_prefill_edges_no_queries_and_empty_cache():
+    # request 0 asks nothing, request 1 has no pages (unmasked: out 0, lse -inf)
+    w = random_prefill_workload(21, 3, 80, 8, 2, 128, 16, causal=False, lens=[40, 0, 77],
+                                qo_lens=[0, 6, 77])
+    run_case(w, "no queries / empty cache")
+
+
+def test_prefill_whole_prompts_tile_boundaries():
+    # prompts whose length straddles the 64-token tiles of G = 4 and the
+    # 32-token sub-blocks and 64-token blocks of the kernel, all of them queries
+    lens = [1, 31, 32, 33, 63, 64, 65, 129, 257]
+    w = random_prefill_workload(22, len(lens), 200, 16, 4, 128, 16, causal=True, lens=lens,
+                                qo_lens=lens)
+    run_case(w, "whole prompts")
+
+
+def test_prefill_is_deterministic():
+    w = random_prefill_workload(23, 3, 600, 8, 2, 128, 16, causal=True)
+    q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    p = make_plan(w, fixed_chunk_tokens=64)
+    a = fb.prefill(q, k, v, p)
+    b = fb.prefill(q, k, v, p)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def _sample_rows(w, n, seed):
+    """(query row, head) pairs: each request's first and last query, a tile
+    boundary, and random ones."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    qo = w.qo_indptr
+    G = w.num_qo_heads // w.num_kv_heads
+    T = fb.binding.PREFILL_ROWS // G
+    for b in range(w.batch):
+        if qo[b + 1] > qo[b]:
+            rows.add((int(qo[b]), int(rng.integers(w.num_qo_heads))))
+            rows.add((int(qo[b + 1]) - 1, int(rng.integers(w.num_qo_heads))))
+            if qo[b + 1] - qo[b] > T:
+                rows.add((int(qo[b]) + T, int(rng.integers(w.num_qo_heads))))
+    while len(rows) < n:
+        rows.add((int(rng.integers(w.num_qo_tokens)), int(rng.integers(w.num_qo_heads))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("cfg", [7, 8])
+def test_prefill_full_size_sampled(cfg):
+    w = workload(cfg)
+    log(f"[case] full-size prefill config {cfg} {w.name} N={w.num_qo_tokens}")
+    q, k, v = w.make_values("cuda")
+    p = make_plan(w)
+    out, lse = fb.prefill(q, k, v, p)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    rows = _sample_rows(w, 96, cfg)
+    t0 = time.time()
+    qh = q.double().cpu().numpy()
+    kh, vh = k.double().cpu().numpy(), v.double().cpu().numpy()
+    O, LSE = oa.prefill_attention_rows(qh, kh, vh, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                       w.last_page_len, rows, w.causal, w.sm_scale)
+    r = np.array([x[0] for x in rows])
+    h = np.array([x[1] for x in rows])
+    got = out[torch.as_tensor(r), torch.as_tensor(h)].double().cpu().numpy()
+    got_l = lse[torch.as_tensor(r), torch.as_tensor(h)].double().cpu().numpy()
+    stats = compare(got, got_l, O, LSE, True, f"prefill config {cfg}")
+    log(f"[ok] config {cfg} items={p.info['num_items']} merges={p.info['num_merges']} "
+        f"rows={len(rows)} oracle {time.time() - t0:.1f}s {stats}")
