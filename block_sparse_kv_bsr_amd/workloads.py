@@ -48,7 +48,12 @@ CONFIG_NAMES = {
     # prefill / append (several query tokens per request, causal)
     7: "prefill_b16_l2048_causal",
     8: "append_b64_q128_skewed",
+    # the skewed batch over a K cache that holds keys before the rotary embedding
+    9: "skewed_b64_loguniform_32_32768_rope",
 }
+
+# Rotary embedding base of the rope workload (the Llama-3 value).
+ROPE_THETA = 500000.0
 
 # fp8 KV caches hold x / FP8_SCALE rounded to OCP E4M3 (torch's cast, round
 # to nearest even; |x / scale| <= 448 for |x| <= 7); the kernel multiplies by
@@ -78,6 +83,9 @@ class Workload:
     # dequantisation scales of an fp8 KV cache (1 otherwise)
     k_scale: float = 1.0
     v_scale: float = 1.0
+    # rotary embedding applied in the kernel (0: K is stored as used)
+    rope_theta: float = 0.0
+    rope_scale: float = 1.0
 
     @property
     def sm_scale(self) -> float:
@@ -349,6 +357,10 @@ def workload(config_id: int) -> Workload:
         return _sparse_prefix(rng, seed)
     if config_id in (7, 8):
         return prefill_workload(config_id)
+    if config_id == 9:  # the skewed batch, K stored before the rotary embedding
+        w = workload(3)
+        return dataclasses.replace(w, name=CONFIG_NAMES[9], config_id=9, value_seed=seed,
+                                   rope_theta=ROPE_THETA)
     if config_id == 6:  # the skewed batch over an fp8 KV cache
         w = workload(3)
         return dataclasses.replace(w, name=CONFIG_NAMES[6], config_id=6, dtype="fp8",

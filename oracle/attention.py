@@ -32,6 +32,14 @@ What it computes, and where that comes from:
   code and V = v_scale * code; ``dequantize_e4m3`` decodes OCP FP8 E4M3 codes
   from the format's definition.
 
+* Same explainer, JIT section: rotary position embedding (RoPE) is one of
+  the operations fused into the attention kernel. Reading (the pages name no
+  variant): the K cache holds keys before the embedding and the kernel
+  rotates q and K at their positions, in the rotate-half convention of the
+  Llama models the workloads are shaped after: dims i and i + d/2 form a
+  pair turned by the angle (position / rope_scale) * rope_theta^(-2i/d).
+  Token t of a request (0-based, listed order) sits at position t; the
+  decode query is the newest token, position L - 1.
 * Same explainer, section on where the attention bottleneck lies: prefill
   attends every token of the prompt at once (and is bound by arithmetic, not
   memory). Reading (the pages give no formula): the query tokens of a
@@ -154,6 +162,62 @@ def decode_attention_rows(q, k_pool, v_pool, kv_indptr, kv_indices, last_page_le
         K, V = gather_kv(k_pool, v_pool, toks, kv_head_of(h, G))
         o, lse = attend(np.asarray(q[b, h:h + 1, :], dtype=np.float64), K, V, sm_scale)
         O[i], LSE[i] = o[0], lse[0]
+    return O, LSE
+
+
+def rope_angles(head_dim: int, positions, theta: float = 1e4, scale: float = 1.0):
+    """Rotation angle of every dim pair at every position: array
+    [len(positions), head_dim / 2], (pos / scale) * theta^(-2i / head_dim)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * i / head_dim)
+    pos = np.asarray(positions, dtype=np.float64).reshape(-1, 1)
+    return (pos / scale) * inv_freq[None, :]
+
+
+def apply_rope(x, positions, theta: float = 1e4, scale: float = 1.0):
+    """Rotate-half rotary embedding of rows x [n, d] (row j at positions[j]):
+    with x = (x1, x2) split at d/2 and angle a, x1' = x1 cos a - x2 sin a and
+    x2' = x2 cos a + x1 sin a."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    a = rope_angles(d, positions, theta, scale)
+    c, s = np.cos(a), np.sin(a)
+    x1, x2 = x[:, :d // 2], x[:, d // 2:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=1)
+
+
+def rope_query_position(kv_len: int) -> int:
+    """The decode query is the request's newest token: position L - 1 (0 for
+    an empty request, which attends nothing anyway)."""
+    return max(kv_len - 1, 0)
+
+
+def decode_attention_rope(q, k_pool, v_pool, kv_indptr, kv_indices, last_page_len, sm_scale=None,
+                          theta: float = 1e4, scale: float = 1.0):
+    """decode_attention over a K cache that holds keys before the rotary
+    embedding: token t of request b is rotated at position t, the query at
+    position L_b - 1, then plain attention. Returns float64 O [B, H_q, d]
+    and LSE [B, H_q]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv, P = k_pool.shape[1], k_pool.shape[2]
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    O = np.zeros((B, Hq, d))
+    LSE = np.full((B, Hq), NEG_INF)
+    for b in range(B):
+        toks = request_tokens(kv_indptr, kv_indices, last_page_len, P, b)
+        L = len(toks)
+        for kvh in range(Hkv):
+            heads = [h for h in range(Hq) if kv_head_of(h, G) == kvh]
+            K, V = gather_kv(k_pool, v_pool, toks, kvh)
+            if L:
+                K = apply_rope(K, np.arange(L), theta, scale)
+            qr = apply_rope(q[b, heads, :], [rope_query_position(L)] * len(heads), theta, scale)
+            o, lse = attend(qr, K, V, sm_scale)
+            O[b, heads, :] = o
+            LSE[b, heads] = lse
     return O, LSE
 
 

@@ -73,3 +73,21 @@ def bruteforce_prefill(q, k_pool, v_pool, qo_indptr, indptr, indices, last, sm_s
                                              for w, (p, s) in zip(ws, seen)) / den
                 LSE[row][h] = top + math.log(den)
     return O, LSE
+
+
+def rope_rows_loops(rows, positions, theta, scale):
+    """Rotary embedding written as plain loops over dim pairs with math.cos
+    and math.sin: pair (i, i + d/2) of a row at position p turns by
+    (p / scale) * theta ** (-2 i / d)."""
+    out = []
+    for x, pos in zip(rows, positions):
+        d = len(x)
+        h = d // 2
+        y = [0.0] * d
+        for i in range(h):
+            ang = (pos / scale) * theta ** (-2.0 * i / d)
+            c, s = math.cos(ang), math.sin(ang)
+            y[i] = float(x[i]) * c - float(x[i + h]) * s
+            y[i + h] = float(x[i + h]) * c + float(x[i]) * s
+        out.append(y)
+    return out

@@ -14,7 +14,7 @@ import numpy as np
 import torch
 
 from block_sparse_kv_bsr_amd.workloads import random_prefill_workload, random_workload
-from tests.bruteforce import bruteforce_decode, bruteforce_prefill
+from tests.bruteforce import bruteforce_decode, bruteforce_prefill, rope_rows_loops
 
 
 def f64_inputs(w):
@@ -334,3 +334,73 @@ def pin_prefill_sdpa(mod):
 
 PREFILL_PINS = [pin_prefill_bruteforce, pin_prefill_is_decode_per_row, pin_prefill_causal_prefix,
                 pin_prefill_sdpa]
+
+
+# --------------------------------------------------------------------- rope
+def pin_rope_closed_forms(mod):
+    """d = 2 is a plane rotation by pos / scale radians (theta^0 = 1); for
+    d = 4 the second pair turns by pos / (scale * sqrt(theta)); position 0
+    is the identity; the embedding keeps every row's norm."""
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((6, 2))
+    pos = np.array([0, 1, 3, 17, 1000, 32767])
+    for scale in (1.0, 4.0):
+        y = mod.apply_rope(x, pos, 1e4, scale)
+        a = pos / scale
+        want = np.stack([x[:, 0] * np.cos(a) - x[:, 1] * np.sin(a),
+                         x[:, 1] * np.cos(a) + x[:, 0] * np.sin(a)], axis=1)
+        assert np.allclose(y, want, atol=1e-12, rtol=0)
+    x4 = rng.standard_normal((3, 4))
+    p4 = np.array([5, 250, 9000])
+    y4 = mod.apply_rope(x4, p4, 1e4, 1.0)
+    a1 = p4 / 100.0  # 1e4 ** (-2 * 1 / 4) = 1 / 100
+    assert np.allclose(y4[:, 1], x4[:, 1] * np.cos(a1) - x4[:, 3] * np.sin(a1), atol=1e-12, rtol=0)
+    assert np.allclose(y4[:, 3], x4[:, 3] * np.cos(a1) + x4[:, 1] * np.sin(a1), atol=1e-12, rtol=0)
+    x8 = rng.standard_normal((4, 128))
+    assert np.array_equal(mod.apply_rope(x8, [0, 0, 0, 0], 1e4, 1.0), x8)
+    y8 = mod.apply_rope(x8, [1, 77, 4096, 131071], 5e5, 1.0)
+    assert np.allclose(np.linalg.norm(y8, axis=1), np.linalg.norm(x8, axis=1), atol=1e-12, rtol=0)
+
+
+def pin_rope_relative(mod):
+    """The score of a rotated query and key depends on the positions only
+    through their difference."""
+    rng = np.random.default_rng(72)
+    q = rng.standard_normal((1, 64))
+    k = rng.standard_normal((1, 64))
+    for m, n, c in ((10, 3, 100), (0, 500, 7), (2047, 2047, 30000)):
+        s1 = (mod.apply_rope(q, [m]) @ mod.apply_rope(k, [n]).T)[0, 0]
+        s2 = (mod.apply_rope(q, [m + c]) @ mod.apply_rope(k, [n + c]).T)[0, 0]
+        assert abs(s1 - s2) <= 1e-10, (m, n, c)
+    # and it does change with the difference
+    s3 = (mod.apply_rope(q, [10]) @ mod.apply_rope(k, [4]).T)[0, 0]
+    s4 = (mod.apply_rope(q, [10]) @ mod.apply_rope(k, [3]).T)[0, 0]
+    assert abs(s3 - s4) > 1e-3
+
+
+def pin_rope_decode(mod):
+    """decode_attention_rope equals the brute-force decode over a cache whose
+    rows were rotated beforehand, by plain loops, at their token index, and a
+    query rotated at position L - 1."""
+    for seed, theta, scale in ((73, 1e4, 1.0), (74, 5e5, 2.0)):
+        w = random_workload(seed, 3, 40, 4, 2, 8, 4, "f32", lens=[37, 1, 20])
+        q, k, v = f64_inputs(w)
+        O, LSE = mod.decode_attention_rope(q, k, v, w.kv_indptr, w.kv_indices, w.last_page_len,
+                                           w.sm_scale, theta, scale)
+        kr, qr = k.copy(), q.copy()
+        P = w.page_size
+        for b in range(w.batch):
+            pages = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+            L = int(w.kv_lens()[b])
+            for t in range(L):
+                pg, sl = int(pages[t // P]), t % P
+                kr[pg, :, sl, :] = np.array(rope_rows_loops(k[pg, :, sl, :], [t] * w.num_kv_heads,
+                                                            theta, scale))
+            qr[b] = np.array(rope_rows_loops(q[b], [L - 1] * w.num_qo_heads, theta, scale))
+        Ob, LSEb = bruteforce_decode(qr, kr, v, w.kv_indptr, w.kv_indices, w.last_page_len,
+                                     w.sm_scale)
+        assert np.max(np.abs(O - np.array(Ob))) <= 1e-12, seed
+        assert np.max(np.abs(LSE - np.array(LSEb))) <= 1e-12, seed
+
+
+ROPE_PINS = [pin_rope_closed_forms, pin_rope_relative, pin_rope_decode]

@@ -6,7 +6,7 @@ import oracle.attention as oa
 from tests import oracle_pins as pins
 
 
-@pytest.mark.parametrize("pin", pins.ALL_PINS + pins.PREFILL_PINS + [pins.pin_bf16],
+@pytest.mark.parametrize("pin", pins.ALL_PINS + pins.PREFILL_PINS + pins.ROPE_PINS + [pins.pin_bf16],
                          ids=lambda f: f.__name__)
 def test_pin(pin):
     pin(oa)
@@ -144,3 +144,52 @@ def test_e4m3_decoder_matches_the_format_and_torch():
     ok = ~np.isnan(ref)
     assert np.array_equal(got[ok], ref[ok])
     assert d(codes, 0.25)[0x38] == 0.25
+
+
+_orig_apply_rope = oa.apply_rope
+_orig_rope_angles = oa.rope_angles
+
+
+def _rope_interleaved(x, positions, theta=1e4, scale=1.0):
+    # pairs (2i, 2i+1) instead of (i, i + d/2)
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+    inv = np.argsort(perm)
+    return _orig_apply_rope(x[:, perm], positions, theta, scale)[:, inv]
+
+
+def _rope_angles_no_two(head_dim, positions, theta=1e4, scale=1.0):
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    pos = np.asarray(positions, dtype=np.float64).reshape(-1, 1)
+    return (pos / scale) * (theta ** (-i / head_dim))[None, :]
+
+
+def _rope_angles_times_scale(head_dim, positions, theta=1e4, scale=1.0):
+    return _orig_rope_angles(head_dim, positions, theta, 1.0 / scale)
+
+
+def _rope_backwards(x, positions, theta=1e4, scale=1.0):
+    return _orig_apply_rope(x, -np.asarray(positions, dtype=np.float64), theta, scale)
+
+
+ROPE_MUTATIONS = {
+    "rope_pairs_interleaved": ("apply_rope", _rope_interleaved),
+    "rope_frequency_exponent": ("rope_angles", _rope_angles_no_two),
+    "rope_scale_multiplies": ("rope_angles", _rope_angles_times_scale),
+    "rope_turns_backwards": ("apply_rope", _rope_backwards),
+    "rope_query_at_L": ("rope_query_position", lambda L: L),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROPE_MUTATIONS))
+def test_rope_oracle_mutations_are_caught(name, monkeypatch):
+    attr, fn = ROPE_MUTATIONS[name]
+    monkeypatch.setattr(oa, attr, fn)
+    caught = []
+    for pin in pins.ROPE_PINS:
+        try:
+            pin(oa)
+        except (AssertionError, ValueError, IndexError, TypeError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake {name} passed every rope pin"
