@@ -127,7 +127,11 @@ def cpu_baseline(w, q, k, v, min_seconds=10.0, max_passes=3):
     times = []
     while len(times) < max_passes and sum(times) < min_seconds:
         t0 = time.perf_counter()
-        oa.decode_attention(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len, w.sm_scale)
+        if w.rope_theta:
+            oa.decode_attention_rope(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len,
+                                     w.sm_scale, w.rope_theta, w.rope_scale)
+        else:
+            oa.decode_attention(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len, w.sm_scale)
         times.append(time.perf_counter() - t0)
     per = statistics.median(times)
     return {"value": w.algorithmic_bytes() / per / 1e9, "unit": "GB/s", "cores": int(threads),
@@ -342,7 +346,8 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record()
-        fb.decode(q, k, v, p, out=out, lse=lse, workspace=ws, k_scale=w.k_scale, v_scale=w.v_scale)
+        fb.decode(q, k, v, p, out=out, lse=lse, workspace=ws, k_scale=w.k_scale, v_scale=w.v_scale,
+                  rope_theta=w.rope_theta or None, rope_scale=w.rope_scale)
         if ev:
             ev[1].record()
 
@@ -378,7 +383,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "f32": "f32", "fp8": "fp8_e4m3 K/V, bf16 q/out"}[w.dtype],
+        "dtype": {"bf16": "bf16", "f32": "f32", "fp8": "fp8_e4m3 K/V, bf16 q/out"}[w.dtype]
+                 + (", rotary embedding applied to K in the kernel" if w.rope_theta else ""),
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_qo_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,

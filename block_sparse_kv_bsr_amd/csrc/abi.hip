@@ -152,9 +152,14 @@ fi_status check_inputs(const fi_plan* plan, const void* q, const void* k_pages,
   return FI_OK;
 }
 
+struct Rope {
+  bool on = false;
+  float theta = 0.f, scale = 0.f;
+};
+
 fi_status launch_run(const fi_plan* plan, const void* q, const void* k_pages,
                      const void* v_pages, float k_scale, float v_scale, void* out, float* lse,
-                     float sm_scale, void* workspace, hipStream_t s) {
+                     float sm_scale, void* workspace, hipStream_t s, Rope rope = Rope()) {
   if (!(sm_scale > 0.f)) sm_scale = 1.0f / std::sqrt((float)plan->head_dim);
   char* ws = static_cast<char*>(workspace);
   fi::DecodeArgs d{};
@@ -180,6 +185,9 @@ fi_status launch_run(const fi_plan* plan, const void* q, const void* k_pages,
   d.v_scale = v_scale;
   d.stream_kv = plan->shared_pages == 0;
   d.sm_scale = sm_scale;
+  d.rope = rope.on;
+  d.rope_theta = rope.theta;
+  d.rope_scale = rope.scale;
   if (plan->num_pitems() > 0) {
     // shared prefixes first: their partials must be in place before the
     // decode kernel's merge trees read them
@@ -224,6 +232,33 @@ fi_status fi_decode_run_scaled(const fi_plan* plan, const void* q, const void* k
   if (st != FI_OK) return st;
   return launch_run(plan, q, k_pages, v_pages, k_scale, v_scale, out, lse, sm_scale, workspace,
                     static_cast<hipStream_t>(stream));
+}
+
+fi_status fi_decode_run_rope(const fi_plan* plan, const void* q, const void* k_pages,
+                             const void* v_pages, float rope_theta, float rope_scale, void* out,
+                             float* lse, float sm_scale, void* workspace, size_t workspace_bytes,
+                             fi_stream_t stream) {
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->dtype != FI_DTYPE_BF16 || plan->head_dim != 128)
+    return fail(FI_ERR_UNSUPPORTED, "the rotary embedding is built for bf16 plans with head_dim 128");
+  if (plan->num_pitems() > 0)
+    return fail(FI_ERR_UNSUPPORTED,
+                "the rotary embedding does not run with shared-prefix items; plan with cascade = -1");
+  if (std::isnan(rope_theta) || std::isinf(rope_theta) || std::isnan(rope_scale) ||
+      std::isinf(rope_scale))
+    return fail(FI_ERR_INVALID_ARG, "rope_theta and rope_scale must be finite");
+  Rope r;
+  r.on = true;
+  r.theta = rope_theta > 0.f ? rope_theta : 10000.f;
+  r.scale = rope_scale > 0.f ? rope_scale : 1.f;
+  if (!(r.theta > 1.f)) return fail(FI_ERR_INVALID_ARG, "rope_theta must exceed 1");
+  if (plan->batch == 0) return FI_OK;
+  fi_status st = check_inputs(plan, q, k_pages, v_pages);
+  if (st != FI_OK) return st;
+  st = check_run(plan, out, lse, workspace, workspace_bytes);
+  if (st != FI_OK) return st;
+  return launch_run(plan, q, k_pages, v_pages, 1.f, 1.f, out, lse, sm_scale, workspace,
+                    static_cast<hipStream_t>(stream), r);
 }
 
 fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,

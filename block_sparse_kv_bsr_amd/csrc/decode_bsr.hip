@@ -42,6 +42,7 @@
 // tree folds inside this same kernel (finish_split).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 
 #include "fi_bsr.h"
@@ -82,7 +83,19 @@ struct DecodeParams {
   int32_t step_slots;
   float scale_log2;     // sm_scale * k_scale * log2(e)
   float v_scale;        // multiplies the output (V dequantisation)
+  double rope_log2_theta;  // rotary embedding: log2(rope_theta)
+  double rope_rev;         // 1 / (2 pi rope_scale): revolutions per radian, positions scaled
 };
+
+// Sine and cosine of the rotary angle of a dim pair at position `pos`. The
+// pair's frequency is a 64-bit binary fraction of a revolution per position,
+// so pos * freq mod 1 is exact integer arithmetic (no loss of phase at large
+// positions); its top 32 bits give the angle for sincospif.
+__device__ __forceinline__ void rope_sincos(uint64_t freq, int pos, float& c, float& s) {
+  const uint64_t ph = (uint64_t)(uint32_t)pos * freq;
+  const float rev = (float)(uint32_t)(ph >> 32) * 0x1p-32f;
+  sincospif(2.f * rev, &s, &c);
+}
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
@@ -397,7 +410,7 @@ __device__ void finish_split(const DecodeParams& p, int node, int lane, float* s
 // from LDS (16*L), softmax state and ~48 for addressing and temporaries.
 // LDS per wave: kRing stages of 2*L KiB plus the page-id window. Waves per SIMD:
 // as many as both budgets allow, at most 3.
-template <int kKv, int D, int G, bool kStream>
+template <int kKv, int D, int G, bool kStream, bool kRope = false>
 struct Tune {
   using R = Row<kKv, D>;
   // An fp8 stage holds half the bytes of a bf16 one and its waves spend less
@@ -405,16 +418,19 @@ struct Tune {
   // fits 2 waves per SIMD in LDS) measured 17% faster than 4 on the skewed
   // batch.
   static constexpr int kRing = kKv == 1 ? 8 : (kStream ? 2 : 4);
-  static constexpr int kRegs = G * R::kElems + G * R::kWords + 16 * R::kLoads + 2 * G + 48;
+  // the rotary embedding keeps q in fp32 (G * kElems) and 4 x 8 rotation terms
+  static constexpr int kRegs = G * R::kElems + (kRope ? G * R::kElems + 32 : G * R::kWords) +
+                               16 * R::kLoads + 2 * G + 48;
   static constexpr int kByRegs = kRegs <= 168 ? 3 : (kRegs <= 240 ? 2 : 1);
   static constexpr int kLdsPerWave = kRing * 2 * R::kLoads * 1024 + kIdWindow * 4;
   static constexpr int kByLds = (160 * 1024) / (4 * kLdsPerWave);
   static constexpr int kWaves = kByRegs < kByLds ? kByRegs : (kByLds >= 1 ? kByLds : 1);
 };
 
-template <int kKv, int D, int G, int kRing, int kWaves, bool kStream, bool kUniform>
+template <int kKv, int D, int G, int kRing, int kWaves, bool kStream, bool kUniform, bool kRope>
 __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) {
   using R = Row<kKv, D>;
+  static_assert(!kRope || (kKv == 2 && D == 128), "the rotary embedding is built for bf16, d 128");
   constexpr int L = R::kLoads;
   constexpr int NW = R::kWords;
   constexpr int NE = R::kElems;
@@ -484,6 +500,41 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
         qw[h][w0 + 1] = v.y;
         qw[h][w0 + 2] = v.z;
         qw[h][w0 + 3] = v.w;
+      }
+    }
+  }
+
+  // ---- rotary embedding (K stored before it): lane `sub` holds dims
+  // 8 sub + e and 64 + 8 sub + e (e < 8) of q and of every K row, which are
+  // exactly the rotate-half pairs i = 8 sub + e. Pair i's frequency, as a
+  // 64-bit fraction of a revolution per position, goes to LDS (lane i
+  // computes it in double precision); q turns at the query position here,
+  // K rows as they are read (consume).
+  __shared__ uint64_t s_freq[kRope ? 64 : 1];
+  float qf[kRope ? G : 1][16];
+  float rc[8], rs[8], dc[8], ds[8];  // this lane's current and per-step rotation
+  int rope_step = 0;
+  int rope_pos0 = 0;
+  if constexpr (kRope) {
+    double g = exp2(-(2.0 * lane / D) * p.rope_log2_theta) * p.rope_rev;
+    g -= floor(g);
+    s_freq[lane] = (uint64_t)ldexp(g, 64);
+    __syncthreads();
+    const int qpos = it[FI_ITEM_Q_POS];
+    rope_pos0 = it[FI_ITEM_KV_POS] + tg;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint64_t f = s_freq[8 * sub + e];
+      float cq, sq;
+      rope_sincos(f, qpos, cq, sq);
+      rope_sincos(f, 8, dc[e], ds[e]);  // a step advances 8 positions
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const uint32_t w1 = qw[h][e >> 1], w2 = qw[h][4 + (e >> 1)];
+        const float x1 = (e & 1) ? bf16_hi(w1) : bf16_lo(w1);
+        const float x2 = (e & 1) ? bf16_hi(w2) : bf16_lo(w2);
+        qf[h][e] = x1 * cq - x2 * sq;
+        qf[h][8 + e] = x2 * cq + x1 * sq;
       }
     }
   }
@@ -601,6 +652,37 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
 
   auto consume = [&](const u32x4_t (&kr)[L], u32x4_t (&vr)[L], bool masked, bool valid) {
     float s[G];
+    if constexpr (kRope) {
+      // this lane's token of the step sits at rope_pos0 + 8 * step; the
+      // rotation is recomputed exactly every 32 steps and advanced by one
+      // step's rotation in between (error ~ 32 fp32 roundings)
+      if ((rope_step & 31) == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rope_sincos(s_freq[8 * sub + e], rope_pos0 + 8 * rope_step, rc[e], rs[e]);
+      }
+      float d[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) d[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w1 = word(kr[0], e >> 1), w2 = word(kr[1], e >> 1);
+        const float x1 = (e & 1) ? bf16_hi(w1) : bf16_lo(w1);
+        const float x2 = (e & 1) ? bf16_hi(w2) : bf16_lo(w2);
+        const float k1 = x1 * rc[e] - x2 * rs[e];
+        const float k2 = x2 * rc[e] + x1 * rs[e];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          d[h] = __builtin_fmaf(k1, qf[h][e], d[h]);
+          d[h] = __builtin_fmaf(k2, qf[h][8 + e], d[h]);
+        }
+        const float c2 = rc[e] * dc[e] - rs[e] * ds[e];
+        rs[e] = rs[e] * dc[e] + rc[e] * ds[e];
+        rc[e] = c2;
+      }
+      ++rope_step;
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[h] = sum8(d[h]) * p.scale_log2;
+    } else {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float d = 0.f;
@@ -629,6 +711,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
       }
       s[h] = sum8(d) * p.scale_log2;
     }
+    }  // kRope
     if (masked) {
 #pragma unroll
       for (int h = 0; h < G; ++h) s[h] = valid ? s[h] : -INFINITY;
@@ -884,32 +967,32 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   }
 }
 
-template <int kKv, int D, int G, bool kStream>
+template <int kKv, int D, int G, bool kStream, bool kRope>
 hipError_t launch_variant(const DecodeParams& prm, int64_t num_items, hipStream_t stream) {
-  using T = Tune<kKv, D, G, kStream>;
+  using T = Tune<kKv, D, G, kStream, kRope>;
   if (prm.page_size % 8 == 0)
-    hipLaunchKernelGGL((decode_bsr_kernel<kKv, D, G, T::kRing, T::kWaves, kStream, true>),
+    hipLaunchKernelGGL((decode_bsr_kernel<kKv, D, G, T::kRing, T::kWaves, kStream, true, kRope>),
                        dim3((uint32_t)num_items), dim3(64), 0, stream, prm);
   else
-    hipLaunchKernelGGL((decode_bsr_kernel<kKv, D, G, T::kRing, T::kWaves, kStream, false>),
+    hipLaunchKernelGGL((decode_bsr_kernel<kKv, D, G, T::kRing, T::kWaves, kStream, false, kRope>),
                        dim3((uint32_t)num_items), dim3(64), 0, stream, prm);
   return hipGetLastError();
 }
 
-template <int kKv, int D, int G>
+template <int kKv, int D, int G, bool kRope>
 hipError_t launch_typed(const DecodeParams& prm, int64_t num_items, bool stream_kv,
                         hipStream_t stream) {
-  return stream_kv ? launch_variant<kKv, D, G, true>(prm, num_items, stream)
-                   : launch_variant<kKv, D, G, false>(prm, num_items, stream);
+  return stream_kv ? launch_variant<kKv, D, G, true, kRope>(prm, num_items, stream)
+                   : launch_variant<kKv, D, G, false, kRope>(prm, num_items, stream);
 }
 
-template <int kKv, int D>
+template <int kKv, int D, bool kRope = false>
 hipError_t launch_group(const DecodeParams& prm, int64_t n, int G, bool st, hipStream_t s) {
   switch (G) {
-    case 1: return launch_typed<kKv, D, 1>(prm, n, st, s);
-    case 2: return launch_typed<kKv, D, 2>(prm, n, st, s);
-    case 4: return launch_typed<kKv, D, 4>(prm, n, st, s);
-    case 8: return launch_typed<kKv, D, 8>(prm, n, st, s);
+    case 1: return launch_typed<kKv, D, 1, kRope>(prm, n, st, s);
+    case 2: return launch_typed<kKv, D, 2, kRope>(prm, n, st, s);
+    case 4: return launch_typed<kKv, D, 4, kRope>(prm, n, st, s);
+    case 8: return launch_typed<kKv, D, 8, kRope>(prm, n, st, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -940,6 +1023,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   // the K dequantisation scale multiplies every score, the V one the output
   prm.scale_log2 = a.sm_scale * a.k_scale * kLog2e;
   prm.v_scale = a.v_scale;
+  prm.rope_log2_theta = a.rope ? std::log2((double)a.rope_theta) : 0.0;
+  prm.rope_rev = a.rope ? 1.0 / (2.0 * M_PI * (double)a.rope_scale) : 0.0;
+  if (a.rope) {
+    if (a.kv_bytes == 2 && a.head_dim == 128)
+      return launch_group<2, 128, true>(prm, a.num_items, a.group, a.stream_kv, stream);
+    return hipErrorInvalidValue;
+  }
   if (a.kv_bytes == 2) {
     if (a.head_dim == 128) return launch_group<2, 128>(prm, a.num_items, a.group, a.stream_kv, stream);
     if (a.head_dim == 64) return launch_group<2, 64>(prm, a.num_items, a.group, a.stream_kv, stream);

@@ -25,6 +25,8 @@ struct DecodeArgs {
   bool stream_kv;           // nontemporal K/V loads (no page listed twice)
   float sm_scale;
   float k_scale, v_scale;   // K/V dequantisation scales (1 unless fp8)
+  bool rope;                // K (and q) stored before the rotary embedding
+  float rope_theta, rope_scale;
 };
 
 struct PrefixArgs {

@@ -372,6 +372,8 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
           it.f[FI_ITEM_NUM_PAGES] = (int32_t)np;
           it.f[FI_ITEM_FIRST_PAGE] = kv_indices[kv_indptr[b] + pre + page0];
           it.f[FI_ITEM_MERGE_NODE] = leaf_node[cpre + c];
+          it.f[FI_ITEM_KV_POS] = (int32_t)((pre + page0) * page_size);
+          it.f[FI_ITEM_Q_POS] = (int32_t)(ntok[b] - 1);
           items.push_back(it);
           page0 += np;
         }

@@ -140,6 +140,8 @@ enum {
                              kv_indices[FI_ITEM_PAGE_BEGIN], so the first
                              loads need no page-table read); 0 if no pages */
   FI_ITEM_MERGE_NODE = 8, /* merge node the partial reports to; -1 if none */
+  FI_ITEM_KV_POS = 9,     /* position in the request of the chunk's first token */
+  FI_ITEM_Q_POS = 10,     /* position of the request's query: its last token */
   FI_ITEM_STRIDE = 16     /* int32 per item */
 };
 
@@ -292,6 +294,24 @@ fi_status fi_decode_run_scaled(const fi_plan* plan, const void* q, const void* k
                                const void* v_pages, float k_scale, float v_scale, void* out,
                                float* lse, float sm_scale, void* workspace,
                                size_t workspace_bytes, fi_stream_t stream);
+
+/*
+ * fi_decode_run for a K cache that holds keys before the rotary position
+ * embedding, which the kernel applies while it reads them (explainer, JIT
+ * section: RoPE is among the operations fused into the attention kernel).
+ * Rotate-half convention: dims i and i + head_dim/2 form a pair turned by
+ * the angle (pos / rope_scale) * rope_theta^(-2i / head_dim); token t of a
+ * request (0-based, listed order) is at position t, the query at position
+ * L_b - 1 (it is the request's newest token, whose K is already cached).
+ * q is given before the embedding too. bf16 plans with head_dim 128 and no
+ * shared-prefix items (create the plan with opts.cascade = -1); else
+ * FI_ERR_UNSUPPORTED. rope_theta <= 0 selects 10000, rope_scale <= 0
+ * selects 1. Other arguments as fi_decode_run.
+ */
+fi_status fi_decode_run_rope(const fi_plan* plan, const void* q, const void* k_pages,
+                             const void* v_pages, float rope_theta, float rope_scale, void* out,
+                             float* lse, float sm_scale, void* workspace, size_t workspace_bytes,
+                             fi_stream_t stream);
 
 /*
  * Merge two attention states over disjoint token sets (the closed form of

@@ -1,0 +1,90 @@
+"""GPU parity of decode with the rotary embedding fused into the K gather
+(fi_decode_run_rope) against the float64 oracle's decode_attention_rope.
+
+The kernel carries each lane's rotation from step to step and recomputes it
+exactly every 32 steps (256 tokens), so the cases run past several
+recomputations, cut requests into chunks that start at nonzero positions,
+and cover every GQA group, page sizes that do and do not divide the 8-token
+step, and both rotary bases.
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_kv_bsr_amd as fb
+import oracle.attention as oa
+from block_sparse_kv_bsr_amd.workloads import random_workload, workload
+from tests.parity import compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    fb.lib()
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def run_rope(w, theta, scale, what, device_values=False, **opts):
+    log(f"[case] {what} B={w.batch} Hq={w.num_qo_heads} Hkv={w.num_kv_heads} P={w.page_size} "
+        f"theta={theta} scale={scale} opts={opts}")
+    if device_values:
+        q, k, v = w.make_values("cuda")
+    else:
+        q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, w.num_qo_heads, w.num_kv_heads,
+                w.head_dim, w.page_size, w.num_pool_pages, w.dtype, cascade=-1, **opts)
+    out, lse = fb.decode(q, k, v, p, rope_theta=theta, rope_scale=scale)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    qh, kh, vh = (t.double().cpu().numpy() for t in (q, k, v))
+    O, LSE = oa.decode_attention_rope(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len,
+                                      w.sm_scale, theta, scale)
+    stats = compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE, True, what)
+    log(f"[ok] {what} items={p.info['num_items']} chunk={p.info['chunk_pages']}p "
+        f"oracle {time.time() - t0:.1f}s {stats}")
+    return p
+
+
+CASES = [
+    # seed, B, maxL, Hq, Hkv, P, theta, scale, fixed_chunk_tokens
+    (81, 4, 3000, 32, 8, 16, 1e4, 1.0, 0),
+    (82, 3, 5000, 8, 8, 16, 5e5, 1.0, 512),
+    (83, 4, 2500, 16, 8, 64, 1e4, 4.0, 0),
+    (84, 5, 700, 16, 2, 12, 5e5, 1.0, 96),
+    (85, 3, 1200, 8, 1, 1, 1e4, 1.0, 0),
+    (86, 4, 900, 64, 8, 16, 1e4, 1.0, 160),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"seed{c[0]}")
+def test_rope_small(case):
+    seed, B, L, Hq, Hkv, P, theta, scale, fixed = case
+    w = random_workload(seed, B, L, Hq, Hkv, 128, P, "bf16")
+    p = run_rope(w, theta, scale, f"rope{seed}", fixed_chunk_tokens=fixed)
+    if fixed:
+        assert p.info["max_chunks_per_request"] > 1
+
+
+def test_rope_empty_and_one_token_requests():
+    w = random_workload(87, 5, 50, 32, 8, 128, 16, "bf16", lens=[0, 1, 9, 0, 300])
+    run_rope(w, 1e4, 1.0, "rope empty/one-token")
+
+
+def test_rope_skewed_batch_full_size():
+    w = workload(9)
+    run_rope(w, w.rope_theta, w.rope_scale, "config9-rope", device_values=True)
+
+
+def test_rope_rejects_what_is_not_built():
+    w = random_workload(88, 2, 40, 8, 2, 64, 16, "bf16")
+    q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, 8, 2, 64, 16, w.num_pool_pages, "bf16")
+    with pytest.raises(fb.FiError, match="head_dim 128"):
+        fb.decode(q, k, v, p, rope_theta=1e4)
