@@ -26,8 +26,12 @@
 // owns query rows 32(w%4) .. +31 and the tokens 32(w/4) .. +31 of every
 // 64-token block; the two partial softmax states of a row are merged through
 // LDS at the end. Prefill: wave w owns rows 32w .. +31 and both 32-token
-// halves of every block, one after the other, so a K/V block serves 256 rows
-// and the matrix work of one half overlaps the softmax of the other. K/V blocks stream into
+// halves of every block, so a K/V block serves 256 rows. Per block a wave
+// reads its K fragments and issues the S^T products, then the loads of a
+// later block, takes one online-softmax step over its tokens (the running
+// max moves at most once per block), reads all its V^T fragments and runs
+// one branch-free stretch of exponentials, P splits and PV products that the
+// scheduler interleaves. K/V blocks stream into
 // an LDS ring of kStages stages with gfx950's direct-to-LDS loads (no
 // staging registers), one barrier per block. Per 32 tokens of a wave:
 //   S^T[token, row] = K . Q^T     v_mfma_f32_32x32x16_bf16, D/16 steps
@@ -50,6 +54,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "fi_bsr.h"
 #include "kernels.h"
@@ -110,6 +115,55 @@ struct Geom {
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) { return (uint32_t)(uintptr_t)p; }
 
+// LDS reads at a lane address plus a compile-time immediate offset (the
+// instruction's 16-bit offset field), as inline asm: the compiler cannot tell
+// which ring stage a direct-to-LDS load writes, and would otherwise wait for
+// every load in flight before each read. The waits are explicit instead.
+template <int OFF>
+__device__ __forceinline__ u32x4_t lds_b128(uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF) : "memory");
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2_t lds_tr_b64(uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF) : "memory");
+  return r;
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1, so that I can
+// appear in template arguments (immediate offsets) inside f.
+template <int I, int N>
+struct StaticFor {
+  template <class F>
+  __device__ __forceinline__ static void run(F& f) {
+    if constexpr (I < N) {
+      f(std::integral_constant<int, I>{});
+      StaticFor<I + 1, N>::run(f);
+    }
+  }
+};
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  StaticFor<0, N>::run(f);
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to a packed bf16 pair (nearest even), and the pair's
+// rounding errors rounded to a second pair: hi + lo is within ~2^-16 of the
+// inputs.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const f32x2_t f = {a, b};
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+  const f32x2_t r = {a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u)};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+}
+
 // s_waitcnt vmcnt(n), leaving the other counters unconstrained.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -155,7 +209,9 @@ __device__ __forceinline__ float sum_with_partner32(float x) {
 // waves of a row group take the two 32-token halves of every block and merge
 // their states at the end. Prefill: 8 row groups (256 rows); each wave takes
 // both halves of every block itself, as two sub-blocks whose products are
-// independent, so one sub-block's matrix work overlaps the other's softmax.
+// independent accumulation chains; one softmax step covers the wave's whole
+// block, and the exponentials of one 16-token step overlap the products of
+// the previous one.
 template <bool kPrefill>
 struct Roles {
   static constexpr bool kSplit = !kPrefill;
@@ -299,9 +355,28 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s, s);
 
-  // addresses that depend only on the lane
+  // LDS byte offsets that depend only on the lane. K fragment q of token row
+  // kt = 32 (wtok + sb) + lane % 32 sits at kt * kRB + piece * 16 with the
+  // piece swizzled by kt % kPieces = lane % kPieces (32 rows are a whole
+  // number of swizzle periods), so the sub-block moves it by a constant. V
+  // fragment t of the transposed read (input role: token 4 (g16/2) + v_k of
+  // a 16-token step, columns 32t + 16 (g16%2) + 4 v_p .. +3) is swizzled by
+  // tok % 4 = v_k, so sub-block, step and run move it by constants too: those
+  // go into the reads' immediate offsets.
   const int g16 = lane >> 4, L16 = lane & 15;
   const int v_k = L16 >> 2, v_p = L16 & 3;  // this lane's input role in a transposed read
+  uint32_t kb[D / 16], vb[D / 32];
+  {
+    const int kt = 32 * wtok + (lane & 31);
+#pragma unroll
+    for (int q = 0; q < D / 16; ++q) kb[q] = kt * kRB + (((2 * q + half) ^ Gm::swz_k(kt)) * 16);
+    const int vt = 32 * wtok + 4 * (g16 >> 1) + v_k;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      const int d = 32 * t + 16 * (g16 & 1) + 4 * v_p;
+      vb[t] = vt * kRB + (((d >> 3) ^ Gm::swz_v(vt)) * 16) + (d & 7) * 2;
+    }
+  }
   // Scores stay unscaled; exp2(c * s - c * m) is one fma and an exp. The
   // running max m is raised only when a sub-block's max passes it by more
   // than kMargin in log2 units (weights stay <= 2^kMargin), so the
@@ -317,111 +392,118 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
     // every wave's loads of block j have landed, and every wave is done
     // reading block j-1, whose stage is refilled next
     __builtin_amdgcn_s_barrier();
-    issue(j + NS - 1, (j + NS - 1) % NS);
 
-    const char* kst = s_ring[st][0];
-    const char* vst = s_ring[st][1];
-    // ---- S^T = K . Q^T of every sub-block first (independent chains)
+    const uint32_t kst = lds_u32(s_ring[st][0]);
+    const uint32_t vst = lds_u32(s_ring[st][1]);
+    // ---- S^T = K . Q^T of every sub-block (independent chains)
     f32x16_t sc[R::kSub];
-#pragma unroll
-    for (int sb = 0; sb < R::kSub; ++sb) {
-      const int kt = 32 * (wtok + sb) + (lane & 31);  // K row = token of the S^T tile
+    static_for<R::kSub>([&](auto SB) {
+      constexpr int sb = decltype(SB)::value;
       u32x4_t kv[D / 16];
 #pragma unroll
-      for (int q = 0; q < D / 16; ++q) {
-        const uint32_t a = lds_u32(kst + kt * kRB + (((2 * q + half) ^ Gm::swz_k(kt)) * 16));
-        asm volatile("ds_read_b128 %0, %1" : "=v"(kv[q]) : "v"(a) : "memory");
-      }
+      for (int q = 0; q < D / 16; ++q) kv[q] = lds_b128<32 * sb * kRB>(kst + kb[q]);
       lgkm_wait_tied<D / 16>(kv);
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[sb][r] = 0.f;
 #pragma unroll
       for (int q = 0; q < D / 16; ++q)
         sc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv[q]), qf[q], sc[sb], 0, 0, 0);
-    }
+    });
+    // the loads of a later block go out while the products run
+    issue(j + NS - 1, (j + NS - 1) % NS);
 
+    // ---- online softmax over the wave's tokens of the block; element r of
+    // sub-block sb holds token 32 (wtok + sb) + 4*half + 8*(r/4) + r%4
+    const int tok0 = j * kBlock + 32 * wtok;
+    if (__builtin_amdgcn_ballot_w64(tok0 + 32 * R::kSub > lim)) {  // some row stops in here
 #pragma unroll
-    for (int sb = 0; sb < R::kSub; ++sb) {
-      f32x16_t& sv = sc[sb];
-      // ---- online softmax; element r holds token m = 4*half + 8*(r/4) + r%4
-      const int tok0 = j * kBlock + 32 * (wtok + sb);
-      if (__builtin_amdgcn_ballot_w64(tok0 + 32 > lim)) {  // some row stops in here
+      for (int sb = 0; sb < R::kSub; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = 4 * half + 8 * (r >> 2) + (r & 3);
-          if (tok0 + m >= lim) sv[r] = -INFINITY;
+          const int m = 32 * sb + 4 * half + 8 * (r >> 2) + (r & 3);
+          if (tok0 + m >= lim) sc[sb][r] = -INFINITY;
         }
+    }
+    float mb = sc[0][0];
+#pragma unroll
+    for (int sb = 0; sb < R::kSub; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mb = fmaxf(mb, sc[sb][r]);
+    mb = max_with_partner32(mb);  // -inf if the row attends none of these tokens
+    const bool up = mb > m_run + margin;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float alpha = up ? __builtin_amdgcn_exp2f((m_run - mb) * c) : 1.f;  // 0 at first
+      l_run *= alpha;
+      if (j > 0) {  // the accumulators are still zero on the first block
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
       }
-      float mb = sv[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mb = fmaxf(mb, sv[r]);
-      mb = max_with_partner32(mb);  // -inf if the row attends none of these tokens
-      const bool up = mb > m_run + margin;
-      if (__builtin_amdgcn_ballot_w64(up)) {
-        const float alpha = up ? __builtin_amdgcn_exp2f((m_run - mb) * c) : 1.f;  // 0 at first
-        l_run *= alpha;
-        if (j > 0 || sb > 0) {  // the accumulators are still zero before that
-#pragma unroll
-          for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-        }
-        m_run = up ? mb : m_run;
-      }
-      // a row with no token yet has m = -inf and only masked scores: weight 0
-      const float mc = m_run == -INFINITY ? 0.f : m_run * c;
-      float ps = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sv[r] = __builtin_amdgcn_exp2f(fmaf(sv[r], c, -mc));
-        ps += sv[r];
-      }
-      l_run += sum_with_partner32(ps);
+      m_run = up ? mb : m_run;
+    }
+    // a row with no token yet has m = -inf and only masked scores: weight 0
+    const float mc = m_run == -INFINITY ? 0.f : m_run * c;
 
-      // ---- O^T += V^T . P^T over two steps of 16 tokens. Step ks takes
-      // elements 8ks .. 8ks+7: contraction index 8*half + i is token
-      // 4*half + 16ks + 8*(i/4) + i%4 of the sub-block. This lane's A fragment
-      // (d = 32t + lane%32) comes from two transposed reads: tokens
-      // 4*half + 16ks + 0..3, then +8.
+    // ---- V^T fragments of every 16-token step, read before the arithmetic
+    // so that the exponentials, the P split and the PV products below form
+    // one branch-free stretch the scheduler can interleave (one step's
+    // products run while the next step's weights are computed). Step
+    // (sb, ks) covers tokens 32 sb + 16 ks .. +15; this lane's A fragment
+    // (d = 32t + lane%32) comes from two transposed reads: tokens
+    // 4*half + 0..3 of the step, then +8.
+    u32x2_t va[R::kSub * 2][D / 32][2];
+    static_for<R::kSub * 2>([&](auto STEP) {
+      constexpr int step = decltype(STEP)::value;
+      constexpr int kOff = 16 * step * kRB;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        va[step][t][0] = lds_tr_b64<kOff>(vst + vb[t]);
+        va[step][t][1] = lds_tr_b64<kOff + 8 * kRB>(vst + vb[t]);
+      }
+    });
+    lgkm_wait_tied<D / 32>(va[0]);
+#pragma unroll
+    for (int step = 1; step < R::kSub * 2; ++step) lgkm_wait_tied<D / 32>(va[step]);
+
+    // ---- P = exp2(c s - c m), then O^T += V^T . P^T. Step ks of a sub-block
+    // takes elements 8ks .. 8ks+7: contraction index 8*half + i is token
+    // 4*half + 16ks + 8*(i/4) + i%4 of the sub-block. P is multiplied as two
+    // bf16 parts, hi = P rounded to bf16 and lo = the rounding error rounded
+    // again: P alone in bf16 carries a relative error up to 2^-8, which a row
+    // that attends few tokens does not average away; hi + lo is within about
+    // 2^-16 of P.
+    float ps = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < R::kSub; ++sb) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        // P = hi + lo in two bf16 parts (hi = P rounded to bf16, lo = the
-        // rounding error rounded again): P alone in bf16 carries a relative
-        // error up to 2^-8, which a row that attends few tokens does not
-        // average away; hi + lo is within about 2^-16 of P.
-        bf16x8_t pb, pl;
+        uint32_t phw[4], plw[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const __bf16 hi = (__bf16)sv[8 * ks + i];
-          pb[i] = hi;
-          pl[i] = (__bf16)(sv[8 * ks + i] - (float)hi);
+        for (int i = 0; i < 4; ++i) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[sb][8 * ks + 2 * i], c, -mc));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[sb][8 * ks + 2 * i + 1], c, -mc));
+          ps += e0 + e1;
+          split_bf16x2(e0, e1, phw[i], plw[i]);
         }
-        u32x2_t va[D / 32][2];
+        const u32x4_t ph = {phw[0], phw[1], phw[2], phw[3]};
+        const u32x4_t pl = {plw[0], plw[1], plw[2], plw[3]};
+        const int step = 2 * sb + ks;
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
-#pragma unroll
-          for (int run = 0; run < 2; ++run) {
-            // input role: token 4*(g16/2) + 16ks + 8run + v_k, columns
-            // 32t + 16*(g16%2) + 4*v_p .. +3
-            const int tok = 32 * (wtok + sb) + 4 * (g16 >> 1) + 16 * ks + 8 * run + v_k;
-            const int d = 32 * t + 16 * (g16 & 1) + 4 * v_p;
-            const uint32_t a = lds_u32(vst + tok * kRB + (((d >> 3) ^ Gm::swz_v(tok)) * 16) + (d & 7) * 2);
-            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(va[t][run]) : "v"(a) : "memory");
-          }
-        }
-        lgkm_wait_tied<D / 32>(va);
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          const u32x4_t av = {va[t][0][0], va[t][0][1], va[t][1][0], va[t][1][1]};
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[t], 0, 0, 0);
+          const u32x4_t av = {va[step][t][0][0], va[step][t][0][1], va[step][t][1][0], va[step][t][1][1]};
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                         __builtin_bit_cast(bf16x8_t, ph), o[t], 0, 0, 0);
         }
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
-          const u32x4_t av = {va[t][0][0], va[t][0][1], va[t][1][0], va[t][1][1]};
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pl, o[t], 0, 0, 0);
+          const u32x4_t av = {va[step][t][0][0], va[step][t][0][1], va[step][t][1][0], va[step][t][1][1]};
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                         __builtin_bit_cast(bf16x8_t, pl), o[t], 0, 0, 0);
         }
       }
     }
+    l_run += sum_with_partner32(ps);
   }
   // loads past the end may still be landing in the ring
   wait_vmcnt<0>();
