@@ -418,6 +418,7 @@ struct Tune {
   // fits 2 waves per SIMD in LDS) measured 17% faster than 4 on the skewed
   // batch.
   static constexpr int kRing = kKv == 1 ? 8 : (kStream ? 2 : 4);
+  static_assert(kRing % 2 == 0, "the main loop reads ring stages two at a time");
   // the rotary embedding keeps q in fp32 (G * kElems) and 4 x 8 rotation terms
   static constexpr int kRegs = G * R::kElems + (kRope ? G * R::kElems + 32 : G * R::kWords) +
                                16 * R::kLoads + 2 * G + 48;
