@@ -119,3 +119,44 @@ def test_binding_refuses_cpu_tensors():
     k = torch.zeros(100, 2, 16, 128, dtype=torch.bfloat16)
     with pytest.raises(RuntimeError, match="GPU"):
         fb.decode(q, k, k, p)
+
+
+def test_rope_run_rejects_what_is_not_built():
+    """fi_decode_run_rope checks the plan before touching any device: only
+    bf16 plans with head_dim 128 and no shared-prefix items, finite
+    parameters."""
+    L = fb.lib()
+    fake = ctypes.c_void_p(0x100000)
+    ip, ix, lp = [np.asarray(a) for a in GOOD]
+    for dtype, d in (("f32", 128), ("bf16", 64), ("fp8", 128)):
+        p = fb.plan(ip, ix, lp, 8, 2, d, 16, 100, dtype)
+        st = L.fi_decode_run_rope(p.handle, fake, fake, fake, 1e4, 1.0, fake, None, 0.0, fake,
+                                  p.info["workspace_bytes"], None)
+        assert st == -2 and "rotary" in L.fi_last_error().decode(), (dtype, d)
+    p = fb.plan(ip, ix, lp, 8, 2, 128, 16, 100, "bf16")
+    st = L.fi_decode_run_rope(p.handle, fake, fake, fake, float("nan"), 1.0, fake, None, 0.0, fake,
+                              p.info["workspace_bytes"], None)
+    assert st == -1
+    st = L.fi_decode_run_rope(p.handle, fake, fake, fake, 0.5, 1.0, fake, None, 0.0, fake,
+                              p.info["workspace_bytes"], None)
+    assert st == -1 and "exceed 1" in L.fi_last_error().decode()
+    # accepted parameters, but the plan was not uploaded to this workspace
+    st = L.fi_decode_run_rope(p.handle, fake, fake, fake, 0.0, 0.0, fake, None, 0.0, fake,
+                              p.info["workspace_bytes"], None)
+    assert st == -6
+
+
+def test_prefill_run_checks_on_the_host():
+    L = fb.lib()
+    fake = ctypes.c_void_p(0x100000)
+    ip, ix, lp = [np.asarray(a) for a in GOOD]
+    p = fb.prefill_plan(np.array([0, 2, 3]), ip, ix, lp, 8, 2, 128, 16, 100)
+    ws = p.info["workspace_bytes"]
+    assert L.fi_prefill_run(None, fake, fake, fake, fake, None, 0.0, fake, ws, None) == -1
+    assert L.fi_prefill_run(p.handle, fake, fake, fake, fake, None, 0.0, fake, ws, None) == -6
+    assert L.fi_prefill_run(p.handle, fake, fake, fake, fake, None, 0.0, fake, ws - 1, None) == -3
+    assert L.fi_prefill_run(p.handle, None, fake, fake, fake, None, 0.0, fake, ws, None) == -1
+    assert L.fi_prefill_run(p.handle, ctypes.c_void_p(0x100008), fake, fake, fake, None, 0.0, fake, ws,
+                            None) == -1
+    assert L.fi_prefill_plan_upload(p.handle, ctypes.c_void_p(0x100010), ws, None) == -1
+    assert L.fi_prefill_plan_upload(p.handle, fake, ws - 1, None) == -3
