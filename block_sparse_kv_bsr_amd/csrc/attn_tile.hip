@@ -93,6 +93,8 @@ struct TileParams {
   int num_qo_heads;
   int num_kv_heads;
   int page_size;
+  uint32_t page_magic;     // ceil(2^32 / page_size) mod 2^32
+  uint32_t page_magic_hi;  // 1 when page_size is 1 (the quotient is then 2^32)
   int group;
   int causal;           // prefill: row r attends VISIBLE + r / G tokens
   float scale_log2;     // sm_scale * log2(e)
@@ -184,6 +186,22 @@ __device__ __forceinline__ void lgkm_wait_tied(u32x4_t (&r)[N]) {
                    "+v"(r[7])::"memory");
   }
 }
+// s_waitcnt lgkmcnt(CNT): the reads of r are done once at most CNT LDS
+// operations issued after them are still in flight (LDS returns in order).
+template <int CNT, int N>
+__device__ __forceinline__ void lgkm_wait_tied_n(u32x4_t (&r)[N]) {
+  static_assert(CNT >= 0 && CNT < 16, "lgkmcnt range");
+  if constexpr (N == 4) {
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "i"(CNT) : "memory");
+  } else {
+    static_assert(N == 8, "4 or 8 fragments");
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
+                   "+v"(r[7])
+                 : "i"(CNT)
+                 : "memory");
+  }
+}
 template <int N>
 __device__ __forceinline__ void lgkm_wait_tied(u32x2_t (&r)[N][2]) {
   if constexpr (N == 2) {
@@ -227,7 +245,7 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   constexpr int NS = Gm::kStages;
   constexpr int kRB = Gm::kRowBytes;
   __shared__ __attribute__((aligned(1024))) char s_ring[NS][2][Gm::kBlockBytes];
-  __shared__ int s_pid[kIds];
+  __shared__ uint32_t s_pid[kIds];  // page byte offsets (page + head) / 128
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -292,8 +310,13 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   }
   lim = min(lim, ntok);
 
-  // ---- page ids of the item (one window: an item has at most kIds pages)
-  if (tid < kIds) s_pid[tid] = p.page_ids[page_begin + min(tid, npg - 1)];
+  // ---- the item's pages (one window: an item has at most kIds pages) as
+  // byte offsets of the page's rows of this KV head in 128-byte units: every
+  // page and head stride is a multiple of 128 bytes, and 2^32 such units
+  // (512 GiB) exceed any device's memory
+  const int64_t head_off = (int64_t)h * p.head_stride;
+  if (tid < kIds)
+    s_pid[tid] = (uint32_t)(((int64_t)p.page_ids[page_begin + min(tid, npg - 1)] * p.page_stride + head_off) >> 7);
 
   // Q^T as the B operand: lane holds Q[row][16s + 8*half .. +8] for step s
   // (a padding row loads the tile's first row and zeroes it, so the loads
@@ -323,23 +346,31 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   // gfx950) and stream past the caches; prefill tiles of one request and KV
   // head read the same K/V, so theirs stay cacheable.
   constexpr int kAux = kPrefill ? 0 : 2;
-  const int64_t head_off = (int64_t)h * p.head_stride;
   const int dma_row = lane / Gm::kPieces;
   const int dma_piece = lane % Gm::kPieces;
+  // tok / page_size as a multiply-high: tok < 2^20 (at most kIds pages of at
+  // most 4096 tokens) and the reciprocal ceil(2^32 / P) is too large by less
+  // than 1, so the quotient is off by less than 2^-12 < 1 / P -- exact for
+  // every P < 4096, and powers of two are exact anyway
+  const uint32_t pmag = p.page_magic, pmag_hi = p.page_magic_hi;
+  const uint32_t psz = (uint32_t)p.page_size;
   auto issue = [&](int j, int st) {
 #pragma unroll
     for (int i = 0; i < Gm::kDmaPerWave; ++i) {
       const int t = (wave * Gm::kDmaPerWave + i) * Gm::kRowsPerDma + dma_row;
-      const int tok = min(j * kBlock + t, ntok - 1);
-      const int pid = s_pid[tok / p.page_size];
-      const int64_t row_off = (int64_t)pid * p.page_stride + head_off + (int64_t)(tok % p.page_size) * kRB;
+      const uint32_t tok = (uint32_t)min(j * kBlock + t, ntok - 1);
+      const uint32_t pg = __umulhi(tok, pmag) + tok * pmag_hi;
+      const uint32_t row_in_page = tok - pg * psz;
+      const uint64_t page_off = (uint64_t)s_pid[pg] << 7;
       const int kp = dma_piece ^ Gm::swz_k(t);
       const int vp = dma_piece ^ Gm::swz_v(t);
+      const uint32_t krow = row_in_page * kRB + kp * 16;
+      const uint32_t vrow = row_in_page * kRB + vp * 16;
       char* kdst = &s_ring[st][0][(wave * Gm::kDmaPerWave + i) * 1024];
       char* vdst = &s_ring[st][1][(wave * Gm::kDmaPerWave + i) * 1024];
-      __builtin_amdgcn_global_load_lds((global_void_t*)(p.k_pages + row_off + kp * 16),
+      __builtin_amdgcn_global_load_lds((global_void_t*)(p.k_pages + (page_off + krow)),
                                        (lds_void_t*)kdst, 16, 0, kAux);
-      __builtin_amdgcn_global_load_lds((global_void_t*)(p.v_pages + row_off + vp * 16),
+      __builtin_amdgcn_global_load_lds((global_void_t*)(p.v_pages + (page_off + vrow)),
                                        (lds_void_t*)vdst, 16, 0, kAux);
     }
   };
@@ -395,22 +426,44 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
 
     const uint32_t kst = lds_u32(s_ring[st][0]);
     const uint32_t vst = lds_u32(s_ring[st][1]);
-    // ---- S^T = K . Q^T of every sub-block (independent chains)
+    // ---- S^T = K . Q^T of every sub-block (independent chains). All K
+    // fragments are requested first; each sub-block's products start as soon
+    // as its own fragments are in, and the scheduling barriers keep the
+    // first sub-block's products ahead of the second's wait.
     f32x16_t sc[R::kSub];
+    u32x4_t kv[R::kSub][D / 16];
     static_for<R::kSub>([&](auto SB) {
       constexpr int sb = decltype(SB)::value;
-      u32x4_t kv[D / 16];
 #pragma unroll
-      for (int q = 0; q < D / 16; ++q) kv[q] = lds_b128<32 * sb * kRB>(kst + kb[q]);
-      lgkm_wait_tied<D / 16>(kv);
+      for (int q = 0; q < D / 16; ++q) kv[sb][q] = lds_b128<32 * sb * kRB>(kst + kb[q]);
+    });
+    static_for<R::kSub>([&](auto SB) {
+      constexpr int sb = decltype(SB)::value;
+      lgkm_wait_tied_n<(R::kSub - 1 - sb) * (D / 16)>(kv[sb]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[sb][r] = 0.f;
 #pragma unroll
       for (int q = 0; q < D / 16; ++q)
-        sc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv[q]), qf[q], sc[sb], 0, 0, 0);
+        sc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv[sb][q]), qf[q], sc[sb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     });
     // the loads of a later block go out while the products run
     issue(j + NS - 1, (j + NS - 1) % NS);
+
+    // ---- V^T fragments of every 16-token step, requested now so that they
+    // arrive during the softmax step below. Step (sb, ks) covers tokens
+    // 32 sb + 16 ks .. +15; this lane's A fragment (d = 32t + lane%32) comes
+    // from two transposed reads: tokens 4*half + 0..3 of the step, then +8.
+    u32x2_t va[R::kSub * 2][D / 32][2];
+    static_for<R::kSub * 2>([&](auto STEP) {
+      constexpr int step = decltype(STEP)::value;
+      constexpr int kOff = 16 * step * kRB;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        va[step][t][0] = lds_tr_b64<kOff>(vst + vb[t]);
+        va[step][t][1] = lds_tr_b64<kOff + 8 * kRB>(vst + vb[t]);
+      }
+    });
 
     // ---- online softmax over the wave's tokens of the block; element r of
     // sub-block sb holds token 32 (wtok + sb) + 4*half + 8*(r/4) + r%4
@@ -445,23 +498,10 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
     // a row with no token yet has m = -inf and only masked scores: weight 0
     const float mc = m_run == -INFINITY ? 0.f : m_run * c;
 
-    // ---- V^T fragments of every 16-token step, read before the arithmetic
-    // so that the exponentials, the P split and the PV products below form
-    // one branch-free stretch the scheduler can interleave (one step's
-    // products run while the next step's weights are computed). Step
-    // (sb, ks) covers tokens 32 sb + 16 ks .. +15; this lane's A fragment
-    // (d = 32t + lane%32) comes from two transposed reads: tokens
-    // 4*half + 0..3 of the step, then +8.
-    u32x2_t va[R::kSub * 2][D / 32][2];
-    static_for<R::kSub * 2>([&](auto STEP) {
-      constexpr int step = decltype(STEP)::value;
-      constexpr int kOff = 16 * step * kRB;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        va[step][t][0] = lds_tr_b64<kOff>(vst + vb[t]);
-        va[step][t][1] = lds_tr_b64<kOff + 8 * kRB>(vst + vb[t]);
-      }
-    });
+    // every V^T fragment is in: the exponentials, the P split and the PV
+    // products below form one branch-free stretch the scheduler can
+    // interleave (one step's products run while the next step's weights are
+    // computed)
     lgkm_wait_tied<D / 32>(va[0]);
 #pragma unroll
     for (int step = 1; step < R::kSub * 2; ++step) lgkm_wait_tied<D / 32>(va[step]);
@@ -582,6 +622,13 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   if (half == 0) p.part_lse[prow] = lse2;
 }
 
+// ceil(2^32 / page_size), split into its low word and the 2^32 bit
+void set_page_magic(TileParams& p) {
+  const uint64_t m = ((1ull << 32) + (uint64_t)p.page_size - 1) / (uint64_t)p.page_size;
+  p.page_magic = (uint32_t)m;
+  p.page_magic_hi = (uint32_t)(m >> 32);
+}
+
 }  // namespace
 
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream) {
@@ -602,6 +649,7 @@ hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream) {
   p.num_qo_heads = a.num_qo_heads;
   p.num_kv_heads = a.num_kv_heads;
   p.page_size = a.page_size;
+  set_page_magic(p);
   p.group = a.group;
   p.scale_log2 = a.sm_scale * kLog2e;
   const dim3 grid((uint32_t)a.num_items), block(64 * kWaves);
@@ -629,6 +677,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.num_qo_heads = a.num_qo_heads;
   p.num_kv_heads = a.num_kv_heads;
   p.page_size = a.page_size;
+  set_page_magic(p);
   p.group = a.group;
   p.causal = a.causal;
   p.scale_log2 = a.sm_scale * kLog2e;
