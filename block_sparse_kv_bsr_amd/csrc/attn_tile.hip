@@ -27,11 +27,12 @@
 // 64-token block; the two partial softmax states of a row are merged through
 // LDS at the end. Prefill: wave w owns rows 32w .. +31 and both 32-token
 // halves of every block, so a K/V block serves 256 rows. Per block a wave
-// reads its K fragments and issues the S^T products, then the loads of a
-// later block, takes one online-softmax step over its tokens (the running
-// max moves at most once per block), reads all its V^T fragments and runs
-// one branch-free stretch of exponentials, P splits and PV products that the
-// scheduler interleaves. K/V blocks stream into
+// requests all its K fragments and issues each sub-block's S^T products as
+// soon as that sub-block's fragments are in, then the loads of a later
+// block and its V^T fragment reads, takes one online-softmax step over its
+// tokens (the running max moves at most once per block) while those reads
+// land, and runs one branch-free stretch of exponentials, P splits and PV
+// products that the scheduler interleaves. K/V blocks stream into
 // an LDS ring of kStages stages with gfx950's direct-to-LDS loads (no
 // staging registers), one barrier per block. Per 32 tokens of a wave:
 //   S^T[token, row] = K . Q^T     v_mfma_f32_32x32x16_bf16, D/16 steps
