@@ -256,7 +256,9 @@ def plan(kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int, num_kv_head
     _check(lib().fi_plan_create(_ptr32(ip), ix_ptr, _ptr32(lp), batch, num_qo_heads,
                                 num_kv_heads, head_dim, page_size, int(num_pool_pages),
                                 _dtype_code(dtype), ctypes.byref(opts), ctypes.byref(h)))
-    return Plan(h.value)
+    p = Plan(h.value)
+    p.num_pool_pages = int(num_pool_pages)
+    return p
 
 
 def _stream(stream) -> int:
@@ -275,6 +277,28 @@ def _require_gpu(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _require_like(t, name, shape, dtype, device):
+    """A caller-supplied output: the kernels write every element of `shape`,
+    so a smaller or differently typed buffer is refused here, before the
+    pointer crosses the C ABI (which cannot see sizes)."""
+    _require_gpu(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, q on {device}")
+
+
+def _require_pool(k_pages, v_pages, q, plan_):
+    """K/V pools on q's device holding at least the plan's pool pages (the
+    planner checked every listed page id against that count)."""
+    for t, n in ((k_pages, "k_pages"), (v_pages, "v_pages")):
+        if t.device != q.device:
+            raise ValueError(f"{n} is on {t.device}, q on {q.device}")
+        if t.shape[0] < plan_.num_pool_pages:
+            raise ValueError(f"{n} holds {t.shape[0]} pages; the plan was made for "
+                             f"{plan_.num_pool_pages}")
+
+
 def _decode_args(q, k_pages, v_pages, plan_: Plan, out, lse, workspace, stream):
     import torch
     for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
@@ -291,14 +315,17 @@ def _decode_args(q, k_pages, v_pages, plan_: Plan, out, lse, workspace, stream):
     kshape = (k_pages.shape[0], info["num_kv_heads"], info["page_size"], d)
     if tuple(k_pages.shape) != kshape or tuple(v_pages.shape) != kshape:
         raise ValueError(f"k_pages/v_pages must have shape [pool, {kshape[1]}, {kshape[2]}, {d}]")
+    _require_pool(k_pages, v_pages, q, plan_)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=want, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    _require_gpu(out, "out")
-    _require_gpu(lse, "lse")
+    _require_like(out, "out", (B, Hq, d), want, q.device)
+    _require_like(lse, "lse", (B, Hq), torch.float32, q.device)
     if workspace is None:
         workspace = plan_.ensure_uploaded(q.device, stream)
+    elif workspace.device != q.device:
+        raise ValueError(f"workspace is on {workspace.device}, q on {q.device}")
     return out, lse, workspace
 
 
@@ -335,15 +362,20 @@ def merge_states(v_a, s_a, v_b, s_b, v_out=None, s_out=None, stream=None):
     import torch
     for t, n in ((v_a, "v_a"), (s_a, "s_a"), (v_b, "v_b"), (s_b, "s_b")):
         _require_gpu(t, n)
-    if v_a.shape != v_b.shape or v_a.dim() != 2:
-        raise ValueError("v_a and v_b must both be [rows, head_dim]")
+    if v_a.shape != v_b.shape or v_a.dim() != 2 or v_a.dtype != v_b.dtype:
+        raise ValueError("v_a and v_b must both be [rows, head_dim] of one dtype")
     rows, d = v_a.shape
     if s_a.shape != (rows,) or s_b.shape != (rows,) or s_a.dtype != torch.float32 or s_b.dtype != torch.float32:
         raise ValueError("s_a and s_b must be float32 [rows]")
+    for t, n in ((s_a, "s_a"), (v_b, "v_b"), (s_b, "s_b")):
+        if t.device != v_a.device:
+            raise ValueError(f"{n} is on {t.device}, v_a on {v_a.device}")
     if v_out is None:
         v_out = torch.empty_like(v_a)
     if s_out is None:
         s_out = torch.empty_like(s_a)
+    _require_like(v_out, "v_out", (rows, d), v_a.dtype, v_a.device)
+    _require_like(s_out, "s_out", (rows,), torch.float32, v_a.device)
     _check(lib().fi_merge_states(_dtype_code(v_a.dtype), ctypes.c_void_p(v_a.data_ptr()),
                                  ctypes.c_void_p(s_a.data_ptr()), ctypes.c_void_p(v_b.data_ptr()),
                                  ctypes.c_void_p(s_b.data_ptr()), ctypes.c_void_p(v_out.data_ptr()),
@@ -422,7 +454,9 @@ def prefill_plan(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_qo_head
                                         num_qo_heads, num_kv_heads, head_dim, page_size,
                                         int(num_pool_pages), _dtype_code(dtype), int(bool(causal)),
                                         ctypes.byref(opts), ctypes.byref(h)))
-    return PrefillPlan(h.value)
+    p = PrefillPlan(h.value)
+    p.num_pool_pages = int(num_pool_pages)
+    return p
 
 
 def prefill(q, k_pages, v_pages, plan_: PrefillPlan, out=None, lse=None,
@@ -440,14 +474,17 @@ def prefill(q, k_pages, v_pages, plan_: PrefillPlan, out=None, lse=None,
     kshape = (k_pages.shape[0], info["num_kv_heads"], info["page_size"], d)
     if tuple(k_pages.shape) != kshape or tuple(v_pages.shape) != kshape:
         raise ValueError(f"k_pages/v_pages must have shape [pool, {kshape[1]}, {kshape[2]}, {d}]")
+    _require_pool(k_pages, v_pages, q, plan_)
     if out is None:
         out = torch.empty((N, Hq, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
-    _require_gpu(out, "out")
-    _require_gpu(lse, "lse")
+    _require_like(out, "out", (N, Hq, d), torch.bfloat16, q.device)
+    _require_like(lse, "lse", (N, Hq), torch.float32, q.device)
     if workspace is None:
         workspace = plan_.ensure_uploaded(q.device, stream)
+    elif workspace.device != q.device:
+        raise ValueError(f"workspace is on {workspace.device}, q on {q.device}")
     scale = float(sm_scale) if sm_scale else 0.0
     _check(lib().fi_prefill_run(plan_.handle, ctypes.c_void_p(q.data_ptr()),
                                 ctypes.c_void_p(k_pages.data_ptr()),

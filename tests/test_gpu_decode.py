@@ -13,7 +13,8 @@ import torch
 
 import block_sparse_kv_bsr_amd as fb
 import oracle.attention as oa
-from block_sparse_kv_bsr_amd.workloads import prefix_workload, random_workload, workload
+from block_sparse_kv_bsr_amd.workloads import (prefix_workload, random_prefill_workload,
+                                               random_workload, workload)
 from tests.parity import compare
 
 pytestmark = pytest.mark.gpu
@@ -285,3 +286,37 @@ def test_merge_states(dtype, d):
     torch.cuda.synchronize()
     assert torch.equal(va2.cpu().view(torch.int16 if dtype == "bf16" else torch.int32),
                        vo.cpu().view(torch.int16 if dtype == "bf16" else torch.int32))
+
+
+def test_binding_refuses_bad_buffers():
+    """The C ABI cannot see buffer sizes, so the binding refuses outputs of the
+    wrong shape or dtype, a pool smaller than the plan's, tensors on another
+    device kind, and mismatched merge inputs, before any kernel runs."""
+    w = random_workload(59, 3, 100, 8, 2, 128, 16, "bf16")
+    q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, 8, 2, 128, 16, w.num_pool_pages, "bf16")
+    B = w.batch
+    with pytest.raises(ValueError, match="out must be"):
+        fb.decode(q, k, v, p, out=torch.empty((B, 8, 64), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError, match="lse must be"):
+        fb.decode(q, k, v, p, lse=torch.empty((B, 8), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError, match="pages"):
+        fb.decode(q, k[:-4].contiguous(), v[:-4].contiguous(), p)
+    with pytest.raises(RuntimeError, match="GPU tensor"):
+        fb.decode(q.cpu(), k, v, p)
+    a = torch.randn(5, 64, device="cuda")
+    s = torch.randn(5, device="cuda")
+    with pytest.raises(ValueError, match="one dtype"):
+        fb.merge_states(a, s, a.bfloat16(), s)
+    with pytest.raises(ValueError, match="v_out must be"):
+        fb.merge_states(a, s, a, s, v_out=torch.empty(4, 64, device="cuda"))
+    wp = random_prefill_workload(60, 2, 80, 8, 2, 128, 16)
+    qp, kp, vp = (t.cuda() for t in wp.make_values("cpu"))
+    pp = fb.prefill_plan(wp.qo_indptr, wp.kv_indptr, wp.kv_indices, wp.last_page_len, 8, 2, 128,
+                         16, wp.num_pool_pages)
+    with pytest.raises(ValueError, match="out must be"):
+        fb.prefill(qp, kp, vp, pp, out=torch.empty((1, 8, 128), dtype=torch.bfloat16, device="cuda"))
+    # the same calls with good buffers still run
+    fb.decode(q, k, v, p)
+    fb.prefill(qp, kp, vp, pp)
+    torch.cuda.synchronize()
