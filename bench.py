@@ -105,6 +105,36 @@ def summarize_counters(fetch_csv, write_csv, workload_name):
     print(open(path).read())
 
 
+# ------------------------------------------------------- streaming ceiling
+def stream_ceiling(dev, flush, nbytes=2 << 30, reps=5):
+    """The box's practical HBM read rate: libfi_bench.so's streaming-read
+    kernel (16-byte nontemporal loads) over 2 GiB, L2/MALL flushed before
+    each pass, HIP events on the stream it runs on; median of `reps`."""
+    import ctypes
+    import torch
+    L = ctypes.CDLL(os.path.join(ROOT, "block_sparse_kv_bsr_amd", "libfi_bench.so"))
+    L.fi_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    L.fi_bench_stream_read.restype = ctypes.c_int
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    ms = []
+    for i in range(reps + 1):
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = L.fi_bench_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream)
+        e1.record()
+        if rc != 0:
+            raise RuntimeError(f"fi_bench_stream_read failed: hipError {rc}")
+        torch.cuda.synchronize()
+        if i:  # the first pass warms the code object
+            ms.append(e0.elapsed_time(e1))
+    del buf
+    return nbytes / (statistics.median(ms) * 1e-3) / 1e9
+
+
 # ------------------------------------------------------------------ oracle
 def cpu_baseline(w, q, k, v, min_seconds=10.0, max_passes=3):
     """Time the float64 oracle on the host over whole batches of the same
@@ -405,6 +435,12 @@ def main():
                      "traffic": None if traffic is None else int(traffic),
                      "kernel": "decode_bsr_kernel"},
     }
+    if not args.counters_run:
+        ceiling = stream_ceiling(dev, flush)
+        result["practical_ceiling"] = {
+            "gbs": round(ceiling, 1), "frac": round(gbs / ceiling, 4),
+            "kernel": "streaming read of 2 GiB with 16-byte nontemporal loads "
+                      "(libfi_bench.so), L2/MALL flushed, median of 5"}
     if not args.no_cpu_baseline and not args.counters_run:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v)
     print(json.dumps(result), flush=True)

@@ -1,8 +1,10 @@
-"""Build the C-ABI library ``libfi_bsr.so`` in-tree for gfx950.
+"""Build the C-ABI library ``libfi_bsr.so`` in-tree for gfx950, and the
+benchmark's measurement helper ``libfi_bench.so`` (a streaming-read kernel,
+not part of the library's interface).
 
 Usage: ``python -m block_sparse_kv_bsr_amd.build``. Compiles every source each
 time it runs (the sources are small); objects go to ``_build/`` at the repo
-root and the library next to this file.
+root and the libraries next to this file.
 """
 import os
 import subprocess
@@ -15,6 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfi_bsr.so")
+BENCH_LIB = os.path.join(PKG, "libfi_bench.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -23,6 +26,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HIP_SOURCES = ["decode_bsr.hip", "attn_tile.hip", "merge_states.hip", "abi.hip"]
 CPP_SOURCES = ["plan.cpp", "prefill_plan.cpp"]
+BENCH_SOURCES = ["bench_stream.hip"]
 
 
 def _run(cmd):
@@ -47,11 +51,17 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, src + ".o")
         jobs.append(["g++", *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    bench_objs = []
+    for src in BENCH_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        jobs.append([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
+        bench_objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         outs = list(ex.map(_run, jobs))
-    tmp = LIB + ".tmp"
-    outs.append(_run([HIPCC, *DEVICE, "-shared", "-fPIC", *objs, "-o", tmp]))
-    os.replace(tmp, LIB)
+    for lib, parts in ((LIB, objs), (BENCH_LIB, bench_objs)):
+        tmp = lib + ".tmp"
+        outs.append(_run([HIPCC, *DEVICE, "-shared", "-fPIC", *parts, "-o", tmp]))
+        os.replace(tmp, lib)
     if verbose:
         for o in outs:
             if o.strip():

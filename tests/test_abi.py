@@ -14,8 +14,8 @@ from block_sparse_kv_bsr_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_functions():
-    text = open(os.path.join(ROOT, "include", "fi_bsr.h")).read()
+def declared_functions(header="fi_bsr.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fi_[a-z_]+)\s*\(", text)))
 
@@ -28,6 +28,20 @@ def test_library_exports_every_declared_symbol():
     L = fb.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
+
+
+def test_bench_helper_library_loads_and_exports_its_symbol():
+    # the benchmark's streaming-read helper lives in its own library
+    path = os.path.join(ROOT, "block_sparse_kv_bsr_amd", "libfi_bench.so")
+    L = ctypes.CDLL(path)
+    names = declared_functions("fi_bench.h")
+    assert names == ["fi_bench_stream_read"]
+    for name in names:
+        assert hasattr(L, name), name
+    # malformed calls are refused before any launch (hipErrorInvalidValue)
+    L.fi_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.fi_bench_stream_read(None, 16, None, None) != 0
+    assert L.fi_bench_stream_read(ctypes.c_void_p(16), 15, ctypes.c_void_p(16), None) != 0
 
 
 def _plan_status(indptr, indices, last, Hq=8, Hkv=2, d=128, P=16, pool=100, dtype=1, opts=None):
