@@ -166,3 +166,59 @@ def test_random_prefill(case):
                                   w.last_page_len, causal, w.sm_scale)
     stats = compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE, True, what)
     log(f"[ok] items={p.info['num_items']} merges={p.info['num_merges']} {stats}")
+
+
+LARGE_PAGES = [
+    # seed, page size, dtype, head_dim, fixed chunk tokens (0: planner's choice)
+    (7300, 100, "bf16", 128, 0),
+    (7301, 256, "bf16", 128, 300),
+    (7302, 1024, "f32", 64, 0),
+    (7303, 4096, "bf16", 128, 0),
+    (7304, 4096, "fp8", 128, 1000),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_PAGES, ids=lambda c: f"P{c[1]}_{c[2]}")
+def test_large_page_sizes_decode(case):
+    """Pages of 100 .. 4096 tokens (the largest the planner takes): requests
+    that end inside their first page, span several, and are cut mid-page."""
+    seed, P, dtype, d, fixed = case
+    lens = [1, P - 1, P, P + 1, 3 * P // 2, 2 * P + 7]
+    what = f"large pages P={P} {dtype} d={d} fixed={fixed} lens={lens}"
+    log(f"[case] {what}")
+    w = random_workload(seed, len(lens), 0, 8, 2, d, P, dtype, lens=lens)
+    q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, 8, 2, d, P, w.num_pool_pages, dtype,
+                fixed_chunk_tokens=fixed)
+    out, lse = fb.decode(q, k, v, p, k_scale=w.k_scale, v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    qh = q.double().cpu().numpy()
+    if dtype == "fp8":
+        kh = oa.dequantize_e4m3(k.view(torch.uint8).cpu().numpy(), w.k_scale)
+        vh = oa.dequantize_e4m3(v.view(torch.uint8).cpu().numpy(), w.v_scale)
+    else:
+        kh, vh = k.double().cpu().numpy(), v.double().cpu().numpy()
+    O, LSE = oa.decode_attention(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len,
+                                 w.sm_scale)
+    stats = compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE,
+                    dtype != "f32", what)
+    log(f"[ok] items={p.info['num_items']} {stats}")
+
+
+@pytest.mark.parametrize("P", [100, 256, 1024, 4096])
+def test_large_page_sizes_prefill(P):
+    lens = [P - 1, P + 1, 2 * P + 7]
+    what = f"prefill large pages P={P} lens={lens}"
+    log(f"[case] {what}")
+    w = random_prefill_workload(7310 + P, len(lens), 0, 8, 2, 128, P, causal=True, lens=lens,
+                                qo_lens=[min(L, 70) for L in lens])
+    q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    p = fb.prefill_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, 8, 2, 128, P,
+                        w.num_pool_pages, causal=True, fixed_chunk_tokens=P if P <= 256 else 0)
+    out, lse = fb.prefill(q, k, v, p)
+    torch.cuda.synchronize()
+    qh, kh, vh = (t.double().cpu().numpy() for t in (q, k, v))
+    O, LSE = oa.prefill_attention(qh, kh, vh, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                  w.last_page_len, True, w.sm_scale)
+    stats = compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE, True, what)
+    log(f"[ok] items={p.info['num_items']} merges={p.info['num_merges']} {stats}")
