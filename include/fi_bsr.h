@@ -426,7 +426,9 @@ enum {
  *                  with causal != 0 every n_b <= L_b
  * kv_indptr, kv_indices, kv_last_page_len: the page table, as for
  *                  fi_plan_create (L_b tokens per request)
- * num_qo_heads, num_kv_heads: G = num_qo_heads / num_kv_heads in 1 .. 128
+ * num_qo_heads, num_kv_heads: G = num_qo_heads / num_kv_heads in
+ *                  1 .. FI_PREFILL_ROWS (a tile holds FI_PREFILL_ROWS / G query
+ *                  tokens; with G not dividing it the last rows are padding)
  * head_dim         64 or 128
  * page_size        1 .. 4096
  * dtype            FI_DTYPE_BF16 (q, K, V, out)

@@ -234,6 +234,12 @@ def test_prefill_plan_rejects(kw, code, needle):
     assert st == code and needle in msg, (st, msg)
 
 
+def test_group_size_limit_is_the_tile_height():
+    # G = FI_PREFILL_ROWS is the largest group: one query token per tile
+    assert _status([0, 2, 3], [0, 2, 3], [5, 6, 7], [16, 3], Hq=256, Hkv=1)[0] == 0
+    assert _status([0, 2, 3], [0, 2, 3], [5, 6, 7], [16, 3], Hq=257, Hkv=1)[0] == -2
+
+
 def test_more_queries_than_tokens_is_fine_without_the_mask():
     assert _status([0, 40, 41], [0, 2, 3], [5, 6, 7], [16, 3], causal=0)[0] == 0
 
