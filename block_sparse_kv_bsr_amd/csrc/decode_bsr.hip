@@ -177,6 +177,26 @@ __device__ __forceinline__ void lds_read_stage(const uint32_t (&addr)[N], u32x4_
   }
 }
 
+// The wait before reading ring stage s of the tail: stage s must have
+// landed, while the kRing - 1 - s stages issued after it may still be in
+// flight (s_waitcnt vmcnt(kPerStage * (kRing - 1 - s))). s is a constant once
+// the tail loop is unrolled, so the switch folds to one wait.
+template <int kPerStage, int kRing>
+__device__ __forceinline__ void wait_stage(int s) {
+  static_assert(kRing >= 1 && kRing <= 8, "tail waits cover rings of 1 to 8 stages");
+  switch (s) {
+    case 0: wait_vmcnt<kPerStage * (kRing - 1)>(); break;
+    case 1: if constexpr (kRing > 1) wait_vmcnt<kPerStage * (kRing - 2)>(); break;
+    case 2: if constexpr (kRing > 2) wait_vmcnt<kPerStage * (kRing - 3)>(); break;
+    case 3: if constexpr (kRing > 3) wait_vmcnt<kPerStage * (kRing - 4)>(); break;
+    case 4: if constexpr (kRing > 4) wait_vmcnt<kPerStage * (kRing - 5)>(); break;
+    case 5: if constexpr (kRing > 5) wait_vmcnt<kPerStage * (kRing - 6)>(); break;
+    case 6: if constexpr (kRing > 6) wait_vmcnt<kPerStage * (kRing - 7)>(); break;
+    case 7: if constexpr (kRing > 7) wait_vmcnt<kPerStage * (kRing - 8)>(); break;
+    default: break;
+  }
+}
+
 __device__ __forceinline__ uint32_t word(const u32x4_t& v, int w) {
   return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
 }
@@ -827,10 +847,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   for (int s = 0; s < kRing; ++s) {
     const int g = g0 + s;
     u32x4_t kr[L], vr[L];
-    if (s == 0) wait_vmcnt<kPerStage * (kRing - 1)>();
-    if (s == 1) wait_vmcnt<kPerStage * (kRing >= 2 ? kRing - 2 : 0)>();
-    if (s == 2) wait_vmcnt<kPerStage * (kRing >= 3 ? kRing - 3 : 0)>();
-    if (s == 3) wait_vmcnt<kPerStage * (kRing >= 4 ? kRing - 4 : 0)>();
+    wait_stage<kPerStage, kRing>(s);
     if (g < ngroups) {
       read_stage(s, kr, vr);
       consume(kr, vr, true, g * 8 + tg < ntok);

@@ -320,3 +320,14 @@ def test_binding_refuses_bad_buffers():
     fb.decode(q, k, v, p)
     fb.prefill(qp, kp, vp, pp)
     torch.cuda.synchronize()
+
+
+def test_fp8_tails_of_five_to_eight_steps():
+    """The fp8 variant keeps 8 steps in flight; a chunk whose last ragged
+    stretch spans 5..8 steps reads ring stages 4..7 in the tail pass, each
+    only after its own loads have landed (lengths 37 .. 127 tokens, one item
+    per request, and the same cut into 40-token chunks)."""
+    lens = [37, 45, 53, 61, 63, 100, 109, 127]
+    for fixed in (0, 40):
+        w = random_workload(61, len(lens), 0, 8, 2, 128, 16, "fp8", lens=lens)
+        run_case(w, what=f"fp8-tails fixed={fixed}", fixed_chunk_tokens=fixed)
