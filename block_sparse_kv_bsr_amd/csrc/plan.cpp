@@ -12,8 +12,11 @@
 // a budget of (compute units x items per CU); a request of n pages is cut into
 // k = ceil(n / C) chunks of near-equal page counts. Units are ordered longest
 // first -- the longest-processing-time rule -- so that the hardware dispatcher,
-// which starts workgroups in grid order as slots free up, places long chunks
-// first and short requests into the gaps. Requests cut into several chunks
+// which starts workgroups in grid order, places long chunks first and short
+// requests into the gaps; and since it hands consecutive workgroups to the
+// CUs in turn, every other layer of num_cus units is reversed (a snake
+// order), so a CU that took a layer's longest unit takes the next layer's
+// shortest. Requests cut into several chunks
 // write partial (output, log-sum-exp) states; per KV head a small tree of
 // merge nodes (fan-in FI_MERGE_FAN_IN) combines them inside the same kernel.
 //
@@ -390,6 +393,14 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
         return a.f[FI_ITEM_KV_HEAD] < b.f[FI_ITEM_KV_HEAD];
       return a.f[FI_ITEM_CHUNK] < b.f[FI_ITEM_CHUNK];
     });
+    // snake: layers of num_cus units alternate longest-first and
+    // shortest-first (dealt in turn, each CU then sums long and short)
+    {
+      const size_t layer = (size_t)std::max<int64_t>(1, num_cus);
+      for (size_t b0 = layer; b0 < items.size(); b0 += 2 * layer)
+        std::reverse(items.begin() + (std::ptrdiff_t)b0,
+                     items.begin() + (std::ptrdiff_t)std::min(items.size(), b0 + layer));
+    }
     p->items.resize(items.size() * FI_ITEM_STRIDE);
     for (size_t i = 0; i < items.size(); ++i)
       std::memcpy(&p->items[i * FI_ITEM_STRIDE], items[i].f, sizeof(items[i].f));

@@ -217,7 +217,10 @@ enum {
  * if even the longest request's full length exceeds that budget), capped by
  * max_chunk_tokens. Items are ordered longest first (ties by request, KV
  * head, chunk) so that long chunks start early and short requests fill the
- * gaps. The input arrays are copied; the caller may free them afterwards.
+ * gaps, except that every other layer of num_cus items is reversed (a snake
+ * order: the dispatcher deals consecutive workgroups to the CUs in turn, so a
+ * CU that takes one layer's longest item takes the next layer's shortest).
+ * The input arrays are copied; the caller may free them afterwards.
  *
  * Shared prefixes (composable block-sparse formats, explainer's Block-Sparse
  * section; cascade attention): for bf16, requests whose page lists begin with

@@ -42,7 +42,7 @@ def prefix_layout(w, p):
     return pre, cpre, base
 
 
-def check_plan(w, p):
+def check_plan(w, p, num_cus=256):
     """Every property a valid plan must have; returns (items, nodes)."""
     info = p.info
     items, nodes = p.work_list(), p.merge_nodes()
@@ -52,9 +52,14 @@ def check_plan(w, p):
     assert nodes.shape[1] == NODE_STRIDE and info["num_merge_nodes"] == len(nodes)
     assert info["num_prefix_items"] == len(pitems)
     assert info["total_kv_tokens"] == int(w.kv_lens().sum())
-    # longest first, ties by (request, kv head, chunk)
+    # longest first, ties by (request, kv head, chunk), every other layer of
+    # num_cus items reversed (snake)
     keys = [(-r[I_NTOK], r[I_REQ], r[I_KVH], r[I_CHUNK]) for r in items]
-    assert keys == sorted(keys)
+    ref = sorted(keys)
+    layer = max(1, num_cus)
+    for k, b0 in enumerate(range(0, len(keys), layer)):
+        want = ref[b0:b0 + layer]
+        assert keys[b0:b0 + layer] == (want if k % 2 == 0 else want[::-1]), k
     S = info["num_partial_slots"]
     fed = np.zeros(S, dtype=np.int64)   # producers per partial slot
     dyn = np.zeros(S, dtype=np.int64)   # producers that report during the decode kernel
@@ -182,7 +187,7 @@ def test_config_plans(cfg):
 def test_plan_properties(seed, batch, max_len, P, hkv, empty, items_per_cu, num_cus, min_chunk):
     w = random_workload(seed, batch, max_len, 4 * hkv, hkv, 64, P, "bf16", empty_every=empty)
     p = make_plan(w, num_cus=num_cus, items_per_cu=items_per_cu, min_chunk_tokens=min_chunk)
-    check_plan(w, p)
+    check_plan(w, p, num_cus=num_cus or 256)
 
 
 @pytest.mark.parametrize("fixed", [1, 16, 48, 100])
