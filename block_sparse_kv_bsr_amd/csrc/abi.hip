@@ -10,6 +10,7 @@
 #include "fi_bsr.h"
 #include "kernels.h"
 #include "plan.h"
+#include "staging.h"
 
 namespace {
 
@@ -24,8 +25,8 @@ fi_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Copies a plan's host image into the workspace through a pinned staging
-// copy the plan keeps (allocated on first use).
+// Copies a plan's host image into the workspace, asynchronously on `stream`,
+// through a cached pinned staging block.
 template <class Plan>
 fi_status upload(Plan* plan, void* workspace, size_t workspace_bytes, fi_stream_t stream) {
   if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
@@ -34,32 +35,16 @@ fi_status upload(Plan* plan, void* workspace, size_t workspace_bytes, fi_stream_
   if ((int64_t)workspace_bytes < plan->ws.total_bytes)
     return fail(FI_ERR_WORKSPACE, "workspace smaller than the plan's workspace_bytes (" +
                                       std::to_string(plan->ws.total_bytes) + ")");
-  const size_t n = plan->image.size();
-  if (n > 0) {
-    if (!plan->pinned) {
-      void* h = nullptr;
-      hipError_t e = hipHostMalloc(&h, n, hipHostMallocDefault);
-      if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
-      std::memcpy(h, plan->image.data(), n);
-      plan->pinned = h;
-    }
-    hipError_t e = hipMemcpyAsync(workspace, plan->pinned, n, hipMemcpyHostToDevice,
-                                  static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
-  }
+  const hipError_t e = fi::staged_upload(workspace, plan->image.data(), plan->image.size(),
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "plan upload");
   plan->uploaded_to = workspace;
   return FI_OK;
 }
 
 template <class Plan>
 void destroy(Plan* plan) {
-  if (!plan) return;
-  if (plan->pinned) {
-    // uploads from the staging copy may still be in flight
-    (void)hipDeviceSynchronize();
-    (void)hipHostFree(plan->pinned);
-  }
-  fi::plan_free_host(plan);
+  if (plan) fi::plan_free_host(plan);
 }
 
 }  // namespace

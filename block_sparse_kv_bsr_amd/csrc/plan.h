@@ -56,7 +56,6 @@ struct fi_plan {
   std::vector<uint8_t> image;   // host copy of the uploaded part of the workspace
   fi::WorkspaceLayout ws;
   // Set by the launch layer.
-  void* pinned = nullptr;        // pinned staging copy of `image`
   const void* uploaded_to = nullptr;
   int64_t num_items() const { return (int64_t)items.size() / FI_ITEM_STRIDE; }
   int64_t num_nodes() const { return (int64_t)nodes.size() / FI_NODE_STRIDE; }
@@ -78,14 +77,13 @@ struct fi_prefill_plan {
     int64_t image_bytes = 0, total_bytes = 0;
   } ws;
   std::vector<uint8_t> image;
-  void* pinned = nullptr;
   const void* uploaded_to = nullptr;
   int64_t num_items() const { return (int64_t)items.size() / FI_QITEM_STRIDE; }
   int64_t num_merges() const { return (int64_t)merges.size() / FI_QMERGE_STRIDE; }
 };
 
 namespace fi {
-// Frees the host parts of a plan (the launch layer frees `pinned` first).
+// Frees a plan (host memory only).
 void plan_free_host(fi_plan* p);
 void plan_free_host(fi_prefill_plan* p);
 

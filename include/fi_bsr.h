@@ -42,10 +42,13 @@
  *
  * Ownership. The caller owns every device buffer (q, pages, out, lse and the
  * workspace). The library allocates no device memory. A plan owns host
- * memory only (its work list and a pinned staging copy) and is immutable
- * after fi_plan_create except for the record of which workspace it was last
- * uploaded to. No call synchronises a stream or the device except
- * fi_plan_destroy (releasing pinned host memory waits for the device).
+ * memory only (its work list) and is immutable after fi_plan_create except
+ * for the record of which workspace it was last uploaded to. Uploads stage
+ * through page-locked host blocks that the library pins on first need and
+ * keeps for the life of the process (one per upload in flight, sized to the
+ * plan image rounded up to a power of two, 64 KiB at least); a block is
+ * reused once the copy it fed has run. No call synchronises a stream or the
+ * device.
  *
  * Errors. Every call returns an fi_status; on failure nothing is launched,
  * the outputs are untouched, and fi_last_error() returns a message for the
@@ -253,10 +256,12 @@ fi_status fi_plan_prefix_members(const fi_plan* plan, const int32_t** members, i
 /*
  * Copy the work list, merge nodes (with their arrival counters set to 0) and
  * page ids into the caller's device
- * workspace (asynchronous host-to-device copy on `stream` from pinned host
- * memory owned by the plan). workspace must be 256-byte aligned and at least
- * info.workspace_bytes long. Call once per plan; the uploaded plan may then
- * serve any number of fi_decode_run calls (e.g. every layer of a step).
+ * workspace (asynchronous host-to-device copy on `stream` from a cached
+ * page-locked staging block; the plan may be destroyed right after).
+ * workspace must be 256-byte aligned and at least info.workspace_bytes long.
+ * Call once per plan; the uploaded plan may then serve any number of
+ * fi_decode_run calls (e.g. every layer of a step). Uploading is not meant
+ * for stream capture: capture the runs, not the upload.
  */
 fi_status fi_plan_upload(fi_plan* plan, void* workspace, size_t workspace_bytes,
                          fi_stream_t stream);
@@ -334,8 +339,8 @@ fi_status fi_merge_states(fi_dtype dtype, const void* v_a, const float* s_a,
                           const void* v_b, const float* s_b, void* v_out, float* s_out,
                           int64_t num_rows, int32_t head_dim, fi_stream_t stream);
 
-/* Free a plan (NULL is ignored). Waits for the device if the plan holds
- * pinned staging memory, so uploads in flight finish first. */
+/* Free a plan (NULL is ignored). Host memory only; does not wait for the
+ * device (an upload in flight keeps its own staging block). */
 void fi_plan_destroy(fi_plan* plan);
 
 /* ======================================================================
@@ -470,7 +475,7 @@ fi_status fi_prefill_plan_merges(const fi_prefill_plan* plan, const int32_t** me
 
 /* Copy items, merges and page ids into the caller's device workspace
  * (256-byte aligned, at least info.workspace_bytes), asynchronously on
- * `stream` from pinned memory the plan owns. */
+ * `stream` through a cached page-locked staging block, as fi_plan_upload. */
 fi_status fi_prefill_plan_upload(fi_prefill_plan* plan, void* workspace, size_t workspace_bytes,
                                  fi_stream_t stream);
 
@@ -489,8 +494,7 @@ fi_status fi_prefill_run(const fi_prefill_plan* plan, const void* q, const void*
                          const void* v_pages, void* out, float* lse, float sm_scale,
                          void* workspace, size_t workspace_bytes, fi_stream_t stream);
 
-/* Free a prefill plan (NULL is ignored); waits for the device if it holds
- * pinned staging memory. */
+/* Free a prefill plan (NULL is ignored); host memory only, no wait. */
 void fi_prefill_plan_destroy(fi_prefill_plan* plan);
 
 /* Message of the last failed call on this thread ("" if none). */

@@ -331,3 +331,43 @@ def test_fp8_tails_of_five_to_eight_steps():
     for fixed in (0, 40):
         w = random_workload(61, len(lens), 0, 8, 2, 128, 16, "fp8", lens=lens)
         run_case(w, what=f"fp8-tails fixed={fixed}", fixed_chunk_tokens=fixed)
+
+
+def test_back_to_back_uploads_through_the_staging_cache():
+    """Plan uploads stage through page-locked blocks the library caches for the
+    process and reuses once their copies have run. Plans whose images fall in
+    different size classes (64 KiB to 512 KiB) are uploaded back to back on
+    one stream with no wait, each followed by a plan that is uploaded and
+    destroyed at once; every surviving plan's decode must then match the
+    oracle, and uploading the same plans again (now through reclaimed
+    blocks) must give bit-identical results."""
+    shapes = [(3, 200, 16), (4, 20000, 1), (2, 60000, 1), (5, 900, 4)]
+    cases = []
+    for i, (B, L, P) in enumerate(shapes):
+        w = random_workload(300 + i, B, L, 8, 2, 128, P, "bf16")
+        q, k, v = (t.cuda() for t in w.make_values("cpu"))
+        p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, 8, 2, 128, P,
+                    w.num_pool_pages, "bf16")
+        cases.append((w, (q, k, v), p))
+    log("[case] staging: workspace bytes", [p.info["workspace_bytes"] for _, _, p in cases])
+    results = []
+    for rnd in range(2):
+        torch.cuda.synchronize()
+        for w, _, p in cases:
+            p.upload(torch.empty(max(256, p.info["workspace_bytes"]), dtype=torch.uint8,
+                                 device="cuda"))
+            other = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, 8, 2, 128, w.page_size,
+                            w.num_pool_pages, "bf16", fixed_chunk_tokens=64)
+            other.upload(torch.empty(max(256, other.info["workspace_bytes"]),
+                                     dtype=torch.uint8, device="cuda"))
+            del other
+        outs = [fb.decode(q, k, v, p) for _, (q, k, v), p in cases]
+        torch.cuda.synchronize()
+        results.append(outs)
+    for (w, (q, k, v), p), (o1, l1), (o2, l2) in zip(cases, results[0], results[1]):
+        qh, kh, vh = host_values(w, q, k, v)
+        O, LSE = oa.decode_attention(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len,
+                                     w.sm_scale)
+        compare(o1.double().cpu().numpy(), l1.double().cpu().numpy(), O, LSE, True, "staging")
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    log("[ok] staging")
