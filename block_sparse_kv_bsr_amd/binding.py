@@ -34,7 +34,7 @@ EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_
             "fi_decode_run_scaled", "fi_merge_states", "fi_plan_destroy", "fi_last_error",
             "fi_prefill_plan_create", "fi_prefill_plan_get_info", "fi_prefill_plan_work_list",
             "fi_prefill_plan_merges", "fi_prefill_plan_upload", "fi_prefill_run",
-            "fi_prefill_plan_destroy", "fi_decode_run_rope"]
+            "fi_prefill_plan_destroy", "fi_decode_run_rope", "fi_decode_run_rope_scaled"]
 QITEM_STRIDE = 12
 QMERGE_STRIDE = 8
 PREFILL_ROWS = 256
@@ -121,6 +121,9 @@ def lib() -> ctypes.CDLL:
     L.fi_decode_run_scaled.restype = i32
     L.fi_decode_run_rope.argtypes = [vp, vp, vp, vp, f32, f32, vp, vp, f32, vp, sz, vp]
     L.fi_decode_run_rope.restype = i32
+    L.fi_decode_run_rope_scaled.argtypes = [vp, vp, vp, vp, f32, f32, f32, f32, vp, vp, f32, vp,
+                                            sz, vp]
+    L.fi_decode_run_rope_scaled.restype = i32
     L.fi_merge_states.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, vp]
     L.fi_merge_states.restype = i32
     L.fi_plan_destroy.argtypes = [vp]
@@ -335,7 +338,7 @@ def decode(q, k_pages, v_pages, plan_: Plan, out=None, lse=None, sm_scale: Optio
     """fi_decode_run_scaled: returns (out [B, H_q, d] in q's dtype, lse [B, H_q]
     float32). k_scale / v_scale dequantise an fp8 KV cache. With rope_theta
     set, K (and q) hold values before the rotary embedding and the kernel
-    applies it (fi_decode_run_rope)."""
+    applies it (fi_decode_run_rope_scaled)."""
     out, lse, workspace = _decode_args(q, k_pages, v_pages, plan_, out, lse, workspace, stream)
     s = ctypes.c_void_p(_stream(stream))
     ws = ctypes.c_void_p(workspace.data_ptr())
@@ -343,12 +346,11 @@ def decode(q, k_pages, v_pages, plan_: Plan, out=None, lse=None, sm_scale: Optio
     o, l = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr())
     scale = float(sm_scale) if sm_scale else 0.0
     if rope_theta:
-        if k_scale != 1.0 or v_scale != 1.0:
-            raise ValueError("the rotary embedding runs without dequantisation scales")
-        _check(lib().fi_decode_run_rope(plan_.handle, ctypes.c_void_p(q.data_ptr()),
-                                        ctypes.c_void_p(k_pages.data_ptr()),
-                                        ctypes.c_void_p(v_pages.data_ptr()), float(rope_theta),
-                                        float(rope_scale), o, l, scale, ws, nbytes, s))
+        _check(lib().fi_decode_run_rope_scaled(plan_.handle, ctypes.c_void_p(q.data_ptr()),
+                                               ctypes.c_void_p(k_pages.data_ptr()),
+                                               ctypes.c_void_p(v_pages.data_ptr()), float(k_scale),
+                                               float(v_scale), float(rope_theta),
+                                               float(rope_scale), o, l, scale, ws, nbytes, s))
         return out, lse
     _check(lib().fi_decode_run_scaled(plan_.handle, ctypes.c_void_p(q.data_ptr()),
                                       ctypes.c_void_p(k_pages.data_ptr()),

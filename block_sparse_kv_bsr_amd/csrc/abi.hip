@@ -219,16 +219,20 @@ fi_status fi_decode_run_scaled(const fi_plan* plan, const void* q, const void* k
                     static_cast<hipStream_t>(stream));
 }
 
-fi_status fi_decode_run_rope(const fi_plan* plan, const void* q, const void* k_pages,
-                             const void* v_pages, float rope_theta, float rope_scale, void* out,
-                             float* lse, float sm_scale, void* workspace, size_t workspace_bytes,
-                             fi_stream_t stream) {
+fi_status fi_decode_run_rope_scaled(const fi_plan* plan, const void* q, const void* k_pages,
+                                    const void* v_pages, float k_scale, float v_scale,
+                                    float rope_theta, float rope_scale, void* out, float* lse,
+                                    float sm_scale, void* workspace, size_t workspace_bytes,
+                                    fi_stream_t stream) {
   if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
-  if (plan->dtype != FI_DTYPE_BF16 || plan->head_dim != 128)
-    return fail(FI_ERR_UNSUPPORTED, "the rotary embedding is built for bf16 plans with head_dim 128");
+  if ((plan->dtype != FI_DTYPE_BF16 && plan->dtype != FI_DTYPE_FP8_E4M3) || plan->head_dim != 128)
+    return fail(FI_ERR_UNSUPPORTED,
+                "the rotary embedding is built for bf16 and fp8 plans with head_dim 128");
   if (plan->num_pitems() > 0)
     return fail(FI_ERR_UNSUPPORTED,
                 "the rotary embedding does not run with shared-prefix items; plan with cascade = -1");
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || std::isinf(k_scale) || std::isinf(v_scale))
+    return fail(FI_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (std::isnan(rope_theta) || std::isinf(rope_theta) || std::isnan(rope_scale) ||
       std::isinf(rope_scale))
     return fail(FI_ERR_INVALID_ARG, "rope_theta and rope_scale must be finite");
@@ -242,8 +246,16 @@ fi_status fi_decode_run_rope(const fi_plan* plan, const void* q, const void* k_p
   if (st != FI_OK) return st;
   st = check_run(plan, out, lse, workspace, workspace_bytes);
   if (st != FI_OK) return st;
-  return launch_run(plan, q, k_pages, v_pages, 1.f, 1.f, out, lse, sm_scale, workspace,
+  return launch_run(plan, q, k_pages, v_pages, k_scale, v_scale, out, lse, sm_scale, workspace,
                     static_cast<hipStream_t>(stream), r);
+}
+
+fi_status fi_decode_run_rope(const fi_plan* plan, const void* q, const void* k_pages,
+                             const void* v_pages, float rope_theta, float rope_scale, void* out,
+                             float* lse, float sm_scale, void* workspace, size_t workspace_bytes,
+                             fi_stream_t stream) {
+  return fi_decode_run_rope_scaled(plan, q, k_pages, v_pages, 1.f, 1.f, rope_theta, rope_scale,
+                                   out, lse, sm_scale, workspace, workspace_bytes, stream);
 }
 
 fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,

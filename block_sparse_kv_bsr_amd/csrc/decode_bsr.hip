@@ -134,6 +134,7 @@ __device__ __forceinline__ uint4 load16(const char* p) {
 }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void global_void_t;
 
@@ -175,6 +176,19 @@ __device__ __forceinline__ void lds_read_stage(const uint32_t (&addr)[N], u32x4_
                  : "+v"(out[0]), "+v"(out[1]), "+v"(out[2]), "+v"(out[3]), "+v"(out[4]),
                    "+v"(out[5]), "+v"(out[6]), "+v"(out[7])::"memory");
   }
+}
+
+// The rotary embedding over an fp8 cache: this lane's rotate-half pairs are
+// bytes 8 sub .. 8 sub + 7 and 64 + 8 sub .. of its token's 128-byte K row
+// (two 8-byte reads at `ak` and ak + 64), packed as (x, y) = first half,
+// (z, w) = second half; its V chunk is read as usual.
+__device__ __forceinline__ void lds_read_k_halves(uint32_t ak, uint32_t av, u32x4_t& k, u32x4_t& v) {
+  u32x2_t a, b;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(a) : "v"(ak) : "memory");
+  asm volatile("ds_read_b64 %0, %1 offset:64" : "=v"(b) : "v"(ak) : "memory");
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(av) : "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(v) :: "memory");
+  k = u32x4_t{a.x, a.y, b.x, b.y};
 }
 
 // The wait before reading ring stage s of the tail: stage s must have
@@ -451,7 +465,7 @@ struct Tune {
 template <int kKv, int D, int G, int kRing, int kWaves, bool kStream, bool kUniform, bool kRope>
 __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) {
   using R = Row<kKv, D>;
-  static_assert(!kRope || (kKv == 2 && D == 128), "the rotary embedding is built for bf16, d 128");
+  static_assert(!kRope || (kKv <= 2 && D == 128), "the rotary embedding is built for bf16 and fp8, d 128");
   constexpr int L = R::kLoads;
   constexpr int NW = R::kWords;
   constexpr int NE = R::kElems;
@@ -514,8 +528,12 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
     for (int j = 0; j < L; ++j) {
 #pragma unroll
       for (int x = 0; x < R::kQLoads; ++x) {
-        const int dim = j * R::kDimStride + sub * R::kPerLoad;
-        const uint4 v = load16(p.q + (qrow0 + h) * R::kBytes + dim * R::kQoBytes + x * 16);
+        // the rotary embedding over an fp8 cache takes the K rows' halves
+        // (dims 8 sub .. 8 sub + 7 and 64 + 8 sub ..), and q the same dims
+        const int off = (kRope && kKv == 1)
+                            ? (x * (D / 2) + sub * 8) * R::kQoBytes
+                            : (j * R::kDimStride + sub * R::kPerLoad) * R::kQoBytes + x * 16;
+        const uint4 v = load16(p.q + (qrow0 + h) * R::kBytes + off);
         const int w0 = (j * R::kQLoads + x) * 4;
         qw[h][w0 + 0] = v.x;
         qw[h][w0 + 1] = v.y;
@@ -526,8 +544,9 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   }
 
   // ---- rotary embedding (K stored before it): lane `sub` holds dims
-  // 8 sub + e and 64 + 8 sub + e (e < 8) of q and of every K row, which are
-  // exactly the rotate-half pairs i = 8 sub + e. Pair i's frequency, as a
+  // 8 sub + e and 64 + 8 sub + e (e < 8) of q and of every K row (a bf16
+  // row's two 16-byte chunks; an fp8 row is read back from LDS as two 8-byte
+  // halves), which are exactly the rotate-half pairs i = 8 sub + e. Pair i's frequency, as a
   // 64-bit fraction of a revolution per position, goes to LDS (lane i
   // computes it in double precision); q turns at the query position here,
   // K rows as they are read (consume).
@@ -650,6 +669,12 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   };
 
   auto read_stage = [&](int stage, u32x4_t (&kr)[L], u32x4_t (&vr)[L]) {
+    if constexpr (kRope && kKv == 1) {
+      // K row of this lane's token: chunks 8 tg .. 8 tg + 7 of the stage
+      lds_read_k_halves(lds_addr(&s_ring[stage][0][8 * tg]) + 8 * sub,
+                        lds_addr(&s_ring[stage][1][lane]), kr[0], vr[0]);
+      return;
+    }
     uint32_t addr[2 * L];
     u32x4_t v[2 * L];
 #pragma unroll
@@ -684,11 +709,35 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
       float d[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) d[h] = 0.f;
+      // pair e of this lane: x1 = dim 8 sub + e, x2 = dim 64 + 8 sub + e
+      float x1v[8], x2v[8];
+      if constexpr (kKv == 1) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f32x2_t a0 = __builtin_amdgcn_cvt_pk_f32_fp8(word(kr[0], u), false);
+          const f32x2_t a1 = __builtin_amdgcn_cvt_pk_f32_fp8(word(kr[0], u), true);
+          const f32x2_t b0 = __builtin_amdgcn_cvt_pk_f32_fp8(word(kr[0], 2 + u), false);
+          const f32x2_t b1 = __builtin_amdgcn_cvt_pk_f32_fp8(word(kr[0], 2 + u), true);
+          x1v[4 * u] = a0[0];
+          x1v[4 * u + 1] = a0[1];
+          x1v[4 * u + 2] = a1[0];
+          x1v[4 * u + 3] = a1[1];
+          x2v[4 * u] = b0[0];
+          x2v[4 * u + 1] = b0[1];
+          x2v[4 * u + 2] = b1[0];
+          x2v[4 * u + 3] = b1[1];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t w1 = word(kr[0], e >> 1), w2 = word(kr[1], e >> 1);
+          x1v[e] = (e & 1) ? bf16_hi(w1) : bf16_lo(w1);
+          x2v[e] = (e & 1) ? bf16_hi(w2) : bf16_lo(w2);
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t w1 = word(kr[0], e >> 1), w2 = word(kr[1], e >> 1);
-        const float x1 = (e & 1) ? bf16_hi(w1) : bf16_lo(w1);
-        const float x2 = (e & 1) ? bf16_hi(w2) : bf16_lo(w2);
+        const float x1 = x1v[e], x2 = x2v[e];
         const float k1 = x1 * rc[e] - x2 * rs[e];
         const float k2 = x2 * rc[e] + x1 * rs[e];
 #pragma unroll
@@ -1046,6 +1095,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.rope) {
     if (a.kv_bytes == 2 && a.head_dim == 128)
       return launch_group<2, 128, true>(prm, a.num_items, a.group, a.stream_kv, stream);
+    if (a.kv_bytes == 1 && a.head_dim == 128)
+      return launch_group<1, 128, true>(prm, a.num_items, a.group, a.stream_kv, stream);
     return hipErrorInvalidValue;
   }
   if (a.kv_bytes == 2) {

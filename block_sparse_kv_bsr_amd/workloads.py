@@ -50,6 +50,8 @@ CONFIG_NAMES = {
     8: "append_b64_q128_skewed",
     # the skewed batch over a K cache that holds keys before the rotary embedding
     9: "skewed_b64_loguniform_32_32768_rope",
+    # the same over an fp8 KV cache
+    10: "skewed_b64_loguniform_32_32768_fp8kv_rope",
 }
 
 # Rotary embedding base of the rope workload (the Llama-3 value).
@@ -361,6 +363,10 @@ def workload(config_id: int) -> Workload:
         w = workload(3)
         return dataclasses.replace(w, name=CONFIG_NAMES[9], config_id=9, value_seed=seed,
                                    rope_theta=ROPE_THETA)
+    if config_id == 10:  # the skewed batch over an fp8 cache of keys before the embedding
+        w = workload(6)
+        return dataclasses.replace(w, name=CONFIG_NAMES[10], config_id=10,
+                                   value_seed=seed, rope_theta=ROPE_THETA)
     if config_id == 6:  # the skewed batch over an fp8 KV cache
         w = workload(3)
         return dataclasses.replace(w, name=CONFIG_NAMES[6], config_id=6, dtype="fp8",

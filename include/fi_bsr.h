@@ -311,15 +311,29 @@ fi_status fi_decode_run_scaled(const fi_plan* plan, const void* q, const void* k
  * the angle (pos / rope_scale) * rope_theta^(-2i / head_dim); token t of a
  * request (0-based, listed order) is at position t, the query at position
  * L_b - 1 (it is the request's newest token, whose K is already cached).
- * q is given before the embedding too. bf16 plans with head_dim 128 and no
- * shared-prefix items (create the plan with opts.cascade = -1); else
- * FI_ERR_UNSUPPORTED. rope_theta <= 0 selects 10000, rope_scale <= 0
- * selects 1. Other arguments as fi_decode_run.
+ * q is given before the embedding too. bf16 or FI_DTYPE_FP8_E4M3 plans
+ * with head_dim 128 and no shared-prefix items (create the plan with
+ * opts.cascade = -1); else FI_ERR_UNSUPPORTED. rope_theta <= 0 selects
+ * 10000, rope_scale <= 0 selects 1. Other arguments as fi_decode_run. This
+ * is fi_decode_run_rope_scaled with both scales 1.
  */
 fi_status fi_decode_run_rope(const fi_plan* plan, const void* q, const void* k_pages,
                              const void* v_pages, float rope_theta, float rope_scale, void* out,
                              float* lse, float sm_scale, void* workspace, size_t workspace_bytes,
                              fi_stream_t stream);
+
+/*
+ * fi_decode_run_rope over a quantised cache: K and V elements count as
+ * k_scale and v_scale times their stored values, as in fi_decode_run_scaled
+ * (the embedding turns the dequantised keys; a scale commutes with the
+ * rotation). Scales must be finite and positive. Other arguments and limits
+ * as fi_decode_run_rope.
+ */
+fi_status fi_decode_run_rope_scaled(const fi_plan* plan, const void* q, const void* k_pages,
+                                    const void* v_pages, float k_scale, float v_scale,
+                                    float rope_theta, float rope_scale, void* out, float* lse,
+                                    float sm_scale, void* workspace, size_t workspace_bytes,
+                                    fi_stream_t stream);
 
 /*
  * Merge two attention states over disjoint token sets (the closed form of
