@@ -72,6 +72,23 @@ def test_graph_decode_with_split_requests():
              [torch.randn_like(q)], "decode")
 
 
+def test_graph_decode_rope_over_fp8_cache():
+    """The rotary-embedding variant over an fp8 cache with dequantisation
+    scales, requests cut into chunks at nonzero positions."""
+    w = random_workload(104, 5, 2000, 32, 8, 128, 16, "fp8")
+    q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, 32, 8, 128, 16, w.num_pool_pages, "fp8",
+                fixed_chunk_tokens=192, cascade=-1)
+    assert p.info["num_merge_nodes"] > 0
+    ws = torch.empty(p.info["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    p.upload(ws)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    _replays(lambda: fb.decode(q, k, v, p, out=out, lse=lse, workspace=ws, k_scale=w.k_scale,
+                               v_scale=w.v_scale, rope_theta=5e5), [q], [out, lse],
+             [torch.randn_like(q)], "decode rope fp8")
+
+
 def test_graph_decode_cascade():
     w = prefix_workload(102, [(6, 6)], 3, 300, 32, 8, 128, 16, "bf16")
     q, k, v = (t.cuda() for t in w.make_values("cpu"))
