@@ -154,20 +154,35 @@ def cpu_baseline(w, q, k, v, min_seconds=10.0, max_passes=3):
         vh = oa.dequantize_e4m3(v.view(torch.uint8).cpu().numpy(), w.v_scale)
     else:
         kh, vh = k.float().cpu().numpy(), v.float().cpu().numpy()
-    times = []
-    while len(times) < max_passes and sum(times) < min_seconds:
-        t0 = time.perf_counter()
+    def run():
         if w.rope_theta:
             oa.decode_attention_rope(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len,
                                      w.sm_scale, w.rope_theta, w.rope_scale)
         else:
             oa.decode_attention(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len, w.sm_scale)
+
+    times = []
+    while len(times) < max_passes and sum(times) < min_seconds:
+        t0 = time.perf_counter()
+        run()
         times.append(time.perf_counter() - t0)
     per = statistics.median(times)
-    return {"value": w.algorithmic_bytes() / per / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "seconds_per_batch": per,
-            "sample": f"whole {w.name} batch ({int(w.kv_lens().sum())} KV tokens), "
-                      f"{len(times)} pass(es), median; numpy float64 on host cores"}
+    res = {"value": w.algorithmic_bytes() / per / 1e9, "unit": "GB/s", "cores": int(threads),
+           "kind": "oracle", "seconds_per_batch": per,
+           "sample": f"whole {w.name} batch ({int(w.kv_lens().sum())} KV tokens), "
+                     f"{len(times)} pass(es), median; numpy float64 on host cores"}
+    # the same oracle held to one host thread, one pass
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        return res
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        run()
+        one = time.perf_counter() - t0
+    res["one_thread"] = {"value": w.algorithmic_bytes() / one / 1e9, "unit": "GB/s",
+                         "seconds_per_batch": one, "cores": 1}
+    return res
 
 
 def cpu_baseline_prefill(w, q, k, v, min_seconds=10.0):

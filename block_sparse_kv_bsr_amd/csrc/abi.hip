@@ -225,9 +225,12 @@ fi_status fi_decode_run_rope_scaled(const fi_plan* plan, const void* q, const vo
                                     float sm_scale, void* workspace, size_t workspace_bytes,
                                     fi_stream_t stream) {
   if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
-  if ((plan->dtype != FI_DTYPE_BF16 && plan->dtype != FI_DTYPE_FP8_E4M3) || plan->head_dim != 128)
+  const bool built = (plan->dtype == FI_DTYPE_BF16 && (plan->head_dim == 128 || plan->head_dim == 64)) ||
+                     (plan->dtype == FI_DTYPE_FP8_E4M3 && plan->head_dim == 128);
+  if (!built)
     return fail(FI_ERR_UNSUPPORTED,
-                "the rotary embedding is built for bf16 and fp8 plans with head_dim 128");
+                "the rotary embedding is built for bf16 plans with head_dim 128 or 64 and fp8 "
+                "plans with head_dim 128");
   if (plan->num_pitems() > 0)
     return fail(FI_ERR_UNSUPPORTED,
                 "the rotary embedding does not run with shared-prefix items; plan with cascade = -1");

@@ -178,10 +178,10 @@ __device__ __forceinline__ void lds_read_stage(const uint32_t (&addr)[N], u32x4_
   }
 }
 
-// The rotary embedding over an fp8 cache: this lane's rotate-half pairs are
-// bytes 8 sub .. 8 sub + 7 and 64 + 8 sub .. of its token's 128-byte K row
-// (two 8-byte reads at `ak` and ak + 64), packed as (x, y) = first half,
-// (z, w) = second half; its V chunk is read as usual.
+// The rotary embedding over 128-byte K rows (fp8 at d 128, bf16 at d 64):
+// this lane's rotate-half pairs are bytes 8 sub .. 8 sub + 7 and 64 + 8 sub
+// .. of its token's row (two 8-byte reads at `ak` and ak + 64), packed as
+// (x, y) = first half, (z, w) = second half; its V chunk is read as usual.
 __device__ __forceinline__ void lds_read_k_halves(uint32_t ak, uint32_t av, u32x4_t& k, u32x4_t& v) {
   u32x2_t a, b;
   asm volatile("ds_read_b64 %0, %1" : "=v"(a) : "v"(ak) : "memory");
@@ -453,8 +453,8 @@ struct Tune {
   // batch.
   static constexpr int kRing = kKv == 1 ? 8 : (kStream ? 2 : 4);
   static_assert(kRing % 2 == 0, "the main loop reads ring stages two at a time");
-  // the rotary embedding keeps q in fp32 (G * kElems) and 4 x 8 rotation terms
-  static constexpr int kRegs = G * R::kElems + (kRope ? G * R::kElems + 32 : G * R::kWords) +
+  // the rotary embedding keeps q in fp32 (G * kElems) and 4 x D/16 rotation terms
+  static constexpr int kRegs = G * R::kElems + (kRope ? G * R::kElems + D / 4 : G * R::kWords) +
                                16 * R::kLoads + 2 * G + 48;
   static constexpr int kByRegs = kRegs <= 168 ? 3 : (kRegs <= 240 ? 2 : 1);
   static constexpr int kLdsPerWave = kRing * 2 * R::kLoads * 1024 + kIdWindow * 4;
@@ -465,8 +465,15 @@ struct Tune {
 template <int kKv, int D, int G, int kRing, int kWaves, bool kStream, bool kUniform, bool kRope>
 __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) {
   using R = Row<kKv, D>;
-  static_assert(!kRope || (kKv <= 2 && D == 128), "the rotary embedding is built for bf16 and fp8, d 128");
+  static_assert(!kRope || (kKv <= 2 && D == 128) || (kKv == 2 && D == 64),
+                "the rotary embedding is built for bf16 (d 128 or 64) and fp8 (d 128)");
   constexpr int L = R::kLoads;
+  // With the rotary embedding a lane holds kPairs rotate-half pairs. Where a
+  // K row is one 128-byte line (fp8 at d 128, bf16 at d 64), the pairs of a
+  // lane sit in two lanes' chunks, and the row is read back from LDS as two
+  // 8-byte halves instead (kHalves).
+  constexpr int kPairs = D / 16;
+  constexpr bool kHalves = kRope && L == 1;
   constexpr int NW = R::kWords;
   constexpr int NE = R::kElems;
 
@@ -528,31 +535,43 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
     for (int j = 0; j < L; ++j) {
 #pragma unroll
       for (int x = 0; x < R::kQLoads; ++x) {
-        // the rotary embedding over an fp8 cache takes the K rows' halves
-        // (dims 8 sub .. 8 sub + 7 and 64 + 8 sub ..), and q the same dims
-        const int off = (kRope && kKv == 1)
-                            ? (x * (D / 2) + sub * 8) * R::kQoBytes
-                            : (j * R::kDimStride + sub * R::kPerLoad) * R::kQoBytes + x * 16;
-        const uint4 v = load16(p.q + (qrow0 + h) * R::kBytes + off);
-        const int w0 = (j * R::kQLoads + x) * 4;
-        qw[h][w0 + 0] = v.x;
-        qw[h][w0 + 1] = v.y;
-        qw[h][w0 + 2] = v.z;
-        qw[h][w0 + 3] = v.w;
+        // the rotary embedding over 128-byte K rows takes the rows' halves
+        // (dims kPairs sub .. + kPairs - 1 and D/2 + kPairs sub ..), and q
+        // the same dims: two 16-byte loads at d 128, two 8-byte ones at d 64
+        if constexpr (kHalves && D == 64) {
+          const char* qr = p.q + (qrow0 + h) * R::kBytes + sub * 8;
+          const uint2 a = *reinterpret_cast<const uint2*>(qr);
+          const uint2 c = *reinterpret_cast<const uint2*>(qr + 64);
+          qw[h][0] = a.x;
+          qw[h][1] = a.y;
+          qw[h][2] = c.x;
+          qw[h][3] = c.y;
+        } else {
+          const int off = kHalves
+                              ? (x * (D / 2) + sub * 8) * R::kQoBytes
+                              : (j * R::kDimStride + sub * R::kPerLoad) * R::kQoBytes + x * 16;
+          const uint4 v = load16(p.q + (qrow0 + h) * R::kBytes + off);
+          const int w0 = (j * R::kQLoads + x) * 4;
+          qw[h][w0 + 0] = v.x;
+          qw[h][w0 + 1] = v.y;
+          qw[h][w0 + 2] = v.z;
+          qw[h][w0 + 3] = v.w;
+        }
       }
     }
   }
 
   // ---- rotary embedding (K stored before it): lane `sub` holds dims
-  // 8 sub + e and 64 + 8 sub + e (e < 8) of q and of every K row (a bf16
-  // row's two 16-byte chunks; an fp8 row is read back from LDS as two 8-byte
-  // halves), which are exactly the rotate-half pairs i = 8 sub + e. Pair i's frequency, as a
-  // 64-bit fraction of a revolution per position, goes to LDS (lane i
-  // computes it in double precision); q turns at the query position here,
-  // K rows as they are read (consume).
+  // kPairs sub + e and D/2 + kPairs sub + e (e < kPairs) of q and of every
+  // K row (a bf16 d-128 row's two 16-byte chunks; a 128-byte row read back
+  // from LDS as two 8-byte halves), which are exactly the rotate-half pairs
+  // i = kPairs sub + e. Pair i's frequency, as a 64-bit fraction of a
+  // revolution per position, goes to LDS (lane i computes it in double
+  // precision); q turns at the query position here, K rows as they are read
+  // (consume). q words: the first kPairs / 2 hold the pairs' first dims.
   __shared__ uint64_t s_freq[kRope ? 64 : 1];
-  float qf[kRope ? G : 1][16];
-  float rc[8], rs[8], dc[8], ds[8];  // this lane's current and per-step rotation
+  float qf[kRope ? G : 1][2 * kPairs];
+  float rc[kPairs], rs[kPairs], dc[kPairs], ds[kPairs];  // current and per-step rotation
   int rope_step = 0;
   int rope_pos0 = 0;
   if constexpr (kRope) {
@@ -563,18 +582,18 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
     const int qpos = it[FI_ITEM_Q_POS];
     rope_pos0 = it[FI_ITEM_KV_POS] + tg;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint64_t f = s_freq[8 * sub + e];
+    for (int e = 0; e < kPairs; ++e) {
+      const uint64_t f = s_freq[kPairs * sub + e];
       float cq, sq;
       rope_sincos(f, qpos, cq, sq);
       rope_sincos(f, 8, dc[e], ds[e]);  // a step advances 8 positions
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const uint32_t w1 = qw[h][e >> 1], w2 = qw[h][4 + (e >> 1)];
+        const uint32_t w1 = qw[h][e >> 1], w2 = qw[h][kPairs / 2 + (e >> 1)];
         const float x1 = (e & 1) ? bf16_hi(w1) : bf16_lo(w1);
         const float x2 = (e & 1) ? bf16_hi(w2) : bf16_lo(w2);
         qf[h][e] = x1 * cq - x2 * sq;
-        qf[h][8 + e] = x2 * cq + x1 * sq;
+        qf[h][kPairs + e] = x2 * cq + x1 * sq;
       }
     }
   }
@@ -669,7 +688,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   };
 
   auto read_stage = [&](int stage, u32x4_t (&kr)[L], u32x4_t (&vr)[L]) {
-    if constexpr (kRope && kKv == 1) {
+    if constexpr (kHalves) {
       // K row of this lane's token: chunks 8 tg .. 8 tg + 7 of the stage
       lds_read_k_halves(lds_addr(&s_ring[stage][0][8 * tg]) + 8 * sub,
                         lds_addr(&s_ring[stage][1][lane]), kr[0], vr[0]);
@@ -704,13 +723,14 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
       // step's rotation in between (error ~ 32 fp32 roundings)
       if ((rope_step & 31) == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rope_sincos(s_freq[8 * sub + e], rope_pos0 + 8 * rope_step, rc[e], rs[e]);
+        for (int e = 0; e < kPairs; ++e)
+          rope_sincos(s_freq[kPairs * sub + e], rope_pos0 + 8 * rope_step, rc[e], rs[e]);
       }
       float d[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) d[h] = 0.f;
-      // pair e of this lane: x1 = dim 8 sub + e, x2 = dim 64 + 8 sub + e
-      float x1v[8], x2v[8];
+      // pair e of this lane: x1 = dim kPairs sub + e, x2 = dim D/2 + kPairs sub + e
+      float x1v[kPairs], x2v[kPairs];
       if constexpr (kKv == 1) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -727,23 +747,30 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
           x2v[4 * u + 2] = b1[0];
           x2v[4 * u + 3] = b1[1];
         }
+      } else if constexpr (kHalves) {  // bf16, d 64: (x, y) first dims, (z, w) second
+#pragma unroll
+        for (int e = 0; e < kPairs; ++e) {
+          const uint32_t w1 = word(kr[0], e >> 1), w2 = word(kr[0], 2 + (e >> 1));
+          x1v[e] = (e & 1) ? bf16_hi(w1) : bf16_lo(w1);
+          x2v[e] = (e & 1) ? bf16_hi(w2) : bf16_lo(w2);
+        }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < kPairs; ++e) {
           const uint32_t w1 = word(kr[0], e >> 1), w2 = word(kr[1], e >> 1);
           x1v[e] = (e & 1) ? bf16_hi(w1) : bf16_lo(w1);
           x2v[e] = (e & 1) ? bf16_hi(w2) : bf16_lo(w2);
         }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < kPairs; ++e) {
         const float x1 = x1v[e], x2 = x2v[e];
         const float k1 = x1 * rc[e] - x2 * rs[e];
         const float k2 = x2 * rc[e] + x1 * rs[e];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           d[h] = __builtin_fmaf(k1, qf[h][e], d[h]);
-          d[h] = __builtin_fmaf(k2, qf[h][8 + e], d[h]);
+          d[h] = __builtin_fmaf(k2, qf[h][kPairs + e], d[h]);
         }
         const float c2 = rc[e] * dc[e] - rs[e] * ds[e];
         rs[e] = rs[e] * dc[e] + rc[e] * ds[e];
@@ -1097,6 +1124,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
       return launch_group<2, 128, true>(prm, a.num_items, a.group, a.stream_kv, stream);
     if (a.kv_bytes == 1 && a.head_dim == 128)
       return launch_group<1, 128, true>(prm, a.num_items, a.group, a.stream_kv, stream);
+    if (a.kv_bytes == 2 && a.head_dim == 64)
+      return launch_group<2, 64, true>(prm, a.num_items, a.group, a.stream_kv, stream);
     return hipErrorInvalidValue;
   }
   if (a.kv_bytes == 2) {

@@ -311,9 +311,9 @@ fi_status fi_decode_run_scaled(const fi_plan* plan, const void* q, const void* k
  * the angle (pos / rope_scale) * rope_theta^(-2i / head_dim); token t of a
  * request (0-based, listed order) is at position t, the query at position
  * L_b - 1 (it is the request's newest token, whose K is already cached).
- * q is given before the embedding too. bf16 or FI_DTYPE_FP8_E4M3 plans
- * with head_dim 128 and no shared-prefix items (create the plan with
- * opts.cascade = -1); else FI_ERR_UNSUPPORTED. rope_theta <= 0 selects
+ * q is given before the embedding too. bf16 plans with head_dim 128 or 64
+ * and FI_DTYPE_FP8_E4M3 plans (head_dim 128), with no shared-prefix items
+ * (create the plan with opts.cascade = -1); else FI_ERR_UNSUPPORTED. rope_theta <= 0 selects
  * 10000, rope_scale <= 0 selects 1. Other arguments as fi_decode_run. This
  * is fi_decode_run_rope_scaled with both scales 1.
  */

@@ -137,12 +137,12 @@ def test_binding_refuses_cpu_tensors():
 
 def test_rope_run_rejects_what_is_not_built():
     """fi_decode_run_rope(_scaled) checks the plan before touching any
-    device: only bf16 and fp8 plans with head_dim 128 and no shared-prefix
-    items, finite parameters, finite positive scales."""
+    device: only bf16 plans (head_dim 128 or 64) and fp8 plans (128) with no
+    shared-prefix items, finite parameters, finite positive scales."""
     L = fb.lib()
     fake = ctypes.c_void_p(0x100000)
     ip, ix, lp = [np.asarray(a) for a in GOOD]
-    for dtype, d in (("f32", 128), ("bf16", 64), ("f32", 64)):
+    for dtype, d in (("f32", 128), ("f32", 64)):
         p = fb.plan(ip, ix, lp, 8, 2, d, 16, 100, dtype)
         st = L.fi_decode_run_rope(p.handle, fake, fake, fake, 1e4, 1.0, fake, None, 0.0, fake,
                                   p.info["workspace_bytes"], None)
@@ -165,6 +165,10 @@ def test_rope_run_rejects_what_is_not_built():
         assert st == -1 and "scale" in L.fi_last_error().decode(), (ks, vs)
     st = L.fi_decode_run_rope_scaled(p8.handle, fake, fake, fake, 0.5, 2.0, 1e4, 1.0, fake, None,
                                      0.0, fake, p8.info["workspace_bytes"], None)
+    assert st == -6
+    p64 = fb.plan(ip, ix, lp, 8, 2, 64, 16, 100, "bf16")
+    st = L.fi_decode_run_rope(p64.handle, fake, fake, fake, 1e4, 1.0, fake, None, 0.0, fake,
+                              p64.info["workspace_bytes"], None)
     assert st == -6
 
 

@@ -1,6 +1,7 @@
-"""GPU parity of decode with the rotary embedding fused into the K gather, over
-bf16 and fp8 caches,
-(fi_decode_run_rope) against the float64 oracle's decode_attention_rope.
+"""GPU parity of decode with the rotary embedding fused into the K gather
+(fi_decode_run_rope / fi_decode_run_rope_scaled), over bf16 caches at
+head_dim 128 and 64 and fp8 caches at 128, against the float64 oracle's
+decode_attention_rope.
 
 The kernel carries each lane's rotation from step to step and recomputes it
 exactly every 32 steps (256 tokens), so the cases run past several
@@ -123,9 +124,30 @@ def test_rope_fp8_skewed_batch_full_size():
     run_rope(w, w.rope_theta, w.rope_scale, "config10-rope-fp8", device_values=True)
 
 
+D64_CASES = [
+    # seed, B, maxL, Hq, Hkv, P, theta, scale, fixed_chunk_tokens
+    (71, 4, 3000, 32, 8, 16, 1e4, 1.0, 0),      # G 4, several exact recomputations
+    (72, 3, 2000, 8, 8, 16, 5e5, 1.0, 512),     # G 1, chunks at nonzero positions
+    (73, 4, 1500, 16, 2, 64, 1e4, 2.0, 0),      # G 8, large pages, position scaling
+    (74, 5, 700, 16, 8, 12, 5e5, 1.0, 96),      # G 2, page size not dividing the step
+    (75, 3, 400, 8, 1, 1, 1e4, 1.0, 0),         # G 8, one token per page
+]
+
+
+@pytest.mark.parametrize("case", D64_CASES, ids=lambda c: f"d64_seed{c[0]}")
+def test_rope_head_dim_64(case):
+    """bf16 at head_dim 64: a K row is one 128-byte line, read back from LDS
+    as two 8-byte halves (4 rotate-half pairs per lane)."""
+    seed, B, L, Hq, Hkv, P, theta, scale, fixed = case
+    w = random_workload(seed, B, L, Hq, Hkv, 64, P, "bf16")
+    p = run_rope(w, theta, scale, f"rope-d64-{seed}", fixed_chunk_tokens=fixed)
+    if fixed:
+        assert p.info["max_chunks_per_request"] > 1
+
+
 def test_rope_rejects_what_is_not_built():
-    w = random_workload(88, 2, 40, 8, 2, 64, 16, "bf16")
+    w = random_workload(88, 2, 40, 8, 2, 64, 16, "f32")
     q, k, v = (t.cuda() for t in w.make_values("cpu"))
-    p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, 8, 2, 64, 16, w.num_pool_pages, "bf16")
-    with pytest.raises(fb.FiError, match="head_dim 128"):
+    p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, 8, 2, 64, 16, w.num_pool_pages, "f32")
+    with pytest.raises(fb.FiError, match="rotary"):
         fb.decode(q, k, v, p, rope_theta=1e4)
