@@ -255,21 +255,24 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
       // requests, or one request twice; a cascade's prefix pages are read by
       // the prefix items instead): a bitmap over the pool when it is not
       // much larger than the page lists, else a sort
-      std::vector<int32_t> ids;
-      ids.reserve((size_t)nnz);
-      for (int32_t b = 0; b < batch; ++b)
-        for (int64_t j = kv_indptr[b] + pre_pages[b]; j < kv_indptr[b + 1]; ++j)
-          ids.push_back(kv_indices[j]);
       if (num_pool_pages <= 64 * nnz + 65536) {
         std::vector<uint64_t> seen((size_t)(num_pool_pages + 63) / 64, 0), twice(seen.size(), 0);
-        for (const int32_t id : ids) {
-          const uint64_t bit = 1ull << (id & 63);
-          uint64_t& w = seen[(size_t)(id >> 6)];
-          if (w & bit) twice[(size_t)(id >> 6)] |= bit;
-          w |= bit;
+        for (int32_t b = 0; b < batch; ++b) {
+          for (int64_t j = kv_indptr[b] + pre_pages[b]; j < kv_indptr[b + 1]; ++j) {
+            const int32_t id = kv_indices[j];
+            const uint64_t bit = 1ull << (id & 63);
+            uint64_t& w = seen[(size_t)(id >> 6)];
+            if (w & bit) twice[(size_t)(id >> 6)] |= bit;
+            w |= bit;
+          }
         }
         for (uint64_t w : twice) p->shared_pages += __builtin_popcountll(w);
       } else {
+        std::vector<int32_t> ids;
+        ids.reserve((size_t)nnz);
+        for (int32_t b = 0; b < batch; ++b)
+          for (int64_t j = kv_indptr[b] + pre_pages[b]; j < kv_indptr[b + 1]; ++j)
+            ids.push_back(kv_indices[j]);
         std::sort(ids.begin(), ids.end());
         for (size_t j = 1; j < ids.size(); ++j)
           if (ids[j] == ids[j - 1] && (j == 1 || ids[j - 1] != ids[j - 2])) ++p->shared_pages;
@@ -279,6 +282,12 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     // ---- items, partial slots, merge trees
     struct Item { int32_t f[FI_ITEM_STRIDE]; };
     std::vector<Item> items;
+    {
+      int64_t n_items = 0;
+      for (int32_t b = 0; b < batch; ++b)
+        n_items += num_kv_heads * std::max<int64_t>(1, dpages[b] > 0 ? fi::ceil_div(dpages[b], C) : 0);
+      items.reserve((size_t)n_items);
+    }
     std::vector<int32_t>& nodes = p->nodes;
     std::vector<int32_t>& pslot = p->prefix_slot;
     if (!groups.empty()) pslot.assign((size_t)batch * num_kv_heads, -1);
@@ -299,6 +308,7 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
       nodes.insert(nodes.end(), f, f + FI_NODE_STRIDE);
       return id;
     };
+    std::vector<int32_t> leaf_node, prev;  // per merge tree, reused
     for (int32_t b = 0; b < batch; ++b) {
       const int64_t n = dpages[b];
       const int64_t pre = pre_pages[b];
@@ -324,13 +334,13 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
         // the k chunk partials, in slots [leaf_base, leaf_base + nchild);
         // each level groups FI_MERGE_FAN_IN children
         const int64_t leaf_base = slot;
-        std::vector<int32_t> leaf_node(nchild, -1);
+        leaf_node.assign((size_t)nchild, -1);
         if (nchild >= 2) {
           slot += nchild;
           if (cpre > 0) pslot[(size_t)b * num_kv_heads + h] = (int32_t)leaf_base;
           int64_t child_begin = leaf_base, nch = nchild;
           int32_t level = 0;
-          std::vector<int32_t> prev;
+          prev.clear();
           for (;;) {
             const int64_t ngroups = fi::ceil_div(nch, FI_MERGE_FAN_IN);
             const bool root = ngroups == 1;
@@ -383,27 +393,24 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
       }
     }
     if (slot > INT32_MAX) return fail(FI_ERR_UNSUPPORTED, "too many partial states");
-    // longest first; ties in (request, KV head, chunk) order
-    std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
-      if (a.f[FI_ITEM_NUM_TOKENS] != b.f[FI_ITEM_NUM_TOKENS])
-        return a.f[FI_ITEM_NUM_TOKENS] > b.f[FI_ITEM_NUM_TOKENS];
-      if (a.f[FI_ITEM_REQUEST] != b.f[FI_ITEM_REQUEST])
-        return a.f[FI_ITEM_REQUEST] < b.f[FI_ITEM_REQUEST];
-      if (a.f[FI_ITEM_KV_HEAD] != b.f[FI_ITEM_KV_HEAD])
-        return a.f[FI_ITEM_KV_HEAD] < b.f[FI_ITEM_KV_HEAD];
-      return a.f[FI_ITEM_CHUNK] < b.f[FI_ITEM_CHUNK];
-    });
+    // longest first; ties in (request, KV head, chunk) order, which is the
+    // order the items were made in: sort 64-bit keys (token count, then
+    // that index) rather than the items themselves
+    std::vector<uint64_t> order(items.size());
+    for (size_t i = 0; i < items.size(); ++i)
+      order[i] = ((uint64_t)(uint32_t)(INT32_MAX - items[i].f[FI_ITEM_NUM_TOKENS]) << 32) | i;
+    std::sort(order.begin(), order.end());
     // snake: layers of num_cus units alternate longest-first and
     // shortest-first (dealt in turn, each CU then sums long and short)
     {
       const size_t layer = (size_t)std::max<int64_t>(1, num_cus);
-      for (size_t b0 = layer; b0 < items.size(); b0 += 2 * layer)
-        std::reverse(items.begin() + (std::ptrdiff_t)b0,
-                     items.begin() + (std::ptrdiff_t)std::min(items.size(), b0 + layer));
+      for (size_t b0 = layer; b0 < order.size(); b0 += 2 * layer)
+        std::reverse(order.begin() + (std::ptrdiff_t)b0,
+                     order.begin() + (std::ptrdiff_t)std::min(order.size(), b0 + layer));
     }
     p->items.resize(items.size() * FI_ITEM_STRIDE);
-    for (size_t i = 0; i < items.size(); ++i)
-      std::memcpy(&p->items[i * FI_ITEM_STRIDE], items[i].f, sizeof(items[i].f));
+    for (size_t i = 0; i < order.size(); ++i)
+      std::memcpy(&p->items[i * FI_ITEM_STRIDE], items[(uint32_t)order[i]].f, sizeof(Item));
     p->num_slots = slot;
     p->max_chunks = max_chunks;
     p->min_chunks_split = min_split;
