@@ -453,11 +453,17 @@ struct Tune {
   // batch.
   static constexpr int kRing = kKv == 1 ? 8 : (kStream ? 2 : 4);
   static_assert(kRing % 2 == 0, "the main loop reads ring stages two at a time");
+  // At G = 8 the query words stay in LDS and are read per head and step
+  // (the 8 lanes of a column read the same 16 bytes, one broadcast): in
+  // registers they would take the wave past 256 and to one wave per SIMD.
+  static constexpr bool kQLds = G == 8 && !kRope && D == 128 && kKv <= 2;
   // the rotary embedding keeps q in fp32 (G * kElems) and 4 x D/16 rotation terms
-  static constexpr int kRegs = G * R::kElems + (kRope ? G * R::kElems + D / 4 : G * R::kWords) +
-                               16 * R::kLoads + 2 * G + 48;
+  static constexpr int kRegs =
+      G * R::kElems + (kRope ? G * R::kElems + D / 4 : (kQLds ? R::kWords : G * R::kWords)) +
+      16 * R::kLoads + 2 * G + 48;
   static constexpr int kByRegs = kRegs <= 168 ? 3 : (kRegs <= 240 ? 2 : 1);
-  static constexpr int kLdsPerWave = kRing * 2 * R::kLoads * 1024 + kIdWindow * 4;
+  static constexpr int kLdsPerWave =
+      kRing * 2 * R::kLoads * 1024 + kIdWindow * 4 + (kQLds ? G * 8 * R::kWords * 4 : 0);
   static constexpr int kByLds = (160 * 1024) / (4 * kLdsPerWave);
   static constexpr int kWaves = kByRegs < kByLds ? kByRegs : (kByLds >= 1 ? kByLds : 1);
 };
@@ -468,6 +474,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
   static_assert(!kRope || (kKv <= 2 && D == 128) || (kKv == 2 && D == 64),
                 "the rotary embedding is built for bf16 (d 128 or 64) and fp8 (d 128)");
   constexpr int L = R::kLoads;
+  constexpr bool kQLds = Tune<kKv, D, G, kStream, kRope>::kQLds;
   // With the rotary embedding a lane holds kPairs rotate-half pairs. Where a
   // K row is one 128-byte line (fp8 at d 128, bf16 at d 64), the pairs of a
   // lane sit in two lanes' chunks, and the row is read back from LDS as two
@@ -559,6 +566,16 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
         }
       }
     }
+  }
+
+  // q words of every head in LDS, [head][sub][word] (see Tune::kQLds)
+  __shared__ __attribute__((aligned(16))) uint32_t s_q[kQLds ? G : 1][8][kQLds ? NW : 1];
+  if constexpr (kQLds) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int w = 0; w < NW; ++w) s_q[h][sub][w] = qw[h][w];
+    __syncthreads();
   }
 
   // ---- rotary embedding (K stored before it): lane `sub` holds dims
@@ -782,6 +799,22 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
     } else {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      // this head's query words: registers, or LDS (Tune::kQLds)
+      uint32_t qh[kQLds ? NW : 1];
+      if constexpr (kQLds) {
+#pragma unroll
+        for (int w = 0; w < NW; w += 4) {
+          const uint4 t = *reinterpret_cast<const uint4*>(&s_q[h][sub][w]);
+          qh[w] = t.x;
+          qh[w + 1] = t.y;
+          qh[w + 2] = t.z;
+          qh[w + 3] = t.w;
+        }
+      }
+      auto qword = [&](int w) -> uint32_t {
+        if constexpr (kQLds) return qh[w];
+        else return qw[h][w];
+      };
       float d = 0.f;
       if constexpr (kKv == 1) {
         // 4 fp8 per K word, widened exactly to two bf16 pairs (converted
@@ -790,9 +823,9 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
         for (int w = 0; w < R::kKvWords; ++w) {
           const uint32_t kw = word(kr[w / 4], w % 4);
           d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw, 1.0f, false),
-                                              __builtin_bit_cast(bf16x2_t, qw[h][2 * w]), d, false);
+                                              __builtin_bit_cast(bf16x2_t, qword(2 * w)), d, false);
           d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw, 1.0f, true),
-                                              __builtin_bit_cast(bf16x2_t, qw[h][2 * w + 1]), d, false);
+                                              __builtin_bit_cast(bf16x2_t, qword(2 * w + 1)), d, false);
         }
       } else {
 #pragma unroll
@@ -800,9 +833,9 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
           const uint32_t kw = word(kr[w / 4], w % 4);
           if constexpr (kKv == 2) {
             d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kw),
-                                                __builtin_bit_cast(bf16x2_t, qw[h][w]), d, false);
+                                                __builtin_bit_cast(bf16x2_t, qword(w)), d, false);
           } else {
-            d = __builtin_fmaf(__uint_as_float(kw), __uint_as_float(qw[h][w]), d);
+            d = __builtin_fmaf(__uint_as_float(kw), __uint_as_float(qword(w)), d);
           }
         }
       }

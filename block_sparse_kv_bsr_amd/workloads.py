@@ -52,6 +52,8 @@ CONFIG_NAMES = {
     9: "skewed_b64_loguniform_32_32768_rope",
     # the same over an fp8 KV cache
     10: "skewed_b64_loguniform_32_32768_fp8kv_rope",
+    # the skewed batch at 64 query heads per 8 KV heads (group 8)
+    11: "skewed_b64_loguniform_32_32768_g8",
 }
 
 # Rotary embedding base of the rope workload (the Llama-3 value).
@@ -363,6 +365,10 @@ def workload(config_id: int) -> Workload:
         w = workload(3)
         return dataclasses.replace(w, name=CONFIG_NAMES[9], config_id=9, value_seed=seed,
                                    rope_theta=ROPE_THETA)
+    if config_id == 11:  # the skewed batch with 64 query heads over 8 KV heads
+        w = workload(3)
+        return dataclasses.replace(w, name=CONFIG_NAMES[11], config_id=11, num_qo_heads=64,
+                                   value_seed=seed)
     if config_id == 10:  # the skewed batch over an fp8 cache of keys before the embedding
         w = workload(6)
         return dataclasses.replace(w, name=CONFIG_NAMES[10], config_id=10,

@@ -110,7 +110,7 @@ def test_all_requests_empty():
     run_case(w, what="all-empty")
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 11])
 def test_config_full_size(cfg):
     w = workload(cfg)
     p, _, _ = run_case(w, device_values=cfg > 1, what=f"config{cfg}")
