@@ -18,7 +18,9 @@
 //    flight per CU to stream HBM. Each lane reads back exactly the 16 bytes
 //    it fetched (ds_read_b128 at lane*16), so LDS sees no bank conflicts.
 //  * GQA packing: each K/V row is loaded once per KV head and serves all G
-//    query heads of the group (query heads kvh*G+i share KV head kvh).
+//    query heads of the group (query heads kvh*G+i share KV head kvh). The
+//    query words live in registers, or at G = 8 in LDS, read per head and
+//    step (Tune::kQLds), which keeps that variant at two waves per SIMD.
 //  * Scores: bf16 pairs go through v_dot2 (two products + accumulate into
 //    fp32 per instruction); the 8 lanes of a token are summed with three DPP
 //    row operations inside a half-row, with no LDS traffic.
