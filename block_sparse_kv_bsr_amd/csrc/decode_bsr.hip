@@ -452,8 +452,9 @@ struct Tune {
   // An fp8 stage holds half the bytes of a bf16 one and its waves spend less
   // time per step; 8 stages (16 KiB in flight per wave, the most that still
   // fits 2 waves per SIMD in LDS) measured 17% faster than 4 on the skewed
-  // batch.
-  static constexpr int kRing = kKv == 1 ? 8 : (kStream ? 2 : 4);
+  // batch. With the rotary embedding the fp8 waves are bound by their vector
+  // work, and 4 stages measured 3% faster than 8.
+  static constexpr int kRing = kKv == 1 ? (kRope ? 4 : 8) : (kStream ? 2 : 4);
   static_assert(kRing % 2 == 0, "the main loop reads ring stages two at a time");
   // At G = 8 the query words stay in LDS and are read per head and step
   // (the 8 lanes of a column read the same 16 bytes, one broadcast): in
