@@ -143,6 +143,11 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
     C = std::min(C, cap);
 
     // ---- items, longest chunk first
+    {
+      int64_t n_items = 0;
+      for (const Tile& t : tiles) n_items += std::max<int64_t>(1, ceil_div(t.range, C));
+      p->items.reserve((size_t)(n_items * num_kv_heads * FI_QITEM_STRIDE));
+    }
     int32_t longest = 0;
     for (const Tile& t : tiles) {
       const int64_t k = std::max<int64_t>(1, ceil_div(t.range, C));
@@ -185,18 +190,25 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
       const int64_t n = p->num_items();
       const int32_t* it = p->items.data();
       auto key = [&](int64_t i, int f) { return it[i * FI_QITEM_STRIDE + f]; };
-      // items of each pair, longest chunk first
+      // items of each pair, longest chunk first; ties in (query row, chunk)
+      // order, which is the order the items of a pair were made in, so the
+      // item index breaks them (keys sorted, not items)
+      struct SortKey {
+        uint32_t req, head, shorter, index;
+        bool operator<(const SortKey& o) const {
+          if (req != o.req) return req < o.req;
+          if (head != o.head) return head < o.head;
+          if (shorter != o.shorter) return shorter < o.shorter;
+          return index < o.index;
+        }
+      };
+      std::vector<SortKey> keys((size_t)n);
+      for (int64_t i = 0; i < n; ++i)
+        keys[(size_t)i] = {(uint32_t)key(i, FI_QITEM_REQUEST), (uint32_t)key(i, FI_QITEM_KV_HEAD),
+                           (uint32_t)(INT32_MAX - key(i, FI_QITEM_NUM_KV)), (uint32_t)i};
+      std::sort(keys.begin(), keys.end());
       std::vector<int64_t> order(n);
-      for (int64_t i = 0; i < n; ++i) order[i] = i;
-      std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b) {
-        for (int f : {FI_QITEM_REQUEST, FI_QITEM_KV_HEAD})
-          if (key(a, f) != key(b, f)) return key(a, f) < key(b, f);
-        if (key(a, FI_QITEM_NUM_KV) != key(b, FI_QITEM_NUM_KV))
-          return key(a, FI_QITEM_NUM_KV) > key(b, FI_QITEM_NUM_KV);
-        for (int f : {FI_QITEM_QO_ROW, FI_QITEM_CHUNK})
-          if (key(a, f) != key(b, f)) return key(a, f) < key(b, f);
-        return false;
-      });
+      for (int64_t i = 0; i < n; ++i) order[i] = keys[(size_t)i].index;
       struct Pair {
         int64_t begin, end, work;
       };
