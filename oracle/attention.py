@@ -144,27 +144,6 @@ def decode_attention(q, k_pool, v_pool, kv_indptr, kv_indices, last_page_len, sm
     return O, LSE
 
 
-def decode_attention_rows(q, k_pool, v_pool, kv_indptr, kv_indices, last_page_len,
-                          rows: Sequence[Tuple[int, int]], sm_scale=None):
-    """The same definition evaluated only for the listed (b, h) rows; used to
-    check single outputs of large batches. Returns (O [n, d], LSE [n])."""
-    q = np.asarray(q, dtype=np.float64) if not hasattr(q, "numpy") else q
-    d = k_pool.shape[-1]
-    Hq = q.shape[1]
-    Hkv, P = k_pool.shape[1], k_pool.shape[2]
-    G = Hq // Hkv
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(d)
-    O = np.zeros((len(rows), d))
-    LSE = np.zeros(len(rows))
-    for i, (b, h) in enumerate(rows):
-        toks = request_tokens(kv_indptr, kv_indices, last_page_len, P, b)
-        K, V = gather_kv(k_pool, v_pool, toks, kv_head_of(h, G))
-        o, lse = attend(np.asarray(q[b, h:h + 1, :], dtype=np.float64), K, V, sm_scale)
-        O[i], LSE[i] = o[0], lse[0]
-    return O, LSE
-
-
 def rope_angles(head_dim: int, positions, theta: float = 1e4, scale: float = 1.0):
     """Rotation angle of every dim pair at every position: array
     [len(positions), head_dim / 2], (pos / scale) * theta^(-2i / head_dim)."""
@@ -267,32 +246,6 @@ def prefill_attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, last_
                 o, lse = attend(q[q0 + i, heads, :], K[:c], V[:c], sm_scale)
                 O[q0 + i, heads, :] = o
                 LSE[q0 + i, heads] = lse
-    return O, LSE
-
-
-def prefill_attention_rows(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, last_page_len,
-                           rows: Sequence[Tuple[int, int]], causal=True, sm_scale=None):
-    """prefill_attention evaluated only for the listed (query row, head)
-    pairs; used to check single outputs of large batches. Returns
-    (O [n, d], LSE [n])."""
-    d = k_pool.shape[-1]
-    Hq = q.shape[1]
-    Hkv, P = k_pool.shape[1], k_pool.shape[2]
-    G = Hq // Hkv
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(d)
-    qo_indptr = np.asarray(qo_indptr)
-    O = np.zeros((len(rows), d))
-    LSE = np.zeros(len(rows))
-    for j, (r, h) in enumerate(rows):
-        b = int(np.searchsorted(qo_indptr, r, side="right")) - 1
-        n = int(qo_indptr[b + 1] - qo_indptr[b])
-        i = r - int(qo_indptr[b])
-        toks = request_tokens(kv_indptr, kv_indices, last_page_len, P, b)
-        c = visible_tokens(len(toks), n, i, causal)
-        K, V = gather_kv(k_pool, v_pool, toks[:c], kv_head_of(h, G))
-        o, lse = attend(np.asarray(q[r, h:h + 1, :], dtype=np.float64), K, V, sm_scale)
-        O[j], LSE[j] = o[0], lse[0]
     return O, LSE
 
 

@@ -49,3 +49,15 @@ def compare(out_gpu, lse_gpu, O, LSE, bf16: bool, what=""):
     if empty.any():
         assert np.all(out_gpu[empty] == 0), f"{what}: empty request output not zero"
     return stats
+
+
+def prefill_request(w, b):
+    """Request b of a prefill workload as a batch of one over the same pool:
+    (first query row, last query row + 1, qo_indptr, kv_indptr, kv_indices,
+    last_page_len). The oracle attends per request, so evaluating it on
+    these slices one request at a time gives exactly the whole-batch result
+    with memory bounded by the largest request."""
+    q0, q1 = int(w.qo_indptr[b]), int(w.qo_indptr[b + 1])
+    p0, p1 = int(w.kv_indptr[b]), int(w.kv_indptr[b + 1])
+    return (q0, q1, np.array([0, q1 - q0]), np.array([0, p1 - p0]),
+            np.asarray(w.kv_indices[p0:p1]), np.asarray(w.last_page_len[b:b + 1]))

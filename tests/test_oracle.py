@@ -193,3 +193,29 @@ def test_rope_oracle_mutations_are_caught(name, monkeypatch):
         except (AssertionError, ValueError, IndexError, TypeError):
             caught.append(pin.__name__)
     assert caught, f"planted mistake {name} passed every rope pin"
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_per_request_slices_equal_the_whole_batch(causal):
+    """The full-size GPU parity evaluates the oracle one request at a time
+    (tests.parity.prefill_request); those slices must give exactly the
+    whole-batch result, including requests with no queries, an unmasked
+    request with no pages, and a causal request whose every token queries."""
+    from block_sparse_kv_bsr_amd.workloads import random_prefill_workload
+    from tests.parity import prefill_request
+    lens = [40, 0, 77, 1, 120, 33] if not causal else [40, 5, 77, 1, 120, 33]
+    qo_lens = [0, 6, 77, 1, 30, 0] if not causal else [0, 5, 77, 1, 30, 0]
+    w = random_prefill_workload(31, len(lens), 120, 8, 2, 64, 16, causal=causal, lens=lens,
+                                qo_lens=qo_lens)
+    q, k, v = (t.double().numpy() for t in w.make_values("cpu"))
+    O, LSE = oa.prefill_attention(q, k, v, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                  w.last_page_len, causal, w.sm_scale)
+    seen = np.zeros(w.num_qo_tokens, dtype=bool)
+    for b in range(w.batch):
+        q0, q1, qo, ip, ix, lp = prefill_request(w, b)
+        o, s = oa.prefill_attention(q[q0:q1], k, v, qo, ip, ix, lp, causal, w.sm_scale)
+        assert np.array_equal(o, O[q0:q1]) and np.array_equal(s, LSE[q0:q1])
+        seen[q0:q1] = True
+    assert seen.all()
+    if not causal:
+        assert np.isneginf(LSE[0:6]).all()  # request 1: no pages, unmasked
