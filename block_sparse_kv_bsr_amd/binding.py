@@ -243,15 +243,30 @@ class Plan:
             self._h = None
 
 
+def _check_lengths(ip: np.ndarray, ix: np.ndarray, lp: np.ndarray) -> int:
+    """The C ABI cannot see array lengths and reads kv_indices up to
+    kv_indptr[batch]: refuse arrays shorter than the page table says, before
+    any pointer crosses. Returns the batch size."""
+    if ip.ndim != 1 or len(ip) < 1:
+        raise ValueError("kv_indptr must be a 1-d array of batch + 1 entries")
+    batch = len(ip) - 1
+    if lp.ndim != 1 or len(lp) != batch:
+        raise ValueError("kv_last_page_len must have one entry per request")
+    if ix.ndim != 1:
+        raise ValueError("kv_indices must be a 1-d array")
+    if int(ip.max()) > len(ix):
+        raise ValueError(f"kv_indices holds {len(ix)} entries; kv_indptr refers to "
+                         f"{int(ip.max())}")
+    return batch
+
+
 def plan(kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int, num_kv_heads: int,
          head_dim: int, page_size: int, num_pool_pages: int, dtype="bf16",
          num_cus: int = 0, items_per_cu: int = 0, min_chunk_tokens: int = 0,
          max_chunk_tokens: int = 0, fixed_chunk_tokens: int = 0, cascade: int = 0) -> Plan:
     """fi_plan_create over host page-table arrays (numpy or CPU tensors)."""
     ip, ix, lp = _i32(kv_indptr), _i32(kv_indices), _i32(kv_last_page_len)
-    batch = len(ip) - 1
-    if len(lp) != batch:
-        raise ValueError("kv_last_page_len must have one entry per request")
+    batch = _check_lengths(ip, ix, lp)
     opts = PlanOpts(num_cus, items_per_cu, min_chunk_tokens, max_chunk_tokens, fixed_chunk_tokens,
                     cascade)
     h = ctypes.c_void_p()
@@ -446,8 +461,8 @@ def prefill_plan(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_qo_head
                  fixed_chunk_tokens: int = 0, num_xcds: int = 0) -> PrefillPlan:
     """fi_prefill_plan_create over host arrays (numpy or CPU tensors)."""
     qp, ip, ix, lp = _i32(qo_indptr), _i32(kv_indptr), _i32(kv_indices), _i32(kv_last_page_len)
-    batch = len(ip) - 1
-    if len(lp) != batch or len(qp) != batch + 1:
+    batch = _check_lengths(ip, ix, lp)
+    if qp.ndim != 1 or len(qp) != batch + 1:
         raise ValueError("qo_indptr, kv_indptr and kv_last_page_len disagree on the batch size")
     opts = PrefillOpts(num_cus, items_per_cu, fixed_chunk_tokens, num_xcds)
     h = ctypes.c_void_p()

@@ -3,8 +3,12 @@
 // live in plan.cpp and prefill_plan.cpp.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <iterator>
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "fi_bsr.h"
@@ -25,6 +29,50 @@ fi_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Which plan's image each workspace holds. A run reads the item list, merge
+// nodes and page ids of the last plan uploaded to its workspace, so it must
+// be that plan: a run of plan A after plan B was uploaded over A's bytes
+// would take B's words for A's requests and pages. Records are address
+// ranges [start, start + workspace bytes of the plan), keyed by start and
+// never overlapping: an upload drops every record its range overlaps
+// (decode and prefill plans alike), a run must find its own plan's record at
+// exactly its workspace, and destroying a plan drops its records. A plan is
+// identified by a serial taken at its first upload, so a new plan that
+// reuses a destroyed plan's address is not mistaken for it.
+struct UploadRecord {
+  uintptr_t end;
+  uint64_t serial;
+};
+std::mutex g_uploads_mu;
+std::map<uintptr_t, UploadRecord> g_uploads;
+std::atomic<uint64_t> g_next_serial{1};
+
+void record_upload(const void* workspace, int64_t bytes, uint64_t serial) {
+  const uintptr_t s = reinterpret_cast<uintptr_t>(workspace);
+  const uintptr_t e = s + (uintptr_t)(bytes > 0 ? bytes : 1);
+  std::lock_guard<std::mutex> lock(g_uploads_mu);
+  auto it = g_uploads.lower_bound(s);
+  if (it != g_uploads.begin() && std::prev(it)->second.end > s) it = std::prev(it);
+  while (it != g_uploads.end() && it->first < e) it = g_uploads.erase(it);
+  g_uploads[s] = UploadRecord{e, serial};
+}
+
+bool holds_plan(const void* workspace, int64_t bytes, uint64_t serial) {
+  if (serial == 0) return false;
+  const uintptr_t s = reinterpret_cast<uintptr_t>(workspace);
+  std::lock_guard<std::mutex> lock(g_uploads_mu);
+  const auto it = g_uploads.find(s);
+  return it != g_uploads.end() && it->second.serial == serial &&
+         it->second.end == s + (uintptr_t)(bytes > 0 ? bytes : 1);
+}
+
+void forget_plan(uint64_t serial) {
+  if (serial == 0) return;
+  std::lock_guard<std::mutex> lock(g_uploads_mu);
+  for (auto it = g_uploads.begin(); it != g_uploads.end();)
+    it = it->second.serial == serial ? g_uploads.erase(it) : std::next(it);
+}
+
 // Copies a plan's host image into the workspace, asynchronously on `stream`,
 // through a cached pinned staging block.
 template <class Plan>
@@ -38,13 +86,16 @@ fi_status upload(Plan* plan, void* workspace, size_t workspace_bytes, fi_stream_
   const hipError_t e = fi::staged_upload(workspace, plan->image.data(), plan->image.size(),
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "plan upload");
-  plan->uploaded_to = workspace;
+  if (plan->serial == 0) plan->serial = g_next_serial.fetch_add(1);
+  record_upload(workspace, plan->ws.total_bytes, plan->serial);
   return FI_OK;
 }
 
 template <class Plan>
 void destroy(Plan* plan) {
-  if (plan) fi::plan_free_host(plan);
+  if (!plan) return;
+  forget_plan(plan->serial);
+  fi::plan_free_host(plan);
 }
 
 }  // namespace
@@ -74,8 +125,10 @@ fi_status fi_prefill_run(const fi_prefill_plan* plan, const void* q, const void*
   if (!workspace) return fail(FI_ERR_INVALID_ARG, "workspace is NULL");
   if ((int64_t)workspace_bytes < plan->ws.total_bytes)
     return fail(FI_ERR_WORKSPACE, "workspace smaller than fi_prefill_info.workspace_bytes");
-  if (plan->uploaded_to != workspace)
-    return fail(FI_ERR_STATE, "plan was not uploaded to this workspace (call fi_prefill_plan_upload)");
+  if (!holds_plan(workspace, plan->ws.total_bytes, plan->serial))
+    return fail(FI_ERR_STATE,
+                "workspace does not hold this plan: it was not uploaded there, or another plan "
+                "was uploaded over it since (call fi_prefill_plan_upload)");
   if (!(sm_scale > 0.f)) sm_scale = 1.0f / std::sqrt((float)plan->head_dim);
   char* ws = static_cast<char*>(workspace);
   fi::PrefillArgs a{};
@@ -122,8 +175,10 @@ fi_status check_run(const fi_plan* plan, void* out, float* lse, void* workspace,
   if (!workspace) return fail(FI_ERR_INVALID_ARG, "workspace is NULL");
   if ((int64_t)workspace_bytes < plan->ws.total_bytes)
     return fail(FI_ERR_WORKSPACE, "workspace smaller than fi_plan_info.workspace_bytes");
-  if (plan->uploaded_to != workspace)
-    return fail(FI_ERR_STATE, "plan was not uploaded to this workspace (call fi_plan_upload)");
+  if (!holds_plan(workspace, plan->ws.total_bytes, plan->serial))
+    return fail(FI_ERR_STATE,
+                "workspace does not hold this plan: it was not uploaded there, or another plan "
+                "was uploaded over it since (call fi_plan_upload)");
   return FI_OK;
 }
 

@@ -55,8 +55,9 @@ struct fi_plan {
   int32_t num_groups = 0, prefix_rows = 0;
   std::vector<uint8_t> image;   // host copy of the uploaded part of the workspace
   fi::WorkspaceLayout ws;
-  // Set by the launch layer.
-  const void* uploaded_to = nullptr;
+  // Identity of this plan in the launch layer's upload records (0 until
+  // the first upload).
+  uint64_t serial = 0;
   int64_t num_items() const { return (int64_t)items.size() / FI_ITEM_STRIDE; }
   int64_t num_nodes() const { return (int64_t)nodes.size() / FI_NODE_STRIDE; }
   int64_t num_pitems() const { return (int64_t)pitems.size() / FI_PITEM_STRIDE; }
@@ -77,7 +78,7 @@ struct fi_prefill_plan {
     int64_t image_bytes = 0, total_bytes = 0;
   } ws;
   std::vector<uint8_t> image;
-  const void* uploaded_to = nullptr;
+  uint64_t serial = 0;  // as for fi_plan
   int64_t num_items() const { return (int64_t)items.size() / FI_QITEM_STRIDE; }
   int64_t num_merges() const { return (int64_t)merges.size() / FI_QMERGE_STRIDE; }
 };

@@ -54,11 +54,20 @@
  * the outputs are untouched, and fi_last_error() returns a message for the
  * calling thread. No C++ exception crosses this boundary. Metadata are fully
  * validated by fi_plan_create (host only); fi_decode_run checks pointers,
- * alignment, workspace size and that the plan was uploaded to that
- * workspace, then launches without reading device memory on the host.
+ * alignment, workspace size and that the workspace still holds this plan,
+ * then launches without reading device memory on the host. "Still holds"
+ * is kept on the host per address range: every upload (decode or prefill
+ * plan) records that its plan occupies [workspace, workspace +
+ * workspace_bytes of the plan) and drops the record of every earlier upload
+ * whose range overlaps it; a run needs its own plan's record at exactly its
+ * workspace address, else it returns FI_ERR_STATE without launching; a
+ * destroyed plan's records are dropped. The record is keyed by address: a
+ * buffer freed and reallocated at the same address by the caller, with no
+ * upload in between, is not detected.
  *
- * Thread safety. Distinct plans may be used from distinct threads. A plan
- * must not be uploaded from two threads at once.
+ * Thread safety. Distinct plans may be used from distinct threads (the
+ * upload records are guarded by a lock). A plan must not be uploaded from
+ * two threads at once.
  */
 #ifndef FI_BSR_H
 #define FI_BSR_H
@@ -77,7 +86,8 @@ typedef enum {
   FI_ERR_WORKSPACE = -3,   /* workspace too small */
   FI_ERR_HIP = -4,         /* a HIP runtime call failed; message has its text */
   FI_ERR_NOMEM = -5,       /* host allocation failed */
-  FI_ERR_STATE = -6        /* plan not uploaded to this workspace */
+  FI_ERR_STATE = -6        /* workspace does not hold this plan (never uploaded
+                              there, or another plan uploaded over it since) */
 } fi_status;
 
 /*
@@ -223,7 +233,10 @@ enum {
  * gaps, except that every other layer of num_cus items is reversed (a snake
  * order: the dispatcher deals consecutive workgroups to the CUs in turn, so a
  * CU that takes one layer's longest item takes the next layer's shortest).
- * The input arrays are copied; the caller may free them afterwards.
+ * The input arrays are copied; the caller may free them afterwards. Their
+ * lengths are not visible across this boundary: kv_indptr must hold batch+1
+ * entries, kv_indices at least kv_indptr[batch] and kv_last_page_len batch
+ * (the Python binding checks the lengths before calling).
  *
  * Shared prefixes (composable block-sparse formats, explainer's Block-Sparse
  * section; cascade attention): for bf16, requests whose page lists begin with
@@ -447,7 +460,8 @@ enum {
  * qo_indptr        host int32 [batch+1], qo_indptr[0] = 0, non-decreasing;
  *                  with causal != 0 every n_b <= L_b
  * kv_indptr, kv_indices, kv_last_page_len: the page table, as for
- *                  fi_plan_create (L_b tokens per request)
+ *                  fi_plan_create (L_b tokens per request; the same array
+ *                  lengths, which this call cannot see, are required)
  * num_qo_heads, num_kv_heads: G = num_qo_heads / num_kv_heads in
  *                  1 .. FI_PREFILL_ROWS (a tile holds FI_PREFILL_ROWS / G query
  *                  tokens; with G not dividing it the last rows are padding)

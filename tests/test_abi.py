@@ -186,3 +186,21 @@ def test_prefill_run_checks_on_the_host():
                             None) == -1
     assert L.fi_prefill_plan_upload(p.handle, ctypes.c_void_p(0x100010), ws, None) == -1
     assert L.fi_prefill_plan_upload(p.handle, fake, ws - 1, None) == -3
+
+
+def test_binding_refuses_arrays_shorter_than_the_page_table():
+    """The C ABI reads kv_indices up to kv_indptr[batch] and cannot see the
+    array's length: the binding refuses a short array before the call."""
+    with pytest.raises(ValueError, match="kv_indices holds 2 entries"):
+        fb.plan([0, 40], [1, 2], [16], 8, 2, 128, 16, 100, "bf16")
+    with pytest.raises(ValueError, match="kv_indices holds 3 entries"):
+        fb.plan([0, 5, 3], [1, 2, 3], [16, 16], 8, 2, 128, 16, 100, "bf16")
+    with pytest.raises(ValueError, match="one entry per request"):
+        fb.plan([0, 2, 3], [5, 6, 7], [16], 8, 2, 128, 16, 100, "bf16")
+    with pytest.raises(ValueError, match="kv_indices holds 2 entries"):
+        fb.prefill_plan([0, 1], [0, 40], [1, 2], [16], 8, 2, 128, 16, 100)
+    with pytest.raises(ValueError, match="disagree"):
+        fb.prefill_plan([0, 1, 2], [0, 2], [1, 2], [16], 8, 2, 128, 16, 100)
+    # the same arrays at their full lengths are accepted
+    fb.plan([0, 2, 3], [5, 6, 7], [16, 3], 8, 2, 128, 16, 100, "bf16")
+    fb.prefill_plan([0, 1], [0, 2], [1, 2], [16], 8, 2, 128, 16, 100)

@@ -371,3 +371,49 @@ def test_back_to_back_uploads_through_the_staging_cache():
         compare(o1.double().cpu().numpy(), l1.double().cpu().numpy(), O, LSE, True, "staging")
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
     log("[ok] staging")
+
+
+def test_workspace_holds_only_the_last_uploaded_plan():
+    """A run reads the item list of the plan last uploaded to its workspace,
+    so it must be that plan: uploading plan B (or a prefill plan) over plan
+    A's workspace makes A's runs fail with FI_ERR_STATE, on the host, with
+    nothing launched, until A is uploaded again; a plan never uploaded fails
+    the same way."""
+    w = random_workload(41, 4, 300, 8, 2, 128, 16, "bf16")
+    q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    mk = lambda **o: fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, 8, 2, 128, 16,
+                             w.num_pool_pages, "bf16", **o)
+    pa, pb = mk(), mk(fixed_chunk_tokens=16)
+    assert pb.info["num_items"] != pa.info["num_items"]
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    pa.upload(ws)
+    oa1, la1 = fb.decode(q, k, v, pa, workspace=ws)
+    pb.upload(ws)
+    with pytest.raises(fb.FiError) as e:
+        fb.decode(q, k, v, pa, workspace=ws)
+    assert e.value.status == -6
+    ob, lb = fb.decode(q, k, v, pb, workspace=ws)
+    torch.cuda.synchronize()
+    qh, kh, vh = host_values(w, q, k, v)
+    O, LSE = oa.decode_attention(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len, w.sm_scale)
+    compare(ob.double().cpu().numpy(), lb.double().cpu().numpy(), O, LSE, True, "second plan")
+    # a prefill plan uploaded over part of the same bytes drops pb's record
+    wp = random_prefill_workload(42, 2, 100, 8, 2, 128, 16)
+    pf = fb.prefill_plan(wp.qo_indptr, wp.kv_indptr, wp.kv_indices, wp.last_page_len, 8, 2, 128,
+                         16, wp.num_pool_pages)
+    pf.upload(ws[256:])
+    with pytest.raises(fb.FiError) as e:
+        fb.decode(q, k, v, pb, workspace=ws)
+    assert e.value.status == -6
+    # uploading A again makes it valid again, with the same result
+    pa.upload(ws)
+    oa2, la2 = fb.decode(q, k, v, pa, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(oa1.view(torch.int16), oa2.view(torch.int16)) and torch.equal(la1, la2)
+    compare(oa2.double().cpu().numpy(), la2.double().cpu().numpy(), O, LSE, True, "first plan again")
+    # a plan that was never uploaded, whatever address it lives at
+    pc = mk(fixed_chunk_tokens=32)
+    with pytest.raises(fb.FiError) as e:
+        fb.decode(q, k, v, pc, workspace=ws)
+    assert e.value.status == -6
+    log("[ok] upload records")
