@@ -417,3 +417,33 @@ def test_workspace_holds_only_the_last_uploaded_plan():
         fb.decode(q, k, v, pc, workspace=ws)
     assert e.value.status == -6
     log("[ok] upload records")
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_full_size_bitwise_repeatable(cfg):
+    """Which wave completes a merge node depends on timing; the merged result
+    must not. Twenty runs of the full-size skewed batch (one-level trees) and
+    the long batch (two-level trees), every other one after a cache flush so
+    arrival orders differ, must equal the first run bit for bit; the test
+    stops at the first mismatch and names the run."""
+    w = workload(cfg)
+    q, k, v = w.make_values("cuda")
+    p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, w.num_qo_heads, w.num_kv_heads,
+                w.head_dim, w.page_size, w.num_pool_pages, w.dtype)
+    nodes = p.merge_nodes()
+    levels = int(nodes[:, 6].max()) + 1 if len(nodes) else 0
+    log(f"[case] repeat config {cfg}: {p.info['num_items']} items, {len(nodes)} merge nodes, "
+        f"{levels} level(s)")
+    if cfg == 4:
+        assert levels >= 2
+    o0, l0 = fb.decode(q, k, v, p)
+    out, lse = torch.empty_like(o0), torch.empty_like(l0)
+    flush = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
+    for run in range(1, 21):
+        if run % 2:
+            flush.zero_()
+        fb.decode(q, k, v, p, out=out, lse=lse)
+        torch.cuda.synchronize()
+        same = torch.equal(out.view(torch.int16), o0.view(torch.int16)) and torch.equal(lse, l0)
+        assert same, f"config {cfg}: run {run} differs from run 0"
+    log(f"[ok] repeat config {cfg}: 20 runs bitwise equal")
