@@ -5,11 +5,13 @@ single kernel launch that attends over the planner's work items and folds the
 partial states of cut requests up their merge trees, with the plan built once
 per batch and uploaded before timing (a serving engine reuses one plan for every layer of a
 decode step; the host planner's own time is reported beside it). Inputs are
-resident in HBM. Before every timed step a 1 GiB fill evicts L2 and the
-256 MB Infinity Cache, outside the timed events.
+resident in HBM. Before every timed step L2 and the 256 MB Infinity Cache
+are flushed (a 1 GiB write, then a 1 GiB read of another buffer, so no dirty
+line is left for the step to write back), outside the timed events.
 
 Prints one JSON line: achieved HBM GB/s over the algorithmic bytes (active K
-and V once per KV head + q read + output written), microseconds per batch,
+and V once per KV head + q read + output written) and microseconds per batch,
+both from the median step (HIP events on the launch stream around each call),
 the decode kernel's roofline fraction against 8 TB/s, and the float64 CPU
 oracle timed on the host on the same workload.
 
@@ -32,23 +34,34 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "achieved HBM GB/s (% of MI355X peak) + µs/batch, skewed-batch paged GQA decode"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak
-DECODE_SRC = os.path.join(ROOT, "block_sparse_kv_bsr_amd", "csrc", "decode_bsr.hip")
+CSRC = os.path.join(ROOT, "block_sparse_kv_bsr_amd", "csrc")
 COPY_PROBE_MIB = 1024
+# the library kernels a step can launch, the source each is built from, and
+# the short name counter summaries use
+KERNELS = {"tile_attend_kernel": ("attn_tile.hip", "tile_attend"),
+           "decode_bsr_kernel": ("decode_bsr.hip", "decode_bsr"),
+           "prefill_merge_kernel": ("merge_states.hip", "prefill_merge")}
 
 
-def source_digest() -> str:
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(kernels=("decode_bsr_kernel",)) -> str:
+    """sha256 (16 hex digits) of the sources the given kernels are built from."""
+    h = hashlib.sha256()
+    for src in sorted({KERNELS[k][0] for k in kernels}):
+        with open(os.path.join(CSRC, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def counters_file(workload_name: str) -> str:
-    return os.path.join(ROOT, "profiles", f"decode_bsr_counters_{workload_name}.txt")
+def counters_file(workload_name: str, kernels=("decode_bsr_kernel",)) -> str:
+    tag = "_".join(KERNELS[k][1] for k in kernels)
+    return os.path.join(ROOT, "profiles", f"{tag}_counters_{workload_name}.txt")
 
 
-def read_traffic(workload_name: str):
-    """HBM bytes per decode launch from the committed counter summary, or None
-    when there is none or the decode kernel source changed since."""
-    path = counters_file(workload_name)
+def read_traffic(workload_name: str, kernels=("decode_bsr_kernel",)):
+    """HBM bytes per step (FETCH + WRITE of every kernel of the step) from the
+    committed counter summary, or None when there is none or a kernel's
+    source changed since."""
+    path = counters_file(workload_name, kernels)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -56,10 +69,10 @@ def read_traffic(workload_name: str):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("decode_source_sha256_16") != source_digest():
+    if vals.get("source_sha256_16") != source_digest(kernels):
         return None
     try:
-        return float(vals["scaled_fetch_bytes_per_launch"]) + float(vals["scaled_write_bytes_per_launch"])
+        return float(vals["scaled_fetch_bytes_per_step"]) + float(vals["scaled_write_bytes_per_step"])
     except (KeyError, ValueError):
         return None
 
@@ -77,29 +90,40 @@ def _pmc_rows(path, counter):
 
 def summarize_counters(fetch_csv, write_csv, workload_name):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
-    dispatch) into bytes per decode launch, scaled by what the same counters
-    read for a plain copy of COPY_PROBE_MIB MiB in the same program."""
-    out = {}
+    dispatch) into bytes per launch of each library kernel found, scaled by
+    what the same counter reads for a plain copy of COPY_PROBE_MIB MiB in the
+    same program, and their sum per step (a step launches each once)."""
+    out, kernels = {}, None
     for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = _pmc_rows(path, counter)
-        dec = [v for k, v in rows if "decode_bsr_kernel" in k]
-        cpy = [v for k, v in rows if "copy" in k.lower() or "elementwise" in k.lower()]
-        if not dec or not cpy:
-            raise SystemExit(f"{path}: no decode or copy dispatches with {counter}")
-        known_kib = COPY_PROBE_MIB * 1024.0
+        found = [k for k in KERNELS if any(k in kn for kn, _ in rows)]
+        kernels = found if kernels is None else kernels
+        if not found or found != kernels:
+            raise SystemExit(f"{path}: library kernels {found} (expected {kernels})")
+        cpy = [v for kn, v in rows if "copy" in kn.lower()]
+        if not cpy:
+            raise SystemExit(f"{path}: no copy dispatch with {counter}")
         probe = max(cpy)
-        scale = known_kib / probe
-        out[f"{name}_kib_raw_mean"] = statistics.mean(dec)
+        scale = COPY_PROBE_MIB * 1024.0 / probe
         out[f"{name}_copy_probe_kib"] = probe
         out[f"{name}_scale"] = scale
-        out[f"scaled_{name}_bytes_per_launch"] = statistics.mean(dec) * 1024.0 * scale
-    path = counters_file(workload_name)
+        total = 0.0
+        for k in kernels:
+            vals = [v for kn, v in rows if k in kn]
+            short = KERNELS[k][1]
+            out[f"{short}_{name}_kib_raw_mean"] = statistics.mean(vals)
+            out[f"{short}_{name}_dispatches"] = len(vals)
+            per = statistics.mean(vals) * 1024.0 * scale
+            out[f"{short}_scaled_{name}_bytes_per_launch"] = per
+            total += per
+        out[f"scaled_{name}_bytes_per_step"] = total
+    path = counters_file(workload_name, kernels)
     with open(path, "w") as f:
-        f.write(f"# decode_bsr_kernel HBM traffic, workload {workload_name}\n")
-        f.write("# from: rocprofv3 --pmc FETCH_SIZE -- python bench.py --counters-run\n")
-        f.write("#  and: rocprofv3 --pmc WRITE_SIZE -- python bench.py --counters-run\n")
+        f.write(f"# HBM traffic of {' + '.join(kernels)}, workload {workload_name}\n")
+        f.write(f"# from: rocprofv3 --pmc FETCH_SIZE -- python bench.py --config <id> --counters-run\n")
+        f.write(f"#  and: rocprofv3 --pmc WRITE_SIZE -- python bench.py --config <id> --counters-run\n")
         f.write(f"# each counter scaled by (known bytes / counter) of a {COPY_PROBE_MIB} MiB copy\n")
-        f.write(f"decode_source_sha256_16 = {source_digest()}\n")
+        f.write(f"source_sha256_16 = {source_digest(kernels)}\n")
         for k, v in out.items():
             f.write(f"{k} = {v:.6g}\n")
     print(open(path).read())
@@ -121,7 +145,7 @@ def stream_ceiling(dev, flush, nbytes=2 << 30, reps=5):
     stream = torch.cuda.current_stream()
     ms = []
     for i in range(reps + 1):
-        flush.zero_()
+        flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         rc = L.fi_bench_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream)
@@ -136,24 +160,32 @@ def stream_ceiling(dev, flush, nbytes=2 << 30, reps=5):
 
 
 # ------------------------------------------------------------------ oracle
+def _one_thread():
+    """A context holding numpy's BLAS to one thread, and the thread count
+    the oracle then uses. The oracle's products (one request and KV head at a
+    time) are too small for BLAS threads to pay off: on the GPU machine's host
+    the 16-thread default ran slower than one thread."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=1), 1
+    except Exception:  # threadpoolctl missing: numpy's default threads
+        import contextlib
+        return contextlib.nullcontext(), os.cpu_count() or 1
+
+
 def cpu_baseline(w, q, k, v, min_seconds=10.0, max_passes=3):
     """Time the float64 oracle on the host over whole batches of the same
-    workload (inputs copied to host memory first, not timed)."""
-    import numpy as np
+    workload (inputs copied to host memory first, not timed), on one thread."""
     import torch
     sys.path.insert(0, ROOT)
     import oracle.attention as oa
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: numpy BLAS default
-        threads = os.cpu_count() or 1
     qh = q.float().cpu().numpy()
     if w.dtype == "fp8":  # the oracle attends over the dequantised cache
         kh = oa.dequantize_e4m3(k.view(torch.uint8).cpu().numpy(), w.k_scale)
         vh = oa.dequantize_e4m3(v.view(torch.uint8).cpu().numpy(), w.v_scale)
     else:
         kh, vh = k.float().cpu().numpy(), v.float().cpu().numpy()
+
     def run():
         if w.rope_theta:
             oa.decode_attention_rope(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len,
@@ -161,28 +193,19 @@ def cpu_baseline(w, q, k, v, min_seconds=10.0, max_passes=3):
         else:
             oa.decode_attention(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len, w.sm_scale)
 
+    ctx, threads = _one_thread()
     times = []
-    while len(times) < max_passes and sum(times) < min_seconds:
-        t0 = time.perf_counter()
-        run()
-        times.append(time.perf_counter() - t0)
+    with ctx:
+        while len(times) < max_passes and sum(times) < min_seconds:
+            t0 = time.perf_counter()
+            run()
+            times.append(time.perf_counter() - t0)
     per = statistics.median(times)
-    res = {"value": w.algorithmic_bytes() / per / 1e9, "unit": "GB/s", "cores": int(threads),
-           "kind": "oracle", "seconds_per_batch": per,
-           "sample": f"whole {w.name} batch ({int(w.kv_lens().sum())} KV tokens), "
-                     f"{len(times)} pass(es), median; numpy float64 on host cores"}
-    # the same oracle held to one host thread, one pass
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:
-        return res
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        run()
-        one = time.perf_counter() - t0
-    res["one_thread"] = {"value": w.algorithmic_bytes() / one / 1e9, "unit": "GB/s",
-                         "seconds_per_batch": one, "cores": 1}
-    return res
+    return {"value": w.algorithmic_bytes() / per / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds_per_batch": per,
+            "sample": f"whole {w.name} batch ({int(w.kv_lens().sum())} KV tokens), "
+                      f"{len(times)} pass(es), median; numpy float64, BLAS held to "
+                      f"{threads} host thread(s)"}
 
 
 def cpu_baseline_prefill(w, q, k, v, min_seconds=10.0):
@@ -192,38 +215,99 @@ def cpu_baseline_prefill(w, q, k, v, min_seconds=10.0):
     import numpy as np
     sys.path.insert(0, ROOT)
     import oracle.attention as oa
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    ctx, threads = _one_thread()
     kh, vh = k.float().cpu().numpy(), v.float().cpu().numpy()
     qo = w.qo_indptr
     L = w.kv_lens()
     flops = 0
     spent = 0.0
     done = 0
-    for b in range(w.batch):
-        n = int(qo[b + 1] - qo[b])
-        if n == 0:
-            continue
-        qh = q[int(qo[b]):int(qo[b + 1])].float().cpu().numpy()
-        ip = np.array([0, w.kv_indptr[b + 1] - w.kv_indptr[b]], dtype=np.int64)
-        ix = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
-        t0 = time.perf_counter()
-        oa.prefill_attention(qh, kh, vh, np.array([0, n]), ip, ix, w.last_page_len[b:b + 1],
-                             w.causal, w.sm_scale)
-        spent += time.perf_counter() - t0
-        Lb = int(L[b])
-        pairs = sum(max(0, Lb - n + i + 1) for i in range(n)) if w.causal else Lb * n
-        flops += 4 * w.head_dim * w.num_qo_heads * pairs
-        done += 1
-        if spent >= min_seconds:
-            break
+    with ctx:
+        for b in range(w.batch):
+            n = int(qo[b + 1] - qo[b])
+            if n == 0:
+                continue
+            qh = q[int(qo[b]):int(qo[b + 1])].float().cpu().numpy()
+            ip = np.array([0, w.kv_indptr[b + 1] - w.kv_indptr[b]], dtype=np.int64)
+            ix = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+            t0 = time.perf_counter()
+            oa.prefill_attention(qh, kh, vh, np.array([0, n]), ip, ix, w.last_page_len[b:b + 1],
+                                 w.causal, w.sm_scale)
+            spent += time.perf_counter() - t0
+            Lb = int(L[b])
+            pairs = sum(max(0, Lb - n + i + 1) for i in range(n)) if w.causal else Lb * n
+            flops += 4 * w.head_dim * w.num_qo_heads * pairs
+            done += 1
+            if spent >= min_seconds:
+                break
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(spent, 2),
             "sample": f"the first {done} request(s) of {w.name} (whole requests, all heads), "
-                      "numpy float64 on host cores"}
+                      f"numpy float64, BLAS held to {threads} host thread(s)"}
+
+
+# ------------------------------------------------------------ timing helpers
+class CacheFlush:
+    """Evicts L2 and the 256 MB Infinity Cache before a timed step, outside
+    its events: a 1 GiB write, then a 1 GiB read of another buffer. The
+    write alone would leave the Infinity Cache full of dirty lines that the
+    timed kernel's own reads then evict, paying their write-back to HBM
+    inside the timed region (2-5 us on the skewed batch, measured); after the
+    read the caches hold clean lines of a buffer the step never touches."""
+
+    def __init__(self, dev):
+        import torch
+        self.wbuf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        self.rbuf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        self.sink = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        import torch
+        self.wbuf.zero_()
+        torch.sum(self.rbuf, dim=0, keepdim=True, out=self.sink)
+
+
+def timed_steps(step, flush, steps, warmup):
+    """Run `warmup` untimed steps, then `steps` steps each bracketed by HIP
+    events on the current stream (the stream the library launches on), the
+    cache flush before each outside the events. Returns (ms per step, wall
+    seconds of the timed loop)."""
+    import torch
+    for _ in range(warmup):
+        if flush:
+            flush()
+        step(None)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if flush:
+            flush()
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [e[0].elapsed_time(e[1]) for e in events], wall
+
+
+def step_stats(step_ms):
+    """Median (what `value` is computed from), mean, p10 and p90 in us."""
+    s = sorted(step_ms)
+    return {"us_per_batch": round(1e3 * statistics.median(s), 2),
+            "us_per_batch_mean": round(1e3 * statistics.mean(s), 2),
+            "us_per_batch_p10_p90": [round(1e3 * s[int(0.1 * (len(s) - 1))], 2),
+                                     round(1e3 * s[int(0.9 * (len(s) - 1))], 2)]}
+
+
+def copy_probe(dev):
+    """For rocprofv3 --pmc runs: one plain copy of COPY_PROBE_MIB MiB, whose
+    counter readings scale the library kernels' readings to bytes."""
+    import torch
+    src = torch.empty(COPY_PROBE_MIB << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def bench_prefill(args, w):
@@ -250,34 +334,26 @@ def bench_prefill(args, w):
     p.upload(ws)
     out = torch.empty_like(q)
     lse = torch.empty((w.num_qo_tokens, w.num_qo_heads), dtype=torch.float32, device=dev)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else CacheFlush(dev)
+    if args.counters_run:
+        copy_probe(dev)
+        args.steps, args.warmup = min(args.steps, 5), 1
 
-    def step(ev=None):
+    def step(ev):
         if ev:
             ev[0].record()
         fb.prefill(q, k, v, p, out=out, lse=lse, workspace=ws)
         if ev:
             ev[1].record()
 
-    for _ in range(args.warmup):
-        if not args.no_flush:
-            flush.zero_()
-        step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if not args.no_flush:
-            flush.zero_()
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = [e[0].elapsed_time(e[1]) for e in events]
-    step_mean = statistics.mean(step_ms)
+    step_ms, wall = timed_steps(step, flush, args.steps, args.warmup)
+    st = step_stats(step_ms)
+    med_ms = st["us_per_batch"] * 1e-3
     flops = w.flops()
-    tflops = flops / (step_mean * 1e-3) / 1e12
+    tflops = flops / (med_ms * 1e-3) / 1e12
     nbytes = w.algorithmic_bytes()
-    kernels = "tile_attend_kernel" + (" + prefill_merge_kernel" if p.info["num_merges"] else "")
+    kernels = ["tile_attend_kernel"] + (["prefill_merge_kernel"] if p.info["num_merges"] else [])
+    traffic = read_traffic(w.name, kernels)
     result = {
         "metric": "algorithmic TFLOP/s (% of MI355X bf16 dense peak) + µs/batch, "
                   "paged causal prefill / append attention",
@@ -286,7 +362,7 @@ def bench_prefill(args, w):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_mean, 5),
+        "ms_per_step": round(med_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -300,10 +376,10 @@ def bench_prefill(args, w):
                    "parallelism": "single-gpu", "plan_items": p.info["num_items"],
                    "plan_merges": p.info["num_merges"], "chunk_tokens": p.info["chunk_tokens"],
                    "l2_mall_flush_between_steps": not args.no_flush},
-        "us_per_batch": round(step_mean * 1e3, 2),
-        "us_per_batch_p10_p90": [round(1e3 * sorted(step_ms)[int(0.1 * (len(step_ms) - 1))], 2),
-                                 round(1e3 * sorted(step_ms)[int(0.9 * (len(step_ms) - 1))], 2)],
-        "hbm_gbs_algorithmic": round(nbytes / (step_mean * 1e-3) / 1e9, 1),
+        **st,
+        "timing": "median step; HIP events on the launch stream around each fi_prefill_run "
+                  "(" + " + ".join(kernels) + ")",
+        "hbm_gbs_algorithmic": round(nbytes / (med_ms * 1e-3) / 1e9, 1),
         "plan_host_us": round(1e6 * statistics.median(plan_t), 1),
         "wall_s_timed_loop": round(wall, 4),
         # the step's events bracket the tile kernel and, for a cut tile, the
@@ -311,9 +387,10 @@ def bench_prefill(args, w):
         # on the tile kernel's own rate when there is a merge
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": kernels},
+                     "traffic": None if traffic is None else int(traffic),
+                     "kernel": " + ".join(kernels)},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.counters_run:
         result["cpu_baseline"] = cpu_baseline_prefill(w, q, k, v)
     print(json.dumps(result), flush=True)
     return 0
@@ -381,19 +458,12 @@ def main():
 
     out = torch.empty((w.batch, w.num_qo_heads, w.head_dim), dtype=q.dtype, device=dev)
     lse = torch.empty((w.batch, w.num_qo_heads), dtype=torch.float32, device=dev)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-
+    flush = None if args.no_flush else CacheFlush(dev)
     if args.counters_run:
-        src = torch.empty(COPY_PROBE_MIB << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(dev)
         args.steps, args.warmup = min(args.steps, 5), 1
 
-    def step(ev=None):
+    def step(ev):
         if ev:
             ev[0].record()
         fb.decode(q, k, v, p, out=out, lse=lse, workspace=ws, k_scale=w.k_scale, v_scale=w.v_scale,
@@ -401,27 +471,15 @@ def main():
         if ev:
             ev[1].record()
 
-    for _ in range(args.warmup):
-        if not args.no_flush:
-            flush.zero_()
-        step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if not args.no_flush:
-            flush.zero_()
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # the step is one launch of the decode kernel, so the step's events also
-    # bracket the kernel the roofline describes
-    step_ms = [e[0].elapsed_time(e[1]) for e in events]
-    step_mean = statistics.mean(step_ms)
+    step_ms, wall = timed_steps(step, flush, args.steps, args.warmup)
+    st = step_stats(step_ms)
+    med_ms = st["us_per_batch"] * 1e-3
     nbytes = w.algorithmic_bytes()
-    gbs = nbytes / (step_mean * 1e-3) / 1e9
-    traffic = read_traffic(w.name)
+    gbs = nbytes / (med_ms * 1e-3) / 1e9
+    # a step is one fi_decode_run: the decode kernel, preceded by the tile
+    # kernel when the plan has shared-prefix items
+    kernels = (["tile_attend_kernel"] if p.info["num_prefix_items"] else []) + ["decode_bsr_kernel"]
+    traffic = read_traffic(w.name, kernels)
     result = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -429,7 +487,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_mean, 5),
+        "ms_per_step": round(med_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -441,12 +499,12 @@ def main():
                    "page_size": w.page_size, "kv_tokens": int(w.kv_lens().sum()),
                    "algorithmic_bytes": nbytes, "parallelism": "single-gpu",
                    "plan_items": p.info["num_items"], "chunk_pages": p.info["chunk_pages"],
+                   "prefix_items": p.info["num_prefix_items"],
                    "l2_mall_flush_between_steps": not args.no_flush},
-        "us_per_batch": round(step_mean * 1e3, 2),
-        "us_per_batch_p10_p90": [round(1e3 * sorted(step_ms)[int(0.1 * (len(step_ms) - 1))], 2),
-                                 round(1e3 * sorted(step_ms)[int(0.9 * (len(step_ms) - 1))], 2)],
+        **st,
+        "timing": "median step; HIP events on the launch stream around each fi_decode_run "
+                  "(" + " + ".join(kernels) + ")",
         "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
-        "decode_kernel_us": round(step_mean * 1e3, 2),
         "plan_host_us": round(1e6 * statistics.median(plan_t), 1),
         "upload_us": round(1e6 * upload_s, 1),
         "upload_first_us": round(1e6 * upload_first_s, 1),
@@ -454,10 +512,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": None if traffic is None else int(traffic),
-                     "kernel": "decode_bsr_kernel"},
+                     "kernel": " + ".join(kernels)},
     }
     if not args.counters_run:
-        ceiling = stream_ceiling(dev, flush)
+        ceiling = stream_ceiling(dev, flush or CacheFlush(dev))
         result["practical_ceiling"] = {
             "gbs": round(ceiling, 1), "frac": round(gbs / ceiling, 4),
             "kernel": "streaming read of 2 GiB with 16-byte nontemporal loads "

@@ -17,34 +17,74 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stdout
 
 
+def _write_csv(path, counter, kernels, copy_kib):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        w.writerow({"Kernel_Name": "at::native::vectorized_elementwise_kernel<FillFunctor>",
+                    "Counter_Name": counter, "Counter_Value": 3 * copy_kib})
+        w.writerow({"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": counter,
+                    "Counter_Value": copy_kib})
+        for name, vals in kernels.items():
+            for v in vals:
+                w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v})
+
+
+def _read(path):
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    return vals
+
+
 def test_counter_summary_scales_by_the_copy_probe(tmp_path, monkeypatch):
     sys.path.insert(0, ROOT)
     import bench
 
-    def write(path, counter, decode_kib, copy_kib):
-        with open(path, "w", newline="") as f:
-            w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
-            w.writeheader()
-            w.writerow({"Kernel_Name": "at::native::elementwise copy", "Counter_Name": counter,
-                        "Counter_Value": copy_kib})
-            for v in decode_kib:
-                w.writerow({"Kernel_Name": "decode_bsr_kernel<2, 128, 4>", "Counter_Name": counter,
-                            "Counter_Value": v})
+    fetch, wr = tmp_path / "f.csv", tmp_path / "w.csv"
+    mib = bench.COPY_PROBE_MIB
+    dec = "decode_bsr_kernel<2, 128, 4>(DecodeParams)"
+    # FETCH reads half the copied bytes (scale 2), WRITE all of them (scale 1);
+    # a bigger fill kernel in the same run is not taken for the copy
+    _write_csv(fetch, "FETCH_SIZE", {dec: [1000.0, 1002.0]}, mib * 1024 / 2)
+    _write_csv(wr, "WRITE_SIZE", {dec: [10.0]}, mib * 1024)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    bench.summarize_counters(str(fetch), str(wr), "unit")
+    path = tmp_path / "profiles" / "decode_bsr_counters_unit.txt"
+    vals = _read(path)
+    assert abs(float(vals["fetch_scale"]) - 2.0) < 1e-9
+    # the file keeps six significant digits
+    assert abs(float(vals["scaled_fetch_bytes_per_step"]) / (1001.0 * 1024 * 2) - 1) < 1e-5
+    assert abs(float(vals["scaled_write_bytes_per_step"]) / (10.0 * 1024) - 1) < 1e-5
+    assert vals["source_sha256_16"] == bench.source_digest(["decode_bsr_kernel"])
+    # read back as the traffic of a step while the source is unchanged
+    t = bench.read_traffic("unit", ["decode_bsr_kernel"])
+    assert abs(t / (1001.0 * 1024 * 2 + 10.0 * 1024) - 1) < 1e-5
+
+
+def test_counter_summary_sums_the_kernels_of_a_step(tmp_path, monkeypatch):
+    """A shared-prefix step launches the tile kernel and the decode kernel:
+    the traffic of the step is the sum of both kernels' per-launch means."""
+    sys.path.insert(0, ROOT)
+    import bench
 
     fetch, wr = tmp_path / "f.csv", tmp_path / "w.csv"
     mib = bench.COPY_PROBE_MIB
-    # FETCH reads half the copied bytes (scale 2), WRITE all of them (scale 1)
-    write(fetch, "FETCH_SIZE", [1000.0, 1002.0], mib * 1024 / 2)
-    write(wr, "WRITE_SIZE", [10.0], mib * 1024)
-    monkeypatch.setattr(bench, "counters_file", lambda name: str(tmp_path / f"{name}.txt"))
+    ks = {"tile_attend_kernel<128, false>(TileParams)": [300.0, 310.0],
+          "decode_bsr_kernel<2, 128, 4>(DecodeParams)": [100.0, 100.0]}
+    _write_csv(fetch, "FETCH_SIZE", ks, mib * 1024)
+    _write_csv(wr, "WRITE_SIZE", {k: [1.0, 3.0] for k in ks}, mib * 1024)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
     bench.summarize_counters(str(fetch), str(wr), "unit")
-    vals = {}
-    for line in open(tmp_path / "unit.txt"):
-        if "=" in line and not line.startswith("#"):
-            k, v = line.split("=", 1)
-            vals[k.strip()] = v.strip()
-    assert abs(float(vals["fetch_scale"]) - 2.0) < 1e-9
-    # the file keeps six significant digits
-    assert abs(float(vals["scaled_fetch_bytes_per_launch"]) / (1001.0 * 1024 * 2) - 1) < 1e-5
-    assert abs(float(vals["scaled_write_bytes_per_launch"]) / (10.0 * 1024) - 1) < 1e-5
-    assert vals["decode_source_sha256_16"] == bench.source_digest()
+    kernels = ["tile_attend_kernel", "decode_bsr_kernel"]
+    vals = _read(tmp_path / "profiles" / "tile_attend_decode_bsr_counters_unit.txt")
+    assert abs(float(vals["tile_attend_scaled_fetch_bytes_per_launch"]) / (305.0 * 1024) - 1) < 1e-5
+    assert abs(float(vals["scaled_fetch_bytes_per_step"]) / (405.0 * 1024) - 1) < 1e-5
+    assert abs(float(vals["scaled_write_bytes_per_step"]) / (4.0 * 1024) - 1) < 1e-5
+    assert vals["source_sha256_16"] == bench.source_digest(kernels)
+    assert bench.read_traffic("unit", kernels) is not None
+    assert bench.read_traffic("unit", ["decode_bsr_kernel"]) is None  # no such summary
