@@ -6,5 +6,5 @@ plus seeded input generators. ``plan``, ``decode``, ``merge_states``,
 ``prefill_plan`` and ``prefill`` load the library on first use and raise if it
 is missing.
 """
-from .binding import (FiError, Plan, PrefillPlan, decode, lib, merge_states, plan,  # noqa: F401
-                      prefill, prefill_plan, FI_DTYPE_BF16, FI_DTYPE_F32)
+from .binding import (FiError, Plan, PrefillPlan, decode, decode_noalloc, lib,  # noqa: F401
+                      merge_states, plan, prefill, prefill_plan, FI_DTYPE_BF16, FI_DTYPE_F32)

@@ -34,7 +34,9 @@ EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_
             "fi_decode_run_scaled", "fi_merge_states", "fi_plan_destroy", "fi_last_error",
             "fi_prefill_plan_create", "fi_prefill_plan_get_info", "fi_prefill_plan_work_list",
             "fi_prefill_plan_merges", "fi_prefill_plan_upload", "fi_prefill_run",
-            "fi_prefill_plan_destroy", "fi_decode_run_rope", "fi_decode_run_rope_scaled"]
+            "fi_prefill_plan_destroy", "fi_decode_run_rope", "fi_decode_run_rope_scaled",
+            "fi_decode_run_noalloc"]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 QITEM_STRIDE = 12
 QMERGE_STRIDE = 8
 PREFILL_ROWS = 256
@@ -63,7 +65,8 @@ class PlanInfo(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("shared_pages", ctypes.c_int64), ("num_prefix_items", ctypes.c_int64),
-                ("num_prefix_groups", ctypes.c_int32), ("prefix_rows_per_item", ctypes.c_int32)]
+                ("num_prefix_groups", ctypes.c_int32), ("prefix_rows_per_item", ctypes.c_int32),
+                ("image_bytes", ctypes.c_int64)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -124,6 +127,8 @@ def lib() -> ctypes.CDLL:
     L.fi_decode_run_rope_scaled.argtypes = [vp, vp, vp, vp, f32, f32, f32, f32, vp, vp, f32, vp,
                                             sz, vp]
     L.fi_decode_run_rope_scaled.restype = i32
+    L.fi_decode_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, sz, vp]
+    L.fi_decode_run_noalloc.restype = i32
     L.fi_merge_states.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i32, vp]
     L.fi_merge_states.restype = i32
     L.fi_plan_destroy.argtypes = [vp]
@@ -371,6 +376,26 @@ def decode(q, k_pages, v_pages, plan_: Plan, out=None, lse=None, sm_scale: Optio
                                       ctypes.c_void_p(k_pages.data_ptr()),
                                       ctypes.c_void_p(v_pages.data_ptr()), float(k_scale),
                                       float(v_scale), o, l, scale, ws, nbytes, s))
+    return out, lse
+
+
+def decode_noalloc(q, k_pages, v_pages, plan_: Plan, workspace, out=None, lse=None,
+                   sm_scale: Optional[float] = None, stream=None):
+    """fi_decode_run_noalloc: the run's partial states and merge counters in
+    the library's static device scratch; ``workspace`` is the buffer the plan
+    was uploaded to (at least info["image_bytes"]). Returns (out, lse)."""
+    if workspace is None:
+        raise ValueError("decode_noalloc needs the workspace the plan was uploaded to")
+    out, lse, workspace = _decode_args(q, k_pages, v_pages, plan_, out, lse, workspace, stream)
+    _check(lib().fi_decode_run_noalloc(plan_.handle, ctypes.c_void_p(q.data_ptr()),
+                                       ctypes.c_void_p(k_pages.data_ptr()),
+                                       ctypes.c_void_p(v_pages.data_ptr()),
+                                       ctypes.c_void_p(out.data_ptr()),
+                                       ctypes.c_void_p(lse.data_ptr()),
+                                       float(sm_scale) if sm_scale else 0.0,
+                                       ctypes.c_void_p(workspace.data_ptr()),
+                                       workspace.numel() * workspace.element_size(),
+                                       ctypes.c_void_p(_stream(stream))))
     return out, lse
 
 

@@ -3,6 +3,7 @@
 // live in plan.cpp and prefill_plan.cpp.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -33,12 +34,14 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // nodes and page ids of the last plan uploaded to its workspace, so it must
 // be that plan: a run of plan A after plan B was uploaded over A's bytes
 // would take B's words for A's requests and pages. Records are address
-// ranges [start, start + workspace bytes of the plan), keyed by start and
-// never overlapping: an upload drops every record its range overlaps
-// (decode and prefill plans alike), a run must find its own plan's record at
-// exactly its workspace, and destroying a plan drops its records. A plan is
-// identified by a serial taken at its first upload, so a new plan that
-// reuses a destroyed plan's address is not mistaken for it.
+// ranges [start, start + extent), keyed by start and never overlapping; the
+// extent is what the plan's runs may touch there (its whole workspace, or
+// only its image when the caller gave no more). An upload drops every record
+// its range overlaps (decode and prefill plans alike), a run must find its
+// own plan's record at exactly its workspace with an extent covering what it
+// touches, and destroying a plan drops its records. A plan is identified by
+// a serial taken at its first upload, so a new plan that reuses a destroyed
+// plan's address is not mistaken for it.
 struct UploadRecord {
   uintptr_t end;
   uint64_t serial;
@@ -57,13 +60,15 @@ void record_upload(const void* workspace, int64_t bytes, uint64_t serial) {
   g_uploads[s] = UploadRecord{e, serial};
 }
 
+// True when the workspace holds this plan's image and its recorded extent
+// covers the `bytes` the run will touch.
 bool holds_plan(const void* workspace, int64_t bytes, uint64_t serial) {
   if (serial == 0) return false;
   const uintptr_t s = reinterpret_cast<uintptr_t>(workspace);
   std::lock_guard<std::mutex> lock(g_uploads_mu);
   const auto it = g_uploads.find(s);
   return it != g_uploads.end() && it->second.serial == serial &&
-         it->second.end == s + (uintptr_t)(bytes > 0 ? bytes : 1);
+         it->second.end >= s + (uintptr_t)(bytes > 0 ? bytes : 1);
 }
 
 void forget_plan(uint64_t serial) {
@@ -74,20 +79,24 @@ void forget_plan(uint64_t serial) {
 }
 
 // Copies a plan's host image into the workspace, asynchronously on `stream`,
-// through a cached pinned staging block.
+// through a cached pinned staging block. The workspace must hold at least
+// the image; the recorded extent is the plan's whole workspace when the
+// caller gave that much, else the image alone.
 template <class Plan>
 fi_status upload(Plan* plan, void* workspace, size_t workspace_bytes, fi_stream_t stream) {
   if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
   if (!workspace) return fail(FI_ERR_INVALID_ARG, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(FI_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-  if ((int64_t)workspace_bytes < plan->ws.total_bytes)
-    return fail(FI_ERR_WORKSPACE, "workspace smaller than the plan's workspace_bytes (" +
-                                      std::to_string(plan->ws.total_bytes) + ")");
+  const int64_t image = (int64_t)plan->image.size();
+  if ((int64_t)workspace_bytes < image)
+    return fail(FI_ERR_WORKSPACE, "workspace smaller than the plan's image (" +
+                                      std::to_string(image) + " bytes)");
   const hipError_t e = fi::staged_upload(workspace, plan->image.data(), plan->image.size(),
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "plan upload");
   if (plan->serial == 0) plan->serial = g_next_serial.fetch_add(1);
-  record_upload(workspace, plan->ws.total_bytes, plan->serial);
+  const int64_t extent = std::min<int64_t>((int64_t)workspace_bytes, plan->ws.total_bytes);
+  record_upload(workspace, std::max<int64_t>(extent, image), plan->serial);
   return FI_OK;
 }
 
@@ -177,8 +186,9 @@ fi_status check_run(const fi_plan* plan, void* out, float* lse, void* workspace,
     return fail(FI_ERR_WORKSPACE, "workspace smaller than fi_plan_info.workspace_bytes");
   if (!holds_plan(workspace, plan->ws.total_bytes, plan->serial))
     return fail(FI_ERR_STATE,
-                "workspace does not hold this plan: it was not uploaded there, or another plan "
-                "was uploaded over it since (call fi_plan_upload)");
+                "workspace does not hold this plan: it was not uploaded there, another plan "
+                "was uploaded over it since, or the upload was given fewer than "
+                "fi_plan_info.workspace_bytes (call fi_plan_upload)");
   return FI_OK;
 }
 
@@ -197,11 +207,29 @@ struct Rope {
   float theta = 0.f, scale = 0.f;
 };
 
+// Where a run keeps what it writes besides out and lse: the merge nodes'
+// arrival counters and the partial states of cut requests.
+struct RunScratch {
+  int32_t* counters;
+  float* part_o;
+  float* part_lse;
+};
+
+RunScratch workspace_scratch(const fi_plan* plan, void* workspace) {
+  char* ws = static_cast<char*>(workspace);
+  return RunScratch{reinterpret_cast<int32_t*>(ws + plan->ws.counters),
+                    reinterpret_cast<float*>(ws + plan->ws.part_o),
+                    reinterpret_cast<float*>(ws + plan->ws.part_lse)};
+}
+
+// Launches the run of an uploaded plan: its image (items, nodes, page ids,
+// prefix items) is read from `workspace`, its scratch from `sc`.
 fi_status launch_run(const fi_plan* plan, const void* q, const void* k_pages,
                      const void* v_pages, float k_scale, float v_scale, void* out, float* lse,
-                     float sm_scale, void* workspace, hipStream_t s, Rope rope = Rope()) {
+                     float sm_scale, const void* workspace, const RunScratch& sc, hipStream_t s,
+                     Rope rope = Rope()) {
   if (!(sm_scale > 0.f)) sm_scale = 1.0f / std::sqrt((float)plan->head_dim);
-  char* ws = static_cast<char*>(workspace);
+  const char* ws = static_cast<const char*>(workspace);
   fi::DecodeArgs d{};
   d.items = reinterpret_cast<const int32_t*>(ws + plan->ws.items);
   d.page_ids = reinterpret_cast<const int32_t*>(ws + plan->ws.page_ids);
@@ -210,10 +238,10 @@ fi_status launch_run(const fi_plan* plan, const void* q, const void* k_pages,
   d.v_pages = v_pages;
   d.out = out;
   d.lse = lse;
-  d.part_o = reinterpret_cast<float*>(ws + plan->ws.part_o);
-  d.part_lse = reinterpret_cast<float*>(ws + plan->ws.part_lse);
+  d.part_o = sc.part_o;
+  d.part_lse = sc.part_lse;
   d.nodes = reinterpret_cast<const int32_t*>(ws + plan->ws.nodes);
-  d.counters = reinterpret_cast<int32_t*>(ws + plan->ws.counters);
+  d.counters = sc.counters;
   d.num_items = plan->num_items();
   d.num_qo_heads = plan->num_qo_heads;
   d.num_kv_heads = plan->num_kv_heads;
@@ -271,7 +299,7 @@ fi_status fi_decode_run_scaled(const fi_plan* plan, const void* q, const void* k
   st = check_run(plan, out, lse, workspace, workspace_bytes);
   if (st != FI_OK) return st;
   return launch_run(plan, q, k_pages, v_pages, k_scale, v_scale, out, lse, sm_scale, workspace,
-                    static_cast<hipStream_t>(stream));
+                    workspace_scratch(plan, workspace), static_cast<hipStream_t>(stream));
 }
 
 fi_status fi_decode_run_rope_scaled(const fi_plan* plan, const void* q, const void* k_pages,
@@ -305,7 +333,7 @@ fi_status fi_decode_run_rope_scaled(const fi_plan* plan, const void* q, const vo
   st = check_run(plan, out, lse, workspace, workspace_bytes);
   if (st != FI_OK) return st;
   return launch_run(plan, q, k_pages, v_pages, k_scale, v_scale, out, lse, sm_scale, workspace,
-                    static_cast<hipStream_t>(stream), r);
+                    workspace_scratch(plan, workspace), static_cast<hipStream_t>(stream), r);
 }
 
 fi_status fi_decode_run_rope(const fi_plan* plan, const void* q, const void* k_pages,
@@ -321,6 +349,108 @@ fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
                         void* workspace, size_t workspace_bytes, fi_stream_t stream) {
   return fi_decode_run_scaled(plan, q, k_pages, v_pages, 1.f, 1.f, out, lse, sm_scale, workspace,
                               workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---- the static scratch of fi_decode_run_noalloc
+// One copy of this array per GPU the library runs on, held until the
+// process ends. In host code its name is a host-side stand-in, not a device
+// address: the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is used.
+static __device__ __align__(256) char scratch[FI_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the scratch array.
+fi_status device_scratch(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FI_ERR_UNSUPPORTED, "device ordinal beyond " + std::to_string(kMaxDevices - 1));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the static scratch");
+    if (!p) return fail(FI_ERR_HIP, "hipGetSymbolAddress returned NULL for the static scratch");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return FI_OK;
+}
+
+// Bytes of scratch a plan's run writes: arrival counters, partial outputs
+// and partial LSE, each section on a 256-byte boundary.
+struct ScratchLayout {
+  int64_t counters = 0, part_o = 0, part_lse = 0, total = 0;
+};
+
+ScratchLayout scratch_layout(const fi_plan* plan) {
+  ScratchLayout l;
+  l.counters = 0;
+  l.part_o = fi::align_up(plan->num_nodes() * 4, 256);
+  l.part_lse = l.part_o + fi::align_up(plan->num_slots * plan->group * (int64_t)plan->head_dim * 4, 256);
+  l.total = l.part_lse + fi::align_up(plan->num_slots * plan->group * 4, 256);
+  return l;
+}
+
+__global__ void zero_words_kernel(int32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+fi_status fi_decode_run_noalloc(const fi_plan* plan, const void* q, const void* k_pages,
+                                const void* v_pages, void* out, float* lse, float sm_scale,
+                                const void* workspace, size_t workspace_bytes,
+                                fi_stream_t stream) {
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->batch == 0) return FI_OK;
+  fi_status st = check_inputs(plan, q, k_pages, v_pages);
+  if (st != FI_OK) return st;
+  if (!out) return fail(FI_ERR_INVALID_ARG, "out is NULL");
+  if (!aligned(out, 16)) return fail(FI_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(FI_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  if (!workspace) return fail(FI_ERR_INVALID_ARG, "workspace is NULL");
+  const int64_t image = (int64_t)plan->image.size();
+  if ((int64_t)workspace_bytes < image)
+    return fail(FI_ERR_WORKSPACE, "workspace smaller than fi_plan_info.image_bytes");
+  if (!holds_plan(workspace, image, plan->serial))
+    return fail(FI_ERR_STATE,
+                "workspace does not hold this plan: it was not uploaded there, or another plan "
+                "was uploaded over it since (call fi_plan_upload)");
+  const ScratchLayout l = scratch_layout(plan);
+  if (l.total > (int64_t)FI_NOALLOC_SCRATCH_BYTES)
+    return fail(FI_ERR_WORKSPACE,
+                "the plan's partial states and merge counters need " + std::to_string(l.total) +
+                    " bytes; the static scratch holds " +
+                    std::to_string((int64_t)FI_NOALLOC_SCRATCH_BYTES) +
+                    " (run this plan with fi_decode_run and a workspace)");
+  char* base = nullptr;
+  st = device_scratch(&base);
+  if (st != FI_OK) return st;
+  const RunScratch sc{reinterpret_cast<int32_t*>(base + l.counters),
+                      reinterpret_cast<float*>(base + l.part_o),
+                      reinterpret_cast<float*>(base + l.part_lse)};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nn = plan->num_nodes();
+  if (nn > 0) {
+    // the array keeps the previous call's contents: counters start at zero
+    hipLaunchKernelGGL(zero_words_kernel, dim3((uint32_t)((nn + 255) / 256)), dim3(256), 0, s,
+                       sc.counters, nn);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "scratch counter clear launch");
+  }
+  return launch_run(plan, q, k_pages, v_pages, 1.f, 1.f, out, lse, sm_scale, workspace, sc, s);
 }
 
 fi_status fi_merge_states(fi_dtype dtype, const void* v_a, const float* s_a, const void* v_b,

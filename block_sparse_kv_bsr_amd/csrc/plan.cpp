@@ -506,6 +506,7 @@ fi_status fi_plan_get_info(const fi_plan* p, fi_plan_info* info) {
   r.num_prefix_items = p->num_pitems();
   r.num_prefix_groups = p->num_groups;
   r.prefix_rows_per_item = p->prefix_rows;
+  r.image_bytes = (int64_t)p->image.size();
   *info = r;
   return FI_OK;
 }

@@ -137,6 +137,10 @@ typedef struct {
   int64_t num_prefix_items;  /* shared-prefix work items (0: no cascade) */
   int32_t num_prefix_groups; /* groups of requests sharing a prefix */
   int32_t prefix_rows_per_item; /* query rows one prefix item covers (128) */
+  int64_t image_bytes;       /* the uploaded plan (work list, merge nodes, page
+                                ids, prefix items): the least workspace
+                                fi_plan_upload accepts; workspace_bytes adds
+                                the partial states fi_decode_run keeps there */
 } fi_plan_info;
 
 /* Fields of one work item in the list returned by fi_plan_work_list. */
@@ -271,7 +275,9 @@ fi_status fi_plan_prefix_members(const fi_plan* plan, const int32_t** members, i
  * page ids into the caller's device
  * workspace (asynchronous host-to-device copy on `stream` from a cached
  * page-locked staging block; the plan may be destroyed right after).
- * workspace must be 256-byte aligned and at least info.workspace_bytes long.
+ * workspace must be 256-byte aligned and at least info.image_bytes long;
+ * fi_decode_run needs info.workspace_bytes (it keeps its partial states in
+ * the same buffer), fi_decode_run_noalloc only the image.
  * Call once per plan; the uploaded plan may then serve any number of
  * fi_decode_run calls (e.g. every layer of a step). Uploading is not meant
  * for stream capture: capture the runs, not the upload.
@@ -302,6 +308,33 @@ fi_status fi_plan_upload(fi_plan* plan, void* workspace, size_t workspace_bytes,
 fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
                         const void* v_pages, void* out, float* lse, float sm_scale,
                         void* workspace, size_t workspace_bytes, fi_stream_t stream);
+
+/*
+ * For callers that cannot allocate device memory during the run (code under
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc):
+ * fi_decode_run with its scratch -- the merge nodes' arrival counters and
+ * the partial states of cut requests -- in a static device array of
+ * FI_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends. The call allocates nothing: it clears the
+ * counters with a small kernel and launches the run, both on `stream`,
+ * which must belong to the current device.
+ *
+ * workspace: the buffer the plan was uploaded to (fi_plan_upload); it needs
+ *            only info.image_bytes and is only read.
+ * Other arguments as for fi_decode_run (unit K/V scales, no rotary
+ * embedding).
+ * Errors: FI_ERR_WORKSPACE when the plan's counters and partial states need
+ * more than FI_NOALLOC_SCRATCH_BYTES (then use fi_decode_run with a
+ * workspace), or when workspace_bytes < info.image_bytes; FI_ERR_STATE as
+ * for fi_decode_run. Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (two streams, or two threads) race and give wrong
+ * results; calls in one stream's order are safe.
+ */
+#define FI_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fi_status fi_decode_run_noalloc(const fi_plan* plan, const void* q, const void* k_pages,
+                                const void* v_pages, void* out, float* lse, float sm_scale,
+                                const void* workspace, size_t workspace_bytes,
+                                fi_stream_t stream);
 
 /*
  * fi_decode_run with dequantisation scales: every K element counts as

@@ -108,10 +108,15 @@ def test_run_without_upload_is_state_error():
 
 
 def test_upload_rejects_small_or_misaligned_workspace():
-    p = fb.plan(*[np.asarray(a) for a in GOOD], 8, 2, 128, 16, 100, "bf16")
+    # cut requests: the image (what an upload needs) is smaller than the
+    # whole workspace (image + partial states, what fi_decode_run needs)
+    p = fb.plan([0, 40, 41], list(range(41)), [16, 3], 8, 2, 128, 16, 100, "bf16",
+                fixed_chunk_tokens=64)
     L = fb.lib()
-    ws = p.info["workspace_bytes"]
-    assert L.fi_plan_upload(p.handle, ctypes.c_void_p(0x100000), ws - 1, None) == -3
+    img, ws = p.info["image_bytes"], p.info["workspace_bytes"]
+    assert 0 < img < ws
+    assert L.fi_plan_upload(p.handle, ctypes.c_void_p(0x100000), img - 1, None) == -3
+    assert "image" in L.fi_last_error().decode()
     assert L.fi_plan_upload(p.handle, ctypes.c_void_p(0x100010), ws, None) == -1
     assert L.fi_plan_upload(p.handle, None, ws, None) == -1
 
