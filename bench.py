@@ -40,6 +40,7 @@ COPY_PROBE_MIB = 1024
 # the short name counter summaries use
 KERNELS = {"tile_attend_kernel": ("attn_tile.hip", "tile_attend"),
            "decode_bsr_kernel": ("decode_bsr.hip", "decode_bsr"),
+           "decode_mma_kernel": ("decode_mma.hip", "decode_mma"),
            "prefill_merge_kernel": ("merge_states.hip", "prefill_merge")}
 
 
@@ -408,6 +409,8 @@ def main():
     ap.add_argument("--items-per-cu", type=int, default=0)
     ap.add_argument("--min-chunk-tokens", type=int, default=0)
     ap.add_argument("--fixed-chunk-tokens", type=int, default=0)
+    ap.add_argument("--decode-kernel", type=int, default=0, choices=[0, 1, 2],
+                    help="0 the library's choice, 1 vector-ALU kernel, 2 matrix-core kernel")
     ap.add_argument("--counters-run", action="store_true",
                     help="short run for rocprofv3 --pmc: a copy probe, then a few steps")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -435,7 +438,7 @@ def main():
     dev = torch.device("cuda:0")
     q, k, v = w.make_values(dev)
     opts = dict(items_per_cu=args.items_per_cu, min_chunk_tokens=args.min_chunk_tokens,
-                fixed_chunk_tokens=args.fixed_chunk_tokens)
+                fixed_chunk_tokens=args.fixed_chunk_tokens, decode_kernel=args.decode_kernel)
 
     # host planner time (median of 20) and upload time
     plan_t = []
@@ -478,7 +481,9 @@ def main():
     gbs = nbytes / (med_ms * 1e-3) / 1e9
     # a step is one fi_decode_run: the decode kernel, preceded by the tile
     # kernel when the plan has shared-prefix items
-    kernels = (["tile_attend_kernel"] if p.info["num_prefix_items"] else []) + ["decode_bsr_kernel"]
+    decode_kernel = ("decode_mma_kernel" if p.info["decode_kernel"] == fb.binding.DECODE_KERNEL_MATRIX
+                     and not w.rope_theta else "decode_bsr_kernel")
+    kernels = (["tile_attend_kernel"] if p.info["num_prefix_items"] else []) + [decode_kernel]
     traffic = read_traffic(w.name, kernels)
     result = {
         "metric": METRIC,

@@ -24,6 +24,7 @@ ITEM_STRIDE = 16
 NODE_STRIDE = 8
 PITEM_STRIDE = 8
 MERGE_FAN_IN = 32
+DECODE_KERNEL_AUTO, DECODE_KERNEL_VECTOR, DECODE_KERNEL_MATRIX = 0, 1, 2
 
 STATUS_NAMES = {0: "FI_OK", -1: "FI_ERR_INVALID_ARG", -2: "FI_ERR_UNSUPPORTED",
                 -3: "FI_ERR_WORKSPACE", -4: "FI_ERR_HIP", -5: "FI_ERR_NOMEM", -6: "FI_ERR_STATE"}
@@ -52,7 +53,8 @@ class FiError(RuntimeError):
 class PlanOpts(ctypes.Structure):
     _fields_ = [("num_cus", ctypes.c_int32), ("items_per_cu", ctypes.c_int32),
                 ("min_chunk_tokens", ctypes.c_int32), ("max_chunk_tokens", ctypes.c_int32),
-                ("fixed_chunk_tokens", ctypes.c_int32), ("cascade", ctypes.c_int32)]
+                ("fixed_chunk_tokens", ctypes.c_int32), ("cascade", ctypes.c_int32),
+                ("decode_kernel", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -66,7 +68,7 @@ class PlanInfo(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("shared_pages", ctypes.c_int64), ("num_prefix_items", ctypes.c_int64),
                 ("num_prefix_groups", ctypes.c_int32), ("prefix_rows_per_item", ctypes.c_int32),
-                ("image_bytes", ctypes.c_int64)]
+                ("image_bytes", ctypes.c_int64), ("decode_kernel", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -268,12 +270,14 @@ def _check_lengths(ip: np.ndarray, ix: np.ndarray, lp: np.ndarray) -> int:
 def plan(kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int, num_kv_heads: int,
          head_dim: int, page_size: int, num_pool_pages: int, dtype="bf16",
          num_cus: int = 0, items_per_cu: int = 0, min_chunk_tokens: int = 0,
-         max_chunk_tokens: int = 0, fixed_chunk_tokens: int = 0, cascade: int = 0) -> Plan:
-    """fi_plan_create over host page-table arrays (numpy or CPU tensors)."""
+         max_chunk_tokens: int = 0, fixed_chunk_tokens: int = 0, cascade: int = 0,
+         decode_kernel: int = 0) -> Plan:
+    """fi_plan_create over host page-table arrays (numpy or CPU tensors).
+    decode_kernel: DECODE_KERNEL_AUTO (0), _VECTOR (1) or _MATRIX (2)."""
     ip, ix, lp = _i32(kv_indptr), _i32(kv_indices), _i32(kv_last_page_len)
     batch = _check_lengths(ip, ix, lp)
     opts = PlanOpts(num_cus, items_per_cu, min_chunk_tokens, max_chunk_tokens, fixed_chunk_tokens,
-                    cascade)
+                    cascade, decode_kernel)
     h = ctypes.c_void_p()
     ix_ptr = _ptr32(ix) if ix.size else ctypes.POINTER(ctypes.c_int32)()
     _check(lib().fi_plan_create(_ptr32(ip), ix_ptr, _ptr32(lp), batch, num_qo_heads,

@@ -27,6 +27,7 @@ struct DecodeArgs {
   float k_scale, v_scale;   // K/V dequantisation scales (1 unless fp8)
   bool rope;                // K (and q) stored before the rotary embedding
   float rope_theta, rope_scale;
+  bool mma;                 // run the matrix-core kernel (decode_mma.hip)
 };
 
 struct PrefixArgs {
@@ -73,6 +74,10 @@ struct MergeTwoArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// The matrix-core decode kernel: built for head_dim 128, bf16 or fp8 K/V,
+// G = 1, 2, 4, 8, page sizes that are multiples of 16, no rotary embedding.
+bool decode_mma_supported(const DecodeArgs& a);
+hipError_t launch_decode_mma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge_two(const MergeTwoArgs& a, hipStream_t stream);
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -145,6 +145,13 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
         o.max_chunk_tokens < 0 || o.fixed_chunk_tokens < 0)
       return fail(FI_ERR_INVALID_ARG, "negative planner option");
     if (o.cascade < -1 || o.cascade > 1) return fail(FI_ERR_INVALID_ARG, "cascade must be -1, 0 or 1");
+    if (o.decode_kernel < FI_DECODE_KERNEL_AUTO || o.decode_kernel > FI_DECODE_KERNEL_MATRIX)
+      return fail(FI_ERR_INVALID_ARG, "decode_kernel must be one of FI_DECODE_KERNEL_*");
+    if (o.decode_kernel == FI_DECODE_KERNEL_MATRIX &&
+        (head_dim != 128 || dtype == FI_DTYPE_F32 || page_size % 16 != 0))
+      return fail(FI_ERR_UNSUPPORTED,
+                  "the matrix-core decode kernel needs head_dim 128, bf16 or fp8 K/V and a page "
+                  "size that is a multiple of 16");
     const int64_t num_cus = o.num_cus ? o.num_cus : 256;
     const int64_t items_per_cu = o.items_per_cu ? o.items_per_cu : 8;
     const int64_t min_chunk_tokens = o.min_chunk_tokens ? o.min_chunk_tokens : 256;
@@ -237,6 +244,16 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     if (C > INT32_MAX) C = INT32_MAX;
 
     std::unique_ptr<fi_plan> p(new fi_plan());
+    p->decode_kernel = o.decode_kernel;
+    // The matrix-core kernel was measured faster for fp8 caches and for eight
+    // query heads per KV head (both bound by vector work in the other kernel).
+    const bool mma_fits = head_dim == 128 && dtype != FI_DTYPE_F32 && page_size % 16 == 0;
+    p->resolved_kernel =
+        o.decode_kernel == FI_DECODE_KERNEL_MATRIX ||
+                (o.decode_kernel == FI_DECODE_KERNEL_AUTO && mma_fits &&
+                 (dtype == FI_DTYPE_FP8_E4M3 || num_qo_heads == 8 * num_kv_heads))
+            ? FI_DECODE_KERNEL_MATRIX
+            : FI_DECODE_KERNEL_VECTOR;
     p->batch = batch;
     p->num_qo_heads = num_qo_heads;
     p->num_kv_heads = num_kv_heads;
@@ -507,6 +524,7 @@ fi_status fi_plan_get_info(const fi_plan* p, fi_plan_info* info) {
   r.num_prefix_groups = p->num_groups;
   r.prefix_rows_per_item = p->prefix_rows;
   r.image_bytes = (int64_t)p->image.size();
+  r.decode_kernel = p->resolved_kernel;
   *info = r;
   return FI_OK;
 }

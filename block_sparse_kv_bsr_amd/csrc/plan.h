@@ -53,6 +53,8 @@ struct fi_plan {
   std::vector<int32_t> members; // request ids, grouped
   std::vector<int32_t> prefix_slot;  // [batch * num_kv_heads], empty without groups
   int32_t num_groups = 0, prefix_rows = 0;
+  int32_t decode_kernel = FI_DECODE_KERNEL_AUTO;   // as asked for
+  int32_t resolved_kernel = FI_DECODE_KERNEL_VECTOR;  // what a run without RoPE launches
   std::vector<uint8_t> image;   // host copy of the uploaded part of the workspace
   fi::WorkspaceLayout ws;
   // Identity of this plan in the launch layer's upload records (0 until

@@ -116,7 +116,19 @@ typedef struct {
   int32_t cascade;            /* shared-prefix cascade: 0 = when it pays
                                  (see fi_plan_create), 1 = whenever requests
                                  share a prefix, -1 = never */
+  int32_t decode_kernel;      /* FI_DECODE_KERNEL_*: which decode kernel the
+                                 plan's runs launch */
 } fi_plan_opts;
+
+/* Decode kernels. Both compute the same attention and merge trees, to the
+ * same tolerance; they differ in where the products run. VECTOR: per-lane
+ * dot products and multiply-adds (every dtype, head_dim and page size, the
+ * rotary embedding). MATRIX: scores and PV on the matrix cores
+ * (v_mfma_f32_16x16x32_bf16 / 16x16x16), for head_dim 128, bf16 or fp8 K/V,
+ * page sizes that are multiples of 16 and no rotary embedding; a run that
+ * does not fit it fails with FI_ERR_UNSUPPORTED. AUTO: MATRIX where it was
+ * measured faster (fp8 caches, eight query heads per KV head), else VECTOR. */
+enum { FI_DECODE_KERNEL_AUTO = 0, FI_DECODE_KERNEL_VECTOR = 1, FI_DECODE_KERNEL_MATRIX = 2 };
 
 typedef struct {
   int64_t num_items;         /* work items = (request, KV head, chunk) */
@@ -141,6 +153,9 @@ typedef struct {
                                 ids, prefix items): the least workspace
                                 fi_plan_upload accepts; workspace_bytes adds
                                 the partial states fi_decode_run keeps there */
+  int32_t decode_kernel;     /* FI_DECODE_KERNEL_VECTOR or _MATRIX: the kernel
+                                a run without the rotary embedding launches
+                                (with it: VECTOR) */
 } fi_plan_info;
 
 /* Fields of one work item in the list returned by fi_plan_work_list. */

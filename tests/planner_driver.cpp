@@ -10,7 +10,7 @@
 // Input, whitespace separated, one call after another:
 //   D|P batch num_qo_heads num_kv_heads head_dim page_size num_pool_pages
 //       dtype causal
-//   n_opts opts...          (0: NULL options; D takes 6 fields, P 4)
+//   n_opts opts...          (0: NULL options; D takes 7 fields, P 4)
 //   n_qo qo_indptr...       (P only)
 //   n_indptr kv_indptr...   (-1: NULL pointer, nothing follows)
 //   n_indices kv_indices...
@@ -72,6 +72,7 @@ uint64_t decode_call(const int32_t* hdr, const std::vector<int32_t>& opts, const
     o.max_chunk_tokens = opts[3];
     o.fixed_chunk_tokens = opts[4];
     o.cascade = opts[5];
+    o.decode_kernel = opts[6];
     po = &o;
   }
   fi_plan* p = nullptr;
@@ -145,7 +146,7 @@ int main() {
     for (int32_t& x : opts)
       if (!(std::cin >> x)) return 2;
     const bool prefill = kind == "P";
-    if ((prefill && n_opts != 0 && n_opts != 4) || (!prefill && n_opts != 0 && n_opts != 6))
+    if ((prefill && n_opts != 0 && n_opts != 4) || (!prefill && n_opts != 0 && n_opts != 7))
       return 2;
     Array qo, ip, ix, lp;
     if (prefill && !read_array(&qo)) return 2;

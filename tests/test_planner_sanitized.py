@@ -80,7 +80,9 @@ def malformed_calls():
         (good, {"hq": 6, "hkv": 4}), (good, {"hq": 24, "hkv": 2}), (good, {"d": 96}),
         (good, {"dtype": 7}), (good, {"P": 0}), (good, {"P": 5000}), (good, {"hq": 0}),
         (good, {"pool": -1}), (good, {"dtype": 2, "d": 64}),
-        (good, {"opts": [-1, 0, 0, 0, 0, 0]}), (good, {"opts": [0, 0, 0, 0, -5, 0]}),
+        (good, {"opts": [-1, 0, 0, 0, 0, 0, 0]}), (good, {"opts": [0, 0, 0, 0, -5, 0, 0]}),
+        (good, {"opts": [0, 0, 0, 0, 0, 0, 3]}), (good, {"opts": [0, 0, 0, 0, 0, 0, 2], "d": 64}),
+        (good, {"opts": [0, 0, 0, 0, 0, 0, 2], "P": 8}),
         ((None, [5, 6, 7], [16, 3]), {}), (([0, 2, 3], None, [16, 3]), {}),
         (([0, 2, 3], [5, 6, 7], None), {}),
     ]
@@ -155,7 +157,8 @@ def random_calls(seed=7, n_decode=160, n_prefill=100):
         if rng.random() < 0.7:
             opts = [int(rng.choice([0, 8, 64, 256])), int(rng.choice([0, 1, 4, 8])),
                     int(rng.choice([0, 1, 16, 300])), int(rng.choice([0, 64, 4096])),
-                    int(rng.choice([0, 0, 1, 20, 100])), int(rng.choice([-1, 0, 1]))]
+                    int(rng.choice([0, 0, 1, 20, 100])), int(rng.choice([-1, 0, 1])),
+                    int(rng.choice([0, 1, 2])) if (d == 128 and dtype and P % 16 == 0) else 0]
         out.append(Call("D", B, G * hkv, hkv, d, P, pool, dtype, ip, ix, lp, opts))
     for i in range(n_prefill):
         B = int(rng.integers(1, 7))
