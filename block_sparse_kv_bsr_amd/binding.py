@@ -68,7 +68,8 @@ class PlanInfo(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("shared_pages", ctypes.c_int64), ("num_prefix_items", ctypes.c_int64),
                 ("num_prefix_groups", ctypes.c_int32), ("prefix_rows_per_item", ctypes.c_int32),
-                ("image_bytes", ctypes.c_int64), ("decode_kernel", ctypes.c_int32)]
+                ("image_bytes", ctypes.c_int64), ("decode_kernel", ctypes.c_int32),
+                ("merge_fan_in", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
       wbase = __builtin_amdgcn_readfirstlane(pl);
       fill_window(wbase);
     }
-    const int pid = s_ids[pl - wbase];
+    const int pid = lds_read_id(&s_ids[pl - wbase]);
     const int64_t off = (int64_t)pid * p.page_stride + head_off + (int64_t)sl * R::kKvBytes;
     const char* kp = p.k_pages + off;
     const char* vp = p.v_pages + off;
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_bsr_kernel(DecodeParams p) 
         wbase = pl;
         fill_window(wbase);
       }
-      u_pid = __builtin_amdgcn_readfirstlane(s_ids[pl - wbase]);
+      u_pid = __builtin_amdgcn_readfirstlane(lds_read_id(&s_ids[pl - wbase]));
       u_cached_pl = pl;
     }
     const int64_t base = (int64_t)u_pid * p.page_stride + kvh_off + (int64_t)sl * R::kKvBytes;

@@ -125,6 +125,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)p;
 }
 
+// A 32-bit LDS read (a page id of the window) through inline asm, with its
+// wait in the same block. In front of an ordinary LDS read the compiler
+// waits for every direct-to-LDS load in flight (vmcnt(0)): it cannot tell
+// that they never write this location, and the wait would drain the K/V
+// loads a wave keeps in flight ahead of its work.
+__device__ __forceinline__ int lds_read_id(const int* p) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+
 // Read a ring stage back: n 16-byte chunks at the given LDS addresses, then
 // wait for them. The wait is tied to the outputs so no use can move above it.
 template <int N>

@@ -247,7 +247,7 @@ __global__ __launch_bounds__(64, 2) void decode_mma_kernel(DecodeParams p) {
         wbase = pl;
         fill_window(wbase);
       }
-      const int pid = __builtin_amdgcn_readfirstlane(s_ids[pl - wbase]);
+      const int pid = __builtin_amdgcn_readfirstlane(lds_read_id(&s_ids[pl - wbase]));
       cached_base = (int64_t)pid * p.page_stride + kvh_off;
       cached_pl = pl;
     }
@@ -363,13 +363,14 @@ __global__ __launch_bounds__(64, 2) void decode_mma_kernel(DecodeParams p) {
       for (int dt = 0; dt < 8; ++dt) vr[dt] = mma_lds_tr8<kOff>(va[dt]);
       mma_wait_tied(kr, vr);
       if (j + 2 < nblocks) issue(j + 2, ST);  // this stage's fragments are in registers
+      // the two tiles' product chains alternate (independent accumulators)
+      sc[0] = mma_f32x4_t{0.f, 0.f, 0.f, 0.f};
+      sc[1] = mma_f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        sc[T] = mma_f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int T = 0; T < 2; ++T)
           sc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen_fp8x8(kr[T * 4 + s]), qb[s], sc[T], 0, 0, 0);
-      }
     } else {
       u32x4_t kr[4];
 #pragma unroll
@@ -427,12 +428,16 @@ __global__ __launch_bounds__(64, 2) void decode_mma_kernel(DecodeParams p) {
       }
       const mma_bf16x8_t ph = __builtin_bit_cast(mma_bf16x8_t, u32x4_t{hw[0], hw[1], hw[2], hw[3]});
       const mma_bf16x8_t pl = __builtin_bit_cast(mma_bf16x8_t, u32x4_t{lw[0], lw[1], lw[2], lw[3]});
+      // all hi products, then all lo ones: consecutive products are independent
+      mma_bf16x8_t vt[8];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const mma_bf16x8_t vt = widen_fp8x8(vr[dt]);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, ph, o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pl, o[dt], 0, 0, 0);
+        vt[dt] = widen_fp8x8(vr[dt]);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[dt], ph, o[dt], 0, 0, 0);
       }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[dt], pl, o[dt], 0, 0, 0);
     } else {
       float pv[4];
 #pragma unroll
@@ -446,11 +451,13 @@ __global__ __launch_bounds__(64, 2) void decode_mma_kernel(DecodeParams p) {
       const mma_s16x4_t ph = __builtin_bit_cast(mma_s16x4_t, u32x2_t{hw[0], hw[1]});
       const mma_s16x4_t pl = __builtin_bit_cast(mma_s16x4_t, u32x2_t{lw[0], lw[1]});
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const mma_s16x4_t vt = __builtin_bit_cast(mma_s16x4_t, vr[dt]);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, ph, o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pl, o[dt], 0, 0, 0);
-      }
+      for (int dt = 0; dt < 8; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mma_s16x4_t, vr[dt]), ph,
+                                                          o[dt], 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mma_s16x4_t, vr[dt]), pl,
+                                                          o[dt], 0, 0, 0);
     }
   };
   for (int j = 0; j < nblocks; j += 2) {

@@ -18,7 +18,8 @@
 // order), so a CU that took a layer's longest unit takes the next layer's
 // shortest. Requests cut into several chunks
 // write partial (output, log-sum-exp) states; per KV head a small tree of
-// merge nodes (fan-in FI_MERGE_FAN_IN) combines them inside the same kernel.
+// merge nodes (fan-in at most FI_MERGE_FAN_IN) combines them inside the same
+// kernel.
 //
 // Plain C++17 with no HIP dependency: the planner is tested on CPU-only hosts.
 #include <algorithm>
@@ -118,6 +119,14 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     if (num_qo_heads % num_kv_heads != 0)
       return fail(FI_ERR_INVALID_ARG, "num_qo_heads is not a multiple of num_kv_heads");
     const int32_t group = num_qo_heads / num_kv_heads;
+    // Children per merge node: as many as the merging wave reads in its first
+    // round of loads (64 / float pairs per lane of one partial state, at most
+    // 16), so a merge costs one round trip: 16 up to G * head_dim = 512, 8
+    // at 1024 (64 query / 8 KV heads at d 128, whose merges cost 21 us of 189
+    // at fan-in 32 on the skewed batch, measured).
+    const int64_t pairs_per_lane = ((int64_t)group * head_dim / 2 + 63) / 64;
+    const int64_t fan_in =
+        std::max<int64_t>(2, std::min<int64_t>({(int64_t)FI_MERGE_FAN_IN, 16, 64 / pairs_per_lane}));
     if (group != 1 && group != 2 && group != 4 && group != 8)
       return fail(FI_ERR_UNSUPPORTED, "GQA group size must be 1, 2, 4 or 8");
     if (head_dim != 64 && head_dim != 128)
@@ -186,7 +195,7 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
             while (q < lim && kv_indices[kv_indptr[b] + q] == kv_indices[kv_indptr[b0] + q]) ++q;
             lcp = q;
           }
-          lcp = std::min<int64_t>(lcp, (int64_t)(FI_MERGE_FAN_IN - 1) * FI_PREFIX_MAX_PAGES);
+          lcp = std::min<int64_t>(lcp, (fan_in - 1) * FI_PREFIX_MAX_PAGES);
           const int64_t saved = (int64_t)(j - i - 1) * lcp * page_size * head_dim * 4 * num_kv_heads;
           if (lcp >= 1 && (o.cascade == 1 || saved >= (int64_t(8) << 20))) {
             Group g{};
@@ -207,13 +216,13 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
         i = j;
       }
       // prefix chunks per group: about num_cus prefix items in all, at most
-      // FI_MERGE_FAN_IN - 1 per tree so every tree's first node still has a
-      // decode child (nodes complete only inside the decode kernel)
+      // fan_in - 1 per tree so every tree's first node still has a decode
+      // child (nodes complete only inside the decode kernel)
       int64_t blocks = 0;
       for (const Group& g : groups) blocks += g.row_blocks;
       for (Group& g : groups) {
         const int64_t want = fi::ceil_div(num_cus, std::max<int64_t>(1, blocks * num_kv_heads));
-        g.chunks = std::max<int64_t>(1, std::min<int64_t>({want, g.lcp, FI_MERGE_FAN_IN - 1}));
+        g.chunks = std::max<int64_t>(1, std::min<int64_t>({want, g.lcp, fan_in - 1}));
         // no prefix item spans more than FI_PREFIX_MAX_PAGES pages
         g.chunks = std::max<int64_t>(g.chunks, fi::ceil_div(g.lcp, FI_PREFIX_MAX_PAGES));
       }
@@ -245,6 +254,7 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
 
     std::unique_ptr<fi_plan> p(new fi_plan());
     p->decode_kernel = o.decode_kernel;
+    p->merge_fan_in = (int32_t)fan_in;
     // The matrix-core kernel was measured faster for fp8 caches and for eight
     // query heads per KV head (both bound by vector work in the other kernel).
     const bool mma_fits = head_dim == 128 && dtype != FI_DTYPE_F32 && page_size % 16 == 0;
@@ -349,7 +359,7 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
       for (int32_t h = 0; h < num_kv_heads; ++h) {
         // merge tree of (b, h): leaves take the cpre prefix partials, then
         // the k chunk partials, in slots [leaf_base, leaf_base + nchild);
-        // each level groups FI_MERGE_FAN_IN children
+        // each level groups fan_in children
         const int64_t leaf_base = slot;
         leaf_node.assign((size_t)nchild, -1);
         if (nchild >= 2) {
@@ -359,14 +369,14 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
           int32_t level = 0;
           prev.clear();
           for (;;) {
-            const int64_t ngroups = fi::ceil_div(nch, FI_MERGE_FAN_IN);
+            const int64_t ngroups = fi::ceil_div(nch, fan_in);
             const bool root = ngroups == 1;
             const int64_t out_base = root ? -1 : slot;
             if (!root) slot += ngroups;
             const int32_t first = (int32_t)(nodes.size() / FI_NODE_STRIDE);
             for (int64_t g = 0; g < ngroups; ++g) {
-              const int64_t c0 = g * FI_MERGE_FAN_IN;
-              const int64_t cnt = std::min<int64_t>(FI_MERGE_FAN_IN, nch - c0);
+              const int64_t c0 = g * fan_in;
+              const int64_t cnt = std::min<int64_t>(fan_in, nch - c0);
               // prefix partials (level 0, children [0, cpre)) do not report
               const int64_t quiet = level == 0 ? std::max<int64_t>(0, std::min(cpre, c0 + cnt) - c0) : 0;
               new_node((int32_t)cnt, (int32_t)(cnt - quiet), child_begin + c0,
@@ -374,9 +384,9 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
             }
             for (size_t i = 0; i < prev.size(); ++i)
               nodes[(size_t)prev[i] * FI_NODE_STRIDE + FI_NODE_PARENT] =
-                  first + (int32_t)(i / FI_MERGE_FAN_IN);
+                  first + (int32_t)(i / fan_in);
             if (level == 0)
-              for (int64_t c = 0; c < nchild; ++c) leaf_node[c] = first + (int32_t)(c / FI_MERGE_FAN_IN);
+              for (int64_t c = 0; c < nchild; ++c) leaf_node[c] = first + (int32_t)(c / fan_in);
             prev.clear();
             for (int64_t g = 0; g < ngroups; ++g) prev.push_back(first + (int32_t)g);
             if (root) break;
@@ -525,6 +535,7 @@ fi_status fi_plan_get_info(const fi_plan* p, fi_plan_info* info) {
   r.prefix_rows_per_item = p->prefix_rows;
   r.image_bytes = (int64_t)p->image.size();
   r.decode_kernel = p->resolved_kernel;
+  r.merge_fan_in = p->merge_fan_in;
   *info = r;
   return FI_OK;
 }

@@ -156,6 +156,8 @@ typedef struct {
   int32_t decode_kernel;     /* FI_DECODE_KERNEL_VECTOR or _MATRIX: the kernel
                                 a run without the rotary embedding launches
                                 (with it: VECTOR) */
+  int32_t merge_fan_in;      /* children per merge node at most: 16, or 8 when
+                                G * head_dim = 1024 (see FI_NODE_*) */
 } fi_plan_info;
 
 /* Fields of one work item in the list returned by fi_plan_work_list. */
@@ -180,7 +182,10 @@ enum {
 /*
  * Fields of one merge node in the list returned by fi_plan_merge_nodes.
  * A request cut into k chunks has, per KV head, a tree of merge nodes with
- * at most FI_MERGE_FAN_IN children each: the leaves' children are the chunk
+ * at most fi_plan_info.merge_fan_in children each (never more than
+ * FI_MERGE_FAN_IN; the planner takes as many as the merging wave loads in
+ * one round: 16, or 8 for partials of G * head_dim = 1024 floats): the
+ * leaves' children are the chunk
  * partials, an inner node's children are its child nodes' merged states, and
  * the root writes the request's output. The wave that brings a node's last
  * child merges the children in slot order (so the result does not depend on
@@ -221,7 +226,7 @@ enum {
   FI_PITEM_PAGE_BEGIN = 6,  /* first page, as an index into kv_indices */
   FI_PITEM_NUM_PAGES = 7,   /* at most FI_PREFIX_MAX_PAGES */
   FI_PITEM_STRIDE = 8,
-  FI_PREFIX_MAX_PAGES = 256 /* a group's prefix is at most (FI_MERGE_FAN_IN - 1)
+  FI_PREFIX_MAX_PAGES = 256 /* a group's prefix is at most (merge_fan_in - 1)
                                chunks of this many pages; shared pages past
                                that stay with the decode items */
 };

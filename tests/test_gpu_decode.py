@@ -122,8 +122,8 @@ def test_config_full_size(cfg):
                                            ("f32", 64, 16, 2), ("f32", 128, 8, 8)])
 def test_merge_tree_levels(dtype, d, hq, hkv):
     """One-token chunks on page size 1 cut requests into up to 1100 chunks:
-    in-kernel merge trees of one, two and three levels, a leaf node with a
-    single child (33 chunks), every per-lane merge width, and repeated runs
+    in-kernel merge trees of one to four levels, leaf nodes with a single
+    child, every per-lane merge width, and repeated runs
     on one workspace. The runs alternate between two query sets, so a merge
     that read a partial state left in some cache by the previous run, or a
     counter not returned to zero, would give a wrong result."""
@@ -131,7 +131,11 @@ def test_merge_tree_levels(dtype, d, hq, hkv):
     w = random_workload(41, len(lens), 0, hq, hkv, d, 1, dtype, lens=lens)
     p, (q, k, v), (o0, l0) = run_case(w, what=f"tree-{dtype}-d{d}-G{hq // hkv}",
                                       fixed_chunk_tokens=1)
-    assert p.merge_nodes()[:, 6].max() == 2
+    # levels of the tree over the longest request's 1100 chunks
+    f, n, levels = p.info["merge_fan_in"], 1100, 0
+    while n > 1:
+        n, levels = -(-n // f), levels + 1
+    assert p.merge_nodes()[:, 6].max() == levels - 1 >= 2
     q2 = torch.flip(q, dims=[0]).contiguous()
     o2, l2 = fb.decode(q2, k, v, p)
     torch.cuda.synchronize()
@@ -154,7 +158,7 @@ CASCADE = [
     (3, [(40, 2)], 0, 20, 16, 4, 64, 4, 0),          # two row blocks of members
     (4, [(2, 9)], 1, 9, 4, 4, 64, 3, 3),             # G 1, page size 3 (prefix 30 tokens)
     (5, [(3, 4)], 0, 5, 32, 4, 128, 16, 0),          # G 8
-    (6, [(33, 40), (2, 3)], 4, 300, 32, 8, 128, 16, 64),  # 40-page prefix, 31 chunks
+    (6, [(33, 40), (2, 3)], 4, 300, 32, 8, 128, 16, 64),  # 40-page prefix, fan-in - 1 chunks
     (7, [(6, 5)], 2, 700, 32, 8, 128, 64, 0),        # page size 64
 ]
 

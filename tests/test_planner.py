@@ -113,7 +113,7 @@ def check_plan(w, p, num_cus=256):
                 dyn[r[I_SLOT]] += 1
     roots = {}
     for i, n in enumerate(nodes):
-        assert 1 <= n[N_COUNT] <= MERGE_FAN_IN
+        assert 1 <= n[N_COUNT] <= info["merge_fan_in"] <= MERGE_FAN_IN
         assert 0 <= n[N_SB] and n[N_SB] + n[N_COUNT] <= S
         if n[N_PARENT] < 0:
             assert n[N_OUT] == -1
@@ -349,3 +349,15 @@ def test_cascade_plan_properties(seed, members, pages, singles, P, hkv, fixed):
     w = prefix_workload(seed, [(members, pages)], singles, 50, 4 * hkv, hkv, 64, P, "bf16")
     p = make_plan(w, cascade=1, fixed_chunk_tokens=fixed)
     check_plan(w, p)
+
+
+@pytest.mark.parametrize("hq,hkv,d,want", [(32, 8, 128, 16), (64, 8, 128, 8), (8, 8, 128, 16),
+                                          (32, 4, 64, 16), (8, 1, 64, 16), (16, 2, 128, 8)])
+def test_merge_fan_in_is_what_one_merge_round_loads(hq, hkv, d, want):
+    """A merge node has as many children as the merging wave loads in its first
+    round: 64 / (float pairs per lane of a G x head_dim partial), at most 16."""
+    w = random_workload(77, 3, 3000, hq, hkv, d, 16, "bf16")
+    p = make_plan(w, fixed_chunk_tokens=16)
+    assert p.info["merge_fan_in"] == want
+    nodes = p.merge_nodes()
+    assert nodes[:, N_COUNT].max() == want
