@@ -482,7 +482,7 @@ def main():
     # a step is one fi_decode_run: the decode kernel, preceded by the tile
     # kernel when the plan has shared-prefix items
     decode_kernel = ("decode_mma_kernel" if p.info["decode_kernel"] == fb.binding.DECODE_KERNEL_MATRIX
-                     and not w.rope_theta else "decode_bsr_kernel")
+                     else "decode_bsr_kernel")
     kernels = (["tile_attend_kernel"] if p.info["num_prefix_items"] else []) + [decode_kernel]
     traffic = read_traffic(w.name, kernels)
     result = {

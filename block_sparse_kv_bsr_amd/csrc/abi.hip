@@ -256,10 +256,14 @@ fi_status launch_run(const fi_plan* plan, const void* q, const void* k_pages,
   d.rope = rope.on;
   d.rope_theta = rope.theta;
   d.rope_scale = rope.scale;
-  if (plan->decode_kernel == FI_DECODE_KERNEL_MATRIX && !fi::decode_mma_supported(d))
-    return fail(FI_ERR_UNSUPPORTED,
-                "the plan asks for the matrix-core decode kernel, which has no rotary embedding");
-  d.mma = plan->resolved_kernel == FI_DECODE_KERNEL_MATRIX && fi::decode_mma_supported(d);
+  // Which decode kernel: the one the plan resolved (by default the
+  // matrix-core kernel for fp8 caches and eight query heads per KV head, with
+  // or without the rotary embedding: bound by vector work in the other
+  // kernel, measured).
+  const bool fits = fi::decode_mma_supported(d);
+  if (plan->resolved_kernel == FI_DECODE_KERNEL_MATRIX && !fits)
+    return fail(FI_ERR_UNSUPPORTED, "the matrix-core decode kernel does not fit this run");
+  d.mma = plan->resolved_kernel == FI_DECODE_KERNEL_MATRIX;
   if (plan->num_pitems() > 0) {
     // shared prefixes first: their partials must be in place before the
     // decode kernel's merge trees read them

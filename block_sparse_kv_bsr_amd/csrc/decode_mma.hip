@@ -37,6 +37,11 @@
 //  * 16-byte pieces of each K and V row are XOR-swizzled in LDS (through the
 //    source addresses of the direct-to-LDS loads) so the fragment reads stay
 //    at or below two-way bank conflicts.
+//  * Rotary embedding (same page, JIT section: fused into the kernel; the
+//    cache holds keys before it): a lane's K and q values already form whole
+//    rotate-half pairs (dims i and i + 64 sit in slices s and s + 2), so each
+//    lane turns its own K rows in fp32 and feeds them as hi + lo bf16 parts,
+//    with q turned once and split the same way: S = Kh.Qh + Kh.Ql + Kl.Qh.
 //
 // Lane layouts (checked on the GPU with in-bounds probes): for
 // v_mfma_f32_16x16x32_bf16, A[m][k] sits in lane m + 16 (k/8), element k%8;
@@ -147,6 +152,16 @@ __device__ __forceinline__ void mma_split(float x, float y, uint32_t& hi, uint32
   lo = pack_bf16(x - __uint_as_float(hi << 16), y - __uint_as_float(hi & 0xFFFF0000u));
 }
 
+// Eight floats as two bf16x8 fragments, hi = bf16(x) and lo = bf16(x - hi):
+// hi + lo is within ~2^-17 of x.
+__device__ __forceinline__ void split_x8(const float (&x)[8], mma_bf16x8_t& hi, mma_bf16x8_t& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mma_split(x[2 * i], x[2 * i + 1], h[i], l[i]);
+  hi = __builtin_bit_cast(mma_bf16x8_t, u32x4_t{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(mma_bf16x8_t, u32x4_t{l[0], l[1], l[2], l[3]});
+}
+
 __device__ __forceinline__ float xor16_max(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -156,7 +171,7 @@ __device__ __forceinline__ float xor32_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int kKv, int G, bool kStream>
+template <int kKv, int G, bool kStream, bool kRope>
 __global__ __launch_bounds__(64, 2) void decode_mma_kernel(DecodeParams p) {
   using M = Mma<kKv>;
   constexpr int D = 128;
@@ -204,17 +219,73 @@ __global__ __launch_bounds__(64, 2) void decode_mma_kernel(DecodeParams p) {
   };
   fill_window(0);
 
+  // ---- rotary embedding (K and q stored before it): this lane's K and q
+  // values are dims 32 s + 8 g + e (s < 4, e < 8), and dims i and i + 64 form
+  // a rotate-half pair, so the lane holds 16 whole pairs, i = 32 s + 8 g + e
+  // for s < 2. Pair i turns by pos * freq_i revolutions; freq_i is kept in
+  // LDS as a 64-bit binary fraction of a revolution per position (lane i
+  // computes it in double precision), so pos * freq_i mod 1 is exact.
+  __shared__ uint64_t s_freq[kRope ? 64 : 1];
+  int kv_pos0 = 0;
+  if constexpr (kRope) {
+    double fq = exp2(-(2.0 * lane / D) * p.rope_log2_theta) * p.rope_rev;
+    fq -= floor(fq);
+    s_freq[lane] = (uint64_t)ldexp(fq, 64);
+    __syncthreads();
+    kv_pos0 = it[FI_ITEM_KV_POS];
+  }
+
   // ---- Q^T, the B operand of the score products: lane n + 16g holds
-  // q[head n][32 s + 8 g .. +7] for s = 0..3 (zero columns past G)
-  mma_bf16x8_t qb[4];
+  // q[head n][32 s + 8 g .. +7] for s = 0..3 (zero columns past G). With the
+  // rotary embedding q is turned at the query position in fp32 and carried
+  // as two bf16 parts, qb (hi) and qbl (lo).
+  mma_bf16x8_t qb[4], qbl[kRope ? 4 : 1];
   {
     const char* qr = p.q + (qrow0 + (n < G ? n : 0)) * (D * 2);
+    uint4 raw[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      uint4 v = load16(qr + (32 * s + 8 * g) * 2);
-      if (n >= G) v = make_uint4(0, 0, 0, 0);
-      qb[s] = __builtin_bit_cast(mma_bf16x8_t, v);
+      raw[s] = load16(qr + (32 * s + 8 * g) * 2);
+      if (n >= G) raw[s] = make_uint4(0, 0, 0, 0);
     }
+    if constexpr (!kRope) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qb[s] = __builtin_bit_cast(mma_bf16x8_t, raw[s]);
+    } else {
+      float x[4][8];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t w[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[s][2 * i] = bf16_lo(w[i]);
+          x[s][2 * i + 1] = bf16_hi(w[i]);
+        }
+      }
+      const int qpos = it[FI_ITEM_Q_POS];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float cq, sq;
+          rope_sincos(s_freq[32 * s + 8 * g + e], qpos, cq, sq);
+          const float a = x[s][e], b = x[s + 2][e];
+          x[s][e] = a * cq - b * sq;
+          x[s + 2][e] = b * cq + a * sq;
+        }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) split_x8(x[s], qb[s], qbl[s]);
+    }
+  }
+  // rotation of this lane's 16 pairs at its token of the current score tile
+  // (position kv_pos0 + 16 t + n for the t-th tile of the item), advanced by
+  // 16 positions per tile and recomputed exactly every 32 tiles
+  float rc[kRope ? 2 : 1][8], rs[kRope ? 2 : 1][8], dc[kRope ? 2 : 1][8], dsn[kRope ? 2 : 1][8];
+  if constexpr (kRope) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rope_sincos(s_freq[32 * s + 8 * g + e], 16, dc[s][e], dsn[s][e]);
   }
 
   // ---- direct-to-LDS loads. Wave-wide load i of a block covers rows
@@ -355,7 +426,84 @@ __global__ __launch_bounds__(64, 2) void decode_mma_kernel(DecodeParams p) {
       wait_vmcnt<0>();
     mma_f32x4_t sc[M::kTiles];
     u32x2_t vr[8];
-    if constexpr (kKv == 1) {
+    if constexpr (kRope) {
+      // K of each tile in fp32, turned at its tokens' positions, then as hi +
+      // lo bf16 parts: S = Kh.Qh + Kh.Ql + Kl.Qh (the dropped Kl.Ql is below
+      // 2^-18 of |K||q|)
+      u32x2_t kr8[kKv == 1 ? 8 : 1];
+      u32x4_t kr16[kKv == 1 ? 1 : 4];
+      if constexpr (kKv == 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kr8[i] = mma_lds_b64<kOff>(ka[i]);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) vr[dt] = mma_lds_tr8<kOff>(va[dt]);
+        mma_wait_tied(kr8, vr);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kr16[i] = mma_lds_b128<kOff>(ka[i]);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) vr[dt] = mma_lds_tr16<kOff>(va[dt]);
+        mma_wait_tied(kr16, vr);
+      }
+      if (j + 2 < nblocks) issue(j + 2, ST);
+#pragma unroll
+      for (int T = 0; T < M::kTiles; ++T) {
+        const int tile = j * M::kTiles + T;
+        if ((tile & 31) == 0) {  // exact rotation every 32 tiles
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              rope_sincos(s_freq[32 * s + 8 * g + e], kv_pos0 + 16 * tile + n, rc[s][e], rs[s][e]);
+        }
+        float x[4][8];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if constexpr (kKv == 1) {
+            const u32x2_t w = kr8[T * 4 + s];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const uint32_t ww = h2 ? w.y : w.x;
+              const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(ww, false);
+              const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(ww, true);
+              x[s][4 * h2 + 0] = lo.x;
+              x[s][4 * h2 + 1] = lo.y;
+              x[s][4 * h2 + 2] = hi.x;
+              x[s][4 * h2 + 3] = hi.y;
+            }
+          } else {
+            const uint32_t w[4] = {kr16[s].x, kr16[s].y, kr16[s].z, kr16[s].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[s][2 * i] = bf16_lo(w[i]);
+              x[s][2 * i + 1] = bf16_hi(w[i]);
+            }
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float a = x[s][e], b = x[s + 2][e];
+            x[s][e] = a * rc[s][e] - b * rs[s][e];
+            x[s + 2][e] = b * rc[s][e] + a * rs[s][e];
+            // advance to the next tile's token (16 positions on)
+            const float c2 = rc[s][e] * dc[s][e] - rs[s][e] * dsn[s][e];
+            rs[s][e] = rs[s][e] * dc[s][e] + rc[s][e] * dsn[s][e];
+            rc[s][e] = c2;
+          }
+        mma_f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          mma_bf16x8_t kh, kl;
+          split_x8(x[s], kh, kl);
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qb[s], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qbl[s], sb, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qb[s], sb, 0, 0, 0);
+        }
+        sc[T] = sa + sb;
+      }
+    } else if constexpr (kKv == 1) {
       u32x2_t kr[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) kr[i] = mma_lds_b64<kOff>(ka[i]);
@@ -513,25 +661,25 @@ __global__ __launch_bounds__(64, 2) void decode_mma_kernel(DecodeParams p) {
   finish_split<kKv, D, G>(p, node, lane, reinterpret_cast<float*>(s_ids));
 }
 
-template <int kKv, int G>
+template <int kKv, int G, bool kRope>
 hipError_t launch_mma_typed(const DecodeParams& prm, int64_t num_items, bool stream_kv,
                             hipStream_t stream) {
   if (stream_kv)
-    hipLaunchKernelGGL((decode_mma_kernel<kKv, G, true>), dim3((uint32_t)num_items), dim3(64), 0,
-                       stream, prm);
+    hipLaunchKernelGGL((decode_mma_kernel<kKv, G, true, kRope>), dim3((uint32_t)num_items),
+                       dim3(64), 0, stream, prm);
   else
-    hipLaunchKernelGGL((decode_mma_kernel<kKv, G, false>), dim3((uint32_t)num_items), dim3(64), 0,
-                       stream, prm);
+    hipLaunchKernelGGL((decode_mma_kernel<kKv, G, false, kRope>), dim3((uint32_t)num_items),
+                       dim3(64), 0, stream, prm);
   return hipGetLastError();
 }
 
-template <int kKv>
+template <int kKv, bool kRope>
 hipError_t launch_mma_group(const DecodeParams& prm, int64_t n, int G, bool st, hipStream_t s) {
   switch (G) {
-    case 1: return launch_mma_typed<kKv, 1>(prm, n, st, s);
-    case 2: return launch_mma_typed<kKv, 2>(prm, n, st, s);
-    case 4: return launch_mma_typed<kKv, 4>(prm, n, st, s);
-    case 8: return launch_mma_typed<kKv, 8>(prm, n, st, s);
+    case 1: return launch_mma_typed<kKv, 1, kRope>(prm, n, st, s);
+    case 2: return launch_mma_typed<kKv, 2, kRope>(prm, n, st, s);
+    case 4: return launch_mma_typed<kKv, 4, kRope>(prm, n, st, s);
+    case 8: return launch_mma_typed<kKv, 8, kRope>(prm, n, st, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -539,16 +687,19 @@ hipError_t launch_mma_group(const DecodeParams& prm, int64_t n, int G, bool st, 
 }  // namespace
 
 bool decode_mma_supported(const DecodeArgs& a) {
-  return !a.rope && a.head_dim == 128 && (a.kv_bytes == 1 || a.kv_bytes == 2) &&
-         a.page_size % 16 == 0 && (a.group == 1 || a.group == 2 || a.group == 4 || a.group == 8);
+  return a.head_dim == 128 && (a.kv_bytes == 1 || a.kv_bytes == 2) && a.page_size % 16 == 0 &&
+         (a.group == 1 || a.group == 2 || a.group == 4 || a.group == 8);
 }
 
 hipError_t launch_decode_mma(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_items <= 0) return hipSuccess;
   if (!decode_mma_supported(a)) return hipErrorInvalidValue;
   const DecodeParams prm = make_decode_params(a);
-  if (a.kv_bytes == 1) return launch_mma_group<1>(prm, a.num_items, a.group, a.stream_kv, stream);
-  return launch_mma_group<2>(prm, a.num_items, a.group, a.stream_kv, stream);
+  if (a.rope)
+    return a.kv_bytes == 1 ? launch_mma_group<1, true>(prm, a.num_items, a.group, a.stream_kv, stream)
+                           : launch_mma_group<2, true>(prm, a.num_items, a.group, a.stream_kv, stream);
+  return a.kv_bytes == 1 ? launch_mma_group<1, false>(prm, a.num_items, a.group, a.stream_kv, stream)
+                         : launch_mma_group<2, false>(prm, a.num_items, a.group, a.stream_kv, stream);
 }
 
 }  // namespace fi

@@ -54,7 +54,7 @@ struct fi_plan {
   std::vector<int32_t> prefix_slot;  // [batch * num_kv_heads], empty without groups
   int32_t num_groups = 0, prefix_rows = 0;
   int32_t decode_kernel = FI_DECODE_KERNEL_AUTO;   // as asked for
-  int32_t resolved_kernel = FI_DECODE_KERNEL_VECTOR;  // what a run without RoPE launches
+  int32_t resolved_kernel = FI_DECODE_KERNEL_VECTOR;  // what the runs launch
   int32_t merge_fan_in = FI_MERGE_FAN_IN;             // children per merge node at most
   std::vector<uint8_t> image;   // host copy of the uploaded part of the workspace
   fi::WorkspaceLayout ws;

@@ -122,12 +122,12 @@ typedef struct {
 
 /* Decode kernels. Both compute the same attention and merge trees, to the
  * same tolerance; they differ in where the products run. VECTOR: per-lane
- * dot products and multiply-adds (every dtype, head_dim and page size, the
- * rotary embedding). MATRIX: scores and PV on the matrix cores
- * (v_mfma_f32_16x16x32_bf16 / 16x16x16), for head_dim 128, bf16 or fp8 K/V,
- * page sizes that are multiples of 16 and no rotary embedding; a run that
- * does not fit it fails with FI_ERR_UNSUPPORTED. AUTO: MATRIX where it was
- * measured faster (fp8 caches, eight query heads per KV head), else VECTOR. */
+ * dot products and multiply-adds (every dtype, head_dim and page size).
+ * MATRIX: scores and PV on the matrix cores (v_mfma_f32_16x16x32_bf16 /
+ * 16x16x16), for head_dim 128, bf16 or fp8 K/V and page sizes that are
+ * multiples of 16 (fi_plan_create refuses a MATRIX plan otherwise). AUTO:
+ * MATRIX where it was measured faster and fits -- fp8 caches and eight query
+ * heads per KV head, with or without the rotary embedding -- else VECTOR. */
 enum { FI_DECODE_KERNEL_AUTO = 0, FI_DECODE_KERNEL_VECTOR = 1, FI_DECODE_KERNEL_MATRIX = 2 };
 
 typedef struct {
@@ -154,8 +154,7 @@ typedef struct {
                                 fi_plan_upload accepts; workspace_bytes adds
                                 the partial states fi_decode_run keeps there */
   int32_t decode_kernel;     /* FI_DECODE_KERNEL_VECTOR or _MATRIX: the kernel
-                                a run without the rotary embedding launches
-                                (with it: VECTOR) */
+                                the plan's runs launch */
   int32_t merge_fan_in;      /* children per merge node at most: 16, or 8 when
                                 G * head_dim = 1024 (see FI_NODE_*) */
 } fi_plan_info;

@@ -5,7 +5,8 @@ page sizes that are multiples of 16). Every case runs through each kernel
 it fits, against the float64 oracle: ragged lengths around the 16- and
 32-token blocks, empty requests, forced splits (merge trees), every group
 size, pages of 16 to 4096 tokens, an item longer than the page-id window,
-the three full-size skewed workloads, and repeat runs for bit equality."""
+the rotary embedding, the five full-size skewed workloads, and repeat runs
+for bit equality."""
 import numpy as np
 import pytest
 import torch
@@ -152,10 +153,66 @@ def test_matrix_kernel_refusals():
         fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, 8, 2, 64, 16, w.num_pool_pages, "bf16",
                 decode_kernel=MATRIX)
     assert e.value.status == -2
-    w = random_workload(242, 2, 100, 8, 2, 128, 16, "bf16")
-    q, k, v = (t.cuda() for t in w.make_values("cpu"))
-    p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, 8, 2, 128, 16, w.num_pool_pages, "bf16",
+    w = random_workload(242, 2, 100, 8, 2, 128, 16, "f32")
+    with pytest.raises(fb.FiError) as e:  # an fp32 cache
+        fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, 8, 2, 128, 16, w.num_pool_pages, "f32",
                 decode_kernel=MATRIX)
-    with pytest.raises(fb.FiError) as e:  # no rotary embedding in the matrix kernel
-        fb.decode(q, k, v, p, rope_theta=1e4)
     assert e.value.status == -2
+
+
+def rope_oracle(w, q, k, v, theta, scale):
+    qh = q.float().cpu().numpy()
+    if w.dtype == "fp8":
+        kh = oa.dequantize_e4m3(k.view(torch.uint8).cpu().numpy(), w.k_scale)
+        vh = oa.dequantize_e4m3(v.view(torch.uint8).cpu().numpy(), w.v_scale)
+    else:
+        kh, vh = k.float().cpu().numpy(), v.float().cpu().numpy()
+    return oa.decode_attention_rope(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len,
+                                    w.sm_scale, theta, scale)
+
+
+ROPE_CASES = [
+    # seed, B, maxL, Hq, Hkv, P, dtype, fixed chunk tokens, theta, position scale
+    (251, 4, 1500, 8, 2, 16, "bf16", 0, 1e4, 1.0),
+    (252, 3, 2000, 32, 4, 64, "bf16", 192, 5e5, 1.0),
+    (253, 4, 1500, 8, 2, 16, "fp8", 64, 1e4, 2.0),
+    (254, 3, 2500, 16, 2, 32, "fp8", 0, 5e5, 1.0),
+    (255, 5, 700, 8, 8, 48, "bf16", 48, 1e4, 1.0),
+    (256, 4, 1200, 64, 8, 16, "fp8", 320, 5e5, 1.0),
+]
+
+
+@pytest.mark.parametrize("kernel", [VECTOR, MATRIX], ids=["vector", "matrix"])
+@pytest.mark.parametrize("case", ROPE_CASES, ids=lambda c: f"rope{c[0]}_{c[6]}_G{c[3] // c[4]}_P{c[5]}")
+def test_rope(case, kernel):
+    """The rotary embedding in both kernels: items longer than 32 score tiles
+    (the matrix kernel's exact recomputation interval), chunks that start at
+    nonzero positions, both bases, a position scale, every group size."""
+    seed, B, L, hq, hkv, P, dt, fixed, theta, scale = case
+    w = random_workload(seed, B, L, hq, hkv, 128, P, dt)
+    q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, hq, hkv, 128, P, w.num_pool_pages, dt,
+                cascade=-1, decode_kernel=kernel, fixed_chunk_tokens=fixed)
+    out, lse = fb.decode(q, k, v, p, rope_theta=theta, rope_scale=scale, k_scale=w.k_scale,
+                         v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    O, LSE = rope_oracle(w, q, k, v, theta, scale)
+    st = compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE, True, f"rope{seed}")
+    log(f"[ok] rope{seed} kernel={kernel} {st}")
+
+
+@pytest.mark.parametrize("cfg", [9, 10])
+def test_rope_full_size_skewed(cfg):
+    """Both kernels on the full-size skewed batch with the rotary embedding
+    (bf16 and fp8 caches, theta 5e5), against one oracle evaluation."""
+    w = workload(cfg)
+    q, k, v = w.make_values("cuda")
+    O, LSE = rope_oracle(w, q, k, v, w.rope_theta, w.rope_scale)
+    for kernel in (VECTOR, MATRIX):
+        p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, w.num_qo_heads, w.num_kv_heads,
+                    w.head_dim, w.page_size, w.num_pool_pages, w.dtype, decode_kernel=kernel)
+        out, lse = fb.decode(q, k, v, p, rope_theta=w.rope_theta, rope_scale=w.rope_scale,
+                             k_scale=w.k_scale, v_scale=w.v_scale)
+        torch.cuda.synchronize()
+        st = compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE, True, w.name)
+        log(f"[ok] config {cfg} kernel={kernel} {st}")
