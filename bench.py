@@ -16,7 +16,7 @@ the decode kernel's roofline fraction against 8 TB/s, and the float64 CPU
 oracle timed on the host on the same workload.
 
     python bench.py [--steps K] [--warmup W] [--config 3]
-    python bench.py --config 7|8        # prefill / append: TFLOP/s on matrix cores
+    python bench.py --config 7|8|12     # prefill / append: TFLOP/s on matrix cores
     python bench.py --summarize-counters FETCH.csv WRITE.csv   # rocprofv3 --pmc output
 """
 from __future__ import annotations
@@ -217,7 +217,12 @@ def cpu_baseline_prefill(w, q, k, v, min_seconds=10.0):
     sys.path.insert(0, ROOT)
     import oracle.attention as oa
     ctx, threads = _one_thread()
-    kh, vh = k.float().cpu().numpy(), v.float().cpu().numpy()
+    if w.dtype == "fp8":  # the oracle attends over the dequantised cache
+        import torch
+        kh = oa.dequantize_e4m3(k.view(torch.uint8).cpu().numpy(), w.k_scale)
+        vh = oa.dequantize_e4m3(v.view(torch.uint8).cpu().numpy(), w.v_scale)
+    else:
+        kh, vh = k.float().cpu().numpy(), v.float().cpu().numpy()
     qo = w.qo_indptr
     L = w.kv_lens()
     flops = 0
@@ -327,7 +332,7 @@ def bench_prefill(args, w):
         t0 = time.perf_counter()
         p = fb.prefill_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len,
                             w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
-                            w.num_pool_pages, causal=w.causal,
+                            w.num_pool_pages, causal=w.causal, dtype=w.dtype,
                             fixed_chunk_tokens=args.fixed_chunk_tokens,
                             items_per_cu=args.items_per_cu)
         plan_t.append(time.perf_counter() - t0)
@@ -343,7 +348,8 @@ def bench_prefill(args, w):
     def step(ev):
         if ev:
             ev[0].record()
-        fb.prefill(q, k, v, p, out=out, lse=lse, workspace=ws)
+        fb.prefill(q, k, v, p, out=out, lse=lse, workspace=ws, k_scale=w.k_scale,
+                   v_scale=w.v_scale)
         if ev:
             ev[1].record()
 
@@ -367,11 +373,14 @@ def bench_prefill(args, w):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        # the products are bf16 either way (fp8 K/V are widened on the way
+        # in); config.kv_dtype names the cache's storage type
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_qo_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "page_size": w.page_size, "qo_tokens": w.num_qo_tokens,
+                   "kv_dtype": w.dtype,
                    "kv_tokens": int(w.kv_lens().sum()), "causal": bool(w.causal),
                    "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
                    "parallelism": "single-gpu", "plan_items": p.info["num_items"],

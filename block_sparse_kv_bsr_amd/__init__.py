@@ -7,4 +7,5 @@ plus seeded input generators. ``plan``, ``decode``, ``merge_states``,
 is missing.
 """
 from .binding import (FiError, Plan, PrefillPlan, decode, decode_noalloc, lib,  # noqa: F401
-                      merge_states, plan, prefill, prefill_plan, FI_DTYPE_BF16, FI_DTYPE_F32)
+                      merge_states, plan, prefill, prefill_plan, FI_DTYPE_BF16, FI_DTYPE_F32,
+                      FI_DTYPE_FP8_E4M3)

@@ -36,7 +36,7 @@ EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_
             "fi_prefill_plan_create", "fi_prefill_plan_get_info", "fi_prefill_plan_work_list",
             "fi_prefill_plan_merges", "fi_prefill_plan_upload", "fi_prefill_run",
             "fi_prefill_plan_destroy", "fi_decode_run_rope", "fi_decode_run_rope_scaled",
-            "fi_decode_run_noalloc"]
+            "fi_decode_run_noalloc", "fi_prefill_run_scaled"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 QITEM_STRIDE = 12
 QMERGE_STRIDE = 8
@@ -88,7 +88,8 @@ class PrefillInfo(ctypes.Structure):
                 ("tokens_per_tile", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
                 ("batch", ctypes.c_int32), ("num_qo_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("page_size", ctypes.c_int32), ("causal", ctypes.c_int32)]
+                ("page_size", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -149,6 +150,8 @@ def lib() -> ctypes.CDLL:
     L.fi_prefill_plan_upload.restype = i32
     L.fi_prefill_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
     L.fi_prefill_run.restype = i32
+    L.fi_prefill_run_scaled.argtypes = [vp, vp, vp, vp, f32, f32, vp, vp, f32, vp, sz, vp]
+    L.fi_prefill_run_scaled.restype = i32
     L.fi_prefill_plan_destroy.argtypes = [vp]
     L.fi_prefill_plan_destroy.restype = None
     L.fi_last_error.argtypes = []
@@ -507,15 +510,19 @@ def prefill_plan(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_qo_head
 
 
 def prefill(q, k_pages, v_pages, plan_: PrefillPlan, out=None, lse=None,
-            sm_scale: Optional[float] = None, workspace=None, stream=None):
-    """fi_prefill_run: returns (out [N, H_q, d] bf16, lse [N, H_q] float32)."""
+            sm_scale: Optional[float] = None, workspace=None, stream=None,
+            k_scale: float = 1.0, v_scale: float = 1.0):
+    """fi_prefill_run_scaled: returns (out [N, H_q, d] bf16, lse [N, H_q]
+    float32). k_scale / v_scale dequantise an fp8 KV cache."""
     import torch
     for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
         _require_gpu(t, n)
     info = plan_.info
     N, Hq, d = info["total_qo_tokens"], info["num_qo_heads"], info["head_dim"]
-    if q.dtype != torch.bfloat16 or k_pages.dtype != torch.bfloat16 or v_pages.dtype != torch.bfloat16:
-        raise ValueError("prefill takes bf16 q, k_pages and v_pages")
+    want_kv = {FI_DTYPE_BF16: (torch.bfloat16,),
+               FI_DTYPE_FP8_E4M3: (torch.float8_e4m3fn, torch.uint8)}[info["dtype"]]
+    if q.dtype != torch.bfloat16 or k_pages.dtype not in want_kv or v_pages.dtype not in want_kv:
+        raise ValueError(f"prefill takes bf16 q and k_pages, v_pages one of {want_kv}")
     if tuple(q.shape) != (N, Hq, d):
         raise ValueError(f"q must have shape {(N, Hq, d)}, got {tuple(q.shape)}")
     kshape = (k_pages.shape[0], info["num_kv_heads"], info["page_size"], d)
@@ -533,11 +540,12 @@ def prefill(q, k_pages, v_pages, plan_: PrefillPlan, out=None, lse=None,
     elif workspace.device != q.device:
         raise ValueError(f"workspace is on {workspace.device}, q on {q.device}")
     scale = float(sm_scale) if sm_scale else 0.0
-    _check(lib().fi_prefill_run(plan_.handle, ctypes.c_void_p(q.data_ptr()),
-                                ctypes.c_void_p(k_pages.data_ptr()),
-                                ctypes.c_void_p(v_pages.data_ptr()),
-                                ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
-                                scale, ctypes.c_void_p(workspace.data_ptr()),
-                                workspace.numel() * workspace.element_size(),
-                                ctypes.c_void_p(_stream(stream))))
+    _check(lib().fi_prefill_run_scaled(plan_.handle, ctypes.c_void_p(q.data_ptr()),
+                                       ctypes.c_void_p(k_pages.data_ptr()),
+                                       ctypes.c_void_p(v_pages.data_ptr()), float(k_scale),
+                                       float(v_scale), ctypes.c_void_p(out.data_ptr()),
+                                       ctypes.c_void_p(lse.data_ptr()), scale,
+                                       ctypes.c_void_p(workspace.data_ptr()),
+                                       workspace.numel() * workspace.element_size(),
+                                       ctypes.c_void_p(_stream(stream))))
     return out, lse

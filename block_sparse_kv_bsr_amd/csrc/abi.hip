@@ -124,7 +124,17 @@ fi_status fi_prefill_plan_upload(fi_prefill_plan* plan, void* workspace, size_t 
 fi_status fi_prefill_run(const fi_prefill_plan* plan, const void* q, const void* k_pages,
                          const void* v_pages, void* out, float* lse, float sm_scale,
                          void* workspace, size_t workspace_bytes, fi_stream_t stream) {
+  return fi_prefill_run_scaled(plan, q, k_pages, v_pages, 1.f, 1.f, out, lse, sm_scale, workspace,
+                               workspace_bytes, stream);
+}
+
+fi_status fi_prefill_run_scaled(const fi_prefill_plan* plan, const void* q, const void* k_pages,
+                                const void* v_pages, float k_scale, float v_scale, void* out,
+                                float* lse, float sm_scale, void* workspace,
+                                size_t workspace_bytes, fi_stream_t stream) {
   if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || std::isinf(k_scale) || std::isinf(v_scale))
+    return fail(FI_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (plan->num_items() == 0) return FI_OK;
   if (!q || !out) return fail(FI_ERR_INVALID_ARG, "q or out is NULL");
   if (!k_pages || !v_pages) return fail(FI_ERR_INVALID_ARG, "k_pages or v_pages is NULL");
@@ -159,7 +169,10 @@ fi_status fi_prefill_run(const fi_prefill_plan* plan, const void* q, const void*
   a.page_size = plan->page_size;
   a.group = plan->group;
   a.causal = plan->causal;
+  a.kv_bytes = plan->dtype == FI_DTYPE_FP8_E4M3 ? 1 : 2;
   a.sm_scale = sm_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = fi::launch_prefill(a, s);
   if (e != hipSuccess) return hip_fail(e, "prefill tile kernel launch");

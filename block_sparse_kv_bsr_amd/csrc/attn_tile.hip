@@ -98,22 +98,33 @@ struct TileParams {
   uint32_t page_magic_hi;  // 1 when page_size is 1 (the quotient is then 2^32)
   int group;
   int causal;           // prefill: row r attends VISIBLE + r / G tokens
-  float scale_log2;     // sm_scale * log2(e)
+  float scale_log2;     // sm_scale * k_scale * log2(e)
+  float v_scale;        // multiplies every output and partial state (V dequantisation)
 };
 
-template <int D>
+template <int D, int kKv = 2>
 struct Geom {
-  static constexpr int kRowBytes = D * 2;
+  static constexpr int kRowBytes = D * kKv;               // bf16 (kKv 2) or fp8 E4M3 (kKv 1)
   static constexpr int kPieces = kRowBytes / 16;          // 16-byte pieces per row
   static constexpr int kBlockBytes = kBlock * kRowBytes;  // one K (or V) block
   static constexpr int kRowsPerDma = 1024 / kRowBytes;    // rows one wave-wide load covers
   static constexpr int kDmaPerWave = kBlockBytes / 1024 / kWaves;
-  static constexpr int kStages = D == 128 ? 3 : 5;        // 96 / 80 KiB of K+V in flight
+  // 96 / 80 KiB of bf16 K+V in flight; fp8 blocks are half the bytes
+  static constexpr int kStages = kKv == 1 ? 4 : (D == 128 ? 3 : 5);
   static_assert(kDmaPerWave >= 1, "block does not cover the workgroup");
-  // piece swizzles: K read 16 rows x 1 piece, V read 8 rows x 4 pieces at a time
-  static __device__ __forceinline__ int swz_k(int t) { return t % kPieces; }
+  static_assert(kKv == 2 || D == 128, "the fp8 tile is built for head_dim 128");
+  // piece swizzles: bf16 K is read 16 rows x 1 piece, V 8 rows x 4 pieces at
+  // a time; fp8 K 16 rows x half a piece, V 8 rows (two runs of four, eight
+  // apart) x 1 piece
+  static __device__ __forceinline__ int swz_k(int t) {
+    if constexpr (kKv == 1) return (t >> 1) & 7;
+    else return t % kPieces;
+  }
   static_assert(kStages * 2 * kBlockBytes >= 4 * 32 * D * 4, "ring too small for the final merge");
-  static __device__ __forceinline__ int swz_v(int t) { return (4 * (t % 4)) % kPieces; }
+  static __device__ __forceinline__ int swz_v(int t) {
+    if constexpr (kKv == 1) return (t & 7) ^ (((t >> 3) & 1) << 2);
+    else return (4 * (t % 4)) % kPieces;
+  }
 };
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) { return (uint32_t)(uintptr_t)p; }
@@ -215,6 +226,42 @@ __device__ __forceinline__ void lgkm_wait_tied(u32x2_t (&r)[N][2]) {
   }
 }
 
+// s_waitcnt lgkmcnt(CNT) tied to fp8 K fragments (see lgkm_wait_tied_n).
+template <int CNT>
+__device__ __forceinline__ void lgkm_wait_tied_n8(u32x2_t (&r)[8]) {
+  static_assert(CNT >= 0 && CNT < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
+                 "+v"(r[7])
+               : "i"(CNT)
+               : "memory");
+}
+__device__ __forceinline__ void lgkm_wait_tied4(u32x2_t (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3])::"memory");
+}
+template <int OFF>
+__device__ __forceinline__ u32x2_t lds_b64(uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x2_t r;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF) : "memory");
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2_t lds_tr8_b64(uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF) : "memory");
+  return r;
+}
+// Eight fp8 (E4M3) codes widened to eight bf16 values (exact) in code order.
+__device__ __forceinline__ bf16x8_t widen8(u32x2_t w) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
+  const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
+  const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
+  const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{a, b, c, d});
+}
+
 __device__ __forceinline__ float max_with_partner32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -239,9 +286,10 @@ struct Roles {
 };
 static_assert(FI_PREFILL_ROWS == 32 * 8, "a prefill tile is 8 row groups of 32 rows");
 
-template <int D, bool kPrefill>
+template <int D, bool kPrefill, int kKv = 2>
 __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
-  using Gm = Geom<D>;
+  static_assert(kKv == 2 || kPrefill, "shared-prefix items read bf16 caches");
+  using Gm = Geom<D, kKv>;
   using R = Roles<kPrefill>;
   constexpr int NS = Gm::kStages;
   constexpr int kRB = Gm::kRowBytes;
@@ -324,7 +372,7 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   // are unconditional)
   bf16x8_t qf[D / 16];
   {
-    const char* qrow = p.q + q_index * kRB;
+    const char* qrow = p.q + q_index * (D * 2);  // q is bf16 whatever the cache holds
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       uint4 v = *reinterpret_cast<const uint4*>(qrow + (16 * s + 8 * half) * 2);
@@ -398,7 +446,21 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   const int g16 = lane >> 4, L16 = lane & 15;
   const int v_k = L16 >> 2, v_p = L16 & 3;  // this lane's input role in a transposed read
   uint32_t kb[D / 16], vb[D / 32];
-  {
+  if constexpr (kKv == 1) {
+    // fp8: K fragment q is half a piece (8 codes, dims 16q + 8 half ..) of
+    // row kt; one transposed byte read per step and tile hands each lane 8
+    // tokens of one column: input lane 2 jj + pp of group g16 points at token
+    // 4 (g16/2) + 8 (jj/4) + jj%4 of the step, columns 32t + 16 (g16%2) +
+    // 8 pp .. +7. Both rows' swizzles are step- and sub-block-invariant.
+    const int kt = 32 * wtok + (lane & 31);
+#pragma unroll
+    for (int q = 0; q < D / 16; ++q) kb[q] = kt * kRB + ((q ^ Gm::swz_k(kt)) * 16) + 8 * half;
+    const int jj = L16 >> 1, pp = L16 & 1;
+    const int vt = 32 * wtok + 4 * (g16 >> 1) + 8 * (jj >> 2) + (jj & 3);
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+      vb[t] = vt * kRB + (((2 * t + (g16 & 1)) ^ Gm::swz_v(vt)) * 16) + 8 * pp;
+  } else {
     const int kt = 32 * wtok + (lane & 31);
 #pragma unroll
     for (int q = 0; q < D / 16; ++q) kb[q] = kt * kRB + (((2 * q + half) ^ Gm::swz_k(kt)) * 16);
@@ -432,20 +494,35 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
     // as its own fragments are in, and the scheduling barriers keep the
     // first sub-block's products ahead of the second's wait.
     f32x16_t sc[R::kSub];
-    u32x4_t kv[R::kSub][D / 16];
+    u32x4_t kv[kKv == 2 ? R::kSub : 1][D / 16];   // bf16 fragments
+    u32x2_t kv8[kKv == 1 ? R::kSub : 1][D / 16];  // fp8 fragments (widened to bf16 for the product)
     static_for<R::kSub>([&](auto SB) {
       constexpr int sb = decltype(SB)::value;
 #pragma unroll
-      for (int q = 0; q < D / 16; ++q) kv[sb][q] = lds_b128<32 * sb * kRB>(kst + kb[q]);
+      for (int q = 0; q < D / 16; ++q) {
+        if constexpr (kKv == 1)
+          kv8[sb][q] = lds_b64<32 * sb * kRB>(kst + kb[q]);
+        else
+          kv[sb][q] = lds_b128<32 * sb * kRB>(kst + kb[q]);
+      }
     });
     static_for<R::kSub>([&](auto SB) {
       constexpr int sb = decltype(SB)::value;
-      lgkm_wait_tied_n<(R::kSub - 1 - sb) * (D / 16)>(kv[sb]);
+      if constexpr (kKv == 1)
+        lgkm_wait_tied_n8<(R::kSub - 1 - sb) * (D / 16)>(kv8[sb]);
+      else
+        lgkm_wait_tied_n<(R::kSub - 1 - sb) * (D / 16)>(kv[sb]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[sb][r] = 0.f;
 #pragma unroll
-      for (int q = 0; q < D / 16; ++q)
-        sc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv[sb][q]), qf[q], sc[sb], 0, 0, 0);
+      for (int q = 0; q < D / 16; ++q) {
+        bf16x8_t kf;
+        if constexpr (kKv == 1)
+          kf = widen8(kv8[sb][q]);
+        else
+          kf = __builtin_bit_cast(bf16x8_t, kv[sb][q]);
+        sc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[q], sc[sb], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
     // the loads of a later block go out while the products run
@@ -455,14 +532,19 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
     // arrive during the softmax step below. Step (sb, ks) covers tokens
     // 32 sb + 16 ks .. +15; this lane's A fragment (d = 32t + lane%32) comes
     // from two transposed reads: tokens 4*half + 0..3 of the step, then +8.
-    u32x2_t va[R::kSub * 2][D / 32][2];
+    u32x2_t va[kKv == 2 ? R::kSub * 2 : 1][D / 32][2];
+    u32x2_t va8[kKv == 1 ? R::kSub * 2 : 1][D / 32];  // fp8: one byte-transposed read per tile
     static_for<R::kSub * 2>([&](auto STEP) {
       constexpr int step = decltype(STEP)::value;
       constexpr int kOff = 16 * step * kRB;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) {
-        va[step][t][0] = lds_tr_b64<kOff>(vst + vb[t]);
-        va[step][t][1] = lds_tr_b64<kOff + 8 * kRB>(vst + vb[t]);
+        if constexpr (kKv == 1) {
+          va8[step][t] = lds_tr8_b64<kOff>(vst + vb[t]);
+        } else {
+          va[step][t][0] = lds_tr_b64<kOff>(vst + vb[t]);
+          va[step][t][1] = lds_tr_b64<kOff + 8 * kRB>(vst + vb[t]);
+        }
       }
     });
 
@@ -503,9 +585,14 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
     // products below form one branch-free stretch the scheduler can
     // interleave (one step's products run while the next step's weights are
     // computed)
-    lgkm_wait_tied<D / 32>(va[0]);
+    if constexpr (kKv == 1) {
 #pragma unroll
-    for (int step = 1; step < R::kSub * 2; ++step) lgkm_wait_tied<D / 32>(va[step]);
+      for (int step = 0; step < R::kSub * 2; ++step) lgkm_wait_tied4(va8[step]);
+    } else {
+      lgkm_wait_tied<D / 32>(va[0]);
+#pragma unroll
+      for (int step = 1; step < R::kSub * 2; ++step) lgkm_wait_tied<D / 32>(va[step]);
+    }
 
     // ---- P = exp2(c s - c m), then O^T += V^T . P^T. Step ks of a sub-block
     // takes elements 8ks .. 8ks+7: contraction index 8*half + i is token
@@ -530,18 +617,22 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
         const u32x4_t ph = {phw[0], phw[1], phw[2], phw[3]};
         const u32x4_t pl = {plw[0], plw[1], plw[2], plw[3]};
         const int step = 2 * sb + ks;
+        bf16x8_t vfr[D / 32];
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
-          const u32x4_t av = {va[step][t][0][0], va[step][t][0][1], va[step][t][1][0], va[step][t][1][1]};
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                         __builtin_bit_cast(bf16x8_t, ph), o[t], 0, 0, 0);
+          if constexpr (kKv == 1) {
+            vfr[t] = widen8(va8[step][t]);
+          } else {
+            const u32x4_t av = {va[step][t][0][0], va[step][t][0][1], va[step][t][1][0], va[step][t][1][1]};
+            vfr[t] = __builtin_bit_cast(bf16x8_t, av);
+          }
         }
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          const u32x4_t av = {va[step][t][0][0], va[step][t][0][1], va[step][t][1][0], va[step][t][1][1]};
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                         __builtin_bit_cast(bf16x8_t, pl), o[t], 0, 0, 0);
-        }
+        for (int t = 0; t < D / 32; ++t)
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[t], __builtin_bit_cast(bf16x8_t, ph), o[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[t], __builtin_bit_cast(bf16x8_t, pl), o[t], 0, 0, 0);
       }
     }
     l_run += sum_with_partner32(ps);
@@ -585,7 +676,9 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   // o = 0 and lse = -inf
   if (!row_ok) return;
   const bool empty = l_run == 0.f;
-  const float inv = empty ? 0.f : 1.f / l_run;
+  // V's dequantisation scale (1 for bf16) multiplies outputs and partial
+  // states alike: the merge of partials is linear in them
+  const float inv = empty ? 0.f : p.v_scale / l_run;
   // log2 units of the scaled scores (m_run is an unscaled score)
   const float lse2 = empty ? -INFINITY : m_run * c + __builtin_amdgcn_logf(l_run);
   if (kPrefill && slot_base < 0) {
@@ -653,6 +746,7 @@ hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream) {
   set_page_magic(p);
   p.group = a.group;
   p.scale_log2 = a.sm_scale * kLog2e;
+  p.v_scale = 1.f;
   const dim3 grid((uint32_t)a.num_items), block(64 * kWaves);
   if (a.head_dim == 128) hipLaunchKernelGGL((tile_attend_kernel<128, false>), grid, block, 0, stream, p);
   else if (a.head_dim == 64) hipLaunchKernelGGL((tile_attend_kernel<64, false>), grid, block, 0, stream, p);
@@ -672,7 +766,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.v_pages = static_cast<const char*>(a.v_pages);
   p.part_o = a.part_o;
   p.part_lse = a.part_lse;
-  const int64_t row = (int64_t)a.head_dim * 2;
+  const int64_t row = (int64_t)a.head_dim * a.kv_bytes;
   p.head_stride = (int64_t)a.page_size * row;
   p.page_stride = (int64_t)a.num_kv_heads * a.page_size * row;
   p.num_qo_heads = a.num_qo_heads;
@@ -681,11 +775,20 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   set_page_magic(p);
   p.group = a.group;
   p.causal = a.causal;
-  p.scale_log2 = a.sm_scale * kLog2e;
+  // K's dequantisation scale multiplies every score, V's the outputs
+  p.scale_log2 = a.sm_scale * a.k_scale * kLog2e;
+  p.v_scale = a.v_scale;
   const dim3 grid((uint32_t)a.num_items), block(64 * kWaves);
-  if (a.head_dim == 128) hipLaunchKernelGGL((tile_attend_kernel<128, true>), grid, block, 0, stream, p);
-  else if (a.head_dim == 64) hipLaunchKernelGGL((tile_attend_kernel<64, true>), grid, block, 0, stream, p);
-  else return hipErrorInvalidValue;
+  if (a.kv_bytes == 1) {
+    if (a.head_dim != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((tile_attend_kernel<128, true, 1>), grid, block, 0, stream, p);
+  } else if (a.head_dim == 128) {
+    hipLaunchKernelGGL((tile_attend_kernel<128, true>), grid, block, 0, stream, p);
+  } else if (a.head_dim == 64) {
+    hipLaunchKernelGGL((tile_attend_kernel<64, true>), grid, block, 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

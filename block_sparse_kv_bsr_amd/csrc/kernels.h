@@ -58,7 +58,9 @@ struct PrefillArgs {
   float* part_lse;          // [slots, FI_PREFILL_ROWS], log2 units
   int64_t num_items, num_merges;
   int32_t num_qo_heads, num_kv_heads, head_dim, page_size, group, causal;
+  int32_t kv_bytes;         // 2 bf16, 1 fp8 e4m3 (q/out bf16)
   float sm_scale;
+  float k_scale, v_scale;   // K/V dequantisation scales (1 for bf16)
 };
 
 struct MergeTwoArgs {
@@ -75,7 +77,8 @@ struct MergeTwoArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // The matrix-core decode kernel: built for head_dim 128, bf16 or fp8 K/V,
-// G = 1, 2, 4, 8, page sizes that are multiples of 16, no rotary embedding.
+// G = 1, 2, 4, 8, page sizes that are multiples of 16, with or without the
+// rotary embedding.
 bool decode_mma_supported(const DecodeArgs& a);
 hipError_t launch_decode_mma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge_two(const MergeTwoArgs& a, hipStream_t stream);

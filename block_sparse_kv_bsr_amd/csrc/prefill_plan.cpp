@@ -68,7 +68,10 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
       return fail(FI_ERR_UNSUPPORTED, "GQA group size above " + std::to_string(FI_PREFILL_ROWS));
     if (head_dim != 64 && head_dim != 128)
       return fail(FI_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
-    if (dtype != FI_DTYPE_BF16) return fail(FI_ERR_UNSUPPORTED, "prefill needs FI_DTYPE_BF16");
+    if (dtype != FI_DTYPE_BF16 && dtype != FI_DTYPE_FP8_E4M3)
+      return fail(FI_ERR_UNSUPPORTED, "prefill needs FI_DTYPE_BF16 or FI_DTYPE_FP8_E4M3");
+    if (dtype == FI_DTYPE_FP8_E4M3 && head_dim != 128)
+      return fail(FI_ERR_UNSUPPORTED, "fp8 prefill is built for head_dim 128");
     std::vector<int64_t> kvlen;
     {
       const fi_status st = fi::check_page_table(kv_indptr, kv_indices, kv_last_page_len, batch,
@@ -104,6 +107,7 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
     p->page_size = page_size;
     p->group = group;
     p->causal = causal ? 1 : 0;
+    p->dtype = dtype;
     p->num_pool_pages = num_pool_pages;
     p->total_qo = total_qo;
     const int64_t T = FI_PREFILL_ROWS / group;  // query tokens per tile
@@ -297,6 +301,7 @@ fi_status fi_prefill_plan_get_info(const fi_prefill_plan* p, fi_prefill_info* in
   r.head_dim = p->head_dim;
   r.page_size = p->page_size;
   r.causal = p->causal;
+  r.dtype = p->dtype;
   *info = r;
   return FI_OK;
 }

@@ -54,6 +54,8 @@ CONFIG_NAMES = {
     10: "skewed_b64_loguniform_32_32768_fp8kv_rope",
     # the skewed batch at 64 query heads per 8 KV heads (group 8)
     11: "skewed_b64_loguniform_32_32768_g8",
+    # the append batch over an fp8 KV cache
+    12: "append_b64_q128_skewed_fp8kv",
 }
 
 # Rotary embedding base of the rope workload (the Llama-3 value).
@@ -264,20 +266,27 @@ class PrefillWorkload(Workload):
 
     def make_values(self, device="cpu"):
         """(q [N, H_q, d], k_pool, v_pool) drawn like the decode workloads:
-        q, then K, then V, N(0, 1) float32 cast to the dtype."""
+        q, then K, then V, N(0, 1) float32 cast to bf16; an fp8 cache holds
+        x / k_scale (resp. v_scale) of the same draws as float8_e4m3fn."""
         import torch
 
-        if self.dtype != "bf16":
-            raise ValueError("prefill workloads are bf16")
+        if self.dtype not in ("bf16", "fp8"):
+            raise ValueError("prefill workloads are bf16 or fp8 (K/V)")
         g = torch.Generator(device=device)
         g.manual_seed(self.value_seed)
         Hq, Hkv, d, P = self.num_qo_heads, self.num_kv_heads, self.head_dim, self.page_size
         N = self.num_pool_pages
 
-        def draw(shape):
-            return torch.randn(shape, generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+        def draw(shape, scale=None):
+            x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+            if scale is None:
+                return x.to(torch.bfloat16)
+            self._poison(x, device)  # NaN stays NaN through the cast
+            return (x / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
 
         q = draw((self.num_qo_tokens, Hq, d))
+        if self.dtype == "fp8":
+            return q, draw((N, Hkv, P, d), self.k_scale), draw((N, Hkv, P, d), self.v_scale)
         k = draw((N, Hkv, P, d))
         v = draw((N, Hkv, P, d))
         self._poison(k, device)
@@ -296,7 +305,8 @@ def prefill_workload(config_id: int) -> PrefillWorkload:
     prefill), page size 16, pool with 20% spare pages. 8: the skewed batch's
     64 histories (log-uniform lengths in [32, 32768]) with their newest
     min(128, L_b) tokens as queries (a chunk appended to each request).
-    32 query / 8 KV heads, head_dim 128, bf16."""
+    32 query / 8 KV heads, head_dim 128, bf16. 12: config 8 over an fp8
+    (E4M3) KV cache with scales 1/64."""
     rng = np.random.default_rng([config_id, 0])
     seed = 1_000_003 * config_id + 1
     if config_id == 7:
@@ -311,6 +321,10 @@ def prefill_workload(config_id: int) -> PrefillWorkload:
                                base.num_pool_pages, base.kv_indptr, base.kv_indices,
                                base.last_page_len, base.unused_pages, seed,
                                qo_indptr=_qo_indptr(qo), causal=True)
+    if config_id == 12:
+        return dataclasses.replace(prefill_workload(8), name=CONFIG_NAMES[12], config_id=12,
+                                   dtype="fp8", value_seed=seed, k_scale=FP8_SCALE,
+                                   v_scale=FP8_SCALE)
     raise ValueError(f"unknown prefill config {config_id}")
 
 
@@ -319,9 +333,10 @@ def random_prefill_workload(seed: int, batch: int, max_len: int, num_qo_heads: i
                             causal: bool = True, max_qo: Optional[int] = None,
                             lens: Optional[List[int]] = None,
                             qo_lens: Optional[List[int]] = None,
-                            spare_pages: int = 3) -> PrefillWorkload:
+                            spare_pages: int = 3, dtype: str = "bf16") -> PrefillWorkload:
     """Small ragged prefill case: KV lengths U{1..max_len} (or given), query
-    counts U{1..min(L_b, max_qo)} (or given; 0 allowed), bf16."""
+    counts U{1..min(L_b, max_qo)} (or given; 0 allowed), bf16 or an fp8 K/V
+    cache (scales 1/64)."""
     rng = np.random.default_rng([seed, 13])
     if lens is None:
         lens = [int(x) for x in rng.integers(1, max_len + 1, size=batch)]
@@ -331,9 +346,11 @@ def random_prefill_workload(seed: int, batch: int, max_len: int, num_qo_heads: i
     npg = sum((L + page_size - 1) // page_size for L in lens)
     pool = npg + spare_pages
     ip, ix, lp, un = paged_structure(lens, page_size, pool, rng)
+    scale = FP8_SCALE if dtype == "fp8" else 1.0
     return PrefillWorkload(f"prefill_{seed}", 0, len(lens), num_qo_heads, num_kv_heads, head_dim,
-                           page_size, "bf16", pool, ip, ix, lp, un, 30_000 + seed,
-                           qo_indptr=_qo_indptr(qo_lens), causal=causal)
+                           page_size, dtype, pool, ip, ix, lp, un, 30_000 + seed,
+                           qo_indptr=_qo_indptr(qo_lens), causal=causal,
+                           k_scale=scale, v_scale=scale)
 
 
 def workload(config_id: int) -> Workload:
@@ -359,7 +376,7 @@ def workload(config_id: int) -> Workload:
         return Workload(CONFIG_NAMES[4], 4, 2, 32, 8, 128, 64, "bf16", 3072, ip, ix, lp, un, seed)
     if config_id == 5:
         return _sparse_prefix(rng, seed)
-    if config_id in (7, 8):
+    if config_id in (7, 8, 12):
         return prefill_workload(config_id)
     if config_id == 9:  # the skewed batch, K stored before the rotary embedding
         w = workload(3)

@@ -468,6 +468,7 @@ typedef struct {
   int32_t tokens_per_tile;    /* query tokens per tile: FI_PREFILL_ROWS / G */
   int32_t chunk_tokens;       /* longest KV chunk of an item */
   int32_t batch, num_qo_heads, num_kv_heads, head_dim, page_size, causal;
+  int32_t dtype;              /* fi_dtype of the K/V pages */
 } fi_prefill_info;
 
 /*
@@ -519,7 +520,9 @@ enum {
  *                  tokens; with G not dividing it the last rows are padding)
  * head_dim         64 or 128
  * page_size        1 .. 4096
- * dtype            FI_DTYPE_BF16 (q, K, V, out)
+ * dtype            of the K/V pages: FI_DTYPE_BF16, or FI_DTYPE_FP8_E4M3
+ *                  (head_dim 128; run with fi_prefill_run_scaled); q and
+ *                  out are bf16 either way
  * causal           nonzero: the causal mask above; 0: every query attends all
  * opts             may be NULL
  *
@@ -565,7 +568,8 @@ fi_status fi_prefill_plan_upload(fi_prefill_plan* plan, void* workspace, size_t 
  * host synchronisation. Calls that use the same workspace must not overlap.
  *
  * q        device bf16 [N, num_qo_heads, head_dim], 16-byte aligned
- * k_pages, v_pages  device bf16 [num_pool_pages, num_kv_heads, page_size, head_dim]
+ * k_pages, v_pages  device [num_pool_pages, num_kv_heads, page_size, head_dim]
+ *          in the plan's dtype (bf16, or one byte per fp8 E4M3 code)
  * out      device bf16 [N, num_qo_heads, head_dim] (written)
  * lse      device float32 [N, num_qo_heads] (written); may be NULL
  * sm_scale score scale; <= 0 selects 1/sqrt(head_dim)
@@ -573,6 +577,24 @@ fi_status fi_prefill_plan_upload(fi_prefill_plan* plan, void* workspace, size_t 
 fi_status fi_prefill_run(const fi_prefill_plan* plan, const void* q, const void* k_pages,
                          const void* v_pages, void* out, float* lse, float sm_scale,
                          void* workspace, size_t workspace_bytes, fi_stream_t stream);
+
+/*
+ * fi_prefill_run with K/V dequantisation scales, for an fp8 (E4M3) paged
+ * cache as the JIT-specialisation section of the FlashInfer blog describes
+ * for its decode and append kernels (K/V stored in 8 bits, scores and
+ * outputs computed from the widened values): every K element counts as
+ * k_scale times its stored value and every V element as v_scale times its
+ * stored value, so the scores are sm_scale * k_scale * q.k and the output is
+ * v_scale times the softmax-weighted sum of stored V. The codes are widened
+ * to bf16 exactly on the way into the matrix cores; the products accumulate
+ * in fp32. Valid for every plan dtype (fi_prefill_run is this call with both
+ * scales 1). Scales must be finite and positive (else FI_ERR_INVALID_ARG).
+ * Other arguments, ownership and errors as fi_prefill_run.
+ */
+fi_status fi_prefill_run_scaled(const fi_prefill_plan* plan, const void* q, const void* k_pages,
+                                const void* v_pages, float k_scale, float v_scale, void* out,
+                                float* lse, float sm_scale, void* workspace,
+                                size_t workspace_bytes, fi_stream_t stream);
 
 /* Free a prefill plan (NULL is ignored); host memory only, no wait. */
 void fi_prefill_plan_destroy(fi_prefill_plan* plan);

@@ -191,6 +191,13 @@ def test_prefill_run_checks_on_the_host():
                             None) == -1
     assert L.fi_prefill_plan_upload(p.handle, ctypes.c_void_p(0x100010), ws, None) == -1
     assert L.fi_prefill_plan_upload(p.handle, fake, ws - 1, None) == -3
+    # the scaled run checks its scales first, then the same as fi_prefill_run
+    for ks, vs in ((0.0, 1.0), (1.0, -1.0), (float("inf"), 1.0), (1.0, float("nan"))):
+        st = L.fi_prefill_run_scaled(p.handle, fake, fake, fake, ks, vs, fake, None, 0.0, fake, ws,
+                                     None)
+        assert st == -1 and "scale" in L.fi_last_error().decode(), (ks, vs)
+    assert L.fi_prefill_run_scaled(p.handle, fake, fake, fake, 0.5, 2.0, fake, None, 0.0, fake, ws,
+                                   None) == -6
 
 
 def test_binding_refuses_arrays_shorter_than_the_page_table():

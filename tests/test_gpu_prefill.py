@@ -4,9 +4,9 @@ merge kernel for cut tiles) through the C ABI against the float64 oracle.
 Small ragged cases cover both head sizes, GQA groups 1..8 and one that is
 not a power of two, page sizes 1..64, causal and unmasked, single-chunk
 tiles (direct output) and cut tiles (forced chunk lengths, merge kernel),
-requests with no queries and an unmasked request with no pages. The two
-full-size workloads run with the plan bench.py times and are checked on
-every output element.
+requests with no queries and an unmasked request with no pages, over bf16
+and fp8 (E4M3, dequantisation scales) caches. The full-size workloads run
+with the plan bench.py times and are checked on every output element.
 """
 import time
 
@@ -35,18 +35,33 @@ def log(*a):
 def make_plan(w, **kw):
     return fb.prefill_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len,
                            w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
-                           w.num_pool_pages, causal=w.causal, **kw)
+                           w.num_pool_pages, causal=w.causal, dtype=w.dtype, **kw)
+
+
+def host_kv(w, k, v):
+    """The cache as the oracle reads it: bf16 widened exactly, fp8 codes
+    decoded and multiplied by the dequantisation scales."""
+    if w.dtype == "fp8":
+        return (oa.dequantize_e4m3(k.view(torch.uint8).cpu().numpy(), w.k_scale),
+                oa.dequantize_e4m3(v.view(torch.uint8).cpu().numpy(), w.v_scale))
+    return k.double().cpu().numpy(), v.double().cpu().numpy()
+
+
+def run(w, q, k, v, p, **kw):
+    return fb.prefill(q, k, v, p, k_scale=w.k_scale, v_scale=w.v_scale, **kw)
 
 
 def run_case(w, what, **opts):
     log(f"[case] {what} B={w.batch} N={w.num_qo_tokens} Hq={w.num_qo_heads} "
-        f"Hkv={w.num_kv_heads} d={w.head_dim} P={w.page_size} causal={w.causal} opts={opts}")
+        f"Hkv={w.num_kv_heads} d={w.head_dim} P={w.page_size} causal={w.causal} "
+        f"kv={w.dtype} opts={opts}")
     q, k, v = (t.cuda() for t in w.make_values("cpu"))
     p = make_plan(w, **opts)
-    out, lse = fb.prefill(q, k, v, p)
+    out, lse = run(w, q, k, v, p)
     torch.cuda.synchronize()
     t0 = time.time()
-    qh, kh, vh = (t.double().cpu().numpy() for t in (q, k, v))
+    qh = q.double().cpu().numpy()
+    kh, vh = host_kv(w, k, v)
     O, LSE = oa.prefill_attention(qh, kh, vh, w.qo_indptr, w.kv_indptr, w.kv_indices,
                                   w.last_page_len, w.causal, w.sm_scale)
     stats = compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE, True, what)
@@ -79,6 +94,45 @@ def test_prefill_small(case):
         assert p.info["num_merges"] > 0
 
 
+# fp8 (E4M3) K/V, head_dim 128: groups 1..8 and 6, page sizes 1..64, causal
+# and unmasked, direct output and cut tiles
+FP8_CASES = [
+    # seed, B, maxL, Hq, Hkv, P, causal, max_qo, fixed_chunk
+    (41, 4, 300, 8, 2, 16, True, None, 0),
+    (42, 3, 700, 32, 8, 16, True, None, 128),
+    (43, 3, 90, 4, 4, 1, False, None, 7),
+    (44, 2, 1000, 8, 1, 64, True, 300, 192),
+    (45, 3, 333, 12, 2, 3, False, 200, 0),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: f"seed{c[0]}")
+def test_prefill_fp8_small(case):
+    seed, B, L, Hq, Hkv, P, causal, max_qo, fixed = case
+    w = random_prefill_workload(seed, B, L, Hq, Hkv, 128, P, causal=causal, max_qo=max_qo,
+                                dtype="fp8")
+    p, _, _ = run_case(w, f"fp8 prefill seed{seed}", fixed_chunk_tokens=fixed)
+    assert p.info["dtype"] == fb.FI_DTYPE_FP8_E4M3
+    if fixed:
+        assert p.info["num_merges"] > 0
+
+
+def test_prefill_fp8_whole_prompts_tile_boundaries():
+    lens = [1, 31, 32, 33, 63, 64, 65, 129, 257]
+    w = random_prefill_workload(46, len(lens), 200, 16, 4, 128, 16, causal=True, lens=lens,
+                                qo_lens=lens, dtype="fp8")
+    run_case(w, "fp8 whole prompts")
+
+
+def test_prefill_fp8_scales_are_applied():
+    """The same codes under other scales: K's scale acts inside the softmax
+    (not a plain factor of the output), V's multiplies the output."""
+    import dataclasses
+    base = random_prefill_workload(47, 2, 200, 8, 2, 128, 16, causal=True, dtype="fp8")
+    w = dataclasses.replace(base, k_scale=base.k_scale * 3.0, v_scale=base.v_scale * 0.25)
+    run_case(w, "fp8 prefill, other scales")
+
+
 def test_prefill_edges_no_queries_and_empty_cache():
     # request 0 asks nothing, request 1 has no pages (unmasked: out 0, lse -inf)
     w = random_prefill_workload(21, 3, 80, 8, 2, 128, 16, causal=False, lens=[40, 0, 77],
@@ -99,13 +153,13 @@ def test_prefill_is_deterministic():
     w = random_prefill_workload(23, 3, 600, 8, 2, 128, 16, causal=True)
     q, k, v = (t.cuda() for t in w.make_values("cpu"))
     p = make_plan(w, fixed_chunk_tokens=64)
-    a = fb.prefill(q, k, v, p)
-    b = fb.prefill(q, k, v, p)
+    a = run(w, q, k, v, p)
+    b = run(w, q, k, v, p)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("cfg", [7, 8])
+@pytest.mark.parametrize("cfg", [7, 8, 12])
 def test_prefill_full_size(cfg):
     """Every (query row, head) of the full-size workload, in the launch
     configuration bench.py times, against the oracle evaluated one request
@@ -114,11 +168,13 @@ def test_prefill_full_size(cfg):
     log(f"[case] full-size prefill config {cfg} {w.name} N={w.num_qo_tokens}")
     q, k, v = w.make_values("cuda")
     p = make_plan(w)
-    out, lse = fb.prefill(q, k, v, p)
+    out, lse = run(w, q, k, v, p)
     torch.cuda.synchronize()
     t0 = time.time()
-    # bf16 values are exact in float32; the oracle widens what it gathers
-    kh, vh = k.float().cpu().numpy(), v.float().cpu().numpy()
+    if w.dtype == "fp8":
+        kh, vh = host_kv(w, k, v)
+    else:  # bf16 values are exact in float32; the oracle widens what it gathers
+        kh, vh = k.float().cpu().numpy(), v.float().cpu().numpy()
     qh = q.float().cpu().numpy()
     out_h, lse_h = out.double().cpu().numpy(), lse.double().cpu().numpy()
     del k, v

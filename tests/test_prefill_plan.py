@@ -222,6 +222,8 @@ def _status(qo, ip, ix, lp, Hq=8, Hkv=2, d=128, P=16, pool=100, dtype=1, causal=
     (dict(qo=[0, 3, 2]), -1, "non-decreasing"),
     (dict(qo=[0, 40, 41]), -1, "more query tokens"),
     (dict(dtype=0), -2, "BF16"),
+    (dict(dtype=7), -2, "BF16"),
+    (dict(dtype=2, d=64), -2, "fp8 prefill is built for head_dim 128"),
     (dict(d=96), -2, "head_dim"),
     (dict(Hq=8, Hkv=3), -1, "multiple"),
     (dict(Hq=512, Hkv=1), -2, "group size"),
@@ -232,6 +234,20 @@ def test_prefill_plan_rejects(kw, code, needle):
     args.update(kw)
     st, msg = _status(args.pop("qo"), args.pop("ip"), args.pop("ix"), args.pop("lp"), **args)
     assert st == code and needle in msg, (st, msg)
+
+
+def test_fp8_plan_is_the_bf16_plan_with_its_dtype():
+    """The cache's element type changes no scheduling: same items and merges,
+    and get_info reports the dtype."""
+    qo, ip, ix, lp = [0, 2, 3], [0, 2, 3], [5, 6, 7], [16, 3]
+    a = fb.prefill_plan(np.array(qo), np.array(ip), np.array(ix), np.array(lp), 8, 2, 128, 16, 100)
+    b = fb.prefill_plan(np.array(qo), np.array(ip), np.array(ix), np.array(lp), 8, 2, 128, 16, 100,
+                        dtype="fp8")
+    assert a.info["dtype"] == fb.FI_DTYPE_BF16 and b.info["dtype"] == fb.FI_DTYPE_FP8_E4M3
+    ia, ib = dict(a.info), dict(b.info)
+    ia.pop("dtype"), ib.pop("dtype")
+    assert ia == ib
+    assert np.array_equal(a.work_list(), b.work_list()) and np.array_equal(a.merges(), b.merges())
 
 
 def test_group_size_limit_is_the_tile_height():
