@@ -121,12 +121,109 @@ def summarize_counters(fetch_csv, write_csv, workload_name):
     path = counters_file(workload_name, kernels)
     with open(path, "w") as f:
         f.write(f"# HBM traffic of {' + '.join(kernels)}, workload {workload_name}\n")
-        f.write(f"# from: rocprofv3 --pmc FETCH_SIZE -- python bench.py --config <id> --counters-run\n")
-        f.write(f"#  and: rocprofv3 --pmc WRITE_SIZE -- python bench.py --config <id> --counters-run\n")
+        f.write(f"# from: cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE --output-format csv "
+                f"-d <dir> -o pmc -- python $REPO/bench.py --config <id> --counters-run "
+                f"--no-cpu-baseline\n")
+        f.write(f"#  and: the same with --pmc WRITE_SIZE; then python bench.py --config <id> "
+                f"--summarize-counters <fetch csv> <write csv>\n")
         f.write(f"# each counter scaled by (known bytes / counter) of a {COPY_PROBE_MIB} MiB copy\n")
         f.write(f"source_sha256_16 = {source_digest(kernels)}\n")
         for k, v in out.items():
             f.write(f"{k} = {v:.6g}\n")
+    print(open(path).read())
+
+
+# $REPO is the repository root
+TRACE_COMMAND = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
+                 "-d $REPO/gpurun_out/trace_{cfg} -o trace -- python $REPO/bench.py --config {cfg} "
+                 "--steps 20 --warmup 5 --no-cpu-baseline")
+
+
+def summarize_trace(stats_csv, bench_log, w, config_id):
+    """Write profiles/<kernels>_<workload>.md from a rocprofv3 --stats
+    kernel summary and the bench line printed by the same traced run."""
+    import csv
+    line = [ln for ln in open(bench_log).read().splitlines() if ln.startswith("{")][-1]
+    res = json.loads(line)
+    kernels = res["roofline"]["kernel"].split(" + ")
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                         float(r["Percentage"])))
+    rows.sort(key=lambda x: -x[5])
+    lib = {k: next((r for r in rows if k in r[0]), None) for k in kernels}
+    missing = [k for k, r in lib.items() if r is None]
+    if missing:
+        raise SystemExit(f"{stats_csv}: no dispatch of {missing}")
+    tag = "_".join(KERNELS[k][1] for k in kernels)
+    path = os.path.join(ROOT, "profiles", f"{tag}_{w.name}.md")
+    prefill = hasattr(w, "qo_indptr")
+    kern_us = sum(r[2] for r in lib.values())
+    ev_us = res["us_per_batch"]
+    o = []
+    o.append(f"# {' + '.join(kernels)} — {w.name}\n")
+    desc = (f"batch {w.batch}, {int(w.kv_lens().sum()):,} KV tokens, {w.num_qo_heads} query / "
+            f"{w.num_kv_heads} KV heads, head_dim {w.head_dim}, page size {w.page_size}, "
+            f"K/V {w.dtype}")
+    if prefill:
+        desc += f", {w.num_qo_tokens:,} query tokens ({'causal' if w.causal else 'unmasked'})"
+    if w.rope_theta:
+        desc += f", rotary embedding (theta {w.rope_theta:g}) applied to K in the kernel"
+    o.append(f"Workload (config {config_id}): {desc}.")
+    if prefill:
+        o.append(f"Algorithmic work per batch: {w.flops():,} flop "
+                 f"(4 x head_dim x query heads per attended (query, token) pair).\n")
+    else:
+        o.append(f"Algorithmic bytes per batch: {w.algorithmic_bytes():,} (K+V of every active "
+                 f"token once per KV head + q + output).\n")
+    o.append("Command (one MI355X; $REPO is the repository root):\n")
+    o.append("    " + TRACE_COMMAND.format(cfg=config_id) + "\n")
+    o.append("`--stats` kernel summary, durations in microseconds:\n")
+    o.append("| kernel | calls | avg | min | max | % of GPU time |")
+    o.append("|---|---|---|---|---|---|")
+    for n, c, a, mn, mx, pc in rows[:8]:
+        o.append(f"| {n[:90]} | {c} | {a:.2f} | {mn:.2f} | {mx:.2f} | {pc:.2f} |")
+    o.append("")
+    o.append("The 1 GiB fill and the 1 GiB sum reduction are bench.py's L2/MALL flush "
+             "before each step (outside the timed events); the streaming-read kernel measures "
+             "the practical ceiling; the remaining torch kernels generate inputs.\n")
+    parts = " + ".join(f"{k} {lib[k][2]:.2f}" for k in kernels)
+    o.append(f"Library kernels per step (rocprofv3 averages): {parts} = {kern_us:.2f} us; "
+             f"bench.py in the same run, HIP events around each step: median {ev_us} us "
+             f"(p10-p90 {res['us_per_batch_p10_p90']}).")
+    if prefill:
+        tf_k = w.flops() / (kern_us * 1e-6) / 1e12
+        o.append(f"Achieved: {tf_k:.1f} TFLOP/s ({100 * tf_k / PEAK_BF16_TFLOPS:.1f}% of the "
+                 f"2.5 PFLOP/s bf16 dense peak) by the kernels' own durations; "
+                 f"{res['value']} TFLOP/s ({100 * res['roofline']['frac']:.1f}%) by the events.")
+    else:
+        gb_k = w.algorithmic_bytes() / (kern_us * 1e-6) / 1e9
+        o.append(f"Achieved: {gb_k / 1e3:.2f} TB/s ({100 * gb_k / PEAK_HBM_GBS:.1f}% of 8 TB/s) by "
+                 f"the kernels' own durations; {res['value'] / 1e3:.2f} TB/s "
+                 f"({100 * res['roofline']['frac']:.1f}%) by the events.")
+        if "practical_ceiling" in res:
+            pc = res["practical_ceiling"]
+            o.append(f"Streaming-read ceiling measured in the same run: {pc['gbs'] / 1e3:.2f} TB/s "
+                     f"(the events figure is {100 * pc['frac']:.1f}% of it).")
+    cf = counters_file(w.name, kernels)
+    if os.path.exists(cf):
+        vals = {}
+        for ln in open(cf):
+            if "=" in ln and not ln.startswith("#"):
+                k, v = ln.split("=", 1)
+                vals[k.strip()] = v.strip()
+        if vals.get("source_sha256_16") == source_digest(kernels):
+            fb_ = float(vals["scaled_fetch_bytes_per_step"])
+            wb_ = float(vals["scaled_write_bytes_per_step"])
+            alg = w.algorithmic_bytes()
+            o.append(f"\nHBM traffic per step ({os.path.basename(cf)}, sources "
+                     f"{vals['source_sha256_16']}): FETCH {fb_:.4g} B ({fb_ / alg:.3f}x the "
+                     f"algorithmic bytes), WRITE {wb_:.4g} B.")
+    o.append(f"\nKernel sources sha256[:16]: {source_digest(kernels)}.")
+    with open(path, "w") as f:
+        f.write("\n".join(o) + "\n")
     print(open(path).read())
 
 
@@ -423,6 +520,8 @@ def main():
     ap.add_argument("--counters-run", action="store_true",
                     help="short run for rocprofv3 --pmc: a copy probe, then a few steps")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
+                    help="write the profiles/ summary of a traced run (no GPU)")
     args = ap.parse_args()
 
     sys.path.insert(0, ROOT)
@@ -431,6 +530,9 @@ def main():
 
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, w.name)
+        return 0
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, w, args.config)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
