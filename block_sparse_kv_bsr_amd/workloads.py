@@ -56,6 +56,9 @@ CONFIG_NAMES = {
     11: "skewed_b64_loguniform_32_32768_g8",
     # the append batch over an fp8 KV cache
     12: "append_b64_q128_skewed_fp8kv",
+    # config 5 with the shared prefix held once in a second cache of
+    # 4096-token blocks (composed formats)
+    13: "sparse_prefix_b32_p64_composed_b4096",
 }
 
 # Rotary embedding base of the rope workload (the Llama-3 value).
@@ -376,6 +379,8 @@ def workload(config_id: int) -> Workload:
         return Workload(CONFIG_NAMES[4], 4, 2, 32, 8, 128, 64, "bf16", 3072, ip, ix, lp, un, seed)
     if config_id == 5:
         return _sparse_prefix(rng, seed)
+    if config_id == 13:
+        return _composed_prefix(seed)
     if config_id in (7, 8, 12):
         return prefill_workload(config_id)
     if config_id == 9:  # the skewed batch, K stored before the rotary embedding
@@ -495,3 +500,142 @@ def prefix_workload(seed: int, groups: List[tuple], singles: int, suffix_max: in
     shared_ids = sum(1 for v in np.unique(ix, return_counts=True)[1] if v > 1)
     return Workload(f"prefix_{seed}", 0, len(lists), num_qo_heads, num_kv_heads, head_dim, P,
                     dtype, pool, ip, ix, lp, unused, 20_000 + seed, shared_pages=shared_ids)
+
+
+# ------------------------------------------------------ composed formats
+@dataclasses.dataclass
+class ComposedWorkload(Workload):
+    """Requests whose KV is a shared prefix, held once in a second cache with
+    its own block size, followed by the request's own tokens in the main
+    paged cache. The prefix cache is [num_prefix_pool_pages, H_kv,
+    prefix_page_size, d]; prefix g lists blocks prefix_indices[
+    prefix_indptr[g] : prefix_indptr[g+1]] (all full but the last, which holds
+    prefix_last_page_len[g] tokens); request b begins with prefix
+    prefix_of[b] (-1: none). The inherited page table is the requests' own
+    tokens."""
+    prefix_page_size: int = 0
+    num_prefix_pool_pages: int = 0
+    prefix_indptr: np.ndarray = None
+    prefix_indices: np.ndarray = None
+    prefix_last_page_len: np.ndarray = None
+    prefix_of: np.ndarray = None
+    prefix_unused_pages: np.ndarray = None
+
+    @property
+    def num_prefixes(self) -> int:
+        return len(self.prefix_indptr) - 1
+
+    def prefix_len(self, g: int) -> int:
+        n = int(self.prefix_indptr[g + 1] - self.prefix_indptr[g])
+        return 0 if n == 0 else (n - 1) * self.prefix_page_size + int(self.prefix_last_page_len[g])
+
+    def total_kv_lens(self) -> np.ndarray:
+        """Tokens each request attends: its prefix and its own."""
+        own = self.kv_lens()
+        return np.array([own[b] + (self.prefix_len(int(self.prefix_of[b]))
+                                   if self.prefix_of[b] >= 0 else 0)
+                         for b in range(self.batch)], dtype=np.int64)
+
+    def algorithmic_bytes(self, unique: bool = True) -> int:
+        """K and V of every prefix once (``unique``) or once per member, and
+        of every request's own tokens, per KV head; plus q and the output."""
+        own = int(self.kv_lens().sum())
+        if unique:
+            used = sorted(set(int(g) for g in self.prefix_of if g >= 0))
+            pre = sum(self.prefix_len(g) for g in used)
+        else:
+            pre = sum(self.prefix_len(int(g)) for g in self.prefix_of if g >= 0)
+        kv = 2 * self.num_kv_heads * self.head_dim * (own + pre) * self.kv_elem_bytes
+        qo = 2 * self.batch * self.num_qo_heads * self.head_dim * self.elem_bytes
+        return kv + qo
+
+    def make_values(self, device="cpu"):
+        """(q, k_pool, v_pool, k_prefix, v_prefix): q and the main cache drawn
+        as the decode workloads draw them, then the prefix cache's K and V,
+        N(0, 1) cast to bf16; unlisted pages and the slots past each last
+        page's length hold NaN."""
+        import torch
+
+        if self.dtype != "bf16":
+            raise ValueError("composed workloads are bf16")
+        q, k, v = super().make_values(device)
+        g = torch.Generator(device=device)
+        g.manual_seed(self.value_seed + 1)
+        shape = (self.num_prefix_pool_pages, self.num_kv_heads, self.prefix_page_size,
+                 self.head_dim)
+        kp = torch.randn(shape, generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+        vp = torch.randn(shape, generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+        nan = float("nan")
+        for pool in (kp, vp):
+            if len(self.prefix_unused_pages):
+                idx = torch.as_tensor(self.prefix_unused_pages.astype(np.int64), device=device)
+                pool.index_fill_(0, idx, nan)
+            for gi in range(self.num_prefixes):
+                if self.prefix_indptr[gi + 1] == self.prefix_indptr[gi]:
+                    continue
+                ell = int(self.prefix_last_page_len[gi])
+                if ell < self.prefix_page_size:
+                    last = int(self.prefix_indices[self.prefix_indptr[gi + 1] - 1])
+                    pool[last, :, ell:, :] = nan
+        return q, k, v, kp, vp
+
+
+def random_composed_workload(seed: int, prefix_lens: List[int], members: List[int],
+                             singles: int, own_max: int, num_qo_heads: int, num_kv_heads: int,
+                             head_dim: int, page_size: int, prefix_page_size: int,
+                             spare_pages: int = 2) -> ComposedWorkload:
+    """Small composed case: prefix g has prefix_lens[g] tokens (0 allowed) in
+    blocks of prefix_page_size and members[g] requests (0 allowed); ``singles``
+    requests have no prefix; every request has U{1..own_max} tokens of its own.
+    Batch order, main-cache pages and prefix-cache blocks are seeded
+    permutations."""
+    rng = np.random.default_rng([seed, 17])
+    of = [g for g, m in enumerate(members) for _ in range(m)] + [-1] * singles
+    of = [of[i] for i in rng.permutation(len(of))]
+    lens = [int(x) for x in rng.integers(1, own_max + 1, size=len(of))]
+    npg = sum((L + page_size - 1) // page_size for L in lens)
+    ip, ix, lp, un = paged_structure(lens, page_size, npg + spare_pages, rng)
+    Pp = prefix_page_size
+    nblk = [(L + Pp - 1) // Pp for L in prefix_lens]
+    ppool = sum(nblk) + spare_pages
+    pip, pix, plp, pun = paged_structure(prefix_lens, Pp, ppool, rng)
+    return ComposedWorkload(f"composed_{seed}", 0, len(of), num_qo_heads, num_kv_heads, head_dim,
+                            page_size, "bf16", npg + spare_pages, ip, ix, lp, un, 40_000 + seed,
+                            prefix_page_size=Pp, num_prefix_pool_pages=ppool,
+                            prefix_indptr=pip, prefix_indices=pix, prefix_last_page_len=plp,
+                            prefix_of=np.asarray(of, dtype=np.int32), prefix_unused_pages=pun)
+
+
+def _composed_prefix(seed) -> ComposedWorkload:
+    """Config 5's 32 requests with their shared 8192-token prefix held once
+    in a second cache as two 4096-token blocks (seeded block order in a
+    4-block pool), and each request's own tokens -- the active 64-token
+    blocks of its suffix, as config 5 draws them -- in the main paged cache
+    (page size 64, the prefix pages removed from every list)."""
+    w5 = workload(5)
+    P, prefix_pages = w5.page_size, 128
+    lists, lens = [], []
+    for b in range(w5.batch):
+        pages = [int(x) for x in w5.kv_indices[w5.kv_indptr[b]:w5.kv_indptr[b + 1]]]
+        lists.append(pages[prefix_pages:])
+        lens.append(w5.kv_len(b) - prefix_pages * P)
+    # renumber the suffix pages into a pool of their own (the prefix pages
+    # leave the main cache)
+    used = sorted(set(x for pl in lists for x in pl))
+    rng = np.random.default_rng([13, 1])
+    spare = 8
+    pool = len(used) + spare
+    perm = rng.permutation(pool).astype(np.int32)
+    remap = {old: int(perm[i]) for i, old in enumerate(used)}
+    lists = [[remap[x] for x in pl] for pl in lists]
+    ip, ix, lp = _pack(lists, lens, P)
+    unused = np.sort(perm[len(used):]).astype(np.int32)
+    Pp, nblk, ppool = 4096, 2, 4
+    pperm = rng.permutation(ppool).astype(np.int32)
+    pip, pix, plp = _pack([list(pperm[:nblk])], [prefix_pages * P], Pp)
+    pun = np.sort(pperm[nblk:]).astype(np.int32)
+    return ComposedWorkload(CONFIG_NAMES[13], 13, w5.batch, w5.num_qo_heads, w5.num_kv_heads,
+                            w5.head_dim, P, "bf16", pool, ip, ix, lp, unused,
+                            1_000_003 * 13 + 1, prefix_page_size=Pp, num_prefix_pool_pages=ppool,
+                            prefix_indptr=pip, prefix_indices=pix, prefix_last_page_len=plp,
+                            prefix_of=np.zeros(w5.batch, dtype=np.int32), prefix_unused_pages=pun)

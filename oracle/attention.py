@@ -40,6 +40,13 @@ What it computes, and where that comes from:
   pair turned by the angle (position / rope_scale) * rope_theta^(-2i/d).
   Token t of a request (0-based, listed order) sits at position t; the
   decode query is the newest token, position L - 1.
+* Same explainer, Block-Sparse section, on composable formats: when many
+  requests share one system prompt, the prefix's KV is stored once and only
+  each request's own KV is kept per request, the decomposition being
+  expressed with different block sizes. Reading: a request's KV history is
+  its prefix's tokens (from a second cache with its own block size) followed
+  by its own tokens (from the paged cache); attention runs over that whole
+  history exactly as over one cache.
 * Same explainer, section on where the attention bottleneck lies: prefill
   attends every token of the prompt at once (and is bound by arithmetic, not
   memory). Reading (the pages give no formula): the query tokens of a
@@ -139,6 +146,40 @@ def decode_attention(q, k_pool, v_pool, kv_indptr, kv_indices, last_page_len, sm
             heads = [h for h in range(Hq) if kv_head_of(h, G) == kvh]
             K, V = gather_kv(k_pool, v_pool, toks, kvh)
             o, lse = attend(q[b, heads, :], K, V, sm_scale)
+            O[b, heads, :] = o
+            LSE[b, heads] = lse
+    return O, LSE
+
+
+def decode_attention_composed(q, k_pool, v_pool, kv_indptr, kv_indices, last_page_len,
+                              k_prefix, v_prefix, prefix_indptr, prefix_indices,
+                              prefix_last_page_len, prefix_of, sm_scale=None):
+    """Decode attention over composed formats: request b attends the tokens
+    of prefix prefix_of[b] (none if -1), held in k_prefix / v_prefix
+    [num_prefix_pages, H_kv, P_prefix, d] with page table (prefix_indptr,
+    prefix_indices, prefix_last_page_len), followed by its own tokens in the
+    paged cache (k_pool, v_pool, kv_indptr, kv_indices, last_page_len).
+    Returns float64 O [B, H_q, d] and LSE [B, H_q]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv, P = k_pool.shape[1], k_pool.shape[2]
+    Pp = k_prefix.shape[2]
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    O = np.zeros((B, Hq, d))
+    LSE = np.full((B, Hq), NEG_INF)
+    for b in range(B):
+        own = request_tokens(kv_indptr, kv_indices, last_page_len, P, b)
+        g = int(prefix_of[b])
+        pre = (request_tokens(prefix_indptr, prefix_indices, prefix_last_page_len, Pp, g)
+               if g >= 0 else [])
+        for kvh in range(Hkv):
+            heads = [h for h in range(Hq) if kv_head_of(h, G) == kvh]
+            Kp, Vp = gather_kv(k_prefix, v_prefix, pre, kvh)
+            Ko, Vo = gather_kv(k_pool, v_pool, own, kvh)
+            o, lse = attend(q[b, heads, :], np.concatenate([Kp, Ko]), np.concatenate([Vp, Vo]),
+                            sm_scale)
             O[b, heads, :] = o
             LSE[b, heads] = lse
     return O, LSE

@@ -8,12 +8,14 @@ merging softmax states. They read the oracle through the module object they
 are given, so ``test_oracle_mutations`` can plant a mistake in the oracle and
 show that some pin catches it.
 """
+import dataclasses
 import math
 
 import numpy as np
 import torch
 
-from block_sparse_kv_bsr_amd.workloads import random_prefill_workload, random_workload
+from block_sparse_kv_bsr_amd.workloads import (random_composed_workload, random_prefill_workload,
+                                               random_workload)
 from tests.bruteforce import bruteforce_decode, bruteforce_prefill, rope_rows_loops
 
 
@@ -404,3 +406,100 @@ def pin_rope_decode(mod):
 
 
 ROPE_PINS = [pin_rope_closed_forms, pin_rope_relative, pin_rope_decode]
+
+
+# ---- composed formats: a prefix cache with its own block size + own pages
+COMPOSED_CASES = [
+    # seed, prefix_lens, members, singles, own_max, Hq, Hkv, d, P, P_prefix
+    (1, [40, 0, 17], [2, 1, 2], 1, 30, 4, 2, 8, 4, 16),
+    (2, [100], [3], 0, 20, 4, 1, 8, 1, 64),
+    (3, [33, 64], [1, 2], 2, 9, 8, 2, 4, 16, 32),
+    (4, [5, 129], [2, 2], 1, 40, 2, 2, 8, 16, 1),
+]
+
+
+def _one_cache(w, k, v, kp, vp):
+    """The composed cache rewritten as one cache of 1-token pages: request
+    b's prefix tokens (block by block, slot by slot, the last block up to its
+    length), then its own tokens, each copied to a page of its own. Returns
+    (k1, v1, indptr, indices, last) for the plain decode definition."""
+    Hkv, d = k.shape[1], k.shape[3]
+    rows_k, rows_v, indptr, indices = [], [], [0], []
+    for b in range(w.batch):
+        toks = []
+        g = int(w.prefix_of[b])
+        if g >= 0:
+            first, stop = int(w.prefix_indptr[g]), int(w.prefix_indptr[g + 1])
+            for j in range(first, stop):
+                n = w.prefix_page_size if j + 1 < stop else int(w.prefix_last_page_len[g])
+                toks += [(kp, vp, int(w.prefix_indices[j]), s) for s in range(n)]
+        first, stop = int(w.kv_indptr[b]), int(w.kv_indptr[b + 1])
+        for j in range(first, stop):
+            n = w.page_size if j + 1 < stop else int(w.last_page_len[b])
+            toks += [(k, v, int(w.kv_indices[j]), s) for s in range(n)]
+        for (kk, vv, pg, s) in toks:
+            indices.append(len(rows_k))
+            rows_k.append(kk[pg, :, s, :])
+            rows_v.append(vv[pg, :, s, :])
+        indptr.append(len(indices))
+    k1 = np.stack(rows_k)[:, :, None, :] if rows_k else np.zeros((0, Hkv, 1, d))
+    v1 = np.stack(rows_v)[:, :, None, :] if rows_v else np.zeros((0, Hkv, 1, d))
+    last = np.array([1 if indptr[b + 1] > indptr[b] else 0 for b in range(w.batch)])
+    return k1, v1, np.array(indptr), np.array(indices, dtype=np.int64), last
+
+
+def _composed(mod, w, q, k, v, kp, vp):
+    return mod.decode_attention_composed(q, k, v, w.kv_indptr, w.kv_indices, w.last_page_len,
+                                         kp, vp, w.prefix_indptr, w.prefix_indices,
+                                         w.prefix_last_page_len, w.prefix_of, w.sm_scale)
+
+
+def _composed_inputs(case):
+    seed, plens, members, singles, own_max, Hq, Hkv, d, P, Pp = case
+    w = random_composed_workload(seed, plens, members, singles, own_max, Hq, Hkv, d, P, Pp)
+    return w, [t.double().numpy() for t in w.make_values("cpu")]
+
+
+def pin_composed_is_one_cache(mod):
+    """Composed formats are a storage layout: the result equals the plain
+    decode definition over the same token sequence held in one cache."""
+    for case in COMPOSED_CASES:
+        w, (q, k, v, kp, vp) = _composed_inputs(case)
+        O, LSE = _composed(mod, w, q, k, v, kp, vp)
+        k1, v1, ip, ix, lp = _one_cache(w, k, v, kp, vp)
+        O1, LSE1 = mod.decode_attention(q, k1, v1, ip, ix, lp, w.sm_scale)
+        assert np.max(np.abs(O - O1)) <= 1e-12, case[0]
+        assert np.array_equal(np.isneginf(LSE), np.isneginf(LSE1)), case[0]
+        assert np.max(np.abs(LSE - LSE1)) <= 1e-12, case[0]
+
+
+def pin_composed_bruteforce(mod):
+    """The same one-cache layout through the pure-Python brute force."""
+    for case in COMPOSED_CASES[:2]:
+        w, (q, k, v, kp, vp) = _composed_inputs(case)
+        O, LSE = _composed(mod, w, q, k, v, kp, vp)
+        k1, v1, ip, ix, lp = _one_cache(w, k, v, kp, vp)
+        Ob, LSEb = bruteforce_decode(q, k1, v1, ip, ix, lp, w.sm_scale)
+        assert np.max(np.abs(O - np.array(Ob))) <= 1e-12, case[0]
+        assert np.max(np.abs(LSE - np.array(LSEb))) <= 1e-12, case[0]
+
+
+def pin_composed_prefix_counts(mod):
+    """A request that shares a prefix with others gets what it gets alone
+    (each request's result depends only on its own tokens), and a constant
+    V over prefix and own tokens returns that constant."""
+    w, (q, k, v, kp, vp) = _composed_inputs(COMPOSED_CASES[0])
+    O, _ = _composed(mod, w, q, k, v, kp, vp)
+    for b in range(w.batch):
+        sub = dataclasses.replace(
+            w, batch=1, kv_indptr=np.array([0, w.kv_indptr[b + 1] - w.kv_indptr[b]]),
+            kv_indices=w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]],
+            last_page_len=w.last_page_len[b:b + 1], prefix_of=w.prefix_of[b:b + 1])
+        Ob, _ = _composed(mod, sub, q[b:b + 1], k, v, kp, vp)
+        assert np.max(np.abs(Ob[0] - O[b])) <= 1e-13, b
+    c = 0.375
+    O, _ = _composed(mod, w, q, k, np.full_like(v, c), kp, np.full_like(vp, c))
+    assert np.max(np.abs(O - c)) <= 1e-13
+
+
+COMPOSED_PINS = [pin_composed_is_one_cache, pin_composed_bruteforce, pin_composed_prefix_counts]

@@ -6,8 +6,8 @@ import oracle.attention as oa
 from tests import oracle_pins as pins
 
 
-@pytest.mark.parametrize("pin", pins.ALL_PINS + pins.PREFILL_PINS + pins.ROPE_PINS + [pins.pin_bf16],
-                         ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", pins.ALL_PINS + pins.PREFILL_PINS + pins.ROPE_PINS +
+                         pins.COMPOSED_PINS + [pins.pin_bf16], ids=lambda f: f.__name__)
 def test_pin(pin):
     pin(oa)
 
@@ -219,3 +219,73 @@ def test_prefill_per_request_slices_equal_the_whole_batch(causal):
     assert seen.all()
     if not causal:
         assert np.isneginf(LSE[0:6]).all()  # request 1: no pages, unmasked
+
+
+# ---- planted mistakes in the composed oracle: each is a whole copy of
+# decode_attention_composed with one error, which some composed pin catches
+def _composed_variant(mistake):
+    import math as _m
+
+    def f(q, k_pool, v_pool, kv_indptr, kv_indices, last_page_len, k_prefix, v_prefix,
+          prefix_indptr, prefix_indices, prefix_last_page_len, prefix_of, sm_scale=None):
+        q = np.asarray(q, dtype=np.float64)
+        B, Hq, d = q.shape
+        Hkv, P, Pp = k_pool.shape[1], k_pool.shape[2], k_prefix.shape[2]
+        G = Hq // Hkv
+        sm_scale = 1.0 / _m.sqrt(d) if sm_scale is None else sm_scale
+        O, LSE = np.zeros((B, Hq, d)), np.full((B, Hq), -np.inf)
+        for b in range(B):
+            own = oa.request_tokens(kv_indptr, kv_indices, last_page_len, P, b)
+            g = int(prefix_of[b])
+            if mistake == "prefix_of_next":
+                g = (g + 1) % (len(prefix_indptr) - 1) if g >= 0 else g
+            pre = []
+            if g >= 0 and mistake != "prefix_dropped":
+                lastp = prefix_last_page_len
+                if mistake == "prefix_last_len_ignored":
+                    lastp = np.full_like(prefix_last_page_len, Pp)
+                if mistake == "prefix_read_at_own_page_size":
+                    Pp_ = P
+                else:
+                    Pp_ = Pp
+                pre = oa.request_tokens(prefix_indptr, prefix_indices, lastp, Pp_, g)
+                pre = [(p_, s_) for p_, s_ in pre if s_ < Pp]
+            for kvh in range(Hkv):
+                heads = [h for h in range(Hq) if h // G == kvh]
+                src = (k_pool, v_pool) if mistake == "prefix_from_main_cache" else (k_prefix, v_prefix)
+                Kp, Vp = oa.gather_kv(*src, pre, kvh) if pre else (np.zeros((0, d)), np.zeros((0, d)))
+                Ko, Vo = oa.gather_kv(k_pool, v_pool, own, kvh)
+                o, lse = oa.attend(q[b, heads, :], np.concatenate([Kp, Ko]),
+                                   np.concatenate([Vp, Vo]), sm_scale)
+                O[b, heads, :], LSE[b, heads] = o, lse
+        return O, LSE
+    return f
+
+
+COMPOSED_MUTATIONS = ["prefix_of_next", "prefix_dropped", "prefix_last_len_ignored",
+                      "prefix_read_at_own_page_size", "prefix_from_main_cache"]
+
+
+@pytest.mark.parametrize("name", COMPOSED_MUTATIONS)
+def test_composed_oracle_mutations_are_caught(name, monkeypatch):
+    monkeypatch.setattr(oa, "decode_attention_composed", _composed_variant(name))
+    caught = []
+    for pin in pins.COMPOSED_PINS:
+        try:
+            pin(oa)
+        except (AssertionError, ValueError, IndexError, TypeError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake {name} passed every composed pin"
+
+
+def test_composed_variant_without_mistake_passes():
+    """The mutation harness itself is faithful: its copy with no mistake
+    passes every composed pin."""
+    import pytest as _p
+    mp = _p.MonkeyPatch()
+    try:
+        mp.setattr(oa, "decode_attention_composed", _composed_variant("none"))
+        for pin in pins.COMPOSED_PINS:
+            pin(oa)
+    finally:
+        mp.undo()
