@@ -164,13 +164,17 @@ def summarize_trace(stats_csv, bench_log, w, config_id):
     ev_us = res["us_per_batch"]
     o = []
     o.append(f"# {' + '.join(kernels)} — {w.name}\n")
-    desc = (f"batch {w.batch}, {int(w.kv_lens().sum()):,} KV tokens, {w.num_qo_heads} query / "
+    tok = (w.total_kv_lens() if hasattr(w, "prefix_of") else w.kv_lens()).sum()
+    desc = (f"batch {w.batch}, {int(tok):,} KV tokens, {w.num_qo_heads} query / "
             f"{w.num_kv_heads} KV heads, head_dim {w.head_dim}, page size {w.page_size}, "
             f"K/V {w.dtype}")
     if prefill:
         desc += f", {w.num_qo_tokens:,} query tokens ({'causal' if w.causal else 'unmasked'})"
     if w.rope_theta:
         desc += f", rotary embedding (theta {w.rope_theta:g}) applied to K in the kernel"
+    if hasattr(w, "prefix_of"):
+        desc += (f", the shared prefix held once in a second cache of {w.prefix_page_size}-token "
+                 f"blocks")
     o.append(f"Workload (config {config_id}): {desc}.")
     if prefill:
         o.append(f"Algorithmic work per batch: {w.flops():,} flop "
@@ -271,7 +275,7 @@ def _one_thread():
         return contextlib.nullcontext(), os.cpu_count() or 1
 
 
-def cpu_baseline(w, q, k, v, min_seconds=10.0, max_passes=3):
+def cpu_baseline(w, q, k, v, min_seconds=10.0, max_passes=3, kp_vp=None):
     """Time the float64 oracle on the host over whole batches of the same
     workload (inputs copied to host memory first, not timed), on one thread."""
     import torch
@@ -284,8 +288,16 @@ def cpu_baseline(w, q, k, v, min_seconds=10.0, max_passes=3):
     else:
         kh, vh = k.float().cpu().numpy(), v.float().cpu().numpy()
 
+    composed = hasattr(w, "prefix_of")
+    if composed:
+        kph, vph = kp_vp[0].float().cpu().numpy(), kp_vp[1].float().cpu().numpy()
+
     def run():
-        if w.rope_theta:
+        if composed:
+            oa.decode_attention_composed(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len,
+                                         kph, vph, w.prefix_indptr, w.prefix_indices,
+                                         w.prefix_last_page_len, w.prefix_of, w.sm_scale)
+        elif w.rope_theta:
             oa.decode_attention_rope(qh, kh, vh, w.kv_indptr, w.kv_indices, w.last_page_len,
                                      w.sm_scale, w.rope_theta, w.rope_scale)
         else:
@@ -299,9 +311,10 @@ def cpu_baseline(w, q, k, v, min_seconds=10.0, max_passes=3):
             run()
             times.append(time.perf_counter() - t0)
     per = statistics.median(times)
+    tot_tokens = (w.total_kv_lens() if composed else w.kv_lens()).sum()
     return {"value": w.algorithmic_bytes() / per / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds_per_batch": per,
-            "sample": f"whole {w.name} batch ({int(w.kv_lens().sum())} KV tokens), "
+            "sample": f"whole {w.name} batch ({int(tot_tokens)} KV tokens), "
                       f"{len(times)} pass(es), median; numpy float64, BLAS held to "
                       f"{threads} host thread(s)"}
 
@@ -547,7 +560,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     fb.lib()
     dev = torch.device("cuda:0")
-    q, k, v = w.make_values(dev)
+    composed = hasattr(w, "prefix_of")  # a prefix cache of its own block size
+    vals = w.make_values(dev)
+    q, k, v = vals[:3]
+    kp_vp = vals[3:] if composed else None
     opts = dict(items_per_cu=args.items_per_cu, min_chunk_tokens=args.min_chunk_tokens,
                 fixed_chunk_tokens=args.fixed_chunk_tokens, decode_kernel=args.decode_kernel)
 
@@ -555,8 +571,16 @@ def main():
     plan_t = []
     for _ in range(20):
         t0 = time.perf_counter()
-        p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, w.num_qo_heads, w.num_kv_heads,
-                    w.head_dim, w.page_size, w.num_pool_pages, w.dtype, **opts)
+        if composed:
+            p = fb.plan_composed(w.kv_indptr, w.kv_indices, w.last_page_len, w.prefix_indptr,
+                                 w.prefix_indices, w.prefix_last_page_len, w.prefix_of,
+                                 w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                                 w.num_pool_pages, w.prefix_page_size, w.num_prefix_pool_pages,
+                                 **opts)
+        else:
+            p = fb.plan(w.kv_indptr, w.kv_indices, w.last_page_len, w.num_qo_heads,
+                        w.num_kv_heads, w.head_dim, w.page_size, w.num_pool_pages, w.dtype,
+                        **opts)
         plan_t.append(time.perf_counter() - t0)
     ws = torch.empty(max(256, p.info["workspace_bytes"]), dtype=torch.uint8, device=dev)
     # upload time, host call to copy done: the first upload pins a staging
@@ -580,8 +604,12 @@ def main():
     def step(ev):
         if ev:
             ev[0].record()
-        fb.decode(q, k, v, p, out=out, lse=lse, workspace=ws, k_scale=w.k_scale, v_scale=w.v_scale,
-                  rope_theta=w.rope_theta or None, rope_scale=w.rope_scale)
+        if composed:
+            fb.decode_composed(q, k, v, kp_vp[0], kp_vp[1], p, out=out, lse=lse, workspace=ws)
+        else:
+            fb.decode(q, k, v, p, out=out, lse=lse, workspace=ws, k_scale=w.k_scale,
+                      v_scale=w.v_scale, rope_theta=w.rope_theta or None,
+                      rope_scale=w.rope_scale)
         if ev:
             ev[1].record()
 
@@ -612,7 +640,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_qo_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-                   "page_size": w.page_size, "kv_tokens": int(w.kv_lens().sum()),
+                   "page_size": w.page_size,
+                   "kv_tokens": int((w.total_kv_lens() if composed else w.kv_lens()).sum()),
+                   **({"prefix_page_size": w.prefix_page_size} if composed else {}),
                    "algorithmic_bytes": nbytes, "parallelism": "single-gpu",
                    "plan_items": p.info["num_items"], "chunk_pages": p.info["chunk_pages"],
                    "prefix_items": p.info["num_prefix_items"],
@@ -637,7 +667,7 @@ def main():
             "kernel": "streaming read of 2 GiB with 16-byte nontemporal loads "
                       "(libfi_bench.so), L2/MALL flushed, median of 5"}
     if not args.no_cpu_baseline and not args.counters_run:
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, kp_vp=kp_vp)
     print(json.dumps(result), flush=True)
     return 0
 

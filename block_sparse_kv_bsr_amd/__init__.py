@@ -6,6 +6,6 @@ plus seeded input generators. ``plan``, ``decode``, ``merge_states``,
 ``prefill_plan`` and ``prefill`` load the library on first use and raise if it
 is missing.
 """
-from .binding import (FiError, Plan, PrefillPlan, decode, decode_noalloc, lib,  # noqa: F401
-                      merge_states, plan, prefill, prefill_plan, FI_DTYPE_BF16, FI_DTYPE_F32,
-                      FI_DTYPE_FP8_E4M3)
+from .binding import (FiError, Plan, PrefillPlan, decode, decode_composed,  # noqa: F401
+                      decode_noalloc, lib, merge_states, plan, plan_composed, prefill,
+                      prefill_plan, FI_DTYPE_BF16, FI_DTYPE_F32, FI_DTYPE_FP8_E4M3)

@@ -22,7 +22,7 @@ FI_DTYPE_BF16 = 1
 FI_DTYPE_FP8_E4M3 = 2
 ITEM_STRIDE = 16
 NODE_STRIDE = 8
-PITEM_STRIDE = 8
+PITEM_STRIDE = 12
 MERGE_FAN_IN = 32
 DECODE_KERNEL_AUTO, DECODE_KERNEL_VECTOR, DECODE_KERNEL_MATRIX = 0, 1, 2
 
@@ -36,7 +36,8 @@ EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_
             "fi_prefill_plan_create", "fi_prefill_plan_get_info", "fi_prefill_plan_work_list",
             "fi_prefill_plan_merges", "fi_prefill_plan_upload", "fi_prefill_run",
             "fi_prefill_plan_destroy", "fi_decode_run_rope", "fi_decode_run_rope_scaled",
-            "fi_decode_run_noalloc", "fi_prefill_run_scaled"]
+            "fi_decode_run_noalloc", "fi_prefill_run_scaled", "fi_plan_create_composed",
+            "fi_decode_run_composed"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 QITEM_STRIDE = 12
 QMERGE_STRIDE = 8
@@ -69,7 +70,7 @@ class PlanInfo(ctypes.Structure):
                 ("shared_pages", ctypes.c_int64), ("num_prefix_items", ctypes.c_int64),
                 ("num_prefix_groups", ctypes.c_int32), ("prefix_rows_per_item", ctypes.c_int32),
                 ("image_bytes", ctypes.c_int64), ("decode_kernel", ctypes.c_int32),
-                ("merge_fan_in", ctypes.c_int32)]
+                ("merge_fan_in", ctypes.c_int32), ("prefix_page_size", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -112,6 +113,10 @@ def lib() -> ctypes.CDLL:
     L.fi_plan_create.argtypes = [pi32, pi32, pi32, i32, i32, i32, i32, i32, i64, i32,
                                  ctypes.POINTER(PlanOpts), ctypes.POINTER(vp)]
     L.fi_plan_create.restype = i32
+    L.fi_plan_create_composed.argtypes = [pi32, pi32, pi32, i32, pi32, pi32, pi32, i32, pi32, i32,
+                                          i32, i32, i32, i64, i32, i64, i32,
+                                          ctypes.POINTER(PlanOpts), ctypes.POINTER(vp)]
+    L.fi_plan_create_composed.restype = i32
     L.fi_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     L.fi_plan_get_info.restype = i32
     L.fi_plan_work_list.argtypes = [vp, ctypes.POINTER(pi32), ctypes.POINTER(i64)]
@@ -126,6 +131,8 @@ def lib() -> ctypes.CDLL:
     f32 = ctypes.c_float
     L.fi_decode_run_scaled.argtypes = [vp, vp, vp, vp, f32, f32, vp, vp, f32, vp, sz, vp]
     L.fi_decode_run_scaled.restype = i32
+    L.fi_decode_run_composed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, sz, vp]
+    L.fi_decode_run_composed.restype = i32
     L.fi_decode_run_rope.argtypes = [vp, vp, vp, vp, f32, f32, vp, vp, f32, vp, sz, vp]
     L.fi_decode_run_rope.restype = i32
     L.fi_decode_run_rope_scaled.argtypes = [vp, vp, vp, vp, f32, f32, f32, f32, vp, vp, f32, vp,
@@ -292,6 +299,37 @@ def plan(kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int, num_kv_head
     return p
 
 
+def plan_composed(kv_indptr, kv_indices, kv_last_page_len, prefix_indptr, prefix_indices,
+                  prefix_last_page_len, prefix_of, num_qo_heads: int, num_kv_heads: int,
+                  head_dim: int, page_size: int, num_pool_pages: int, prefix_page_size: int,
+                  num_prefix_pool_pages: int, dtype="bf16", num_cus: int = 0,
+                  items_per_cu: int = 0, min_chunk_tokens: int = 0, max_chunk_tokens: int = 0,
+                  fixed_chunk_tokens: int = 0, decode_kernel: int = 0) -> Plan:
+    """fi_plan_create_composed: the requests' own pages (kv_*), the prefix
+    cache's table (prefix_*) and prefix_of [batch] (-1: no prefix)."""
+    ip, ix, lp = _i32(kv_indptr), _i32(kv_indices), _i32(kv_last_page_len)
+    batch = _check_lengths(ip, ix, lp)
+    pip, pix, plp = _i32(prefix_indptr), _i32(prefix_indices), _i32(prefix_last_page_len)
+    num_prefixes = _check_lengths(pip, pix, plp)
+    of = _i32(prefix_of)
+    if of.ndim != 1 or len(of) != batch:
+        raise ValueError("prefix_of must have one entry per request")
+    opts = PlanOpts(num_cus, items_per_cu, min_chunk_tokens, max_chunk_tokens, fixed_chunk_tokens,
+                    0, decode_kernel)
+    h = ctypes.c_void_p()
+    null = ctypes.POINTER(ctypes.c_int32)()
+    _check(lib().fi_plan_create_composed(
+        _ptr32(ip), _ptr32(ix) if ix.size else null, _ptr32(lp), batch, _ptr32(pip),
+        _ptr32(pix) if pix.size else null, _ptr32(plp) if plp.size else null, num_prefixes,
+        _ptr32(of) if of.size else null, num_qo_heads, num_kv_heads, head_dim, page_size,
+        int(num_pool_pages), prefix_page_size, int(num_prefix_pool_pages), _dtype_code(dtype),
+        ctypes.byref(opts), ctypes.byref(h)))
+    p = Plan(h.value)
+    p.num_pool_pages = int(num_pool_pages)
+    p.num_prefix_pool_pages = int(num_prefix_pool_pages)
+    return p
+
+
 def _stream(stream) -> int:
     import torch
     if stream is None:
@@ -384,6 +422,34 @@ def decode(q, k_pages, v_pages, plan_: Plan, out=None, lse=None, sm_scale: Optio
                                       ctypes.c_void_p(k_pages.data_ptr()),
                                       ctypes.c_void_p(v_pages.data_ptr()), float(k_scale),
                                       float(v_scale), o, l, scale, ws, nbytes, s))
+    return out, lse
+
+
+def decode_composed(q, k_pages, v_pages, k_prefix, v_prefix, plan_: Plan, out=None, lse=None,
+                    sm_scale: Optional[float] = None, workspace=None, stream=None):
+    """fi_decode_run_composed: the requests' own pages in k_pages / v_pages,
+    the prefixes in k_prefix / v_prefix [prefix pool, H_kv, prefix_page_size,
+    d]. Returns (out, lse)."""
+    import torch
+    info = plan_.info
+    for t, n in ((k_prefix, "k_prefix"), (v_prefix, "v_prefix")):
+        _require_gpu(t, n)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{n} must be bf16")
+        want = (info["num_kv_heads"], info["prefix_page_size"], info["head_dim"])
+        if tuple(t.shape[1:]) != want or t.shape[0] < plan_.num_prefix_pool_pages:
+            raise ValueError(f"{n} must have shape [>= {plan_.num_prefix_pool_pages}, "
+                             f"{want[0]}, {want[1]}, {want[2]}]")
+        if t.device != q.device:
+            raise ValueError(f"{n} is on {t.device}, q on {q.device}")
+    out, lse, workspace = _decode_args(q, k_pages, v_pages, plan_, out, lse, workspace, stream)
+    scale = float(sm_scale) if sm_scale else 0.0
+    _check(lib().fi_decode_run_composed(
+        plan_.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_pages.data_ptr()),
+        ctypes.c_void_p(v_pages.data_ptr()), ctypes.c_void_p(k_prefix.data_ptr()),
+        ctypes.c_void_p(v_prefix.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_void_p(lse.data_ptr()), scale, ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), ctypes.c_void_p(_stream(stream))))
     return out, lse
 
 

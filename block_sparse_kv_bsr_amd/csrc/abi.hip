@@ -206,7 +206,12 @@ fi_status check_run(const fi_plan* plan, void* out, float* lse, void* workspace,
 }
 
 fi_status check_inputs(const fi_plan* plan, const void* q, const void* k_pages,
-                       const void* v_pages) {
+                       const void* v_pages, bool composed_run = false) {
+  if (plan->composed != composed_run)
+    return fail(FI_ERR_INVALID_ARG, plan->composed
+                                        ? "a composed plan runs with fi_decode_run_composed"
+                                        : "fi_decode_run_composed needs a plan made by "
+                                          "fi_plan_create_composed");
   if (!q) return fail(FI_ERR_INVALID_ARG, "q is NULL");
   if (plan->num_items() > 0 && (!k_pages || !v_pages))
     return fail(FI_ERR_INVALID_ARG, "k_pages or v_pages is NULL");
@@ -240,7 +245,8 @@ RunScratch workspace_scratch(const fi_plan* plan, void* workspace) {
 fi_status launch_run(const fi_plan* plan, const void* q, const void* k_pages,
                      const void* v_pages, float k_scale, float v_scale, void* out, float* lse,
                      float sm_scale, const void* workspace, const RunScratch& sc, hipStream_t s,
-                     Rope rope = Rope()) {
+                     Rope rope = Rope(), const void* k_prefix = nullptr,
+                     const void* v_prefix = nullptr) {
   if (!(sm_scale > 0.f)) sm_scale = 1.0f / std::sqrt((float)plan->head_dim);
   const char* ws = static_cast<const char*>(workspace);
   fi::DecodeArgs d{};
@@ -286,15 +292,16 @@ fi_status launch_run(const fi_plan* plan, const void* q, const void* k_pages,
     pa.prefix_slot = reinterpret_cast<const int32_t*>(ws + plan->ws.prefix_slot);
     pa.page_ids = d.page_ids;
     pa.q = q;
-    pa.k_pages = k_pages;
-    pa.v_pages = v_pages;
+    // a composed plan's prefixes live in the prefix cache, with its block size
+    pa.k_pages = plan->composed ? k_prefix : k_pages;
+    pa.v_pages = plan->composed ? v_prefix : v_pages;
     pa.part_o = d.part_o;
     pa.part_lse = d.part_lse;
     pa.num_items = plan->num_pitems();
     pa.num_qo_heads = plan->num_qo_heads;
     pa.num_kv_heads = plan->num_kv_heads;
     pa.head_dim = plan->head_dim;
-    pa.page_size = plan->page_size;
+    pa.page_size = plan->composed ? plan->prefix_page_size : plan->page_size;
     pa.group = plan->group;
     pa.sm_scale = sm_scale;
     const hipError_t ep = fi::launch_prefix(pa, s);
@@ -306,6 +313,28 @@ fi_status launch_run(const fi_plan* plan, const void* q, const void* k_pages,
 }
 
 }  // namespace
+
+fi_status fi_decode_run_composed(const fi_plan* plan, const void* q, const void* k_pages,
+                                 const void* v_pages, const void* k_prefix, const void* v_prefix,
+                                 void* out, float* lse, float sm_scale, void* workspace,
+                                 size_t workspace_bytes, fi_stream_t stream) {
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  if (!plan->composed)
+    return fail(FI_ERR_INVALID_ARG,
+                "fi_decode_run_composed needs a plan made by fi_plan_create_composed");
+  if (plan->batch == 0) return FI_OK;
+  fi_status st = check_inputs(plan, q, k_pages, v_pages, true);
+  if (st != FI_OK) return st;
+  if (plan->num_pitems() > 0 && (!k_prefix || !v_prefix))
+    return fail(FI_ERR_INVALID_ARG, "k_prefix or v_prefix is NULL");
+  if (!aligned(k_prefix, 16) || !aligned(v_prefix, 16))
+    return fail(FI_ERR_INVALID_ARG, "k_prefix and v_prefix must be 16-byte aligned");
+  st = check_run(plan, out, lse, workspace, workspace_bytes);
+  if (st != FI_OK) return st;
+  return launch_run(plan, q, k_pages, v_pages, 1.f, 1.f, out, lse, sm_scale, workspace,
+                    workspace_scratch(plan, workspace), static_cast<hipStream_t>(stream), Rope(),
+                    k_prefix, v_prefix);
+}
 
 fi_status fi_decode_run_scaled(const fi_plan* plan, const void* q, const void* k_pages,
                                const void* v_pages, float k_scale, float v_scale, void* out,

@@ -307,6 +307,7 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   const int row = wrow * 32 + (lane & 31);
 
   int h, nrows, page_begin, npg, ntok;
+  int tok_off = 0;      // slot of the chunk's first token in its first page
   int lim;              // tokens of the chunk this row attends (may be <= 0)
   int64_t q_index;      // row of q (and, for prefill, of out / lse) x heads + head
   // prefix: partial row = prefix_slot[b][h] + chunk; prefill: slot (-1 = direct)
@@ -322,7 +323,8 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
     const int chunk = it[FI_PITEM_CHUNK];
     page_begin = it[FI_PITEM_PAGE_BEGIN];
     npg = it[FI_PITEM_NUM_PAGES];  // <= FI_PREFIX_MAX_PAGES = kIds
-    ntok = npg * p.page_size;
+    tok_off = it[FI_PITEM_TOKEN_BEGIN];
+    ntok = it[FI_PITEM_NUM_TOKENS];  // tok_off + ntok <= npg * page_size
     row_ok = row < nrows;
     const int b = p.members[member_base + row_begin + (row_ok ? row / G : 0)];
     gi = row_ok ? row % G : 0;
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
 #pragma unroll
     for (int i = 0; i < Gm::kDmaPerWave; ++i) {
       const int t = (wave * Gm::kDmaPerWave + i) * Gm::kRowsPerDma + dma_row;
-      const uint32_t tok = (uint32_t)min(j * kBlock + t, ntok - 1);
+      const uint32_t tok = (uint32_t)(min(j * kBlock + t, ntok - 1) + tok_off);
       const uint32_t pg = __umulhi(tok, pmag) + tok * pmag_hi;
       const uint32_t row_in_page = tok - pg * psz;
       const uint64_t page_off = (uint64_t)s_pid[pg] << 7;

@@ -95,6 +95,26 @@ fi_status check_page_table(const int32_t* kv_indptr, const int32_t* kv_indices,
   return FI_OK;
 }
 
+namespace {
+
+// The prefix cache of a composed plan (fi_plan_create_composed).
+struct Composed {
+  const int32_t* indptr;
+  const int32_t* indices;
+  const int32_t* last;
+  int32_t num_prefixes;
+  const int32_t* prefix_of;
+  int32_t page_size;
+  int64_t num_pool_pages;
+};
+
+fi_status create_plan(const int32_t* kv_indptr, const int32_t* kv_indices,
+                      const int32_t* kv_last_page_len, int32_t batch, int32_t num_qo_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                      int64_t num_pool_pages, fi_dtype dtype, const fi_plan_opts* opts,
+                      const Composed* comp, fi_plan** out_plan);
+
+}  // namespace
 }  // namespace fi
 
 extern "C" {
@@ -106,7 +126,37 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
                          int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
                          int32_t page_size, int64_t num_pool_pages, fi_dtype dtype,
                          const fi_plan_opts* opts, fi_plan** out_plan) {
-  using fi::fail;
+  return fi::create_plan(kv_indptr, kv_indices, kv_last_page_len, batch, num_qo_heads,
+                         num_kv_heads, head_dim, page_size, num_pool_pages, dtype, opts, nullptr,
+                         out_plan);
+}
+
+fi_status fi_plan_create_composed(const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  const int32_t* kv_last_page_len, int32_t batch,
+                                  const int32_t* prefix_indptr, const int32_t* prefix_indices,
+                                  const int32_t* prefix_last_page_len, int32_t num_prefixes,
+                                  const int32_t* prefix_of, int32_t num_qo_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                  int64_t num_pool_pages, int32_t prefix_page_size,
+                                  int64_t num_prefix_pool_pages, fi_dtype dtype,
+                                  const fi_plan_opts* opts, fi_plan** out_plan) {
+  const fi::Composed c{prefix_indptr, prefix_indices, prefix_last_page_len, num_prefixes,
+                       prefix_of, prefix_page_size, num_prefix_pool_pages};
+  return fi::create_plan(kv_indptr, kv_indices, kv_last_page_len, batch, num_qo_heads,
+                         num_kv_heads, head_dim, page_size, num_pool_pages, dtype, opts, &c,
+                         out_plan);
+}
+
+}  // extern "C"
+
+namespace fi {
+namespace {
+
+fi_status create_plan(const int32_t* kv_indptr, const int32_t* kv_indices,
+                      const int32_t* kv_last_page_len, int32_t batch, int32_t num_qo_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                      int64_t num_pool_pages, fi_dtype dtype, const fi_plan_opts* opts,
+                      const Composed* comp, fi_plan** out_plan) {
   try {
     if (!out_plan) return fail(FI_ERR_INVALID_ARG, "out_plan is NULL");
     *out_plan = nullptr;
@@ -142,11 +192,36 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
       if (st != FI_OK) return st;
     }
     const int64_t nnz = batch > 0 ? kv_indptr[batch] : 0;
+    // composed: tokens of each prefix, and of the prefix each request begins with
+    std::vector<int64_t> pre_tok, lead(batch, 0);
+    int64_t pre_nnz = 0;
+    if (comp) {
+      if (dtype != FI_DTYPE_BF16) return fail(FI_ERR_UNSUPPORTED, "composed formats need FI_DTYPE_BF16");
+      if (comp->num_prefixes < 0) return fail(FI_ERR_INVALID_ARG, "num_prefixes < 0");
+      const fi_status st = check_page_table(comp->indptr, comp->indices, comp->last,
+                                            comp->num_prefixes, comp->page_size,
+                                            comp->num_pool_pages, &pre_tok);
+      if (st != FI_OK) return fail(st, "prefix table: " + g_last_error);
+      pre_nnz = comp->num_prefixes > 0 ? comp->indptr[comp->num_prefixes] : 0;
+      if (batch > 0 && !comp->prefix_of) return fail(FI_ERR_INVALID_ARG, "prefix_of is NULL");
+      for (int32_t b = 0; b < batch; ++b) {
+        const int32_t g = comp->prefix_of[b];
+        if (g < -1 || g >= comp->num_prefixes)
+          return fail(FI_ERR_INVALID_ARG, "prefix_of[" + std::to_string(b) +
+                                              "] outside [-1, num_prefixes)");
+        if (g >= 0) lead[b] = pre_tok[g];
+        if (lead[b] > 0 && ntok[b] == 0)
+          return fail(FI_ERR_INVALID_ARG, "request " + std::to_string(b) +
+                                              " has a prefix but no token of its own");
+        if (lead[b] + ntok[b] > INT32_MAX)
+          return fail(FI_ERR_INVALID_ARG, "request longer than 2^31-1 tokens");
+      }
+    }
     std::vector<int64_t> npages(batch);
     int64_t total_tokens = 0;
     for (int32_t b = 0; b < batch; ++b) {
       npages[b] = kv_indptr[b + 1] - kv_indptr[b];
-      total_tokens += ntok[b];
+      total_tokens += lead[b] + ntok[b];
     }
     fi_plan_opts o{};
     if (opts) o = *opts;
@@ -171,13 +246,39 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     struct Group {
       int64_t member_base, members, lcp, chunks, row_blocks;
       int32_t first;  // a member; its first lcp pages are the prefix
+      // the prefix's tokens, its first page as an index into the uploaded
+      // page ids, and the size of its pages
+      int64_t tokens, page_base, psize;
     };
     std::vector<Group> groups;
     std::vector<int32_t> members;
     std::vector<int32_t> group_of(batch, -1);
     std::vector<int64_t> pre_pages(batch, 0);
     const int64_t kPrefixRows = 128;
-    if (o.cascade >= 0 && dtype == FI_DTYPE_BF16 && batch >= 2) {
+    if (comp) {
+      // one group per prefix with members, in prefix order; members in
+      // batch order
+      std::vector<std::vector<int32_t>> mem((size_t)comp->num_prefixes);
+      for (int32_t b = 0; b < batch; ++b)
+        if (lead[b] > 0) mem[(size_t)comp->prefix_of[b]].push_back(b);
+      for (int32_t g = 0; g < comp->num_prefixes; ++g) {
+        if (mem[(size_t)g].empty()) continue;
+        Group gr{};
+        gr.member_base = (int64_t)members.size();
+        gr.members = (int64_t)mem[(size_t)g].size();
+        gr.lcp = comp->indptr[g + 1] - comp->indptr[g];
+        gr.first = mem[(size_t)g][0];
+        gr.row_blocks = fi::ceil_div(gr.members * group, kPrefixRows);
+        gr.tokens = pre_tok[(size_t)g];
+        gr.page_base = nnz + comp->indptr[g];
+        gr.psize = comp->page_size;
+        for (int32_t b : mem[(size_t)g]) {
+          members.push_back(b);
+          group_of[b] = (int32_t)groups.size();
+        }
+        groups.push_back(gr);
+      }
+    } else if (o.cascade >= 0 && dtype == FI_DTYPE_BF16 && batch >= 2) {
       std::vector<std::pair<int32_t, int32_t>> firsts;  // (first page, request)
       for (int32_t b = 0; b < batch; ++b)
         if (npages[b] >= 2) firsts.emplace_back(kv_indices[kv_indptr[b]], b);
@@ -204,6 +305,9 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
             g.lcp = lcp;
             g.first = b0;
             g.row_blocks = fi::ceil_div(g.members * group, kPrefixRows);
+            g.tokens = lcp * page_size;
+            g.page_base = kv_indptr[b0];
+            g.psize = page_size;
             for (size_t t = i; t < j; ++t) {
               const int32_t b = firsts[t].second;
               members.push_back(b);
@@ -215,16 +319,35 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
         }
         i = j;
       }
-      // prefix chunks per group: about num_cus prefix items in all, at most
-      // fan_in - 1 per tree so every tree's first node still has a decode
-      // child (nodes complete only inside the decode kernel)
+    }
+    // prefix chunks per group: about num_cus prefix items in all, at most
+    // fan_in - 1 per tree so every tree's first node still has a decode
+    // child (nodes complete only inside the decode kernel). Shared pages of
+    // the requests' own lists are cut at page boundaries; a composed prefix
+    // into near-equal token ranges (of at least 64 tokens), each touching at
+    // most FI_PREFIX_MAX_PAGES pages.
+    {
       int64_t blocks = 0;
       for (const Group& g : groups) blocks += g.row_blocks;
-      for (Group& g : groups) {
+      for (size_t gi = 0; gi < groups.size(); ++gi) {
+        Group& g = groups[gi];
         const int64_t want = fi::ceil_div(num_cus, std::max<int64_t>(1, blocks * num_kv_heads));
-        g.chunks = std::max<int64_t>(1, std::min<int64_t>({want, g.lcp, fan_in - 1}));
-        // no prefix item spans more than FI_PREFIX_MAX_PAGES pages
-        g.chunks = std::max<int64_t>(g.chunks, fi::ceil_div(g.lcp, FI_PREFIX_MAX_PAGES));
+        if (comp) {
+          g.chunks = std::max<int64_t>(
+              1, std::min<int64_t>({want, fan_in - 1, fi::ceil_div(g.tokens, 64)}));
+          g.chunks = std::max<int64_t>(
+              g.chunks, fi::ceil_div(g.tokens, (FI_PREFIX_MAX_PAGES - 1) * g.psize));
+          if (g.chunks > fan_in - 1)
+            return fail(FI_ERR_UNSUPPORTED,
+                        "prefix " + std::to_string(comp->prefix_of[g.first]) + " holds " +
+                            std::to_string(g.tokens) + " tokens, more than " +
+                            std::to_string(fan_in - 1) + " chunks of " +
+                            std::to_string((FI_PREFIX_MAX_PAGES - 1) * g.psize) + " cover");
+        } else {
+          g.chunks = std::max<int64_t>(1, std::min<int64_t>({want, g.lcp, fan_in - 1}));
+          // no prefix item spans more than FI_PREFIX_MAX_PAGES pages
+          g.chunks = std::max<int64_t>(g.chunks, fi::ceil_div(g.lcp, FI_PREFIX_MAX_PAGES));
+        }
       }
     }
     std::vector<int64_t> dpages(batch);  // pages left to the decode items
@@ -276,6 +399,9 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     p->total_tokens = total_tokens;
     p->num_groups = (int32_t)groups.size();
     p->prefix_rows = (int32_t)kPrefixRows;
+    p->composed = comp != nullptr;
+    p->prefix_page_size = comp ? comp->page_size : 0;
+    p->num_prefix_pool_pages = comp ? comp->num_pool_pages : 0;
     p->members = members;
     {
       // physical pages that the decode items read more than once (several
@@ -412,8 +538,8 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
           it.f[FI_ITEM_NUM_PAGES] = (int32_t)np;
           it.f[FI_ITEM_FIRST_PAGE] = kv_indices[kv_indptr[b] + pre + page0];
           it.f[FI_ITEM_MERGE_NODE] = leaf_node[cpre + c];
-          it.f[FI_ITEM_KV_POS] = (int32_t)((pre + page0) * page_size);
-          it.f[FI_ITEM_Q_POS] = (int32_t)(ntok[b] - 1);
+          it.f[FI_ITEM_KV_POS] = (int32_t)(lead[b] + (pre + page0) * page_size);
+          it.f[FI_ITEM_Q_POS] = (int32_t)(lead[b] + ntok[b] - 1);
           items.push_back(it);
           page0 += np;
         }
@@ -447,7 +573,19 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
       const Group& g = groups[gi];
       const int64_t per_block = kPrefixRows / group;
       for (int64_t c = 0, page0 = 0; c < g.chunks; ++c) {
-        const int64_t np = g.lcp / g.chunks + (c < g.lcp % g.chunks ? 1 : 0);
+        // the chunk's tokens [t0, t0 + nt) of the prefix
+        int64_t t0, nt;
+        if (comp) {
+          t0 = c * g.tokens / g.chunks;
+          nt = (c + 1) * g.tokens / g.chunks - t0;
+        } else {
+          const int64_t np = g.lcp / g.chunks + (c < g.lcp % g.chunks ? 1 : 0);
+          t0 = page0 * page_size;
+          nt = np * page_size;
+          page0 += np;
+        }
+        const int64_t tok_off = t0 % g.psize;
+        const int64_t npg = fi::ceil_div(tok_off + nt, g.psize);
         for (int32_t h = 0; h < num_kv_heads; ++h) {
           for (int64_t rb = 0; rb < g.row_blocks; ++rb) {
             const int64_t m0 = rb * per_block;
@@ -459,12 +597,13 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
             f[FI_PITEM_ROW_BEGIN] = (int32_t)m0;
             f[FI_PITEM_NUM_ROWS] = (int32_t)(nm * group);
             f[FI_PITEM_CHUNK] = (int32_t)c;
-            f[FI_PITEM_PAGE_BEGIN] = (int32_t)(kv_indptr[g.first] + page0);
-            f[FI_PITEM_NUM_PAGES] = (int32_t)np;
+            f[FI_PITEM_PAGE_BEGIN] = (int32_t)(g.page_base + t0 / g.psize);
+            f[FI_PITEM_NUM_PAGES] = (int32_t)npg;
+            f[FI_PITEM_TOKEN_BEGIN] = (int32_t)tok_off;
+            f[FI_PITEM_NUM_TOKENS] = (int32_t)nt;
             p->pitems.insert(p->pitems.end(), f, f + FI_PITEM_STRIDE);
           }
         }
-        page0 += np;
       }
     }
 
@@ -479,7 +618,7 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     ws.counters = off;
     off = fi::align_up(off + nn * 4, 256);
     ws.page_ids = off;
-    off = fi::align_up(off + nnz * 4, 256);
+    off = fi::align_up(off + (nnz + pre_nnz) * 4, 256);
     ws.pitems = off;
     off = fi::align_up(off + (int64_t)p->pitems.size() * 4, 256);
     ws.members = off;
@@ -502,6 +641,8 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     put(ws.members, members);
     put(ws.prefix_slot, pslot);
     if (nnz > 0) std::memcpy(p->image.data() + ws.page_ids, kv_indices, nnz * 4);
+    if (pre_nnz > 0)
+      std::memcpy(p->image.data() + ws.page_ids + nnz * 4, comp->indices, pre_nnz * 4);
 
     *out_plan = p.release();
     return FI_OK;
@@ -511,6 +652,11 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     return fail(FI_ERR_INVALID_ARG, "unexpected error in fi_plan_create");
   }
 }
+
+}  // namespace
+}  // namespace fi
+
+extern "C" {
 
 fi_status fi_plan_get_info(const fi_plan* p, fi_plan_info* info) {
   if (!p || !info) return fi::fail(FI_ERR_INVALID_ARG, "NULL plan or info");
@@ -536,6 +682,7 @@ fi_status fi_plan_get_info(const fi_plan* p, fi_plan_info* info) {
   r.image_bytes = (int64_t)p->image.size();
   r.decode_kernel = p->resolved_kernel;
   r.merge_fan_in = p->merge_fan_in;
+  r.prefix_page_size = p->prefix_page_size;
   *info = r;
   return FI_OK;
 }

@@ -20,7 +20,7 @@ struct WorkspaceLayout {
   int64_t items = 0;      // int32 [num_items][FI_ITEM_STRIDE]
   int64_t nodes = 0;      // int32 [num_nodes][FI_NODE_STRIDE]
   int64_t counters = 0;   // int32 [num_nodes], 0 between runs
-  int64_t page_ids = 0;   // int32 [nnz]
+  int64_t page_ids = 0;   // int32 [nnz] (composed: then the prefix cache's block ids)
   int64_t pitems = 0;     // int32 [num_prefix_items][FI_PITEM_STRIDE]
   int64_t members = 0;    // int32 request ids of the prefix groups
   int64_t prefix_slot = 0;  // int32 [batch][num_kv_heads]: first prefix slot or -1
@@ -56,6 +56,10 @@ struct fi_plan {
   int32_t decode_kernel = FI_DECODE_KERNEL_AUTO;   // as asked for
   int32_t resolved_kernel = FI_DECODE_KERNEL_VECTOR;  // what the runs launch
   int32_t merge_fan_in = FI_MERGE_FAN_IN;             // children per merge node at most
+  // composed formats: prefixes in a second cache of prefix_page_size blocks
+  bool composed = false;
+  int32_t prefix_page_size = 0;
+  int64_t num_prefix_pool_pages = 0;
   std::vector<uint8_t> image;   // host copy of the uploaded part of the workspace
   fi::WorkspaceLayout ws;
   // Identity of this plan in the launch layer's upload records (0 until

@@ -157,6 +157,8 @@ typedef struct {
                                 the plan's runs launch */
   int32_t merge_fan_in;      /* children per merge node at most: 16, or 8 when
                                 G * head_dim = 1024 (see FI_NODE_*) */
+  int32_t prefix_page_size;  /* block size of the prefix cache of a composed
+                                plan (fi_plan_create_composed); 0 otherwise */
 } fi_plan_info;
 
 /* Fields of one work item in the list returned by fi_plan_work_list. */
@@ -209,11 +211,13 @@ enum {
  * Fields of one shared-prefix work item (fi_plan_prefix_items). Requests
  * whose page lists start with the same physical pages form a group; the
  * common run of whole pages (never a request's last page) is the group's
- * prefix. A prefix item attends the query rows of up to
+ * prefix. A plan made by fi_plan_create_composed has one group per prefix
+ * of its prefix cache instead. A prefix item attends the query rows of up to
  * prefix_rows_per_item / G members of one group (row r: member
  * ROW_BEGIN + r / G, query head KV_HEAD * G + r % G) over one chunk of the
- * prefix, and writes one partial state per member, into the first slots of
- * that member's merge tree.
+ * prefix -- NUM_TOKENS tokens starting TOKEN_BEGIN tokens into page
+ * PAGE_BEGIN -- and writes one partial state per member, into the first
+ * slots of that member's merge tree.
  */
 enum {
   FI_PITEM_GROUP = 0,
@@ -222,9 +226,14 @@ enum {
   FI_PITEM_ROW_BEGIN = 3,   /* first member (within the group) of this item */
   FI_PITEM_NUM_ROWS = 4,    /* query rows: members in this item x G */
   FI_PITEM_CHUNK = 5,       /* prefix chunk number = child index in the trees */
-  FI_PITEM_PAGE_BEGIN = 6,  /* first page, as an index into kv_indices */
-  FI_PITEM_NUM_PAGES = 7,   /* at most FI_PREFIX_MAX_PAGES */
-  FI_PITEM_STRIDE = 8,
+  FI_PITEM_PAGE_BEGIN = 6,  /* first page, as an index into kv_indices
+                               (composed plans: kv_indices followed by
+                               prefix_indices) */
+  FI_PITEM_NUM_PAGES = 7,   /* pages the chunk touches, at most FI_PREFIX_MAX_PAGES */
+  FI_PITEM_TOKEN_BEGIN = 8, /* first token's slot in page PAGE_BEGIN (0 unless
+                               composed) */
+  FI_PITEM_NUM_TOKENS = 9,  /* tokens in the chunk */
+  FI_PITEM_STRIDE = 12,
   FI_PREFIX_MAX_PAGES = 256 /* a group's prefix is at most (merge_fan_in - 1)
                                chunks of this many pages; shared pages past
                                that stay with the decode items */
@@ -275,6 +284,50 @@ fi_status fi_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
                          int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
                          int32_t page_size, int64_t num_pool_pages, fi_dtype dtype,
                          const fi_plan_opts* opts, fi_plan** out_plan);
+
+/*
+ * Composed formats (explainer's Block-Sparse section: a prefix that many
+ * requests share is stored once, each request's own KV separately, the two
+ * with different block sizes). Request b attends the tokens of prefix
+ * prefix_of[b], held in a second cache of prefix_page_size-token blocks,
+ * followed by its own tokens in the paged cache, exactly as if both sat in
+ * one cache. Host only; the run is fi_decode_run_composed.
+ *
+ * kv_indptr .. num_pool_pages  the requests' own tokens, as fi_plan_create
+ * prefix_indptr    host int32 [num_prefixes+1], prefix_indptr[0] = 0,
+ *                  non-decreasing
+ * prefix_indices   host int32 [prefix_indptr[num_prefixes]], blocks of the
+ *                  prefix cache, each in [0, num_prefix_pool_pages)
+ * prefix_last_page_len host int32 [num_prefixes]: tokens in a prefix's last
+ *                  block, in [1, prefix_page_size] (a prefix with no blocks:
+ *                  any value in [0, prefix_page_size], and it holds nothing)
+ * num_prefixes     >= 0
+ * prefix_of        host int32 [batch]: -1 (no prefix) or a prefix index;
+ *                  a request with a non-empty prefix must hold at least one
+ *                  token of its own (its newest token, being decoded)
+ * prefix_page_size block size of the prefix cache, 1 .. 4096
+ * num_prefix_pool_pages blocks in the caller's k_prefix / v_prefix
+ * dtype            FI_DTYPE_BF16 (the prefix tile kernel reads bf16)
+ *
+ * Every prefix with members is one group (see FI_PITEM_*): its tokens are
+ * cut into chunks of near-equal token counts, at most merge_fan_in - 1 of
+ * them, each touching at most FI_PREFIX_MAX_PAGES blocks (a prefix longer
+ * than (merge_fan_in - 1) x (FI_PREFIX_MAX_PAGES - 1) x prefix_page_size
+ * tokens is FI_ERR_UNSUPPORTED). opts.cascade is ignored (no shared pages
+ * are looked for in the requests' own lists). Other options, the decode
+ * items over the requests' own pages and their merge trees as
+ * fi_plan_create. Errors: FI_ERR_INVALID_ARG for malformed tables or
+ * prefix_of, FI_ERR_UNSUPPORTED as above.
+ */
+fi_status fi_plan_create_composed(const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  const int32_t* kv_last_page_len, int32_t batch,
+                                  const int32_t* prefix_indptr, const int32_t* prefix_indices,
+                                  const int32_t* prefix_last_page_len, int32_t num_prefixes,
+                                  const int32_t* prefix_of, int32_t num_qo_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                  int64_t num_pool_pages, int32_t prefix_page_size,
+                                  int64_t num_prefix_pool_pages, fi_dtype dtype,
+                                  const fi_plan_opts* opts, fi_plan** out_plan);
 
 /* Sizes and choices of a plan. */
 fi_status fi_plan_get_info(const fi_plan* plan, fi_plan_info* info);
@@ -327,6 +380,22 @@ fi_status fi_plan_upload(fi_plan* plan, void* workspace, size_t workspace_bytes,
 fi_status fi_decode_run(const fi_plan* plan, const void* q, const void* k_pages,
                         const void* v_pages, void* out, float* lse, float sm_scale,
                         void* workspace, size_t workspace_bytes, fi_stream_t stream);
+
+/*
+ * The run of a composed plan (fi_plan_create_composed; the other decode
+ * runs refuse such a plan with FI_ERR_INVALID_ARG, and this one refuses any
+ * other plan): the prefix tile kernel over the prefix cache, then the decode
+ * kernel over the requests' own pages, their states merged per request.
+ *
+ * k_prefix, v_prefix  device bf16 [num_prefix_pool_pages, num_kv_heads,
+ *          prefix_page_size, head_dim], 16-byte aligned; may be NULL when no
+ *          request has a non-empty prefix
+ * Other arguments, ownership, streams and errors as fi_decode_run.
+ */
+fi_status fi_decode_run_composed(const fi_plan* plan, const void* q, const void* k_pages,
+                                 const void* v_pages, const void* k_prefix, const void* v_prefix,
+                                 void* out, float* lse, float sm_scale, void* workspace,
+                                 size_t workspace_bytes, fi_stream_t stream);
 
 /*
  * For callers that cannot allocate device memory during the run (code under

@@ -13,7 +13,7 @@ import oracle.attention as oa
 
 I_REQ, I_KVH, I_PB, I_NTOK, I_SLOT, I_CHUNK, I_NP, I_FIRST, I_NODE = range(9)
 N_COUNT, N_SB, N_PARENT, N_OUT, N_REQ, N_KVH, N_LEVEL, N_ARR = range(8)
-P_GROUP, P_KVH, P_MBASE, P_ROW0, P_NROWS, P_CHUNK, P_PB, P_NP = range(8)
+P_GROUP, P_KVH, P_MBASE, P_ROW0, P_NROWS, P_CHUNK, P_PB, P_NP, P_TOFF, P_NTOK = range(10)
 
 
 def make_plan(w, **opts):
@@ -279,6 +279,7 @@ def run_plan_f64(w, p):
             slot_state[int(r[I_SLOT])] = st
     for r in pitems:
         h = int(r[P_KVH])
+        assert r[P_TOFF] == 0 and r[P_NTOK] == r[P_NP] * P  # whole shared pages
         K, V = oa.gather_kv(k, v, span(int(r[P_PB]), int(r[P_NP]), P), h)
         ms = members[r[P_MBASE] + r[P_ROW0]: r[P_MBASE] + r[P_ROW0] + r[P_NROWS] // G]
         for b in ms:
