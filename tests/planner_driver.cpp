@@ -8,13 +8,16 @@
 // compares those lines with the same calls on the regular library.
 //
 // Input, whitespace separated, one call after another:
-//   D|P batch num_qo_heads num_kv_heads head_dim page_size num_pool_pages
+//   D|P|C batch num_qo_heads num_kv_heads head_dim page_size num_pool_pages
 //       dtype causal
-//   n_opts opts...          (0: NULL options; D takes 7 fields, P 4)
+//   n_opts opts...          (0: NULL options; D and C take 7 fields, P 4)
 //   n_qo qo_indptr...       (P only)
 //   n_indptr kv_indptr...   (-1: NULL pointer, nothing follows)
 //   n_indices kv_indices...
 //   n_last kv_last_page_len...
+//   C only: prefix_page_size num_prefix_pool_pages, then the prefix
+//   table's three arrays and prefix_of, as above (num_prefixes is the
+//   prefix_indptr array's length - 1, 0 if it is NULL)
 // Output per call: "<index> <status> <hash>".
 #include <cstdint>
 #include <cstdio>
@@ -44,6 +47,7 @@ struct Hash {
 struct Array {
   std::unique_ptr<int32_t[]> data;
   bool null = false;
+  int64_t n = 0;
   const int32_t* ptr() const { return null ? nullptr : data.get(); }
 };
 
@@ -54,6 +58,7 @@ bool read_array(Array* a) {
     a->null = true;
     return true;
   }
+  a->n = n;
   a->data.reset(new int32_t[n > 0 ? n : 1]);
   for (int64_t i = 0; i < n; ++i)
     if (!(std::cin >> a->data[i])) return false;
@@ -61,8 +66,14 @@ bool read_array(Array* a) {
   return true;
 }
 
+struct Prefixes {
+  int32_t page_size = 0;
+  int64_t pool = 0;
+  Array ip, ix, lp, of;
+};
+
 uint64_t decode_call(const int32_t* hdr, const std::vector<int32_t>& opts, const Array& ip,
-                     const Array& ix, const Array& lp, int* status) {
+                     const Array& ix, const Array& lp, const Prefixes* pre, int* status) {
   fi_plan_opts o{};
   const fi_plan_opts* po = nullptr;
   if (!opts.empty()) {
@@ -76,8 +87,16 @@ uint64_t decode_call(const int32_t* hdr, const std::vector<int32_t>& opts, const
     po = &o;
   }
   fi_plan* p = nullptr;
-  *status = fi_plan_create(ip.ptr(), ix.ptr(), lp.ptr(), hdr[0], hdr[1], hdr[2], hdr[3], hdr[4],
-                           hdr[5], (fi_dtype)hdr[6], po, &p);
+  if (pre) {
+    const int32_t num_prefixes = pre->ip.null ? 0 : (int32_t)(pre->ip.n - 1);
+    *status = fi_plan_create_composed(ip.ptr(), ix.ptr(), lp.ptr(), hdr[0], pre->ip.ptr(),
+                                      pre->ix.ptr(), pre->lp.ptr(), num_prefixes, pre->of.ptr(),
+                                      hdr[1], hdr[2], hdr[3], hdr[4], hdr[5], pre->page_size,
+                                      pre->pool, (fi_dtype)hdr[6], po, &p);
+  } else {
+    *status = fi_plan_create(ip.ptr(), ix.ptr(), lp.ptr(), hdr[0], hdr[1], hdr[2], hdr[3],
+                             hdr[4], hdr[5], (fi_dtype)hdr[6], po, &p);
+  }
   Hash h;
   h.mix(*status);
   if (*status != FI_OK) return h.h;
@@ -145,15 +164,23 @@ int main() {
     std::vector<int32_t> opts(n_opts);
     for (int32_t& x : opts)
       if (!(std::cin >> x)) return 2;
-    const bool prefill = kind == "P";
+    const bool prefill = kind == "P", composed = kind == "C";
     if ((prefill && n_opts != 0 && n_opts != 4) || (!prefill && n_opts != 0 && n_opts != 7))
       return 2;
     Array qo, ip, ix, lp;
     if (prefill && !read_array(&qo)) return 2;
     if (!read_array(&ip) || !read_array(&ix) || !read_array(&lp)) return 2;
+    Prefixes pre;
+    if (composed) {
+      if (!(std::cin >> pre.page_size >> pre.pool)) return 2;
+      if (!read_array(&pre.ip) || !read_array(&pre.ix) || !read_array(&pre.lp) ||
+          !read_array(&pre.of))
+        return 2;
+    }
     int status = 0;
     const uint64_t h = prefill ? prefill_call(hdr, opts, qo, ip, ix, lp, &status)
-                               : decode_call(hdr, opts, ip, ix, lp, &status);
+                               : decode_call(hdr, opts, ip, ix, lp, composed ? &pre : nullptr,
+                                             &status);
     std::printf("%d %d %llu\n", index, status, (unsigned long long)h);
   }
   return 0;

@@ -49,9 +49,12 @@ class Call:
     """One planner call: kind 'D' (fi_plan_create) or 'P' (prefill)."""
 
     def __init__(self, kind, batch, hq, hkv, d, P, pool, dtype, ip, ix, lp, opts=None, qo=None,
-                 causal=1):
+                 causal=1, prefixes=None):
         self.kind, self.hdr = kind, [batch, hq, hkv, d, P, pool, dtype, causal]
         self.ip, self.ix, self.lp, self.qo, self.opts = ip, ix, lp, qo, opts
+        # kind 'C': (prefix_page_size, pool, prefix_indptr, prefix_indices,
+        # prefix_last_page_len, prefix_of)
+        self.prefixes = prefixes
 
     def text(self):
         def arr(a):
@@ -64,6 +67,9 @@ class Call:
         if self.kind == "P":
             parts.append(arr(self.qo))
         parts += [arr(self.ip), arr(self.ix), arr(self.lp)]
+        if self.kind == "C":
+            Pp, ppool, pip, pix, plp, of = self.prefixes
+            parts += [f"{Pp} {ppool}", arr(pip), arr(pix), arr(plp), arr(of)]
         return "\n".join(parts)
 
 
@@ -103,6 +109,17 @@ def malformed_calls():
         a.update(kw)
         out.append(Call("P", 2, a["hq"], a["hkv"], a["d"], a["P"], a["pool"], a["dtype"], a["ip"],
                         a["ix"], a["lp"], a["opts"], a["qo"], a["causal"]))
+    comp = [dict(of=[0, 2]), dict(of=[-2, 0]), dict(of=None), dict(pix=[4, 1, 10]),
+            dict(plp=[70, 5]), dict(plp=[0, 5]), dict(Pp=0), dict(Pp=5000), dict(dtype=2),
+            dict(pip=None), dict(pip=[1, 2, 3]), dict(pip=[0, 2, 1]), dict(ppool=-1),
+            dict(ip=[0, 0, 1], ix=[7], lp=[0, 3]),                 # a prefix, no own token
+            dict(Pp=1, pip=[0, 4000, 4001], pix=list(range(4001)), plp=[1, 1], ppool=4001)]
+    for kw in comp:
+        a = dict(ip=[0, 2, 3], ix=[5, 6, 7], lp=[16, 3], Pp=64, ppool=10, pip=[0, 2, 3],
+                 pix=[4, 1, 8], plp=[64, 5], of=[0, 1], dtype=1)
+        a.update(kw)
+        out.append(Call("C", 2, 8, 2, 128, 16, 100, a["dtype"], a["ip"], a["ix"], a["lp"],
+                        prefixes=(a["Pp"], a["ppool"], a["pip"], a["pix"], a["plp"], a["of"])))
     return out
 
 
@@ -176,6 +193,24 @@ def random_calls(seed=7, n_decode=160, n_prefill=100):
         qoi = np.concatenate([[0], np.cumsum(qo)]).tolist()
         out.append(Call("P", B, G * hkv, hkv, int(rng.choice([64, 128])), P, pool, 1, ip, ix, lp,
                         opts, qoi, causal))
+    for i in range(60):
+        B = int(rng.integers(1, 10))
+        P = int(rng.choice(sizes))
+        lens = [int(x) for x in rng.integers(1, 500, size=B)]
+        nprefix = int(rng.integers(0, 4))
+        Pp = int(rng.choice([1, 7, 16, 64, 512, 4096]))
+        plens = [int(x) for x in rng.integers(0, 3000 if Pp > 1 else 900, size=nprefix)]
+        of = [int(rng.integers(-1, nprefix)) for _ in range(B)]
+        G = int(rng.choice([1, 2, 4, 8]))
+        hkv = int(rng.choice([1, 2, 8]))
+        ip, ix, lp, pool = _page_table(rng, lens, P, int(rng.integers(0, 4)))
+        pip, pix, plp, ppool = _page_table(rng, plens, Pp, int(rng.integers(0, 3)))
+        opts = None
+        if rng.random() < 0.5:
+            opts = [int(rng.choice([0, 8, 256])), int(rng.choice([0, 1, 8])),
+                    int(rng.choice([0, 16, 300])), 0, int(rng.choice([0, 1, 100])), 0, 0]
+        out.append(Call("C", B, G * hkv, hkv, int(rng.choice([64, 128])), P, pool, 1, ip, ix, lp,
+                        opts, prefixes=(Pp, ppool, pip, pix, plp, of)))
     return out
 
 
@@ -186,6 +221,11 @@ def full_size_calls():
         dt = {"f32": 0, "bf16": 1, "fp8": 2}[w.dtype]
         out.append(Call("D", w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
                         w.num_pool_pages, dt, w.kv_indptr, w.kv_indices, w.last_page_len))
+    w = workload(13)
+    out.append(Call("C", w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                    w.num_pool_pages, 1, w.kv_indptr, w.kv_indices, w.last_page_len,
+                    prefixes=(w.prefix_page_size, w.num_prefix_pool_pages, w.prefix_indptr,
+                              w.prefix_indices, w.prefix_last_page_len, w.prefix_of)))
     for cfg in (7, 8):
         w = prefill_workload(cfg)
         out.append(Call("P", w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
@@ -209,15 +249,22 @@ def _mix_array(h, a):
 
 def regular_line(call: Call):
     L = fb.lib()
+    extra = call.prefixes[2:] if call.kind == "C" else ()
     keep = [np.ascontiguousarray(a, dtype=np.int32) if a is not None else None
-            for a in (call.qo, call.ip, call.ix, call.lp)]
+            for a in (call.qo, call.ip, call.ix, call.lp, *extra)]
     ptrs = [None if a is None else (a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
                                     if a.size else ctypes.cast(ctypes.c_void_p(16),
                                                                ctypes.POINTER(ctypes.c_int32)))
             for a in keep]
     h = ctypes.c_void_p()
     b, hq, hkv, d, P, pool, dtype, causal = call.hdr
-    if call.kind == "D":
+    if call.kind == "C":
+        opts = ctypes.byref(binding.PlanOpts(*call.opts)) if call.opts is not None else None
+        nprefix = len(keep[4]) - 1 if keep[4] is not None else 0
+        st = L.fi_plan_create_composed(ptrs[1], ptrs[2], ptrs[3], b, ptrs[4], ptrs[5], ptrs[6],
+                                       nprefix, ptrs[7], hq, hkv, d, P, pool, call.prefixes[0],
+                                       call.prefixes[1], dtype, opts, ctypes.byref(h))
+    elif call.kind == "D":
         opts = ctypes.byref(binding.PlanOpts(*call.opts)) if call.opts is not None else None
         st = L.fi_plan_create(ptrs[1], ptrs[2], ptrs[3], b, hq, hkv, d, P, pool, dtype, opts,
                               ctypes.byref(h))
@@ -228,7 +275,7 @@ def regular_line(call: Call):
     hs = _fnv(1469598103934665603, st)
     if st != 0:
         return st, hs
-    if call.kind == "D":
+    if call.kind in ("D", "C"):
         p = binding.Plan(h.value)
         for k in ("num_items", "num_partial_slots", "workspace_bytes"):
             hs = _fnv(hs, p.info[k])
