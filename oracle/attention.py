@@ -54,7 +54,8 @@ What it computes, and where that comes from:
   causally, to itself and every earlier token. A request holding L tokens
   with n query tokens gives query i (0-based) the first L - n + i + 1 tokens;
   n = 1 is the decode step above. Without the causal mask every query sees
-  all L tokens.
+  all L tokens. With the rotary embedding the queries keep those
+  positions: query i sits at L - n + i (so n <= L is required).
 
 Everything is float64. The exact result of the method is plain softmax
 attention over the listed tokens, so the oracle is that definition, written
@@ -285,6 +286,50 @@ def prefill_attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, last_
             for i in range(n):
                 c = visible_tokens(L, n, i, causal)
                 o, lse = attend(q[q0 + i, heads, :], K[:c], V[:c], sm_scale)
+                O[q0 + i, heads, :] = o
+                LSE[q0 + i, heads] = lse
+    return O, LSE
+
+
+def prefill_query_position(kv_len: int, qo_len: int, i: int) -> int:
+    """Query token i of qo_len is one of the request's newest tokens, all of
+    them cached: its position is kv_len - qo_len + i (masked or not)."""
+    return kv_len - qo_len + i
+
+
+def prefill_attention_rope(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, last_page_len,
+                           causal=True, sm_scale=None, theta: float = 1e4, scale: float = 1.0):
+    """prefill_attention over a K cache that holds keys before the rotary
+    embedding: token t of request b is rotated at position t and its query
+    token i at prefill_query_position(L_b, n_b, i), then the same masked
+    attention. Every request's queries must be cached tokens (n_b <= L_b).
+    Returns float64 O [N, H_q, d] and LSE [N, H_q]."""
+    q = np.asarray(q, dtype=np.float64)
+    N, Hq, d = q.shape
+    Hkv, P = k_pool.shape[1], k_pool.shape[2]
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    O = np.zeros((N, Hq, d))
+    LSE = np.full((N, Hq), NEG_INF)
+    for b in range(len(qo_indptr) - 1):
+        q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
+        n = q1 - q0
+        if n == 0:
+            continue
+        toks = request_tokens(kv_indptr, kv_indices, last_page_len, P, b)
+        L = len(toks)
+        if n > L:
+            raise ValueError("the queries of a request must be cached tokens")
+        for kvh in range(Hkv):
+            heads = [h for h in range(Hq) if kv_head_of(h, G) == kvh]
+            K, V = gather_kv(k_pool, v_pool, toks, kvh)
+            K = apply_rope(K, np.arange(L), theta, scale)
+            for i in range(n):
+                c = visible_tokens(L, n, i, causal)
+                pos = prefill_query_position(L, n, i)
+                qr = apply_rope(q[q0 + i, heads, :], [pos] * len(heads), theta, scale)
+                o, lse = attend(qr, K[:c], V[:c], sm_scale)
                 O[q0 + i, heads, :] = o
                 LSE[q0 + i, heads] = lse
     return O, LSE

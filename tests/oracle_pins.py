@@ -405,7 +405,69 @@ def pin_rope_decode(mod):
         assert np.max(np.abs(LSE - np.array(LSEb))) <= 1e-12, seed
 
 
+def _prefill_rope(mod, w, q, k, v, theta, scale, causal=None):
+    return mod.prefill_attention_rope(q, k, v, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                      w.last_page_len, w.causal if causal is None else causal,
+                                      w.sm_scale, theta, scale)
+
+
+def pin_prefill_rope_bruteforce(mod):
+    """prefill_attention_rope equals the pure-Python prefill brute force over
+    a cache rotated beforehand by plain loops (token t at position t) and
+    query rows rotated at L - n + i, causal and unmasked."""
+    for seed, causal, theta, scale in ((81, True, 1e4, 1.0), (82, False, 5e5, 2.0)):
+        w = random_prefill_workload(seed, 3, 30, 4, 2, 8, 4, causal=causal,
+                                    lens=[29, 1, 12], qo_lens=[5, 1, 12])
+        q, k, v = f64_inputs(w)
+        O, LSE = _prefill_rope(mod, w, q, k, v, theta, scale)
+        kr, qr = k.copy(), q.copy()
+        P = w.page_size
+        for b in range(w.batch):
+            pages = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+            L = int(w.kv_lens()[b])
+            n = int(w.qo_indptr[b + 1] - w.qo_indptr[b])
+            for t in range(L):
+                pg, sl = int(pages[t // P]), t % P
+                kr[pg, :, sl, :] = np.array(rope_rows_loops(k[pg, :, sl, :], [t] * w.num_kv_heads,
+                                                            theta, scale))
+            for i in range(n):
+                row = int(w.qo_indptr[b]) + i
+                qr[row] = np.array(rope_rows_loops(q[row], [L - n + i] * w.num_qo_heads, theta,
+                                                   scale))
+        Ob, LSEb = bruteforce_prefill(qr, kr, v, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                      w.last_page_len, w.sm_scale, causal)
+        assert np.max(np.abs(O - np.array(Ob))) <= 1e-12, seed
+        fin = ~np.isneginf(np.array(LSEb))
+        assert np.max(np.abs(LSE[fin] - np.array(LSEb)[fin])) <= 1e-12, seed
+
+
+def pin_prefill_rope_is_decode_rope(mod):
+    """Causal query i of a request is a decode step over the request cut
+    after its own position (decode puts its query at the last position):
+    each row equals decode_attention_rope over that cut page table."""
+    w = random_prefill_workload(83, 2, 70, 8, 2, 16, 8, causal=True, lens=[70, 33],
+                                qo_lens=[9, 33])
+    q, k, v = f64_inputs(w)
+    theta, scale = 1e4, 1.0
+    O, LSE = _prefill_rope(mod, w, q, k, v, theta, scale)
+    P = w.page_size
+    for b in range(w.batch):
+        L = int(w.kv_lens()[b])
+        n = int(w.qo_indptr[b + 1] - w.qo_indptr[b])
+        pages = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+        for i in range(n):
+            c = L - n + i + 1
+            npg = (c + P - 1) // P
+            row = int(w.qo_indptr[b]) + i
+            Od, LSEd = mod.decode_attention_rope(q[row:row + 1], k, v, np.array([0, npg]),
+                                                 pages[:npg], np.array([c - (npg - 1) * P]),
+                                                 w.sm_scale, theta, scale)
+            assert np.max(np.abs(O[row] - Od[0])) <= 1e-12, (b, i)
+            assert np.max(np.abs(LSE[row] - LSEd[0])) <= 1e-12, (b, i)
+
+
 ROPE_PINS = [pin_rope_closed_forms, pin_rope_relative, pin_rope_decode]
+PREFILL_ROPE_PINS = [pin_prefill_rope_bruteforce, pin_prefill_rope_is_decode_rope]
 
 
 # ---- composed formats: a prefix cache with its own block size + own pages

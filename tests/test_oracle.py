@@ -7,7 +7,8 @@ from tests import oracle_pins as pins
 
 
 @pytest.mark.parametrize("pin", pins.ALL_PINS + pins.PREFILL_PINS + pins.ROPE_PINS +
-                         pins.COMPOSED_PINS + [pins.pin_bf16], ids=lambda f: f.__name__)
+                         pins.COMPOSED_PINS + pins.PREFILL_ROPE_PINS + [pins.pin_bf16],
+                         ids=lambda f: f.__name__)
 def test_pin(pin):
     pin(oa)
 
@@ -289,3 +290,41 @@ def test_composed_variant_without_mistake_passes():
             pin(oa)
     finally:
         mp.undo()
+
+
+# ---- planted mistakes in the prefill rotary embedding
+def _qpos_plus_one(kv_len, qo_len, i):
+    return kv_len - qo_len + i + 1
+
+
+def _qpos_top_left(kv_len, qo_len, i):
+    return i
+
+
+def _qpos_last(kv_len, qo_len, i):
+    return kv_len - 1
+
+
+def _qpos_zero(kv_len, qo_len, i):
+    return 0  # the query left unrotated
+
+
+PREFILL_ROPE_MUTATIONS = {
+    "query_one_past_its_position": ("prefill_query_position", _qpos_plus_one),
+    "query_at_its_index": ("prefill_query_position", _qpos_top_left),
+    "every_query_at_the_last_position": ("prefill_query_position", _qpos_last),
+    "query_not_rotated": ("prefill_query_position", _qpos_zero),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_ROPE_MUTATIONS))
+def test_prefill_rope_oracle_mutations_are_caught(name, monkeypatch):
+    attr, fn = PREFILL_ROPE_MUTATIONS[name]
+    monkeypatch.setattr(oa, attr, fn)
+    caught = []
+    for pin in pins.PREFILL_ROPE_PINS:
+        try:
+            pin(oa)
+        except (AssertionError, ValueError, IndexError, TypeError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake {name} passed every prefill RoPE pin"
