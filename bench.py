@@ -347,8 +347,13 @@ def cpu_baseline_prefill(w, q, k, v, min_seconds=10.0):
             ip = np.array([0, w.kv_indptr[b + 1] - w.kv_indptr[b]], dtype=np.int64)
             ix = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
             t0 = time.perf_counter()
-            oa.prefill_attention(qh, kh, vh, np.array([0, n]), ip, ix, w.last_page_len[b:b + 1],
-                                 w.causal, w.sm_scale)
+            if w.rope_theta:
+                oa.prefill_attention_rope(qh, kh, vh, np.array([0, n]), ip, ix,
+                                          w.last_page_len[b:b + 1], w.causal, w.sm_scale,
+                                          w.rope_theta, w.rope_scale)
+            else:
+                oa.prefill_attention(qh, kh, vh, np.array([0, n]), ip, ix,
+                                     w.last_page_len[b:b + 1], w.causal, w.sm_scale)
             spent += time.perf_counter() - t0
             Lb = int(L[b])
             pairs = sum(max(0, Lb - n + i + 1) for i in range(n)) if w.causal else Lb * n
@@ -443,6 +448,7 @@ def bench_prefill(args, w):
         p = fb.prefill_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len,
                             w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
                             w.num_pool_pages, causal=w.causal, dtype=w.dtype,
+                            rope=bool(w.rope_theta),
                             fixed_chunk_tokens=args.fixed_chunk_tokens,
                             items_per_cu=args.items_per_cu)
         plan_t.append(time.perf_counter() - t0)
@@ -459,7 +465,7 @@ def bench_prefill(args, w):
         if ev:
             ev[0].record()
         fb.prefill(q, k, v, p, out=out, lse=lse, workspace=ws, k_scale=w.k_scale,
-                   v_scale=w.v_scale)
+                   v_scale=w.v_scale, rope_theta=w.rope_theta or None, rope_scale=w.rope_scale)
         if ev:
             ev[1].record()
 
@@ -491,6 +497,7 @@ def bench_prefill(args, w):
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "page_size": w.page_size, "qo_tokens": w.num_qo_tokens,
                    "kv_dtype": w.dtype,
+                   **({"rope_theta": w.rope_theta} if w.rope_theta else {}),
                    "kv_tokens": int(w.kv_lens().sum()), "causal": bool(w.causal),
                    "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
                    "parallelism": "single-gpu", "plan_items": p.info["num_items"],

@@ -37,7 +37,7 @@ EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_
             "fi_prefill_plan_merges", "fi_prefill_plan_upload", "fi_prefill_run",
             "fi_prefill_plan_destroy", "fi_decode_run_rope", "fi_decode_run_rope_scaled",
             "fi_decode_run_noalloc", "fi_prefill_run_scaled", "fi_plan_create_composed",
-            "fi_decode_run_composed"]
+            "fi_decode_run_composed", "fi_prefill_run_rope"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 QITEM_STRIDE = 12
 QMERGE_STRIDE = 8
@@ -78,7 +78,8 @@ class PlanInfo(ctypes.Structure):
 
 class PrefillOpts(ctypes.Structure):
     _fields_ = [("num_cus", ctypes.c_int32), ("items_per_cu", ctypes.c_int32),
-                ("fixed_chunk_tokens", ctypes.c_int32), ("num_xcds", ctypes.c_int32)]
+                ("fixed_chunk_tokens", ctypes.c_int32), ("num_xcds", ctypes.c_int32),
+                ("rope", ctypes.c_int32)]
 
 
 class PrefillInfo(ctypes.Structure):
@@ -90,7 +91,7 @@ class PrefillInfo(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("num_qo_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("causal", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("rope", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -159,6 +160,8 @@ def lib() -> ctypes.CDLL:
     L.fi_prefill_run.restype = i32
     L.fi_prefill_run_scaled.argtypes = [vp, vp, vp, vp, f32, f32, vp, vp, f32, vp, sz, vp]
     L.fi_prefill_run_scaled.restype = i32
+    L.fi_prefill_run_rope.argtypes = [vp, vp, vp, vp, f32, f32, vp, vp, f32, vp, sz, vp]
+    L.fi_prefill_run_rope.restype = i32
     L.fi_prefill_plan_destroy.argtypes = [vp]
     L.fi_prefill_plan_destroy.restype = None
     L.fi_last_error.argtypes = []
@@ -557,13 +560,15 @@ class PrefillPlan:
 def prefill_plan(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int,
                  num_kv_heads: int, head_dim: int, page_size: int, num_pool_pages: int,
                  causal: bool = True, dtype="bf16", num_cus: int = 0, items_per_cu: int = 0,
-                 fixed_chunk_tokens: int = 0, num_xcds: int = 0) -> PrefillPlan:
-    """fi_prefill_plan_create over host arrays (numpy or CPU tensors)."""
+                 fixed_chunk_tokens: int = 0, num_xcds: int = 0, rope: bool = False) -> PrefillPlan:
+    """fi_prefill_plan_create over host arrays (numpy or CPU tensors). With
+    ``rope`` the plan is for runs over a K cache of keys before the rotary
+    embedding (fi_prefill_run_rope)."""
     qp, ip, ix, lp = _i32(qo_indptr), _i32(kv_indptr), _i32(kv_indices), _i32(kv_last_page_len)
     batch = _check_lengths(ip, ix, lp)
     if qp.ndim != 1 or len(qp) != batch + 1:
         raise ValueError("qo_indptr, kv_indptr and kv_last_page_len disagree on the batch size")
-    opts = PrefillOpts(num_cus, items_per_cu, fixed_chunk_tokens, num_xcds)
+    opts = PrefillOpts(num_cus, items_per_cu, fixed_chunk_tokens, num_xcds, int(bool(rope)))
     h = ctypes.c_void_p()
     ix_ptr = _ptr32(ix) if ix.size else ctypes.POINTER(ctypes.c_int32)()
     _check(lib().fi_prefill_plan_create(_ptr32(qp), _ptr32(ip), ix_ptr, _ptr32(lp), batch,
@@ -577,9 +582,12 @@ def prefill_plan(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_qo_head
 
 def prefill(q, k_pages, v_pages, plan_: PrefillPlan, out=None, lse=None,
             sm_scale: Optional[float] = None, workspace=None, stream=None,
-            k_scale: float = 1.0, v_scale: float = 1.0):
+            k_scale: float = 1.0, v_scale: float = 1.0, rope_theta: Optional[float] = None,
+            rope_scale: float = 1.0):
     """fi_prefill_run_scaled: returns (out [N, H_q, d] bf16, lse [N, H_q]
-    float32). k_scale / v_scale dequantise an fp8 KV cache."""
+    float32). k_scale / v_scale dequantise an fp8 KV cache. A plan made with
+    ``rope=True`` runs fi_prefill_run_rope (q and K before the embedding;
+    rope_theta None or <= 0 selects 10000)."""
     import torch
     for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
         _require_gpu(t, n)
@@ -606,6 +614,21 @@ def prefill(q, k_pages, v_pages, plan_: PrefillPlan, out=None, lse=None,
     elif workspace.device != q.device:
         raise ValueError(f"workspace is on {workspace.device}, q on {q.device}")
     scale = float(sm_scale) if sm_scale else 0.0
+    if info["rope"]:
+        if k_scale != 1.0 or v_scale != 1.0:
+            raise ValueError("a rope prefill plan runs over bf16 caches (no scales)")
+        _check(lib().fi_prefill_run_rope(plan_.handle, ctypes.c_void_p(q.data_ptr()),
+                                         ctypes.c_void_p(k_pages.data_ptr()),
+                                         ctypes.c_void_p(v_pages.data_ptr()),
+                                         float(rope_theta or 0.0), float(rope_scale),
+                                         ctypes.c_void_p(out.data_ptr()),
+                                         ctypes.c_void_p(lse.data_ptr()), scale,
+                                         ctypes.c_void_p(workspace.data_ptr()),
+                                         workspace.numel() * workspace.element_size(),
+                                         ctypes.c_void_p(_stream(stream))))
+        return out, lse
+    if rope_theta:
+        raise ValueError("rope_theta given for a plan made without rope=True")
     _check(lib().fi_prefill_run_scaled(plan_.handle, ctypes.c_void_p(q.data_ptr()),
                                        ctypes.c_void_p(k_pages.data_ptr()),
                                        ctypes.c_void_p(v_pages.data_ptr()), float(k_scale),

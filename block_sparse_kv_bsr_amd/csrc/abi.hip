@@ -121,20 +121,15 @@ fi_status fi_prefill_plan_upload(fi_prefill_plan* plan, void* workspace, size_t 
   return upload(plan, workspace, workspace_bytes, stream);
 }
 
-fi_status fi_prefill_run(const fi_prefill_plan* plan, const void* q, const void* k_pages,
-                         const void* v_pages, void* out, float* lse, float sm_scale,
-                         void* workspace, size_t workspace_bytes, fi_stream_t stream) {
-  return fi_prefill_run_scaled(plan, q, k_pages, v_pages, 1.f, 1.f, out, lse, sm_scale, workspace,
-                               workspace_bytes, stream);
-}
+namespace {
 
-fi_status fi_prefill_run_scaled(const fi_prefill_plan* plan, const void* q, const void* k_pages,
-                                const void* v_pages, float k_scale, float v_scale, void* out,
-                                float* lse, float sm_scale, void* workspace,
-                                size_t workspace_bytes, fi_stream_t stream) {
-  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
-  if (!(k_scale > 0.f) || !(v_scale > 0.f) || std::isinf(k_scale) || std::isinf(v_scale))
-    return fail(FI_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+// The prefill run shared by the entry points below (checks, then the tile
+// kernel and, for cut tiles, the merge kernel). rope_theta > 0 selects the
+// rotary variant.
+fi_status prefill_run(const fi_prefill_plan* plan, const void* q, const void* k_pages,
+                      const void* v_pages, float k_scale, float v_scale, float rope_theta,
+                      float rope_scale, void* out, float* lse, float sm_scale, void* workspace,
+                      size_t workspace_bytes, fi_stream_t stream) {
   if (plan->num_items() == 0) return FI_OK;
   if (!q || !out) return fail(FI_ERR_INVALID_ARG, "q or out is NULL");
   if (!k_pages || !v_pages) return fail(FI_ERR_INVALID_ARG, "k_pages or v_pages is NULL");
@@ -173,12 +168,56 @@ fi_status fi_prefill_run_scaled(const fi_prefill_plan* plan, const void* q, cons
   a.sm_scale = sm_scale;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.rope = rope_theta > 0.f;
+  a.rope_theta = rope_theta;
+  a.rope_scale = rope_scale;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = fi::launch_prefill(a, s);
   if (e != hipSuccess) return hip_fail(e, "prefill tile kernel launch");
   e = fi::launch_prefill_merge(a, s);
   if (e != hipSuccess) return hip_fail(e, "prefill merge kernel launch");
   return FI_OK;
+}
+
+}  // namespace
+
+fi_status fi_prefill_run(const fi_prefill_plan* plan, const void* q, const void* k_pages,
+                         const void* v_pages, void* out, float* lse, float sm_scale,
+                         void* workspace, size_t workspace_bytes, fi_stream_t stream) {
+  return fi_prefill_run_scaled(plan, q, k_pages, v_pages, 1.f, 1.f, out, lse, sm_scale, workspace,
+                               workspace_bytes, stream);
+}
+
+fi_status fi_prefill_run_scaled(const fi_prefill_plan* plan, const void* q, const void* k_pages,
+                                const void* v_pages, float k_scale, float v_scale, void* out,
+                                float* lse, float sm_scale, void* workspace,
+                                size_t workspace_bytes, fi_stream_t stream) {
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || std::isinf(k_scale) || std::isinf(v_scale))
+    return fail(FI_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+  if (plan->rope)
+    return fail(FI_ERR_INVALID_ARG, "a plan made with fi_prefill_opts.rope runs with "
+                                    "fi_prefill_run_rope");
+  return prefill_run(plan, q, k_pages, v_pages, k_scale, v_scale, 0.f, 1.f, out, lse, sm_scale,
+                     workspace, workspace_bytes, stream);
+}
+
+fi_status fi_prefill_run_rope(const fi_prefill_plan* plan, const void* q, const void* k_pages,
+                              const void* v_pages, float rope_theta, float rope_scale, void* out,
+                              float* lse, float sm_scale, void* workspace,
+                              size_t workspace_bytes, fi_stream_t stream) {
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  if (!plan->rope)
+    return fail(FI_ERR_INVALID_ARG, "fi_prefill_run_rope needs a plan made with "
+                                    "fi_prefill_opts.rope");
+  if (std::isnan(rope_theta) || std::isinf(rope_theta) || std::isnan(rope_scale) ||
+      std::isinf(rope_scale))
+    return fail(FI_ERR_INVALID_ARG, "rope_theta and rope_scale must be finite");
+  if (!(rope_theta > 0.f)) rope_theta = 10000.f;
+  if (!(rope_scale > 0.f)) rope_scale = 1.f;
+  if (!(rope_theta > 1.f)) return fail(FI_ERR_INVALID_ARG, "rope_theta must exceed 1");
+  return prefill_run(plan, q, k_pages, v_pages, 1.f, 1.f, rope_theta, rope_scale, out, lse,
+                     sm_scale, workspace, workspace_bytes, stream);
 }
 
 void fi_prefill_plan_destroy(fi_prefill_plan* plan) { destroy(plan); }

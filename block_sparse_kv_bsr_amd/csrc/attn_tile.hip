@@ -100,6 +100,8 @@ struct TileParams {
   int causal;           // prefill: row r attends VISIBLE + r / G tokens
   float scale_log2;     // sm_scale * k_scale * log2(e)
   float v_scale;        // multiplies every output and partial state (V dequantisation)
+  double rope_log2_theta;  // rotary embedding: log2(rope_theta)
+  double rope_rev;         // 1 / (2 pi rope_scale): revolutions per radian, positions scaled
 };
 
 template <int D, int kKv = 2>
@@ -226,6 +228,17 @@ __device__ __forceinline__ void lgkm_wait_tied(u32x2_t (&r)[N][2]) {
   }
 }
 
+// s_waitcnt lgkmcnt(CNT), then every register of r redefined by an empty
+// asm statement ordered after the wait: no use of a value read can be
+// scheduled above it.
+template <int CNT, typename T, int N>
+__device__ __forceinline__ void lgkm_wait_then(T (&r)[N]) {
+  static_assert(CNT >= 0 && CNT < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(CNT) : "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
+}
+
 // s_waitcnt lgkmcnt(CNT) tied to fp8 K fragments (see lgkm_wait_tied_n).
 template <int CNT>
 __device__ __forceinline__ void lgkm_wait_tied_n8(u32x2_t (&r)[8]) {
@@ -253,6 +266,25 @@ __device__ __forceinline__ u32x2_t lds_tr8_b64(uint32_t a) {
   asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF) : "memory");
   return r;
 }
+template <int OFF>
+__device__ __forceinline__ void lds_w128(uint32_t a, u32x4_t v) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(a), "v"(v), "i"(OFF) : "memory");
+}
+__device__ __forceinline__ void lds_w64(uint32_t a, u32x2_t v) {
+  asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+
+// Cosine and sine of the rotary angle of a dim pair at position pos: the
+// pair's frequency is a 64-bit binary fraction of a revolution per position,
+// so pos * freq mod 1 is exact integer arithmetic; its top 32 bits give the
+// angle for sincospif.
+__device__ __forceinline__ void rot_sincos(uint64_t freq, uint32_t pos, float& c, float& s) {
+  const uint64_t ph = (uint64_t)pos * freq;
+  const float rev = (float)(uint32_t)(ph >> 32) * 0x1p-32f;
+  sincospif(2.f * rev, &s, &c);
+}
+
 // Eight fp8 (E4M3) codes widened to eight bf16 values (exact) in code order.
 __device__ __forceinline__ bf16x8_t widen8(u32x2_t w) {
   const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
@@ -278,23 +310,35 @@ __device__ __forceinline__ float sum_with_partner32(float x) {
 // independent accumulation chains; one softmax step covers the wave's whole
 // block, and the exponentials of one 16-token step overlap the products of
 // the previous one.
-template <bool kPrefill>
+template <bool kPrefill, bool kRope = false>
 struct Roles {
-  static constexpr bool kSplit = !kPrefill;
+  // a rope tile (prefill with the rotary embedding) takes the split layout:
+  // its waves hold the queries' lo parts too, so each takes half a block
+  static constexpr bool kSplit = !kPrefill || kRope;
   static constexpr int kRowGroups = kSplit ? 4 : 8;
   static constexpr int kSub = kSplit ? 1 : 2;  // 32-token sub-blocks per wave and block
 };
 static_assert(FI_PREFILL_ROWS == 32 * 8, "a prefill tile is 8 row groups of 32 rows");
 
-template <int D, bool kPrefill, int kKv = 2>
+template <int D, bool kPrefill, int kKv = 2, bool kRope = false>
 __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   static_assert(kKv == 2 || kPrefill, "shared-prefix items read bf16 caches");
+  static_assert(!kRope || (kPrefill && kKv == 2 && D == 128), "rope tiles: bf16 prefill, d 128");
   using Gm = Geom<D, kKv>;
-  using R = Roles<kPrefill>;
+  using R = Roles<kPrefill, kRope>;
   constexpr int NS = Gm::kStages;
   constexpr int kRB = Gm::kRowBytes;
   __shared__ __attribute__((aligned(1024))) char s_ring[NS][2][Gm::kBlockBytes];
   __shared__ uint32_t s_pid[kIds];  // page byte offsets (page + head) / 128
+  // rotary embedding: each pair's frequency (a 64-bit fraction of a
+  // revolution per position), the rotations of the 64 rows of a block
+  // relative to its first token, [row][pair] (cos, sin), the rotation of the
+  // block's first token (two blocks, by parity), and the lo bf16 parts of the
+  // rotated K block (its hi parts replace K in the ring stage)
+  __shared__ uint64_t s_freq[kRope ? D / 2 : 1];
+  __shared__ __attribute__((aligned(16))) float2 s_rrow[kRope ? kBlock * D / 2 : 1];
+  __shared__ __attribute__((aligned(16))) float2 s_rbase[kRope ? 2 * D / 2 : 1];
+  __shared__ __attribute__((aligned(1024))) char s_klo[kRope ? Gm::kBlockBytes : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -308,6 +352,7 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
 
   int h, nrows, page_begin, npg, ntok;
   int tok_off = 0;      // slot of the chunk's first token in its first page
+  int kv_pos = 0, q_pos = 0;  // rope: positions of the chunk's first token and of the tile's first query
   int lim;              // tokens of the chunk this row attends (may be <= 0)
   int64_t q_index;      // row of q (and, for prefill, of out / lse) x heads + head
   // prefix: partial row = prefix_slot[b][h] + chunk; prefill: slot (-1 = direct)
@@ -339,6 +384,10 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
     const int kv_begin = it[FI_QITEM_KV_BEGIN];
     ntok = it[FI_QITEM_NUM_KV];
     const int visible = it[FI_QITEM_VISIBLE];
+    if constexpr (kRope) {
+      kv_pos = kv_begin;
+      q_pos = it[FI_QITEM_Q_POS];
+    }
     page_begin = it[FI_QITEM_PAGE_BEGIN];
     slot_base = it[FI_QITEM_SLOT];
     npg = (ntok + p.page_size - 1) / p.page_size;  // <= FI_PREFILL_MAX_PAGES = kIds
@@ -380,6 +429,51 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
       uint4 v = *reinterpret_cast<const uint4*>(qrow + (16 * s + 8 * half) * 2);
       if (!row_ok) v = make_uint4(0, 0, 0, 0);
       qf[s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  // rope: frequencies, the row table and block 0's base rotation; the
+  // lane's query row turned at its position and split into hi (qf) and lo
+  // (ql) bf16 parts. Pairs (i, i + 64) sit in steps s and s + 4 of one lane.
+  bf16x8_t ql[kRope ? D / 16 : 1];
+  if constexpr (kRope) {
+    if (tid < D / 2) {
+      double fq = exp2(-(2.0 * tid / D) * p.rope_log2_theta) * p.rope_rev;
+      fq -= floor(fq);
+      s_freq[tid] = (uint64_t)ldexp(fq, 64);
+    }
+    __syncthreads();
+    for (int e = tid; e < kBlock * D / 2; e += 512) {
+      float cs, sn;
+      rot_sincos(s_freq[e % (D / 2)], (uint32_t)(e / (D / 2)), cs, sn);
+      s_rrow[e] = make_float2(cs, sn);
+    }
+    if (tid < D / 2) {
+      float cs, sn;
+      rot_sincos(s_freq[tid], (uint32_t)kv_pos, cs, sn);
+      s_rbase[tid] = make_float2(cs, sn);
+    }
+    const uint32_t qp = (uint32_t)(q_pos + (row_ok ? row / G : 0));
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      float x[8], y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = (float)qf[s][e];
+        y[e] = (float)qf[s + D / 32][e];
+      }
+      uint32_t xh[4], xl[4], yh[4], yl[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float c0, s0, c1, s1;
+        rot_sincos(s_freq[16 * s + 8 * half + e], qp, c0, s0);
+        rot_sincos(s_freq[16 * s + 8 * half + e + 1], qp, c1, s1);
+        split_bf16x2(x[e] * c0 - y[e] * s0, x[e + 1] * c1 - y[e + 1] * s1, xh[e / 2], xl[e / 2]);
+        split_bf16x2(y[e] * c0 + x[e] * s0, y[e + 1] * c1 + x[e + 1] * s1, yh[e / 2], yl[e / 2]);
+      }
+      qf[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{xh[0], xh[1], xh[2], xh[3]});
+      ql[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{xl[0], xl[1], xl[2], xl[3]});
+      qf[s + D / 32] = __builtin_bit_cast(bf16x8_t, u32x4_t{yh[0], yh[1], yh[2], yh[3]});
+      ql[s + D / 32] = __builtin_bit_cast(bf16x8_t, u32x4_t{yl[0], yl[1], yl[2], yl[3]});
     }
   }
   // q and the page ids are in before any K/V load is issued, so the waits on
@@ -491,11 +585,96 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
 
     const uint32_t kst = lds_u32(s_ring[st][0]);
     const uint32_t vst = lds_u32(s_ring[st][1]);
+    f32x16_t sc[R::kSub];
+    if constexpr (kRope) {
+      // ---- turn block j's K rows: thread t takes row t / 8 and pairs
+      // 8 (t % 8) .. +7 (dims i and i + 64), at position kv_pos + 64 j + row
+      // (the block's base rotation times the row's, both from exact
+      // phases), in fp32; the hi bf16 parts replace K in the stage, the lo
+      // parts go to s_klo, at the same swizzled places
+      const int rr = tid >> 3, gg = tid & 7;
+      const int sw = Gm::swz_k(rr);
+      const uint32_t pa = rr * kRB + ((gg ^ sw) * 16), pb = rr * kRB + (((gg + 8) ^ sw) * 16);
+      const uint32_t klo = lds_u32(s_klo);
+      const uint32_t rra = lds_u32(&s_rrow[rr * (D / 2) + 8 * gg]);
+      const uint32_t rba = lds_u32(&s_rbase[(j & 1) * (D / 2) + 8 * gg]);
+      u32x4_t kx[2], rt[8];
+      kx[0] = lds_b128<0>(kst + pa);
+      kx[1] = lds_b128<0>(kst + pb);
+      rt[0] = lds_b128<0>(rra);
+      rt[1] = lds_b128<16>(rra);
+      rt[2] = lds_b128<32>(rra);
+      rt[3] = lds_b128<48>(rra);
+      rt[4] = lds_b128<0>(rba);
+      rt[5] = lds_b128<16>(rba);
+      rt[6] = lds_b128<32>(rba);
+      rt[7] = lds_b128<48>(rba);
+      lgkm_wait_then<0>(kx);
+      lgkm_wait_then<0>(rt);
+      // the next block's base rotation, read after the next barrier (its
+      // buffer was last read before this block's barrier)
+      if (tid < D / 2) {
+        u32x2_t fw[1];
+        fw[0] = lds_b64<0>(lds_u32(&s_freq[tid]));
+        lgkm_wait_then<0>(fw);
+        float cs, sn;
+        rot_sincos(((uint64_t)fw[0].y << 32) | fw[0].x, (uint32_t)(kv_pos + (j + 1) * kBlock), cs,
+                   sn);
+        lds_w64(lds_u32(&s_rbase[((j + 1) & 1) * (D / 2) + tid]),
+                u32x2_t{__float_as_uint(cs), __float_as_uint(sn)});
+      }
+      uint32_t xh[4], xl[4], yh[4], yl[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float cs[2], sn[2], x[2], y[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int k = e + u;  // pair 8 gg + k: float2 k of the row and base tables
+          const float rc = __uint_as_float(rt[k / 2][2 * (k % 2)]);
+          const float rs = __uint_as_float(rt[k / 2][2 * (k % 2) + 1]);
+          const float bc = __uint_as_float(rt[4 + k / 2][2 * (k % 2)]);
+          const float bs = __uint_as_float(rt[4 + k / 2][2 * (k % 2) + 1]);
+          cs[u] = bc * rc - bs * rs;
+          sn[u] = bs * rc + bc * rs;
+          const uint32_t wx = kx[0][k / 2], wy = kx[1][k / 2];
+          x[u] = __uint_as_float(k % 2 ? (wx & 0xFFFF0000u) : (wx << 16));
+          y[u] = __uint_as_float(k % 2 ? (wy & 0xFFFF0000u) : (wy << 16));
+        }
+        split_bf16x2(x[0] * cs[0] - y[0] * sn[0], x[1] * cs[1] - y[1] * sn[1], xh[e / 2], xl[e / 2]);
+        split_bf16x2(y[0] * cs[0] + x[0] * sn[0], y[1] * cs[1] + x[1] * sn[1], yh[e / 2], yl[e / 2]);
+      }
+      lds_w128<0>(kst + pa, u32x4_t{xh[0], xh[1], xh[2], xh[3]});
+      lds_w128<0>(kst + pb, u32x4_t{yh[0], yh[1], yh[2], yh[3]});
+      lds_w128<0>(klo + pa, u32x4_t{xl[0], xl[1], xl[2], xl[3]});
+      lds_w128<0>(klo + pb, u32x4_t{yl[0], yl[1], yl[2], yl[3]});
+      // every wave's rotated rows are in place before any fragment is read
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+
+      // ---- S^T = Kh.Qh + Kh.Ql + Kl.Qh (one sub-block per wave)
+      u32x4_t kh[D / 16], kl[D / 16];
+#pragma unroll
+      for (int q = 0; q < D / 16; ++q) {
+        kh[q] = lds_b128<0>(kst + kb[q]);
+        kl[q] = lds_b128<0>(klo + kb[q]);
+      }
+      lgkm_wait_then<0>(kh);
+      lgkm_wait_then<0>(kl);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[0][r] = 0.f;
+#pragma unroll
+      for (int q = 0; q < D / 16; ++q) {
+        const bf16x8_t h8 = __builtin_bit_cast(bf16x8_t, kh[q]);
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h8, qf[q], sc[0], 0, 0, 0);
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h8, ql[q], sc[0], 0, 0, 0);
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kl[q]), qf[q],
+                                                        sc[0], 0, 0, 0);
+      }
+    } else {
     // ---- S^T = K . Q^T of every sub-block (independent chains). All K
     // fragments are requested first; each sub-block's products start as soon
     // as its own fragments are in, and the scheduling barriers keep the
     // first sub-block's products ahead of the second's wait.
-    f32x16_t sc[R::kSub];
     u32x4_t kv[kKv == 2 ? R::kSub : 1][D / 16];   // bf16 fragments
     u32x2_t kv8[kKv == 1 ? R::kSub : 1][D / 16];  // fp8 fragments (widened to bf16 for the product)
     static_for<R::kSub>([&](auto SB) {
@@ -527,6 +706,7 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     });
+    }  // kRope
     // the loads of a later block go out while the products run
     issue(j + NS - 1, (j + NS - 1) % NS);
 
@@ -781,7 +961,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.scale_log2 = a.sm_scale * a.k_scale * kLog2e;
   p.v_scale = a.v_scale;
   const dim3 grid((uint32_t)a.num_items), block(64 * kWaves);
-  if (a.kv_bytes == 1) {
+  if (a.rope) {
+    if (a.head_dim != 128 || a.kv_bytes != 2) return hipErrorInvalidValue;
+    p.rope_log2_theta = std::log2((double)a.rope_theta);
+    p.rope_rev = 1.0 / (2.0 * M_PI * (double)a.rope_scale);
+    hipLaunchKernelGGL((tile_attend_kernel<128, true, 2, true>), grid, block, 0, stream, p);
+  } else if (a.kv_bytes == 1) {
     if (a.head_dim != 128) return hipErrorInvalidValue;
     hipLaunchKernelGGL((tile_attend_kernel<128, true, 1>), grid, block, 0, stream, p);
   } else if (a.head_dim == 128) {

@@ -61,6 +61,8 @@ struct PrefillArgs {
   int32_t kv_bytes;         // 2 bf16, 1 fp8 e4m3 (q/out bf16)
   float sm_scale;
   float k_scale, v_scale;   // K/V dequantisation scales (1 for bf16)
+  bool rope;                // K and q stored before the rotary embedding
+  float rope_theta, rope_scale;
 };
 
 struct MergeTwoArgs {

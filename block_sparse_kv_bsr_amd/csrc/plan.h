@@ -77,6 +77,7 @@ struct fi_prefill_plan {
   int32_t batch = 0, num_qo_heads = 0, num_kv_heads = 0, head_dim = 0, page_size = 0;
   int32_t group = 0, causal = 1, tokens_per_tile = 0, chunk_tokens = 0;
   fi_dtype dtype = FI_DTYPE_BF16;  // of the K/V pages (q and out are bf16)
+  int32_t rope = 0;                // tiles for fi_prefill_run_rope
   int64_t num_pool_pages = 0, total_qo = 0, total_kv = 0, visible_pairs = 0;
   int64_t num_tiles = 0, num_slots = 0;
   std::vector<int32_t> items;   // num_items * FI_QITEM_STRIDE

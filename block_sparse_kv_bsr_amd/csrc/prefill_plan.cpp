@@ -72,6 +72,12 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
       return fail(FI_ERR_UNSUPPORTED, "prefill needs FI_DTYPE_BF16 or FI_DTYPE_FP8_E4M3");
     if (dtype == FI_DTYPE_FP8_E4M3 && head_dim != 128)
       return fail(FI_ERR_UNSUPPORTED, "fp8 prefill is built for head_dim 128");
+    const bool rope = opts && opts->rope;
+    if (rope && (dtype != FI_DTYPE_BF16 || head_dim != 128))
+      return fail(FI_ERR_UNSUPPORTED, "prefill with the rotary embedding is built for bf16, head_dim 128");
+    if (rope && group > FI_PREFILL_ROWS / 2)
+      return fail(FI_ERR_UNSUPPORTED, "prefill with the rotary embedding needs G <= " +
+                                          std::to_string(FI_PREFILL_ROWS / 2));
     std::vector<int64_t> kvlen;
     {
       const fi_status st = fi::check_page_table(kv_indptr, kv_indices, kv_last_page_len, batch,
@@ -83,10 +89,11 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
       if (qo_indptr[b + 1] < qo_indptr[b])
         return fail(FI_ERR_INVALID_ARG, "qo_indptr is not non-decreasing at request " +
                                             std::to_string(b));
-      if (causal && qo_indptr[b + 1] - qo_indptr[b] > kvlen[b])
+      if ((causal || rope) && qo_indptr[b + 1] - qo_indptr[b] > kvlen[b])
         return fail(FI_ERR_INVALID_ARG, "request " + std::to_string(b) +
                                             " has more query tokens than cached tokens "
-                                            "(causal queries are the newest cached tokens)");
+                                            "(causal or rotated queries are the newest cached "
+                                            "tokens)");
     }
     const int64_t total_qo = batch > 0 ? qo_indptr[batch] : 0;
     if (total_qo * (int64_t)num_qo_heads > INT32_MAX)
@@ -110,14 +117,17 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
     p->dtype = dtype;
     p->num_pool_pages = num_pool_pages;
     p->total_qo = total_qo;
-    const int64_t T = FI_PREFILL_ROWS / group;  // query tokens per tile
+    p->rope = rope ? 1 : 0;
+    // query tokens per tile: a rope tile is half as tall (its kernel keeps
+    // the queries' lo parts in registers too)
+    const int64_t T = (rope ? FI_PREFILL_ROWS / 2 : FI_PREFILL_ROWS) / group;
     p->tokens_per_tile = (int32_t)T;
 
     // ---- tiles: (request, KV head, block of T query tokens); the range a
     // tile attends is what its last query sees
     struct Tile {
       int32_t b, qo_row, nqo;
-      int64_t visible, range;
+      int64_t visible, range, qpos;
     };
     std::vector<Tile> tiles;
     int64_t work = 0;
@@ -129,7 +139,7 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
         const int64_t nq = std::min<int64_t>(T, n - t0);
         const int64_t vis = causal ? L - n + t0 + 1 : L;
         const int64_t range = causal ? vis + nq - 1 : L;
-        tiles.push_back({b, (int32_t)(qo_indptr[b] + t0), (int32_t)nq, vis, range});
+        tiles.push_back({b, (int32_t)(qo_indptr[b] + t0), (int32_t)nq, vis, range, L - n + t0});
         work += range * num_kv_heads;
       }
     }
@@ -181,6 +191,7 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
           f[FI_QITEM_PAGE_BEGIN] = (int32_t)(kv_indptr[t.b] + begin / page_size);
           f[FI_QITEM_SLOT] = k > 1 ? (int32_t)(slot0 + c) : -1;
           f[FI_QITEM_CHUNK] = (int32_t)c;
+          f[FI_QITEM_Q_POS] = (int32_t)t.qpos;
           longest = std::max(longest, f[FI_QITEM_NUM_KV]);
           p->items.insert(p->items.end(), f, f + FI_QITEM_STRIDE);
         }
@@ -302,6 +313,7 @@ fi_status fi_prefill_plan_get_info(const fi_prefill_plan* p, fi_prefill_info* in
   r.page_size = p->page_size;
   r.causal = p->causal;
   r.dtype = p->dtype;
+  r.rope = p->rope;
   *info = r;
   return FI_OK;
 }

@@ -59,6 +59,8 @@ CONFIG_NAMES = {
     # config 5 with the shared prefix held once in a second cache of
     # 4096-token blocks (composed formats)
     13: "sparse_prefix_b32_p64_composed_b4096",
+    # the append batch over a K cache that holds keys before the rotary embedding
+    14: "append_b64_q128_skewed_rope",
 }
 
 # Rotary embedding base of the rope workload (the Llama-3 value).
@@ -309,7 +311,8 @@ def prefill_workload(config_id: int) -> PrefillWorkload:
     64 histories (log-uniform lengths in [32, 32768]) with their newest
     min(128, L_b) tokens as queries (a chunk appended to each request).
     32 query / 8 KV heads, head_dim 128, bf16. 12: config 8 over an fp8
-    (E4M3) KV cache with scales 1/64."""
+    (E4M3) KV cache with scales 1/64. 14: config 8 with q and K before the
+    rotary embedding (theta 5e5)."""
     rng = np.random.default_rng([config_id, 0])
     seed = 1_000_003 * config_id + 1
     if config_id == 7:
@@ -328,6 +331,9 @@ def prefill_workload(config_id: int) -> PrefillWorkload:
         return dataclasses.replace(prefill_workload(8), name=CONFIG_NAMES[12], config_id=12,
                                    dtype="fp8", value_seed=seed, k_scale=FP8_SCALE,
                                    v_scale=FP8_SCALE)
+    if config_id == 14:
+        return dataclasses.replace(prefill_workload(8), name=CONFIG_NAMES[14], config_id=14,
+                                   value_seed=seed, rope_theta=ROPE_THETA)
     raise ValueError(f"unknown prefill config {config_id}")
 
 
@@ -336,7 +342,8 @@ def random_prefill_workload(seed: int, batch: int, max_len: int, num_qo_heads: i
                             causal: bool = True, max_qo: Optional[int] = None,
                             lens: Optional[List[int]] = None,
                             qo_lens: Optional[List[int]] = None,
-                            spare_pages: int = 3, dtype: str = "bf16") -> PrefillWorkload:
+                            spare_pages: int = 3, dtype: str = "bf16",
+                            rope_theta: float = 0.0, rope_scale: float = 1.0) -> PrefillWorkload:
     """Small ragged prefill case: KV lengths U{1..max_len} (or given), query
     counts U{1..min(L_b, max_qo)} (or given; 0 allowed), bf16 or an fp8 K/V
     cache (scales 1/64)."""
@@ -353,7 +360,8 @@ def random_prefill_workload(seed: int, batch: int, max_len: int, num_qo_heads: i
     return PrefillWorkload(f"prefill_{seed}", 0, len(lens), num_qo_heads, num_kv_heads, head_dim,
                            page_size, dtype, pool, ip, ix, lp, un, 30_000 + seed,
                            qo_indptr=_qo_indptr(qo_lens), causal=causal,
-                           k_scale=scale, v_scale=scale)
+                           k_scale=scale, v_scale=scale, rope_theta=rope_theta,
+                           rope_scale=rope_scale)
 
 
 def workload(config_id: int) -> Workload:
@@ -381,7 +389,7 @@ def workload(config_id: int) -> Workload:
         return _sparse_prefix(rng, seed)
     if config_id == 13:
         return _composed_prefix(seed)
-    if config_id in (7, 8, 12):
+    if config_id in (7, 8, 12, 14):
         return prefill_workload(config_id)
     if config_id == 9:  # the skewed batch, K stored before the rotary embedding
         w = workload(3)

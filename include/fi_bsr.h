@@ -523,6 +523,11 @@ typedef struct {
                                  most FI_PREFILL_MAX_PAGES pages) */
   int32_t num_xcds;           /* L2 domains the dispatcher deals workgroups
                                  over in turn (default 8, MI355X's XCDs) */
+  int32_t rope;               /* nonzero: a plan for fi_prefill_run_rope --
+                                 tiles of FI_PREFILL_ROWS / 2 rows; needs
+                                 FI_DTYPE_BF16, head_dim 128, G <= 128 and
+                                 every request's queries among its cached
+                                 tokens (n_b <= L_b, masked or not) */
 } fi_prefill_opts;
 
 typedef struct {
@@ -538,11 +543,13 @@ typedef struct {
   int32_t chunk_tokens;       /* longest KV chunk of an item */
   int32_t batch, num_qo_heads, num_kv_heads, head_dim, page_size, causal;
   int32_t dtype;              /* fi_dtype of the K/V pages */
+  int32_t rope;               /* made with fi_prefill_opts.rope */
 } fi_prefill_info;
 
 /*
  * Fields of one prefill work item (fi_prefill_plan_work_list). A tile is
- * FI_PREFILL_ROWS query rows of one request and KV head: row j is query
+ * FI_PREFILL_ROWS query rows (FI_PREFILL_ROWS / 2 in a rope plan) of one
+ * request and KV head: row j is query
  * token j / G of the tile and query head KV_HEAD * G + j % G. An item
  * attends a tile over one chunk of the request's tokens; a tile whose
  * attended range exceeds one chunk is cut into several items whose partial
@@ -560,6 +567,11 @@ enum {
   FI_QITEM_PAGE_BEGIN = 7, /* index into kv_indices of the chunk's first page */
   FI_QITEM_SLOT = 8,       /* -1: the item writes out / lse; else its partial slot */
   FI_QITEM_CHUNK = 9,      /* chunk number within the tile */
+  FI_QITEM_Q_POS = 10,     /* position of the tile's first query token in its
+                              request, L - n + (its index among the request's
+                              queries); negative only for an unmasked request
+                              with more queries than tokens (rope plans refuse
+                              those) */
   FI_QITEM_STRIDE = 12,
   FI_PREFILL_ROWS = 256,      /* query rows per tile */
   FI_PREFILL_MAX_PAGES = 256  /* pages per chunk at most */
@@ -664,6 +676,25 @@ fi_status fi_prefill_run_scaled(const fi_prefill_plan* plan, const void* q, cons
                                 const void* v_pages, float k_scale, float v_scale, void* out,
                                 float* lse, float sm_scale, void* workspace,
                                 size_t workspace_bytes, fi_stream_t stream);
+
+/*
+ * Prefill / append over a K cache that holds keys before the rotary
+ * position embedding (explainer's JIT section: RoPE fused into the attention
+ * kernel), for a plan made with fi_prefill_opts.rope (the other prefill runs
+ * refuse such a plan, and this one any other plan, with FI_ERR_INVALID_ARG).
+ * Rotate-half pairs (dims i and i + 64) turn by (pos / rope_scale) *
+ * rope_theta^(-2i / 128); token t of a request sits at position t and its
+ * query i of n at L - n + i (q arrives before the embedding, as K). The
+ * kernel turns each K block once per tile in LDS and each query row once,
+ * both in fp32 from exact phases, and multiplies them as hi + lo bf16
+ * parts (S = Kh.Qh + Kh.Ql + Kl.Qh). rope_theta <= 0 selects 10000,
+ * rope_scale <= 0 selects 1. Other arguments, ownership and errors as
+ * fi_prefill_run (bf16 q, K, V, out).
+ */
+fi_status fi_prefill_run_rope(const fi_prefill_plan* plan, const void* q, const void* k_pages,
+                              const void* v_pages, float rope_theta, float rope_scale, void* out,
+                              float* lse, float sm_scale, void* workspace,
+                              size_t workspace_bytes, fi_stream_t stream);
 
 /* Free a prefill plan (NULL is ignored); host memory only, no wait. */
 void fi_prefill_plan_destroy(fi_prefill_plan* plan);

@@ -128,6 +128,7 @@ uint64_t prefill_call(const int32_t* hdr, const std::vector<int32_t>& opts, cons
     o.items_per_cu = opts[1];
     o.fixed_chunk_tokens = opts[2];
     o.num_xcds = opts[3];
+    o.rope = opts.size() > 4 ? opts[4] : 0;
     po = &o;
   }
   fi_prefill_plan* p = nullptr;
@@ -165,7 +166,8 @@ int main() {
     for (int32_t& x : opts)
       if (!(std::cin >> x)) return 2;
     const bool prefill = kind == "P", composed = kind == "C";
-    if ((prefill && n_opts != 0 && n_opts != 4) || (!prefill && n_opts != 0 && n_opts != 7))
+    if ((prefill && n_opts != 0 && n_opts != 4 && n_opts != 5) ||
+        (!prefill && n_opts != 0 && n_opts != 7))
       return 2;
     Array qo, ip, ix, lp;
     if (prefill && !read_array(&qo)) return 2;

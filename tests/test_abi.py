@@ -198,6 +198,19 @@ def test_prefill_run_checks_on_the_host():
         assert st == -1 and "scale" in L.fi_last_error().decode(), (ks, vs)
     assert L.fi_prefill_run_scaled(p.handle, fake, fake, fake, 0.5, 2.0, fake, None, 0.0, fake, ws,
                                    None) == -6
+    # rope runs and plans go together
+    assert L.fi_prefill_run_rope(p.handle, fake, fake, fake, 1e4, 1.0, fake, None, 0.0, fake, ws,
+                                 None) == -1
+    assert "fi_prefill_opts.rope" in L.fi_last_error().decode()
+    pr = fb.prefill_plan(np.array([0, 2, 3]), ip, ix, lp, 8, 2, 128, 16, 100, rope=True)
+    wr = pr.info["workspace_bytes"]
+    assert L.fi_prefill_run(pr.handle, fake, fake, fake, fake, None, 0.0, fake, wr, None) == -1
+    assert "fi_prefill_run_rope" in L.fi_last_error().decode()
+    for th, sc in ((0.5, 1.0), (float("inf"), 1.0), (1e4, float("nan"))):
+        assert L.fi_prefill_run_rope(pr.handle, fake, fake, fake, th, sc, fake, None, 0.0, fake, wr,
+                                     None) == -1, (th, sc)
+    assert L.fi_prefill_run_rope(pr.handle, fake, fake, fake, 0.0, 0.0, fake, None, 0.0, fake, wr,
+                                 None) == -6   # defaults accepted; not uploaded
 
 
 def test_binding_refuses_arrays_shorter_than_the_page_table():

@@ -35,7 +35,15 @@ def log(*a):
 def make_plan(w, **kw):
     return fb.prefill_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len,
                            w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
-                           w.num_pool_pages, causal=w.causal, dtype=w.dtype, **kw)
+                           w.num_pool_pages, causal=w.causal, dtype=w.dtype,
+                           rope=bool(w.rope_theta), **kw)
+
+
+def oracle(w, qh, kh, vh, qo, ip, ix, lp):
+    if w.rope_theta:
+        return oa.prefill_attention_rope(qh, kh, vh, qo, ip, ix, lp, w.causal, w.sm_scale,
+                                         w.rope_theta, w.rope_scale)
+    return oa.prefill_attention(qh, kh, vh, qo, ip, ix, lp, w.causal, w.sm_scale)
 
 
 def host_kv(w, k, v):
@@ -48,13 +56,14 @@ def host_kv(w, k, v):
 
 
 def run(w, q, k, v, p, **kw):
-    return fb.prefill(q, k, v, p, k_scale=w.k_scale, v_scale=w.v_scale, **kw)
+    return fb.prefill(q, k, v, p, k_scale=w.k_scale, v_scale=w.v_scale,
+                      rope_theta=w.rope_theta or None, rope_scale=w.rope_scale, **kw)
 
 
 def run_case(w, what, **opts):
     log(f"[case] {what} B={w.batch} N={w.num_qo_tokens} Hq={w.num_qo_heads} "
         f"Hkv={w.num_kv_heads} d={w.head_dim} P={w.page_size} causal={w.causal} "
-        f"kv={w.dtype} opts={opts}")
+        f"kv={w.dtype} rope={w.rope_theta} opts={opts}")
     q, k, v = (t.cuda() for t in w.make_values("cpu"))
     p = make_plan(w, **opts)
     out, lse = run(w, q, k, v, p)
@@ -62,8 +71,7 @@ def run_case(w, what, **opts):
     t0 = time.time()
     qh = q.double().cpu().numpy()
     kh, vh = host_kv(w, k, v)
-    O, LSE = oa.prefill_attention(qh, kh, vh, w.qo_indptr, w.kv_indptr, w.kv_indices,
-                                  w.last_page_len, w.causal, w.sm_scale)
+    O, LSE = oracle(w, qh, kh, vh, w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len)
     stats = compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE, True, what)
     log(f"[ok] {what} items={p.info['num_items']} merges={p.info['num_merges']} "
         f"oracle {time.time() - t0:.1f}s {stats}")
@@ -159,7 +167,53 @@ def test_prefill_is_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("cfg", [7, 8, 12])
+# rotary embedding (q and K before it), bf16, head_dim 128: groups 1 .. 8 and
+# 6, page sizes 1 .. 64, causal and unmasked, direct output and cut tiles,
+# positions past 2^15 (theta and scale varied)
+ROPE_CASES = [
+    # seed, B, maxL, Hq, Hkv, P, causal, max_qo, fixed_chunk, theta, scale
+    (61, 4, 300, 8, 2, 16, True, None, 0, 1e4, 1.0),
+    (62, 3, 700, 32, 8, 16, True, None, 128, 5e5, 1.0),
+    (63, 3, 90, 4, 4, 1, False, None, 7, 1e4, 2.0),
+    (64, 2, 1000, 8, 1, 64, True, 300, 192, 5e5, 1.0),
+    (65, 3, 333, 12, 2, 3, False, 200, 0, 1e6, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES, ids=lambda c: f"seed{c[0]}")
+def test_prefill_rope_small(case):
+    seed, B, L, Hq, Hkv, P, causal, max_qo, fixed, theta, scale = case
+    w = random_prefill_workload(seed, B, L, Hq, Hkv, 128, P, causal=causal, max_qo=max_qo,
+                                rope_theta=theta, rope_scale=scale)
+    p, _, _ = run_case(w, f"rope prefill seed{seed}", fixed_chunk_tokens=fixed)
+    assert p.info["rope"] == 1 and p.info["tokens_per_tile"] == 128 // (Hq // Hkv)
+    if fixed:
+        assert p.info["num_merges"] > 0
+
+
+def test_prefill_rope_whole_prompts_and_long_positions():
+    """Whole prompts across tile and block edges, and a request of 40,000
+    tokens whose last 70 are queries (positions past 2^15, a chunk cut)."""
+    lens = [1, 31, 32, 33, 63, 64, 65, 129, 257]
+    w = random_prefill_workload(66, len(lens), 200, 16, 4, 128, 16, causal=True, lens=lens,
+                                qo_lens=lens, rope_theta=5e5)
+    run_case(w, "rope whole prompts")
+    w = random_prefill_workload(67, 1, 40000, 8, 2, 128, 16, causal=True, lens=[40000],
+                                qo_lens=[70], rope_theta=5e5)
+    run_case(w, "rope long positions")
+
+
+def test_prefill_rope_is_deterministic():
+    w = random_prefill_workload(68, 3, 600, 8, 2, 128, 16, causal=True, rope_theta=1e4)
+    q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    p = make_plan(w, fixed_chunk_tokens=64)
+    a = run(w, q, k, v, p)
+    b = run(w, q, k, v, p)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("cfg", [7, 8, 12, 14])
 def test_prefill_full_size(cfg):
     """Every (query row, head) of the full-size workload, in the launch
     configuration bench.py times, against the oracle evaluated one request
@@ -184,7 +238,7 @@ def test_prefill_full_size(cfg):
         q0, q1, qo, ip, ix, lp = prefill_request(w, b)
         if q1 == q0:
             continue
-        O, LSE = oa.prefill_attention(qh[q0:q1], kh, vh, qo, ip, ix, lp, w.causal, w.sm_scale)
+        O, LSE = oracle(w, qh[q0:q1], kh, vh, qo, ip, ix, lp)
         st = compare(out_h[q0:q1], lse_h[q0:q1], O, LSE, True, f"prefill config {cfg} request {b}")
         for key in ("max_abs_vs_rounded", "lse_max_abs"):
             worst[key] = max(worst[key], st.get(key, 0.0))

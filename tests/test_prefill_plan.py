@@ -236,6 +236,57 @@ def test_prefill_plan_rejects(kw, code, needle):
     assert st == code and needle in msg, (st, msg)
 
 
+def test_rope_plan_has_half_height_tiles_and_query_positions():
+    """A rope plan cuts each request's queries into tiles of 128 / G tokens
+    and records the position of each tile's first query, L - n + index."""
+    from block_sparse_kv_bsr_amd.workloads import random_prefill_workload
+    w = random_prefill_workload(5, 4, 700, 16, 4, 128, 16, causal=True)
+    a = fb.prefill_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, 16, 4, 128, 16,
+                        w.num_pool_pages)
+    b = fb.prefill_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, 16, 4, 128, 16,
+                        w.num_pool_pages, rope=True)
+    assert a.info["rope"] == 0 and b.info["rope"] == 1
+    assert a.info["tokens_per_tile"] == 64 and b.info["tokens_per_tile"] == 32
+    L, n = w.kv_lens(), np.diff(w.qo_indptr)
+    for p in (a, b):
+        T = p.info["tokens_per_tile"]
+        for r in p.work_list():
+            req = int(r[0])
+            first = int(r[2]) - int(w.qo_indptr[req])   # tile's first query index
+            assert first % T == 0 and r[3] <= T
+            assert r[10] == L[req] - n[req] + first
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(dtype=2), -2, "rotary"),
+    (dict(d=64), -2, "rotary"),
+    (dict(Hq=256, Hkv=1), -2, "G <="),
+])
+def test_rope_plan_rejects(kw, code, needle):
+    import ctypes
+    L = fb.lib()
+    a = dict(Hq=8, Hkv=2, d=128, dtype=1)
+    a.update(kw)
+    arrs = [np.asarray(x, dtype=np.int32) for x in ([0, 2, 3], [0, 2, 3], [5, 6, 7], [16, 3])]
+    p32 = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    opts = binding.PrefillOpts(0, 0, 0, 0, 1)
+    h = ctypes.c_void_p()
+    st = L.fi_prefill_plan_create(p32(arrs[0]), p32(arrs[1]), p32(arrs[2]), p32(arrs[3]), 2,
+                                  a["Hq"], a["Hkv"], a["d"], 16, 100, a["dtype"], 1,
+                                  ctypes.byref(opts), ctypes.byref(h))
+    assert st == code and needle in L.fi_last_error().decode(), (st, L.fi_last_error())
+
+
+def test_rope_plan_needs_cached_queries_also_unmasked():
+    """Rotated queries are cached tokens: an unmasked request with more
+    queries than tokens is refused for a rope plan (allowed without)."""
+    ip, ix, lp = np.array([0, 1]), np.array([3]), np.array([5])
+    qo = np.array([0, 7])
+    fb.prefill_plan(qo, ip, ix, lp, 8, 2, 128, 16, 10, causal=False)
+    with pytest.raises(fb.FiError, match="more query tokens"):
+        fb.prefill_plan(qo, ip, ix, lp, 8, 2, 128, 16, 10, causal=False, rope=True)
+
+
 def test_fp8_plan_is_the_bf16_plan_with_its_dtype():
     """The cache's element type changes no scheduling: same items and merges,
     and get_info reports the dtype."""
