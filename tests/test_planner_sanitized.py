@@ -99,7 +99,9 @@ def malformed_calls():
         out.append(Call("D", batch, a["hq"], a["hkv"], a["d"], a["P"], a["pool"], a["dtype"],
                         ip, ix, lp, a["opts"]))
     out.append(Call("D", -1, 8, 2, 128, 16, 100, 1, [0], [], []))
-    pre = [dict(qo=[1, 2, 3]), dict(qo=[0, 3, 2]), dict(qo=[0, 40, 41]), dict(dtype=0),
+    pre = [dict(opts=[0, 0, 0, 0, 1], dtype=2), dict(opts=[0, 0, 0, 0, 1], d=64),
+           dict(opts=[0, 0, 0, 0, 1], causal=0, qo=[0, 2, 40]),
+           dict(qo=[1, 2, 3]), dict(qo=[0, 3, 2]), dict(qo=[0, 40, 41]), dict(dtype=0),
            dict(d=96), dict(hq=8, hkv=3), dict(hq=512, hkv=1), dict(ix=[5, 6, 700]),
            dict(hq=257, hkv=1), dict(qo=None), dict(lp=[16, 0]),
            dict(opts=[-1, 0, 0, 0]), dict(opts=[0, 0, -3, 0])]
@@ -191,8 +193,11 @@ def random_calls(seed=7, n_decode=160, n_prefill=100):
             opts = [int(rng.choice([0, 8, 256])), int(rng.choice([0, 1, 4])),
                     int(rng.choice([0, 0, 16, 64, 512])), int(rng.choice([0, 1, 3, 8]))]
         qoi = np.concatenate([[0], np.cumsum(qo)]).tolist()
-        out.append(Call("P", B, G * hkv, hkv, int(rng.choice([64, 128])), P, pool, 1, ip, ix, lp,
-                        opts, qoi, causal))
+        d = int(rng.choice([64, 128]))
+        # rope plans: bf16, d 128, every request's queries cached
+        if d == 128 and all(n <= L for n, L in zip(qo, lens)) and rng.random() < 0.4:
+            opts = (opts or [0, 0, 0, 0]) + [1]
+        out.append(Call("P", B, G * hkv, hkv, d, P, pool, 1, ip, ix, lp, opts, qoi, causal))
     for i in range(60):
         B = int(rng.integers(1, 10))
         P = int(rng.choice(sizes))
