@@ -573,6 +573,8 @@ def main():
     kp_vp = vals[3:] if composed else None
     opts = dict(items_per_cu=args.items_per_cu, min_chunk_tokens=args.min_chunk_tokens,
                 fixed_chunk_tokens=args.fixed_chunk_tokens, decode_kernel=args.decode_kernel)
+    if not composed:
+        opts["rope"] = bool(w.rope_theta)
 
     # host planner time (median of 20) and upload time
     plan_t = []

@@ -55,7 +55,7 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [("num_cus", ctypes.c_int32), ("items_per_cu", ctypes.c_int32),
                 ("min_chunk_tokens", ctypes.c_int32), ("max_chunk_tokens", ctypes.c_int32),
                 ("fixed_chunk_tokens", ctypes.c_int32), ("cascade", ctypes.c_int32),
-                ("decode_kernel", ctypes.c_int32)]
+                ("decode_kernel", ctypes.c_int32), ("rope", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -285,13 +285,14 @@ def plan(kv_indptr, kv_indices, kv_last_page_len, num_qo_heads: int, num_kv_head
          head_dim: int, page_size: int, num_pool_pages: int, dtype="bf16",
          num_cus: int = 0, items_per_cu: int = 0, min_chunk_tokens: int = 0,
          max_chunk_tokens: int = 0, fixed_chunk_tokens: int = 0, cascade: int = 0,
-         decode_kernel: int = 0) -> Plan:
+         decode_kernel: int = 0, rope: bool = False) -> Plan:
     """fi_plan_create over host page-table arrays (numpy or CPU tensors).
-    decode_kernel: DECODE_KERNEL_AUTO (0), _VECTOR (1) or _MATRIX (2)."""
+    decode_kernel: DECODE_KERNEL_AUTO (0), _VECTOR (1) or _MATRIX (2); rope:
+    the plan's runs apply the rotary embedding (sizes the items only)."""
     ip, ix, lp = _i32(kv_indptr), _i32(kv_indices), _i32(kv_last_page_len)
     batch = _check_lengths(ip, ix, lp)
     opts = PlanOpts(num_cus, items_per_cu, min_chunk_tokens, max_chunk_tokens, fixed_chunk_tokens,
-                    cascade, decode_kernel)
+                    cascade, decode_kernel, int(bool(rope)))
     h = ctypes.c_void_p()
     ix_ptr = _ptr32(ix) if ix.size else ctypes.POINTER(ctypes.c_int32)()
     _check(lib().fi_plan_create(_ptr32(ip), ix_ptr, _ptr32(lp), batch, num_qo_heads,

@@ -236,8 +236,21 @@ fi_status create_plan(const int32_t* kv_indptr, const int32_t* kv_indices,
       return fail(FI_ERR_UNSUPPORTED,
                   "the matrix-core decode kernel needs head_dim 128, bf16 or fp8 K/V and a page "
                   "size that is a multiple of 16");
+    // The matrix-core kernel was measured faster for fp8 caches and for eight
+    // query heads per KV head (both bound by vector work in the other kernel).
+    const bool mma_fits = head_dim == 128 && dtype != FI_DTYPE_F32 && page_size % 16 == 0;
+    const bool mma =
+        o.decode_kernel == FI_DECODE_KERNEL_MATRIX ||
+        (o.decode_kernel == FI_DECODE_KERNEL_AUTO && mma_fits &&
+         (dtype == FI_DTYPE_FP8_E4M3 || num_qo_heads == 8 * num_kv_heads));
     const int64_t num_cus = o.num_cus ? o.num_cus : 256;
-    const int64_t items_per_cu = o.items_per_cu ? o.items_per_cu : 8;
+    // Items per CU: 8 keeps every item resident from the start (two waves per
+    // SIMD) and was measured best for the vector kernel; the matrix kernel
+    // without the rotary embedding moves more per item for the same fixed
+    // costs and measured faster with 6 (fp8 skewed batch 91.0 against 93.7
+    // us, 64 / 8 heads 168.6 against 171.5); with the embedding it is bound
+    // by vector work and needs the 8 (135.5 against 170.5 us).
+    const int64_t items_per_cu = o.items_per_cu ? o.items_per_cu : (mma && !o.rope ? 6 : 8);
     const int64_t min_chunk_tokens = o.min_chunk_tokens ? o.min_chunk_tokens : 256;
 
     // ---- shared-prefix groups: requests (of two pages or more) whose lists
@@ -378,15 +391,7 @@ fi_status create_plan(const int32_t* kv_indptr, const int32_t* kv_indices,
     std::unique_ptr<fi_plan> p(new fi_plan());
     p->decode_kernel = o.decode_kernel;
     p->merge_fan_in = (int32_t)fan_in;
-    // The matrix-core kernel was measured faster for fp8 caches and for eight
-    // query heads per KV head (both bound by vector work in the other kernel).
-    const bool mma_fits = head_dim == 128 && dtype != FI_DTYPE_F32 && page_size % 16 == 0;
-    p->resolved_kernel =
-        o.decode_kernel == FI_DECODE_KERNEL_MATRIX ||
-                (o.decode_kernel == FI_DECODE_KERNEL_AUTO && mma_fits &&
-                 (dtype == FI_DTYPE_FP8_E4M3 || num_qo_heads == 8 * num_kv_heads))
-            ? FI_DECODE_KERNEL_MATRIX
-            : FI_DECODE_KERNEL_VECTOR;
+    p->resolved_kernel = mma ? FI_DECODE_KERNEL_MATRIX : FI_DECODE_KERNEL_VECTOR;
     p->batch = batch;
     p->num_qo_heads = num_qo_heads;
     p->num_kv_heads = num_kv_heads;

@@ -108,7 +108,10 @@ typedef struct fi_plan fi_plan; /* opaque, host-owned */
 /* Planner knobs. Zero selects the default for every field. */
 typedef struct {
   int32_t num_cus;            /* compute units to balance over (default 256) */
-  int32_t items_per_cu;       /* target work items per CU (default 8) */
+  int32_t items_per_cu;       /* target work items per CU (default 8; 6 for a
+                                 plan that runs the matrix-core kernel
+                                 without the rotary embedding, which
+                                 measured faster with fewer, longer items) */
   int32_t min_chunk_tokens;   /* never cut a request finer than this (default 256) */
   int32_t max_chunk_tokens;   /* cap on chunk length; 0 = no cap */
   int32_t fixed_chunk_tokens; /* >0: use exactly this chunk length (rounded up
@@ -118,6 +121,10 @@ typedef struct {
                                  share a prefix, -1 = never */
   int32_t decode_kernel;      /* FI_DECODE_KERNEL_*: which decode kernel the
                                  plan's runs launch */
+  int32_t rope;               /* nonzero: the plan's runs apply the rotary
+                                 embedding (fi_decode_run_rope*); only sizes
+                                 the items (see items_per_cu) -- every run
+                                 entry point stays correct with any plan */
 } fi_plan_opts;
 
 /* Decode kernels. Both compute the same attention and merge trees, to the

@@ -84,6 +84,7 @@ uint64_t decode_call(const int32_t* hdr, const std::vector<int32_t>& opts, const
     o.fixed_chunk_tokens = opts[4];
     o.cascade = opts[5];
     o.decode_kernel = opts[6];
+    o.rope = opts.size() > 7 ? opts[7] : 0;
     po = &o;
   }
   fi_plan* p = nullptr;
@@ -167,7 +168,7 @@ int main() {
       if (!(std::cin >> x)) return 2;
     const bool prefill = kind == "P", composed = kind == "C";
     if ((prefill && n_opts != 0 && n_opts != 4 && n_opts != 5) ||
-        (!prefill && n_opts != 0 && n_opts != 7))
+        (!prefill && n_opts != 0 && n_opts != 7 && n_opts != 8))
       return 2;
     Array qo, ip, ix, lp;
     if (prefill && !read_array(&qo)) return 2;
