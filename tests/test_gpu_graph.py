@@ -7,7 +7,8 @@ import pytest
 import torch
 
 import block_sparse_kv_bsr_amd as fb
-from block_sparse_kv_bsr_amd.workloads import prefix_workload, random_prefill_workload, random_workload
+from block_sparse_kv_bsr_amd.workloads import (prefix_workload, random_composed_workload,
+                                               random_prefill_workload, random_workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -115,3 +116,48 @@ def test_graph_prefill_with_cut_tiles():
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
     _replays(lambda: fb.prefill(q, k, v, p, out=out, lse=lse, workspace=ws), [q], [out, lse],
              [torch.randn_like(q)], "prefill")
+
+
+def test_graph_decode_composed():
+    """Composed formats: the prefix cache's blocks (256 tokens) and the
+    requests' own pages in one captured run, requests cut into chunks."""
+    w = random_composed_workload(105, [3000], [9], 2, 400, 32, 8, 128, 16, 256)
+    q, k, v, kp, vp = (t.cuda() for t in w.make_values("cpu"))
+    p = fb.plan_composed(w.kv_indptr, w.kv_indices, w.last_page_len, w.prefix_indptr,
+                         w.prefix_indices, w.prefix_last_page_len, w.prefix_of, w.num_qo_heads,
+                         w.num_kv_heads, w.head_dim, w.page_size, w.num_pool_pages,
+                         w.prefix_page_size, w.num_prefix_pool_pages)
+    assert p.info["num_prefix_items"] > 0 and p.info["num_merge_nodes"] > 0
+    ws = torch.empty(p.info["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    p.upload(ws)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    _replays(lambda: fb.decode_composed(q, k, v, kp, vp, p, out=out, lse=lse, workspace=ws), [q],
+             [out, lse], [torch.randn_like(q)], "decode composed")
+
+
+def _prefill_graph(w, what):
+    q, k, v = (t.cuda() for t in w.make_values("cpu"))
+    p = fb.prefill_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, w.num_qo_heads,
+                        w.num_kv_heads, w.head_dim, w.page_size, w.num_pool_pages,
+                        causal=w.causal, dtype=w.dtype, rope=bool(w.rope_theta),
+                        fixed_chunk_tokens=128)
+    assert p.info["num_merges"] > 0
+    ws = torch.empty(p.info["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    p.upload(ws)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    _replays(lambda: fb.prefill(q, k, v, p, out=out, lse=lse, workspace=ws, k_scale=w.k_scale,
+                                v_scale=w.v_scale, rope_theta=w.rope_theta or None,
+                                rope_scale=w.rope_scale), [q], [out, lse],
+             [torch.randn_like(q)], what)
+
+
+def test_graph_prefill_fp8_cache():
+    _prefill_graph(random_prefill_workload(106, 3, 900, 8, 2, 128, 16, causal=True, dtype="fp8"),
+                   "prefill fp8")
+
+
+def test_graph_prefill_rope():
+    _prefill_graph(random_prefill_workload(107, 3, 900, 8, 2, 128, 16, causal=True,
+                                           rope_theta=5e5), "prefill rope")
