@@ -61,6 +61,9 @@ CONFIG_NAMES = {
     13: "sparse_prefix_b32_p64_composed_b4096",
     # the append batch over a K cache that holds keys before the rotary embedding
     14: "append_b64_q128_skewed_rope",
+    # multi-head latent attention decode: the skewed batch's histories as a
+    # paged latent cache (512 + 64 per token, 64-token pages), 96 heads
+    15: "mla_skewed_b64_loguniform_32_32768_h96",
 }
 
 # Rotary embedding base of the rope workload (the Llama-3 value).
@@ -647,3 +650,135 @@ def _composed_prefix(seed) -> ComposedWorkload:
                             1_000_003 * 13 + 1, prefix_page_size=Pp, num_prefix_pool_pages=ppool,
                             prefix_indptr=pip, prefix_indices=pix, prefix_last_page_len=plp,
                             prefix_of=np.zeros(w5.batch, dtype=np.int32), prefix_unused_pages=pun)
+
+
+# ----------------------------------------------------------- latent attention
+# Latent width and rotary-key width of the MLA cache (DeepSeek-V2/V3 and
+# Kimi K3 geometry), and the pre-absorption query/key head width (128 without
+# rotary, 64 with) that sets the softmax scale.
+MLA_DC = 512
+MLA_DR = 64
+MLA_QK_DIM = 192
+
+
+@dataclasses.dataclass
+class MLAWorkload:
+    """Multi-head latent attention over a paged latent cache. Request b holds
+    the tokens of its listed pages (kv_indptr / kv_indices / last_page_len,
+    as for Workload); its query tokens are rows qo_indptr[b] ..
+    qo_indptr[b+1]-1 of q_nope [N, H, 512] and q_pe [N, H, 64], its newest
+    cached tokens (causal). The pools are ckv [pages, P, 512] and kpe
+    [pages, P, 64]."""
+    name: str
+    config_id: int
+    batch: int
+    num_heads: int
+    page_size: int
+    num_pool_pages: int
+    kv_indptr: np.ndarray
+    kv_indices: np.ndarray
+    last_page_len: np.ndarray
+    unused_pages: np.ndarray
+    value_seed: int
+    qo_indptr: np.ndarray
+    causal: bool = True
+    dtype: str = "bf16"
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(MLA_QK_DIM)
+
+    @property
+    def num_qo_tokens(self) -> int:
+        return int(self.qo_indptr[-1])
+
+    def qo_lens(self) -> np.ndarray:
+        return np.diff(self.qo_indptr).astype(np.int64)
+
+    def kv_len(self, b: int) -> int:
+        n = int(self.kv_indptr[b + 1] - self.kv_indptr[b])
+        return 0 if n == 0 else (n - 1) * self.page_size + int(self.last_page_len[b])
+
+    def kv_lens(self) -> np.ndarray:
+        return np.array([self.kv_len(b) for b in range(self.batch)], dtype=np.int64)
+
+    def visible_pairs(self) -> int:
+        tot = 0
+        for L, n in zip(self.kv_lens(), self.qo_lens()):
+            L, n = int(L), int(n)
+            tot += sum(max(0, L - n + i + 1) for i in range(n)) if self.causal else L * n
+        return tot
+
+    def flops(self) -> int:
+        """Per (query head, visible token): d_c + d_r multiply-adds for the
+        score and d_c for the weighted latent sum."""
+        return 2 * (2 * MLA_DC + MLA_DR) * self.num_heads * self.visible_pairs()
+
+    def algorithmic_bytes(self) -> int:
+        """Every cached latent and rotary key once, plus q read and the output
+        written (bf16)."""
+        tok = int(self.kv_lens().sum())
+        q = self.num_qo_tokens * self.num_heads * (MLA_DC + MLA_DR) * 2
+        out = self.num_qo_tokens * self.num_heads * MLA_DC * 2
+        return tok * (MLA_DC + MLA_DR) * 2 + q + out
+
+    def make_values(self, device="cpu"):
+        """(q_nope, q_pe, ckv_pool, kpe_pool): drawn in that order, N(0, 1)
+        float32 cast to bf16; unlisted pages and the slots past each last
+        page's length hold NaN."""
+        import torch
+
+        g = torch.Generator(device=device)
+        g.manual_seed(self.value_seed)
+        N, H, P = self.num_qo_tokens, self.num_heads, self.page_size
+
+        def draw(shape):
+            return torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+
+        q_nope = draw((N, H, MLA_DC)).to(torch.bfloat16)
+        q_pe = draw((N, H, MLA_DR)).to(torch.bfloat16)
+        pools = []
+        for d in (MLA_DC, MLA_DR):
+            x = draw((self.num_pool_pages, P, d))
+            if len(self.unused_pages):
+                idx = torch.as_tensor(self.unused_pages.astype(np.int64), device=device)
+                x.index_fill_(0, idx, float("nan"))
+            for b in range(self.batch):
+                first, stop = int(self.kv_indptr[b]), int(self.kv_indptr[b + 1])
+                ell = int(self.last_page_len[b])
+                if stop > first and ell < P:
+                    x[int(self.kv_indices[stop - 1]), ell:, :] = float("nan")
+            pools.append(x.to(torch.bfloat16))
+        return q_nope, q_pe, pools[0], pools[1]
+
+
+def mla_workload(config_id: int) -> MLAWorkload:
+    """15: the skewed batch's 64 history lengths (log-uniform in [32, 32768],
+    the same draws as config 3) as a latent cache in 64-token pages, one
+    query token per request, 96 heads (Kimi K3's global query heads)."""
+    if config_id != 15:
+        raise ValueError(f"unknown MLA config {config_id}")
+    rng = np.random.default_rng([config_id, 0])
+    lens = [int(x) for x in workload(3).kv_lens()]
+    P = 64
+    pool = sum((L + P - 1) // P for L in lens) + 64
+    ip, ix, lp, un = paged_structure(lens, P, pool, rng)
+    return MLAWorkload(CONFIG_NAMES[15], 15, len(lens), 96, P, pool, ip, ix, lp, un,
+                       1_000_003 * config_id + 1, qo_indptr=_qo_indptr([1] * len(lens)))
+
+
+def random_mla_workload(seed: int, batch: int, max_len: int, num_heads: int, page_size: int,
+                        max_qo: int = 1, lens: Optional[List[int]] = None,
+                        qo_lens: Optional[List[int]] = None, causal: bool = True,
+                        spare_pages: int = 3) -> MLAWorkload:
+    """Small ragged MLA case: history lengths U{1..max_len} (or given; 0
+    allowed), query tokens U{1..min(L_b, max_qo)} per request (or given)."""
+    rng = np.random.default_rng([seed, 19])
+    if lens is None:
+        lens = [int(x) for x in rng.integers(1, max_len + 1, size=batch)]
+    if qo_lens is None:
+        qo_lens = [int(rng.integers(1, max(1, min(L, max_qo)) + 1)) if L > 0 else 0 for L in lens]
+    npg = sum((L + page_size - 1) // page_size for L in lens)
+    ip, ix, lp, un = paged_structure(lens, page_size, npg + spare_pages, rng)
+    return MLAWorkload(f"mla_{seed}", 0, len(lens), num_heads, page_size, npg + spare_pages, ip,
+                       ix, lp, un, 40_000 + seed, qo_indptr=_qo_indptr(qo_lens), causal=causal)

@@ -56,6 +56,26 @@ What it computes, and where that comes from:
   n = 1 is the decode step above. Without the causal mask every query sees
   all L tokens. With the rotary embedding the queries keep those
   positions: query i sits at L - n + i (so n <= L is required).
+* FlashInfer 0.6.17 release write-up, section 2 on Blackwell / Kimi K3 MLA
+  support: multi-head latent attention (MLA, from DeepSeek-V2) caches one
+  compressed latent vector per token in place of per-head K and V; attention
+  needs the up-projection that turns latents into K and V, and writing the
+  restored K/V to shared memory first was the bottleneck the new kernel
+  removes by packing query-token rows and query-head rows into one tile; head
+  counts need not be powers of two and a request may carry several
+  (speculative) query tokens. Reading: the up-projections are folded into
+  the query and the output (the absorbed form), so the method attends in the
+  latent space. Token t of a request caches a latent c_t (d_c = 512) and a
+  rotary key k_t (d_r = 64, stored after its rotation); query token i, head h
+  brings q_nope (its no-rotary part already multiplied by that head's key
+  up-projection, d_c) and q_pe (its rotary part, already rotated, d_r). The
+  score of token t is sm_scale (q_nope . c_t + q_pe . k_t), the output is
+  the softmax-weighted sum of the latents c_t (the caller applies the value
+  up-projection), and every head reads the same cache: multi-query
+  attention with key [c_t, k_t] and value c_t. The query tokens of a request
+  are its newest cached tokens with the causal mask, as for prefill. The
+  scale is the model's (1 / sqrt(d_nope + d_r) before absorption, not the
+  latent width), so the caller passes it.
 
 Everything is float64. The exact result of the method is plain softmax
 attention over the listed tokens, so the oracle is that definition, written
@@ -332,6 +352,54 @@ def prefill_attention_rope(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, 
                 o, lse = attend(qr, K[:c], V[:c], sm_scale)
                 O[q0 + i, heads, :] = o
                 LSE[q0 + i, heads] = lse
+    return O, LSE
+
+
+def gather_latent(ckv_pool, kpe_pool, tokens):
+    """Dense [T, d_c] latents and [T, d_r] rotary keys of one request, in
+    token order."""
+    if not tokens:
+        return np.zeros((0, ckv_pool.shape[-1])), np.zeros((0, kpe_pool.shape[-1]))
+    pages = np.array([p for p, _ in tokens])
+    slots = np.array([s for _, s in tokens])
+    return (np.asarray(ckv_pool[pages, slots, :], dtype=np.float64),
+            np.asarray(kpe_pool[pages, slots, :], dtype=np.float64))
+
+
+def mla_attention(q_nope, q_pe, ckv_pool, kpe_pool, qo_indptr, kv_indptr, kv_indices,
+                  last_page_len, sm_scale, causal=True):
+    """Multi-head latent attention in the latent space over a paged cache.
+
+    q_nope [N, H, d_c], q_pe [N, H, d_r]: request b's query tokens are rows
+    qo_indptr[b] .. qo_indptr[b+1]-1. ckv_pool [pages, P, d_c] and kpe_pool
+    [pages, P, d_r] share the page table (kv_indptr, kv_indices,
+    last_page_len, as for decode_attention). Query token i of request b
+    attends the first visible_tokens(L_b, n_b, i, causal) tokens with score
+    sm_scale (q_nope . c_t + q_pe . k_t). Returns float64 O [N, H, d_c] (the
+    weighted sum of latents) and LSE [N, H] (natural log); a query that sees
+    no token gets O = 0 and LSE = -inf.
+    """
+    q_nope = np.asarray(q_nope, dtype=np.float64)
+    q_pe = np.asarray(q_pe, dtype=np.float64)
+    N, H, dc = q_nope.shape
+    P = ckv_pool.shape[1]
+    O = np.zeros((N, H, dc))
+    LSE = np.full((N, H), NEG_INF)
+    for b in range(len(qo_indptr) - 1):
+        q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
+        n = q1 - q0
+        if n == 0:
+            continue
+        toks = request_tokens(kv_indptr, kv_indices, last_page_len, P, b)
+        L = len(toks)
+        C, R = gather_latent(ckv_pool, kpe_pool, toks)
+        K = np.concatenate([C, R], axis=1)  # the key every head reads
+        for i in range(n):
+            c = visible_tokens(L, n, i, causal)
+            rows = np.concatenate([q_nope[q0 + i], q_pe[q0 + i]], axis=1)  # [H, d_c + d_r]
+            o, lse = attend(rows, K[:c], C[:c], sm_scale)
+            O[q0 + i] = o
+            LSE[q0 + i] = lse
     return O, LSE
 
 

@@ -91,3 +91,44 @@ def rope_rows_loops(rows, positions, theta, scale):
             y[i + h] = float(x[i + h]) * c + float(x[i]) * s
         out.append(y)
     return out
+
+
+def bruteforce_mla(q_nope, q_pe, ckv_pool, kpe_pool, qo_indptr, indptr, indices, last, sm_scale,
+                   causal):
+    """Latent attention written out with plain loops: every head scores a
+    token as sm_scale (q_nope . latent + q_pe . rotary key) and averages the
+    latents; query i of n over L tokens sits at position L - n + i."""
+    N, H, dc = q_nope.shape
+    dr = q_pe.shape[2]
+    P = ckv_pool.shape[1]
+    O = [[[0.0] * dc for _ in range(H)] for _ in range(N)]
+    LSE = [[-math.inf] * H for _ in range(N)]
+    for b in range(len(qo_indptr) - 1):
+        toks = []
+        first, stop = int(indptr[b]), int(indptr[b + 1])
+        for j in range(first, stop):
+            count = P if j + 1 < stop else int(last[b])
+            toks.extend((int(indices[j]), slot) for slot in range(count))
+        n = int(qo_indptr[b + 1]) - int(qo_indptr[b])
+        for i in range(n):
+            row = int(qo_indptr[b]) + i
+            pos = len(toks) - n + i
+            seen = [t for k, t in enumerate(toks) if (k <= pos or not causal)]
+            for h in range(H):
+                if not seen:
+                    continue
+                scores = []
+                for (p, s) in seen:
+                    dot = math.fsum([float(q_nope[row, h, c]) * float(ckv_pool[p, s, c])
+                                     for c in range(dc)] +
+                                    [float(q_pe[row, h, c]) * float(kpe_pool[p, s, c])
+                                     for c in range(dr)])
+                    scores.append(sm_scale * dot)
+                top = max(scores)
+                ws = [math.exp(x - top) for x in scores]
+                den = math.fsum(ws)
+                for c in range(dc):
+                    O[row][h][c] = math.fsum(w * float(ckv_pool[p, s, c])
+                                             for w, (p, s) in zip(ws, seen)) / den
+                LSE[row][h] = top + math.log(den)
+    return O, LSE

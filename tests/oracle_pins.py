@@ -14,9 +14,9 @@ import math
 import numpy as np
 import torch
 
-from block_sparse_kv_bsr_amd.workloads import (random_composed_workload, random_prefill_workload,
-                                               random_workload)
-from tests.bruteforce import bruteforce_decode, bruteforce_prefill, rope_rows_loops
+from block_sparse_kv_bsr_amd.workloads import (random_composed_workload, random_mla_workload,
+                                               random_prefill_workload, random_workload)
+from tests.bruteforce import bruteforce_decode, bruteforce_mla, bruteforce_prefill, rope_rows_loops
 
 
 def f64_inputs(w):
@@ -565,3 +565,142 @@ def pin_composed_prefix_counts(mod):
 
 
 COMPOSED_PINS = [pin_composed_is_one_cache, pin_composed_bruteforce, pin_composed_prefix_counts]
+
+
+
+# ------------------------------------------------------ latent attention (MLA)
+MLA_TINY = [
+    # seed, batch, max_len, heads, page size, max query tokens, d_c, d_r, causal
+    (71, 3, 23, 3, 4, 3, 8, 4, True),
+    (72, 4, 19, 2, 16, 1, 6, 2, True),
+    (73, 2, 17, 5, 1, 4, 4, 4, False),
+    (74, 3, 30, 1, 8, 5, 8, 2, True),
+]
+
+
+def _mla_values(w, dc, dr, seed):
+    """float64 q_nope, q_pe, latent pool, rotary-key pool of small widths
+    for the structure of ``w`` (unlisted slots hold NaN)."""
+    rng = np.random.default_rng([seed, 5])
+    N, H, P = w.num_qo_tokens, w.num_heads, w.page_size
+    qn, qp = rng.standard_normal((N, H, dc)), rng.standard_normal((N, H, dr))
+    ckv = np.full((w.num_pool_pages, P, dc), np.nan)
+    kpe = np.full((w.num_pool_pages, P, dr), np.nan)
+    for b in range(w.batch):
+        first, stop = int(w.kv_indptr[b]), int(w.kv_indptr[b + 1])
+        for j in range(first, stop):
+            n = P if j + 1 < stop else int(w.last_page_len[b])
+            pg = int(w.kv_indices[j])
+            ckv[pg, :n] = rng.standard_normal((n, dc))
+            kpe[pg, :n] = rng.standard_normal((n, dr))
+    return qn, qp, ckv, kpe
+
+
+def _mla(mod, w, qn, qp, ckv, kpe, sm_scale=0.3, qo_indptr=None, causal=None):
+    return mod.mla_attention(qn, qp, ckv, kpe, w.qo_indptr if qo_indptr is None else qo_indptr,
+                             w.kv_indptr, w.kv_indices, w.last_page_len, sm_scale,
+                             w.causal if causal is None else causal)
+
+
+def _mla_dense(w, ckv, kpe, b):
+    """Dense [L, d_c] latents and [L, d_r] rotary keys of request b, straight
+    from the page table."""
+    P = w.page_size
+    first, stop = int(w.kv_indptr[b]), int(w.kv_indptr[b + 1])
+    rows = [(int(w.kv_indices[j]), s) for j in range(first, stop)
+            for s in range(P if j + 1 < stop else int(w.last_page_len[b]))]
+    if not rows:
+        return np.zeros((0, ckv.shape[-1])), np.zeros((0, kpe.shape[-1]))
+    return (np.stack([ckv[p, s] for p, s in rows]), np.stack([kpe[p, s] for p, s in rows]))
+
+
+def pin_mla_bruteforce(mod, tol=1e-12):
+    for (seed, B, L, H, P, mq, dc, dr, causal) in MLA_TINY:
+        w = random_mla_workload(seed, B, L, H, P, max_qo=mq, causal=causal)
+        qn, qp, ckv, kpe = _mla_values(w, dc, dr, seed)
+        O, LSE = _mla(mod, w, qn, qp, ckv, kpe)
+        Ob, LSEb = bruteforce_mla(qn, qp, ckv, kpe, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                  w.last_page_len, 0.3, causal)
+        assert np.max(np.abs(O - np.array(Ob))) <= tol, seed
+        assert np.max(np.abs(LSE - np.array(LSEb))) <= tol, seed
+
+
+def pin_mla_explicit_heads(mod):
+    """The latent form against per-head attention over up-projected K and V
+    (torch's float64 scaled_dot_product_attention): head h has key
+    up-projection W_k[h] [d_c, d_n] and value up-projection W_v[h] [d_c, d_v];
+    its key of token t is [c_t W_k[h], k_t], its value c_t W_v[h], its query
+    [q_n, q_pe]. The latent form takes q_nope = W_k[h] q_n, and its output
+    times W_v[h] must equal the per-head output."""
+    F = torch.nn.functional
+    dc, dr, dn, dv, H = 12, 4, 6, 5, 3
+    w = random_mla_workload(75, 3, 29, H, 4, max_qo=4, lens=[29, 11, 6], qo_lens=[4, 2, 6])
+    rng = np.random.default_rng([75, 6])
+    _, qp, ckv, kpe = _mla_values(w, dc, dr, 75)
+    Wk, Wv = rng.standard_normal((H, dc, dn)), rng.standard_normal((H, dc, dv))
+    qn_heads = rng.standard_normal((w.num_qo_tokens, H, dn))
+    qn = np.einsum("hcn,thn->thc", Wk, qn_heads)
+    scale = 1.0 / math.sqrt(dn + dr)
+    O, _ = _mla(mod, w, qn, qp, ckv, kpe, sm_scale=scale)
+    for b in range(w.batch):
+        C, R = _mla_dense(w, ckv, kpe, b)
+        L, r0, r1 = C.shape[0], int(w.qo_indptr[b]), int(w.qo_indptr[b + 1])
+        n = r1 - r0
+        mask = torch.tensor([[t <= L - n + i for t in range(L)] for i in range(n)])
+        for h in range(H):
+            K = torch.from_numpy(np.concatenate([C @ Wk[h], R], axis=1))[None]   # [1, L, dn+dr]
+            V = torch.from_numpy(C @ Wv[h])[None]                               # [1, L, dv]
+            Q = torch.from_numpy(np.concatenate([qn_heads[r0:r1, h], qp[r0:r1, h]], axis=1))[None]
+            ref = F.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=scale)[0]
+            got = torch.from_numpy(O[r0:r1, h] @ Wv[h])
+            assert torch.allclose(got, ref, atol=1e-11, rtol=0), (b, h)
+
+
+def pin_mla_without_rotary_is_mqa(mod):
+    """With q_pe = 0 the rotary keys drop out: latent attention is the
+    (pinned) prefill / decode oracle with one KV head whose K and V are both
+    the latents and every head in its group."""
+    for causal, mq in ((True, 4), (True, 1), (False, 3)):
+        w = random_mla_workload(76, 4, 26, 4, 4, max_qo=mq, causal=causal)
+        qn, qp, ckv, kpe = _mla_values(w, 8, 4, 76)
+        O, LSE = _mla(mod, w, qn, np.zeros_like(qp), ckv, kpe)
+        pool = ckv[:, None]  # [pages, 1 KV head, P, d_c]
+        Oref, LSEref = mod.prefill_attention(qn, pool, pool, w.qo_indptr, w.kv_indptr,
+                                             w.kv_indices, w.last_page_len, causal, 0.3)
+        assert np.allclose(O, Oref, atol=1e-13, rtol=0) and np.allclose(LSE, LSEref, atol=1e-13,
+                                                                         rtol=0), (causal, mq)
+
+
+def pin_mla_rotary_shift(mod):
+    """Adding one vector u to every cached rotary key moves each score of a
+    (query token, head) by sm_scale q_pe . u, the same for all its tokens:
+    outputs stay, LSE moves by exactly that amount."""
+    w = random_mla_workload(77, 3, 31, 3, 8, max_qo=3)
+    qn, qp, ckv, kpe = _mla_values(w, 8, 4, 77)
+    u = np.array([0.5, -1.25, 2.0, 0.75])
+    O, LSE = _mla(mod, w, qn, qp, ckv, kpe)
+    O2, LSE2 = _mla(mod, w, qn, qp, ckv, kpe + u)
+    assert np.allclose(O, O2, atol=1e-12, rtol=0)
+    assert np.allclose(LSE2 - LSE, 0.3 * (qp @ u), atol=1e-12, rtol=0)
+
+
+def pin_mla_single_and_constant(mod):
+    """A one-token history returns its latent with LSE = the scaled score; a
+    history whose latents are all one vector returns that vector."""
+    w = random_mla_workload(78, 3, 1, 2, 4, lens=[1, 1, 1], qo_lens=[1, 1, 1])
+    qn, qp, ckv, kpe = _mla_values(w, 6, 2, 78)
+    O, LSE = _mla(mod, w, qn, qp, ckv, kpe)
+    for b in range(3):
+        pg = int(w.kv_indices[w.kv_indptr[b]])
+        assert np.allclose(O[b], ckv[pg, 0][None], atol=1e-14, rtol=0)
+        assert np.allclose(LSE[b], 0.3 * (qn[b] @ ckv[pg, 0] + qp[b] @ kpe[pg, 0]), atol=1e-12)
+    w = random_mla_workload(79, 3, 40, 2, 4, max_qo=3)
+    qn, qp, ckv, kpe = _mla_values(w, 6, 2, 79)
+    c = np.array([1.5, -2.0, 0.25, 3.0, -0.5, 1.0])
+    ckv = np.where(np.isnan(ckv), np.nan, c[None, None, :])
+    O, _ = _mla(mod, w, qn, qp, ckv, kpe)
+    assert np.allclose(O, np.broadcast_to(c, O.shape), atol=1e-13, rtol=0)
+
+
+MLA_PINS = [pin_mla_bruteforce, pin_mla_explicit_heads, pin_mla_without_rotary_is_mqa,
+            pin_mla_rotary_shift, pin_mla_single_and_constant]

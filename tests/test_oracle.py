@@ -7,7 +7,8 @@ from tests import oracle_pins as pins
 
 
 @pytest.mark.parametrize("pin", pins.ALL_PINS + pins.PREFILL_PINS + pins.ROPE_PINS +
-                         pins.COMPOSED_PINS + pins.PREFILL_ROPE_PINS + [pins.pin_bf16],
+                         pins.COMPOSED_PINS + pins.PREFILL_ROPE_PINS + pins.MLA_PINS +
+                         [pins.pin_bf16],
                          ids=lambda f: f.__name__)
 def test_pin(pin):
     pin(oa)
@@ -328,3 +329,57 @@ def test_prefill_rope_oracle_mutations_are_caught(name, monkeypatch):
         except (AssertionError, ValueError, IndexError, TypeError):
             caught.append(pin.__name__)
     assert caught, f"planted mistake {name} passed every prefill RoPE pin"
+
+
+_orig_gather_latent = oa.gather_latent
+_orig_mla = oa.mla_attention
+
+
+def _latent_no_rotary(ckv_pool, kpe_pool, tokens):
+    C, R = _orig_gather_latent(ckv_pool, kpe_pool, tokens)
+    return C, np.zeros_like(R)
+
+
+def _latent_rotary_shifted(ckv_pool, kpe_pool, tokens):
+    C, R = _orig_gather_latent(ckv_pool, kpe_pool, tokens)
+    return C, np.roll(R, 1, axis=0)
+
+
+def _latent_reversed(ckv_pool, kpe_pool, tokens):
+    C, R = _orig_gather_latent(ckv_pool, kpe_pool, tokens)
+    return C[::-1], R[::-1]
+
+
+def _mla_rotary_unscaled(q_nope, q_pe, ckv, kpe, qo, ip, ix, lp, sm_scale, causal=True):
+    return _orig_mla(q_nope, np.asarray(q_pe) / sm_scale, ckv, kpe, qo, ip, ix, lp, sm_scale,
+                     causal)
+
+
+def _mla_first_head_query(q_nope, q_pe, ckv, kpe, qo, ip, ix, lp, sm_scale, causal=True):
+    qn = np.broadcast_to(np.asarray(q_nope)[:, :1], np.shape(q_nope))
+    return _orig_mla(qn, q_pe, ckv, kpe, qo, ip, ix, lp, sm_scale, causal)
+
+
+MLA_MUTATIONS = {
+    "mla_rotary_key_dropped": ("gather_latent", _latent_no_rotary),
+    "mla_rotary_key_of_previous_token": ("gather_latent", _latent_rotary_shifted),
+    "mla_history_reversed": ("gather_latent", _latent_reversed),
+    "mla_scale_misses_rotary_part": ("mla_attention", _mla_rotary_unscaled),
+    "mla_heads_share_one_query": ("mla_attention", _mla_first_head_query),
+    "causal_excludes_own_token": ("visible_tokens", _visible_off_by_one),
+    "missing_sm_scale": ("attend", _attend_no_scale),
+    "lse_base_2": ("attend", _attend_log2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MLA_MUTATIONS))
+def test_mla_oracle_mutations_are_caught(name, monkeypatch):
+    attr, fn = MLA_MUTATIONS[name]
+    monkeypatch.setattr(oa, attr, fn)
+    caught = []
+    for pin in pins.MLA_PINS:
+        try:
+            pin(oa)
+        except (AssertionError, ValueError, IndexError, TypeError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake {name} passed every MLA pin"
