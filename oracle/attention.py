@@ -116,14 +116,14 @@ def request_tokens(kv_indptr, kv_indices, last_page_len, page_size, b) -> List[T
 def attend(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float):
     """Softmax attention of query rows over one token set.
 
-    q_rows [G, d], K [T, d], V [T, d] (float64). Returns (O [G, d], LSE [G])
+    q_rows [G, d], K [T, d], V [T, d_v] (float64). Returns (O [G, d_v], LSE [G])
     where s_t = sm_scale * q . k_t, O = sum_t softmax(s)_t v_t and
     LSE = ln sum_t exp(s_t) (natural log of the scaled scores).
     An empty token set gives O = 0 and LSE = -inf.
     """
-    G, d = q_rows.shape
+    G = q_rows.shape[0]
     if K.shape[0] == 0:
-        return np.zeros((G, d)), np.full(G, NEG_INF)
+        return np.zeros((G, V.shape[1])), np.full(G, NEG_INF)
     s = sm_scale * (q_rows @ K.T)              # [G, T]
     m = s.max(axis=1, keepdims=True)
     w = np.exp(s - m)

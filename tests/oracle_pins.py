@@ -615,14 +615,22 @@ def _mla_dense(w, ckv, kpe, b):
 
 
 def pin_mla_bruteforce(mod, tol=1e-12):
-    for (seed, B, L, H, P, mq, dc, dr, causal) in MLA_TINY:
-        w = random_mla_workload(seed, B, L, H, P, max_qo=mq, causal=causal)
+    for (seed, B, L, H, P, mq, dc, dr, causal) in MLA_TINY + [(70, 3, 9, 2, 4, 2, 6, 4, False)]:
+        # seed 70: no mask and a request without tokens (its rows: O = 0 of
+        # the latent width, LSE = -inf)
+        lens = [9, 0, 5] if seed == 70 else None
+        w = random_mla_workload(seed, B, L, H, P, max_qo=mq, causal=causal, lens=lens,
+                                qo_lens=[2, 1, 1] if lens else None)
         qn, qp, ckv, kpe = _mla_values(w, dc, dr, seed)
         O, LSE = _mla(mod, w, qn, qp, ckv, kpe)
         Ob, LSEb = bruteforce_mla(qn, qp, ckv, kpe, w.qo_indptr, w.kv_indptr, w.kv_indices,
                                   w.last_page_len, 0.3, causal)
-        assert np.max(np.abs(O - np.array(Ob))) <= tol, seed
-        assert np.max(np.abs(LSE - np.array(LSEb))) <= tol, seed
+        Ob, LSEb = np.array(Ob), np.array(LSEb)
+        assert O.shape == Ob.shape, seed
+        assert np.max(np.abs(O - Ob)) <= tol, seed
+        assert np.array_equal(np.isneginf(LSE), np.isneginf(LSEb)), seed
+        fin = ~np.isneginf(LSEb)
+        assert np.max(np.abs(LSE[fin] - LSEb[fin]), initial=0.0) <= tol, seed
 
 
 def pin_mla_explicit_heads(mod):
