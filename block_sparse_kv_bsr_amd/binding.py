@@ -37,12 +37,15 @@ EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_
             "fi_prefill_plan_merges", "fi_prefill_plan_upload", "fi_prefill_run",
             "fi_prefill_plan_destroy", "fi_decode_run_rope", "fi_decode_run_rope_scaled",
             "fi_decode_run_noalloc", "fi_prefill_run_scaled", "fi_plan_create_composed",
-            "fi_decode_run_composed", "fi_prefill_run_rope"]
+            "fi_decode_run_composed", "fi_prefill_run_rope", "fi_mla_plan_create", "fi_mla_run"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 QITEM_STRIDE = 12
 QMERGE_STRIDE = 8
 PREFILL_ROWS = 256
 PREFILL_MAX_PAGES = 256
+MLA_ROWS = 32
+MLA_DC = 512
+MLA_DR = 64
 
 
 class FiError(RuntimeError):
@@ -91,7 +94,8 @@ class PrefillInfo(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("num_qo_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("causal", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("rope", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("rope", ctypes.c_int32), ("mla", ctypes.c_int32),
+                ("head_dim_kpe", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -164,6 +168,11 @@ def lib() -> ctypes.CDLL:
     L.fi_prefill_run_rope.restype = i32
     L.fi_prefill_plan_destroy.argtypes = [vp]
     L.fi_prefill_plan_destroy.restype = None
+    L.fi_mla_plan_create.argtypes = [pi32, pi32, pi32, pi32, i32, i32, i32, i32, i32, i64, i32,
+                                     ctypes.POINTER(PrefillOpts), ctypes.POINTER(vp)]
+    L.fi_mla_plan_create.restype = i32
+    L.fi_mla_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, sz, vp]
+    L.fi_mla_run.restype = i32
     L.fi_last_error.argtypes = []
     L.fi_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -638,4 +647,69 @@ def prefill(q, k_pages, v_pages, plan_: PrefillPlan, out=None, lse=None,
                                        ctypes.c_void_p(workspace.data_ptr()),
                                        workspace.numel() * workspace.element_size(),
                                        ctypes.c_void_p(_stream(stream))))
+    return out, lse
+
+
+def mla_plan(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_heads: int, page_size: int,
+             num_pool_pages: int, causal: bool = True, num_cus: int = 0, items_per_cu: int = 0,
+             fixed_chunk_tokens: int = 0, num_xcds: int = 0) -> PrefillPlan:
+    """fi_mla_plan_create (latent width 512, rotary-key width 64) over host
+    arrays; the plan is a PrefillPlan run by ``mla``."""
+    qp, ip, ix, lp = _i32(qo_indptr), _i32(kv_indptr), _i32(kv_indices), _i32(kv_last_page_len)
+    batch = _check_lengths(ip, ix, lp)
+    if qp.ndim != 1 or len(qp) != batch + 1:
+        raise ValueError("qo_indptr, kv_indptr and kv_last_page_len disagree on the batch size")
+    opts = PrefillOpts(num_cus, items_per_cu, fixed_chunk_tokens, num_xcds, 0)
+    h = ctypes.c_void_p()
+    ix_ptr = _ptr32(ix) if ix.size else ctypes.POINTER(ctypes.c_int32)()
+    _check(lib().fi_mla_plan_create(_ptr32(qp), _ptr32(ip), ix_ptr, _ptr32(lp), batch, num_heads,
+                                    MLA_DC, MLA_DR, page_size, int(num_pool_pages),
+                                    int(bool(causal)), ctypes.byref(opts), ctypes.byref(h)))
+    p = PrefillPlan(h.value)
+    p.num_pool_pages = int(num_pool_pages)
+    return p
+
+
+def mla(q_nope, q_pe, ckv_pages, kpe_pages, plan_: PrefillPlan, sm_scale: float, out=None,
+        lse=None, workspace=None, stream=None):
+    """fi_mla_run: returns (out [N, H, 512] bf16, lse [N, H] float32).
+    q_nope [N, H, 512], q_pe [N, H, 64], ckv_pages [pool, P, 512], kpe_pages
+    [pool, P, 64], all bf16; sm_scale is required (the model's)."""
+    import torch
+    for t, n in ((q_nope, "q_nope"), (q_pe, "q_pe"), (ckv_pages, "ckv_pages"),
+                 (kpe_pages, "kpe_pages")):
+        _require_gpu(t, n)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{n} must be bf16")
+        if t.device != q_nope.device:
+            raise ValueError(f"{n} is on {t.device}, q_nope on {q_nope.device}")
+    info = plan_.info
+    if not info["mla"]:
+        raise ValueError("mla() runs plans made by mla_plan()")
+    N, H, P = info["total_qo_tokens"], info["num_qo_heads"], info["page_size"]
+    if tuple(q_nope.shape) != (N, H, MLA_DC) or tuple(q_pe.shape) != (N, H, MLA_DR):
+        raise ValueError(f"q_nope / q_pe must have shapes {(N, H, MLA_DC)} / {(N, H, MLA_DR)}")
+    for t, n, d in ((ckv_pages, "ckv_pages", MLA_DC), (kpe_pages, "kpe_pages", MLA_DR)):
+        if t.dim() != 3 or tuple(t.shape[1:]) != (P, d):
+            raise ValueError(f"{n} must have shape [pool, {P}, {d}]")
+        if t.shape[0] < plan_.num_pool_pages:
+            raise ValueError(f"{n} holds {t.shape[0]} pages; the plan was made for "
+                             f"{plan_.num_pool_pages}")
+    if out is None:
+        out = torch.empty((N, H, MLA_DC), dtype=torch.bfloat16, device=q_nope.device)
+    if lse is None:
+        lse = torch.empty((N, H), dtype=torch.float32, device=q_nope.device)
+    _require_like(out, "out", (N, H, MLA_DC), torch.bfloat16, q_nope.device)
+    _require_like(lse, "lse", (N, H), torch.float32, q_nope.device)
+    if workspace is None:
+        workspace = plan_.ensure_uploaded(q_nope.device, stream)
+    elif workspace.device != q_nope.device:
+        raise ValueError(f"workspace is on {workspace.device}, q_nope on {q_nope.device}")
+    _check(lib().fi_mla_run(plan_.handle, ctypes.c_void_p(q_nope.data_ptr()),
+                            ctypes.c_void_p(q_pe.data_ptr()), ctypes.c_void_p(ckv_pages.data_ptr()),
+                            ctypes.c_void_p(kpe_pages.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                            ctypes.c_void_p(lse.data_ptr()), float(sm_scale),
+                            ctypes.c_void_p(workspace.data_ptr()),
+                            workspace.numel() * workspace.element_size(),
+                            ctypes.c_void_p(_stream(stream))))
     return out, lse

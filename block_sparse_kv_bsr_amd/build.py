@@ -25,7 +25,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Packed fp32 VALU ops are kept out of every device code object.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HIP_SOURCES = ["decode_bsr.hip", "decode_mma.hip", "attn_tile.hip", "merge_states.hip", "abi.hip",
-               "staging.hip"]
+               "staging.hip", "mla_attend.hip"]
 CPP_SOURCES = ["plan.cpp", "prefill_plan.cpp"]
 BENCH_SOURCES = ["bench_stream.hip"]
 

@@ -130,6 +130,7 @@ fi_status prefill_run(const fi_prefill_plan* plan, const void* q, const void* k_
                       const void* v_pages, float k_scale, float v_scale, float rope_theta,
                       float rope_scale, void* out, float* lse, float sm_scale, void* workspace,
                       size_t workspace_bytes, fi_stream_t stream) {
+  if (plan->mla) return fail(FI_ERR_INVALID_ARG, "a plan made with fi_mla_plan_create runs with fi_mla_run");
   if (plan->num_items() == 0) return FI_OK;
   if (!q || !out) return fail(FI_ERR_INVALID_ARG, "q or out is NULL");
   if (!k_pages || !v_pages) return fail(FI_ERR_INVALID_ARG, "k_pages or v_pages is NULL");
@@ -218,6 +219,51 @@ fi_status fi_prefill_run_rope(const fi_prefill_plan* plan, const void* q, const 
   if (!(rope_theta > 1.f)) return fail(FI_ERR_INVALID_ARG, "rope_theta must exceed 1");
   return prefill_run(plan, q, k_pages, v_pages, 1.f, 1.f, rope_theta, rope_scale, out, lse,
                      sm_scale, workspace, workspace_bytes, stream);
+}
+
+fi_status fi_mla_run(const fi_prefill_plan* plan, const void* q_nope, const void* q_pe,
+                     const void* ckv_pages, const void* kpe_pages, void* out, float* lse,
+                     float sm_scale, void* workspace, size_t workspace_bytes, fi_stream_t stream) {
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  if (!plan->mla) return fail(FI_ERR_INVALID_ARG, "fi_mla_run needs a plan made with fi_mla_plan_create");
+  if (!(sm_scale > 0.f) || std::isinf(sm_scale))
+    return fail(FI_ERR_INVALID_ARG, "sm_scale must be finite and positive (the model's scale)");
+  if (plan->num_items() == 0) return FI_OK;
+  if (!q_nope || !q_pe || !out) return fail(FI_ERR_INVALID_ARG, "q_nope, q_pe or out is NULL");
+  if (!ckv_pages || !kpe_pages) return fail(FI_ERR_INVALID_ARG, "ckv_pages or kpe_pages is NULL");
+  if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(ckv_pages, 16) ||
+      !aligned(kpe_pages, 16) || !aligned(out, 16))
+    return fail(FI_ERR_INVALID_ARG, "q_nope, q_pe, ckv_pages, kpe_pages and out must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(FI_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  if (!workspace) return fail(FI_ERR_INVALID_ARG, "workspace is NULL");
+  if ((int64_t)workspace_bytes < plan->ws.total_bytes)
+    return fail(FI_ERR_WORKSPACE, "workspace smaller than fi_prefill_info.workspace_bytes");
+  if (!holds_plan(workspace, plan->ws.total_bytes, plan->serial))
+    return fail(FI_ERR_STATE,
+                "workspace does not hold this plan: it was not uploaded there, or another plan "
+                "was uploaded over it since (call fi_prefill_plan_upload)");
+  char* ws = static_cast<char*>(workspace);
+  fi::MlaArgs a{};
+  a.items = reinterpret_cast<const int32_t*>(ws + plan->ws.items);
+  a.merges = reinterpret_cast<const int32_t*>(ws + plan->ws.merges);
+  a.page_ids = reinterpret_cast<const int32_t*>(ws + plan->ws.page_ids);
+  a.q_nope = q_nope;
+  a.q_pe = q_pe;
+  a.ckv = ckv_pages;
+  a.kpe = kpe_pages;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = reinterpret_cast<float*>(ws + plan->ws.part_o);
+  a.part_lse = reinterpret_cast<float*>(ws + plan->ws.part_lse);
+  a.num_items = plan->num_items();
+  a.num_merges = plan->num_merges();
+  a.num_heads = plan->num_qo_heads;
+  a.page_size = plan->page_size;
+  a.causal = plan->causal;
+  a.sm_scale = sm_scale;
+  const hipError_t e = fi::launch_mla(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "MLA kernel launch");
+  return FI_OK;
 }
 
 void fi_prefill_plan_destroy(fi_prefill_plan* plan) { destroy(plan); }

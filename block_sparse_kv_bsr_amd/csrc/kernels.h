@@ -65,6 +65,23 @@ struct PrefillArgs {
   float rope_theta, rope_scale;
 };
 
+struct MlaArgs {
+  const int32_t* items;     // device, [num_items][FI_QITEM_STRIDE]
+  const int32_t* merges;    // device, [num_merges][FI_QMERGE_STRIDE]
+  const int32_t* page_ids;  // device, the request page lists
+  const void* q_nope;       // bf16 [N, num_heads, 512]
+  const void* q_pe;         // bf16 [N, num_heads, 64]
+  const void* ckv;          // bf16 [pool, page_size, 512]
+  const void* kpe;          // bf16 [pool, page_size, 64]
+  void* out;                // bf16 [N, num_heads, 512]
+  float* lse;               // [N, num_heads] natural log, or null
+  float* part_o;            // [slots, FI_MLA_ROWS, 512]
+  float* part_lse;          // [slots, FI_MLA_ROWS], log2 units
+  int64_t num_items, num_merges;
+  int32_t num_heads, page_size, causal;
+  float sm_scale;
+};
+
 struct MergeTwoArgs {
   const void* v_a;
   const float* s_a;
@@ -87,5 +104,7 @@ hipError_t launch_merge_two(const MergeTwoArgs& a, hipStream_t stream);
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_merge(const PrefillArgs& a, hipStream_t stream);
+// Latent attention tiles, then the merge of cut tiles (mla_attend.hip).
+hipError_t launch_mla(const MlaArgs& a, hipStream_t stream);
 
 }  // namespace fi

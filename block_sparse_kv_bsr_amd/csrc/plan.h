@@ -78,6 +78,8 @@ struct fi_prefill_plan {
   int32_t group = 0, causal = 1, tokens_per_tile = 0, chunk_tokens = 0;
   fi_dtype dtype = FI_DTYPE_BF16;  // of the K/V pages (q and out are bf16)
   int32_t rope = 0;                // tiles for fi_prefill_run_rope
+  int32_t mla = 0;                 // fi_mla_plan_create: latent attention tiles
+  int32_t head_dim_kpe = 0;        // MLA: rotary-key width
   int64_t num_pool_pages = 0, total_qo = 0, total_kv = 0, visible_pairs = 0;
   int64_t num_tiles = 0, num_slots = 0;
   std::vector<int32_t> items;   // num_items * FI_QITEM_STRIDE

@@ -44,16 +44,18 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 }  // namespace fi
 
-extern "C" {
+namespace fi {
+namespace {
 
-fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr,
-                                 const int32_t* kv_indices, const int32_t* kv_last_page_len,
-                                 int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t page_size, int64_t num_pool_pages,
-                                 fi_dtype dtype, int32_t causal, const fi_prefill_opts* opts,
-                                 fi_prefill_plan** out_plan) {
-  using fi::ceil_div;
-  using fi::fail;
+// The planner of both call families. mla: multi-head latent attention, one
+// latent "KV head" shared by num_qo_heads query heads, tiles of FI_MLA_ROWS
+// (query token, head) rows.
+fi_status build_tile_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                          int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t page_size, int64_t num_pool_pages,
+                          fi_dtype dtype, int32_t causal, const fi_prefill_opts* opts, bool mla,
+                          fi_prefill_plan** out_plan) {
   try {
     if (!out_plan) return fail(FI_ERR_INVALID_ARG, "out_plan is NULL");
     *out_plan = nullptr;
@@ -64,15 +66,18 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
     if (num_qo_heads % num_kv_heads != 0)
       return fail(FI_ERR_INVALID_ARG, "num_qo_heads is not a multiple of num_kv_heads");
     const int32_t group = num_qo_heads / num_kv_heads;
-    if (group > FI_PREFILL_ROWS)
+    if (!mla && group > FI_PREFILL_ROWS)
       return fail(FI_ERR_UNSUPPORTED, "GQA group size above " + std::to_string(FI_PREFILL_ROWS));
-    if (head_dim != 64 && head_dim != 128)
+    if (!mla && head_dim != 64 && head_dim != 128)
       return fail(FI_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     if (dtype != FI_DTYPE_BF16 && dtype != FI_DTYPE_FP8_E4M3)
       return fail(FI_ERR_UNSUPPORTED, "prefill needs FI_DTYPE_BF16 or FI_DTYPE_FP8_E4M3");
     if (dtype == FI_DTYPE_FP8_E4M3 && head_dim != 128)
       return fail(FI_ERR_UNSUPPORTED, "fp8 prefill is built for head_dim 128");
     const bool rope = opts && opts->rope;
+    if (mla && rope)
+      return fail(FI_ERR_UNSUPPORTED, "MLA plans take rotated q_pe and k_pe (fi_prefill_opts.rope "
+                                      "must be 0)");
     if (rope && (dtype != FI_DTYPE_BF16 || head_dim != 128))
       return fail(FI_ERR_UNSUPPORTED, "prefill with the rotary embedding is built for bf16, head_dim 128");
     if (rope && group > FI_PREFILL_ROWS / 2)
@@ -103,7 +108,7 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
     if (o.num_cus < 0 || o.items_per_cu < 0 || o.fixed_chunk_tokens < 0 || o.num_xcds < 0)
       return fail(FI_ERR_INVALID_ARG, "negative planner option");
     const int64_t num_cus = o.num_cus ? o.num_cus : 256;
-    const int64_t items_per_cu = o.items_per_cu ? o.items_per_cu : 4;
+    const int64_t items_per_cu = o.items_per_cu ? o.items_per_cu : (mla ? 2 : 4);
     const int64_t num_xcds = o.num_xcds ? o.num_xcds : 8;
 
     auto p = std::make_unique<fi_prefill_plan>();
@@ -118,15 +123,20 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
     p->num_pool_pages = num_pool_pages;
     p->total_qo = total_qo;
     p->rope = rope ? 1 : 0;
+    p->mla = mla ? 1 : 0;
     // query tokens per tile: a rope tile is half as tall (its kernel keeps
-    // the queries' lo parts in registers too)
-    const int64_t T = (rope ? FI_PREFILL_ROWS / 2 : FI_PREFILL_ROWS) / group;
+    // the queries' lo parts in registers too); an MLA tile holds FI_MLA_ROWS
+    // rows, whole query tokens or one token's heads in blocks
+    const int64_t T = mla ? std::max(1, FI_MLA_ROWS / group)
+                          : (rope ? FI_PREFILL_ROWS / 2 : FI_PREFILL_ROWS) / group;
+    const int32_t head_blocks = mla && group > FI_MLA_ROWS ? (group + FI_MLA_ROWS - 1) / FI_MLA_ROWS : 1;
     p->tokens_per_tile = (int32_t)T;
 
-    // ---- tiles: (request, KV head, block of T query tokens); the range a
-    // tile attends is what its last query sees
+    // ---- tiles: (request, KV head, block of T query tokens, and for MLA
+    // with more than FI_MLA_ROWS heads a block of heads); the range a tile
+    // attends is what its last query sees
     struct Tile {
-      int32_t b, qo_row, nqo;
+      int32_t b, qo_row, nqo, head_begin;
       int64_t visible, range, qpos;
     };
     std::vector<Tile> tiles;
@@ -139,8 +149,11 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
         const int64_t nq = std::min<int64_t>(T, n - t0);
         const int64_t vis = causal ? L - n + t0 + 1 : L;
         const int64_t range = causal ? vis + nq - 1 : L;
-        tiles.push_back({b, (int32_t)(qo_indptr[b] + t0), (int32_t)nq, vis, range, L - n + t0});
-        work += range * num_kv_heads;
+        for (int32_t hb = 0; hb < head_blocks; ++hb) {
+          tiles.push_back({b, (int32_t)(qo_indptr[b] + t0), (int32_t)nq, hb * FI_MLA_ROWS, vis,
+                           range, L - n + t0});
+          work += range * num_kv_heads;
+        }
       }
     }
     p->num_tiles = (int64_t)tiles.size() * num_kv_heads;
@@ -151,7 +164,9 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
     if (o.fixed_chunk_tokens > 0) {
       C = ceil_div(o.fixed_chunk_tokens, page_size) * page_size;
     } else {
-      const int64_t want = std::max<int64_t>(ceil_div(work, num_cus * items_per_cu), 512);
+      // an MLA partial state is FI_MLA_ROWS x 512 floats (64 KiB), as many
+      // bytes as 57 cached latent rows: its chunks stay long
+      const int64_t want = std::max<int64_t>(ceil_div(work, num_cus * items_per_cu), mla ? 1024 : 512);
       C = ceil_div(want, page_size) * page_size;
     }
     C = std::min(C, cap);
@@ -174,6 +189,7 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
           m[FI_QMERGE_KV_HEAD] = h;
           m[FI_QMERGE_SLOT_BEGIN] = (int32_t)slot0;
           m[FI_QMERGE_NUM_CHUNKS] = (int32_t)k;
+          m[FI_QMERGE_HEAD_BEGIN] = t.head_begin;
           p->merges.insert(p->merges.end(), m, m + FI_QMERGE_STRIDE);
           p->num_slots += k;
         }
@@ -192,6 +208,7 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
           f[FI_QITEM_SLOT] = k > 1 ? (int32_t)(slot0 + c) : -1;
           f[FI_QITEM_CHUNK] = (int32_t)c;
           f[FI_QITEM_Q_POS] = (int32_t)t.qpos;
+          f[FI_QITEM_HEAD_BEGIN] = t.head_begin;
           longest = std::max(longest, f[FI_QITEM_NUM_KV]);
           p->items.insert(p->items.end(), f, f + FI_QITEM_STRIDE);
         }
@@ -207,7 +224,8 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
       auto key = [&](int64_t i, int f) { return it[i * FI_QITEM_STRIDE + f]; };
       // items of each pair, longest chunk first; ties in (query row, chunk)
       // order, which is the order the items of a pair were made in, so the
-      // item index breaks them (keys sorted, not items)
+      // item index breaks them (keys sorted, not items). MLA: chunk order
+      // (the tiles of one chunk, which read the same latent rows, adjacent)
       struct SortKey {
         uint32_t req, head, shorter, index;
         bool operator<(const SortKey& o) const {
@@ -220,7 +238,9 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
       std::vector<SortKey> keys((size_t)n);
       for (int64_t i = 0; i < n; ++i)
         keys[(size_t)i] = {(uint32_t)key(i, FI_QITEM_REQUEST), (uint32_t)key(i, FI_QITEM_KV_HEAD),
-                           (uint32_t)(INT32_MAX - key(i, FI_QITEM_NUM_KV)), (uint32_t)i};
+                           (uint32_t)(mla ? key(i, FI_QITEM_KV_BEGIN)
+                                          : INT32_MAX - key(i, FI_QITEM_NUM_KV)),
+                           (uint32_t)i};
       std::sort(keys.begin(), keys.end());
       std::vector<int64_t> order(n);
       for (int64_t i = 0; i < n; ++i) order[i] = keys[(size_t)i].index;
@@ -274,9 +294,10 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
     off = fi::align_up(off + nnz * 4, 256);
     ws.image_bytes = off;
     ws.part_o = off;
-    off = fi::align_up(off + p->num_slots * FI_PREFILL_ROWS * (int64_t)head_dim * 4, 256);
+    const int64_t slot_rows = mla ? FI_MLA_ROWS : FI_PREFILL_ROWS;
+    off = fi::align_up(off + p->num_slots * slot_rows * (int64_t)head_dim * 4, 256);
     ws.part_lse = off;
-    off = fi::align_up(off + p->num_slots * FI_PREFILL_ROWS * 4, 256);
+    off = fi::align_up(off + p->num_slots * slot_rows * 4, 256);
     ws.total_bytes = std::max<int64_t>(off, 256);
     p->image.assign(ws.image_bytes, 0);
     if (!p->items.empty()) std::memcpy(p->image.data() + ws.items, p->items.data(), p->items.size() * 4);
@@ -287,10 +308,46 @@ fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_ind
     *out_plan = p.release();
     return FI_OK;
   } catch (const std::bad_alloc&) {
-    return fail(FI_ERR_NOMEM, "host allocation failed in fi_prefill_plan_create");
+    return fail(FI_ERR_NOMEM, "host allocation failed in the prefill / MLA planner");
   } catch (...) {
-    return fail(FI_ERR_INVALID_ARG, "unexpected error in fi_prefill_plan_create");
+    return fail(FI_ERR_INVALID_ARG, "unexpected error in the prefill / MLA planner");
   }
+}
+
+}  // namespace
+}  // namespace fi
+
+extern "C" {
+
+fi_status fi_prefill_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                 const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                                 int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t page_size, int64_t num_pool_pages,
+                                 fi_dtype dtype, int32_t causal, const fi_prefill_opts* opts,
+                                 fi_prefill_plan** out_plan) {
+  return fi::build_tile_plan(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch,
+                             num_qo_heads, num_kv_heads, head_dim, page_size, num_pool_pages,
+                             dtype, causal, opts, false, out_plan);
+}
+
+fi_status fi_mla_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                             int32_t batch, int32_t num_heads, int32_t head_dim_ckv,
+                             int32_t head_dim_kpe, int32_t page_size, int64_t num_pool_pages,
+                             int32_t causal, const fi_prefill_opts* opts,
+                             fi_prefill_plan** out_plan) {
+  if (out_plan) *out_plan = nullptr;
+  if (head_dim_ckv != 512 || head_dim_kpe != 64)
+    return fi::fail(FI_ERR_UNSUPPORTED, "MLA is built for a 512-wide latent and a 64-wide "
+                                        "rotary key");
+  if (num_heads <= 0 || num_heads > 4096)
+    return fi::fail(FI_ERR_INVALID_ARG, "num_heads must be in 1 .. 4096");
+  const fi_status st = fi::build_tile_plan(qo_indptr, kv_indptr, kv_indices, kv_last_page_len,
+                                           batch, num_heads, 1, head_dim_ckv, page_size,
+                                           num_pool_pages, FI_DTYPE_BF16, causal, opts, true,
+                                           out_plan);
+  if (st == FI_OK) (*out_plan)->head_dim_kpe = head_dim_kpe;
+  return st;
 }
 
 fi_status fi_prefill_plan_get_info(const fi_prefill_plan* p, fi_prefill_info* info) {
@@ -314,6 +371,8 @@ fi_status fi_prefill_plan_get_info(const fi_prefill_plan* p, fi_prefill_info* in
   r.causal = p->causal;
   r.dtype = p->dtype;
   r.rope = p->rope;
+  r.mla = p->mla;
+  r.head_dim_kpe = p->head_dim_kpe;
   *info = r;
   return FI_OK;
 }

@@ -551,6 +551,11 @@ typedef struct {
   int32_t batch, num_qo_heads, num_kv_heads, head_dim, page_size, causal;
   int32_t dtype;              /* fi_dtype of the K/V pages */
   int32_t rope;               /* made with fi_prefill_opts.rope */
+  int32_t mla;                /* made with fi_mla_plan_create: num_qo_heads is the
+                                 head count, num_kv_heads 1, head_dim the latent
+                                 width, head_dim_kpe the rotary-key width, and
+                                 partial slots hold FI_MLA_ROWS rows */
+  int32_t head_dim_kpe;       /* MLA plans; 0 otherwise */
 } fi_prefill_info;
 
 /*
@@ -579,8 +584,13 @@ enum {
                               queries); negative only for an unmasked request
                               with more queries than tokens (rope plans refuse
                               those) */
+  FI_QITEM_HEAD_BEGIN = 11, /* MLA plans: first (query token, head) row of the
+                              tile, counted token-major from the tile's first
+                              query token (0 unless a token's heads span
+                              several tiles); 0 in other plans */
   FI_QITEM_STRIDE = 12,
   FI_PREFILL_ROWS = 256,      /* query rows per tile */
+  FI_MLA_ROWS = 32,           /* (query token, head) rows per MLA tile */
   FI_PREFILL_MAX_PAGES = 256  /* pages per chunk at most */
 };
 
@@ -592,6 +602,7 @@ enum {
   FI_QMERGE_KV_HEAD = 2,
   FI_QMERGE_SLOT_BEGIN = 3,
   FI_QMERGE_NUM_CHUNKS = 4,
+  FI_QMERGE_HEAD_BEGIN = 5, /* MLA plans: as FI_QITEM_HEAD_BEGIN */
   FI_QMERGE_STRIDE = 8
 };
 
@@ -702,6 +713,85 @@ fi_status fi_prefill_run_rope(const fi_prefill_plan* plan, const void* q, const 
                               const void* v_pages, float rope_theta, float rope_scale, void* out,
                               float* lse, float sm_scale, void* workspace,
                               size_t workspace_bytes, fi_stream_t stream);
+
+/* ======================================================================
+ * Multi-head latent attention (MLA) over a paged latent cache (FlashInfer
+ * 0.6.17 release write-up, llm-wiki.hwlabs.dev, section 2 on Blackwell and
+ * Kimi K3 MLA support: MLA caches a compressed latent vector per token
+ * instead of per-head K and V; restoring K/V by up-projection and writing it
+ * to shared memory before attention was the bottleneck, which the kernel
+ * removes by packing query-token rows and query-head rows into one tile;
+ * head counts that are not powers of two and several (speculative) query
+ * tokens per request are supported).
+ *
+ * Attention runs in the latent space (the up-projections folded into the
+ * query and the output by the caller). Token t of a request caches a latent
+ * c_t (head_dim_ckv = 512) and a rotary key k_t (head_dim_kpe = 64, stored
+ * rotated). Query token i of request b and head h bring q_nope[r,h] (512,
+ * the no-rotary query part already multiplied by the head's key
+ * up-projection) and q_pe[r,h] (64, rotated), r = qo_indptr[b] + i. Query
+ * tokens are the request's newest cached tokens, with the causal mask as for
+ * prefill (query i of n over L tokens attends the first L - n + i + 1):
+ *     s_t = sm_scale (<q_nope[r,h], c_t> + <q_pe[r,h], k_t>)
+ *     out[r,h] = sum_t softmax(s)_t c_t,   lse[r,h] = ln sum_t exp(s_t)
+ * Every head reads the same cache rows, so one latent row loaded serves all
+ * heads and query tokens of the request.
+ *
+ * Layout: q_nope [N, num_heads, 512], q_pe [N, num_heads, 64], out [N,
+ * num_heads, 512], all bf16 (N = qo_indptr[batch]); lse [N, num_heads]
+ * float32; ckv_pages [num_pool_pages, page_size, 512] and kpe_pages
+ * [num_pool_pages, page_size, 64] bf16, addressed by one page table.
+ * ====================================================================== */
+
+/*
+ * Build the work list of one MLA call; the plan is a fi_prefill_plan (get
+ * its info, work list and merges, upload it and destroy it with the
+ * fi_prefill_plan_* calls; fi_prefill_run* refuse it and fi_mla_run refuses
+ * other plans). Host only.
+ *
+ * qo_indptr, kv_indptr, kv_indices, kv_last_page_len, page_size,
+ * num_pool_pages, causal, opts: as for fi_prefill_plan_create (opts.rope
+ * must be 0)
+ * num_heads        1 .. 4096 query heads (any count)
+ * head_dim_ckv     512; head_dim_kpe 64 (else FI_ERR_UNSUPPORTED)
+ *
+ * Tiles are FI_MLA_ROWS (query token, head) rows of one request, token-major:
+ * FI_MLA_ROWS / num_heads whole query tokens when num_heads <= FI_MLA_ROWS,
+ * else one query token's heads HEAD_BEGIN .. HEAD_BEGIN + FI_MLA_ROWS - 1.
+ * Each tile's range is cut into chunks of C tokens (whole pages, at most
+ * FI_PREFILL_MAX_PAGES pages; C fills num_cus x items_per_cu, default 2, and
+ * is never below 1024 tokens) unless fixed_chunk_tokens is set. Every tile of
+ * a request reads the same latent rows, so a request's items share an L2
+ * domain as a prefill pair's do, and within it the tiles of one chunk are
+ * adjacent (they run side by side and the later ones find the rows in L2).
+ */
+fi_status fi_mla_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                             int32_t batch, int32_t num_heads, int32_t head_dim_ckv,
+                             int32_t head_dim_kpe, int32_t page_size, int64_t num_pool_pages,
+                             int32_t causal, const fi_prefill_opts* opts,
+                             fi_prefill_plan** out_plan);
+
+/*
+ * Run MLA for an uploaded plan on `stream`: the tile kernel (matrix cores),
+ * then, if some tile was cut into several chunks, the merge kernel. No host
+ * synchronisation; calls that use the same workspace must not overlap.
+ *
+ * q_nope, q_pe, out, lse, ckv_pages, kpe_pages: device buffers in the layout
+ *          above, 16-byte aligned; lse may be NULL
+ * sm_scale the model's score scale (1 / sqrt of the query/key head width
+ *          before absorption, e.g. 1/sqrt(192)); must be finite and
+ *          positive (the latent width does not define it)
+ * workspace, workspace_bytes, stream: as fi_prefill_run
+ *
+ * Scores and the weighted latent sum run on the matrix cores in bf16 with
+ * fp32 accumulation; the softmax weights are multiplied as hi + lo bf16
+ * parts. Errors: FI_ERR_INVALID_ARG (NULL pointer, not an MLA plan, bad
+ * scale), FI_ERR_WORKSPACE / FI_ERR_STATE as fi_prefill_run, FI_ERR_HIP.
+ */
+fi_status fi_mla_run(const fi_prefill_plan* plan, const void* q_nope, const void* q_pe,
+                     const void* ckv_pages, const void* kpe_pages, void* out, float* lse,
+                     float sm_scale, void* workspace, size_t workspace_bytes, fi_stream_t stream);
 
 /* Free a prefill plan (NULL is ignored); host memory only, no wait. */
 void fi_prefill_plan_destroy(fi_prefill_plan* plan);
