@@ -17,6 +17,7 @@ oracle timed on the host on the same workload.
 
     python bench.py [--steps K] [--warmup W] [--config 3]
     python bench.py --config 7|8|12     # prefill / append: TFLOP/s on matrix cores
+    python bench.py --config 15         # latent attention (MLA) decode: HBM GB/s
     python bench.py --summarize-counters FETCH.csv WRITE.csv   # rocprofv3 --pmc output
 """
 from __future__ import annotations
@@ -41,7 +42,9 @@ COPY_PROBE_MIB = 1024
 KERNELS = {"tile_attend_kernel": ("attn_tile.hip", "tile_attend"),
            "decode_bsr_kernel": ("decode_bsr.hip", "decode_bsr"),
            "decode_mma_kernel": ("decode_mma.hip", "decode_mma"),
-           "prefill_merge_kernel": ("merge_states.hip", "prefill_merge")}
+           "prefill_merge_kernel": ("merge_states.hip", "prefill_merge"),
+           "mla_attend_kernel": ("mla_attend.hip", "mla_attend"),
+           "mla_merge_kernel": ("mla_attend.hip", "mla_merge")}
 
 
 def source_digest(kernels=("decode_bsr_kernel",)) -> str:
@@ -159,18 +162,24 @@ def summarize_trace(stats_csv, bench_log, w, config_id):
         raise SystemExit(f"{stats_csv}: no dispatch of {missing}")
     tag = "_".join(KERNELS[k][1] for k in kernels)
     path = os.path.join(ROOT, "profiles", f"{tag}_{w.name}.md")
-    prefill = hasattr(w, "qo_indptr")
+    mla = hasattr(w, "num_heads")
+    prefill = hasattr(w, "qo_indptr") and not mla
     kern_us = sum(r[2] for r in lib.values())
     ev_us = res["us_per_batch"]
     o = []
     o.append(f"# {' + '.join(kernels)} — {w.name}\n")
     tok = (w.total_kv_lens() if hasattr(w, "prefix_of") else w.kv_lens()).sum()
-    desc = (f"batch {w.batch}, {int(tok):,} KV tokens, {w.num_qo_heads} query / "
-            f"{w.num_kv_heads} KV heads, head_dim {w.head_dim}, page size {w.page_size}, "
-            f"K/V {w.dtype}")
+    if mla:
+        desc = (f"batch {w.batch}, {int(tok):,} cached tokens (latent 512 + rotary key 64, "
+                f"bf16), {w.num_heads} query heads, {w.num_qo_tokens} query token(s), page "
+                f"size {w.page_size}; algorithmic work {w.flops():,} flop")
+    else:
+        desc = (f"batch {w.batch}, {int(tok):,} KV tokens, {w.num_qo_heads} query / "
+                f"{w.num_kv_heads} KV heads, head_dim {w.head_dim}, page size {w.page_size}, "
+                f"K/V {w.dtype}")
     if prefill:
         desc += f", {w.num_qo_tokens:,} query tokens ({'causal' if w.causal else 'unmasked'})"
-    if w.rope_theta:
+    if getattr(w, "rope_theta", 0):
         desc += f", rotary embedding (theta {w.rope_theta:g}) applied to K in the kernel"
     if hasattr(w, "prefix_of"):
         desc += (f", the shared prefix held once in a second cache of {w.prefix_page_size}-token "
@@ -179,6 +188,9 @@ def summarize_trace(stats_csv, bench_log, w, config_id):
     if prefill:
         o.append(f"Algorithmic work per batch: {w.flops():,} flop "
                  f"(4 x head_dim x query heads per attended (query, token) pair).\n")
+    elif mla:
+        o.append(f"Algorithmic bytes per batch: {w.algorithmic_bytes():,} (every cached latent "
+                 f"and rotary key once + q + output).\n")
     else:
         o.append(f"Algorithmic bytes per batch: {w.algorithmic_bytes():,} (K+V of every active "
                  f"token once per KV head + q + output).\n")
@@ -207,6 +219,11 @@ def summarize_trace(stats_csv, bench_log, w, config_id):
         o.append(f"Achieved: {gb_k / 1e3:.2f} TB/s ({100 * gb_k / PEAK_HBM_GBS:.1f}% of 8 TB/s) by "
                  f"the kernels' own durations; {res['value'] / 1e3:.2f} TB/s "
                  f"({100 * res['roofline']['frac']:.1f}%) by the events.")
+        if mla:
+            tf_k = w.flops() / (kern_us * 1e-6) / 1e12
+            o.append(f"Matrix-core rate: {tf_k:.1f} TFLOP/s algorithmic "
+                     f"({100 * tf_k / PEAK_BF16_TFLOPS:.1f}% of 2.5 PFLOP/s) by the kernels' "
+                     f"durations.")
         if "practical_ceiling" in res:
             pc = res["practical_ceiling"]
             o.append(f"Streaming-read ceiling measured in the same run: {pc['gbs'] / 1e3:.2f} TB/s "
@@ -524,6 +541,122 @@ def bench_prefill(args, w):
     return 0
 
 
+def cpu_baseline_mla(w, qn, qp, ckv, kpe, min_seconds=10.0):
+    """Time the float64 latent-attention oracle on the host over whole
+    requests, one after another, until min_seconds have passed; report its
+    rate in the benchmark's unit (algorithmic GB/s)."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import oracle.attention as oa
+    ctx, threads = _one_thread()
+    ch, kh = ckv.float().cpu().numpy(), kpe.float().cpu().numpy()
+    qo, L = w.qo_indptr, w.kv_lens()
+    nbytes, spent, done = 0, 0.0, 0
+    with ctx:
+        for b in range(w.batch):
+            q0, q1 = int(qo[b]), int(qo[b + 1])
+            if q1 == q0:
+                continue
+            qa, qb = qn[q0:q1].float().cpu().numpy(), qp[q0:q1].float().cpu().numpy()
+            ip = np.array([0, w.kv_indptr[b + 1] - w.kv_indptr[b]], dtype=np.int64)
+            ix = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+            t0 = time.perf_counter()
+            oa.mla_attention(qa, qb, ch, kh, np.array([0, q1 - q0]), ip, ix,
+                             w.last_page_len[b:b + 1], w.sm_scale, w.causal)
+            spent += time.perf_counter() - t0
+            nbytes += int(L[b]) * (512 + 64) * 2 + (q1 - q0) * w.num_heads * (2 * 512 + 64) * 2
+            done += 1
+            if spent >= min_seconds:
+                break
+    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(spent, 2),
+            "sample": f"the first {done} request(s) of {w.name} (whole requests, all heads), "
+                      f"numpy float64, BLAS held to {threads} host thread(s)"}
+
+
+def bench_mla(args, w):
+    """Multi-head latent attention decode: one step = fi_mla_run over the
+    batch (the tile kernel, plus the merge kernel for cut tiles). Reported as
+    achieved HBM GB/s of the algorithmic bytes (every cached latent and
+    rotary key once, q, out) against the 8 TB/s peak: at 96 heads the work
+    is 173 flop per byte, below the matrix cores' 312 flop per byte ridge."""
+    import torch
+    import block_sparse_kv_bsr_amd as fb
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    fb.lib()
+    dev = torch.device("cuda:0")
+    qn, qp, ckv, kpe = w.make_values(dev)
+    plan_t = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        p = fb.mla_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, w.num_heads,
+                        w.page_size, w.num_pool_pages, causal=w.causal,
+                        fixed_chunk_tokens=args.fixed_chunk_tokens, items_per_cu=args.items_per_cu)
+        plan_t.append(time.perf_counter() - t0)
+    ws = torch.empty(max(256, p.info["workspace_bytes"]), dtype=torch.uint8, device=dev)
+    p.upload(ws)
+    out = torch.empty((w.num_qo_tokens, w.num_heads, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.num_qo_tokens, w.num_heads), dtype=torch.float32, device=dev)
+    flush = None if args.no_flush else CacheFlush(dev)
+    if args.counters_run:
+        copy_probe(dev)
+        args.steps, args.warmup = min(args.steps, 5), 1
+
+    def step(ev):
+        if ev:
+            ev[0].record()
+        fb.mla(qn, qp, ckv, kpe, p, w.sm_scale, out=out, lse=lse, workspace=ws)
+        if ev:
+            ev[1].record()
+
+    step_ms, wall = timed_steps(step, flush, args.steps, args.warmup)
+    st = step_stats(step_ms)
+    med_ms = st["us_per_batch"] * 1e-3
+    nbytes, flops = w.algorithmic_bytes(), w.flops()
+    gbs = nbytes / (med_ms * 1e-3) / 1e9
+    tflops = flops / (med_ms * 1e-3) / 1e12
+    kernels = ["mla_attend_kernel"] + (["mla_merge_kernel"] if p.info["num_merges"] else [])
+    traffic = read_traffic(w.name, kernels)
+    result = {
+        "metric": "achieved HBM GB/s (% of MI355X peak) + µs/batch, paged latent-attention "
+                  "(MLA) decode",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(med_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "num_heads": w.num_heads,
+                   "latent_dim": 512, "rope_dim": 64, "page_size": w.page_size,
+                   "qo_tokens": w.num_qo_tokens, "kv_tokens": int(w.kv_lens().sum()),
+                   "causal": bool(w.causal), "sm_scale": w.sm_scale,
+                   "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                   "parallelism": "single-gpu", "plan_items": p.info["num_items"],
+                   "plan_merges": p.info["num_merges"], "chunk_tokens": p.info["chunk_tokens"],
+                   "l2_mall_flush_between_steps": not args.no_flush},
+        **st,
+        "timing": "median step; HIP events on the launch stream around each fi_mla_run "
+                  "(" + " + ".join(kernels) + ")",
+        "tflops_algorithmic": round(tflops, 1),
+        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "plan_host_us": round(1e6 * statistics.median(plan_t), 1),
+        "wall_s_timed_loop": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None if traffic is None else int(traffic),
+                     "kernel": " + ".join(kernels)},
+    }
+    if not args.no_cpu_baseline and not args.counters_run:
+        result["cpu_baseline"] = cpu_baseline_mla(w, qn, qp, ckv, kpe)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 # ------------------------------------------------------------------- bench
 def main():
     ap = argparse.ArgumentParser()
@@ -560,6 +693,8 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "this decode path runs on a single MI355X and has no multi-GPU mode.", flush=True)
         return 2
+    if hasattr(w, "num_heads"):
+        return bench_mla(args, w)
     if hasattr(w, "qo_indptr"):
         return bench_prefill(args, w)
 

@@ -27,6 +27,11 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 HIP_SOURCES = ["decode_bsr.hip", "decode_mma.hip", "attn_tile.hip", "merge_states.hip", "abi.hip",
                "staging.hip", "mla_attend.hip"]
 CPP_SOURCES = ["plan.cpp", "prefill_plan.cpp"]
+# Per-source device flags. The latent-attention kernel keeps its matrix
+# accumulators in ordinary vector registers (everything fits in 256): with
+# accumulation registers the compiler copied all 64 output accumulators out
+# and back around the rarely taken rescale branch on every block.
+EXTRA = {"mla_attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 BENCH_SOURCES = ["bench_stream.hip"]
 
 
@@ -46,7 +51,8 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        jobs.append([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *COMMON, *DEVICE, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src),
+                     "-o", obj])
         objs.append(obj)
     for src in CPP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")

@@ -14,32 +14,40 @@
 // request read the same cache rows, so one latent row in LDS serves them all.
 //
 // Work item: a tile of 32 (query token, head) rows of one request over one
-// chunk of its tokens (whole pages). One workgroup of 4 waves, one per SIMD;
-// each wave scores all 32 rows against every token of a block (the same
-// scores and softmax state in every wave) and owns a quarter of the output,
-// 128 latent dims. Per 32-token block and wave:
-//   S^T[token, row] = K . Q^T     v_mfma_f32_32x32x16_bf16, 36 depth steps
-//                                 (32 over the latent, 4 over the rotary key)
-//   online softmax per row (a lane owns one row: 16 tokens in the lane, the
-//   other 16 in lane l^32), running max raised lazily
-//   O^T[d, row] += V^T . P^T      2 token steps x 4 tiles of 32 dims, P split
+// chunk of its tokens (whole pages). One workgroup of 4 waves and 80 KiB of
+// LDS, so two workgroups share a CU (two waves per SIMD, independent of each
+// other). Wave w takes rows 16 (w/2) .. +15 of the tile and output dims
+// 256 (w%2) .. +255. The two waves of a row half score one 16-token tile of
+// each block each, over the full depth, and swap the raw scores through LDS,
+// so both hold the block's 32 scores per row and the same softmax state.
+// Per 32-token block and wave:
+//   S^T[token, row] = K . Q^T     v_mfma_f32_16x16x32_bf16: the wave's token
+//                                 tile x 18 depth steps (16 over the latent,
+//                                 2 over the rotary key), then the partner's
+//                                 tile from LDS
+//   online softmax per row (lane n + 16g holds row n and tokens 4g .. 4g+3 of
+//   each tile: the row's maximum is a lane-local maximum and two lane swaps;
+//   every lane keeps its own running sum), running max raised lazily
+//   O^T[d, row] += V^T . P^T      16 dim tiles x 1 token step of 32, P split
 //                                 in two bf16 parts (hi + lo) for precision
-// Lane layout of v_mfma_f32_32x32x16_bf16 (A 32x16, B 16x32, C 32x32):
-// A[m][k] in lane m + 32*(k/8), element k%8; B[k][n] in lane n + 32*(k/8);
-// C[m][n] in lane n + 32*((m%8)/4), element 4*(m/8) + m%4. P^T comes straight
-// from the S^T accumulators (the PV contraction index enumerates the block's
-// tokens in the order the S^T layout leaves them); V^T fragments come from
-// the row-major latent rows through ds_read_b64_tr_b16 (within each 16-lane
-// group, output lane 4p+q element k is element q of input lane 4k+p).
+// Lane layout of v_mfma_f32_16x16x32_bf16: A[m][k] in lane m + 16 (k/8),
+// element k%8; B[k][n] in lane n + 16 (k/8), element k%8; C[m][n] in lane
+// n + 16 (m/4), element m%4. P^T comes straight from the S^T accumulators:
+// contraction slot 8g + e is token 4g + e of tile 0 (e < 4) or 4g + e - 4 of
+// tile 1. V^T fragments come from the row-major latent rows through
+// ds_read_b64_tr_b16 (within each 16-lane group, output lane 4p+q element k
+// is element q of input lane 4k+p), two per tile: tokens 4g .. 4g+3 and
+// 16 + 4g .. +3.
 //
-// LDS ring of 4 stages of 32 tokens, filled by direct-to-LDS loads: a
-// latent row is one wave-wide 1 KiB load, placed at a row pitch of 1072
-// bytes (48 bytes of padding: 268 words, 12 banks apart, so the 16 lanes of
-// a K fragment read -- 16 rows, one 16-byte piece -- and of a transposed V
-// read -- 4 rows x 32 bytes -- fall in distinct banks, and every fragment
-// address is a lane base plus a compile-time offset); the rotary keys follow
-// as 128-byte rows, eight per wave-wide load, their 16-byte pieces
-// XOR-swizzled by (row / 2) mod 8.
+// LDS ring of 2 stages of 32 tokens, filled by direct-to-LDS loads; a
+// block's loads go out as soon as every wave is done with the stage they
+// refill, one block ahead. A latent row is one wave-wide 1 KiB load, placed
+// at a row pitch of 1072 bytes (48 bytes of padding: 268 words, 12 banks
+// apart, so the 16 lanes of a K fragment read -- 16 rows, one 16-byte piece
+// -- and of a transposed V read -- 4 rows x 32 bytes -- fall in distinct
+// banks, and every fragment address is a lane base plus a compile-time
+// offset); the rotary keys follow as 128-byte rows, eight per wave-wide
+// load, their 16-byte pieces XOR-swizzled by (row / 2) mod 8.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -54,7 +62,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -65,21 +73,25 @@ constexpr int kDc = 512;                      // latent width
 constexpr int kDr = 64;                       // rotary-key width
 constexpr int kRows = FI_MLA_ROWS;            // rows per tile
 constexpr int kWaves = 4;
-constexpr int kDw = kDc / kWaves;             // output dims per wave
+constexpr int kRw = 16;                       // rows per wave
+constexpr int kDw = kDc / 2;                  // output dims per wave
 constexpr int kBlk = 32;                      // tokens per ring stage
-constexpr int kStages = 4;
+constexpr int kStages = 2;
 constexpr int kCRow = kDc * 2 + 48;           // LDS pitch of a latent row
 constexpr int kCBytes = kBlk * kCRow;
 constexpr int kPBytes = kBlk * kDr * 2;
 constexpr int kStageBytes = kCBytes + kPBytes;
-constexpr int kSteps = (kDc + kDr) / 16;      // depth steps of the score product
-constexpr int kLoadsPerWave = kBlk / kWaves + 1;  // direct-to-LDS loads per wave and block
+constexpr int kSteps = (kDc + kDr) / 32;      // depth steps of the score product
+constexpr int kLatSteps = kDc / 32;
 constexpr int kIds = FI_PREFILL_MAX_PAGES;    // page-id window
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kMargin = 8.0f;  // lazy-rescale margin, log2 units
 static_assert(kWaves * 64 >= kIds, "one page id per thread");
-static_assert(kBlk / kWaves == 8, "a wave loads eight latent rows and eight rotary-key rows");
+static_assert(kRows == 2 * kRw, "a tile is two row halves");
+static_assert(kBlk == 8 * kWaves, "each wave loads eight rows of a block");
+static_assert(kStages * kStageBytes + kIds * 4 + kWaves * 64 * 16 <= 80 * 1024,
+              "two workgroups share a CU's LDS");
 
 struct MlaParams {
   const int32_t* items;     // [num_items][FI_QITEM_STRIDE]
@@ -121,6 +133,15 @@ __device__ __forceinline__ u32x2_t lds_tr_b64(uint32_t a) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF) : "memory");
   return r;
 }
+// LDS write of registers a matrix instruction has just written. The
+// hardware does not hold an LDS instruction back until an MFMA's results
+// are in its destination registers, and the compiler pads only its own
+// instructions for that, not inline asm: so the write waits 24 wait states
+// itself (more than the longest MFMA needs before its results may be read
+// by an LDS instruction).
+__device__ __forceinline__ void lds_w128_after_mfma(uint32_t a, u32x4_t v) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\tds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
 // One page id, read and waited for in one statement (the wait covers LDS
 // operations only; the ring's loads are counted by vmcnt).
 __device__ __forceinline__ int lds_id(const int* p) {
@@ -145,6 +166,15 @@ __device__ __forceinline__ void lgkm_wait_then(T (&r)[N]) {
   asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(CNT) : "memory");
 #pragma unroll
   for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
+}
+
+// The same for V^T fragment pairs.
+template <int CNT, int N>
+__device__ __forceinline__ void lgkm_wait_then(u32x2_t (&r)[N][2]) {
+  static_assert(CNT >= 0 && CNT < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(CNT) : "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i][0]), "+v"(r[i][1]));
 }
 
 template <int I, int N>
@@ -172,25 +202,35 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uin
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
 }
 
-__device__ __forceinline__ float max_with_partner32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+// maximum / sum over lanes l, l^16, l^32, l^48 (the four lanes of a row)
+__device__ __forceinline__ float row_max4(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float sum_with_partner32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+__device__ __forceinline__ float row_sum4(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(256, 1) void mla_attend_kernel(MlaParams p) {
+__global__ __launch_bounds__(64 * kWaves, 2) void mla_attend_kernel(MlaParams p) {
   __shared__ __attribute__((aligned(1024))) char s_ring[kStages * kStageBytes];
   __shared__ int s_pid[kIds];
+  // each wave's token tile of scores, [wave][lane] x 16 bytes
+  __shared__ __attribute__((aligned(16))) float s_x[kWaves * 64 * 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = lane >> 5;
+  const int rh = wave >> 1;   // row half
+  const int dh = wave & 1;    // output-dim half
+  const int n = lane & 15;    // this lane's row within the wave's 16
+  const int g = lane >> 4;    // 16-lane group
   const int H = p.num_heads;
-  const int d0 = kDw * wave;  // first output dim of this wave
+  const int d0 = kDw * dh;    // first output dim of this wave
 
   const int32_t* it = p.items + (int64_t)blockIdx.x * FI_QITEM_STRIDE;
   const int qo_row = it[FI_QITEM_QO_ROW];
@@ -202,9 +242,9 @@ __global__ __launch_bounds__(256, 1) void mla_attend_kernel(MlaParams p) {
   const int slot = it[FI_QITEM_SLOT];
   const int head_begin = it[FI_QITEM_HEAD_BEGIN];
 
-  // this lane's row (column n = lane % 32 of the tiles): (query token, head)
-  // number head_begin + lane % 32, token-major from the tile's first token
-  const int row = lane & 31;
+  // this lane's row: (query token, head) number head_begin + row,
+  // token-major from the tile's first token
+  const int row = kRw * rh + n;
   const int f = head_begin + row;
   const bool row_ok = f < nqo * H;
   const int qi = row_ok ? f / H : 0;
@@ -217,28 +257,31 @@ __global__ __launch_bounds__(256, 1) void mla_attend_kernel(MlaParams p) {
     // out = 0, lse = -inf, no cache read at all
     if (row_ok) {
       __bf16* dst = p.out + q_index * kDc + d0;
-      for (int d = 4 * half; d < kDw; d += 8) *reinterpret_cast<uint2*>(dst + d) = make_uint2(0u, 0u);
-      if (wave == 0 && half == 0 && p.lse) p.lse[q_index] = -INFINITY;
+      for (int d = 4 * g; d < kDw; d += 16) *reinterpret_cast<uint2*>(dst + d) = make_uint2(0u, 0u);
+      if (dh == 0 && g == 0 && p.lse) p.lse[q_index] = -INFINITY;
     }
     return;
   }
+  // a row half of padding rows loads and waits like the others but computes
+  // nothing
+  const bool rows_on = head_begin + kRw * rh < nqo * H;
 
   // ---- the chunk's pages (it starts on a page boundary; at most kIds)
   const int P = p.page_size;
   const int npg = (ntok + P - 1) / P;
   if (tid < kIds) s_pid[tid] = p.page_ids[page_begin + min(tid, npg - 1)];
 
-  // Q^T as the B operand: lane holds Q[row][16s + 8*half .. +8] for depth
-  // step s (latent part for s < 32, rotary part after); a padding row loads
-  // the tile's first row and zeroes it, so the loads are unconditional
+  // Q^T as the B operand: lane n + 16g holds Q[row n][32s + 8g .. +8] for
+  // depth step s (latent part for s < 16, rotary part after); a padding row
+  // loads the tile's first row and zeroes it, so the loads are unconditional
   bf16x8_t qf[kSteps];
   {
     const char* qn = p.q_nope + q_index * (kDc * 2);
     const char* qp = p.q_pe + q_index * (kDr * 2);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      uint4 v = s < kDc / 16 ? *reinterpret_cast<const uint4*>(qn + (16 * s + 8 * half) * 2)
-                             : *reinterpret_cast<const uint4*>(qp + (16 * (s - kDc / 16) + 8 * half) * 2);
+      uint4 v = s < kLatSteps ? *reinterpret_cast<const uint4*>(qn + (32 * s + 8 * g) * 2)
+                              : *reinterpret_cast<const uint4*>(qp + (32 * (s - kLatSteps) + 8 * g) * 2);
       if (!row_ok) v = make_uint4(0, 0, 0, 0);
       qf[s] = __builtin_bit_cast(bf16x8_t, v);
     }
@@ -252,10 +295,9 @@ __global__ __launch_bounds__(256, 1) void mla_attend_kernel(MlaParams p) {
   // 8w .. 8w+7 of the block: their rotary keys with one wave-wide load (lane
   // l: row 8w + l/8, swizzled piece l%8 from the global piece it stands
   // for), and each latent row with one wave-wide load (lane l: bytes 16l ..
-  // +15) whose pool row comes from lane 8i. Rows past the chunk's end
-  // re-read its last token (the same number of loads on every path, so the
-  // vmcnt waits are exact). The latent rows are read by every tile of the
-  // chunk, so the loads stay cacheable.
+  // +15) whose pool row comes from lane 8i (which looked up row 8w + i). The
+  // latent rows are read by every tile of the chunk, so the loads stay
+  // cacheable.
   const uint32_t pmag = p.page_magic, pmag_hi = p.page_magic_hi;
   const uint32_t psz = (uint32_t)P;
   const int my_t = 8 * wave + (lane >> 3);
@@ -269,39 +311,39 @@ __global__ __launch_bounds__(256, 1) void mla_attend_kernel(MlaParams p) {
     __builtin_amdgcn_global_load_lds((global_void_t*)(p.kpe + prow * (kDr * 2) + kslot * 16),
                                      (lds_void_t*)(stage + kCBytes + 8 * wave * (kDr * 2)), 16, 0, 0);
     const uint32_t rlo = (uint32_t)prow, rhi = (uint32_t)((uint64_t)prow >> 32);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    static_for<8>([&](auto I) {
+      constexpr int i = decltype(I)::value;
       const uint64_t r = ((uint64_t)__builtin_amdgcn_readlane(rhi, 8 * i) << 32) |
                          __builtin_amdgcn_readlane(rlo, 8 * i);
       __builtin_amdgcn_global_load_lds((global_void_t*)(p.ckv + r * (kDc * 2) + lane * 16),
                                        (lds_void_t*)(stage + (8 * wave + i) * kCRow), 16, 0, 0);
-    }
+    });
   };
 
   // LDS byte offsets that depend only on the lane. K fragment of depth step
-  // s < 32: token row lane % 32, latent piece 2s + half (lane base + 32 s);
-  // rotary steps: piece 2(s-32) + half of the swizzled 128-byte row. V^T
-  // fragment of tile t, token step ks and run r (input role: token 16 ks +
-  // 8 r + 4 (g16/2) + v_k, dims d0 + 32 t + 16 (g16%2) + 4 v_p .. +3): lane
-  // base plus (16 ks + 8 r) rows and 64 t bytes.
-  const int m = lane & 31;
-  const uint32_t kbase = m * kCRow + 16 * half;
-  uint32_t pbase[kDr / 16];
+  // s < 16 of this wave's token tile (tokens 16 dh ..): token row 16 dh + n,
+  // latent piece 4s + g (lane base + 64 s); rotary steps: piece 4(s-16) + g
+  // of the swizzled 128-byte row (one base per step). V^T fragment of dim
+  // tile td (input role: token 4g + L16/4 (+16 for the second read), dims
+  // d0 + 16 td + 4 (L16%4) .. +3): lane base + 32 td bytes (+ 16 rows).
+  const int kt = 16 * dh + n;  // this lane's token row of the K fragments
+  const uint32_t kbase = kt * kCRow + 16 * g;
+  uint32_t pbase[kSteps - kLatSteps];
 #pragma unroll
-  for (int s = 0; s < kDr / 16; ++s) pbase[s] = kCBytes + m * (kDr * 2) + 16 * ((2 * s + half) ^ ((m >> 1) & 7));
-  const int g16 = lane >> 4, L16 = lane & 15;
-  const uint32_t vbase = (4 * (g16 >> 1) + (L16 >> 2)) * kCRow + 2 * (d0 + 16 * (g16 & 1) + 4 * (L16 & 3));
+  for (int s = 0; s < kSteps - kLatSteps; ++s)
+    pbase[s] = kCBytes + kt * (kDr * 2) + 16 * ((4 * s + g) ^ ((kt >> 1) & 7));
+  const uint32_t xme = lds_u32(s_x) + 1024 * wave + 16 * lane;           // this wave's scores
+  const uint32_t xpart = lds_u32(s_x) + 1024 * (wave ^ 1) + 16 * lane;   // the partner's
+  const int L16 = lane & 15;
+  const uint32_t vbase = (4 * g + (L16 >> 2)) * kCRow + 2 * (d0 + 4 * (L16 & 3));
 
-  f32x16_t o[kDw / 32];
+  f32x4_t o[kDw / 16];
 #pragma unroll
-  for (int t = 0; t < kDw / 32; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int t = 0; t < kDw / 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;  // l_run: this lane's share of the row sum
 
   const int nblocks = (ntok + kBlk - 1) / kBlk;
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue(s, s);
+  issue(0, 0);
 
   // Scores stay unscaled; exp2(c * s - c * m) is one fma and an exp. The
   // running max is raised only when a block's max passes it by more than
@@ -312,163 +354,172 @@ __global__ __launch_bounds__(256, 1) void mla_attend_kernel(MlaParams p) {
   const uint32_t ring = lds_u32(s_ring);
 
   for (int j = 0; j < nblocks; ++j) {
-    const int st = j % kStages;
-    // this wave's loads of block j have landed (later blocks may be in flight)
-    wait_vmcnt<kLoadsPerWave * (kStages - 2)>();
+    const int st = j & 1;
+    // this wave's loads of block j have landed
+    wait_vmcnt<0>();
     // every wave's loads of block j have landed, and every wave is done
-    // reading block j-1, whose stage is refilled below
+    // reading block j-1, whose stage the next block's loads refill now
     __builtin_amdgcn_s_barrier();
+    if (j + 1 < nblocks) issue(j + 1, st ^ 1);
+    if (!rows_on) {
+      __builtin_amdgcn_s_barrier();  // the score swap's barrier, kept in step
+      continue;
+    }
     const uint32_t sb = ring + st * kStageBytes;
 
-    // ---- S^T = K . Q^T: 36 depth steps, fragments read in groups of 4,
-    // the next group requested before the current one's products
-    f32x16_t sc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-    u32x4_t kf[2][4];
-    auto read_group = [&](auto G, u32x4_t(&dst)[4]) {
-      constexpr int g = decltype(G)::value;
-      if constexpr (g < kDc / 64) {
-        dst[0] = lds_b128<32 * (4 * g + 0)>(sb + kbase);
-        dst[1] = lds_b128<32 * (4 * g + 1)>(sb + kbase);
-        dst[2] = lds_b128<32 * (4 * g + 2)>(sb + kbase);
-        dst[3] = lds_b128<32 * (4 * g + 3)>(sb + kbase);
-      } else {
-        dst[0] = lds_b128<0>(sb + pbase[0]);
-        dst[1] = lds_b128<0>(sb + pbase[1]);
-        dst[2] = lds_b128<0>(sb + pbase[2]);
-        dst[3] = lds_b128<0>(sb + pbase[3]);
-      }
+    // ---- S^T = K . Q^T for this wave's 16-token tile, 18 depth steps;
+    // fragments read six steps at a time, the next group requested before
+    // the current group's products
+    f32x4_t sme = {0.f, 0.f, 0.f, 0.f};
+    u32x4_t kf[2][6];
+    auto read_group = [&](auto G, u32x4_t(&dst)[6]) {
+      constexpr int gi = decltype(G)::value;
+      static_for<6>([&](auto I) {
+        constexpr int s = 6 * gi + decltype(I)::value;
+        if constexpr (s < kLatSteps)
+          dst[decltype(I)::value] = lds_b128<64 * s>(sb + kbase);
+        else
+          dst[decltype(I)::value] = lds_b128<0>(sb + pbase[s - kLatSteps]);
+      });
     };
     read_group(std::integral_constant<int, 0>{}, kf[0]);
-    static_for<kSteps / 4>([&](auto G) {
-      constexpr int g = decltype(G)::value;
-      if constexpr (g + 1 < kSteps / 4) {
-        read_group(std::integral_constant<int, g + 1>{}, kf[(g + 1) & 1]);
-        lgkm_wait_then<4>(kf[g & 1]);
+    static_for<kSteps / 6>([&](auto G) {
+      constexpr int gi = decltype(G)::value;
+      if constexpr (gi + 1 < kSteps / 6) {
+        read_group(std::integral_constant<int, gi + 1>{}, kf[(gi + 1) & 1]);
+        lgkm_wait_then<6>(kf[gi & 1]);
       } else {
-        lgkm_wait_then<0>(kf[g & 1]);
+        lgkm_wait_then<0>(kf[gi & 1]);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[g & 1][i]),
-                                                     qf[4 * g + i], sc, 0, 0, 0);
-    });
-
-    // the loads of a later block go out while the products run
-    issue(j + kStages - 1, (j + kStages - 1) % kStages);
-
-    // ---- V^T fragments of both 16-token steps, requested now so that they
-    // arrive during the softmax step below
-    u32x2_t va[2][kDw / 32][2];
-    static_for<2>([&](auto KS) {
-      constexpr int ks = decltype(KS)::value;
-      static_for<kDw / 32>([&](auto T) {
-        constexpr int t = decltype(T)::value;
-        va[ks][t][0] = lds_tr_b64<(16 * ks) * kCRow + 64 * t>(sb + vbase);
-        va[ks][t][1] = lds_tr_b64<(16 * ks + 8) * kCRow + 64 * t>(sb + vbase);
+      static_for<6>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        sme = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[gi & 1][i]),
+                                                      qf[6 * gi + i], sme, 0, 0, 0);
       });
     });
+    // swap tiles with the partner wave of the row half (same lanes, same
+    // rows): after the barrier both waves hold the block's 32 scores
+    lds_w128_after_mfma(xme, u32x4_t{__float_as_uint(sme[0]), __float_as_uint(sme[1]),
+                                     __float_as_uint(sme[2]), __float_as_uint(sme[3])});
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    f32x4_t sc[2];
+    {
+      u32x4_t xo[1];
+      xo[0] = lds_b128<0>(xpart);
+      lgkm_wait_then<0>(xo);
+      const f32x4_t spart = {__uint_as_float(xo[0][0]), __uint_as_float(xo[0][1]), __uint_as_float(xo[0][2]),
+                             __uint_as_float(xo[0][3])};
+      sc[0] = dh == 0 ? sme : spart;
+      sc[1] = dh == 0 ? spart : sme;
+    }
 
-    // ---- online softmax over the block; element r holds token
-    // 4*half + 8*(r/4) + r%4 of the block
+    // ---- V^T fragments of the first four dim tiles, requested now so that
+    // they arrive during the softmax step below
+    u32x2_t va[2][4][2];
+    auto read_v = [&](auto H4, u32x2_t(&dst)[4][2]) {
+      constexpr int h4 = decltype(H4)::value;
+      static_for<4>([&](auto T) {
+        constexpr int td = 4 * h4 + decltype(T)::value;
+        dst[decltype(T)::value][0] = lds_tr_b64<32 * td>(sb + vbase);
+        dst[decltype(T)::value][1] = lds_tr_b64<16 * kCRow + 32 * td>(sb + vbase);
+      });
+    };
+    read_v(std::integral_constant<int, 0>{}, va[0]);
+
+    // ---- online softmax over the block; element e of tile tt holds token
+    // 16 tt + 4g + e of the block
     const int tok0 = j * kBlk;
     if (__builtin_amdgcn_ballot_w64(tok0 + kBlk > lim)) {  // some row stops in here
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (tok0 + 4 * half + 8 * (r >> 2) + (r & 3) >= lim) sc[r] = -INFINITY;
-    }
-    float mb = sc[0];
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mb = fmaxf(mb, sc[r]);
-    mb = max_with_partner32(mb);  // -inf if the row attends none of these tokens
+        for (int e = 0; e < 4; ++e)
+          if (tok0 + 16 * tt + 4 * g + e >= lim) sc[tt][e] = -INFINITY;
+    }
+    float mb = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mb = row_max4(mb);  // -inf if the row attends none of these tokens
     const bool up = mb > m_run + margin;
     if (__builtin_amdgcn_ballot_w64(up)) {
       const float alpha = up ? __builtin_amdgcn_exp2f((m_run - mb) * c) : 1.f;  // 0 at first
       l_run *= alpha;
       if (j > 0) {  // the accumulators are still zero on the first block
 #pragma unroll
-        for (int t = 0; t < kDw / 32; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        for (int t = 0; t < kDw / 16; ++t) o[t] *= alpha;
       }
       m_run = up ? mb : m_run;
     }
     // a row with no token yet has m = -inf and only masked scores: weight 0
     const float mc = m_run == -INFINITY ? 0.f : m_run * c;
 
-    lgkm_wait_then<0>(va[0][0]);
-    lgkm_wait_then<0>(va[0][1]);
-    lgkm_wait_then<0>(va[0][2]);
-    lgkm_wait_then<0>(va[0][3]);
-    lgkm_wait_then<0>(va[1][0]);
-    lgkm_wait_then<0>(va[1][1]);
-    lgkm_wait_then<0>(va[1][2]);
-    lgkm_wait_then<0>(va[1][3]);
-
-    // ---- P = exp2(c s - c m), then O^T += V^T . P^T. Step ks takes
-    // elements 8ks .. 8ks+7: contraction index 8*half + i is token
-    // 4*half + 16ks + 8*(i/4) + i%4 of the block. P is multiplied as two
-    // bf16 parts, hi = P rounded to bf16 and lo = the rounding error rounded
-    // again: P alone in bf16 carries a relative error up to 2^-8, which a row
-    // that attends few tokens does not average away.
-    float ps = 0.f;
+    // ---- P^T = exp2(c s - c m) as hi + lo bf16 parts (P alone in bf16
+    // carries a relative error up to 2^-8, which a row that attends few
+    // tokens does not average away), then O^T += V^T . P^T
+    float pv[8];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint32_t phw[4], plw[4];
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[8 * ks + 2 * i], c, -mc));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[8 * ks + 2 * i + 1], c, -mc));
-        ps += e0 + e1;
-        split_bf16x2(e0, e1, phw[i], plw[i]);
-      }
-      const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, u32x4_t{phw[0], phw[1], phw[2], phw[3]});
-      const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, u32x4_t{plw[0], plw[1], plw[2], plw[3]});
-      bf16x8_t vfr[kDw / 32];
+      for (int e = 0; e < 4; ++e) pv[4 * tt + e] = __builtin_amdgcn_exp2f(fmaf(sc[tt][e], c, -mc));
+    uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int t = 0; t < kDw / 32; ++t)
-        vfr[t] = __builtin_bit_cast(bf16x8_t, u32x4_t{va[ks][t][0][0], va[ks][t][0][1],
-                                                      va[ks][t][1][0], va[ks][t][1][1]});
-#pragma unroll
-      for (int t = 0; t < kDw / 32; ++t) o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[t], ph, o[t], 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < kDw / 32; ++t) o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[t], pl, o[t], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      l_run += pv[2 * i] + pv[2 * i + 1];
+      split_bf16x2(pv[2 * i], pv[2 * i + 1], hw[i], lw[i]);
     }
-    l_run += sum_with_partner32(ps);
+    const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, u32x4_t{hw[0], hw[1], hw[2], hw[3]});
+    const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, u32x4_t{lw[0], lw[1], lw[2], lw[3]});
+    // four groups of four dim tiles, the next group's fragments requested
+    // before the current group's products
+    static_for<kDw / 64>([&](auto H4) {
+      constexpr int h4 = decltype(H4)::value;
+      if constexpr (h4 + 1 < kDw / 64) {
+        read_v(std::integral_constant<int, h4 + 1>{}, va[(h4 + 1) & 1]);
+        lgkm_wait_then<8>(va[h4 & 1]);
+      } else {
+        lgkm_wait_then<0>(va[h4 & 1]);
+      }
+      bf16x8_t vt[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        vt[t] = __builtin_bit_cast(bf16x8_t, u32x4_t{va[h4 & 1][t][0][0], va[h4 & 1][t][0][1],
+                                                     va[h4 & 1][t][1][0], va[h4 & 1][t][1][1]});
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        o[4 * h4 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[t], ph, o[4 * h4 + t], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        o[4 * h4 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[t], pl, o[4 * h4 + t], 0, 0, 0);
+    });
   }
-  // loads past the end may still be landing in the ring
+  // the last block's loads may still be landing in the ring
   wait_vmcnt<0>();
 
-  // ---- this row's state over the wave's 128 dims: o / l and lse; a row
+  // ---- this row's state over the wave's 256 dims: o / l and lse; a row
   // that attended nothing has o = 0 and lse = -inf
   if (!row_ok) return;
-  const bool empty = l_run == 0.f;
-  const float inv = empty ? 0.f : 1.f / l_run;
-  const float lse2 = empty ? -INFINITY : m_run * c + __builtin_amdgcn_logf(l_run);
+  const float l_tot = row_sum4(l_run);
+  const bool empty = l_tot == 0.f;
+  const float inv = empty ? 0.f : 1.f / l_tot;
+  const float lse2 = empty ? -INFINITY : m_run * c + __builtin_amdgcn_logf(l_tot);
+  // lane n + 16g holds O^T[16 td + 4g + e][n], e = 0 .. 3
   if (slot < 0) {
-    __bf16* dst = p.out + q_index * kDc + d0;
+    __bf16* dst = p.out + q_index * kDc + d0 + 4 * g;
 #pragma unroll
-    for (int t = 0; t < kDw / 32; ++t)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        // elements 4*q4 .. +3 are dims 32t + 8*q4 + 4*half .. +3
-        const bf16x4_t v = {(__bf16)(o[t][4 * q4] * inv), (__bf16)(o[t][4 * q4 + 1] * inv),
-                            (__bf16)(o[t][4 * q4 + 2] * inv), (__bf16)(o[t][4 * q4 + 3] * inv)};
-        *reinterpret_cast<bf16x4_t*>(dst + 32 * t + 8 * q4 + 4 * half) = v;
-      }
-    if (wave == 0 && half == 0 && p.lse) p.lse[q_index] = lse2 * kLn2;
+    for (int t = 0; t < kDw / 16; ++t) {
+      const bf16x4_t v = {(__bf16)(o[t][0] * inv), (__bf16)(o[t][1] * inv), (__bf16)(o[t][2] * inv),
+                          (__bf16)(o[t][3] * inv)};
+      *reinterpret_cast<bf16x4_t*>(dst + 16 * t) = v;
+    }
+    if (dh == 0 && g == 0 && p.lse) p.lse[q_index] = lse2 * kLn2;
     return;
   }
-  float* dst = p.part_o + ((int64_t)slot * kRows + row) * kDc + d0;
+  float* dst = p.part_o + ((int64_t)slot * kRows + row) * kDc + d0 + 4 * g;
 #pragma unroll
-  for (int t = 0; t < kDw / 32; ++t)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<float4*>(dst + 32 * t + 8 * q4 + 4 * half) =
-          make_float4(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv, o[t][4 * q4 + 2] * inv,
-                      o[t][4 * q4 + 3] * inv);
-  if (wave == 0 && half == 0) p.part_lse[(int64_t)slot * kRows + row] = lse2;
+  for (int t = 0; t < kDw / 16; ++t)
+    *reinterpret_cast<float4*>(dst + 16 * t) =
+        make_float4(o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv);
+  if (dh == 0 && g == 0) p.part_lse[(int64_t)slot * kRows + row] = lse2;
 }
 
 // Folds the chunk states of cut tiles (log2-unit lse) into bf16 out and

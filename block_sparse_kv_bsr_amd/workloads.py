@@ -394,6 +394,8 @@ def workload(config_id: int) -> Workload:
         return _composed_prefix(seed)
     if config_id in (7, 8, 12, 14):
         return prefill_workload(config_id)
+    if config_id == 15:
+        return mla_workload(config_id)
     if config_id == 9:  # the skewed batch, K stored before the rotary embedding
         w = workload(3)
         return dataclasses.replace(w, name=CONFIG_NAMES[9], config_id=9, value_seed=seed,

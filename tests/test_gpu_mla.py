@@ -70,6 +70,8 @@ CASES = [
     (8, 3, 260, 1, 16, 5, True, 48),       # one head
     (9, 4, 333, 32, 3, 1, True, 0),        # page size 3
     (10, 2, 40, 64, 16, 2, True, 0),       # short histories (a row attends one block)
+    (11, 3, 150, 200, 16, 1, True, 48),    # six blocks of 32 heads and one of 8
+    (12, 4, 120, 24, 16, 3, True, 0),      # a tile of one whole token (24 rows of 32)
 ]
 
 

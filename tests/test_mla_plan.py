@@ -113,7 +113,8 @@ CASES = [
     # seed, batch, max_len, heads, page size, max query tokens, causal, fixed chunk
     (1, 3, 300, 96, 16, 1, True, 64),     # three head blocks, cut tiles
     (2, 4, 200, 12, 4, 3, True, 32),      # two tokens per tile, speculative queries
-    (3, 3, 150, 40, 1, 2, True, 17),      # a 32 + 8 head split, page size 1
+    (3, 3, 150, 40, 1, 2, True, 17),      # a tile across token boundaries, page size 1
+    (6, 3, 150, 200, 16, 2, True, 48),    # six blocks of 32 heads and one of 8
     (4, 2, 90, 5, 64, 4, False, 0),       # six tokens per tile, no mask
     (5, 3, 400, 128, 16, 1, True, 0),     # planner's own chunk length
 ]
@@ -141,11 +142,11 @@ def test_full_size_mla_workload_plans():
     p = make(w)
     check_plan(w, p)
     info = p.info
-    # 96 heads: three tiles per request; long requests cut into chunks of
-    # at least 1024 tokens
+    # 96 heads: three tiles of 32 heads per request; long requests cut into
+    # chunks of at least 1024 tokens
     assert info["num_tiles"] == 3 * w.batch
     assert info["chunk_tokens"] >= 1024 and info["num_items"] >= 2 * 256
-    # the workspace's partial states: 32 rows x 512 floats per slot
+    # the workspace's partial states: FI_MLA_ROWS rows x 512 floats per slot
     assert info["workspace_bytes"] >= info["num_partial_slots"] * R * 512 * 4
 
 
