@@ -241,8 +241,9 @@ def summarize_trace(stats_csv, bench_log, w, config_id):
             alg = w.algorithmic_bytes()
             o.append(f"\nHBM traffic per step ({os.path.basename(cf)}, sources "
                      f"{vals['source_sha256_16']}): FETCH {fb_:.4g} B, WRITE {wb_:.4g} B; "
-                     f"together {(fb_ + wb_) / alg:.3f}x the algorithmic bytes (reads of K, V "
-                     f"and q plus writes of the output).")
+                     f"together {(fb_ + wb_) / alg:.3f}x the algorithmic bytes ("
+                     + ("reads of the latents, rotary keys and q plus writes of the output"
+                        if mla else "reads of K, V and q plus writes of the output") + ").")
     o.append(f"\nKernel sources sha256[:16]: {source_digest(kernels)}.")
     with open(path, "w") as f:
         f.write("\n".join(o) + "\n")
