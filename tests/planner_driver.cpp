@@ -121,7 +121,7 @@ uint64_t decode_call(const int32_t* hdr, const std::vector<int32_t>& opts, const
 }
 
 uint64_t prefill_call(const int32_t* hdr, const std::vector<int32_t>& opts, const Array& qo,
-                      const Array& ip, const Array& ix, const Array& lp, int* status) {
+                      const Array& ip, const Array& ix, const Array& lp, bool mla, int* status) {
   fi_prefill_opts o{};
   const fi_prefill_opts* po = nullptr;
   if (!opts.empty()) {
@@ -133,8 +133,12 @@ uint64_t prefill_call(const int32_t* hdr, const std::vector<int32_t>& opts, cons
     po = &o;
   }
   fi_prefill_plan* p = nullptr;
-  *status = fi_prefill_plan_create(qo.ptr(), ip.ptr(), ix.ptr(), lp.ptr(), hdr[0], hdr[1], hdr[2],
-                                   hdr[3], hdr[4], hdr[5], (fi_dtype)hdr[6], hdr[7], po, &p);
+  // MLA: hdr = batch, heads, latent width, rotary width, page size, pool, -, causal
+  *status = mla ? fi_mla_plan_create(qo.ptr(), ip.ptr(), ix.ptr(), lp.ptr(), hdr[0], hdr[1], hdr[2],
+                                     hdr[3], hdr[4], hdr[5], hdr[7], po, &p)
+                : fi_prefill_plan_create(qo.ptr(), ip.ptr(), ix.ptr(), lp.ptr(), hdr[0], hdr[1],
+                                         hdr[2], hdr[3], hdr[4], hdr[5], (fi_dtype)hdr[6], hdr[7],
+                                         po, &p);
   Hash h;
   h.mix(*status);
   if (*status != FI_OK) return h.h;
@@ -166,7 +170,8 @@ int main() {
     std::vector<int32_t> opts(n_opts);
     for (int32_t& x : opts)
       if (!(std::cin >> x)) return 2;
-    const bool prefill = kind == "P", composed = kind == "C";
+    const bool mla = kind == "M";
+    const bool prefill = kind == "P" || mla, composed = kind == "C";
     if ((prefill && n_opts != 0 && n_opts != 4 && n_opts != 5) ||
         (!prefill && n_opts != 0 && n_opts != 7 && n_opts != 8))
       return 2;
@@ -181,7 +186,7 @@ int main() {
         return 2;
     }
     int status = 0;
-    const uint64_t h = prefill ? prefill_call(hdr, opts, qo, ip, ix, lp, &status)
+    const uint64_t h = prefill ? prefill_call(hdr, opts, qo, ip, ix, lp, mla, &status)
                                : decode_call(hdr, opts, ip, ix, lp, composed ? &pre : nullptr,
                                              &status);
     std::printf("%d %d %llu\n", index, status, (unsigned long long)h);

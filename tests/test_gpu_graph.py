@@ -161,3 +161,19 @@ def test_graph_prefill_fp8_cache():
 def test_graph_prefill_rope():
     _prefill_graph(random_prefill_workload(107, 3, 900, 8, 2, 128, 16, causal=True,
                                            rope_theta=5e5), "prefill rope")
+
+
+def test_graph_mla():
+    """MLA decode (tile kernel + merge of cut tiles) captured and replayed."""
+    from block_sparse_kv_bsr_amd.workloads import random_mla_workload
+    w = random_mla_workload(108, 4, 900, 96, 16, max_qo=2)
+    qn, qp, ckv, kpe = (t.cuda() for t in w.make_values("cpu"))
+    p = fb.mla_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, w.num_heads,
+                    w.page_size, w.num_pool_pages, fixed_chunk_tokens=128)
+    assert p.info["num_merges"] > 0
+    ws = torch.empty(p.info["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    p.upload(ws)
+    out = torch.empty((w.num_qo_tokens, w.num_heads, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.num_qo_tokens, w.num_heads), dtype=torch.float32, device="cuda")
+    _replays(lambda: fb.mla(qn, qp, ckv, kpe, p, w.sm_scale, out=out, lse=lse, workspace=ws),
+             [qn], [out, lse], [torch.randn_like(qn)], "mla")

@@ -22,7 +22,7 @@ import pytest
 
 import block_sparse_kv_bsr_amd as fb
 from block_sparse_kv_bsr_amd import binding
-from block_sparse_kv_bsr_amd.workloads import prefill_workload, workload
+from block_sparse_kv_bsr_amd.workloads import mla_workload, prefill_workload, workload
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "block_sparse_kv_bsr_amd", "csrc")
@@ -46,7 +46,9 @@ def driver(tmp_path_factory):
 
 # ------------------------------------------------------------------ cases
 class Call:
-    """One planner call: kind 'D' (fi_plan_create) or 'P' (prefill)."""
+    """One planner call: kind 'D' (fi_plan_create), 'P' (prefill), 'C'
+    (composed) or 'M' (MLA: hq = heads, hkv = latent width, d = rotary
+    width)."""
 
     def __init__(self, kind, batch, hq, hkv, d, P, pool, dtype, ip, ix, lp, opts=None, qo=None,
                  causal=1, prefixes=None):
@@ -64,7 +66,7 @@ class Call:
             return " ".join(map(str, [len(a)] + a))
         parts = [self.kind, " ".join(map(str, self.hdr))]
         parts.append(arr(self.opts) if self.opts is not None else "0")
-        if self.kind == "P":
+        if self.kind in ("P", "M"):
             parts.append(arr(self.qo))
         parts += [arr(self.ip), arr(self.ix), arr(self.lp)]
         if self.kind == "C":
@@ -111,6 +113,14 @@ def malformed_calls():
         a.update(kw)
         out.append(Call("P", 2, a["hq"], a["hkv"], a["d"], a["P"], a["pool"], a["dtype"], a["ip"],
                         a["ix"], a["lp"], a["opts"], a["qo"], a["causal"]))
+    mla = [dict(hkv=576), dict(d=128), dict(hq=0), dict(hq=5000), dict(opts=[0, 0, 0, 0, 1]),
+           dict(qo=[0, 40, 41]), dict(ix=[5, 6, 700]), dict(qo=None), dict(opts=[0, -2, 0, 0])]
+    for kw in mla:
+        a = dict(qo=[0, 2, 3], ip=[0, 2, 3], ix=[5, 6, 7], lp=[16, 3], hq=96, hkv=512, d=64, P=16,
+                 pool=100, causal=1, opts=None)
+        a.update(kw)
+        out.append(Call("M", 2, a["hq"], a["hkv"], a["d"], a["P"], a["pool"], 1, a["ip"], a["ix"],
+                        a["lp"], a["opts"], a["qo"], a["causal"]))
     comp = [dict(of=[0, 2]), dict(of=[-2, 0]), dict(of=None), dict(pix=[4, 1, 10]),
             dict(plp=[70, 5]), dict(plp=[0, 5]), dict(Pp=0), dict(Pp=5000), dict(dtype=2),
             dict(pip=None), dict(pip=[1, 2, 3]), dict(pip=[0, 2, 1]), dict(ppool=-1),
@@ -216,6 +226,20 @@ def random_calls(seed=7, n_decode=160, n_prefill=100):
                     int(rng.choice([0, 16, 300])), 0, int(rng.choice([0, 1, 100])), 0, 0]
         out.append(Call("C", B, G * hkv, hkv, int(rng.choice([64, 128])), P, pool, 1, ip, ix, lp,
                         opts, prefixes=(Pp, ppool, pip, pix, plp, of)))
+    for i in range(60):
+        B = int(rng.integers(1, 7))
+        P = int(rng.choice(sizes))
+        lens = [int(x) for x in rng.integers(0, 900, size=B)]
+        causal = int(rng.random() < 0.8)
+        qo = [int(rng.integers(0, min(L, 6) + 1)) if causal else int(rng.integers(0, 5)) for L in lens]
+        H = int(rng.choice([1, 5, 12, 16, 32, 40, 96, 128, 200]))
+        ip, ix, lp, pool = _page_table(rng, lens, P, int(rng.integers(0, 4)))
+        opts = None
+        if rng.random() < 0.7:
+            opts = [int(rng.choice([0, 8, 256])), int(rng.choice([0, 1, 4])),
+                    int(rng.choice([0, 0, 16, 64, 1000])), int(rng.choice([0, 1, 8]))]
+        qoi = np.concatenate([[0], np.cumsum(qo)]).tolist()
+        out.append(Call("M", B, H, 512, 64, P, pool, 1, ip, ix, lp, opts, qoi, causal))
     return out
 
 
@@ -231,6 +255,9 @@ def full_size_calls():
                     w.num_pool_pages, 1, w.kv_indptr, w.kv_indices, w.last_page_len,
                     prefixes=(w.prefix_page_size, w.num_prefix_pool_pages, w.prefix_indptr,
                               w.prefix_indices, w.prefix_last_page_len, w.prefix_of)))
+    w = mla_workload(15)
+    out.append(Call("M", w.batch, w.num_heads, 512, 64, w.page_size, w.num_pool_pages, 1,
+                    w.kv_indptr, w.kv_indices, w.last_page_len, None, w.qo_indptr, int(w.causal)))
     for cfg in (7, 8):
         w = prefill_workload(cfg)
         out.append(Call("P", w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
@@ -273,6 +300,10 @@ def regular_line(call: Call):
         opts = ctypes.byref(binding.PlanOpts(*call.opts)) if call.opts is not None else None
         st = L.fi_plan_create(ptrs[1], ptrs[2], ptrs[3], b, hq, hkv, d, P, pool, dtype, opts,
                               ctypes.byref(h))
+    elif call.kind == "M":
+        opts = ctypes.byref(binding.PrefillOpts(*call.opts)) if call.opts is not None else None
+        st = L.fi_mla_plan_create(ptrs[0], ptrs[1], ptrs[2], ptrs[3], b, hq, hkv, d, P, pool,
+                                  causal, opts, ctypes.byref(h))
     else:
         opts = ctypes.byref(binding.PrefillOpts(*call.opts)) if call.opts is not None else None
         st = L.fi_prefill_plan_create(ptrs[0], ptrs[1], ptrs[2], ptrs[3], b, hq, hkv, d, P, pool,
