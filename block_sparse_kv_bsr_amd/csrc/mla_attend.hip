@@ -526,7 +526,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void mla_attend_kernel(MlaParams p)
 // natural-log lse: the closed form of softmax over a disjoint union of token
 // sets (FlashInfer paper explainer, visionhong.com, benchmark section: the
 // split scheduler's pieces are merged). A thread per (row, 4 dims), two rows
-// per workgroup; the chunks are summed in slot order.
+// per workgroup; the chunks are summed in slot order in one pass.
 __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams p) {
   const int32_t* mg = p.merges + (int64_t)blockIdx.x * FI_QMERGE_STRIDE;
   const int r = blockIdx.y * 2 + (threadIdx.x >> 7);
@@ -539,23 +539,44 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams p) {
   const int k = mg[FI_QMERGE_NUM_CHUNKS];
   const int c4 = 4 * (threadIdx.x & 127);
   const float* lse_r = p.part_lse + slot0 * kRows + r;
-  float mx = -INFINITY;
-  for (int ch = 0; ch < k; ++ch) mx = fmaxf(mx, lse_r[(int64_t)ch * kRows]);
+  const float* o_r = p.part_o + (slot0 * kRows + r) * kDc + c4;
+  // one pass in chunk order, eight chunks' loads in flight at a time, the
+  // running maximum raised per group of eight (a chunk the row attended
+  // nothing of has s = -inf and weight 0)
+  float mx = -INFINITY, den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
-  if (mx != -INFINITY) {
-#pragma unroll 4
-    for (int ch = 0; ch < k; ++ch) {
-      const float s = lse_r[(int64_t)ch * kRows];
-      // a chunk the row attended nothing of has s = -inf and weight 0
-      const float w = s == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s - mx);
-      const float4 v = *reinterpret_cast<const float4*>(p.part_o + ((slot0 + ch) * kRows + r) * kDc + c4);
-      den += w;
-      acc.x += w * v.x;
-      acc.y += w * v.y;
-      acc.z += w * v.z;
-      acc.w += w * v.w;
+  for (int c0 = 0; c0 < k; c0 += 8) {
+    const int nb = min(8, k - c0);
+    float s[8];
+    float4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t ch = c0 + min(i, nb - 1);  // the tail re-reads the group's last chunk
+      s[i] = lse_r[ch * kRows];
+      v[i] = *reinterpret_cast<const float4*>(o_r + ch * kRows * kDc);
     }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < nb) bm = fmaxf(bm, s[i]);
+    const float mn = fmaxf(mx, bm);
+    if (mn == -INFINITY) continue;
+    const float a = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - mn);
+    den *= a;
+    acc.x *= a;
+    acc.y *= a;
+    acc.z *= a;
+    acc.w *= a;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float w = (i >= nb || s[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[i] - mn);
+      den += w;
+      acc.x += w * v[i].x;
+      acc.y += w * v[i].y;
+      acc.z += w * v[i].z;
+      acc.w += w * v[i].w;
+    }
+    mx = mn;
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const bf16x4_t v = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv),
