@@ -42,12 +42,11 @@
 // LDS ring of 2 stages of 32 tokens, filled by direct-to-LDS loads; a
 // block's loads go out as soon as every wave is done with the stage they
 // refill, one block ahead. A latent row is one wave-wide 1 KiB load, placed
-// at a row pitch of 1072 bytes (48 bytes of padding: 268 words, 12 banks
-// apart, so the 16 lanes of a K fragment read -- 16 rows, one 16-byte piece
-// -- and of a transposed V read -- 4 rows x 32 bytes -- fall in distinct
-// banks, and every fragment address is a lane base plus a compile-time
-// offset); the rotary keys follow as 128-byte rows, eight per wave-wide
-// load, their 16-byte pieces XOR-swizzled by (row / 2) mod 8.
+// at a row pitch of 1072 bytes (48 bytes of padding, 268 words) in a
+// permuted row order (lds_row), so K fragment reads and transposed V reads
+// are free of bank conflicts and every fragment address is a lane base plus
+// a compile-time offset; the rotary keys follow as 128-byte rows, eight per
+// wave-wide load, their 16-byte pieces XOR-swizzled by (row / 2) mod 8.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -114,6 +113,14 @@ struct MlaParams {
 };
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// LDS row of token t of a block: within each 16-token half, tokens 0..7 take
+// the even rows and 8..15 the odd ones. At a pitch of 268 words (12 banks mod
+// 64) the 16 rows a K fragment read touches (one half) still fall on 16
+// distinct 4-bank slots, and the 8 rows a transposed V read of two 16-lane
+// groups touches (8 consecutive tokens) on rows 8 banks apart, so neither
+// read conflicts on 64 banks.
+__device__ __forceinline__ constexpr int lds_row(int t) { return (t & ~15) | ((t & 7) << 1) | ((t >> 3) & 1); }
 
 // LDS reads at a lane address plus a compile-time offset (the instruction's
 // offset field), as inline asm: the compiler cannot tell which ring stage a
@@ -316,7 +323,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void mla_attend_kernel(MlaParams p)
       const uint64_t r = ((uint64_t)__builtin_amdgcn_readlane(rhi, 8 * i) << 32) |
                          __builtin_amdgcn_readlane(rlo, 8 * i);
       __builtin_amdgcn_global_load_lds((global_void_t*)(p.ckv + r * (kDc * 2) + lane * 16),
-                                       (lds_void_t*)(stage + (8 * wave + i) * kCRow), 16, 0, 0);
+                                       (lds_void_t*)(stage + lds_row(8 * wave + i) * kCRow), 16, 0, 0);
     });
   };
 
@@ -326,8 +333,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void mla_attend_kernel(MlaParams p)
   // of the swizzled 128-byte row (one base per step). V^T fragment of dim
   // tile td (input role: token 4g + L16/4 (+16 for the second read), dims
   // d0 + 16 td + 4 (L16%4) .. +3): lane base + 32 td bytes (+ 16 rows).
-  const int kt = 16 * dh + n;  // this lane's token row of the K fragments
-  const uint32_t kbase = kt * kCRow + 16 * g;
+  const int kt = 16 * dh + n;  // this lane's token of the K fragments
+  const uint32_t kbase = lds_row(kt) * kCRow + 16 * g;
   uint32_t pbase[kSteps - kLatSteps];
 #pragma unroll
   for (int s = 0; s < kSteps - kLatSteps; ++s)
@@ -335,7 +342,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void mla_attend_kernel(MlaParams p)
   const uint32_t xme = lds_u32(s_x) + 1024 * wave + 16 * lane;           // this wave's scores
   const uint32_t xpart = lds_u32(s_x) + 1024 * (wave ^ 1) + 16 * lane;   // the partner's
   const int L16 = lane & 15;
-  const uint32_t vbase = (4 * g + (L16 >> 2)) * kCRow + 2 * (d0 + 4 * (L16 & 3));
+  // (the second read's tokens are 16 later: lds_row adds 16 rows)
+  const uint32_t vbase = lds_row(4 * g + (L16 >> 2)) * kCRow + 2 * (d0 + 4 * (L16 & 3));
 
   f32x4_t o[kDw / 16];
 #pragma unroll
