@@ -74,3 +74,35 @@ def test_prefill_pool_beyond_4gib():
     compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE, True, "prefill >4 GiB")
     del k_big, v_big
     torch.cuda.empty_cache()
+
+
+def test_mla_pool_beyond_4gib():
+    """The latent pool (1 KiB per token) past 4 GiB: every listed page but
+    one sits above the 4 GiB mark of the latent pool."""
+    from block_sparse_kv_bsr_amd.workloads import random_mla_workload
+    P = 16
+    page = P * 512 * 2
+    pool = (5 << 30) // page + 7
+    w = random_mla_workload(113, 4, 700, 40, P, max_qo=2)
+    qn, qp, ckv, kpe = (t.cuda() for t in w.make_values("cpu"))
+    used = np.unique(w.kv_indices)
+    rng = np.random.default_rng(8)
+    low = (4 << 30) // page + 1
+    new_ids = np.concatenate([[5], low + rng.choice(pool - low, len(used) - 1, replace=False)])
+    remap = {int(o): int(n) for o, n in zip(used, new_ids)}
+    idx = torch.as_tensor(new_ids.astype(np.int64), device="cuda")
+    src = torch.as_tensor(used.astype(np.int64), device="cuda")
+    ckv_big = torch.empty((pool, P, 512), dtype=torch.bfloat16, device="cuda")
+    kpe_big = torch.empty((pool, P, 64), dtype=torch.bfloat16, device="cuda")
+    ckv_big.index_copy_(0, idx, ckv[src])
+    kpe_big.index_copy_(0, idx, kpe[src])
+    ix = np.array([remap[int(x)] for x in w.kv_indices], dtype=np.int32)
+    p = fb.mla_plan(w.qo_indptr, w.kv_indptr, ix, w.last_page_len, w.num_heads, P, pool,
+                    fixed_chunk_tokens=128)
+    out, lse = fb.mla(qn, qp, ckv_big, kpe_big, p, w.sm_scale)
+    torch.cuda.synchronize()
+    O, LSE = oa.mla_attention(*(t.double().cpu().numpy() for t in (qn, qp, ckv, kpe)), w.qo_indptr,
+                              w.kv_indptr, w.kv_indices, w.last_page_len, w.sm_scale, True)
+    compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE, True, "mla >4 GiB")
+    del ckv_big, kpe_big
+    torch.cuda.empty_cache()
