@@ -39,7 +39,7 @@ EXPORTED = ["fi_plan_create", "fi_plan_get_info", "fi_plan_work_list", "fi_plan_
             "fi_decode_run_noalloc", "fi_prefill_run_scaled", "fi_plan_create_composed",
             "fi_decode_run_composed", "fi_prefill_run_rope", "fi_mla_plan_create", "fi_mla_run"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
-QITEM_STRIDE = 12
+QITEM_STRIDE = 16
 QMERGE_STRIDE = 8
 PREFILL_ROWS = 256
 PREFILL_MAX_PAGES = 256

@@ -253,6 +253,7 @@ fi_status fi_mla_run(const fi_prefill_plan* plan, const void* q_nope, const void
   a.kpe = kpe_pages;
   a.out = out;
   a.lse = lse;
+  a.counters = reinterpret_cast<int32_t*>(ws + plan->ws.counters);
   a.part_o = reinterpret_cast<float*>(ws + plan->ws.part_o);
   a.part_lse = reinterpret_cast<float*>(ws + plan->ws.part_lse);
   a.num_items = plan->num_items();

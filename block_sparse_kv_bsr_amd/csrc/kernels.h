@@ -75,7 +75,8 @@ struct MlaArgs {
   const void* kpe;          // bf16 [pool, page_size, 64]
   void* out;                // bf16 [N, num_heads, 512]
   float* lse;               // [N, num_heads] natural log, or null
-  float* part_o;            // [slots, FI_MLA_ROWS, 512]
+  int32_t* counters;        // device, [num_merges] arrival counts, 0 between runs
+  float* part_o;            // [slots, FI_MLA_ROWS x 512] (the kernel's own order)
   float* part_lse;          // [slots, FI_MLA_ROWS], log2 units
   int64_t num_items, num_merges;
   int32_t num_heads, page_size, causal;
@@ -104,7 +105,7 @@ hipError_t launch_merge_two(const MergeTwoArgs& a, hipStream_t stream);
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_merge(const PrefillArgs& a, hipStream_t stream);
-// Latent attention tiles, then the merge of cut tiles (mla_attend.hip).
+// Latent attention tiles; cut tiles merge in the same launch (mla_attend.hip).
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream);
 
 }  // namespace fi

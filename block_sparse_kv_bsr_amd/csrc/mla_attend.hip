@@ -39,6 +39,10 @@
 // is element q of input lane 4k+p), two per tile: tokens 4g .. 4g+3 and
 // 16 + 4g .. +3.
 //
+// A tile whose tokens are cut into several chunks (items) merges in this
+// kernel: each chunk writes its partial state and counts its arrival at the
+// tile's merge; the chunk that completes the count merges all of them.
+//
 // LDS ring of 2 stages of 32 tokens, filled by direct-to-LDS loads; a
 // block's loads go out as soon as every wave is done with the stage they
 // refill, one block ahead. A latent row is one wave-wide 1 KiB load, placed
@@ -102,7 +106,8 @@ struct MlaParams {
   const char* kpe;          // bf16 [pages, P, 64]
   __bf16* out;              // bf16 [N, H, 512]
   float* lse;               // [N, H] natural log, or null
-  float* part_o;            // [slots, kRows, 512]
+  int32_t* counters;        // [merges] arrivals, 0 between runs
+  float* part_o;            // [slots][kRows * 512] in the kernel's register order
   float* part_lse;          // [slots, kRows], log2 units
   int num_heads;
   int page_size;
@@ -155,6 +160,44 @@ __device__ __forceinline__ int lds_id(const int* p) {
   int v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_u32(p)) : "memory");
   return v;
+}
+
+// The partial states of a cut tile pass between work-groups that may run on
+// different XCDs, whose L2 caches are private. They are written and read as
+// relaxed agent-scope atomics, which the compiler issues with the sc1 cache
+// policy: stores write through to the device-coherent level and loads read
+// from it, with no cache flush.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent2(float* p, float a, float b) {
+  const uint64_t u = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2_t load_coherent2(const float* p) {
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x2_t{__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32))};
+}
+
+// A wave's block of a partial state (kRw x kDw floats, 16 KiB) as a buffer
+// resource in scalar registers, and one 8-byte piece of it read from the
+// coherent level (cache policy sc1, as the atomic loads above): the merge's
+// many loads then share one lane offset register.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+__device__ __forceinline__ BufRes wave_partial(const float* part_o, int64_t slot, int wave) {
+  const float* b = part_o + slot * (kRows * kDc) + wave * (kRw * kDw);
+  // 0x20000: the 32-bit data format every untyped access of gfx9 needs
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(b), (short)0, kRw * kDw * 4, 0x00020000);
+}
+// lane_off: the lane's byte offset (a vector register); run_off: the run's
+// (uniform, a scalar register or constant)
+__device__ __forceinline__ u32x2_t load_coherent_run(BufRes r, uint32_t lane_off, int run_off) {
+  constexpr int kSc1 = 16;  // cache policy bit sc1
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)lane_off, run_off, kSc1);
 }
 
 // s_waitcnt vmcnt(n), leaving the other counters unconstrained.
@@ -505,92 +548,124 @@ __global__ __launch_bounds__(64 * kWaves, 2) void mla_attend_kernel(MlaParams p)
 
   // ---- this row's state over the wave's 256 dims: o / l and lse; a row
   // that attended nothing has o = 0 and lse = -inf
-  if (!row_ok) return;
   const float l_tot = row_sum4(l_run);
   const bool empty = l_tot == 0.f;
   const float inv = empty ? 0.f : 1.f / l_tot;
   const float lse2 = empty ? -INFINITY : m_run * c + __builtin_amdgcn_logf(l_tot);
   // lane n + 16g holds O^T[16 td + 4g + e][n], e = 0 .. 3
   if (slot < 0) {
-    __bf16* dst = p.out + q_index * kDc + d0 + 4 * g;
+    if (row_ok) {
+      __bf16* dst = p.out + q_index * kDc + d0 + 4 * g;
 #pragma unroll
-    for (int t = 0; t < kDw / 16; ++t) {
-      const bf16x4_t v = {(__bf16)(o[t][0] * inv), (__bf16)(o[t][1] * inv), (__bf16)(o[t][2] * inv),
-                          (__bf16)(o[t][3] * inv)};
-      *reinterpret_cast<bf16x4_t*>(dst + 16 * t) = v;
+      for (int t = 0; t < kDw / 16; ++t) {
+        const bf16x4_t v = {(__bf16)(o[t][0] * inv), (__bf16)(o[t][1] * inv), (__bf16)(o[t][2] * inv),
+                            (__bf16)(o[t][3] * inv)};
+        *reinterpret_cast<bf16x4_t*>(dst + 16 * t) = v;
+      }
+      if (dh == 0 && g == 0 && p.lse) p.lse[q_index] = lse2 * kLn2;
     }
-    if (dh == 0 && g == 0 && p.lse) p.lse[q_index] = lse2 * kLn2;
     return;
   }
-  float* dst = p.part_o + ((int64_t)slot * kRows + row) * kDc + d0 + 4 * g;
-#pragma unroll
-  for (int t = 0; t < kDw / 16; ++t)
-    *reinterpret_cast<float4*>(dst + 16 * t) =
-        make_float4(o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv);
-  if (dh == 0 && g == 0) p.part_lse[(int64_t)slot * kRows + row] = lse2;
-}
 
-// Folds the chunk states of cut tiles (log2-unit lse) into bf16 out and
-// natural-log lse: the closed form of softmax over a disjoint union of token
-// sets (FlashInfer paper explainer, visionhong.com, benchmark section: the
-// split scheduler's pieces are merged). A thread per (row, 4 dims), two rows
-// per workgroup; the chunks are summed in slot order in one pass.
-__global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams p) {
-  const int32_t* mg = p.merges + (int64_t)blockIdx.x * FI_QMERGE_STRIDE;
-  const int r = blockIdx.y * 2 + (threadIdx.x >> 7);
-  const int H = p.num_heads;
-  const int f = mg[FI_QMERGE_HEAD_BEGIN] + r;
-  if (f >= mg[FI_QMERGE_NUM_QO] * H) return;
-  const int qi = f / H;
-  const int64_t q_index = (int64_t)(mg[FI_QMERGE_QO_ROW] + qi) * H + (f - qi * H);
+  // ---- a cut tile: this chunk's state goes to its partial slot in the
+  // order the registers hold it (wave w's 16 x 256 floats as 32 runs of 512
+  // bytes, run 2 td + h holding elements 2h, 2h + 1 of dim tile td of every
+  // lane), written through to the device-coherent level; then the chunk
+  // counts its arrival, and the chunk that arrives last merges the tile.
+  const int merge = it[FI_QITEM_MERGE];
+  const int32_t* mg = p.merges + (int64_t)merge * FI_QMERGE_STRIDE;
+  const int nch = mg[FI_QMERGE_NUM_CHUNKS];
   const int64_t slot0 = mg[FI_QMERGE_SLOT_BEGIN];
-  const int k = mg[FI_QMERGE_NUM_CHUNKS];
-  const int c4 = 4 * (threadIdx.x & 127);
-  const float* lse_r = p.part_lse + slot0 * kRows + r;
-  const float* o_r = p.part_o + (slot0 * kRows + r) * kDc + c4;
-  // one pass in chunk order, eight chunks' loads in flight at a time, the
-  // running maximum raised per group of eight (a chunk the row attended
-  // nothing of has s = -inf and weight 0)
-  float mx = -INFINITY, den = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = 0; c0 < k; c0 += 8) {
-    const int nb = min(8, k - c0);
-    float s[8];
-    float4 v[8];
+  constexpr int kWaveFloats = kRw * kDw;  // 4096
+  if (row_ok) {
+    float* dst = p.part_o + (int64_t)slot * (kRows * kDc) + wave * kWaveFloats + 2 * lane;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t ch = c0 + min(i, nb - 1);  // the tail re-reads the group's last chunk
-      s[i] = lse_r[ch * kRows];
-      v[i] = *reinterpret_cast<const float4*>(o_r + ch * kRows * kDc);
+    for (int t = 0; t < kDw / 16; ++t) {
+      store_coherent2(dst + (2 * t) * 128, o[t][0] * inv, o[t][1] * inv);
+      store_coherent2(dst + (2 * t + 1) * 128, o[t][2] * inv, o[t][3] * inv);
     }
-    float bm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < nb) bm = fmaxf(bm, s[i]);
-    const float mn = fmaxf(mx, bm);
-    if (mn == -INFINITY) continue;
-    const float a = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - mn);
-    den *= a;
-    acc.x *= a;
-    acc.y *= a;
-    acc.z *= a;
-    acc.w *= a;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float w = (i >= nb || s[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[i] - mn);
-      den += w;
-      acc.x += w * v[i].x;
-      acc.y += w * v[i].y;
-      acc.z += w * v[i].z;
-      acc.w += w * v[i].w;
-    }
-    mx = mn;
+    if (dh == 0 && g == 0) store_coherent(p.part_lse + (int64_t)slot * kRows + row, lse2);
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  const bf16x4_t v = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv),
-                      (__bf16)(acc.w * inv)};
-  *reinterpret_cast<bf16x4_t*>(p.out + q_index * kDc + c4) = v;
-  if (c4 == 0 && p.lse) p.lse[q_index] = den > 0.f ? (mx + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
+  // Each wave's stores are complete (acknowledged by the coherent level)
+  // before the barrier, so every store of the work-group is before the
+  // arrival that thread 0 issues after it. The page-id window is free now
+  // (every wave has left the block loop) and carries the election.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(p.counters + merge, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == nch - 1;
+    if (last) __hip_atomic_store(p.counters + merge, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_pid[0] = last;
+  }
+  __syncthreads();
+  if (!s_pid[0] || !row_ok) return;
+
+  // ---- the merge (closed form of softmax over a disjoint union of token
+  // sets; FlashInfer paper explainer, visionhong.com, benchmark section: the
+  // split scheduler's pieces are merged): each lane folds its own elements
+  // of every chunk, in chunk order (so the result does not depend on which
+  // chunk finished last), in two passes over half of its runs each, four
+  // chunks' loads in flight, the running maximum raised per group of four
+  // (a chunk the row attended nothing of has lse = -inf and weight 0).
+  // Every load reads the coherent level.
+  const float* lse0 = p.part_lse + slot0 * kRows + row;
+  __bf16* dst = p.out + q_index * kDc + d0 + 4 * g;
+  float mx = -INFINITY, den = 0.f;
+  static_for<2>([&](auto PASS) {
+    constexpr int kHalf = kDw / 16;  // runs per pass
+    constexpr int r0 = decltype(PASS)::value * kHalf;
+    constexpr int kK = 4;            // chunks per group
+    f32x2_t acc[kHalf];
+#pragma unroll
+    for (int i = 0; i < kHalf; ++i) acc[i] = f32x2_t{0.f, 0.f};
+    mx = -INFINITY;
+    den = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += kK) {
+      float sv[kK];
+      u32x2_t v[kK][kHalf];
+#pragma unroll
+      for (int k = 0; k < kK; ++k) {
+        const int ch = min(c0 + k, nch - 1);  // a short group re-reads its last chunk, weight 0
+        sv[k] = load_coherent(lse0 + (int64_t)ch * kRows);
+        const BufRes r = wave_partial(p.part_o, slot0 + ch, wave);
+#pragma unroll
+        for (int i = 0; i < kHalf; ++i) v[k][i] = load_coherent_run(r, 8u * lane, 512 * (r0 + i));
+      }
+#pragma unroll
+      for (int k = 1; k < kK; ++k)
+        if (c0 + k >= nch) sv[k] = -INFINITY;
+      const float mn = fmaxf(mx, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+      if (mn == -INFINITY) continue;
+      const float a = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - mn);
+      float w[kK];
+#pragma unroll
+      for (int k = 0; k < kK; ++k) w[k] = sv[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[k] - mn);
+      den = den * a + ((w[0] + w[1]) + (w[2] + w[3]));
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) {
+        float x = acc[i][0] * a, y = acc[i][1] * a;
+#pragma unroll
+        for (int k = 0; k < kK; ++k) {
+          x = fmaf(w[k], __uint_as_float(v[k][i][0]), x);
+          y = fmaf(w[k], __uint_as_float(v[k][i][1]), y);
+        }
+        acc[i] = f32x2_t{x, y};
+      }
+      mx = mn;
+    }
+    // run 2 td + h holds dims d0 + 16 td + 4g + 2h, +1 of the row
+    const float rinv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+    for (int t = r0 / 2; t < (r0 + kHalf) / 2; ++t) {
+      const int i = 2 * t - r0;
+      const bf16x4_t o4 = {(__bf16)(acc[i][0] * rinv), (__bf16)(acc[i][1] * rinv),
+                           (__bf16)(acc[i + 1][0] * rinv), (__bf16)(acc[i + 1][1] * rinv)};
+      *reinterpret_cast<bf16x4_t*>(dst + 16 * t) = o4;
+    }
+  });
+  if (dh == 0 && g == 0 && p.lse)
+    p.lse[q_index] = den > 0.f ? (mx + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -607,6 +682,7 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
   p.kpe = static_cast<const char*>(a.kpe);
   p.out = static_cast<__bf16*>(a.out);
   p.lse = a.lse;
+  p.counters = a.counters;
   p.part_o = a.part_o;
   p.part_lse = a.part_lse;
   p.num_heads = a.num_heads;
@@ -617,9 +693,6 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
   p.causal = a.causal;
   p.scale_log2 = a.sm_scale * kLog2e;
   hipLaunchKernelGGL(mla_attend_kernel, dim3((uint32_t)a.num_items), dim3(64 * kWaves), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.num_merges <= 0) return e;
-  hipLaunchKernelGGL(mla_merge_kernel, dim3((uint32_t)a.num_merges, kRows / 2), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -71,8 +71,9 @@ struct fi_plan {
 };
 
 // Work list of one prefill / append call. Workspace sections (each on a
-// 256-byte boundary): items, merges and page ids (copied from the host),
-// then the partial states of cut tiles (written by the tile kernel).
+// 256-byte boundary): items, merges, page ids and (MLA plans) one arrival
+// counter per merge, all copied from the host (the counters as zeros), then
+// the partial states of cut tiles (written by the tile kernel).
 struct fi_prefill_plan {
   int32_t batch = 0, num_qo_heads = 0, num_kv_heads = 0, head_dim = 0, page_size = 0;
   int32_t group = 0, causal = 1, tokens_per_tile = 0, chunk_tokens = 0;
@@ -85,7 +86,7 @@ struct fi_prefill_plan {
   std::vector<int32_t> items;   // num_items * FI_QITEM_STRIDE
   std::vector<int32_t> merges;  // num_merges * FI_QMERGE_STRIDE
   struct {
-    int64_t items = 0, merges = 0, page_ids = 0, part_o = 0, part_lse = 0;
+    int64_t items = 0, merges = 0, page_ids = 0, counters = 0, part_o = 0, part_lse = 0;
     int64_t image_bytes = 0, total_bytes = 0;
   } ws;
   std::vector<uint8_t> image;

@@ -209,6 +209,7 @@ fi_status build_tile_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
           f[FI_QITEM_CHUNK] = (int32_t)c;
           f[FI_QITEM_Q_POS] = (int32_t)t.qpos;
           f[FI_QITEM_HEAD_BEGIN] = t.head_begin;
+          f[FI_QITEM_MERGE] = k > 1 ? (int32_t)(p->num_merges() - 1) : -1;
           longest = std::max(longest, f[FI_QITEM_NUM_KV]);
           p->items.insert(p->items.end(), f, f + FI_QITEM_STRIDE);
         }
@@ -292,6 +293,10 @@ fi_status build_tile_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
     off = fi::align_up(off + (int64_t)p->merges.size() * 4, 256);
     ws.page_ids = off;
     off = fi::align_up(off + nnz * 4, 256);
+    // MLA: the merges' arrival counters, uploaded as zeros (the chunk that
+    // completes a merge sets its counter back to 0)
+    ws.counters = off;
+    if (mla) off = fi::align_up(off + p->num_merges() * 4, 256);
     ws.image_bytes = off;
     ws.part_o = off;
     const int64_t slot_rows = mla ? FI_MLA_ROWS : FI_PREFILL_ROWS;

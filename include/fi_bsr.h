@@ -588,7 +588,9 @@ enum {
                               tile, counted token-major from the tile's first
                               query token (0 unless a token's heads span
                               several tiles); 0 in other plans */
-  FI_QITEM_STRIDE = 12,
+  FI_QITEM_MERGE = 12,      /* index of the tile's merge (fi_prefill_plan_merges)
+                              when the tile is cut, else -1 */
+  FI_QITEM_STRIDE = 16,     /* int32 per item; fields past MERGE are 0 */
   FI_PREFILL_ROWS = 256,      /* query rows per tile */
   FI_MLA_ROWS = 32,           /* (query token, head) rows per MLA tile */
   FI_PREFILL_MAX_PAGES = 256  /* pages per chunk at most */
@@ -773,8 +775,12 @@ fi_status fi_mla_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr,
                              fi_prefill_plan** out_plan);
 
 /*
- * Run MLA for an uploaded plan on `stream`: the tile kernel (matrix cores),
- * then, if some tile was cut into several chunks, the merge kernel. No host
+ * Run MLA for an uploaded plan on `stream`: one launch of the tile kernel
+ * (matrix cores). A cut tile's chunks write partial states to the
+ * workspace and count their arrival at the tile's merge (a counter in the
+ * uploaded workspace image, 0 after the upload); the chunk that arrives last
+ * merges the partials in chunk order, so the result does not depend on
+ * which chunk finished last, and sets the counter back to 0. No host
  * synchronisation; calls that use the same workspace must not overlap.
  *
  * q_nope, q_pe, out, lse, ckv_pages, kpe_pages: device buffers in the layout

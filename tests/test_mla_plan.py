@@ -11,7 +11,7 @@ from block_sparse_kv_bsr_amd import binding
 from block_sparse_kv_bsr_amd.workloads import mla_workload, random_mla_workload
 import oracle.attention as oa
 
-REQ, KVH, QROW, NQO, KV0, NKV, VIS, PG0, SLOT, CHUNK, QPOS, HB = range(12)
+REQ, KVH, QROW, NQO, KV0, NKV, VIS, PG0, SLOT, CHUNK, QPOS, HB, MERGE = range(13)
 M_QROW, M_NQO, M_KVH, M_SLOT0, M_NCH, M_HB = range(6)
 R = binding.MLA_ROWS
 ERR_INVALID, ERR_UNSUPPORTED = -1, -2
@@ -70,10 +70,16 @@ def check_plan(w, p):
         assert slots == ([-1] if len(its) == 1 else list(range(slots[0], slots[0] + len(its))))
     cut = {k: v for k, v in tiles.items() if len(v) > 1}
     assert len(merges) == len(cut) == info["num_merges"]
-    for m in merges:
+    for mi, m in enumerate(merges):
         its = cut[(int(m[M_QROW]), int(m[M_HB]))]
         assert int(m[M_NCH]) == len(its) and int(m[M_NQO]) == int(its[0][NQO])
         assert int(m[M_SLOT0]) == min(int(x[SLOT]) for x in its)
+        # each chunk of a cut tile names the tile's merge (its arrival counter)
+        assert all(int(x[MERGE]) == mi for x in its)
+    for its in tiles.values():
+        if len(its) == 1:
+            assert int(its[0][MERGE]) == -1
+    assert np.all(items[:, MERGE + 1:] == 0)
     # within a request, chunk-major: the tiles that read one chunk are adjacent
     for b in set(int(x) for x in items[:, REQ]):
         kv0 = items[items[:, REQ] == b][:, KV0]
