@@ -43,8 +43,7 @@ KERNELS = {"tile_attend_kernel": ("attn_tile.hip", "tile_attend"),
            "decode_bsr_kernel": ("decode_bsr.hip", "decode_bsr"),
            "decode_mma_kernel": ("decode_mma.hip", "decode_mma"),
            "prefill_merge_kernel": ("merge_states.hip", "prefill_merge"),
-           "mla_attend_kernel": ("mla_attend.hip", "mla_attend"),
-           "mla_merge_kernel": ("mla_attend.hip", "mla_merge")}
+           "mla_attend_kernel": ("mla_attend.hip", "mla_attend")}
 
 
 def source_digest(kernels=("decode_bsr_kernel",)) -> str:
@@ -577,7 +576,7 @@ def cpu_baseline_mla(w, qn, qp, ckv, kpe, min_seconds=10.0):
 
 def bench_mla(args, w):
     """Multi-head latent attention decode: one step = fi_mla_run over the
-    batch (the tile kernel, plus the merge kernel for cut tiles). Reported as
+    batch (one launch of the tile kernel; cut tiles merge inside it). Reported as
     achieved HBM GB/s of the algorithmic bytes (every cached latent and
     rotary key once, q, out) against the 8 TB/s peak: at 96 heads the work
     is 173 flop per byte, below the matrix cores' 312 flop per byte ridge."""
@@ -616,7 +615,7 @@ def bench_mla(args, w):
     nbytes, flops = w.algorithmic_bytes(), w.flops()
     gbs = nbytes / (med_ms * 1e-3) / 1e9
     tflops = flops / (med_ms * 1e-3) / 1e12
-    kernels = ["mla_attend_kernel"] + (["mla_merge_kernel"] if p.info["num_merges"] else [])
+    kernels = ["mla_attend_kernel"]
     traffic = read_traffic(w.name, kernels)
     result = {
         "metric": "achieved HBM GB/s (% of MI355X peak) + µs/batch, paged latent-attention "
