@@ -112,7 +112,7 @@ typedef struct {
                                  plan that runs the matrix-core kernel
                                  without the rotary embedding, which
                                  measured faster with fewer, longer items) */
-  int32_t min_chunk_tokens;   /* never cut a request finer than this (default 256) */
+  int32_t min_chunk_tokens;   /* never cut a request finer than this (default 32) */
   int32_t max_chunk_tokens;   /* cap on chunk length; 0 = no cap */
   int32_t fixed_chunk_tokens; /* >0: use exactly this chunk length (rounded up
                                  to whole pages) instead of the heuristic */
