@@ -155,6 +155,7 @@ fi_status prefill_run(const fi_prefill_plan* plan, const void* q, const void* k_
   a.v_pages = v_pages;
   a.out = out;
   a.lse = lse;
+  a.counters = reinterpret_cast<int32_t*>(ws + plan->ws.counters);
   a.part_o = reinterpret_cast<float*>(ws + plan->ws.part_o);
   a.part_lse = reinterpret_cast<float*>(ws + plan->ws.part_lse);
   a.num_items = plan->num_items();
@@ -173,10 +174,8 @@ fi_status prefill_run(const fi_prefill_plan* plan, const void* q, const void* k_
   a.rope_theta = rope_theta;
   a.rope_scale = rope_scale;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fi::launch_prefill(a, s);
+  const hipError_t e = fi::launch_prefill(a, s);
   if (e != hipSuccess) return hip_fail(e, "prefill tile kernel launch");
-  e = fi::launch_prefill_merge(a, s);
-  if (e != hipSuccess) return hip_fail(e, "prefill merge kernel launch");
   return FI_OK;
 }
 

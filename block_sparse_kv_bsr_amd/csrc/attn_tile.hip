@@ -57,6 +57,7 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "coherent.h"
 #include "fi_bsr.h"
 #include "kernels.h"
 
@@ -89,6 +90,8 @@ struct TileParams {
   const char* v_pages;
   float* part_o;
   float* part_lse;
+  const int32_t* merges;  // prefill: merges of cut tiles (FI_QMERGE_*)
+  int32_t* counters;      // prefill: their arrival counts, 0 between runs
   int64_t page_stride;  // bytes between physical pages
   int64_t head_stride;  // bytes between KV heads within a page
   int num_qo_heads;
@@ -822,6 +825,9 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   // loads past the end may still be landing in the ring
   wait_vmcnt<0>();
 
+  // waves that hand their state on (the second token half of a split tile)
+  // stay until the last barrier of a cut prefill tile, idle
+  bool holds = true;
   if constexpr (R::kSplit) {
   // ---- merge the two token halves of each row: waves 4..7 hand (m, l, o)
   // to waves 0..3 through the (drained) ring, lane-for-lane
@@ -837,8 +843,9 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
     s_ml[wrow][1][lane] = l_run;
   }
   __syncthreads();
-  if (wtok == 1) return;
-  {
+  holds = wtok == 0;
+  if (!kPrefill && !holds) return;
+  if (holds) {
     // either half may have attended nothing (m = -inf, l = 0, o = 0)
     const float m2 = s_ml[wrow][0][lane], l2 = s_ml[wrow][1][lane];
     const float mm = fmaxf(m_run, m2);
@@ -856,22 +863,41 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
 
   // ---- this row's state: o / l and lse; a row that attended nothing has
   // o = 0 and lse = -inf
-  if (!row_ok) return;
+  const bool mine = holds && row_ok;  // this lane holds a row of the tile
   const bool empty = l_run == 0.f;
   // V's dequantisation scale (1 for bf16) multiplies outputs and partial
   // states alike: the merge of partials is linear in them
   const float inv = empty ? 0.f : p.v_scale / l_run;
   // log2 units of the scaled scores (m_run is an unscaled score)
   const float lse2 = empty ? -INFINITY : m_run * c + __builtin_amdgcn_logf(l_run);
-  if (kPrefill && slot_base < 0) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  if constexpr (!kPrefill) {
+    // prefix rows: partial state to slot prefix_slot[b][h] + chunk (G rows
+    // per slot), merged by the decode kernel's trees
+    if (!mine) return;
+    float* dst = p.part_o + ((int64_t)slot_base * G + gi) * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        // elements 4*q4 .. +3 are d = 32t + 8*q4 + 4*half .. +3
+        const int d = 32 * t + 8 * q4 + 4 * half;
+        *reinterpret_cast<float4*>(dst + d) =
+            make_float4(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv, o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv);
+      }
+    }
+    if (half == 0) p.part_lse[(int64_t)slot_base * G + gi] = lse2;
+    return;
+  } else {
+  if (slot_base < 0) {
     // the tile's only chunk: bf16 out and natural-log lse of the row
+    if (!mine) return;
     __bf16* dst = p.out + q_index * D;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = 32 * t + 8 * q4 + 4 * half;
-        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
         const bf16x4_t v = {(__bf16)(o[t][4 * q4] * inv), (__bf16)(o[t][4 * q4 + 1] * inv),
                             (__bf16)(o[t][4 * q4 + 2] * inv), (__bf16)(o[t][4 * q4 + 3] * inv)};
         *reinterpret_cast<bf16x4_t*>(dst + d) = v;
@@ -880,22 +906,111 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
     if (half == 0 && p.lse) p.lse[q_index] = lse2 * kLn2;
     return;
   }
-  // partial state: prefix rows go to slot prefix_slot[b][h] + chunk (G rows
-  // per slot), prefill rows to slot * 128 + row
-  const int64_t prow = kPrefill ? (int64_t)slot_base * FI_PREFILL_ROWS + row
-                                : (int64_t)slot_base * G + gi;
-  float* dst = p.part_o + prow * D;
+
+  // ---- a cut tile: this chunk's state goes to its partial slot in the
+  // order the registers hold it (row group w's 32 rows x D floats as D / 4
+  // runs of 512 bytes, run 8t + j holding elements 2j, 2j + 1 of tile t of
+  // every lane), written through to the device-coherent level; then the
+  // chunk counts its arrival at the tile's merge, and the chunk that
+  // arrives last merges the tile (closed form of softmax over a disjoint
+  // union of token sets; FlashInfer paper explainer, visionhong.com,
+  // benchmark section: the split scheduler's pieces are merged).
+  constexpr int kRuns = D / 4;
+  constexpr int kBlockFloats = 32 * D;  // one row group's state
+  const int merge = p.pitems[(int64_t)blockIdx.x * FI_QITEM_STRIDE + FI_QITEM_MERGE];
+  const int32_t* mg = p.merges + (int64_t)merge * FI_QMERGE_STRIDE;
+  const int nch = mg[FI_QMERGE_NUM_CHUNKS];
+  const int64_t slot0 = mg[FI_QMERGE_SLOT_BEGIN];
+  constexpr int64_t kSlotFloats = (int64_t)FI_PREFILL_ROWS * D;
+  if (mine) {
+    float* dst = p.part_o + (int64_t)slot_base * kSlotFloats + wrow * kBlockFloats + 2 * lane;
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
+    for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      // elements 4*q4 .. +3 are d = 32t + 8*q4 + 4*half .. +3
-      const int d = 32 * t + 8 * q4 + 4 * half;
-      *reinterpret_cast<float4*>(dst + d) =
-          make_float4(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv, o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv);
-    }
+      for (int jp = 0; jp < 8; ++jp)
+        store_coherent2(dst + (8 * t + jp) * 128, o[t][2 * jp] * inv, o[t][2 * jp + 1] * inv);
+    if (half == 0) store_coherent(p.part_lse + (int64_t)slot_base * FI_PREFILL_ROWS + row, lse2);
   }
-  if (half == 0) p.part_lse[prow] = lse2;
+  // Each wave's stores are complete (acknowledged by the coherent level)
+  // before the barrier, so every store of the work-group precedes the
+  // arrival thread 0 issues after it. The page-id window is free now (every
+  // wave has left the block loop) and carries the election.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(p.counters + merge, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == nch - 1;
+    if (last) __hip_atomic_store(p.counters + merge, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_pid[0] = (uint32_t)last;
+  }
+  __syncthreads();
+  if (!s_pid[0] || !mine) return;
+
+  // ---- the merge: each lane folds its own elements of every chunk in
+  // chunk order (so the result does not depend on which chunk finished
+  // last), 16 runs per pass with four chunks' loads in flight, the running
+  // maximum raised per group of four (a chunk the row attended nothing of
+  // has lse = -inf and weight 0). Every load reads the coherent level.
+  const float* lse0 = p.part_lse + slot0 * FI_PREFILL_ROWS + row;
+  __bf16* out_row = p.out + q_index * D;
+  float mx = -INFINITY, den = 0.f;
+  static_for<kRuns / 16>([&](auto PASS) {
+    constexpr int r0 = decltype(PASS)::value * 16;
+    constexpr int kK = 4;  // chunks per group
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    f32x2_t acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = f32x2_t{0.f, 0.f};
+    mx = -INFINITY;
+    den = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += kK) {
+      float sv[kK];
+      coh_u32x2_t v[kK][16];
+#pragma unroll
+      for (int k = 0; k < kK; ++k) {
+        const int ch = min(c0 + k, nch - 1);  // a short group re-reads its last chunk, weight 0
+        sv[k] = load_coherent(lse0 + (int64_t)ch * FI_PREFILL_ROWS);
+        const BufRes rs = buffer_of(p.part_o + (slot0 + ch) * kSlotFloats + wrow * kBlockFloats,
+                                    kBlockFloats * 4);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[k][i] = load_coherent_run(rs, 8u * lane, 512 * (r0 + i));
+      }
+#pragma unroll
+      for (int k = 1; k < kK; ++k)
+        if (c0 + k >= nch) sv[k] = -INFINITY;
+      const float mn = fmaxf(mx, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+      if (mn == -INFINITY) continue;
+      const float a = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - mn);
+      float w[kK];
+#pragma unroll
+      for (int k = 0; k < kK; ++k) w[k] = sv[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[k] - mn);
+      den = den * a + ((w[0] + w[1]) + (w[2] + w[3]));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = acc[i][0] * a, y = acc[i][1] * a;
+#pragma unroll
+        for (int k = 0; k < kK; ++k) {
+          x = fmaf(w[k], __uint_as_float(v[k][i][0]), x);
+          y = fmaf(w[k], __uint_as_float(v[k][i][1]), y);
+        }
+        acc[i] = f32x2_t{x, y};
+      }
+      mx = mn;
+    }
+    // runs 8t + 2q4 and 8t + 2q4 + 1 hold dims 32t + 8q4 + 4half .. +3
+    const float rinv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const int run = r0 + i;
+      const int d = 32 * (run / 8) + 8 * ((run % 8) / 2) + 4 * half;
+      const bf16x4_t o4 = {(__bf16)(acc[i][0] * rinv), (__bf16)(acc[i][1] * rinv),
+                           (__bf16)(acc[i + 1][0] * rinv), (__bf16)(acc[i + 1][1] * rinv)};
+      *reinterpret_cast<bf16x4_t*>(out_row + d) = o4;
+    }
+  });
+  if (half == 0 && p.lse)
+    p.lse[q_index] = den > 0.f ? (mx + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
+  }  // kPrefill
 }
 
 // ceil(2^32 / page_size), split into its low word and the 2^32 bit
@@ -948,6 +1063,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.v_pages = static_cast<const char*>(a.v_pages);
   p.part_o = a.part_o;
   p.part_lse = a.part_lse;
+  p.merges = a.merges;
+  p.counters = a.counters;
   const int64_t row = (int64_t)a.head_dim * a.kv_bytes;
   p.head_stride = (int64_t)a.page_size * row;
   p.page_stride = (int64_t)a.num_kv_heads * a.page_size * row;

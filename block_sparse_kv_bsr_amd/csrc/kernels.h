@@ -54,7 +54,8 @@ struct PrefillArgs {
   const void* v_pages;
   void* out;                // bf16 [N, num_qo_heads, head_dim]
   float* lse;               // [N, num_qo_heads] natural log, or null
-  float* part_o;            // [slots, FI_PREFILL_ROWS, head_dim]
+  int32_t* counters;        // device, [num_merges] arrival counts, 0 between runs
+  float* part_o;            // [slots, FI_PREFILL_ROWS x head_dim] (the kernel's own order)
   float* part_lse;          // [slots, FI_PREFILL_ROWS], log2 units
   int64_t num_items, num_merges;
   int32_t num_qo_heads, num_kv_heads, head_dim, page_size, group, causal;
@@ -104,7 +105,6 @@ hipError_t launch_decode_mma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge_two(const MergeTwoArgs& a, hipStream_t stream);
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
-hipError_t launch_prefill_merge(const PrefillArgs& a, hipStream_t stream);
 // Latent attention tiles; cut tiles merge in the same launch (mla_attend.hip).
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream);
 

@@ -11,11 +11,8 @@
 //
 // merge_two_kernel is the standalone elementwise merge of two state arrays
 // (natural-log LSE); each thread handles one 16-byte column of a row. (The
-// decode run merges its own partial states inside the decode kernel.)
-// prefill_merge_kernel folds the KV-chunk partials of cut prefill tiles
-// (log2-unit LSE) into bf16 out and natural-log lse: a thread per (row, 4
-// columns), the chunks' loads independent of each other, summed in slot
-// order.
+// decode, prefill and latent-attention runs merge their own partial states
+// inside their kernels.)
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -82,62 +79,7 @@ __global__ __launch_bounds__(256) void merge_two_kernel(MergeTwoArgs a) {
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
-  constexpr int kTPR = D / 4;         // threads per row, 4 columns each
-  constexpr int kRPB = 256 / kTPR;    // rows per workgroup
-  const int32_t* m = a.merges + (int64_t)blockIdx.x * FI_QMERGE_STRIDE;
-  const int rows = m[FI_QMERGE_NUM_QO] * a.group;
-  const int r = blockIdx.y * kRPB + threadIdx.x / kTPR;
-  if (r >= rows) return;
-  const int qo_row = m[FI_QMERGE_QO_ROW];
-  const int h = m[FI_QMERGE_KV_HEAD];
-  const int64_t slot0 = m[FI_QMERGE_SLOT_BEGIN];
-  const int k = m[FI_QMERGE_NUM_CHUNKS];
-  const int c4 = 4 * (threadIdx.x % kTPR);
-  const float* lse_r = a.part_lse + slot0 * FI_PREFILL_ROWS + r;
-  float mx = -INFINITY;
-#pragma unroll 8
-  for (int c = 0; c < k; ++c) mx = fmaxf(mx, lse_r[(int64_t)c * FI_PREFILL_ROWS]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
-  if (mx != -INFINITY) {
-#pragma unroll 4
-    for (int c = 0; c < k; ++c) {
-      const float s = lse_r[(int64_t)c * FI_PREFILL_ROWS];
-      // a chunk the row attended nothing of has s = -inf and weight 0
-      const float w = s == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s - mx);
-      const float4 o = *reinterpret_cast<const float4*>(
-          a.part_o + ((slot0 + c) * FI_PREFILL_ROWS + r) * D + c4);
-      den += w;
-      acc.x += w * o.x;
-      acc.y += w * o.y;
-      acc.z += w * o.z;
-      acc.w += w * o.w;
-    }
-  }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  const int64_t q_index =
-      (int64_t)(qo_row + r / a.group) * a.num_qo_heads + (int64_t)h * a.group + r % a.group;
-  uint2 packed;
-  packed.x = pack_bf16(acc.x * inv, acc.y * inv);
-  packed.y = pack_bf16(acc.z * inv, acc.w * inv);
-  *reinterpret_cast<uint2*>(static_cast<__bf16*>(a.out) + q_index * D + c4) = packed;
-  if (c4 == 0 && a.lse)
-    a.lse[q_index] = den > 0.f ? (mx + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
-}
-
 }  // namespace
-
-hipError_t launch_prefill_merge(const PrefillArgs& a, hipStream_t stream) {
-  if (a.num_merges <= 0) return hipSuccess;
-  const uint32_t rpb = 256 / (a.head_dim / 4);
-  const dim3 grid((uint32_t)a.num_merges, (FI_PREFILL_ROWS + rpb - 1) / rpb), block(256);
-  if (a.head_dim == 128) hipLaunchKernelGGL((prefill_merge_kernel<128>), grid, block, 0, stream, a);
-  else if (a.head_dim == 64) hipLaunchKernelGGL((prefill_merge_kernel<64>), grid, block, 0, stream, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
 
 hipError_t launch_merge_two(const MergeTwoArgs& a, hipStream_t stream) {
   if (a.num_rows <= 0) return hipSuccess;

@@ -56,6 +56,7 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "coherent.h"
 #include "fi_bsr.h"
 #include "kernels.h"
 
@@ -162,42 +163,10 @@ __device__ __forceinline__ int lds_id(const int* p) {
   return v;
 }
 
-// The partial states of a cut tile pass between work-groups that may run on
-// different XCDs, whose L2 caches are private. They are written and read as
-// relaxed agent-scope atomics, which the compiler issues with the sc1 cache
-// policy: stores write through to the device-coherent level and loads read
-// from it, with no cache flush.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_coherent2(float* p, float a, float b) {
-  const uint64_t u = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ f32x2_t load_coherent2(const float* p) {
-  const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return f32x2_t{__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32))};
-}
-
 // A wave's block of a partial state (kRw x kDw floats, 16 KiB) as a buffer
-// resource in scalar registers, and one 8-byte piece of it read from the
-// coherent level (cache policy sc1, as the atomic loads above): the merge's
-// many loads then share one lane offset register.
-typedef __amdgpu_buffer_rsrc_t BufRes;
+// resource.
 __device__ __forceinline__ BufRes wave_partial(const float* part_o, int64_t slot, int wave) {
-  const float* b = part_o + slot * (kRows * kDc) + wave * (kRw * kDw);
-  // 0x20000: the 32-bit data format every untyped access of gfx9 needs
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(b), (short)0, kRw * kDw * 4, 0x00020000);
-}
-// lane_off: the lane's byte offset (a vector register); run_off: the run's
-// (uniform, a scalar register or constant)
-__device__ __forceinline__ u32x2_t load_coherent_run(BufRes r, uint32_t lane_off, int run_off) {
-  constexpr int kSc1 = 16;  // cache policy bit sc1
-  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)lane_off, run_off, kSc1);
+  return buffer_of(part_o + slot * (kRows * kDc) + wave * (kRw * kDw), kRw * kDw * 4);
 }
 
 // s_waitcnt vmcnt(n), leaving the other counters unconstrained.
@@ -623,7 +592,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void mla_attend_kernel(MlaParams p)
     den = 0.f;
     for (int c0 = 0; c0 < nch; c0 += kK) {
       float sv[kK];
-      u32x2_t v[kK][kHalf];
+      coh_u32x2_t v[kK][kHalf];
 #pragma unroll
       for (int k = 0; k < kK; ++k) {
         const int ch = min(c0 + k, nch - 1);  // a short group re-reads its last chunk, weight 0

@@ -71,8 +71,8 @@ struct fi_plan {
 };
 
 // Work list of one prefill / append call. Workspace sections (each on a
-// 256-byte boundary): items, merges, page ids and (MLA plans) one arrival
-// counter per merge, all copied from the host (the counters as zeros), then
+// 256-byte boundary): items, merges, page ids and one arrival counter per
+// merge, all copied from the host (the counters as zeros), then
 // the partial states of cut tiles (written by the tile kernel).
 struct fi_prefill_plan {
   int32_t batch = 0, num_qo_heads = 0, num_kv_heads = 0, head_dim = 0, page_size = 0;

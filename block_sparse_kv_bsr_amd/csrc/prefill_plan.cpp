@@ -226,7 +226,10 @@ fi_status build_tile_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
       // items of each pair, longest chunk first; ties in (query row, chunk)
       // order, which is the order the items of a pair were made in, so the
       // item index breaks them (keys sorted, not items). MLA: chunk order
-      // (the tiles of one chunk, which read the same latent rows, adjacent)
+      // (the tiles of one chunk, which read the same latent rows, adjacent).
+      // (Keeping a cut tile's chunks together instead, so that its merge in
+      // the kernel comes earlier, measured 1-5% slower: the longest-first
+      // order balances the CUs better.)
       struct SortKey {
         uint32_t req, head, shorter, index;
         bool operator<(const SortKey& o) const {
@@ -293,10 +296,10 @@ fi_status build_tile_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
     off = fi::align_up(off + (int64_t)p->merges.size() * 4, 256);
     ws.page_ids = off;
     off = fi::align_up(off + nnz * 4, 256);
-    // MLA: the merges' arrival counters, uploaded as zeros (the chunk that
+    // the merges' arrival counters, uploaded as zeros (the chunk that
     // completes a merge sets its counter back to 0)
     ws.counters = off;
-    if (mla) off = fi::align_up(off + p->num_merges() * 4, 256);
+    off = fi::align_up(off + p->num_merges() * 4, 256);
     ws.image_bytes = off;
     ws.part_o = off;
     const int64_t slot_rows = mla ? FI_MLA_ROWS : FI_PREFILL_ROWS;

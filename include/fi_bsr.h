@@ -565,7 +565,8 @@ typedef struct {
  * token j / G of the tile and query head KV_HEAD * G + j % G. An item
  * attends a tile over one chunk of the request's tokens; a tile whose
  * attended range exceeds one chunk is cut into several items whose partial
- * states a merge pass combines.
+ * states the run merges (in the same launch: the chunk that arrives last
+ * merges them all, in chunk order).
  */
 enum {
   FI_QITEM_REQUEST = 0,
@@ -664,8 +665,12 @@ fi_status fi_prefill_plan_upload(fi_prefill_plan* plan, void* workspace, size_t 
                                  fi_stream_t stream);
 
 /*
- * Run prefill / append attention for an uploaded plan on `stream`: the tile
- * kernel (matrix cores), then, if some tile was cut, the merge kernel. No
+ * Run prefill / append attention for an uploaded plan on `stream`: one
+ * launch of the tile kernel (matrix cores). A cut tile's chunks write
+ * partial states to the workspace and count their arrival at the tile's
+ * merge (a counter in the uploaded workspace image, 0 after the upload); the
+ * chunk that arrives last merges them in chunk order, so the result does not
+ * depend on which chunk finished last, and sets the counter back to 0. No
  * host synchronisation. Calls that use the same workspace must not overlap.
  *
  * q        device bf16 [N, num_qo_heads, head_dim], 16-byte aligned

@@ -6,7 +6,9 @@ Small ragged cases cover head counts 1 .. 128 (powers of two and not: 5, 12,
 64, the causal mask and none, tiles cut into several chunks and not, and
 chunks that end inside a 32-token block; NaN fills every unlisted page and
 every slot past a request's last token. The full 96-head workload runs with
-the plan bench.py times and is checked on every output element.
+the plan bench.py times and is checked on every output element, and twenty
+runs of it must agree bit for bit (cut tiles merge in whichever chunk
+arrives last).
 """
 import time
 
@@ -107,6 +109,30 @@ def test_mla_is_deterministic():
     b = fb.mla(qn, qp, ckv, kpe, p, w.sm_scale)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_mla_full_size_bitwise_repeatable():
+    """Which chunk of a cut tile arrives last, and so merges the tile,
+    depends on timing; the merged result must not. Twenty runs of the
+    full-size 96-head batch (96 merged tiles), every other one after a cache
+    flush so arrival orders differ, must equal the first run bit for bit;
+    the test stops at the first mismatch and names the run."""
+    w = mla_workload(15)
+    qn, qp, ckv, kpe = (t.cuda() for t in w.make_values("cuda"))
+    p = make(w)
+    log(f"[case] mla repeat: {p.info['num_items']} items, {p.info['num_merges']} merges")
+    assert p.info["num_merges"] > 0
+    o0, l0 = fb.mla(qn, qp, ckv, kpe, p, w.sm_scale)
+    out, lse = torch.empty_like(o0), torch.empty_like(l0)
+    flush = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
+    for run in range(1, 21):
+        if run % 2:
+            flush.zero_()
+        fb.mla(qn, qp, ckv, kpe, p, w.sm_scale, out=out, lse=lse)
+        torch.cuda.synchronize()
+        same = torch.equal(out.view(torch.int16), o0.view(torch.int16)) and torch.equal(lse, l0)
+        assert same, f"run {run} differs from run 0"
+    log("[ok] mla repeat: 20 runs bitwise equal")
 
 
 def test_mla_full_size():

@@ -167,6 +167,32 @@ def test_prefill_is_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("cfg", [8, 14])
+def test_full_size_cut_tiles_bitwise_repeatable(cfg):
+    """Which chunk of a cut tile arrives last, and so merges the tile,
+    depends on timing; the merged result must not. Twenty runs of the
+    full-size append batch (bf16, and with the rotary embedding), every
+    other one after a cache flush so arrival orders differ, must equal the
+    first run bit for bit; the test stops at the first mismatch."""
+    w = workload(cfg)
+    q, k, v = w.make_values("cuda")
+    p = make_plan(w)
+    log(f"[case] prefill repeat config {cfg}: {p.info['num_items']} items, "
+        f"{p.info['num_merges']} merges")
+    assert p.info["num_merges"] > 0
+    o0, l0 = run(w, q, k, v, p)
+    out, lse = torch.empty_like(o0), torch.empty_like(l0)
+    flush = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
+    for r in range(1, 21):
+        if r % 2:
+            flush.zero_()
+        run(w, q, k, v, p, out=out, lse=lse)
+        torch.cuda.synchronize()
+        same = torch.equal(out.view(torch.int16), o0.view(torch.int16)) and torch.equal(lse, l0)
+        assert same, f"config {cfg}: run {r} differs from run 0"
+    log(f"[ok] prefill repeat config {cfg}: 20 runs bitwise equal")
+
+
 # rotary embedding (q and K before it), bf16, head_dim 128: groups 1 .. 8 and
 # 6, page sizes 1 .. 64, causal and unmasked, direct output and cut tiles,
 # positions past 2^15 (theta and scale varied)

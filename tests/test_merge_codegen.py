@@ -1,10 +1,10 @@
 """The instruction-level facts the in-kernel merges rely on, checked on the
 gfx950 code objects inside the built libfi_bsr.so (CPU only; the
 disassembly is of this repository's own build): the decode kernels' merge
-trees (vector and matrix kernels, one wave per item) and the latent-attention
-kernel's merge of cut tiles (four waves per item, same facts with a barrier
-between the waves' waits and the arrival, and between the arrival and the
-election).
+trees (vector and matrix kernels, one wave per item) and the merges of cut
+tiles in the latent-attention kernel (four waves per item) and the prefill
+tile kernel (eight): the same facts, with a barrier between the waves' waits
+and the arrival, and between the arrival and the election.
 
 A wave that finished a chunk of a cut request stores its partial state and
 then counts its arrival at a merge node with a relaxed agent-scope atomic
@@ -36,7 +36,7 @@ MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 # kernels whose merges follow the protocol: the decode kernels (one wave per
 # item) and the latent-attention tile kernel (four waves per item)
 DECODE = ("decode_bsr_kernel", "decode_mma_kernel")
-KERNELS = DECODE + ("mla_attend_kernel",)
+KERNELS = DECODE + ("mla_attend_kernel", "tile_attend_kernel")
 
 
 def _tool(name):
@@ -101,6 +101,18 @@ def mla_kernel(kernels):
     found = [v for k, v in kernels.items() if "mla_attend_kernel" in k]
     assert len(found) == 1
     return found[0]
+
+
+@pytest.fixture(scope="module")
+def prefill_kernels(kernels):
+    """{head_dim: [...]} of the prefill variants of the tile kernel (bf16
+    d 128 and 64, fp8, rotary); the shared-prefix variants merge nothing."""
+    out = {}
+    for k, v in kernels.items():
+        m = re.search(r"tile_attend_kernelILi(\d+)ELb1E", k)
+        if m:
+            out.setdefault(int(m.group(1)), []).append((k, v))
+    return out
 
 
 def _branch_targets(start, ins):
@@ -257,14 +269,17 @@ def check_mla_election(start, ins):
     return "no election branch"
 
 
-def check_mla_coherent(start, ins):
-    """Facts 3 and 4: the merge's loads and the partial stores use sc1."""
+def check_mla_coherent(start, ins, runs=32):
+    """Facts 3 and 4: the merge's loads and the partial stores use sc1 (a
+    lane stores its part of the state as `runs` float pairs: 32 for the
+    latent kernel's 16 x 256 floats per wave and the prefill tile's 32 x 128,
+    16 for 32 x 64)."""
     i = _arrival(ins)
     loads = _vec_loads(ins[i:])
     if not loads or not all(" sc1" in " " + x[2] for x in loads):
         return "a load after the arrival without sc1"
     stores = [x for x in ins[:i] if x[1].startswith("global_store") and "sc1" in x[2]]
-    if len(stores) < 32:  # 32 per lane: 16 x 256 floats per wave as float pairs
+    if len(stores) < runs:
         return "no write-through partial stores"
     return None
 
@@ -303,3 +318,24 @@ def test_mla_checks_catch_planted_reorderings(mla_kernel):
     j = next(k for k in range(i + 1, len(ins)) if ins[k][1].startswith("buffer_load"))
     stale = ins[:j] + [(ins[j][0], ins[j][1], ins[j][2].replace(" sc1", ""))] + ins[j + 1:]
     assert check_mla_coherent(start, stale) is not None
+
+
+# ---- the prefill / append tile kernel merges its cut tiles the same way
+# (eight waves per item; in the rotary variant four of them hand their state
+# to the other four and stay, idle, for the barriers).
+
+def test_prefill_variants_have_one_arrival(prefill_kernels):
+    assert sorted(prefill_kernels) == [64, 128] and len(prefill_kernels[128]) == 3
+    for d, ks in prefill_kernels.items():
+        for name, (_, ins) in ks:
+            adds = [x for x in ins if x[1].startswith("global_atomic_add")]
+            assert len(adds) == 1 and "sc0" in adds[0][2], name
+            assert len([x for x in _vec_loads(ins) if x[1].startswith("buffer_load")]) >= d // 4, name
+
+
+@pytest.mark.parametrize("check", MLA_CHECKS, ids=lambda f: f.__name__)
+def test_prefill_fact_holds(prefill_kernels, check):
+    for d, ks in prefill_kernels.items():
+        for name, (start, ins) in ks:
+            got = check(start, ins, runs=d // 4) if check is check_mla_coherent else check(start, ins)
+            assert got is None, (name, got)
