@@ -27,6 +27,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -42,15 +43,40 @@ COPY_PROBE_MIB = 1024
 KERNELS = {"tile_attend_kernel": ("attn_tile.hip", "tile_attend"),
            "decode_bsr_kernel": ("decode_bsr.hip", "decode_bsr"),
            "decode_mma_kernel": ("decode_mma.hip", "decode_mma"),
-           "prefill_merge_kernel": ("merge_states.hip", "prefill_merge"),
            "mla_attend_kernel": ("mla_attend.hip", "mla_attend")}
 
 
+def _with_headers(src: str) -> list:
+    """src and every header of this repository it includes, directly or not
+    (paths under csrc/ or include/), in a fixed order."""
+    seen, todo = [], [os.path.join(CSRC, src)]
+    while todo:
+        path = todo.pop(0)
+        if path in seen:
+            continue
+        seen.append(path)
+        with open(path) as f:
+            for ln in f:
+                m = re.match(r'\s*#\s*include\s+"([^"]+)"', ln)
+                if not m:
+                    continue
+                for d in (CSRC, os.path.join(ROOT, "include")):
+                    cand = os.path.join(d, m.group(1))
+                    if os.path.exists(cand):
+                        todo.append(cand)
+                        break
+    return seen
+
+
 def source_digest(kernels=("decode_bsr_kernel",)) -> str:
-    """sha256 (16 hex digits) of the sources the given kernels are built from."""
+    """sha256 (16 hex digits) of the sources the given kernels are built
+    from, with the repository headers they include."""
     h = hashlib.sha256()
+    files = []
     for src in sorted({KERNELS[k][0] for k in kernels}):
-        with open(os.path.join(CSRC, src), "rb") as f:
+        files += [f for f in _with_headers(src) if f not in files]
+    for path in files:
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -450,8 +476,8 @@ def copy_probe(dev):
 
 
 def bench_prefill(args, w):
-    """Prefill / append: one step = fi_prefill_run over the batch (the tile
-    kernel, plus the merge kernel when some tile is cut). Reported as
+    """Prefill / append: one step = fi_prefill_run over the batch (one launch
+    of the tile kernel; cut tiles merge inside it). Reported as
     algorithmic TFLOP/s (4 d H_q flops per attended (query, token) pair)
     against the bf16 dense matrix-core peak."""
     import torch
@@ -493,7 +519,7 @@ def bench_prefill(args, w):
     flops = w.flops()
     tflops = flops / (med_ms * 1e-3) / 1e12
     nbytes = w.algorithmic_bytes()
-    kernels = ["tile_attend_kernel"] + (["prefill_merge_kernel"] if p.info["num_merges"] else [])
+    kernels = ["tile_attend_kernel"]
     traffic = read_traffic(w.name, kernels)
     result = {
         "metric": "algorithmic TFLOP/s (% of MI355X bf16 dense peak) + µs/batch, "
@@ -527,9 +553,6 @@ def bench_prefill(args, w):
         "hbm_gbs_algorithmic": round(nbytes / (med_ms * 1e-3) / 1e9, 1),
         "plan_host_us": round(1e6 * statistics.median(plan_t), 1),
         "wall_s_timed_loop": round(wall, 4),
-        # the step's events bracket the tile kernel and, for a cut tile, the
-        # merge kernel after it on the same stream: the figure is a lower bound
-        # on the tile kernel's own rate when there is a merge
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None if traffic is None else int(traffic),
