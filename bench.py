@@ -68,16 +68,42 @@ def _with_headers(src: str) -> list:
     return seen
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without its comments and with runs of white space
+    collapsed: edits to comments and layout leave the digest unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":  # a literal, kept whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            i = text.find("*/", i + 2)
+            i = n if i < 0 else i + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest(kernels=("decode_bsr_kernel",)) -> str:
-    """sha256 (16 hex digits) of the sources the given kernels are built
-    from, with the repository headers they include."""
+    """sha256 (16 hex digits) of the code (comments and layout aside) of the
+    sources the given kernels are built from, with the repository headers
+    they include."""
     h = hashlib.sha256()
     files = []
     for src in sorted({KERNELS[k][0] for k in kernels}):
         files += [f for f in _with_headers(src) if f not in files]
     for path in files:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -245,12 +245,14 @@ fi_status create_plan(const int32_t* kv_indptr, const int32_t* kv_indices,
          (dtype == FI_DTYPE_FP8_E4M3 || num_qo_heads == 8 * num_kv_heads));
     const int64_t num_cus = o.num_cus ? o.num_cus : 256;
     // Items per CU: 8 keeps every item resident from the start (two waves per
-    // SIMD) and was measured best for the vector kernel; the matrix kernel
-    // without the rotary embedding moves more per item for the same fixed
-    // costs and measured faster with 6 (fp8 skewed batch 91.0 against 93.7
-    // us, 64 / 8 heads 168.6 against 171.5); with the embedding it is bound
-    // by vector work and needs the 8 (135.5 against 170.5 us).
-    const int64_t items_per_cu = o.items_per_cu ? o.items_per_cu : (mma && !o.rope ? 6 : 8);
+    // SIMD) and was measured best for the vector kernel (with the rotary
+    // embedding too: 179.9 against 206.2 us at 12); the matrix kernel
+    // without the embedding moves more per item for the same fixed costs
+    // and measured faster with 6 (fp8 skewed batch 91.0 against 93.7 us,
+    // 64 / 8 heads 168.6 against 171.5); with it, bound by vector work, it
+    // measured best at 16 (fp8 skewed batch 129.0 against 133.4 at 8, 130.2
+    // at 20, 134.9 at 24, 168.4 at 6).
+    const int64_t items_per_cu = o.items_per_cu ? o.items_per_cu : (mma ? (o.rope ? 16 : 6) : 8);
     // The floor matters only for batches too small to fill the budget with
     // whole requests, which are latency-bound: there shorter chunks finish
     // sooner (tiny batch 17.7 -> 9.4 us, shared-prefix batch 44.4 -> 39.1 us

@@ -108,10 +108,10 @@ typedef struct fi_plan fi_plan; /* opaque, host-owned */
 /* Planner knobs. Zero selects the default for every field. */
 typedef struct {
   int32_t num_cus;            /* compute units to balance over (default 256) */
-  int32_t items_per_cu;       /* target work items per CU (default 8; 6 for a
-                                 plan that runs the matrix-core kernel
-                                 without the rotary embedding, which
-                                 measured faster with fewer, longer items) */
+  int32_t items_per_cu;       /* target work items per CU (default 8; for a
+                                 plan that runs the matrix-core kernel, 6
+                                 without the rotary embedding and 16 with
+                                 it, each measured best) */
   int32_t min_chunk_tokens;   /* never cut a request finer than this (default 32) */
   int32_t max_chunk_tokens;   /* cap on chunk length; 0 = no cap */
   int32_t fixed_chunk_tokens; /* >0: use exactly this chunk length (rounded up

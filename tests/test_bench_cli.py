@@ -88,3 +88,18 @@ def test_counter_summary_sums_the_kernels_of_a_step(tmp_path, monkeypatch):
     assert vals["source_sha256_16"] == bench.source_digest(kernels)
     assert bench.read_traffic("unit", kernels) is not None
     assert bench.read_traffic("unit", ["decode_bsr_kernel"]) is None  # no such summary
+
+
+def test_source_digest_follows_code_not_comments():
+    """The profiles record a digest of the kernel sources they were measured
+    with: comments and layout do not enter it, code does, and the repository
+    headers a source includes are part of it."""
+    sys.path.insert(0, ROOT)
+    import bench
+    code = 'int f(int x) {\n  return x + 1;  // add one\n}\n/* end */ const char* s = "a // b";\n'
+    assert bench._code_only(code) == bench._code_only(code.replace("add one", "plus 1")
+                                                      .replace("\n", "\n\n  "))
+    assert bench._code_only(code) != bench._code_only(code.replace("x + 1", "x + 2"))
+    assert bench._code_only(code) != bench._code_only(code.replace('"a // b"', '"a // c"'))
+    files = [os.path.basename(f) for f in bench._with_headers("attn_tile.hip")]
+    assert files[0] == "attn_tile.hip" and "coherent.h" in files and "fi_bsr.h" in files
