@@ -524,7 +524,7 @@ typedef struct fi_prefill_plan fi_prefill_plan; /* opaque, host-owned */
 /* Planner knobs. Zero selects the default for every field. */
 typedef struct {
   int32_t num_cus;            /* compute units to balance over (default 256) */
-  int32_t items_per_cu;       /* target work items per CU (default 4) */
+  int32_t items_per_cu;       /* target work items per CU (default 2) */
   int32_t fixed_chunk_tokens; /* >0: cut KV ranges into chunks of exactly this
                                  many tokens (rounded up to whole pages, at
                                  most FI_PREFILL_MAX_PAGES pages) */
