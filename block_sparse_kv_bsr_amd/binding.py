@@ -42,7 +42,8 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 QITEM_STRIDE = 16
 QMERGE_STRIDE = 8
 PREFILL_ROWS = 256
-PREFILL_MAX_PAGES = 256
+PREFILL_MAX_PAGES = 512
+MLA_MAX_PAGES = 256
 MLA_ROWS = 32
 MLA_DC = 512
 MLA_DR = 64

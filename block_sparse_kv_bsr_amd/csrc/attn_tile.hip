@@ -73,7 +73,8 @@ typedef __attribute__((address_space(1))) void global_void_t;
 
 constexpr int kWaves = 8;
 constexpr int kBlock = 64;   // tokens per ring stage (32 per wave half)
-constexpr int kIds = 256;    // page-id window
+constexpr int kIds = FI_PREFILL_MAX_PAGES;  // page-id window
+static_assert(FI_PREFIX_MAX_PAGES <= kIds && kIds <= 512, "page-id window: one id per thread");
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kMargin = 8.0f;  // lazy-rescale margin, log2 units
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
     }
     page_begin = it[FI_QITEM_PAGE_BEGIN];
     slot_base = it[FI_QITEM_SLOT];
-    npg = (ntok + p.page_size - 1) / p.page_size;  // <= FI_PREFILL_MAX_PAGES = kIds
+    npg = (ntok + p.page_size - 1) / p.page_size;  // <= FI_PREFILL_MAX_PAGES = kIds, ntok <= 2^20
     row_ok = row < nrows;
     const int qi = row_ok ? row / G : 0;
     gi = row_ok ? row % G : 0;
@@ -496,10 +497,11 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   constexpr int kAux = kPrefill ? 0 : 2;
   const int dma_row = lane / Gm::kPieces;
   const int dma_piece = lane % Gm::kPieces;
-  // tok / page_size as a multiply-high: tok < 2^20 (at most kIds pages of at
-  // most 4096 tokens) and the reciprocal ceil(2^32 / P) is too large by less
-  // than 1, so the quotient is off by less than 2^-12 < 1 / P -- exact for
-  // every P < 4096, and powers of two are exact anyway
+  // tok / page_size as a multiply-high: tok < 2^20 (a prefill chunk holds at
+  // most 2^20 tokens, a prefix item at most 256 pages of at most 4096) and the
+  // reciprocal ceil(2^32 / P) is too large by less than 1, so the quotient is
+  // off by less than 2^-12 < 1 / P -- exact for every P < 4096, and powers of
+  // two are exact anyway
   const uint32_t pmag = p.page_magic, pmag_hi = p.page_magic_hi;
   const uint32_t psz = (uint32_t)p.page_size;
   auto issue = [&](int j, int st) {

@@ -87,7 +87,7 @@ constexpr int kPBytes = kBlk * kDr * 2;
 constexpr int kStageBytes = kCBytes + kPBytes;
 constexpr int kSteps = (kDc + kDr) / 32;      // depth steps of the score product
 constexpr int kLatSteps = kDc / 32;
-constexpr int kIds = FI_PREFILL_MAX_PAGES;    // page-id window
+constexpr int kIds = FI_MLA_MAX_PAGES;        // page-id window
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kMargin = 8.0f;  // lazy-rescale margin, log2 units

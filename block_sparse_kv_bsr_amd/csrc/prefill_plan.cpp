@@ -162,8 +162,14 @@ fi_status build_tile_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
     }
     p->num_tiles = (int64_t)tiles.size() * num_kv_heads;
 
-    // ---- one chunk length C (whole pages, at most FI_PREFILL_MAX_PAGES)
-    const int64_t cap = (int64_t)FI_PREFILL_MAX_PAGES * page_size;
+    // ---- one chunk length C (whole pages, at most the kernel's page-id
+    // window; a prefill chunk also at most 2^20 tokens, the range over which
+    // the tile kernel's reciprocal division by the page size is exact). The
+    // longer prefill window measured 2.1-2.8% faster on the append batches
+    // than 256 pages (fewer cut tiles).
+    const int64_t cap_pages = mla ? (int64_t)FI_MLA_MAX_PAGES
+                                  : std::min<int64_t>(FI_PREFILL_MAX_PAGES, (int64_t(1) << 20) / page_size);
+    const int64_t cap = cap_pages * page_size;
     int64_t C;
     if (o.fixed_chunk_tokens > 0) {
       C = ceil_div(o.fixed_chunk_tokens, page_size) * page_size;

@@ -527,7 +527,8 @@ typedef struct {
   int32_t items_per_cu;       /* target work items per CU (default 2) */
   int32_t fixed_chunk_tokens; /* >0: cut KV ranges into chunks of exactly this
                                  many tokens (rounded up to whole pages, at
-                                 most FI_PREFILL_MAX_PAGES pages) */
+                                 most the chunk cap: FI_PREFILL_MAX_PAGES or
+                                 FI_MLA_MAX_PAGES pages) */
   int32_t num_xcds;           /* L2 domains the dispatcher deals workgroups
                                  over in turn (default 8, MI355X's XCDs) */
   int32_t rope;               /* nonzero: a plan for fi_prefill_run_rope --
@@ -594,7 +595,9 @@ enum {
   FI_QITEM_STRIDE = 16,     /* int32 per item; fields past MERGE are 0 */
   FI_PREFILL_ROWS = 256,      /* query rows per tile */
   FI_MLA_ROWS = 32,           /* (query token, head) rows per MLA tile */
-  FI_PREFILL_MAX_PAGES = 256  /* pages per chunk at most */
+  FI_PREFILL_MAX_PAGES = 512, /* pages per prefill chunk at most, and never
+                                 more than 2^20 tokens (256 pages of 4096) */
+  FI_MLA_MAX_PAGES = 256      /* pages per MLA chunk at most */
 };
 
 /* Fields of one merge of a cut tile (fi_prefill_plan_merges): its chunks'
@@ -631,8 +634,8 @@ enum {
  * Tiles: each request's query tokens in blocks of FI_PREFILL_ROWS / G, per
  * KV head. A tile attends the tokens its last query sees; that range is cut
  * into chunks of C tokens (whole pages, at most FI_PREFILL_MAX_PAGES
- * pages), C chosen so the items fill num_cus x items_per_cu (never finer
- * than 512 tokens) unless fixed_chunk_tokens is set.
+ * pages and 2^20 tokens), C chosen so the items fill num_cus x items_per_cu
+ * (never finer than 512 tokens) unless fixed_chunk_tokens is set.
  *
  * Order: every tile of one (request, KV head) reads the same K/V, so the
  * pairs are dealt to num_xcds bins, heaviest pair first into the least
@@ -766,7 +769,7 @@ fi_status fi_prefill_run_rope(const fi_prefill_plan* plan, const void* q, const 
  * FI_MLA_ROWS / num_heads whole query tokens when num_heads <= FI_MLA_ROWS,
  * else one query token's heads HEAD_BEGIN .. HEAD_BEGIN + FI_MLA_ROWS - 1.
  * Each tile's range is cut into chunks of C tokens (whole pages, at most
- * FI_PREFILL_MAX_PAGES pages; C fills num_cus x items_per_cu, default 2, and
+ * FI_MLA_MAX_PAGES pages; C fills num_cus x items_per_cu, default 2, and
  * is never below 1024 tokens) unless fixed_chunk_tokens is set. Every tile of
  * a request reads the same latent rows, so a request's items share an L2
  * domain as a prefill pair's do, and within it the tiles of one chunk are

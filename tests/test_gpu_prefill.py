@@ -90,6 +90,7 @@ CASES = [
     (8, 3, 700, 32, 8, 128, 16, True, None, 128),
     (9, 4, 333, 8, 8, 128, 3, False, 200, 0),
     (10, 2, 1000, 4, 1, 128, 64, True, 300, 192),
+    (11, 2, 1500, 8, 2, 128, 1, True, None, 512),  # 512 one-token pages per chunk: the whole id window
 ]
 
 

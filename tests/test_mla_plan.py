@@ -49,7 +49,7 @@ def check_plan(w, p):
         assert int(it[VIS]) == (int(L[b]) - n + t0 + 1 if w.causal else int(L[b]))
         assert int(it[KV0]) % P == 0
         assert int(it[PG0]) == int(w.kv_indptr[b]) + int(it[KV0]) // P
-        assert int(it[NKV]) <= binding.PREFILL_MAX_PAGES * P
+        assert int(it[NKV]) <= binding.MLA_MAX_PAGES * P
         tiles.setdefault((int(it[QROW]), int(it[HB])), []).append(it)
     # every (query token, head) row in exactly one tile
     cover = {}

@@ -50,7 +50,8 @@ def check_prefill_plan(w, p):
         assert int(it[VIS]) == want_vis
         assert int(it[KV0]) % P == 0
         assert int(it[PG0]) == int(w.kv_indptr[b]) + int(it[KV0]) // P
-        assert int(it[NKV]) <= binding.PREFILL_MAX_PAGES * P
+        # the chunk cap: the kernel's page-id window and 2^20 tokens
+        assert int(it[NKV]) <= min(binding.PREFILL_MAX_PAGES, (1 << 20) // P) * P
         assert int(it[NKV]) > 0 or Lb == 0
     # every (request, head, query token) covered by exactly one tile
     cover = {}
@@ -176,6 +177,22 @@ def _pair_positions(items):
     for i, x in enumerate(items):
         pos.setdefault((int(x[REQ]), int(x[KVH])), []).append(i)
     return pos
+
+
+@pytest.mark.parametrize("P", [16, 1000, 3000, 4096])
+def test_chunk_cap_is_the_window_and_2_20_tokens(P):
+    """A prefill chunk holds at most FI_PREFILL_MAX_PAGES pages (the tile
+    kernel's page-id window) and at most 2^20 tokens (the range over which
+    its reciprocal division by the page size is exact), whatever chunk
+    length is asked for."""
+    cap = min(binding.PREFILL_MAX_PAGES, (1 << 20) // P) * P
+    L = 3 * cap + P // 2
+    w = random_prefill_workload(31, 1, L, 4, 1, 128, P, causal=True, lens=[L], qo_lens=[3])
+    p = make_plan(w, fixed_chunk_tokens=1 << 30)
+    items = p.work_list()
+    assert items[:, NKV].max() == cap and len(items) == 4
+    assert items[:, NKV].max() <= 1 << 20
+    check_prefill_plan(w, p)
 
 
 def test_order_one_bin_is_pairs_heaviest_first():
