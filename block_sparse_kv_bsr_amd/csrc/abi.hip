@@ -124,8 +124,8 @@ fi_status fi_prefill_plan_upload(fi_prefill_plan* plan, void* workspace, size_t 
 namespace {
 
 // The prefill run shared by the entry points below (checks, then the tile
-// kernel and, for cut tiles, the merge kernel). rope_theta > 0 selects the
-// rotary variant.
+// kernel, which also merges cut tiles). rope_theta > 0 selects the rotary
+// variant.
 fi_status prefill_run(const fi_prefill_plan* plan, const void* q, const void* k_pages,
                       const void* v_pages, float k_scale, float v_scale, float rope_theta,
                       float rope_scale, void* out, float* lse, float sm_scale, void* workspace,

@@ -1,9 +1,9 @@
-"""GPU parity of prefill / append attention: the HIP tile kernel (and the
-merge kernel for cut tiles) through the C ABI against the float64 oracle.
+"""GPU parity of prefill / append attention: the HIP tile kernel (which also
+merges cut tiles) through the C ABI against the float64 oracle.
 
 Small ragged cases cover both head sizes, GQA groups 1..8 and one that is
 not a power of two, page sizes 1..64, causal and unmasked, single-chunk
-tiles (direct output) and cut tiles (forced chunk lengths, merge kernel),
+tiles (direct output) and cut tiles (forced chunk lengths, in-kernel merge),
 requests with no queries and an unmasked request with no pages, over bf16
 and fp8 (E4M3, dequantisation scales) caches. The full-size workloads run
 with the plan bench.py times and are checked on every output element.

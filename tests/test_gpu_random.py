@@ -8,7 +8,7 @@ drawn independently:
   embedding on some bf16 d = 128 cases;
 * cascade: random groups of requests sharing a prefix, forced on;
 * prefill / append: any GQA group the tile holds (not only powers of two),
-  causal or not, forced chunk lengths (merge kernel).
+  causal or not, forced chunk lengths (cut tiles merged in the kernel).
 
 Every case prints its parameters before it runs.
 """
