@@ -12,6 +12,7 @@ from block_sparse_kv_bsr_amd.workloads import random_prefill_workload, workload
 import oracle.attention as oa
 
 REQ, KVH, QROW, NQO, KV0, NKV, VIS, PG0, SLOT, CHUNK = range(10)
+MERGE = 12
 M_QROW, M_NQO, M_KVH, M_SLOT0, M_NCH = range(5)
 
 
@@ -77,11 +78,17 @@ def check_prefill_plan(w, p):
     # merges: exactly the cut tiles
     cut = {k: its for k, its in tiles.items() if len(its) > 1}
     assert len(merges) == len(cut) == info["num_merges"]
-    for m in merges:
+    for mi, m in enumerate(merges):
         b = int(np.searchsorted(qo, m[M_QROW], side="right")) - 1
         its = cut[(b, int(m[M_KVH]), int(m[M_QROW]))]
         assert int(m[M_NCH]) == len(its) and int(m[M_NQO]) == int(its[0][NQO])
         assert int(m[M_SLOT0]) == min(int(x[SLOT]) for x in its)
+        # each chunk of a cut tile names the tile's merge (its arrival counter)
+        assert all(int(x[MERGE]) == mi for x in its)
+    for its in tiles.values():
+        if len(its) == 1:
+            assert int(its[0][MERGE]) == -1
+    assert np.all(items[:, MERGE + 1:] == 0)
     used = sorted(int(x) for x in items[:, SLOT] if x >= 0)
     assert used == list(range(info["num_partial_slots"]))
     assert info["visible_pairs"] == w.visible_pairs()
