@@ -8,7 +8,9 @@ drawn independently:
   embedding on some bf16 d = 128 cases;
 * cascade: random groups of requests sharing a prefix, forced on;
 * prefill / append: any GQA group the tile holds (not only powers of two),
-  causal or not, forced chunk lengths (cut tiles merged in the kernel).
+  causal or not, forced chunk lengths (cut tiles merged in the kernel);
+* in-kernel merges of prefill and latent-attention tiles cut into many short
+  chunks, repeated for bit-identical results and checked against the oracle.
 
 Every case prints its parameters before it runs.
 """
@@ -18,8 +20,8 @@ import torch
 
 import block_sparse_kv_bsr_amd as fb
 import oracle.attention as oa
-from block_sparse_kv_bsr_amd.workloads import (prefix_workload, random_prefill_workload,
-                                               random_workload)
+from block_sparse_kv_bsr_amd.workloads import (prefix_workload, random_mla_workload,
+                                               random_prefill_workload, random_workload)
 from tests.parity import compare
 
 pytestmark = pytest.mark.gpu
@@ -221,4 +223,66 @@ def test_large_page_sizes_prefill(P):
     O, LSE = oa.prefill_attention(qh, kh, vh, w.qo_indptr, w.kv_indptr, w.kv_indices,
                                   w.last_page_len, True, w.sm_scale)
     stats = compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), O, LSE, True, what)
+    log(f"[ok] items={p.info['num_items']} merges={p.info['num_merges']} {stats}")
+
+
+def _merge_cases(n, seed):
+    """Random plans with many chunks per cut tile (short forced chunks), for
+    the in-kernel merges of the prefill and latent-attention tile kernels."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = "mla" if i % 2 else "prefill"
+        P = int(rng.choice([1, 4, 16]))
+        B = int(rng.integers(1, 5))
+        L = int(rng.integers(100, 1500))
+        fixed = int(rng.choice([16, 32, 48, 96]))
+        heads = int(rng.choice([8, 16, 40, 96])) if kind == "mla" else int(rng.choice([4, 8, 16]))
+        out.append((7400 + i, kind, B, L, P, fixed, heads))
+    return out
+
+
+MERGE_CASES = _merge_cases(12, 20261205)
+
+
+@pytest.mark.parametrize("case", MERGE_CASES, ids=lambda c: f"mg{c[0]}_{c[1]}_P{c[4]}_c{c[5]}")
+def test_random_in_kernel_merges(case):
+    """Cut tiles merged by whichever chunk arrives last: each case is run five
+    times, every other run after a cache flush so arrival orders differ, and
+    every run must equal the first bit for bit; the first is also compared
+    with the float64 oracle. Chunks of 16-96 tokens give up to ~90 chunks
+    per tile (many groups in the merging loop)."""
+    seed, kind, B, L, P, fixed, heads = case
+    log(f"[case] merges seed{seed} {kind} B={B} L<={L} P={P} chunk={fixed} heads={heads}")
+    if kind == "mla":
+        w = random_mla_workload(seed, B, L, heads, P, max_qo=2)
+        qn, qp, ckv, kpe = (t.cuda() for t in w.make_values("cpu"))
+        p = fb.mla_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, heads, P,
+                        w.num_pool_pages, causal=w.causal, fixed_chunk_tokens=fixed)
+        run = lambda out=None, lse=None: fb.mla(qn, qp, ckv, kpe, p, w.sm_scale, out=out, lse=lse)
+    else:
+        w = random_prefill_workload(seed, B, L, heads, 2, 128, P, causal=True, max_qo=60)
+        q, k, v = (t.cuda() for t in w.make_values("cpu"))
+        p = fb.prefill_plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.last_page_len, heads, 2, 128,
+                            P, w.num_pool_pages, causal=True, fixed_chunk_tokens=fixed)
+        run = lambda out=None, lse=None: fb.prefill(q, k, v, p, out=out, lse=lse)
+    assert p.info["num_merges"] > 0
+    o0, l0 = run()
+    out, lse = torch.empty_like(o0), torch.empty_like(l0)
+    flush = torch.empty(1 << 26, dtype=torch.uint8, device="cuda")
+    for r in range(1, 5):
+        if r % 2:
+            flush.zero_()
+        run(out, lse)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), o0.view(torch.int16)) and torch.equal(lse, l0), r
+    if kind == "mla":
+        h = [t.double().cpu().numpy() for t in (qn, qp, ckv, kpe)]
+        O, LSE = oa.mla_attention(h[0], h[1], h[2], h[3], w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                  w.last_page_len, w.sm_scale, w.causal)
+    else:
+        qh, kh, vh = (t.double().cpu().numpy() for t in (q, k, v))
+        O, LSE = oa.prefill_attention(qh, kh, vh, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                      w.last_page_len, True, w.sm_scale)
+    stats = compare(o0.double().cpu().numpy(), l0.double().cpu().numpy(), O, LSE, True, kind)
     log(f"[ok] items={p.info['num_items']} merges={p.info['num_merges']} {stats}")
