@@ -187,9 +187,9 @@ def summarize_counters(fetch_csv, write_csv, workload_name):
     print(open(path).read())
 
 
-# $REPO is the repository root
+# $REPO is the repository root, $OUT any directory for the profiler's output
 TRACE_COMMAND = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
-                 "-d $REPO/gpurun_out/trace_{cfg} -o trace -- python $REPO/bench.py --config {cfg} "
+                 "-d $OUT/trace_{cfg} -o trace -- python $REPO/bench.py --config {cfg} "
                  "--steps 20 --warmup 5 --no-cpu-baseline")
 
 
@@ -245,7 +245,7 @@ def summarize_trace(stats_csv, bench_log, w, config_id):
     else:
         o.append(f"Algorithmic bytes per batch: {w.algorithmic_bytes():,} (K+V of every active "
                  f"token once per KV head + q + output).\n")
-    o.append("Command (one MI355X; $REPO is the repository root):\n")
+    o.append("Command (one MI355X; $REPO is the repository root, $OUT any output directory):\n")
     o.append("    " + TRACE_COMMAND.format(cfg=config_id) + "\n")
     o.append("`--stats` kernel summary, durations in microseconds:\n")
     o.append("| kernel | calls | avg | min | max | % of GPU time |")
@@ -335,8 +335,8 @@ def stream_ceiling(dev, flush, nbytes=2 << 30, reps=5):
 def _one_thread():
     """A context holding numpy's BLAS to one thread, and the thread count
     the oracle then uses. The oracle's products (one request and KV head at a
-    time) are too small for BLAS threads to pay off: on the GPU machine's host
-    the 16-thread default ran slower than one thread."""
+    time) are too small for BLAS threads to pay off: on a 16-thread host the
+    default of 16 BLAS threads ran slower than one thread."""
     try:
         from threadpoolctl import threadpool_limits
         return threadpool_limits(limits=1), 1
