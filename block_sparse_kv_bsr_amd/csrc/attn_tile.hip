@@ -424,14 +424,17 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
 
   // Q^T as the B operand: lane holds Q[row][16s + 8*half .. +8] for step s
   // (a padding row loads the tile's first row and zeroes it, so the loads
-  // are unconditional)
+  // are unconditional). Without the rotary embedding the loads stay in
+  // flight while the first K/V blocks are requested (they are waited for,
+  // and padding rows zeroed, after those requests).
   bf16x8_t qf[D / 16];
   {
     const char* qrow = p.q + q_index * (D * 2);  // q is bf16 whatever the cache holds
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       uint4 v = *reinterpret_cast<const uint4*>(qrow + (16 * s + 8 * half) * 2);
-      if (!row_ok) v = make_uint4(0, 0, 0, 0);
+      if constexpr (kRope)
+        if (!row_ok) v = make_uint4(0, 0, 0, 0);
       qf[s] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -480,9 +483,8 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
       ql[s + D / 32] = __builtin_bit_cast(bf16x8_t, u32x4_t{yl[0], yl[1], yl[2], yl[3]});
     }
   }
-  // q and the page ids are in before any K/V load is issued, so the waits on
-  // the ring below count K/V loads only
-  wait_vmcnt<0>();
+  // the page ids are in LDS before any K/V load is issued (q may still be on
+  // its way)
   __syncthreads();  // s_pid is written
 
   // ---- direct-to-LDS loads of block j into stage st: wave-wide load i of
@@ -535,6 +537,15 @@ __global__ __launch_bounds__(512) void tile_attend_kernel(TileParams p) {
   const int nblocks = (ntok + kBlock - 1) / kBlock;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s, s);
+  // q (issued before the ring loads) is in: vector memory loads complete in
+  // order, so at most this stage-filling's loads remain. From here on only
+  // ring loads are in flight, which the waits in the loop count.
+  wait_vmcnt<2 * Gm::kDmaPerWave * (NS - 1)>();
+  if constexpr (!kRope) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      if (!row_ok) qf[s] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+  }
 
   // LDS byte offsets that depend only on the lane. K fragment q of token row
   // kt = 32 (wtok + sb) + lane % 32 sits at kt * kRB + piece * 16 with the
