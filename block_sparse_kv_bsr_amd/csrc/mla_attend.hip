@@ -292,22 +292,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void mla_attend_kernel(MlaParams p)
 
   // Q^T as the B operand: lane n + 16g holds Q[row n][32s + 8g .. +8] for
   // depth step s (latent part for s < 16, rotary part after); a padding row
-  // loads the tile's first row and zeroes it, so the loads are unconditional
+  // loads the tile's first row and zeroes it, so the loads are
+  // unconditional. The loads stay in flight while the first block is
+  // requested.
   bf16x8_t qf[kSteps];
   {
     const char* qn = p.q_nope + q_index * (kDc * 2);
     const char* qp = p.q_pe + q_index * (kDr * 2);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      uint4 v = s < kLatSteps ? *reinterpret_cast<const uint4*>(qn + (32 * s + 8 * g) * 2)
-                              : *reinterpret_cast<const uint4*>(qp + (32 * (s - kLatSteps) + 8 * g) * 2);
-      if (!row_ok) v = make_uint4(0, 0, 0, 0);
+      const uint4 v = s < kLatSteps ? *reinterpret_cast<const uint4*>(qn + (32 * s + 8 * g) * 2)
+                                    : *reinterpret_cast<const uint4*>(qp + (32 * (s - kLatSteps) + 8 * g) * 2);
       qf[s] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
-  // q and the page ids are in before any ring load is issued, so the vmcnt
-  // waits below count ring loads only
-  wait_vmcnt<0>();
+  // the page ids are in LDS before any ring load is issued (q may still be
+  // on its way)
   __syncthreads();
 
   // ---- direct-to-LDS loads of block j into stage st. Wave w loads rows
@@ -364,6 +364,13 @@ __global__ __launch_bounds__(64 * kWaves, 2) void mla_attend_kernel(MlaParams p)
 
   const int nblocks = (ntok + kBlk - 1) / kBlk;
   issue(0, 0);
+  // q (issued before block 0's loads) is in: vector memory loads complete in
+  // order, so at most block 0's nine loads remain; from here on only ring
+  // loads are in flight
+  wait_vmcnt<9>();
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s)
+    if (!row_ok) qf[s] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
 
   // Scores stay unscaled; exp2(c * s - c * m) is one fma and an exp. The
   // running max is raised only when a block's max passes it by more than
